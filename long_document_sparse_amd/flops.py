@@ -1,0 +1,80 @@
+"""Algorithmic work of one forward: allowed (query, key) pairs, FLOPs and bytes.
+
+The cost model is the O(n(w+g)) count of the Longformer pages ("LongFormer: The
+Long-Document Transformer" notes, "Sliding Window" and "Global Attention"; the
+bmjup.com explainer's complexity formula): every allowed pair costs one
+d-long dot product for Q.K^T and one d-long axpy for P.V, i.e. 4*d FLOPs.
+Masked-off, padded and tile-waste work is not counted, nor is the softmax.
+
+Bytes count each input row the forward must read once and each output row
+once: Q at local rows, Qg at global rows, K and V at valid rows, Kg and Vg at
+valid rows when the batch row has any global token, O at every row, and the
+two float32 masks.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import numpy as np
+
+
+def _flags(lmask, gmask):
+    v = np.asarray(lmask) != 0
+    g = v & (np.asarray(gmask) != 0)
+    return v, g
+
+
+def row_counts(lmask_row, gmask_row, window: int, gap: int) -> np.ndarray:
+    """Allowed-key count of every query row of one (batch row, head); 0 for padding."""
+    v, g = _flags(lmask_row, gmask_row)
+    n = v.shape[0]
+    r = window // 2
+    s = gap + 1
+    nglob = int(g.sum())
+    nvalid = int(v.sum())
+    out = np.zeros(n, np.int64)
+    winkey = (v & ~g).astype(np.int64)
+    for rho in range(min(s, n)):
+        sub = winkey[rho::s]
+        m = sub.shape[0]
+        pre = np.concatenate([[0], np.cumsum(sub)])
+        t = np.arange(m)
+        lo = np.maximum(t - r, 0)
+        hi = np.minimum(t + r, m - 1)
+        out[rho::s] = pre[hi + 1] - pre[lo] + nglob
+    out[g] = nvalid
+    out[~v] = 0
+    return out
+
+
+def pairs(lmask, gmask, window: int, dilation: Sequence[int]) -> int:
+    lm = np.asarray(lmask)
+    gm = np.asarray(gmask)
+    total = 0
+    for b in range(lm.shape[0]):
+        for gap in dilation:
+            total += int(row_counts(lm[b], gm[b], window, int(gap)).sum())
+    return total
+
+
+def flops(lmask, gmask, window: int, dilation: Sequence[int], d: int) -> int:
+    return 4 * d * pairs(lmask, gmask, window, dilation)
+
+
+def global_pairs(lmask, gmask, H: int) -> int:
+    """Pairs of the global rows alone (each global row sees every valid key)."""
+    v, g = _flags(lmask, gmask)
+    return int(H * (v.sum(axis=1) * g.sum(axis=1)).sum())
+
+
+def hbm_bytes(lmask, gmask, H: int, d: int, elt: int) -> int:
+    v, g = _flags(lmask, gmask)
+    n = v.shape[1]
+    total = 0
+    for b in range(v.shape[0]):
+        nv = int(v[b].sum())
+        ng = int(g[b].sum())
+        rows = (nv - ng) + ng + 2 * nv + (2 * nv if ng > 0 else 0) + n
+        total += H * rows * d * elt
+    total += 2 * 4 * v.size
+    return total

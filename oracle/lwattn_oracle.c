@@ -1,0 +1,211 @@
+/*
+ * lwattn_oracle.c -- CPU oracle for the Longformer window + global attention
+ * forward.  TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the HIP path under long_document_sparse_amd/.
+ *
+ * It is the plain definition of the method, computed directly in double
+ * precision, one query row at a time, over an explicit list of allowed keys:
+ *
+ *   - "LongFormer: The Long-Document Transformer" notes (coding-zuo.github.io),
+ *     section "Sliding Window": every token looks at w/2 tokens on each side.
+ *   - same page, section "Dilated Sliding Window": the window has gaps, as in
+ *     a dilated convolution; different heads may use different dilations.
+ *   - same page, section "Global Attention": pre-selected tokens attend to every
+ *     token and every token attends to them; the global scores use their own
+ *     projections Qg, Kg, Vg, the window scores use Qs, Ks, Vs.
+ *   - FasterTransformer Longformer encoder guide (hnwysp.cn), "compute flow":
+ *     a local token's softmax spans its window plus the global tokens, a global
+ *     token's softmax spans the whole sequence, and the output row of a padded
+ *     query is zeroed; the global token indices are the stable partition of
+ *     the global flags (global_idx, global_token_nums).
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *   window  : keys i + k*s for -w/2 <= k <= w/2, with s = gap + 1 (the dilation
+ *             value is the number of skipped positions between taps); keys
+ *             outside [0, n) do not exist.
+ *   padding : lmask[j] == 0 makes j a padded position: it is never a key, its
+ *             output row is exactly zero, and it is never global ("padding
+ *             wins" over the global flag).
+ *   masks   : a mask value counts as set when it compares != 0.0f.
+ *   globals : a local row uses Q.K and V both for its window keys and for the
+ *             global keys; a global row uses Qg.Kg and Vg over all valid keys.
+ *             A global key inside a local row's window is counted once.
+ *   masking : excluded keys are left out of the softmax (no additive bias).
+ *   softmax : two passes -- the maximum over the allowed set, then
+ *             p_j = exp(x_j - max) / sum_k exp(x_k - max).
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (see oracle/__init__.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define LWO_PADDED 0
+#define LWO_GLOBAL 1
+#define LWO_LOCAL 2
+
+typedef struct {
+  int32_t B, H, n, d;
+  int32_t window;        /* w; reach w/2 on each side */
+  const int32_t* gap;    /* [H] dilation gap per head (stride = gap + 1) */
+  double scale;          /* multiplies q.k */
+  const float *Q, *K, *V, *Qg, *Kg, *Vg; /* [B,H,n,d] */
+  const float* lmask;    /* [B,n] */
+  const float* gmask;    /* [B,n] */
+} lwo_problem;
+
+static int is_valid(const float* lm, int64_t j) { return lm[j] != 0.0f; }
+static int is_global(const float* lm, const float* gm, int64_t j) {
+  return lm[j] != 0.0f && gm[j] != 0.0f;
+}
+
+/* Global-index compaction: for every batch row, the ascending positions of the
+ * global tokens (valid and flagged), then -1 up to n; and their count. */
+int lwo_compact(const float* lmask, const float* gmask, int32_t B, int32_t n,
+                int32_t* gidx, int32_t* gcnt) {
+  for (int32_t b = 0; b < B; ++b) {
+    const float* lm = lmask + (int64_t)b * n;
+    const float* gm = gmask + (int64_t)b * n;
+    int32_t* out = gidx + (int64_t)b * n;
+    int32_t count = 0;
+    for (int32_t j = 0; j < n; ++j)
+      if (is_global(lm, gm, j)) out[count++] = j;
+    for (int32_t k = count; k < n; ++k) out[k] = -1;
+    gcnt[b] = count;
+  }
+  return 0;
+}
+
+/* The allowed key set of query row i of one batch row, ascending within each
+ * part (window keys first, then the global keys).  Writes the keys to `keys`
+ * (capacity n), the row kind to *kind, and returns the number of keys. */
+int64_t lwo_allowed(const float* lm, const float* gm, int32_t n, int32_t window,
+                    int32_t gap, int32_t i, int32_t* keys, int32_t* kind) {
+  int64_t cnt = 0;
+  if (!is_valid(lm, i)) {
+    *kind = LWO_PADDED;
+    return 0;
+  }
+  if (is_global(lm, gm, i)) {
+    *kind = LWO_GLOBAL;
+    for (int32_t j = 0; j < n; ++j)
+      if (is_valid(lm, j)) keys[cnt++] = j;
+    return cnt;
+  }
+  *kind = LWO_LOCAL;
+  const int64_t s = (int64_t)gap + 1;
+  const int64_t r = window / 2;
+  /* taps k with 0 <= i + k*s <= n-1, limited to |k| <= r */
+  int64_t klo = -((int64_t)i / s);
+  int64_t khi = ((int64_t)n - 1 - i) / s;
+  if (klo < -r) klo = -r;
+  if (khi > r) khi = r;
+  for (int64_t k = klo; k <= khi; ++k) {
+    int64_t j = (int64_t)i + k * s;
+    if (is_valid(lm, j) && !is_global(lm, gm, j)) keys[cnt++] = (int32_t)j;
+  }
+  for (int32_t j = 0; j < n; ++j)
+    if (is_global(lm, gm, j)) keys[cnt++] = j;
+  return cnt;
+}
+
+/* One output row (b, h, i) into out[0..d). keys/p are scratch of size n. */
+static void lwo_row(const lwo_problem* p, int32_t b, int32_t h, int32_t i,
+                    int32_t* keys, double* prob, double* out) {
+  const int32_t n = p->n, d = p->d;
+  const float* lm = p->lmask + (int64_t)b * n;
+  const float* gm = p->gmask + (int64_t)b * n;
+  int32_t kind;
+  int64_t cnt = lwo_allowed(lm, gm, n, p->window, p->gap[h], i, keys, &kind);
+  for (int32_t c = 0; c < d; ++c) out[c] = 0.0;
+  if (kind == LWO_PADDED) return;
+
+  const int64_t head = ((int64_t)b * p->H + h) * (int64_t)n * d;
+  const float* q = (kind == LWO_GLOBAL ? p->Qg : p->Q) + head + (int64_t)i * d;
+  const float* kmat = (kind == LWO_GLOBAL ? p->Kg : p->K) + head;
+  const float* vmat = (kind == LWO_GLOBAL ? p->Vg : p->V) + head;
+
+  /* scores x_t = scale * <q, k_j> and their maximum */
+  double mx = -INFINITY;
+  for (int64_t t = 0; t < cnt; ++t) {
+    const float* kr = kmat + (int64_t)keys[t] * d;
+    double dot = 0.0;
+    for (int32_t c = 0; c < d; ++c) dot += (double)q[c] * (double)kr[c];
+    prob[t] = p->scale * dot;
+    if (prob[t] > mx) mx = prob[t];
+  }
+  /* softmax over the allowed set */
+  double sum = 0.0;
+  for (int64_t t = 0; t < cnt; ++t) {
+    prob[t] = exp(prob[t] - mx);
+    sum += prob[t];
+  }
+  for (int64_t t = 0; t < cnt; ++t) prob[t] /= sum;
+  /* weighted sum of the value rows */
+  for (int64_t t = 0; t < cnt; ++t) {
+    const float* vr = vmat + (int64_t)keys[t] * d;
+    for (int32_t c = 0; c < d; ++c) out[c] += prob[t] * (double)vr[c];
+  }
+}
+
+/* Selected rows: rows[t] is the flat index (b*H + h)*n + i; out is [nrows, d].
+ * Rows are independent, so they are spread over `threads` OpenMP threads. */
+int lwo_rows(const lwo_problem* p, const int64_t* rows, int64_t nrows,
+             double* out, int32_t threads) {
+  const int64_t total = (int64_t)p->B * p->H * p->n;
+  for (int64_t t = 0; t < nrows; ++t)
+    if (rows[t] < 0 || rows[t] >= total) return 1;
+  if (threads < 1) threads = 1;
+  int err = 0;
+#pragma omp parallel num_threads(threads)
+  {
+    int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)(p->n > 0 ? p->n : 1));
+    double* prob = (double*)malloc(sizeof(double) * (size_t)(p->n > 0 ? p->n : 1));
+    if (!keys || !prob) {
+#pragma omp atomic write
+      err = 2;
+    } else {
+#pragma omp for schedule(dynamic, 64)
+      for (int64_t t = 0; t < nrows; ++t) {
+        int64_t f = rows[t];
+        int32_t i = (int32_t)(f % p->n);
+        int64_t bh = f / p->n;
+        int32_t h = (int32_t)(bh % p->H);
+        int32_t b = (int32_t)(bh / p->H);
+        lwo_row(p, b, h, i, keys, prob, out + t * p->d);
+      }
+    }
+    free(keys);
+    free(prob);
+  }
+  return err;
+}
+
+/* Every row: out is [B,H,n,d]. */
+int lwo_forward(const lwo_problem* p, double* out, int32_t threads) {
+  const int64_t total = (int64_t)p->B * p->H * p->n;
+  if (threads < 1) threads = 1;
+  int err = 0;
+#pragma omp parallel num_threads(threads)
+  {
+    int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)(p->n > 0 ? p->n : 1));
+    double* prob = (double*)malloc(sizeof(double) * (size_t)(p->n > 0 ? p->n : 1));
+    if (!keys || !prob) {
+#pragma omp atomic write
+      err = 2;
+    } else {
+#pragma omp for schedule(dynamic, 64)
+      for (int64_t f = 0; f < total; ++f) {
+        int32_t i = (int32_t)(f % p->n);
+        int64_t bh = f / p->n;
+        lwo_row(p, (int32_t)(bh / p->H), (int32_t)(bh % p->H), i, keys, prob,
+                out + f * p->d);
+      }
+    }
+    free(keys);
+    free(prob);
+  }
+  return err;
+}

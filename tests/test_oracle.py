@@ -1,0 +1,300 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test fixes the oracle to something the pages or the mathematics determine:
+hand-derived key sets (tests/golden/allowed_sets.txt), a dense brute force that
+builds the mask differently, the textbook softmax attention of torch's
+scaled_dot_product_attention in float64, closed forms (Q = 0, constant V),
+exact zeros, invariance to rows the method never reads, the residue-class
+decomposition of a dilated window, and numpy.flatnonzero for the compaction.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bruteforce import dense_forward
+from long_document_sparse_amd import flops, workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "allowed_sets.txt")
+
+
+def _parse_golden():
+    cases = []
+    cur = None
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("case"):
+                kv = dict(tok.split("=") for tok in line.split()[1:])
+                ints = lambda s: [int(x) for x in s.split(",") if x]
+                cur = dict(n=int(kv["n"]), window=int(kv["window"]), gap=int(kv["gap"]),
+                           pad=ints(kv["pad"]), glob=ints(kv["global"]), rows={})
+                cases.append(cur)
+                continue
+            i, rest = line.split(":")
+            rest = rest.strip()
+            cur["rows"][int(i)] = None if rest == "padded" else [int(x) for x in rest.split()]
+    return cases
+
+
+GOLDEN_CASES = _parse_golden()
+
+
+def _masks(n, pad, glob):
+    lm = np.ones(n, np.float32)
+    lm[pad] = 0.0
+    gm = np.zeros(n, np.float32)
+    gm[glob] = 1.0
+    return lm, gm
+
+
+def test_golden_file_is_complete():
+    assert len(GOLDEN_CASES) == 5
+    for c in GOLDEN_CASES:
+        assert sorted(c["rows"]) == list(range(c["n"]))
+
+
+@pytest.mark.parametrize("case", GOLDEN_CASES, ids=lambda c: f"n{c['n']}w{c['window']}g{c['gap']}")
+def test_allowed_sets_match_hand_derivation(case):
+    lm, gm = _masks(case["n"], case["pad"], case["glob"])
+    for i, want in case["rows"].items():
+        kind, keys = oracle.allowed(lm, gm, case["window"], case["gap"], i)
+        if want is None:
+            assert kind == oracle.PADDED and keys.size == 0
+        else:
+            assert sorted(keys.tolist()) == want
+            assert len(set(keys.tolist())) == len(keys), "a key counted twice"
+
+
+@pytest.mark.parametrize("case", GOLDEN_CASES, ids=lambda c: f"n{c['n']}w{c['window']}g{c['gap']}")
+def test_zero_query_closed_form(case):
+    """Q = Qg = 0 and one-hot V rows: O_i = 1/|A_i| on the channels of A_i."""
+    n = case["n"]
+    d = 16
+    lm, gm = _masks(n, case["pad"], case["glob"])
+    Q = np.zeros((1, 1, n, d), np.float32)
+    K = np.random.default_rng(0).standard_normal((1, 1, n, d)).astype(np.float32)
+    Kg = np.random.default_rng(1).standard_normal((1, 1, n, d)).astype(np.float32)
+    V = np.zeros((1, 1, n, d), np.float32)
+    V[0, 0, np.arange(n), np.arange(n)] = 1.0
+    out = oracle.forward(Q, K, V, Q, Kg, V, lm[None], gm[None], case["window"], [case["gap"]],
+                         scale=0.7)
+    for i, want in case["rows"].items():
+        exp = np.zeros(d)
+        if want is not None:
+            exp[want] = 1.0 / len(want)
+        assert np.array_equal(out[0, 0, i], exp), (i, out[0, 0, i], exp)
+
+
+def _random_problem(rng, B, H, n, d, window, gaps, n_glob, pad_frac, glob_in_pad=True):
+    lm = np.ones((B, n), np.float32)
+    gm = np.zeros((B, n), np.float32)
+    for b in range(B):
+        npad = int(rng.integers(0, int(pad_frac * n) + 1)) if pad_frac > 0 else 0
+        if npad:
+            # scattered padding, not only a tail
+            lm[b, rng.choice(n, size=npad, replace=False)] = 0.0
+        g = min(n_glob, n)
+        if g:
+            gm[b, rng.choice(n, size=g, replace=False)] = 1.0
+        if glob_in_pad and npad and n > 1:
+            # a position that is both padded and flagged global
+            j = int(np.flatnonzero(lm[b] == 0)[0])
+            gm[b, j] = 1.0
+    arrs = [rng.standard_normal((B, H, n, d)).astype(np.float32) for _ in range(6)]
+    return arrs, lm, gm
+
+
+CASES = []
+for n in (1, 2, 7, 33, 64, 128, 257):
+    for window in (0, 2, 4, 8, 2 * n + 2):
+        CASES.append((n, window))
+
+
+@pytest.mark.parametrize("n,window", CASES)
+def test_oracle_matches_dense_bruteforce(n, window):
+    rng = np.random.default_rng(1000 * n + window)
+    H = 4
+    gaps = [0, 1, 2, 3]
+    for n_glob, pad_frac in ((0, 0.0), (1, 0.0), (5, 0.2), (3, 0.5)):
+        arrs, lm, gm = _random_problem(rng, 2, H, n, 8, window, gaps, n_glob, pad_frac)
+        scale = float(rng.uniform(0.1, 1.0))
+        got = oracle.forward(*arrs, lm, gm, window, gaps, scale=scale, threads=2)
+        want = dense_forward(*arrs, lm, gm, window, gaps, scale)
+        assert np.max(np.abs(got - want)) < 1e-12
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    m = None if mask is None else torch.from_numpy(mask)
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), attn_mask=m, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("gap", [0, 1, 3])
+def test_wide_window_is_full_attention(gap):
+    """w >= 2n (undilated): every row sees every key -> textbook attention."""
+    rng = np.random.default_rng(7)
+    B, H, n, d = 2, 3, 50, 16
+    arrs = [rng.standard_normal((B, H, n, d)).astype(np.float32) for _ in range(6)]
+    lm = np.ones((B, n), np.float32)
+    gm = np.zeros((B, n), np.float32)
+    gm[0, [0, 17]] = 1.0
+    scale = 1.0 / math.sqrt(d)
+    out = oracle.forward(*arrs, lm, gm, 2 * n, [0] * H, scale=scale)
+    Q, K, V, Qg, Kg, Vg = arrs
+    ref_local = _sdpa(Q, K, V, scale)
+    ref_glob = _sdpa(Qg, Kg, Vg, scale)
+    glob = gm != 0
+    ref = np.where(glob[:, None, :, None], ref_glob, ref_local)
+    assert np.max(np.abs(out - ref)) < 1e-12
+    # a window wider than the sequence with gap > 0 keeps only the taps on the
+    # query's residue class: compare with attention restricted to that class
+    if gap:
+        out = oracle.forward(*arrs, lm, np.zeros_like(gm), 4 * n, [gap] * H, scale=scale)
+        s = gap + 1
+        idx = np.arange(n)
+        same = (idx[:, None] - idx[None, :]) % s == 0
+        ref = _sdpa(Q, K, V, scale, mask=same)
+        assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_global_rows_are_full_attention_under_global_projections():
+    rng = np.random.default_rng(11)
+    B, H, n, d = 2, 2, 96, 32
+    arrs = [rng.standard_normal((B, H, n, d)).astype(np.float32) for _ in range(6)]
+    lm = np.ones((B, n), np.float32)
+    lm[0, 80:] = 0.0
+    lm[1, [3, 40, 41]] = 0.0
+    gm = np.zeros((B, n), np.float32)
+    gm[0, [0, 5, 79]] = 1.0
+    gm[1, [1, 2, 95]] = 1.0
+    scale = 0.3
+    out = oracle.forward(*arrs, lm, gm, 8, [0, 2], scale=scale)
+    _, _, _, Qg, Kg, Vg = arrs
+    for b in range(B):
+        keymask = np.broadcast_to(lm[b] != 0, (n, n)).copy()
+        ref = _sdpa(Qg[b], Kg[b], Vg[b], scale, mask=keymask[None].repeat(H, 0))
+        for i in np.flatnonzero((gm[b] != 0) & (lm[b] != 0)):
+            assert np.max(np.abs(out[b, :, i] - ref[:, i])) < 1e-12
+
+
+def test_constant_values_and_row_sums():
+    """V = Vg = constant row c -> O = c on every valid row, i.e. sum_j p_ij = 1."""
+    rng = np.random.default_rng(3)
+    B, H, n, d = 2, 3, 70, 8
+    arrs, lm, gm = _random_problem(rng, B, H, n, d, 10, [0, 1, 2], 4, 0.3)
+    c = rng.standard_normal(d).astype(np.float32)
+    arrs[2] = np.broadcast_to(c, (B, H, n, d)).copy()
+    arrs[5] = np.broadcast_to(c, (B, H, n, d)).copy()
+    out = oracle.forward(*arrs, lm, gm, 10, [0, 1, 2], scale=2.0)
+    valid = lm != 0
+    for b in range(B):
+        assert np.max(np.abs(out[b][:, valid[b]] - c)) < 1e-12
+        assert np.all(out[b][:, ~valid[b]] == 0.0)
+    ones = np.ones((B, H, n, d), np.float32)
+    out = oracle.forward(arrs[0], arrs[1], ones, arrs[3], arrs[4], ones, lm, gm, 10, [0, 1, 2],
+                         scale=2.0)
+    assert np.max(np.abs(out[:, :, :, 0][np.broadcast_to(valid[:, None], (B, H, n))] - 1.0)) < 1e-13
+
+
+def test_padded_rows_are_exact_zero_and_poison_is_ignored():
+    rng = np.random.default_rng(5)
+    B, H, n, d = 2, 2, 64, 16
+    arrs, lm, gm = _random_problem(rng, B, H, n, d, 6, [0, 1], 3, 0.3)
+    out = oracle.forward(*arrs, lm, gm, 6, [0, 1], scale=0.5)
+    valid = lm != 0
+    glob = valid & (gm != 0)
+    for b in range(B):
+        assert np.all(out[b][:, ~valid[b]] == 0.0)
+    # poison every row the method never reads with large values
+    Q, K, V, Qg, Kg, Vg = (a.copy() for a in arrs)
+    for b in range(B):
+        pad = ~valid[b]
+        K[b][:, pad] = 1e3
+        V[b][:, pad] = -1e3
+        Kg[b][:, pad] = 1e3
+        Vg[b][:, pad] = 1e3
+        Qg[b][:, ~glob[b]] = 1e3
+        Q[b][:, glob[b] | pad] = -1e3
+    out2 = oracle.forward(Q, K, V, Qg, Kg, Vg, lm, gm, 6, [0, 1], scale=0.5)
+    assert np.array_equal(out, out2)
+
+
+@pytest.mark.parametrize("gap", [1, 2, 3])
+def test_dilation_is_residue_class_decomposition(gap):
+    """No globals, no padding: a head with stride s equals s undilated problems on x[rho::s]."""
+    rng = np.random.default_rng(gap)
+    B, H, n, d = 1, 1, 61, 8
+    window = 6
+    arrs = [rng.standard_normal((B, H, n, d)).astype(np.float32) for _ in range(6)]
+    lm = np.ones((B, n), np.float32)
+    gm = np.zeros((B, n), np.float32)
+    out = oracle.forward(*arrs, lm, gm, window, [gap], scale=0.4)
+    s = gap + 1
+    for rho in range(s):
+        sub = [a[:, :, rho::s].copy() for a in arrs]
+        m = sub[0].shape[2]
+        o = oracle.forward(*sub, np.ones((B, m), np.float32), np.zeros((B, m), np.float32),
+                           window, [0], scale=0.4)
+        assert np.array_equal(o, out[:, :, rho::s])
+
+
+def test_compaction_matches_flatnonzero():
+    rng = np.random.default_rng(9)
+    masks = []
+    for n in (1, 5, 63, 64, 65, 1000, 4097):
+        for B in (1, 3):
+            lm = (rng.random((B, n)) > 0.2).astype(np.float32)
+            gm = (rng.random((B, n)) > 0.9).astype(np.float32)
+            masks.append((lm, gm))
+    masks.append((np.ones((2, 300), np.float32), np.zeros((2, 300), np.float32)))   # none
+    masks.append((np.ones((2, 300), np.float32), np.ones((2, 300), np.float32)))    # all
+    masks.append((np.zeros((2, 300), np.float32), np.ones((2, 300), np.float32)))   # padding wins
+    neg = np.ones((1, 8), np.float32)
+    gneg = np.array([[-0.0, 0.0, 2.0, np.nan, -1.0, 0, 0, 1e-30]], np.float32)
+    masks.append((neg, gneg))
+    for lm, gm in masks:
+        gidx, gcnt = oracle.compact(lm, gm)
+        B, n = lm.shape
+        for b in range(B):
+            want = np.flatnonzero((lm[b] != 0) & (gm[b] != 0))
+            assert gcnt[b] == want.size
+            assert np.array_equal(gidx[b, :want.size], want)
+            assert np.all(gidx[b, want.size:] == -1)
+
+
+def test_pair_counter_matches_oracle_key_sets():
+    """The bench's FLOP model counts exactly the oracle's allowed keys."""
+    rng = np.random.default_rng(21)
+    for n, window, gaps in ((40, 6, [0, 1, 2]), (129, 16, [0, 3]), (17, 100, [0, 2])):
+        _, lm, gm = _random_problem(rng, 2, len(gaps), n, 4, window, gaps, 3, 0.3)
+        want = 0
+        for b in range(2):
+            for gap in gaps:
+                for i in range(n):
+                    want += oracle.allowed(lm[b], gm[b], window, gap, i)[1].size
+        assert flops.pairs(lm, gm, window, gaps) == want
+
+
+def test_full_attention_pair_count_matches_page():
+    """n = 4096 under full attention is "about 16 million" token pairs (4096^2)."""
+    n = 4096
+    lm = np.ones((1, n), np.float32)
+    gm = np.zeros((1, n), np.float32)
+    assert flops.pairs(lm, gm, 2 * n, [0]) == 4096 * 4096 == 16_777_216
+
+
+def test_rows_equal_forward_rows():
+    spec = workloads.custom(2, 3, 300, 64, 40, "bf16", dilation=[0, 1, 2], seed=4, n_global=5,
+                            pad_mode="per_batch", pad_lo=0, pad_hi=50)
+    x = workloads.generate(spec)
+    full = oracle.forward(*x.tensors(), x.lmask, x.gmask, spec.window, spec.dilation, spec.scale)
+    idx = np.random.default_rng(0).choice(2 * 3 * 300, size=200, replace=False)
+    part = oracle.rows(*x.tensors(), x.lmask, x.gmask, spec.window, idx, spec.dilation, spec.scale)
+    assert np.array_equal(part, full.reshape(-1, 64)[idx])

@@ -1,0 +1,149 @@
+/*
+ * lwattn.h -- Longformer self-attention forward (sliding window, per-head
+ * dilation, task-driven global attention) on AMD Instinct MI355X (gfx950).
+ *
+ * What one forward computes, per batch row b, head h and query position i
+ * (the pages' definition; the readings of what they leave open are spelled
+ * out on each argument):
+ *
+ *   valid(j)  = local_attn_mask[b][j] != 0          (0.0 marks padding)
+ *   global(j) = valid(j) && global_attn_mask[b][j] != 0
+ *
+ *   padded row  (!valid(i)) : O[b,h,i,:] = 0 exactly.
+ *   global row  (global(i)) : softmax over every valid key j of
+ *                             scale * <Qg_i, Kg_j>, weights applied to Vg_j.
+ *   local row   (otherwise) : softmax over the window keys
+ *                             { i + k*(dilation[h]+1) : |k| <= window/2,
+ *                               0 <= key < n, valid, not global }
+ *                             together with every global key (each key once)
+ *                             of scale * <Q_i, K_j>, weights applied to V_j.
+ *
+ * Sources:
+ *   "LongFormer: The Long-Document Transformer" notes (coding-zuo.github.io),
+ *   sections "Sliding Window" (w/2 keys each side), "Dilated Sliding Window"
+ *   (gapped taps, per-head dilation) and "Global Attention" (symmetric global
+ *   tokens, separate Qg/Kg/Vg projections, banded Q.K^T).
+ *   FasterTransformer Longformer encoder guide (hnwysp.cn): inputs
+ *   local_attn_mask / global_attn_mask [batch, seq] with 1.0 = attends, the
+ *   [batch, head, seq, dim] multi-head layout, head dim 64, the global-index
+ *   partition (global_idx, global_token_nums), the masked softmax (local rows
+ *   over window + globals, global rows over the whole sequence, padded query
+ *   rows zeroed) and the float / half / bf16 instantiations.
+ *
+ * Conventions for every function: plain C, never throws, never aborts; every
+ * failure is a status code.  Device pointers are HIP device allocations on the
+ * plan's device.  The caller owns every tensor; a plan owns its workspace.
+ */
+#ifndef LWATTN_H_
+#define LWATTN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lwattn_plan_s* lwattn_plan_t;
+
+/* Storage type of Q, K, V, Qg, Kg, Vg and O.  Scores, softmax and the output
+ * accumulation are always float32. */
+typedef enum { LWATTN_F32 = 0, LWATTN_BF16 = 1 } lwattn_dtype;
+
+typedef enum {
+  LWATTN_OK = 0,
+  LWATTN_E_INVALID = 1,           /* bad argument: null/misaligned pointer, bad config */
+  LWATTN_E_UNSUPPORTED = 2,       /* valid but not implemented (d != 64) */
+  LWATTN_E_NOMEM = 3,             /* workspace allocation failed */
+  LWATTN_E_DEVICE = 4,            /* a HIP call failed */
+  LWATTN_E_TOO_MANY_GLOBALS = 5   /* a batch row had more than max_global global tokens */
+} lwattn_status;
+
+typedef struct {
+  int32_t B, H, n, d;     /* batch, heads, sequence length, head dim.  d must be 64
+                             (the FasterTransformer guide states the same limit).
+                             B, H or n equal to 0 is an empty problem: the forward
+                             launches nothing and returns LWATTN_OK. */
+  int32_t window;         /* w >= 0 and even: w/2 taps on each side of the query
+                             ("Sliding Window").  w = 0 keeps the query itself. */
+  const int32_t* dilation;/* host array [H] (copied by lwattn_plan): gap per head,
+                             >= 0; taps are dilation+1 positions apart ("Dilated
+                             Sliding Window").  NULL means 0 for every head. */
+  int32_t max_global;     /* bound on global tokens per batch row (the guide's
+                             max_global_token_num).  Sizes the workspace; more
+                             global tokens in a row is reported by
+                             lwattn_sync_status as LWATTN_E_TOO_MANY_GLOBALS. */
+  float scale;            /* > 0, finite: multiplies every q.k (the guide's
+                             attn_scaler); 1/sqrt(d) for the usual attention. */
+  int32_t dtype;          /* lwattn_dtype */
+} lwattn_config;
+
+/* Validates a configuration without touching any device.  Returns LWATTN_OK,
+ * LWATTN_E_INVALID (null cfg, negative sizes, odd or negative window, negative
+ * dilation, max_global < 0, scale not > 0 and finite, unknown dtype, or
+ * B*H*n*d beyond 2^40 elements, B*n beyond 2^31-1, n beyond 2^28) or
+ * LWATTN_E_UNSUPPORTED (d != 64). */
+lwattn_status lwattn_check_config(const lwattn_config* cfg);
+
+/* Validates cfg, selects HIP device `hip_device`, allocates the plan and its
+ * device workspace (flags and index lists of size B*n, per-row status, and the
+ * split-softmax partials of the global rows, about
+ * B*H*ceil(max_global/32)*nsplit*32*66*4 bytes).  On success *out owns them;
+ * release with lwattn_destroy.  On failure *out is NULL. */
+lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_t* out);
+
+/* Enqueues one forward on `stream` (asynchronous; no allocation, no host sync).
+ *   Q, K, V, Qg, Kg, Vg : device, [B,H,n,d] contiguous, dtype; 16-byte aligned.
+ *                         Only Qg rows at global positions and Q rows at local
+ *                         positions are read.
+ *   local_attn_mask     : device float32 [B,n]; != 0 marks a real token.
+ *   global_attn_mask    : device float32 [B,n]; != 0 marks a global token.
+ *   O                   : device, [B,H,n,d], dtype; every row is written.  Must
+ *                         not overlap any input.
+ * Returns LWATTN_E_INVALID before launching anything if the plan or a pointer
+ * is null or misaligned, LWATTN_E_DEVICE if a launch fails.  Data-dependent
+ * errors (too many global tokens) are reported by lwattn_sync_status; O is
+ * then undefined.  One plan serves one stream at a time. */
+lwattn_status lwattn_forward(lwattn_plan_t plan,
+                             const void* Q, const void* K, const void* V,
+                             const void* Qg, const void* Kg, const void* Vg,
+                             const float* local_attn_mask, const float* global_attn_mask,
+                             void* O, hipStream_t stream);
+
+/* Frees the plan and its workspace.  NULL is a no-op. */
+lwattn_status lwattn_destroy(lwattn_plan_t plan);
+
+/* Copies the global-index lists of the last forward on `stream` (stream-ordered,
+ * asynchronous) into caller-owned device buffers:
+ *   gidx [B,n] int32: ascending global positions of row b, then -1 to the end;
+ *   gcnt [B]   int32: the number of global tokens of row b.
+ * (The FasterTransformer guide's global_idx / global_token_nums.)  Returns
+ * LWATTN_E_INVALID for a null plan or pointer, LWATTN_E_DEVICE if the copy
+ * cannot be enqueued. */
+lwattn_status lwattn_global_index(lwattn_plan_t plan, int32_t* gidx, int32_t* gcnt,
+                                  hipStream_t stream);
+
+/* Synchronizes `stream`, then reports the device-side status of the last
+ * forward: LWATTN_E_TOO_MANY_GLOBALS if any row exceeded max_global, else
+ * LWATTN_OK (or LWATTN_E_DEVICE if a HIP call failed). */
+lwattn_status lwattn_sync_status(lwattn_plan_t plan, hipStream_t stream);
+
+/* Kernel timing for measurement.  While enabled, every forward records HIP
+ * events around each of its kernel launches on its stream (up to `max_calls`
+ * forwards are kept).  lwattn_timing_read synchronizes on the recorded events
+ * and returns, per kernel of the forward, the summed duration in milliseconds
+ * (ms[k] for k < *nkernels, at most `cap`) and the number of recorded forwards.
+ * Kernel order: 0 = global-index compaction, 1 = attention (local and global
+ * rows), 2 = global-row merge. */
+lwattn_status lwattn_timing_enable(lwattn_plan_t plan, int32_t max_calls);
+lwattn_status lwattn_timing_read(lwattn_plan_t plan, float* ms, int32_t cap,
+                                 int32_t* nkernels, int32_t* ncalls);
+lwattn_status lwattn_timing_disable(lwattn_plan_t plan);
+
+/* Static description of a status code. */
+const char* lwattn_strerror(lwattn_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LWATTN_H_ */

@@ -1,0 +1,358 @@
+// lwattn.hip -- host runtime and C ABI of the Longformer window + global
+// attention forward (declared in include/lwattn.h).
+//
+// A plan validates the configuration once, derives the launch geometry and
+// owns the device workspace; a forward only enqueues three kernels on the
+// caller's stream (see kernels.hpp) and never allocates or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kernels.hpp"
+#include "lwattn.h"
+
+namespace {
+
+constexpr int kNumKernels = 3;
+
+// LWATTN_DEBUG=1 in the environment prints every failing HIP call to stderr.
+bool hip_ok(hipError_t e, const char* what) {
+  if (e == hipSuccess) return true;
+  static const bool debug = [] {
+    const char* v = std::getenv("LWATTN_DEBUG");
+    return v && *v && *v != '0';
+  }();
+  if (debug) std::fprintf(stderr, "lwattn: %s failed: %s\n", what, hipGetErrorString(e));
+  return false;
+}
+
+}  // namespace
+
+struct lwattn_plan_s {
+  lwattn_config cfg;
+  std::vector<int32_t> gap;
+  int device = 0;
+  // geometry
+  int nqt = 0, nqg = 0, nsplit = 0, ksplit = 0;
+  int n_glob_wg = 0, n_band_wg = 0, blocks_per_b = 0;
+  size_t smem = 0;
+  // workspace
+  uint8_t* flags = nullptr;
+  int32_t* gidx = nullptr;
+  int32_t* gcnt = nullptr;
+  int32_t* status = nullptr;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  int32_t* head_stride = nullptr;
+  int32_t* head_blk = nullptr;
+  // timing
+  int timing_cap = 0;
+  int timing_calls = 0;
+  std::vector<hipEvent_t> events;   // (kNumKernels + 1) per recorded forward
+};
+
+static void free_plan(lwattn_plan_s* p) {
+  if (!p) return;
+  (void)hipFree(p->flags);
+  (void)hipFree(p->gidx);
+  (void)hipFree(p->gcnt);
+  (void)hipFree(p->status);
+  (void)hipFree(p->part_o);
+  (void)hipFree(p->part_ml);
+  (void)hipFree(p->head_stride);
+  (void)hipFree(p->head_blk);
+  for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
+  delete p;
+}
+
+static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+extern "C" {
+
+const char* lwattn_strerror(lwattn_status s) {
+  switch (s) {
+    case LWATTN_OK: return "ok";
+    case LWATTN_E_INVALID: return "invalid argument";
+    case LWATTN_E_UNSUPPORTED: return "unsupported configuration (head dim must be 64)";
+    case LWATTN_E_NOMEM: return "device workspace allocation failed";
+    case LWATTN_E_DEVICE: return "HIP runtime error";
+    case LWATTN_E_TOO_MANY_GLOBALS: return "a batch row has more global tokens than max_global";
+  }
+  return "unknown status";
+}
+
+lwattn_status lwattn_check_config(const lwattn_config* c) {
+  if (!c) return LWATTN_E_INVALID;
+  if (c->B < 0 || c->H < 0 || c->n < 0 || c->d <= 0) return LWATTN_E_INVALID;
+  if (c->window < 0 || (c->window & 1)) return LWATTN_E_INVALID;
+  if (c->max_global < 0) return LWATTN_E_INVALID;
+  if (!(c->scale > 0.0f) || !std::isfinite(c->scale)) return LWATTN_E_INVALID;
+  if (c->dtype != LWATTN_F32 && c->dtype != LWATTN_BF16) return LWATTN_E_INVALID;
+  if (c->dilation) {
+    for (int h = 0; h < c->H; ++h) {
+      if (c->dilation[h] < 0) return LWATTN_E_INVALID;
+      if ((int64_t)c->dilation[h] + 1 > (int64_t)INT32_MAX / 2) return LWATTN_E_INVALID;
+    }
+  }
+  const int64_t elems = (int64_t)c->B * c->H * c->n * c->d;
+  if (elems > ((int64_t)1 << 40)) return LWATTN_E_INVALID;
+  if ((int64_t)c->B * c->n > ((int64_t)1 << 31) - 1) return LWATTN_E_INVALID;
+  if (c->n > (1 << 28)) return LWATTN_E_INVALID;   // keeps window/tile arithmetic in int32
+  if (c->d != lwk::D) return LWATTN_E_UNSUPPORTED;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_t* out) {
+  if (!out) return LWATTN_E_INVALID;
+  *out = nullptr;
+  lwattn_status st = lwattn_check_config(cfg);
+  if (st != LWATTN_OK) return st;
+  int ndev = 0;
+  if (!hip_ok(hipGetDeviceCount(&ndev), "hipGetDeviceCount") || hip_device < 0 || hip_device >= ndev)
+    return hip_device < 0 ? LWATTN_E_INVALID : LWATTN_E_DEVICE;
+  if (!hip_ok(hipSetDevice(hip_device), "hipSetDevice")) return LWATTN_E_DEVICE;
+
+  lwattn_plan_s* p = new (std::nothrow) lwattn_plan_s();
+  if (!p) return LWATTN_E_NOMEM;
+  p->cfg = *cfg;
+  p->device = hip_device;
+  const int B = cfg->B, H = cfg->H, n = cfg->n;
+  p->gap.assign(H, 0);
+  if (cfg->dilation)
+    for (int h = 0; h < H; ++h) p->gap[h] = cfg->dilation[h];
+  p->cfg.dilation = nullptr;   // the plan keeps its own copy
+
+  // band geometry: per head, sum over residue classes of ceil(n_rho / 128)
+  std::vector<int32_t> stride(H), blk(H + 1, 0);
+  for (int h = 0; h < H; ++h) {
+    const int s = p->gap[h] + 1;
+    stride[h] = s;
+    int64_t nb = 0;
+    for (int rho = 0; rho < s && rho < n; ++rho) {
+      const int64_t nr = ((int64_t)n - rho + s - 1) / s;
+      nb += (nr + lwk::ROWS_WG - 1) / lwk::ROWS_WG;
+    }
+    blk[h + 1] = blk[h] + (int32_t)nb;
+  }
+  p->blocks_per_b = blk[H];
+  const int64_t nband = (int64_t)B * blk[H];
+  // global-row geometry
+  p->nqt = ceil_div(cfg->max_global, 32);
+  p->nqg = ceil_div(p->nqt, lwk::NW);
+  int64_t nglob = 0;
+  if (p->nqt > 0 && n > 0 && B > 0 && H > 0) {
+    const int64_t units = (int64_t)B * H * p->nqg;
+    int64_t want = (512 + units - 1) / units;
+    const int64_t maxs = (n + 127) / 128;
+    if (want > maxs) want = maxs;
+    if (want < 1) want = 1;
+    p->ksplit = ceil_div(ceil_div(n, want), 32) * 32;
+    p->nsplit = ceil_div(n, p->ksplit);
+    nglob = units * p->nsplit;
+  }
+  const int64_t nglob_pad = (nglob + 7) / 8 * 8;
+  if (nband + nglob_pad > INT32_MAX) {
+    free_plan(p);
+    return LWATTN_E_INVALID;
+  }
+  p->n_band_wg = (int)nband;
+  p->n_glob_wg = (int)nglob_pad;
+  p->smem = (cfg->dtype == LWATTN_BF16 ? lwk::SlotLay<true>::BYTES : lwk::SlotLay<false>::BYTES) * 2;
+
+  // workspace
+  const size_t bn = (size_t)B * n;
+  bool ok = true;
+  auto alloc = [&](void** ptr, size_t bytes) {
+    if (!ok) return;
+    if (bytes == 0) bytes = 16;
+    if (!hip_ok(hipMalloc(ptr, bytes), "hipMalloc")) { ok = false; *ptr = nullptr; }
+  };
+  alloc((void**)&p->flags, bn);
+  alloc((void**)&p->gidx, bn * 4);
+  alloc((void**)&p->gcnt, (size_t)B * 4);
+  alloc((void**)&p->status, (size_t)B * 4);
+  const size_t nparts = (size_t)B * H * p->nqt * (p->nsplit > 0 ? p->nsplit : 0) * 32;
+  alloc((void**)&p->part_o, nparts * lwk::D * 4);
+  alloc((void**)&p->part_ml, nparts * 2 * 4);
+  alloc((void**)&p->head_stride, (size_t)H * 4);
+  alloc((void**)&p->head_blk, (size_t)(H + 1) * 4);
+  if (!ok) {
+    free_plan(p);
+    return LWATTN_E_NOMEM;
+  }
+  if ((H > 0 && !hip_ok(hipMemcpy(p->head_stride, stride.data(), (size_t)H * 4, hipMemcpyHostToDevice), "hipMemcpy")) ||
+      !hip_ok(hipMemcpy(p->head_blk, blk.data(), (size_t)(H + 1) * 4, hipMemcpyHostToDevice), "hipMemcpy") ||
+      (B > 0 && !hip_ok(hipMemset(p->status, 0, (size_t)B * 4), "hipMemset")) ||
+      (B > 0 && !hip_ok(hipMemset(p->gcnt, 0, (size_t)B * 4), "hipMemset"))) {
+    free_plan(p);
+    return LWATTN_E_DEVICE;
+  }
+  *out = p;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_destroy(lwattn_plan_t p) {
+  if (!p) return LWATTN_OK;
+  (void)hipSetDevice(p->device);
+  free_plan(p);
+  return LWATTN_OK;
+}
+
+static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, const void* V,
+                             const void* Qg, const void* Kg, const void* Vg,
+                             const float* lmask, const float* gmask, void* O, hipStream_t stream) {
+  if (!p) return LWATTN_E_INVALID;
+  const lwattn_config& c = p->cfg;
+  if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
+  const void* ptrs[] = {Q, K, V, Qg, Kg, Vg, O};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return LWATTN_E_INVALID;
+  if (!lmask || !gmask || ((uintptr_t)lmask & 3u) || ((uintptr_t)gmask & 3u)) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+
+  lwk::Params prm;
+  prm.Q = (const uint8_t*)Q;
+  prm.K = (const uint8_t*)K;
+  prm.V = (const uint8_t*)V;
+  prm.Qg = (const uint8_t*)Qg;
+  prm.Kg = (const uint8_t*)Kg;
+  prm.Vg = (const uint8_t*)Vg;
+  prm.O = (uint8_t*)O;
+  prm.lmask = lmask;
+  prm.gmask = gmask;
+  prm.flags = p->flags;
+  prm.gidx = p->gidx;
+  prm.gcnt = p->gcnt;
+  prm.status = p->status;
+  prm.part_o = p->part_o;
+  prm.part_ml = p->part_ml;
+  prm.head_stride = p->head_stride;
+  prm.head_blk = p->head_blk;
+  prm.B = c.B;
+  prm.H = c.H;
+  prm.n = c.n;
+  prm.r = (int)std::min<int64_t>(c.window / 2, c.n);
+  prm.max_global = c.max_global;
+  prm.nqt = p->nqt;
+  prm.nqg = p->nqg;
+  prm.nsplit = p->nsplit;
+  prm.ksplit = p->ksplit;
+  prm.n_glob_wg = p->n_glob_wg;
+  prm.n_band_wg = p->n_band_wg;
+  prm.blocks_per_b = p->blocks_per_b;
+  prm.c = c.scale * 1.4426950408889634f;
+
+  const bool timed = p->timing_cap > 0 && p->timing_calls < p->timing_cap;
+  hipEvent_t* ev = timed ? &p->events[(size_t)p->timing_calls * (kNumKernels + 1)] : nullptr;
+  if (timed && !hip_ok(hipEventRecord(ev[0], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
+
+  hipLaunchKernelGGL(lwk::compact_kernel, dim3(c.B), dim3(lwk::CT), 0, stream, prm);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  if (timed && !hip_ok(hipEventRecord(ev[1], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
+
+  const int grid = p->n_glob_wg + p->n_band_wg;
+  if (c.dtype == LWATTN_BF16)
+    hipLaunchKernelGGL(lwk::attn_kernel<true>, dim3(grid), dim3(lwk::NT), p->smem, stream, prm);
+  else
+    hipLaunchKernelGGL(lwk::attn_kernel<false>, dim3(grid), dim3(lwk::NT), p->smem, stream, prm);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  if (timed && !hip_ok(hipEventRecord(ev[2], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
+
+  if (p->nqt > 0) {
+    const int mgrid = c.B * c.H * p->nqt;
+    if (c.dtype == LWATTN_BF16)
+      hipLaunchKernelGGL(lwk::merge_kernel<true>, dim3(mgrid), dim3(256), 0, stream, prm);
+    else
+      hipLaunchKernelGGL(lwk::merge_kernel<false>, dim3(mgrid), dim3(256), 0, stream, prm);
+    if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  }
+  if (timed) {
+    if (!hip_ok(hipEventRecord(ev[3], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
+    ++p->timing_calls;
+  }
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_global_index(lwattn_plan_t p, int32_t* gidx, int32_t* gcnt, hipStream_t stream) {
+  if (!p || !gidx || !gcnt) return LWATTN_E_INVALID;
+  const size_t B = (size_t)p->cfg.B, n = (size_t)p->cfg.n;
+  if (B == 0) return LWATTN_OK;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  if (n > 0 && !hip_ok(hipMemcpyAsync(gidx, p->gidx, B * n * 4, hipMemcpyDeviceToDevice, stream), "hipMemcpyAsync"))
+    return LWATTN_E_DEVICE;
+  if (!hip_ok(hipMemcpyAsync(gcnt, p->gcnt, B * 4, hipMemcpyDeviceToDevice, stream), "hipMemcpyAsync"))
+    return LWATTN_E_DEVICE;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_sync_status(lwattn_plan_t p, hipStream_t stream) {
+  if (!p) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  if (!hip_ok(hipStreamSynchronize(stream), "hipStreamSynchronize")) return LWATTN_E_DEVICE;
+  const int B = p->cfg.B;
+  if (B == 0) return LWATTN_OK;
+  std::vector<int32_t> st(B);
+  if (!hip_ok(hipMemcpy(st.data(), p->status, (size_t)B * 4, hipMemcpyDeviceToHost), "hipMemcpy"))
+    return LWATTN_E_DEVICE;
+  for (int b = 0; b < B; ++b)
+    if (st[b]) return LWATTN_E_TOO_MANY_GLOBALS;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_timing_enable(lwattn_plan_t p, int32_t max_calls) {
+  if (!p || max_calls <= 0) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
+  p->events.clear();
+  p->timing_cap = 0;
+  p->timing_calls = 0;
+  const size_t ne = (size_t)max_calls * (kNumKernels + 1);
+  p->events.reserve(ne);
+  for (size_t i = 0; i < ne; ++i) {
+    hipEvent_t e;
+    if (!hip_ok(hipEventCreate(&e), "hipEventCreate")) return LWATTN_E_DEVICE;
+    p->events.push_back(e);
+  }
+  p->timing_cap = max_calls;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_timing_read(lwattn_plan_t p, float* ms, int32_t cap, int32_t* nkernels,
+                                 int32_t* ncalls) {
+  if (!p || !nkernels || !ncalls || (cap > 0 && !ms)) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  float tot[kNumKernels] = {0.f, 0.f, 0.f};
+  for (int call = 0; call < p->timing_calls; ++call) {
+    hipEvent_t* ev = &p->events[(size_t)call * (kNumKernels + 1)];
+    if (!hip_ok(hipEventSynchronize(ev[kNumKernels]), "hipEventSynchronize")) return LWATTN_E_DEVICE;
+    for (int k = 0; k < kNumKernels; ++k) {
+      float t = 0.f;
+      if (!hip_ok(hipEventElapsedTime(&t, ev[k], ev[k + 1]), "hipEventElapsedTime")) return LWATTN_E_DEVICE;
+      tot[k] += t;
+    }
+  }
+  for (int k = 0; k < kNumKernels && k < cap; ++k) ms[k] = tot[k];
+  *nkernels = kNumKernels;
+  *ncalls = p->timing_calls;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_timing_disable(lwattn_plan_t p) {
+  if (!p) return LWATTN_E_INVALID;
+  (void)hipSetDevice(p->device);
+  for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
+  p->events.clear();
+  p->timing_cap = 0;
+  p->timing_calls = 0;
+  return LWATTN_OK;
+}
+
+}  // extern "C"

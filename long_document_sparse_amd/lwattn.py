@@ -1,0 +1,209 @@
+"""Thin ctypes binding of the C ABI in include/lwattn.h.
+
+Argument marshalling only: every step of the forward runs in the HIP kernels of
+liblwattn.so.  Torch provides device memory and the current stream.  If the
+library is missing, every entry point raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblwattn.so")
+
+LWATTN_F32, LWATTN_BF16 = 0, 1
+OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_DEVICE, E_TOO_MANY_GLOBALS = range(6)
+KERNELS = ("compact", "attention", "merge")
+
+# (name, restype, argtypes) of every exported function, in header order
+_c_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("B", _i32), ("H", _i32), ("n", _i32), ("d", _i32),
+        ("window", _i32),
+        ("dilation", ctypes.POINTER(_i32)),
+        ("max_global", _i32),
+        ("scale", ctypes.c_float),
+        ("dtype", _i32),
+    ]
+
+
+SIGNATURES = [
+    ("lwattn_check_config", ctypes.c_int, [ctypes.POINTER(Config)]),
+    ("lwattn_plan", ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_int, ctypes.POINTER(_c_p)]),
+    ("lwattn_forward", ctypes.c_int, [_c_p] * 9 + [_c_p, _c_p]),
+    ("lwattn_destroy", ctypes.c_int, [_c_p]),
+    ("lwattn_global_index", ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
+    ("lwattn_sync_status", ctypes.c_int, [_c_p, _c_p]),
+    ("lwattn_timing_enable", ctypes.c_int, [_c_p, _i32]),
+    ("lwattn_timing_read", ctypes.c_int, [_c_p, ctypes.POINTER(ctypes.c_float), _i32,
+                                          ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    ("lwattn_timing_disable", ctypes.c_int, [_c_p]),
+    ("lwattn_strerror", ctypes.c_char_p, [ctypes.c_int]),
+]
+
+_lib = None
+
+
+class LwattnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        # Bind to the HIP runtime torch already carries: both export the SONAME
+        # libamdhip64.so.7, so loading torch first makes the dynamic linker reuse
+        # its copy instead of mapping a second runtime into the process.
+        import torch  # noqa: F401
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"HIP library {path} is not built; run `python -m long_document_sparse_amd.build` "
+                "(hipcc --offload-arch=gfx950) first")
+        lib = ctypes.CDLL(path)
+        for name, res, args in SIGNATURES:
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return load_library().lwattn_strerror(int(status)).decode()
+
+
+def make_config(B: int, H: int, n: int, d: int = 64, window: int = 512,
+                dilation: Optional[Sequence[int]] = None, max_global: int = 64,
+                scale: Optional[float] = None, dtype: str = "bf16"):
+    """Returns (Config, keepalive) -- the dilation array must outlive the call."""
+    dil = None
+    ptr = None
+    if dilation is not None:
+        dil = (_i32 * len(dilation))(*[int(x) for x in dilation])
+        ptr = ctypes.cast(dil, ctypes.POINTER(_i32))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d) if d > 0 else 1.0
+    code = {"bf16": LWATTN_BF16, "f32": LWATTN_F32}.get(dtype, 99) if isinstance(dtype, str) else int(dtype)
+    return Config(B, H, n, d, window, ptr, max_global, scale, code), dil
+
+
+def check_config(**kw) -> int:
+    cfg, keep = make_config(**kw)
+    return load_library().lwattn_check_config(ctypes.byref(cfg))
+
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class Plan:
+    """One configuration: lwattn_plan on construction, lwattn_destroy on close()."""
+
+    def __init__(self, B: int, H: int, n: int, d: int = 64, window: int = 512,
+                 dilation: Optional[Sequence[int]] = None, max_global: int = 64,
+                 scale: Optional[float] = None, dtype: str = "bf16", device: int = 0):
+        self.lib = load_library()
+        self.shape = (B, H, n, d)
+        self.dtype = dtype
+        self.device = device
+        cfg, keep = make_config(B, H, n, d, window, dilation, max_global, scale, dtype)
+        self.cfg = cfg
+        handle = ctypes.c_void_p()
+        st = self.lib.lwattn_plan(ctypes.byref(cfg), device, ctypes.byref(handle))
+        if st != OK:
+            raise LwattnError(st, "lwattn_plan")
+        self.handle = handle
+        del keep
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.lwattn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, t, name, dtype):
+        import torch
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a device tensor")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def forward(self, q, k, v, qg, kg, vg, lmask, gmask, out=None, stream=None):
+        """Enqueue one forward; returns O (allocated if `out` is None)."""
+        import torch
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        for t, name in ((q, "q"), (k, "k"), (v, "v"), (qg, "qg"), (kg, "kg"), (vg, "vg")):
+            self._check(t, name, tdt)
+            if tuple(t.shape) != self.shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {self.shape}")
+        B, H, n, d = self.shape
+        for t, name in ((lmask, "local_attn_mask"), (gmask, "global_attn_mask")):
+            self._check(t, name, torch.float32)
+            if tuple(t.shape) != (B, n):
+                raise ValueError(f"{name} must be [B,n]")
+        if out is None:
+            out = torch.empty(self.shape, dtype=tdt, device=q.device)
+        else:
+            self._check(out, "out", tdt)
+            if tuple(out.shape) != self.shape:
+                raise ValueError("out has the wrong shape")
+        st = self.lib.lwattn_forward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     qg.data_ptr(), kg.data_ptr(), vg.data_ptr(),
+                                     lmask.data_ptr(), gmask.data_ptr(), out.data_ptr(),
+                                     _stream_handle(stream))
+        if st != OK:
+            raise LwattnError(st, "lwattn_forward")
+        return out
+
+    __call__ = forward
+
+    def global_index(self, stream=None):
+        """(gidx [B,n] int32, gcnt [B] int32) of the last forward, as device tensors."""
+        import torch
+        B, H, n, d = self.shape
+        dev = torch.device("cuda", self.device)
+        gidx = torch.empty((B, n), dtype=torch.int32, device=dev)
+        gcnt = torch.empty((B,), dtype=torch.int32, device=dev)
+        st = self.lib.lwattn_global_index(self.handle, gidx.data_ptr(), gcnt.data_ptr(),
+                                          _stream_handle(stream))
+        if st != OK:
+            raise LwattnError(st, "lwattn_global_index")
+        return gidx, gcnt
+
+    def sync_status(self, stream=None) -> int:
+        return int(self.lib.lwattn_sync_status(self.handle, _stream_handle(stream)))
+
+    def timing_enable(self, max_calls: int):
+        st = self.lib.lwattn_timing_enable(self.handle, int(max_calls))
+        if st != OK:
+            raise LwattnError(st, "lwattn_timing_enable")
+
+    def timing_read(self):
+        """({kernel: total ms}, calls) over the forwards recorded since timing_enable."""
+        ms = (ctypes.c_float * 8)()
+        nk, nc = _i32(), _i32()
+        st = self.lib.lwattn_timing_read(self.handle, ms, 8, ctypes.byref(nk), ctypes.byref(nc))
+        if st != OK:
+            raise LwattnError(st, "lwattn_timing_read")
+        return {KERNELS[i]: float(ms[i]) for i in range(nk.value)}, int(nc.value)
+
+    def timing_disable(self):
+        self.lib.lwattn_timing_disable(self.handle)

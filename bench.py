@@ -1,0 +1,171 @@
+#!/usr/bin/env python3
+"""Benchmark of the Longformer window + global attention forward on one MI355X.
+
+One step = one lwattn_forward (global-index compaction, band + global-row
+attention, global-row merge) over one batch of seeded synthetic input that is
+already resident in device memory.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload base]
+                  [--no-cpu-baseline]
+
+The default workload is "base": B=1, H=12, n=4096, d=64, w=512 (+-256), no
+dilation, one global token at position 0, bf16 storage, fp32 accumulation.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "window+global attn fwd tokens/s & TFLOP/s (% bf16 MFMA peak), n=4096 w=512"
+
+
+def describe(spec):
+    glob = (f"{spec.n_global} global tokens " +
+            ("at the start" if spec.global_mode == "first" else "at random positions"))
+    pad = {"none": "no padding",
+           "per_batch": f"padded tail U{{{spec.pad_lo}..{spec.pad_hi}}} per sequence",
+           "one_seq": f"one sequence with a padded tail U{{{spec.pad_lo}..{spec.pad_hi}}}"}[spec.pad_mode]
+    dil = sorted(set(spec.dilation))
+    return (f"{spec.name}: B={spec.B} H={spec.H} n={spec.n} d={spec.d} w={spec.window} "
+            f"dilation {dil} {spec.dtype}; {glob}; {pad}")
+
+
+def cpu_baseline(x, budget_s=12.0):
+    """The oracle, as it is, on the host cores: a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    spec = x.spec
+    threads = oracle.default_threads()
+    n, H, B = spec.n, spec.H, spec.B
+    total_heads = B * H
+
+    def run_heads(k):
+        rows = np.arange(k * n, dtype=np.int64)       # all rows of the first k (b, h) pairs
+        t0 = time.perf_counter()
+        oracle.rows(*x.tensors(), x.lmask, x.gmask, spec.window, rows, spec.dilation,
+                    spec.scale, threads=threads)
+        return time.perf_counter() - t0
+
+    t1 = run_heads(1)
+    k = int(max(1, min(total_heads, budget_s / max(t1, 1e-6))))
+    if k > 1:
+        t = run_heads(k)
+    else:
+        t = t1
+    t_full = t * total_heads / k
+    return {
+        "value": round(B * n / t_full, 3),
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"every query row of {k} of the {total_heads} (batch, head) pairs "
+                   f"({k * n} rows, {t:.2f} s), scaled to the full workload"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="base")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-timing", action="store_true",
+                    help="do not record per-kernel HIP events (roofline fields become null)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over (batch, head) with no communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_document_sparse_amd import flops as fl
+    from long_document_sparse_amd import lwattn, workloads
+
+    spec = workloads.named(args.workload)
+    x = workloads.generate(spec)
+    dev = torch.device("cuda", 0)
+    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    ts = [torch.from_numpy(a).to(dev).to(tdt) for a in x.tensors()]
+    lm = torch.from_numpy(x.lmask).to(dev)
+    gm = torch.from_numpy(x.gmask).to(dev)
+    out = torch.empty_like(ts[0])
+    plan = lwattn.Plan(spec.B, spec.H, spec.n, spec.d, spec.window, spec.dilation,
+                       spec.max_global, spec.scale, spec.dtype)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        plan(*ts, lm, gm, out=out)
+    st = plan.sync_status()
+    if st != lwattn.OK:
+        raise SystemExit(f"forward failed: {lwattn.strerror(st)}")
+
+    if not args.no_timing:
+        plan.timing_enable(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        plan(*ts, lm, gm, out=out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = plan.sync_status()
+    if st != lwattn.OK:
+        raise SystemExit(f"forward failed: {lwattn.strerror(st)}")
+
+    ms_step = elapsed * 1e3 / args.steps
+    tokens = spec.B * spec.n
+    value = tokens / (elapsed / args.steps)
+    flop = fl.flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
+    nbytes = fl.hbm_bytes(x.lmask, x.gmask, spec.H, spec.d, 2 if spec.dtype == "bf16" else 4)
+    peak = PEAK_TFLOPS[spec.dtype]
+
+    roofline = None
+    kernels = None
+    if not args.no_timing:
+        tot, calls = plan.timing_read()
+        kernels = {k: round(v * 1e3 / calls, 3) for k, v in tot.items()}   # us per launch
+        t_attn = tot["attention"] / calls * 1e-3                            # s per launch
+        achieved = flop / t_attn / 1e12
+        roofline = {"bound": "mfma", "kernel": "attn_kernel", "achieved": round(achieved, 2),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": None,
+                    "algorithmic_flop": flop, "algorithmic_bytes": nbytes,
+                    "hbm_view_GBs": round(nbytes / t_attn / 1e9, 1)}
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded, N(0,1)/sqrt(d) inputs; no dataset)",
+        "config": {"workload": describe(spec), "global_batch": spec.B, "seq_len": spec.n,
+                   "heads": spec.H, "head_dim": spec.d, "window": spec.window,
+                   "parallelism": "single GPU"},
+        "tflops_per_s": round(flop / (elapsed / args.steps) / 1e12, 2),
+        "pct_mfma_peak": round(100 * flop / (elapsed / args.steps) / 1e12 / peak, 2),
+        "kernel_us": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(x)
+    plan.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -81,7 +81,7 @@ typedef struct {
 /* Validates a configuration without touching any device.  Returns LWATTN_OK,
  * LWATTN_E_INVALID (null cfg, negative sizes, odd or negative window, negative
  * dilation, max_global < 0, scale not > 0 and finite, unknown dtype, or
- * B*H*n*d beyond 2^40 elements, B*n beyond 2^31-1, n beyond 2^28) or
+ * B*H*n*d beyond 2^40 elements, B*n beyond 2^31-1, n beyond 2^23) or
  * LWATTN_E_UNSUPPORTED (d != 64). */
 lwattn_status lwattn_check_config(const lwattn_config* cfg);
 

@@ -30,6 +30,13 @@
 // are per-lane reductions plus one exchange with lane l^32.  The probabilities
 // stay in registers and are the B operand of O^T += V^T * P^T; V is stored
 // transposed in LDS so that each lane reads runs of 4 keys at one d.
+//
+// Staging.  Every thread of a workgroup loads one 16-byte chunk of K and of V
+// per tile (two for float32) into registers two tiles ahead of its use and
+// writes them to one of two LDS slots one step ahead, so a global load has two
+// compute steps to arrive.  Key positions are computed, not loaded; the
+// padding flag of a key is loaded beside its K/V chunk and padded keys are
+// zeroed on the way into LDS.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,6 +50,7 @@ constexpr int KT = 32;         // keys per tile
 constexpr int NW = 4;          // waves per workgroup
 constexpr int NT = 64 * NW;    // threads per workgroup
 constexpr int ROWS_WG = 32 * NW;
+constexpr int MAXH_ARG = 32;   // per-head tables passed by value up to this many heads
 constexpr float TAU = 8.0f;    // lazy-rescale threshold, log2 units
 constexpr float M_INIT = -1e30f;
 
@@ -60,16 +68,22 @@ struct Params {
   int32_t* gidx;           // [B][n]
   int32_t* gcnt;           // [B]
   int32_t* status;         // [B]: 1 if the row has more than max_global globals
+  int32_t* vlen;           // [B]: number of real tokens if they form a prefix, else -1
   float* part_o;           // [B][H][nqt][nsplit][32][64]
   float* part_ml;          // [B][H][nqt][nsplit][32][2]
-  const int32_t* head_stride;  // [H]: dilation gap + 1
+  const int32_t* head_stride;  // [H]: dilation gap + 1 (device copy, any H)
   const int32_t* head_blk;     // [H+1]: prefix of band workgroups per batch row
   int32_t B, H, n, r;      // r = min(window/2, n)
   int32_t max_global, nqt, nqg, nsplit, ksplit;
   int32_t n_glob_wg;       // padded to a multiple of 8
   int32_t n_band_wg;
   int32_t blocks_per_b;    // head_blk[H]
+  int32_t mask_vec;        // masks 16-byte aligned and n % 4 == 0
+  int32_t uni_stride;      // > 0: every head has this stride
+  int32_t blocks_per_head; // band workgroups of one head when uni_stride > 0
   float c;                 // scale * log2(e)
+  int32_t hs[MAXH_ARG];    // head_stride by value when H <= MAXH_ARG
+  int32_t hb[MAXH_ARG + 1];
 };
 
 // ---------------------------------------------------------------------------
@@ -99,78 +113,89 @@ struct SlotLay {
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = Lay<BF>::KBYTES;
   static constexpr int POS_OFF = V_OFF + Lay<BF>::VBYTES;
-  static constexpr int OK_OFF = POS_OFF + KT * 4;
-  static constexpr int CLEAN_OFF = OK_OFF + KT;
-  static constexpr int BYTES = (CLEAN_OFF + 4 + 15) / 16 * 16;
-  static constexpr int NCH = KT * Lay<BF>::CH / NT;   // chunks per thread per array
+  static constexpr int OK_OFF = POS_OFF + KT * 4;      // uint32: bit k = key k usable
+  static constexpr int BYTES = (OK_OFF + 4 + 15) / 16 * 16;
+  static constexpr int NCH = KT * Lay<BF>::CH / NT;    // chunks per thread per array
 };
 
-// Which keys a tile holds.
-enum TileMode { TM_BAND = 0, TM_GCOL = 1, TM_SLICE = 2 };
+// Which keys a tile holds.  Positions are computed for every key, clamped to
+// an existing row, so that every global load of the staging path is issued
+// unconditionally (no divergent branch around a load); keys that do not exist
+// or are padding are zeroed on the way into LDS.
 struct TileDesc {
-  int mode;
-  int j0;      // first key: subsequence index (band), list index (gcol), position (slice)
-  int jend;    // one past the last usable j (band: nr, gcol: g, slice: slice end)
+  int list;    // 0: position = base + jj*stride;  1: position = gl[jj] (global-index list)
+  int j0;      // index of the tile's first key (subsequence index, or list index)
+  int jend;    // one past the last existing key index (>= 1 whenever the tile is used)
+  int base, stride;
 };
 
 struct Ctx {
-  const uint8_t* fl;       // flags of the batch row
-  const int32_t* gi;       // gidx of the batch row
-  int rho, s;              // residue class and stride (band)
+  const uint8_t* fl;       // flags of the batch row (global memory)
+  const int32_t* gl;       // global positions of the batch row (LDS copy or global memory)
+  int rho, s;              // residue class and stride of the band
 };
 
-__device__ __forceinline__ void key_pos(const TileDesc& td, const Ctx& cx, int k, int& pos, bool& ok) {
+__device__ __forceinline__ void key_pos(const TileDesc& td, const Ctx& cx, int k, int& pos, bool& in) {
   const int jj = td.j0 + k;
-  if (td.mode == TM_GCOL) {
-    ok = jj < td.jend;
-    pos = ok ? cx.gi[jj] : 0;
-  } else if (td.mode == TM_BAND) {
-    ok = jj >= 0 && jj < td.jend;
-    pos = ok ? cx.rho + jj * cx.s : 0;
-    ok = ok && (cx.fl[pos] & 1);
-  } else {
-    ok = jj < td.jend;
-    pos = ok ? jj : 0;
-    ok = ok && (cx.fl[pos] & 1);
-  }
+  in = (jj >= 0) & (jj < td.jend);
+  const int jc = min(max(jj, 0), td.jend - 1);
+  if (td.list)
+    pos = cx.gl[jc];
+  else
+    pos = td.base + jc * td.stride;
 }
 
 template <bool BF>
 struct Stage {
   static constexpr int NCH = SlotLay<BF>::NCH;
   uint4 kr[NCH], vr[NCH];
-  int pos;
-  bool ok;
+  bool in[NCH];     // the chunk's key exists
+  uint8_t fl[NCH];  // raw flag byte of that key (bit0: real token), inspected at store time
+  int pos;          // position of key tid % KT
+  bool okin;        // key tid % KT exists
+  uint8_t okfl;     // its raw flag byte
+  bool list;        // keys come from the global-index list (always real tokens)
 };
 
-// Issue the global loads of one tile into registers.
+// Issue the global loads of one tile into registers.  Nothing here consumes a
+// loaded value, and no load sits under a divergent branch, so the compiler
+// need not wait for them before the next tile's compute.
 template <bool BF>
 __device__ __forceinline__ void stage_load(Stage<BF>& st, const TileDesc& td, const Ctx& cx,
                                            const uint8_t* kbase, const uint8_t* vbase) {
   constexpr int CH = Lay<BF>::CH;
   constexpr int RB = D * Lay<BF>::ELT;
   const int tid = threadIdx.x;
+  st.list = td.list != 0;
 #pragma unroll
   for (int e = 0; e < Stage<BF>::NCH; ++e) {
     const int q = tid + NT * e;
     const int kt = q / CH, ch = q % CH;
     int pos;
-    bool ok;
-    key_pos(td, cx, kt, pos, ok);
-    if (ok) {
-      st.kr[e] = *reinterpret_cast<const uint4*>(kbase + (int64_t)pos * RB + ch * 16);
-      st.vr[e] = *reinterpret_cast<const uint4*>(vbase + (int64_t)pos * RB + ch * 16);
-    } else {
-      st.kr[e] = make_uint4(0, 0, 0, 0);
-      st.vr[e] = make_uint4(0, 0, 0, 0);
-    }
+    bool in;
+    key_pos(td, cx, kt, pos, in);
+    st.in[e] = in;
+    st.kr[e] = *reinterpret_cast<const uint4*>(kbase + (int64_t)pos * RB + ch * 16);
+    st.vr[e] = *reinterpret_cast<const uint4*>(vbase + (int64_t)pos * RB + ch * 16);
+    st.fl[e] = cx.fl[pos];
   }
-  if (tid < KT) key_pos(td, cx, tid, st.pos, st.ok);
+  int pos;
+  bool in;
+  key_pos(td, cx, tid & (KT - 1), pos, in);
+  st.pos = pos;
+  st.okin = in;
+  st.okfl = cx.fl[pos];
 }
 
-// Write the staged registers into an LDS slot (V transposed for bf16).
+// Sentinel window index of a global key outside the row's residue class.
+constexpr int JREL_NONE = -(1 << 30);
+
+// Write the staged registers into an LDS slot (V transposed for bf16).  For a
+// global-column tile the slot also gets, per key, its index in the band's
+// residue subsequence (or JREL_NONE), used to drop keys already in the window.
 template <bool BF>
-__device__ __forceinline__ void stage_store(const Stage<BF>& st, uint8_t* slot) {
+__device__ __forceinline__ void stage_store(const Stage<BF>& st, uint8_t* slot, const TileDesc& td,
+                                            const Ctx& cx) {
   using SL = SlotLay<BF>;
   constexpr int CH = Lay<BF>::CH;
   const int tid = threadIdx.x;
@@ -178,26 +203,76 @@ __device__ __forceinline__ void stage_store(const Stage<BF>& st, uint8_t* slot) 
   for (int e = 0; e < Stage<BF>::NCH; ++e) {
     const int q = tid + NT * e;
     const int kt = q / CH, ch = q % CH;
-    *reinterpret_cast<uint4*>(slot + SL::K_OFF + kt * Lay<BF>::KROW + ch * 16) = st.kr[e];
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    const bool use = st.in[e] && (st.list || (st.fl[e] & 1));
+    const uint4 kv = use ? st.kr[e] : z;
+    const uint4 vv = use ? st.vr[e] : z;
+    *reinterpret_cast<uint4*>(slot + SL::K_OFF + kt * Lay<BF>::KROW + ch * 16) = kv;
     if constexpr (BF) {
-      const uint32_t w[4] = {st.vr[e].x, st.vr[e].y, st.vr[e].z, st.vr[e].w};
+      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const uint16_t hv = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
         *reinterpret_cast<uint16_t*>(slot + SL::V_OFF + (ch * 8 + t) * Lay<BF>::VROW + kt * 2) = hv;
       }
     } else {
-      *reinterpret_cast<uint4*>(slot + SL::V_OFF + kt * Lay<BF>::VROW + ch * 16) = st.vr[e];
+      *reinterpret_cast<uint4*>(slot + SL::V_OFF + kt * Lay<BF>::VROW + ch * 16) = vv;
     }
   }
   if (tid < 64) {
-    const bool ok = tid < KT ? st.ok : true;
-    const uint64_t all = __ballot(ok);
-    if (tid < KT) {
-      reinterpret_cast<int32_t*>(slot + SL::POS_OFF)[tid] = st.pos;
-      slot[SL::OK_OFF + tid] = ok ? 1 : 0;
+    const uint64_t bits = __ballot(tid < KT && st.okin && (st.list || (st.okfl & 1)));
+    if (tid < KT && td.list) {
+      const int dp = st.pos - cx.rho;
+      const int jrel = (dp >= 0 && dp % cx.s == 0) ? dp / cx.s : JREL_NONE;
+      reinterpret_cast<int32_t*>(slot + SL::POS_OFF)[tid] = jrel;
     }
-    if (tid == 0) *reinterpret_cast<int32_t*>(slot + SL::CLEAN_OFF) = (all == ~0ull) ? 1 : 0;
+    if (tid == 0) *reinterpret_cast<uint32_t*>(slot + SL::OK_OFF) = (uint32_t)bits;
+  }
+}
+
+// Runs `comp(u, slot)` for tiles u = 0..U-1.  bf16: two-deep register
+// prefetch (loads issued two steps before their LDS store); float32, whose
+// MFMA work per tile is 8x longer, keeps one register set.  `pre()` runs once
+// after the first loads are issued and before the first barrier.  Every thread
+// of the workgroup must call it with the same U >= 1.
+template <bool BF, class DescFn, class CompFn, class PreFn>
+__device__ __forceinline__ void tile_pipeline(int U, DescFn desc, CompFn comp, PreFn pre,
+                                              const Ctx& cx, const uint8_t* kbase,
+                                              const uint8_t* vbase, uint8_t* smem) {
+  using SL = SlotLay<BF>;
+  uint8_t* slot0 = smem;
+  uint8_t* slot1 = smem + SL::BYTES;
+  if constexpr (BF) {
+    Stage<BF> s0, s1;
+    stage_load<BF>(s0, desc(0), cx, kbase, vbase);
+    if (U > 1) stage_load<BF>(s1, desc(1), cx, kbase, vbase);
+    pre();
+    stage_store<BF>(s0, slot0, desc(0), cx);
+    __syncthreads();
+    for (int u = 0; u < U; u += 2) {
+      if (u + 2 < U) stage_load<BF>(s0, desc(u + 2), cx, kbase, vbase);
+      comp(u, slot0);
+      if (u + 1 < U) stage_store<BF>(s1, slot1, desc(u + 1), cx);
+      __syncthreads();
+      if (u + 1 >= U) break;
+      if (u + 3 < U) stage_load<BF>(s1, desc(u + 3), cx, kbase, vbase);
+      comp(u + 1, slot1);
+      if (u + 2 < U) stage_store<BF>(s0, slot0, desc(u + 2), cx);
+      __syncthreads();
+    }
+  } else {
+    Stage<BF> st;
+    stage_load<BF>(st, desc(0), cx, kbase, vbase);
+    pre();
+    stage_store<BF>(st, slot0, desc(0), cx);
+    __syncthreads();
+    for (int u = 0; u < U; ++u) {
+      const bool more = u + 1 < U;
+      if (more) stage_load<BF>(st, desc(u + 1), cx, kbase, vbase);
+      comp(u, (u & 1) ? slot1 : slot0);
+      if (more) stage_store<BF>(st, (u & 1) ? slot0 : slot1, desc(u + 1), cx);
+      __syncthreads();
+    }
   }
 }
 
@@ -210,12 +285,9 @@ struct QOp<true> {
   __device__ void load(const uint8_t* row, bool ok, int h) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      if (ok) {
-        uint4 v = *reinterpret_cast<const uint4*>(row + (32 * h + 8 * c) * 2);
-        q[c] = __builtin_bit_cast(bf16x8, v);
-      } else {
-        q[c] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-      }
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (ok) v = *reinterpret_cast<const uint4*>(row + (32 * h + 8 * c) * 2);
+      q[c] = __builtin_bit_cast(bf16x8, v);
     }
   }
 };
@@ -225,8 +297,8 @@ struct QOp<false> {
   __device__ void load(const uint8_t* row, bool ok, int h) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      float4 v = ok ? *reinterpret_cast<const float4*>(row + (32 * h + 4 * c) * 4)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ok) v = *reinterpret_cast<const float4*>(row + (32 * h + 4 * c) * 4);
       q[4 * c + 0] = v.x;
       q[4 * c + 1] = v.y;
       q[4 * c + 2] = v.z;
@@ -303,6 +375,19 @@ __device__ __forceinline__ int key_of(int r, int lane) {
   return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
+// Maximum of x over lanes l and l^32 (the two lanes holding one query row).
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second; with both operands x, the two results hold x of
+// both halves, and x itself is kept in the max.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(x, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 struct Softmax {
   float m, l;          // running max (log2 units, lazy) and this lane's partial sum
   f32x16 o[2];         // O^T accumulators: d = 32*db + 8*(r/4) + 4*(lane/32) + r%4
@@ -312,12 +397,14 @@ struct Softmax {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { o[0][r] = 0.f; o[1][r] = 0.f; }
   }
-  // s: masked scores (excluded = -inf); returns probabilities in p.
+  // s: masked scores (excluded = -inf); returns probabilities in p.  The max
+  // is only raised when some row's scores exceed it by more than 2^TAU, so the
+  // O rescale is rare; every probability stays below 2^TAU.
   __device__ __forceinline__ void update(const f32x16& s, float c, float (&p)[16]) {
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = half_max(mx);
     const float mnew = fmaxf(m, mx * c);
     if (__any(mnew > m + TAU)) {
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -338,72 +425,141 @@ struct Softmax {
 
 // ---------------------------------------------------------------------------
 // Kernel 1: flags + global-index compaction, one workgroup per batch row.
+// Each thread takes 4 consecutive positions per pass (one float4 of each
+// mask); a wave's 256 positions are counted with 4 ballots.
 constexpr int CT = 1024;
+constexpr int CPT = 4;
+// exclusive prefix over the wave of a per-lane count in [0, 7], and the wave total
+__device__ __forceinline__ void wave_count(int mine, int lane, int& before, int& total) {
+  before = 0;
+  total = 0;
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit) {
+    const uint64_t bal = __ballot((mine >> bit) & 1);
+    before += __popcll(bal & ((1ull << lane) - 1ull)) << bit;
+    total += __popcll(bal) << bit;
+  }
+}
 __global__ __launch_bounds__(CT) void compact_kernel(Params p) {
   __shared__ int wsum[CT / 64];
+  __shared__ int vsum[CT / 64];
+  __shared__ int first_pad;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = p.n;
   const float* lm = p.lmask + (int64_t)b * n;
   const float* gm = p.gmask + (int64_t)b * n;
   uint8_t* fl = p.flags + (int64_t)b * n;
   int32_t* gi = p.gidx + (int64_t)b * n;
-  int carry = 0;
-  for (int base = 0; base < n; base += CT) {
-    const int j = base + tid;
-    bool v = false, g = false;
-    if (j < n) {
-      v = lm[j] != 0.0f;
-      g = v && (gm[j] != 0.0f);
-      fl[j] = (uint8_t)((v ? 1 : 0) | (g ? 2 : 0));
+  if (tid == 0) first_pad = n;
+  __syncthreads();
+  int carry = 0, nvalid = 0;
+  const bool vec = p.mask_vec != 0;   // masks 16-byte aligned and n % 4 == 0
+  for (int base = 0; base < n; base += CT * CPT) {
+    const int j0 = base + tid * CPT;
+    float lv[CPT], gv[CPT];
+    if (vec && j0 + CPT <= n) {
+      const float4 a = *reinterpret_cast<const float4*>(lm + j0);
+      const float4 c = *reinterpret_cast<const float4*>(gm + j0);
+      lv[0] = a.x; lv[1] = a.y; lv[2] = a.z; lv[3] = a.w;
+      gv[0] = c.x; gv[1] = c.y; gv[2] = c.z; gv[3] = c.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        lv[e] = (j0 + e < n) ? lm[j0 + e] : 0.0f;
+        gv[e] = (j0 + e < n) ? gm[j0 + e] : 0.0f;
+      }
     }
-    const uint64_t bal = __ballot(g);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(bal);
+    bool g[CPT];
+    uint32_t packed = 0;
+    int mine = 0, myvalid = 0, mypad = n;
+#pragma unroll
+    for (int e = CPT - 1; e >= 0; --e) {
+      const bool v = lv[e] != 0.0f;
+      g[e] = v && (gv[e] != 0.0f);
+      packed |= (uint32_t)((v ? 1 : 0) | (g[e] ? 2 : 0)) << (8 * e);
+      mine += g[e] ? 1 : 0;
+      myvalid += v ? 1 : 0;
+      if (!v && j0 + e < n) mypad = j0 + e;
+    }
+    if ((n % 4) == 0 && j0 + CPT <= n) {
+      *reinterpret_cast<uint32_t*>(fl + j0) = packed;   // 4-byte aligned: b*n and j0 are multiples of 4
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e)
+        if (j0 + e < n) fl[j0 + e] = (uint8_t)(packed >> (8 * e));
+    }
+    if (mypad < n) atomicMin(&first_pad, mypad);
+    int before, wtot, vb, vtot;
+    wave_count(mine, lane, before, wtot);
+    wave_count(myvalid, lane, vb, vtot);
+    if (lane == 0) {
+      wsum[wave] = wtot;
+      vsum[wave] = vtot;
+    }
     __syncthreads();
-    int wpre = 0, tot = 0;
+    int wpre = 0, tot = 0, vt = 0;
 #pragma unroll
     for (int w = 0; w < CT / 64; ++w) {
       const int c = wsum[w];
       wpre += (w < wave) ? c : 0;
       tot += c;
+      vt += vsum[w];
     }
-    if (g) gi[carry + wpre + before] = j;
+    int k = carry + wpre + before;
+#pragma unroll
+    for (int e = 0; e < CPT; ++e)
+      if (g[e]) gi[k++] = j0 + e;
     carry += tot;
+    nvalid += vt;
     __syncthreads();
   }
   for (int k = carry + tid; k < n; k += CT) gi[k] = -1;
   if (tid == 0) {
     p.gcnt[b] = carry;
     p.status[b] = carry > p.max_global ? 1 : 0;
+    p.vlen[b] = (first_pad == nvalid) ? nvalid : -1;   // real tokens form the prefix [0, nvalid)
   }
 }
 
 // ---------------------------------------------------------------------------
 // Kernel 2: attention.
+// mask_kind: 0 none, 1 window tile (key usable and |i - j| <= r),
+//            2 global columns (usable and not already in the row's window),
+//            3 key usable only.  Every mask is a select, never a branch.
 template <bool BF>
 __device__ __forceinline__ void process_tile(const QOp<BF>& qo, Softmax& sm, const uint8_t* slot,
                                              int lane, float c, int mask_kind, int my_i, int band_j0,
-                                             int r, int rho, int s) {
+                                             int r) {
   using SL = SlotLay<BF>;
   f32x16 sc = qk_tile(qo, slot, lane);
   if (mask_kind != 0) {
-    const uint8_t* okv = slot + SL::OK_OFF;
-    const int32_t* posv = reinterpret_cast<const int32_t*>(slot + SL::POS_OFF);
+    const uint32_t okb = *reinterpret_cast<const uint32_t*>(slot + SL::OK_OFF);
+    const int h = lane >> 5;
+    if (mask_kind == 2) {
+      const int4* jr = reinterpret_cast<const int4*>(slot + SL::POS_OFF);
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int k = key_of(rr, lane);
-      bool allowed = okv[k] != 0;
-      if (mask_kind == 1) {            // window tile: |i - j| <= r
-        const int dj = my_i - (band_j0 + k);
-        allowed = allowed && dj <= r && dj >= -r;
-      } else if (mask_kind == 2) {     // global columns: skip the ones already in the window
-        const int dp = posv[k] - rho;
-        if (dp >= 0 && dp % s == 0) {
-          const int dj = my_i - dp / s;
-          allowed = allowed && !(dj <= r && dj >= -r);
+      for (int a = 0; a < 4; ++a) {
+        const int4 v = jr[2 * a + h];          // keys 8a + 4h .. 8a + 4h + 3
+        const int jv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int k = 8 * a + 4 * h + e;
+          const int dj = my_i - jv[e];
+          const bool allowed = ((okb >> k) & 1u) && !(dj <= r && dj >= -r);
+          sc[4 * a + e] = allowed ? sc[4 * a + e] : -INFINITY;
         }
       }
-      if (!allowed) sc[rr] = -INFINITY;
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int k = key_of(rr, lane);
+        bool allowed = (okb >> k) & 1u;
+        if (mask_kind == 1) {
+          const int dj = my_i - (band_j0 + k);
+          allowed = allowed && dj <= r && dj >= -r;
+        }
+        sc[rr] = allowed ? sc[rr] : -INFINITY;
+      }
     }
   }
   float pr[16];
@@ -422,17 +578,19 @@ __device__ __forceinline__ void store_row4(uint8_t* dst, const float* v) {
   }
 }
 
+// Number of global positions a band workgroup keeps in LDS; global columns
+// beyond it are read from the global-index list directly (second pass).
+constexpr int GL_MAX = 512;
+
 template <bool BF>
-__device__ void band_wg(const Params& p, int lb, uint8_t* smem) {
+constexpr int smem_bytes_general() { return 2 * SlotLay<BF>::BYTES + GL_MAX * 4; }
+
+template <bool BF>
+__device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t* smem) {
   using SL = SlotLay<BF>;
   constexpr int RB = D * Lay<BF>::ELT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h32 = lane >> 5, qi = lane & 31;
-  const int b = lb / p.blocks_per_b;
-  int rem = lb - b * p.blocks_per_b;
-  int h = 0;
-  while (p.head_blk[h + 1] <= rem) ++h;
-  int local = rem - p.head_blk[h];
-  const int s = p.head_stride[h];
+  const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = p.n;
   int rho = 0, nr = 0;
   for (rho = 0; rho < s; ++rho) {
@@ -443,78 +601,104 @@ __device__ void band_wg(const Params& p, int lb, uint8_t* smem) {
   }
   const int R0 = local * ROWS_WG;
   const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
+  const int32_t* gidx_b = p.gidx + (int64_t)b * n;
+  int32_t* gl_lds = reinterpret_cast<int32_t*>(smem + 2 * SL::BYTES);
   Ctx cx;
   cx.fl = p.flags + (int64_t)b * n;
-  cx.gi = p.gidx + (int64_t)b * n;
+  cx.gl = gl_lds;
   cx.rho = rho;
   cx.s = s;
 
-  const int my_i = R0 + 32 * wave + qi;
-  const bool row_in = my_i < nr;
-  const int my_pos = rho + (row_in ? my_i : 0) * s;
-  const uint8_t my_fl = row_in ? cx.fl[my_pos] : 0;
-  const bool wave_work = __any((my_fl & 3) == 1);
-
-  QOp<BF> qo;
-  qo.load(p.Q + (head + my_pos) * RB, row_in && ((my_fl & 3) == 1), h32);
-  Softmax sm;
-  sm.init();
-
-  int g = p.gcnt[b];
-  if (g > p.max_global) g = p.max_global;
-  const int ngt = (g + KT - 1) / KT;
   const int r = p.r;
   const int kb = R0 - r;
   const int T = (31 + 2 * r) / 32 + 1;
   const int t_lo = (-kb - 31 > 0) ? (-kb - 31 + 31) / 32 : 0;
   int t_hi = (nr - 1 - kb) / 32;
   if (t_hi > NW - 1 + T - 1) t_hi = NW - 1 + T - 1;
-  const int U = ngt + (t_hi - t_lo + 1);
+  const int nband = t_hi - t_lo + 1;
+  int g = p.gcnt[b];
+  if (g > p.max_global) g = p.max_global;
+  const int gmain = g < GL_MAX ? g : GL_MAX;
+  const int ngt = (gmain + KT - 1) / KT;
+  const int U = nband + ngt;
 
-  const uint8_t* kbase = p.K + head * RB;
-  const uint8_t* vbase = p.V + head * RB;
+  const int my_i = R0 + 32 * wave + qi;
+  const bool row_in = my_i < nr;
+  const int my_pos = rho + (row_in ? my_i : 0) * s;
+  const uint8_t my_fl = cx.fl[my_pos];
+  QOp<BF> qo;
+  qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
+  Softmax sm;
+  sm.init();
+  const bool wave_work = __any(row_in && (my_fl & 3) == 1);
+
   auto desc = [&](int u) {
     TileDesc td;
-    if (u < ngt) {
-      td.mode = TM_GCOL;
-      td.j0 = u * KT;
-      td.jend = g;
-    } else {
-      td.mode = TM_BAND;
-      td.j0 = kb + (t_lo + u - ngt) * KT;
+    if (u < nband) {
+      td.list = 0;
+      td.j0 = kb + (t_lo + u) * KT;
       td.jend = nr;
+      td.base = rho;
+      td.stride = s;
+    } else {
+      td.list = 1;
+      td.j0 = (u - nband) * KT;
+      td.jend = gmain;
+      td.base = 0;
+      td.stride = 0;
     }
     return td;
   };
-
-  Stage<BF> st;
-  stage_load<BF>(st, desc(0), cx, kbase, vbase);
-  stage_store<BF>(st, smem);
-  __syncthreads();
-  for (int u = 0; u < U; ++u) {
-    const bool more = u + 1 < U;
-    if (more) stage_load<BF>(st, desc(u + 1), cx, kbase, vbase);
-    const uint8_t* slot = smem + (u & 1) * SL::BYTES;
-    if (wave_work) {
-      if (u < ngt) {
-        process_tile<BF>(qo, sm, slot, lane, p.c, 2, my_i, 0, r, rho, s);
-      } else {
-        const int t = t_lo + (u - ngt);
-        const int up = t - wave;
-        if (up >= 0 && up < T) {
-          const int clean = *reinterpret_cast<const int32_t*>(slot + SL::CLEAN_OFF);
-          const bool diag = (up == 0) || (32 * up + 31 > 2 * r);
-          process_tile<BF>(qo, sm, slot, lane, p.c, (diag || !clean) ? 1 : 0, my_i, kb + t * KT, r,
-                           rho, s);
-        }
+  auto comp = [&](int u, const uint8_t* slot) {
+    if (!wave_work) return;
+    if (u < nband) {
+      const int t = t_lo + u;
+      const int up = t - wave;
+      if (up >= 0 && up < T) {
+        const uint32_t okb = *reinterpret_cast<const uint32_t*>(slot + SL::OK_OFF);
+        const bool diag = (up == 0) || (32 * up + 31 > 2 * r);
+        process_tile<BF>(qo, sm, slot, lane, p.c, (diag || okb != 0xFFFFFFFFu) ? 1 : 0, my_i,
+                         kb + t * KT, r);
       }
+    } else {
+      process_tile<BF>(qo, sm, slot, lane, p.c, 2, my_i, 0, r);
     }
-    if (more) stage_store<BF>(st, smem + ((u + 1) & 1) * SL::BYTES);
+  };
+  auto fill_gl = [&]() {
+    for (int j = tid; j < gmain; j += NT) gl_lds[j] = gidx_b[j];
+  };
+  auto nothing = []() {};
+  const uint8_t* kbase = p.K + head * RB;
+  const uint8_t* vbase = p.V + head * RB;
+  if (nband >= 2 || ngt == 0) {
+    tile_pipeline<BF>(U, desc, comp, fill_gl, cx, kbase, vbase, smem);
+  } else {
+    fill_gl();
     __syncthreads();
+    tile_pipeline<BF>(U, desc, comp, nothing, cx, kbase, vbase, smem);
+  }
+  if (g > GL_MAX) {
+    // global columns past the LDS copy: positions straight from the list
+    Ctx cx2 = cx;
+    cx2.gl = gidx_b + GL_MAX;
+    const int U2 = (g - GL_MAX + KT - 1) / KT;
+    auto desc2 = [&](int u) {
+      TileDesc td;
+      td.list = 1;
+      td.j0 = u * KT;
+      td.jend = g - GL_MAX;
+      td.base = 0;
+      td.stride = 0;
+      return td;
+    };
+    auto comp2 = [&](int u, const uint8_t* slot) {
+      if (wave_work) process_tile<BF>(qo, sm, slot, lane, p.c, 2, my_i, 0, r);
+    };
+    tile_pipeline<BF>(U2, desc2, comp2, nothing, cx2, kbase, vbase, smem);
   }
 
   // normalise and store this lane's half of its query row (global rows are
-  // written by the merge kernel)
+  // written by the merge kernel, padded rows get exact zeros)
   const float lt = sm.l + __shfl_xor(sm.l, 32);
   if (row_in && (my_fl & 2) == 0) {
     const bool valid = (my_fl & 1) != 0;
@@ -534,16 +718,10 @@ __device__ void band_wg(const Params& p, int lb, uint8_t* smem) {
 }
 
 template <bool BF>
-__device__ void global_wg(const Params& p, int lg, uint8_t* smem) {
-  using SL = SlotLay<BF>;
+__device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t* smem) {
   constexpr int RB = D * Lay<BF>::ELT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h32 = lane >> 5, qi = lane & 31;
-  const int sp = lg % p.nsplit;
-  int t = lg / p.nsplit;
-  const int qg = t % p.nqg;
-  t /= p.nqg;
-  const int h = t % p.H;
-  const int b = t / p.H;
+  const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   int g = p.gcnt[b];
   if (g > p.max_global) g = p.max_global;
   const int nqt_b = (g + 31) / 32;
@@ -552,17 +730,18 @@ __device__ void global_wg(const Params& p, int lg, uint8_t* smem) {
   const bool wave_work = qt < nqt_b;
   const int n = p.n;
   const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
+  const int32_t* gidx_b = p.gidx + (int64_t)b * n;
   Ctx cx;
   cx.fl = p.flags + (int64_t)b * n;
-  cx.gi = p.gidx + (int64_t)b * n;
+  cx.gl = gidx_b;
   cx.rho = 0;
   cx.s = 1;
 
   const int qidx = qt * 32 + qi;
   const bool qok = wave_work && qidx < g;
-  const int qpos = qok ? cx.gi[qidx] : 0;
+  const int qpos = gidx_b[qok ? qidx : 0];
   QOp<BF> qo;
-  qo.load(p.Qg + (head + qpos) * RB, qok, h32);
+  qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
   Softmax sm;
   sm.init();
 
@@ -570,32 +749,23 @@ __device__ void global_wg(const Params& p, int lg, uint8_t* smem) {
   int j_end = j_start + p.ksplit;
   if (j_end > n) j_end = n;
   const int U = (j_end - j_start + KT - 1) / KT;
-  const uint8_t* kbase = p.Kg + head * RB;
-  const uint8_t* vbase = p.Vg + head * RB;
   auto desc = [&](int u) {
     TileDesc td;
-    td.mode = TM_SLICE;
+    td.list = 0;
     td.j0 = j_start + u * KT;
     td.jend = j_end;
+    td.base = 0;
+    td.stride = 1;
     return td;
   };
-  if (U > 0) {
-    Stage<BF> st;
-    stage_load<BF>(st, desc(0), cx, kbase, vbase);
-    stage_store<BF>(st, smem);
-    __syncthreads();
-    for (int u = 0; u < U; ++u) {
-      const bool more = u + 1 < U;
-      if (more) stage_load<BF>(st, desc(u + 1), cx, kbase, vbase);
-      const uint8_t* slot = smem + (u & 1) * SL::BYTES;
-      if (wave_work) {
-        const int clean = *reinterpret_cast<const int32_t*>(slot + SL::CLEAN_OFF);
-        process_tile<BF>(qo, sm, slot, lane, p.c, clean ? 0 : 3, 0, 0, 0, 0, 1);
-      }
-      if (more) stage_store<BF>(st, smem + ((u + 1) & 1) * SL::BYTES);
-      __syncthreads();
-    }
-  }
+  auto comp = [&](int u, const uint8_t* slot) {
+    if (!wave_work) return;
+    const uint32_t okb = *reinterpret_cast<const uint32_t*>(slot + SlotLay<BF>::OK_OFF);
+    process_tile<BF>(qo, sm, slot, lane, p.c, okb == 0xFFFFFFFFu ? 0 : 3, 0, 0, 0);
+  };
+  auto nothing = []() {};
+  tile_pipeline<BF>(U, desc, comp, nothing, cx, p.Kg + head * RB, p.Vg + head * RB, smem);
+
   const float lt = sm.l + __shfl_xor(sm.l, 32);
   if (qok) {
     const int64_t pidx = ((((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp) * 32 + qi;
@@ -613,6 +783,516 @@ __device__ void global_wg(const Params& p, int lg, uint8_t* smem) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fast path for bf16 storage and batch rows whose real tokens are a prefix
+// [0, nv) (no padding, or a padded tail): the common case.
+//
+// Keys are fetched with buffer loads whose range is the nv real rows of the
+// (batch, head), so the hardware returns zeros for every key before the start,
+// past the end or in the padded tail -- no clamping, no flag loads, no zeroing
+// selects.  Validity of the 32 keys of a tile is then pure scalar arithmetic.
+// K and V tiles are stored row-major (128 B rows) with 16-byte chunks XOR-
+// swizzled per row: thread t writes physical chunk t (conflict-free b128
+// stores).  The QK^T A operand is a b128 read per lane; the PV A operand
+// (V^T, four consecutive keys at one d per lane) comes from ds_read_b64_tr_b16:
+// within a 16-lane group, source lane 4e+q reads V[k0+e][d0+4q .. +3] and
+// output lane i receives V[k0+e][d0+i] for e = 0..3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+constexpr int FK_OFF = 0;                       // K tile, 32 x 128 B
+constexpr int FV_OFF = 4096;                    // V tile, 32 x 128 B
+constexpr int FSLOT = 8192;
+constexpr int F_DIST = 4;                       // tiles u+2 .. u+F_DIST are in flight during step u
+constexpr int F_NSLOT = F_DIST + 1;             // LDS ring: tiles u .. u+F_DIST
+constexpr int F_GL_OFF = F_NSLOT * FSLOT;       // int32[GL_MAX]: global positions
+constexpr int F_JR_OFF = F_GL_OFF + GL_MAX * 4; // int32[GL_MAX]: their window index (or JREL_NONE)
+constexpr int F_SMEM = F_JR_OFF + GL_MAX * 4;
+constexpr int OOB_OFF = 0x7FFFFF00;             // a buffer offset past any range
+
+__device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+struct FStage {
+  uint4 k, v;
+};
+
+// Per-lane LDS byte offsets used by the compute of every tile.
+struct FLane {
+  int k[4];   // K row lane%32, logical chunk 4*(lane/32) + c
+  int v[2];   // transpose-read source address for d block db (c2 / key-block offsets are immediates)
+  __device__ void init(int lane) {
+    const int row = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k[c] = FK_OFF + row * 128 + (((4 * h + c) ^ swz_k(row)) * 16);
+    const int g1 = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int chunk = (4 * db + 2 * g1 + (q >> 1)) ^ (2 * e);   // row & 3 == e for every row read
+      v[db] = FV_OFF + (4 * h + e) * 128 + chunk * 16 + (q & 1) * 8;
+    }
+  }
+};
+
+__device__ __forceinline__ f32x16 fqk(const QOp<true>& qo, const uint8_t* slot, const FLane& fl) {
+  f32x16 s = {};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + fl.k[c]);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qo.q[c], s, 0, 0, 0);
+  }
+  return s;
+}
+
+__device__ __forceinline__ s16x4 tr_read(const uint8_t* addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(addr));
+}
+
+__device__ __forceinline__ void fpv(f32x16 (&o)[2], const bf16x8 (&pb)[2], const uint8_t* slot,
+                                    const FLane& fl) {
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const s16x4 lo = tr_read(slot + fl.v[db] + c2 * 2048);          // keys 16c2 + 4h + e
+      const s16x4 hi = tr_read(slot + fl.v[db] + c2 * 2048 + 1024);   // keys 16c2 + 8 + 4h + e
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[c2], o[db],
+                                                      0, 0, 0);
+    }
+  }
+}
+
+// Bits [lo, hi) of a 32-bit word (empty when hi <= lo).
+__device__ __forceinline__ uint32_t bit_range(int lo, int hi) {
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > 32 ? 32 : hi;
+  if (hi <= lo) return 0u;
+  const uint32_t upto_hi = hi >= 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u);
+  return upto_hi & ~((1u << lo) - 1u);
+}
+
+// What one wave does with tile u (wave-uniform).
+struct FTile {
+  bool act;        // this wave computes on the tile
+  int kind;        // 0 no mask, 1 window tile, 2 global columns, 3 usable keys only
+  uint32_t okb;    // usable keys
+  int j0;          // band: subsequence index of key 0; global columns: list index of key 0
+};
+
+// Bits [lo, hi) of a 32-bit word, per lane.
+__device__ __forceinline__ uint32_t bit_range_v(int lo, int hi) {
+  lo = min(max(lo, 0), 32);
+  hi = min(max(hi, 0), 32);
+  const uint64_t m = ((1ull << hi) - 1ull) & ~((1ull << lo) - 1ull);
+  return (uint32_t)m;
+}
+
+// This lane's allowed keys of a masked tile (bit k = key k).
+__device__ __forceinline__ uint32_t lane_mask(const FTile& ti, int my_i, int r, const int32_t* jr,
+                                              int lane) {
+  if (ti.kind == 1) return ti.okb & bit_range_v(my_i - r - ti.j0, my_i + r - ti.j0 + 1);
+  if (ti.kind == 2) {
+    // drop the global keys that already sit in this row's window (only this
+    // lane's 16 keys matter: 8a + 4h + e)
+    const int h = lane >> 5;
+    uint32_t m = ti.okb;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int4 v = *reinterpret_cast<const int4*>(jr + 8 * a + 4 * h);
+      const int jv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int dj = my_i - jv[e];
+        const uint32_t inwin = (uint32_t)(dj <= r && dj >= -r);
+        m &= ~(inwin << (8 * a + 4 * h + e));
+      }
+    }
+    return m;
+  }
+  return ti.okb;
+}
+
+// Excluded scores become -inf: one bit extract and one bit-select per score.
+__device__ __forceinline__ void apply_mask(f32x16& sc, uint32_t m, int lane) {
+  const uint32_t m4 = m >> (4 * (lane >> 5));
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int bit = 8 * a + e;
+      const uint32_t keep = (uint32_t)((int32_t)(m4 << (31 - bit)) >> 31);
+      const uint32_t x = __float_as_uint(sc[4 * a + e]);
+      sc[4 * a + e] = __uint_as_float((x & keep) | (0xFF800000u & ~keep));
+    }
+  }
+}
+
+// Online-softmax update of one tile; the probabilities come out as bf16 and
+// the row sum is taken over those rounded values (the ones PV multiplies).
+__device__ __forceinline__ void softmax_bf16(Softmax& sm, const f32x16& s, float c, bf16x8 (&pb)[2]) {
+  float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+  mx = half_max(mx);
+  const float mnew = fmaxf(sm.m, mx * c);
+  if (__any(mnew > sm.m + TAU)) {
+    const float alpha = __builtin_amdgcn_exp2f(sm.m - mnew);
+    sm.l *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sm.o[0][r] *= alpha; sm.o[1][r] *= alpha; }
+    sm.m = mnew;
+  }
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc = sm.l;
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      bf16x2 pp;
+      pp[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e], c, -sm.m));
+      pp[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e + 1], c, -sm.m));
+      pb[c2][e] = pp[0];
+      pb[c2][e + 1] = pp[1];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+    }
+  }
+  sm.l = acc;
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource: base, stride 0, num_records = bytes; out-of-range loads
+// return zeros.
+__device__ __forceinline__ i32x4 make_desc(const void* base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 d;
+  d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  d[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);
+  d[2] = __builtin_amdgcn_readfirstlane(bytes);
+  d[3] = 0x00020000;
+  return d;
+}
+
+// One 16-byte buffer load per lane straight into LDS: lane l writes
+// lds_base + 16*l.  Written as inline asm so that the compiler does not wait
+// for it before every LDS read; the pipeline below waits explicitly.  The
+// instruction has no register destination.
+__device__ __forceinline__ void dma16(i32x4 desc, int voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(desc), "s"(lds_base)
+      : "memory", "m0");
+}
+// Wait until at most 2*c of this wave's loads are outstanding.
+__device__ __forceinline__ void wait_tiles(int c) {
+  if (c <= 0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (c == 1)
+    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
+
+// Software-pipelined tile loop.  Tile t goes, by buffer-to-LDS loads, into
+// LDS slot t % F_NSLOT, issued F_DIST steps ahead of its first use (the ring
+// has F_DIST + 1 slots).  Step u issues the QK^T MFMAs of tile u+1 first, runs
+// the softmax of tile u on the VALU while they execute, then the PV MFMAs of
+// tile u; before the barrier it waits for tile u+2, which step u+1 reads.  The
+// loop is unrolled by two so the score registers alternate without copies.
+template <class InfoFn, class OffFn, class PreFn>
+__device__ __forceinline__ void fpipe(int U, bool wave_work, InfoFn info, OffFn offs, PreFn pre,
+                                      i32x4 dk, i32x4 dv, const QOp<true>& qo, Softmax& sm,
+                                      const FLane& fl, int lane, float c, int my_i, int r,
+                                      const int32_t* jr, uint8_t* smem) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t lds0 =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + wave * 1024;
+  auto slot = [&](int u) { return smem + (u % F_NSLOT) * FSLOT; };
+  auto issue = [&](int u) {
+    int ok, ov;
+    offs(u, ok, ov);
+    const uint32_t base = lds0 + (u % F_NSLOT) * FSLOT;
+    dma16(dk, ok, base + FK_OFF);
+    dma16(dv, ov, base + FV_OFF);
+  };
+  const int last0 = U - 1 < F_DIST ? U - 1 : F_DIST;
+  for (int v = 0; v <= last0; ++v) issue(v);
+  pre();
+  wait_tiles(last0 - 1);           // tiles 0 and 1 have landed
+  __syncthreads();
+  FTile cur = info(0);
+  f32x16 S0, S1;
+  if (wave_work && cur.act) S0 = fqk(qo, slot(0), fl);
+  auto step = [&](int u, f32x16& Sin, f32x16& Sout) {
+    if (u >= 1 && u + F_DIST < U) issue(u + F_DIST);
+    FTile nxt;
+    nxt.act = false;
+    nxt.kind = 0;
+    nxt.okb = 0;
+    nxt.j0 = 0;
+    if (u + 1 < U) nxt = info(u + 1);
+    if (wave_work && nxt.act) Sout = fqk(qo, slot(u + 1), fl);
+    if (wave_work && cur.act) {
+      if (cur.kind != 0)
+        apply_mask(Sin, lane_mask(cur, my_i, r, jr + (cur.kind == 2 ? cur.j0 : 0), lane), lane);
+      bf16x8 pb[2];
+      softmax_bf16(sm, Sin, c, pb);
+      fpv(sm.o, pb, slot(u), fl);
+    }
+    const int last = U - 1 < u + F_DIST ? U - 1 : u + F_DIST;
+    wait_tiles(last - (u + 2));
+    __syncthreads();
+    cur = nxt;
+  };
+  for (int u = 0; u < U; u += 2) {
+    step(u, S0, S1);
+    if (u + 1 >= U) break;
+    step(u + 1, S1, S0);
+  }
+}
+
+__device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, int nv,
+                             uint8_t* smem) {
+  constexpr int RB = 128;
+  const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int n = p.n;
+  int rho = 0, nr = 0;
+  for (rho = 0; rho < s; ++rho) {
+    nr = (n - rho + s - 1) / s;
+    const int nb = (nr + ROWS_WG - 1) / ROWS_WG;
+    if (local < nb) break;
+    local -= nb;
+  }
+  const int R0 = local * ROWS_WG;
+  const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
+  const int nrv = nv > rho ? (nv - rho + s - 1) / s : 0;   // subsequence keys that are real tokens
+
+  const int r = p.r;
+  const int kb = R0 - r;
+  const int T = (31 + 2 * r) / 32 + 1;
+  const int t_lo = (-kb - 31 > 0) ? (-kb - 31 + 31) / 32 : 0;
+  int t_hi = (nr - 1 - kb) / 32;
+  if (t_hi > NW - 1 + T - 1) t_hi = NW - 1 + T - 1;
+  const int nband = t_hi - t_lo + 1;
+  int g = p.gcnt[b];
+  if (g > p.max_global) g = p.max_global;
+  const int gmain = g < GL_MAX ? g : GL_MAX;
+  const int ngt = (gmain + KT - 1) / KT;
+  const int U = nband + ngt;
+
+  const int my_i = R0 + 32 * wave + qi;
+  const bool row_in = my_i < nr;
+  const int my_pos = rho + (row_in ? my_i : 0) * s;
+  const uint8_t my_fl = p.flags[(int64_t)b * n + my_pos];
+  QOp<true> qo;
+  qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
+  Softmax sm;
+  sm.init();
+  FLane fl;
+  fl.init(lane);
+  const bool wave_work = __any(row_in && (my_fl & 3) == 1);
+
+  int32_t* gl = reinterpret_cast<int32_t*>(smem + F_GL_OFF);
+  int32_t* jr = reinterpret_cast<int32_t*>(smem + F_JR_OFF);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * RB, nv * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * RB, nv * RB);
+  const i32x4 dk = make_desc(p.K + head * RB, nv * RB);
+  const i32x4 dv = make_desc(p.V + head * RB, nv * RB);
+  const int srow = tid >> 3, pc = tid & 7;
+  const int ck16 = (pc ^ swz_k(srow)) * 16, cv16 = (pc ^ swz_v(srow)) * 16;
+  const int band_off0 = (rho + (kb + t_lo * KT + srow) * s) * RB;
+  const int band_step = KT * s * RB;
+  auto offs = [&](int u, int& ok, int& ov) {
+    int rowoff;
+    if (u < nband) {
+      rowoff = band_off0 + u * band_step;
+      ok = rowoff + ck16;
+      ov = rowoff + cv16;
+    } else {
+      const int idx = (u - nband) * KT + srow;
+      const bool in = idx < gmain;
+      rowoff = gl[in ? idx : 0] * RB;
+      ok = in ? rowoff + ck16 : OOB_OFF;
+      ov = in ? rowoff + cv16 : OOB_OFF;
+    }
+  };
+  auto info = [&](int u) {
+    FTile ti;
+    if (u < nband) {
+      const int t = t_lo + u;
+      const int up = t - wave;
+      ti.act = up >= 0 && up < T;
+      ti.j0 = kb + t * KT;
+      ti.okb = bit_range(-ti.j0, nrv - ti.j0);
+      const bool diag = (up == 0) || (32 * up + 31 > 2 * r);
+      ti.kind = (diag || ti.okb != 0xFFFFFFFFu) ? 1 : 0;
+    } else {
+      ti.act = true;
+      ti.j0 = (u - nband) * KT;
+      ti.okb = bit_range(0, gmain - ti.j0);
+      ti.kind = 2;
+    }
+    return ti;
+  };
+  const int32_t* gidx_b = p.gidx + (int64_t)b * n;
+  auto fill = [&]() {
+    for (int j = tid; j < gmain; j += NT) {
+      const int pos = gidx_b[j];
+      const int dp = pos - rho;
+      gl[j] = pos;
+      jr[j] = (dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
+    }
+  };
+  auto nothing = []() {};
+  if (nband > F_DIST || ngt == 0) {   // the prologue's loads are all band tiles
+    fpipe(U, wave_work, info, offs, fill, dk, dv, qo, sm, fl, lane, p.c, my_i, r, jr, smem);
+  } else {
+    fill();
+    __syncthreads();
+    fpipe(U, wave_work, info, offs, nothing, dk, dv, qo, sm, fl, lane, p.c, my_i, r, jr, smem);
+  }
+  if (g > GL_MAX) {
+    // global columns past the LDS copy: positions and window indices from the list
+    const int U2 = (g - GL_MAX + KT - 1) / KT;
+    for (int u2 = 0; u2 < U2; ++u2) {
+      __syncthreads();
+      const int j0 = GL_MAX + u2 * KT;
+      for (int j = tid; j < KT; j += NT) {
+        const int idx = j0 + j;
+        const int pos = idx < g ? gidx_b[idx] : 0;
+        const int dp = pos - rho;
+        gl[j] = pos;
+        jr[j] = (idx < g && dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
+      }
+      __syncthreads();
+      const int idx = j0 + srow;
+      const bool in = idx < g;
+      const int rowoff = gl[srow] * RB;
+      const uint4 kv = bload(rk, in ? rowoff + ck16 : OOB_OFF);
+      const uint4 vv = bload(rv, in ? rowoff + cv16 : OOB_OFF);
+      *reinterpret_cast<uint4*>(smem + FK_OFF + tid * 16) = kv;
+      *reinterpret_cast<uint4*>(smem + FV_OFF + tid * 16) = vv;
+      __syncthreads();
+      if (wave_work) {
+        FTile ti;
+        ti.act = true;
+        ti.kind = 2;
+        ti.okb = bit_range(0, g - j0);
+        ti.j0 = 0;
+        f32x16 sc = fqk(qo, smem, fl);
+        apply_mask(sc, lane_mask(ti, my_i, r, jr, lane), lane);
+        bf16x8 pb[2];
+        softmax_bf16(sm, sc, p.c, pb);
+        fpv(sm.o, pb, smem, fl);
+      }
+    }
+  }
+
+  // normalise and store (global rows are written by the merge kernel, padded
+  // rows get exact zeros)
+  const float lt = sm.l + __shfl_xor(sm.l, 32);
+  if (row_in && (my_fl & 2) == 0) {
+    const bool valid = (my_fl & 1) != 0;
+    const float inv = valid ? 1.0f / lt : 0.0f;
+    uint8_t* orow = p.O + (head + my_pos) * RB;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = valid ? sm.o[db][4 * a + e] * inv : 0.0f;
+        store_row4<true>(orow + (32 * db + 8 * a + 4 * h32) * 2, v);
+      }
+    }
+  }
+}
+
+__device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, int nv,
+                               uint8_t* smem) {
+  constexpr int RB = 128;
+  const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  int g = p.gcnt[b];
+  if (g > p.max_global) g = p.max_global;
+  const int nqt_b = (g + 31) / 32;
+  if (qg * NW >= nqt_b) return;                     // uniform over the workgroup
+  const int qt = qg * NW + wave;
+  const bool wave_work = qt < nqt_b;
+  const int n = p.n;
+  const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
+  const int32_t* gidx_b = p.gidx + (int64_t)b * n;
+  const int qidx = qt * 32 + qi;
+  const bool qok = wave_work && qidx < g;
+  const int qpos = gidx_b[qok ? qidx : 0];
+  QOp<true> qo;
+  qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
+  Softmax sm;
+  sm.init();
+  FLane fl;
+  fl.init(lane);
+
+  const int j_start = sp * p.ksplit;
+  int j_end = j_start + p.ksplit;
+  if (j_end > n) j_end = n;
+  const int j_use = j_end < nv ? j_end : nv;        // keys of the slice that are real tokens
+  const int U = (j_end - j_start + KT - 1) / KT;
+  const i32x4 dk = make_desc(p.Kg + head * RB, nv * RB);
+  const i32x4 dv = make_desc(p.Vg + head * RB, nv * RB);
+  const int srow = tid >> 3, pc = tid & 7;
+  const int ck16 = (pc ^ swz_k(srow)) * 16, cv16 = (pc ^ swz_v(srow)) * 16;
+  const int off0 = (j_start + srow) * RB;
+  auto offs = [&](int u, int& ok, int& ov) {
+    const int rowoff = off0 + u * KT * RB;
+    ok = rowoff + ck16;
+    ov = rowoff + cv16;
+  };
+  auto info = [&](int u) {
+    FTile ti;
+    ti.act = true;
+    ti.j0 = j_start + u * KT;
+    ti.okb = bit_range(0, j_use - ti.j0);
+    ti.kind = ti.okb == 0xFFFFFFFFu ? 0 : 3;
+    return ti;
+  };
+  auto nothing = []() {};
+  fpipe(U, wave_work, info, offs, nothing, dk, dv, qo, sm, fl, lane, p.c, 0, 0, nullptr, smem);
+
+  const float lt = sm.l + __shfl_xor(sm.l, 32);
+  if (qok) {
+    const int64_t pidx = ((((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp) * 32 + qi;
+    float* po = p.part_o + pidx * D;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<float4*>(po + 32 * db + 8 * a + 4 * h32) =
+            make_float4(sm.o[db][4 * a], sm.o[db][4 * a + 1], sm.o[db][4 * a + 2], sm.o[db][4 * a + 3]);
+    if (h32 == 0) {
+      p.part_ml[pidx * 2 + 0] = sm.m;
+      p.part_ml[pidx * 2 + 1] = lt;
+    }
+  }
+}
+
+template <bool BF>
+constexpr int smem_bytes() {
+  return (BF && F_SMEM > smem_bytes_general<BF>()) ? F_SMEM : smem_bytes_general<BF>();
+}
+
 // The logical workgroup order keeps neighbouring query blocks of one head on
 // one XCD (workgroups are dealt to the 8 XCDs round-robin by hardware id), so
 // that their overlapping key halos are served by that XCD's L2.
@@ -628,14 +1308,57 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(Params p) {
   const int bid = blockIdx.x;
   if (bid < p.n_glob_wg) {
     const int lg = bid;
-    if (lg < p.B * p.H * p.nqg * p.nsplit) global_wg<BF>(p, lg, smem);
+    if (lg >= p.B * p.H * p.nqg * p.nsplit) return;
+    const int sp = lg % p.nsplit;
+    int t = lg / p.nsplit;
+    const int qg = t % p.nqg;
+    t /= p.nqg;
+    const int h = t % p.H;
+    const int b = t / p.H;
+    if constexpr (BF) {
+      const int nv = p.vlen[b];
+      if (nv >= 0) {
+        global_wg_fast(p, b, h, qg, sp, nv, smem);
+        return;
+      }
+    }
+    global_wg<BF>(p, b, h, qg, sp, smem);
   } else {
-    band_wg<BF>(p, xcd_remap(bid - p.n_glob_wg, p.n_band_wg), smem);
+    const int lb = xcd_remap(bid - p.n_glob_wg, p.n_band_wg);
+    const int b = lb / p.blocks_per_b;
+    const int rem = lb - b * p.blocks_per_b;
+    int h, local, s;
+    if (p.uni_stride > 0) {
+      h = rem / p.blocks_per_head;
+      local = rem - h * p.blocks_per_head;
+      s = p.uni_stride;
+    } else if (p.H <= MAXH_ARG) {
+      h = 0;
+      while (p.hb[h + 1] <= rem) ++h;
+      local = rem - p.hb[h];
+      s = p.hs[h];
+    } else {
+      h = 0;
+      while (p.head_blk[h + 1] <= rem) ++h;
+      local = rem - p.head_blk[h];
+      s = p.head_stride[h];
+    }
+    if constexpr (BF) {
+      const int nv = p.vlen[b];
+      if (nv >= 0) {
+        band_wg_fast(p, b, h, local, s, nv, smem);
+        return;
+      }
+    }
+    band_wg<BF>(p, b, h, local, s, smem);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 3: merge of the global-row partials, one workgroup per (b, h, 32 globals).
+// Kernel 3: merge of the global-row partials.  One workgroup per (b, h, tile
+// of 32 global rows); 8 threads per row, each owning 8 of the 64 channels.
+// The split loop is unrolled so that its loads are in flight together.
+constexpr int MERGE_UNROLL = 8;
 template <bool BF>
 __global__ __launch_bounds__(256) void merge_kernel(Params p) {
   const int wg = blockIdx.x;
@@ -647,23 +1370,47 @@ __global__ __launch_bounds__(256) void merge_kernel(Params p) {
   const int q = threadIdx.x >> 3, seg = threadIdx.x & 7;
   const int idx = qt * 32 + q;
   if (idx >= g) return;
+  const int pos = p.gidx[(int64_t)b * p.n + idx];
   const int64_t base = ((int64_t)bh * p.nqt + qt) * p.nsplit;
+  const int ns = p.nsplit;
   float mstar = -INFINITY;
-  for (int sp = 0; sp < p.nsplit; ++sp) mstar = fmaxf(mstar, p.part_ml[((base + sp) * 32 + q) * 2]);
+  for (int s0 = 0; s0 < ns; s0 += MERGE_UNROLL) {
+    float mv[MERGE_UNROLL];
+#pragma unroll
+    for (int e = 0; e < MERGE_UNROLL; ++e)
+      mv[e] = (s0 + e < ns) ? p.part_ml[((base + s0 + e) * 32 + q) * 2] : -INFINITY;
+#pragma unroll
+    for (int e = 0; e < MERGE_UNROLL; ++e) mstar = fmaxf(mstar, mv[e]);
+  }
   float L = 0.f;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int sp = 0; sp < p.nsplit; ++sp) {
-    const int64_t pi = (base + sp) * 32 + q;
-    const float w = __builtin_amdgcn_exp2f(p.part_ml[pi * 2] - mstar);
-    L += w * p.part_ml[pi * 2 + 1];
-    const float4 a = *reinterpret_cast<const float4*>(p.part_o + pi * D + seg * 8);
-    const float4 c = *reinterpret_cast<const float4*>(p.part_o + pi * D + seg * 8 + 4);
-    acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-    acc[4] += w * c.x; acc[5] += w * c.y; acc[6] += w * c.z; acc[7] += w * c.w;
+  for (int s0 = 0; s0 < ns; s0 += MERGE_UNROLL) {
+    float2 ml[MERGE_UNROLL];
+    float4 a[MERGE_UNROLL], c[MERGE_UNROLL];
+#pragma unroll
+    for (int e = 0; e < MERGE_UNROLL; ++e) {
+      if (s0 + e < ns) {
+        const int64_t pi = (base + s0 + e) * 32 + q;
+        ml[e] = *reinterpret_cast<const float2*>(p.part_ml + pi * 2);
+        a[e] = *reinterpret_cast<const float4*>(p.part_o + pi * D + seg * 8);
+        c[e] = *reinterpret_cast<const float4*>(p.part_o + pi * D + seg * 8 + 4);
+      } else {
+        ml[e] = make_float2(-INFINITY, 0.f);
+        a[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        c[e] = a[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < MERGE_UNROLL; ++e) {
+      const float w = __builtin_amdgcn_exp2f(ml[e].x - mstar);
+      L += w * ml[e].y;
+      acc[0] += w * a[e].x; acc[1] += w * a[e].y; acc[2] += w * a[e].z; acc[3] += w * a[e].w;
+      acc[4] += w * c[e].x; acc[5] += w * c[e].y; acc[6] += w * c[e].z; acc[7] += w * c[e].w;
+    }
   }
   const float inv = 1.0f / L;
+#pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] *= inv;
-  const int pos = p.gidx[(int64_t)b * p.n + idx];
   constexpr int RB = D * Lay<BF>::ELT;
   uint8_t* orow = p.O + ((int64_t)bh * p.n + pos) * RB + seg * 8 * Lay<BF>::ELT;
   store_row4<BF>(orow, acc);

@@ -41,12 +41,15 @@ struct lwattn_plan_s {
   // geometry
   int nqt = 0, nqg = 0, nsplit = 0, ksplit = 0;
   int n_glob_wg = 0, n_band_wg = 0, blocks_per_b = 0;
+  int uni_stride = 0, blocks_per_head = 0;
+  std::vector<int32_t> stride_host, blk_host;
   size_t smem = 0;
   // workspace
   uint8_t* flags = nullptr;
   int32_t* gidx = nullptr;
   int32_t* gcnt = nullptr;
   int32_t* status = nullptr;
+  int32_t* vlen = nullptr;
   float* part_o = nullptr;
   float* part_ml = nullptr;
   int32_t* head_stride = nullptr;
@@ -63,6 +66,7 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->gidx);
   (void)hipFree(p->gcnt);
   (void)hipFree(p->status);
+  (void)hipFree(p->vlen);
   (void)hipFree(p->part_o);
   (void)hipFree(p->part_ml);
   (void)hipFree(p->head_stride);
@@ -103,7 +107,7 @@ lwattn_status lwattn_check_config(const lwattn_config* c) {
   const int64_t elems = (int64_t)c->B * c->H * c->n * c->d;
   if (elems > ((int64_t)1 << 40)) return LWATTN_E_INVALID;
   if ((int64_t)c->B * c->n > ((int64_t)1 << 31) - 1) return LWATTN_E_INVALID;
-  if (c->n > (1 << 28)) return LWATTN_E_INVALID;   // keeps window/tile arithmetic in int32
+  if (c->n > (1 << 23)) return LWATTN_E_INVALID;   // keeps row byte offsets of one head in int32
   if (c->d != lwk::D) return LWATTN_E_UNSUPPORTED;
   return LWATTN_OK;
 }
@@ -141,6 +145,12 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
     blk[h + 1] = blk[h] + (int32_t)nb;
   }
   p->blocks_per_b = blk[H];
+  p->stride_host = stride;
+  p->blk_host = blk;
+  bool uni = H > 0;
+  for (int h = 1; h < H; ++h) uni = uni && stride[h] == stride[0];
+  p->uni_stride = uni ? stride[0] : 0;
+  p->blocks_per_head = uni ? blk[1] : 0;
   const int64_t nband = (int64_t)B * blk[H];
   // global-row geometry
   p->nqt = ceil_div(cfg->max_global, 32);
@@ -163,7 +173,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   }
   p->n_band_wg = (int)nband;
   p->n_glob_wg = (int)nglob_pad;
-  p->smem = (cfg->dtype == LWATTN_BF16 ? lwk::SlotLay<true>::BYTES : lwk::SlotLay<false>::BYTES) * 2;
+  p->smem = cfg->dtype == LWATTN_BF16 ? lwk::smem_bytes<true>() : lwk::smem_bytes<false>();
 
   // workspace
   const size_t bn = (size_t)B * n;
@@ -177,6 +187,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->gidx, bn * 4);
   alloc((void**)&p->gcnt, (size_t)B * 4);
   alloc((void**)&p->status, (size_t)B * 4);
+  alloc((void**)&p->vlen, (size_t)B * 4);
   const size_t nparts = (size_t)B * H * p->nqt * (p->nsplit > 0 ? p->nsplit : 0) * 32;
   alloc((void**)&p->part_o, nparts * lwk::D * 4);
   alloc((void**)&p->part_ml, nparts * 2 * 4);
@@ -232,6 +243,7 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   prm.gidx = p->gidx;
   prm.gcnt = p->gcnt;
   prm.status = p->status;
+  prm.vlen = p->vlen;
   prm.part_o = p->part_o;
   prm.part_ml = p->part_ml;
   prm.head_stride = p->head_stride;
@@ -249,6 +261,11 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   prm.n_band_wg = p->n_band_wg;
   prm.blocks_per_b = p->blocks_per_b;
   prm.c = c.scale * 1.4426950408889634f;
+  prm.mask_vec = ((((uintptr_t)lmask | (uintptr_t)gmask) & 15u) == 0 && (c.n % 4) == 0) ? 1 : 0;
+  prm.uni_stride = p->uni_stride;
+  prm.blocks_per_head = p->blocks_per_head;
+  for (int h = 0; h < lwk::MAXH_ARG; ++h) prm.hs[h] = h < c.H ? p->stride_host[h] : 0;
+  for (int h = 0; h <= lwk::MAXH_ARG; ++h) prm.hb[h] = h <= c.H ? p->blk_host[h] : 0;
 
   const bool timed = p->timing_cap > 0 && p->timing_calls < p->timing_cap;
   hipEvent_t* ev = timed ? &p->events[(size_t)p->timing_calls * (kNumKernels + 1)] : nullptr;

@@ -49,7 +49,8 @@ class Spec:
     # structure recipe
     global_mode: str = "first"      # "first": positions [0, g); "random": uniform in valid prefix
     n_global: int = 1
-    pad_mode: str = "none"          # "none" | "per_batch" (U{lo..hi} each) | "one_seq" (one b, U{lo..hi})
+    pad_mode: str = "none"          # "none" | "per_batch" (tail U{lo..hi} each) | "one_seq" (one b,
+                                    # tail U{lo..hi}) | "scatter" (U{lo..hi} padded positions anywhere)
     pad_lo: int = 0
     pad_hi: int = 0
     k_boost_frac: float = 0.0       # fraction of K rows per (b,h) multiplied by k_boost
@@ -109,6 +110,7 @@ def generate(spec: Spec, strong: bool = False, seed: Optional[int] = None) -> In
 
     # 1. pad lengths (and 2. which sequence is padded)
     pad_len = np.zeros(B, np.int64)
+    lmask = np.ones((B, n), np.float32)
     if spec.pad_mode == "per_batch":
         pad_len = rng.integers(spec.pad_lo, spec.pad_hi, size=B, endpoint=True)
     elif spec.pad_mode == "one_seq":
@@ -116,21 +118,26 @@ def generate(spec: Spec, strong: bool = False, seed: Optional[int] = None) -> In
         which = int(rng.integers(0, B))
         pad_len[which] = length
     pad_len = np.minimum(pad_len, n)
-    lmask = np.ones((B, n), np.float32)
-    for b in range(B):
-        if pad_len[b]:
-            lmask[b, n - pad_len[b]:] = 0.0
+    if spec.pad_mode == "scatter":
+        for b in range(B):
+            cnt = min(int(rng.integers(spec.pad_lo, spec.pad_hi, endpoint=True)), n)
+            lmask[b, rng.choice(n, size=cnt, replace=False)] = 0.0
+            pad_len[b] = cnt
+    else:
+        for b in range(B):
+            if pad_len[b]:
+                lmask[b, n - pad_len[b]:] = 0.0
 
-    # 3. global positions, inside the valid prefix
+    # 3. global positions, among the real tokens
     gmask = np.zeros((B, n), np.float32)
     global_pos = []
     for b in range(B):
-        nv = n - int(pad_len[b])
-        g = min(spec.n_global, nv)
+        valid = np.flatnonzero(lmask[b] != 0)
+        g = min(spec.n_global, valid.size)
         if spec.global_mode == "first":
-            pos = np.arange(g)
+            pos = valid[:g]
         else:
-            pos = np.sort(rng.choice(nv, size=g, replace=False))
+            pos = np.sort(valid[rng.choice(valid.size, size=g, replace=False)])
         gmask[b, pos] = 1.0
         global_pos.append(pos.astype(np.int64))
 

@@ -38,6 +38,8 @@ SMALL = [
     (1, 1, 1, 2, "f32", [0], 1, "first", "none", 0),                   # n = 1
     (1, 1, 31, 10, "bf16", [3], 31, "first", "none", 0),               # every token global
     (2, 2, 700, 60, "bf16", [0, 1], 70, "random", "per_batch", 650),   # > 2 global tiles, long pads
+    (2, 3, 600, 64, "bf16", [0, 1, 3], 6, "random", "scatter", 150),   # padding anywhere
+    (2, 2, 333, 40, "f32", [0, 2], 5, "random", "scatter", 80),
 ]
 
 
@@ -171,6 +173,26 @@ def test_empty_problem_and_bad_pointers():
     assert lib.lwattn_forward(plan2.handle, *ptrs, mk.data_ptr(), mk.data_ptr(), None, s) == lw.E_INVALID
     assert lib.lwattn_forward(plan2.handle, t.data_ptr() + 4, *ptrs[1:], mk.data_ptr(), mk.data_ptr(),
                               t.data_ptr(), s) == lw.E_INVALID
+
+
+def test_mixed_prefix_and_scattered_padding_in_one_call():
+    """Rows whose real tokens are a prefix and rows padded anywhere, in one launch."""
+    spec = workloads.custom(4, 2, 500, 64, 96, "bf16", [0, 2], seed=8, n_global=7,
+                            pad_mode="per_batch", pad_hi=120)
+    x = workloads.generate(spec)
+    rng = np.random.default_rng(3)
+    x.lmask[1, rng.choice(500, size=60, replace=False)] = 0.0      # scattered in row 1
+    x.lmask[3, :40] = 0.0                                          # padded head in row 3
+    x.gmask[1] = 0.0
+    x.gmask[1, np.flatnonzero(x.lmask[1])[[0, 5, 77]]] = 1.0
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec)
+    out, st = run(plan, ts, lm, gm)
+    assert st == lw.OK
+    got = to_np64(out)
+    want = oracle.forward(*x.tensors(), x.lmask, x.gmask, spec.window, spec.dilation, spec.scale)
+    _padded_rows_zero(got, x)
+    assert np.max(np.abs(got - want)) <= TOL_ABS["bf16"]
 
 
 def test_all_padded_and_all_global_rows():

@@ -47,7 +47,7 @@ namespace lwk {
 
 constexpr int D = 64;          // head dim (fixed)
 constexpr int KT = 32;         // keys per tile
-constexpr int NW = 4;          // waves per workgroup
+constexpr int NW = 2;          // waves per workgroup
 constexpr int NT = 64 * NW;    // threads per workgroup
 constexpr int ROWS_WG = 32 * NW;
 constexpr int MAXH_ARG = 32;   // per-head tables passed by value up to this many heads
@@ -801,11 +801,18 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int FK_OFF = 0;                       // K tile, 32 x 128 B
 constexpr int FV_OFF = 4096;                    // V tile, 32 x 128 B
 constexpr int FSLOT = 8192;
-constexpr int F_DIST = 4;                       // tiles u+2 .. u+F_DIST are in flight during step u
+#ifndef LW_F_DIST
+#define LW_F_DIST 4
+#endif
+#ifndef LW_STAGE_REGS
+#define LW_STAGE_REGS 1   // 1: stage K/V through registers; 0: buffer loads straight into LDS
+#endif
+constexpr int F_DIST = LW_F_DIST;               // tiles u+2 .. u+F_DIST are in flight during step u
 constexpr int F_NSLOT = F_DIST + 1;             // LDS ring: tiles u .. u+F_DIST
 constexpr int F_GL_OFF = F_NSLOT * FSLOT;       // int32[GL_MAX]: global positions
 constexpr int F_JR_OFF = F_GL_OFF + GL_MAX * 4; // int32[GL_MAX]: their window index (or JREL_NONE)
 constexpr int F_SMEM = F_JR_OFF + GL_MAX * 4;
+constexpr int FCH = 256 / NT;                   // 16-byte chunks per thread per 4 KB tile array
 constexpr int OOB_OFF = 0x7FFFFF00;             // a buffer offset past any range
 
 __device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
@@ -819,31 +826,31 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
 }
 
 struct FStage {
-  uint4 k, v;
+  uint4 k[256 / (64 * NW)], v[256 / (64 * NW)];   // FCH chunks of K and of V
 };
 
 // Per-lane LDS byte offsets used by the compute of every tile.
 struct FLane {
-  int k[4];   // K row lane%32, logical chunk 4*(lane/32) + c
-  int v[2];   // transpose-read source address for d block db (c2 / key-block offsets are immediates)
+  int k[4];   // offsets in a K tile: row lane%32, logical chunk 4*(lane/32) + c
+  int v[2];   // offsets in a V tile: transpose-read source for d block db (c2 / key-block offsets are immediates)
   __device__ void init(int lane) {
     const int row = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) k[c] = FK_OFF + row * 128 + (((4 * h + c) ^ swz_k(row)) * 16);
+    for (int c = 0; c < 4; ++c) k[c] = row * 128 + (((4 * h + c) ^ swz_k(row)) * 16);
     const int g1 = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       const int chunk = (4 * db + 2 * g1 + (q >> 1)) ^ (2 * e);   // row & 3 == e for every row read
-      v[db] = FV_OFF + (4 * h + e) * 128 + chunk * 16 + (q & 1) * 8;
+      v[db] = (4 * h + e) * 128 + chunk * 16 + (q & 1) * 8;
     }
   }
 };
 
-__device__ __forceinline__ f32x16 fqk(const QOp<true>& qo, const uint8_t* slot, const FLane& fl) {
+__device__ __forceinline__ f32x16 fqk(const QOp<true>& qo, const uint8_t* kt, const FLane& fl) {
   f32x16 s = {};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + fl.k[c]);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + fl.k[c]);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qo.q[c], s, 0, 0, 0);
   }
   return s;
@@ -854,20 +861,24 @@ __device__ __forceinline__ s16x4 tr_read(const uint8_t* addr) {
       (__attribute__((address_space(3))) s16x4*)(addr));
 }
 
-__device__ __forceinline__ void fpv(f32x16 (&o)[2], const bf16x8 (&pb)[2], const uint8_t* slot,
+__device__ __forceinline__ void fpv(f32x16 (&o)[2], const bf16x8 (&pb)[2], const uint8_t* vt,
                                     const FLane& fl) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      const s16x4 lo = tr_read(slot + fl.v[db] + c2 * 2048);          // keys 16c2 + 4h + e
-      const s16x4 hi = tr_read(slot + fl.v[db] + c2 * 2048 + 1024);   // keys 16c2 + 8 + 4h + e
+      const s16x4 lo = tr_read(vt + fl.v[db] + c2 * 2048);            // keys 16c2 + 4h + e
+      const s16x4 hi = tr_read(vt + fl.v[db] + c2 * 2048 + 1024);     // keys 16c2 + 8 + 4h + e
       typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[c2], o[db],
                                                       0, 0, 0);
     }
   }
+}
+
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Bits [lo, hi) of a 32-bit word (empty when hi <= lo).
@@ -935,12 +946,20 @@ __device__ __forceinline__ void apply_mask(f32x16& sc, uint32_t m, int lane) {
   }
 }
 
+// v_max3_f32 without the NaN-quieting copies the compiler adds around fmaxf.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // Online-softmax update of one tile; the probabilities come out as bf16 and
 // the row sum is taken over those rounded values (the ones PV multiplies).
 __device__ __forceinline__ void softmax_bf16(Softmax& sm, const f32x16& s, float c, bf16x8 (&pb)[2]) {
-  float mx = fmaxf(s[0], s[1]);
+  float mx = max3f(s[0], s[1], s[2]);
 #pragma unroll
-  for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+  for (int r = 3; r < 15; r += 2) mx = max3f(mx, s[r], s[r + 1]);
+  mx = max3f(mx, s[15], s[15]);
   mx = half_max(mx);
   const float mnew = fmaxf(sm.m, mx * c);
   if (__any(mnew > sm.m + TAU)) {
@@ -995,14 +1014,23 @@ __device__ __forceinline__ void dma16(i32x4 desc, int voff, uint32_t lds_base) {
       : "v"(voff), "s"(desc), "s"(lds_base)
       : "memory", "m0");
 }
-// Wait until at most 2*c of this wave's loads are outstanding.
+// Wait until at most c tiles' loads (2*FCH per tile and thread) are outstanding.
+template <int C>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(2 * FCH * C <= 63, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * FCH * C) : "memory");
+}
 __device__ __forceinline__ void wait_tiles(int c) {
-  if (c <= 0)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if (c == 1)
-    asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  static_assert(F_DIST <= 8, "wait_tiles covers up to 6 tiles in flight");
+  switch (c < 0 ? 0 : c) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<1>(); break;
+    case 2: wait_vm<2>(); break;
+    case 3: wait_vm<3>(); break;
+    case 4: wait_vm<4>(); break;
+    case 5: wait_vm<5>(); break;
+    default: wait_vm<6>(); break;
+  }
 }
 
 // Software-pipelined tile loop.  Tile t goes, by buffer-to-LDS loads, into
@@ -1013,54 +1041,167 @@ __device__ __forceinline__ void wait_tiles(int c) {
 // loop is unrolled by two so the score registers alternate without copies.
 template <class InfoFn, class OffFn, class PreFn>
 __device__ __forceinline__ void fpipe(int U, bool wave_work, InfoFn info, OffFn offs, PreFn pre,
-                                      i32x4 dk, i32x4 dv, const QOp<true>& qo, Softmax& sm,
+                                      i32x4 dk, i32x4 dv, __amdgpu_buffer_rsrc_t rk,
+                                      __amdgpu_buffer_rsrc_t rv, const QOp<true>& qo, Softmax& sm,
                                       const FLane& fl, int lane, float c, int my_i, int r,
                                       const int32_t* jr, uint8_t* smem) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lds0 =
       (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + wave * 1024;
   auto slot = [&](int u) { return smem + (u % F_NSLOT) * FSLOT; };
-  auto issue = [&](int u) {
-    int ok, ov;
-    offs(u, ok, ov);
+  [[maybe_unused]] auto issue = [&](int u) {
     const uint32_t base = lds0 + (u % F_NSLOT) * FSLOT;
-    dma16(dk, ok, base + FK_OFF);
-    dma16(dv, ov, base + FV_OFF);
+#pragma unroll
+    for (int e = 0; e < FCH; ++e) {
+      int ok, ov;
+      offs(u, e, ok, ov);
+      dma16(dk, ok, base + FK_OFF + e * NT * 16);
+      dma16(dv, ov, base + FV_OFF + e * NT * 16);
+    }
   };
+#if LW_STAGE_REGS
+  // Register staging: tile t is loaded into register set t % 2 two steps
+  // before its LDS store, stored into slot t % F_NSLOT one step before use.
+  FStage rs[2];
+  auto rload = [&](FStage& set, int u) {
+#pragma unroll
+    for (int e = 0; e < FCH; ++e) {
+      int ok, ov;
+      offs(u, e, ok, ov);
+      set.k[e] = bload(rk, ok);
+      set.v[e] = bload(rv, ov);
+    }
+  };
+  auto rstore = [&](const FStage& set, int u) {
+    uint8_t* sl = slot(u);
+#pragma unroll
+    for (int e = 0; e < FCH; ++e) {
+      *reinterpret_cast<uint4*>(sl + FK_OFF + (threadIdx.x + NT * e) * 16) = set.k[e];
+      *reinterpret_cast<uint4*>(sl + FV_OFF + (threadIdx.x + NT * e) * 16) = set.v[e];
+    }
+  };
+  rload(rs[0], 0);
+  if (U > 1) rload(rs[1], 1);
+  pre();
+  rstore(rs[0], 0);
+  if (U > 1) rstore(rs[1], 1);
+  if (U > 2) rload(rs[0], 2);
+  if (U > 3) rload(rs[1], 3);
+  __syncthreads();
+#else
   const int last0 = U - 1 < F_DIST ? U - 1 : F_DIST;
   for (int v = 0; v <= last0; ++v) issue(v);
   pre();
   wait_tiles(last0 - 1);           // tiles 0 and 1 have landed
   __syncthreads();
+#endif
   FTile cur = info(0);
   f32x16 S0, S1;
-  if (wave_work && cur.act) S0 = fqk(qo, slot(0), fl);
-  auto step = [&](int u, f32x16& Sin, f32x16& Sout) {
+  if (wave_work && cur.act) S0 = fqk(qo, slot(0) + FK_OFF, fl);
+  auto step = [&](int u, f32x16& Sin, f32x16& Sout, FStage& R) {
+#if !LW_STAGE_REGS
     if (u >= 1 && u + F_DIST < U) issue(u + F_DIST);
+#endif
     FTile nxt;
     nxt.act = false;
     nxt.kind = 0;
     nxt.okb = 0;
     nxt.j0 = 0;
     if (u + 1 < U) nxt = info(u + 1);
-    if (wave_work && nxt.act) Sout = fqk(qo, slot(u + 1), fl);
+    if (wave_work && nxt.act) Sout = fqk(qo, slot(u + 1) + FK_OFF, fl);
     if (wave_work && cur.act) {
       if (cur.kind != 0)
         apply_mask(Sin, lane_mask(cur, my_i, r, jr + (cur.kind == 2 ? cur.j0 : 0), lane), lane);
       bf16x8 pb[2];
       softmax_bf16(sm, Sin, c, pb);
-      fpv(sm.o, pb, slot(u), fl);
+      fpv(sm.o, pb, slot(u) + FV_OFF, fl);
     }
+#if LW_STAGE_REGS
+    if (u + 2 < U) rstore(R, u + 2);     // R holds tile u+2
+    __syncthreads();
+    if (u + 4 < U) rload(R, u + 4);
+#else
     const int last = U - 1 < u + F_DIST ? U - 1 : u + F_DIST;
     wait_tiles(last - (u + 2));
     __syncthreads();
+#endif
     cur = nxt;
   };
+#if LW_STAGE_REGS
+  FStage& RA = rs[0];
+  FStage& RB = rs[1];
+#else
+  FStage RA, RB;
+#endif
   for (int u = 0; u < U; u += 2) {
-    step(u, S0, S1);
+    step(u, S0, S1, RA);
     if (u + 1 >= U) break;
-    step(u + 1, S1, S0);
+    step(u + 1, S1, S0, RB);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fast band workgroup: NW x 32 query rows of one (batch, head, residue class)
+// against 64 keys per step, held as two 32-key halves in the tile layout
+// above (K halves at +0 / +4 KB, V halves at +8 KB / +12 KB of a 16 KB slot).
+// With two waves every wave needs the same 64-key tiles, so the workgroup
+// steps without skew; the halves give each step two independent MFMA and
+// softmax chains.  Keys reach LDS by buffer loads issued two steps ahead
+// into a ring of three slots.
+constexpr int W_SLOT = 16384;
+constexpr int W_NSLOT = 3;
+constexpr int W_GL_OFF = W_NSLOT * W_SLOT;
+constexpr int W_JR_OFF = W_GL_OFF + GL_MAX * 4;
+constexpr int W_SMEM = W_JR_OFF + GL_MAX * 4;
+constexpr int W_CH = 512 / NT;          // 16-byte chunks per thread per 8 KB array of a step
+
+// s_waitcnt vmcnt(N): at most N of this wave's loads outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N <= 63, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Softmax over the two halves of a step (one running max per row).
+__device__ __forceinline__ void softmax2_bf16(Softmax& sm, const f32x16& sa, const f32x16& sb,
+                                              float c, bf16x8 (&pa)[2], bf16x8 (&pbb)[2]) {
+  float mx = max3f(sa[0], sa[1], sa[2]);
+#pragma unroll
+  for (int r = 3; r < 15; r += 2) mx = max3f(mx, sa[r], sa[r + 1]);
+  mx = max3f(mx, sa[15], sb[0]);
+#pragma unroll
+  for (int r = 1; r < 15; r += 2) mx = max3f(mx, sb[r], sb[r + 1]);
+  mx = max3f(mx, sb[15], sb[15]);
+  mx = half_max(mx);
+  const float mnew = fmaxf(sm.m, mx * c);
+  if (__any(mnew > sm.m + TAU)) {
+    const float alpha = __builtin_amdgcn_exp2f(sm.m - mnew);
+    sm.l *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { sm.o[0][r] *= alpha; sm.o[1][r] *= alpha; }
+    sm.m = mnew;
+  }
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc_a = sm.l, acc_b = 0.f;
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      bf16x2 xa, xb;
+      xa[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sa[8 * c2 + e], c, -sm.m));
+      xa[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sa[8 * c2 + e + 1], c, -sm.m));
+      xb[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sb[8 * c2 + e], c, -sm.m));
+      xb[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sb[8 * c2 + e + 1], c, -sm.m));
+      pa[c2][e] = xa[0];
+      pa[c2][e + 1] = xa[1];
+      pbb[c2][e] = xb[0];
+      pbb[c2][e + 1] = xb[1];
+      acc_a = __builtin_amdgcn_fdot2_f32_bf16(xa, ones, acc_a, false);
+      acc_b = __builtin_amdgcn_fdot2_f32_bf16(xb, ones, acc_b, false);
+    }
+  }
+  sm.l = acc_a + acc_b;
 }
 
 __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, int nv,
@@ -1080,20 +1221,22 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
   const int nrv = nv > rho ? (nv - rho + s - 1) / s : 0;   // subsequence keys that are real tokens
 
+  // band tiles of 64 keys: tile t holds subsequence keys kb + 64t .. kb + 64t + 63
   const int r = p.r;
   const int kb = R0 - r;
-  const int T = (31 + 2 * r) / 32 + 1;
-  const int t_lo = (-kb - 31 > 0) ? (-kb - 31 + 31) / 32 : 0;
-  int t_hi = (nr - 1 - kb) / 32;
-  if (t_hi > NW - 1 + T - 1) t_hi = NW - 1 + T - 1;
+  const int T = (ROWS_WG - 1 + 2 * r) / 64 + 1;
+  const int t_lo = (-kb - 63 > 0) ? (-kb - 63 + 63) / 64 : 0;
+  int t_hi = (nr - 1 - kb) / 64;
+  if (t_hi > T - 1) t_hi = T - 1;
   const int nband = t_hi - t_lo + 1;
   int g = p.gcnt[b];
   if (g > p.max_global) g = p.max_global;
   const int gmain = g < GL_MAX ? g : GL_MAX;
-  const int ngt = (gmain + KT - 1) / KT;
+  const int ngt = (gmain + 63) / 64;
   const int U = nband + ngt;
 
-  const int my_i = R0 + 32 * wave + qi;
+  const int R0w = R0 + 32 * wave;
+  const int my_i = R0w + qi;
   const bool row_in = my_i < nr;
   const int my_pos = rho + (row_in ? my_i : 0) * s;
   const uint8_t my_fl = p.flags[(int64_t)b * n + my_pos];
@@ -1105,49 +1248,40 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   fl.init(lane);
   const bool wave_work = __any(row_in && (my_fl & 3) == 1);
 
-  int32_t* gl = reinterpret_cast<int32_t*>(smem + F_GL_OFF);
-  int32_t* jr = reinterpret_cast<int32_t*>(smem + F_JR_OFF);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * RB, nv * RB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * RB, nv * RB);
+  int32_t* gl = reinterpret_cast<int32_t*>(smem + W_GL_OFF);
+  int32_t* jr = reinterpret_cast<int32_t*>(smem + W_JR_OFF);
   const i32x4 dk = make_desc(p.K + head * RB, nv * RB);
   const i32x4 dv = make_desc(p.V + head * RB, nv * RB);
-  const int srow = tid >> 3, pc = tid & 7;
-  const int ck16 = (pc ^ swz_k(srow)) * 16, cv16 = (pc ^ swz_v(srow)) * 16;
-  const int band_off0 = (rho + (kb + t_lo * KT + srow) * s) * RB;
-  const int band_step = KT * s * RB;
-  auto offs = [&](int u, int& ok, int& ov) {
-    int rowoff;
-    if (u < nband) {
-      rowoff = band_off0 + u * band_step;
-      ok = rowoff + ck16;
-      ov = rowoff + cv16;
-    } else {
-      const int idx = (u - nband) * KT + srow;
-      const bool in = idx < gmain;
-      rowoff = gl[in ? idx : 0] * RB;
-      ok = in ? rowoff + ck16 : OOB_OFF;
-      ov = in ? rowoff + cv16 : OOB_OFF;
-    }
-  };
-  auto info = [&](int u) {
-    FTile ti;
-    if (u < nband) {
-      const int t = t_lo + u;
-      const int up = t - wave;
-      ti.act = up >= 0 && up < T;
-      ti.j0 = kb + t * KT;
-      ti.okb = bit_range(-ti.j0, nrv - ti.j0);
-      const bool diag = (up == 0) || (32 * up + 31 > 2 * r);
-      ti.kind = (diag || ti.okb != 0xFFFFFFFFu) ? 1 : 0;
-    } else {
-      ti.act = true;
-      ti.j0 = (u - nband) * KT;
-      ti.okb = bit_range(0, gmain - ti.j0);
-      ti.kind = 2;
-    }
-    return ti;
-  };
+  // thread tid stages chunks q = tid + NT*e of each 8 KB array: key row q/8 of
+  // the step (half q/256), physical chunk q%8
+  int ck16[W_CH], cv16[W_CH], srow[W_CH];
+#pragma unroll
+  for (int e = 0; e < W_CH; ++e) {
+    const int q = tid + NT * e;
+    srow[e] = q >> 3;
+    ck16[e] = ((q & 7) ^ swz_k(srow[e] & 31)) * 16;
+    cv16[e] = ((q & 7) ^ swz_v(srow[e] & 31)) * 16;
+  }
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
+  const uint32_t lds0 =
+      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + wave * 1024;
+  auto issue = [&](int u) {
+    const uint32_t base = lds0 + (u % W_NSLOT) * W_SLOT;
+#pragma unroll
+    for (int e = 0; e < W_CH; ++e) {
+      int rowoff;
+      bool in = true;
+      if (u < nband) {
+        rowoff = (rho + (kb + (t_lo + u) * 64 + srow[e]) * s) * RB;
+      } else {
+        const int idx = (u - nband) * 64 + srow[e];
+        in = idx < gmain;
+        rowoff = gl[in ? idx : 0] * RB;
+      }
+      dma16(dk, in ? rowoff + ck16[e] : OOB_OFF, base + e * NT * 16);
+      dma16(dv, in ? rowoff + cv16[e] : OOB_OFF, base + 8192 + e * NT * 16);
+    }
+  };
   auto fill = [&]() {
     for (int j = tid; j < gmain; j += NT) {
       const int pos = gidx_b[j];
@@ -1156,47 +1290,126 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
       jr[j] = (dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
     }
   };
-  auto nothing = []() {};
-  if (nband > F_DIST || ngt == 0) {   // the prologue's loads are all band tiles
-    fpipe(U, wave_work, info, offs, fill, dk, dv, qo, sm, fl, lane, p.c, my_i, r, jr, smem);
-  } else {
+  // the list must be in LDS before the first global-column tile is issued
+  const bool early_fill = nband < 2 && ngt > 0;
+  if (early_fill) {
     fill();
     __syncthreads();
-    fpipe(U, wave_work, info, offs, nothing, dk, dv, qo, sm, fl, lane, p.c, my_i, r, jr, smem);
   }
+  issue(0);
+  if (U > 1) issue(1);
+  if (!early_fill) fill();
+  if (U > 1)
+    wait_loads<2 * W_CH>();   // tile 0 landed (tile 1's 2*W_CH loads may still fly)
+  else
+    wait_loads<0>();
+  __syncthreads();
+
+  for (int u = 0; u < U; ++u) {
+    if (u + 2 < U) issue(u + 2);
+    const uint8_t* sl = smem + (u % W_NSLOT) * W_SLOT;
+    if (wave_work) {
+      // per-half masks (wave-uniform)
+      int kind[2], j0[2];
+      uint32_t okb[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        if (u < nband) {
+          j0[hf] = kb + (t_lo + u) * 64 + 32 * hf;
+          okb[hf] = bit_range(-j0[hf], nrv - j0[hf]);
+          const bool inside = j0[hf] >= R0w + 31 - r && j0[hf] + 31 <= R0w + r;
+          kind[hf] = (inside && okb[hf] == 0xFFFFFFFFu) ? 0 : 1;
+        } else {
+          j0[hf] = (u - nband) * 64 + 32 * hf;
+          okb[hf] = bit_range(0, gmain - j0[hf]);
+          kind[hf] = 2;
+        }
+      }
+      // QK^T of both halves, chains interleaved
+      f32x16 sa = {}, sb = {};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        sa = mfma_bf16(*reinterpret_cast<const bf16x8*>(sl + fl.k[cc]), qo.q[cc], sa);
+        sb = mfma_bf16(*reinterpret_cast<const bf16x8*>(sl + 4096 + fl.k[cc]), qo.q[cc], sb);
+      }
+      if (kind[0] != 0) {
+        FTile ti;
+        ti.act = true; ti.kind = kind[0]; ti.okb = okb[0]; ti.j0 = j0[0];
+        apply_mask(sa, lane_mask(ti, my_i, r, jr + (kind[0] == 2 ? j0[0] : 0), lane), lane);
+      }
+      if (kind[1] != 0) {
+        FTile ti;
+        ti.act = true; ti.kind = kind[1]; ti.okb = okb[1]; ti.j0 = j0[1];
+        apply_mask(sb, lane_mask(ti, my_i, r, jr + (kind[1] == 2 ? j0[1] : 0), lane), lane);
+      }
+      bf16x8 pa[2], pbb[2];
+      softmax2_bf16(sm, sa, sb, p.c, pa, pbb);
+      // PV of both halves, alternating accumulators
+      const uint8_t* va = sl + 8192;
+      const uint8_t* vb = sl + 8192 + 4096;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const s16x4 lo = tr_read(va + fl.v[db] + c2 * 2048);
+          const s16x4 hi = tr_read(va + fl.v[db] + c2 * 2048 + 1024);
+          sm.o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                               pa[c2], sm.o[db]);
+        }
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const s16x4 lo = tr_read(vb + fl.v[db] + c2 * 2048);
+          const s16x4 hi = tr_read(vb + fl.v[db] + c2 * 2048 + 1024);
+          sm.o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                               pbb[c2], sm.o[db]);
+        }
+      }
+    }
+    if (u + 2 < U)
+      wait_loads<2 * W_CH>();   // tile u+1 landed; tile u+2 may still fly
+    else
+      wait_loads<0>();
+    __syncthreads();
+  }
+
   if (g > GL_MAX) {
-    // global columns past the LDS copy: positions and window indices from the list
+    // global columns past the LDS copy, 32 at a time through the first slot
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * RB, nv * RB);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * RB, nv * RB);
     const int U2 = (g - GL_MAX + KT - 1) / KT;
     for (int u2 = 0; u2 < U2; ++u2) {
       __syncthreads();
-      const int j0 = GL_MAX + u2 * KT;
+      const int jb = GL_MAX + u2 * KT;
       for (int j = tid; j < KT; j += NT) {
-        const int idx = j0 + j;
+        const int idx = jb + j;
         const int pos = idx < g ? gidx_b[idx] : 0;
         const int dp = pos - rho;
         gl[j] = pos;
         jr[j] = (idx < g && dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
       }
       __syncthreads();
-      const int idx = j0 + srow;
-      const bool in = idx < g;
-      const int rowoff = gl[srow] * RB;
-      const uint4 kv = bload(rk, in ? rowoff + ck16 : OOB_OFF);
-      const uint4 vv = bload(rv, in ? rowoff + cv16 : OOB_OFF);
-      *reinterpret_cast<uint4*>(smem + FK_OFF + tid * 16) = kv;
-      *reinterpret_cast<uint4*>(smem + FV_OFF + tid * 16) = vv;
+#pragma unroll
+      for (int e = 0; e < W_CH / 2; ++e) {
+        const int q = tid + NT * e;            // chunk of the 32-key tile
+        const int row = q >> 3;
+        const bool in = jb + row < g;
+        const int rowoff = gl[row] * RB;
+        const int k16 = ((q & 7) ^ swz_k(row)) * 16, v16 = ((q & 7) ^ swz_v(row)) * 16;
+        *reinterpret_cast<uint4*>(smem + q * 16) = bload(rk, in ? rowoff + k16 : OOB_OFF);
+        *reinterpret_cast<uint4*>(smem + 8192 + q * 16) = bload(rv, in ? rowoff + v16 : OOB_OFF);
+      }
       __syncthreads();
       if (wave_work) {
         FTile ti;
         ti.act = true;
         ti.kind = 2;
-        ti.okb = bit_range(0, g - j0);
+        ti.okb = bit_range(0, g - jb);
         ti.j0 = 0;
         f32x16 sc = fqk(qo, smem, fl);
         apply_mask(sc, lane_mask(ti, my_i, r, jr, lane), lane);
         bf16x8 pb[2];
         softmax_bf16(sm, sc, p.c, pb);
-        fpv(sm.o, pb, smem, fl);
+        fpv(sm.o, pb, smem + 8192, fl);
       }
     }
   }
@@ -1252,13 +1465,21 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   const int U = (j_end - j_start + KT - 1) / KT;
   const i32x4 dk = make_desc(p.Kg + head * RB, nv * RB);
   const i32x4 dv = make_desc(p.Vg + head * RB, nv * RB);
-  const int srow = tid >> 3, pc = tid & 7;
-  const int ck16 = (pc ^ swz_k(srow)) * 16, cv16 = (pc ^ swz_v(srow)) * 16;
-  const int off0 = (j_start + srow) * RB;
-  auto offs = [&](int u, int& ok, int& ov) {
-    const int rowoff = off0 + u * KT * RB;
-    ok = rowoff + ck16;
-    ov = rowoff + cv16;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.Kg + head * RB, nv * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.Vg + head * RB, nv * RB);
+  int ck16[FCH], cv16[FCH], off0[FCH];
+#pragma unroll
+  for (int e = 0; e < FCH; ++e) {
+    const int q = tid + NT * e;
+    const int srow = q >> 3;
+    ck16[e] = ((q & 7) ^ swz_k(srow)) * 16;
+    cv16[e] = ((q & 7) ^ swz_v(srow)) * 16;
+    off0[e] = (j_start + srow) * RB;
+  }
+  auto offs = [&](int u, int e, int& ok, int& ov) {
+    const int rowoff = off0[e] + u * KT * RB;
+    ok = rowoff + ck16[e];
+    ov = rowoff + cv16[e];
   };
   auto info = [&](int u) {
     FTile ti;
@@ -1269,7 +1490,7 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
     return ti;
   };
   auto nothing = []() {};
-  fpipe(U, wave_work, info, offs, nothing, dk, dv, qo, sm, fl, lane, p.c, 0, 0, nullptr, smem);
+  fpipe(U, wave_work, info, offs, nothing, dk, dv, rk, rv, qo, sm, fl, lane, p.c, 0, 0, nullptr, smem);
 
   const float lt = sm.l + __shfl_xor(sm.l, 32);
   if (qok) {
@@ -1290,7 +1511,8 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
 
 template <bool BF>
 constexpr int smem_bytes() {
-  return (BF && F_SMEM > smem_bytes_general<BF>()) ? F_SMEM : smem_bytes_general<BF>();
+  constexpr int f = F_SMEM > W_SMEM ? F_SMEM : W_SMEM;
+  return (BF && f > smem_bytes_general<BF>()) ? f : smem_bytes_general<BF>();
 }
 
 // The logical workgroup order keeps neighbouring query blocks of one head on
@@ -1302,12 +1524,14 @@ __device__ __forceinline__ int xcd_remap(int pid, int count) {
   return x * q + (x < rem ? x : rem) + idx;
 }
 
+// Band workgroups come first in dispatch order (they are the long ones);
+// global-row workgroups fill the gaps behind them.
 template <bool BF>
-__global__ __launch_bounds__(NT, 2) void attn_kernel(Params p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int bid = blockIdx.x;
-  if (bid < p.n_glob_wg) {
-    const int lg = bid;
+  if (bid >= p.n_band_wg) {
+    const int lg = bid - p.n_band_wg;
     if (lg >= p.B * p.H * p.nqg * p.nsplit) return;
     const int sp = lg % p.nsplit;
     int t = lg / p.nsplit;
@@ -1324,7 +1548,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(Params p) {
     }
     global_wg<BF>(p, b, h, qg, sp, smem);
   } else {
-    const int lb = xcd_remap(bid - p.n_glob_wg, p.n_band_wg);
+    const int lb = xcd_remap(bid, p.n_band_wg);
     const int b = lb / p.blocks_per_b;
     const int rem = lb - b * p.blocks_per_b;
     int h, local, s;

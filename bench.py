@@ -6,14 +6,23 @@ attention, global-row merge) over one batch of seeded synthetic input that is
 already resident in device memory.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload base]
-                  [--no-cpu-baseline]
+                  [--no-cpu-baseline] [--no-timing] [--copy-probe MIB]
 
 The default workload is "base": B=1, H=12, n=4096, d=64, w=512 (+-256), no
 dilation, one global token at position 0, bf16 storage, fp32 accumulation.
+
+Timing is "warm": forwards run back to back, so inputs that fit the 256 MB
+last-level cache stay there between steps.  Per-kernel durations come from
+HIP events that the library records on the stream the kernels run on.
+
+--copy-probe runs, after the timed loop, a plain device-to-device copy of the
+given size a few times; a counter pass over the same command then gives the
+ratio between what FETCH_SIZE / WRITE_SIZE report and the bytes a copy of
+known size must move.
 """
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -25,6 +34,9 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "window+global attn fwd tokens/s & TFLOP/s (% bf16 MFMA peak), n=4096 w=512"
+KERNEL_SOURCES = ("long_document_sparse_amd/csrc/kernels.hpp",
+                  "long_document_sparse_amd/csrc/lwattn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.txt")
 
 
 def describe(spec):
@@ -32,43 +44,77 @@ def describe(spec):
             ("at the start" if spec.global_mode == "first" else "at random positions"))
     pad = {"none": "no padding",
            "per_batch": f"padded tail U{{{spec.pad_lo}..{spec.pad_hi}}} per sequence",
-           "one_seq": f"one sequence with a padded tail U{{{spec.pad_lo}..{spec.pad_hi}}}"}[spec.pad_mode]
+           "one_seq": f"one sequence with a padded tail U{{{spec.pad_lo}..{spec.pad_hi}}}",
+           "scatter": f"U{{{spec.pad_lo}..{spec.pad_hi}}} padded positions anywhere"}[spec.pad_mode]
     dil = sorted(set(spec.dilation))
     return (f"{spec.name}: B={spec.B} H={spec.H} n={spec.n} d={spec.d} w={spec.window} "
             f"dilation {dil} {spec.dtype}; {glob}; {pad}")
 
 
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attn_kernel launch from the committed counter summary, or
+    None when there is none for this workload or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    want = source_hash()
+    for line in lines:
+        if not line.startswith("{"):
+            continue
+        rec = json.loads(line)
+        if rec.get("workload") == workload and rec.get("source_sha256") == want:
+            return rec
+    return None
+
+
 def cpu_baseline(x, budget_s=12.0):
-    """The oracle, as it is, on the host cores: a bounded sample of the workload."""
+    """The oracle, as it is, on the host cores over a bounded sample of the workload."""
     import numpy as np
     import oracle
     spec = x.spec
     threads = oracle.default_threads()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
     n, H, B = spec.n, spec.H, spec.B
     total_heads = B * H
+    args = (*x.tensors(), x.lmask, x.gmask, spec.window)
 
     def run_heads(k):
         rows = np.arange(k * n, dtype=np.int64)       # all rows of the first k (b, h) pairs
         t0 = time.perf_counter()
-        oracle.rows(*x.tensors(), x.lmask, x.gmask, spec.window, rows, spec.dilation,
-                    spec.scale, threads=threads)
+        oracle.rows(*args, rows, spec.dilation, spec.scale, threads=threads)
         return time.perf_counter() - t0
 
     t1 = run_heads(1)
-    k = int(max(1, min(total_heads, budget_s / max(t1, 1e-6))))
-    if k > 1:
-        t = run_heads(k)
+    if t1 * total_heads <= budget_s / 2:
+        # the whole forward is cheap: repeat it until the budget is used
+        reps, t = 0, 0.0
+        while t < budget_s:
+            t0 = time.perf_counter()
+            oracle.forward(*args, spec.dilation, spec.scale, threads=threads)
+            t += time.perf_counter() - t0
+            reps += 1
+        value = B * n * reps / t
+        sample = f"the whole forward, repeated {reps} times ({t:.2f} s)"
     else:
-        t = t1
-    t_full = t * total_heads / k
-    return {
-        "value": round(B * n / t_full, 3),
-        "unit": "tokens/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": (f"every query row of {k} of the {total_heads} (batch, head) pairs "
-                   f"({k * n} rows, {t:.2f} s), scaled to the full workload"),
-    }
+        k = int(max(1, min(total_heads, budget_s / max(t1, 1e-6))))
+        t = run_heads(k) if k > 1 else t1
+        value = B * n / (t * total_heads / k)
+        sample = (f"every query row of {k} of the {total_heads} (batch, head) pairs "
+                  f"({k * n} rows, {t:.2f} s), scaled to the full workload")
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample}
 
 
 def main():
@@ -80,10 +126,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel HIP events (roofline fields become null)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after timing, copy MIB MiB device to device 5 times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards over (batch, head) with no communication).", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported here "
+              "(the path would shard over (batch, head) pairs with no communication).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -100,7 +149,6 @@ def main():
     out = torch.empty_like(ts[0])
     plan = lwattn.Plan(spec.B, spec.H, spec.n, spec.d, spec.window, spec.dilation,
                        spec.max_global, spec.scale, spec.dtype)
-    stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
         plan(*ts, lm, gm, out=out)
@@ -120,6 +168,14 @@ def main():
     if st != lwattn.OK:
         raise SystemExit(f"forward failed: {lwattn.strerror(st)}")
 
+    if args.copy_probe > 0:
+        src = torch.empty(args.copy_probe << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     ms_step = elapsed * 1e3 / args.steps
     tokens = spec.B * spec.n
     value = tokens / (elapsed / args.steps)
@@ -133,12 +189,27 @@ def main():
         tot, calls = plan.timing_read()
         kernels = {k: round(v * 1e3 / calls, 3) for k, v in tot.items()}   # us per launch
         t_attn = tot["attention"] / calls * 1e-3                            # s per launch
-        achieved = flop / t_attn / 1e12
-        roofline = {"bound": "mfma", "kernel": "attn_kernel", "achieved": round(achieved, 2),
-                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                    "traffic": None,
-                    "algorithmic_flop": flop, "algorithmic_bytes": nbytes,
-                    "hbm_view_GBs": round(nbytes / t_attn / 1e9, 1)}
+        tflops = flop / t_attn / 1e12
+        gbs = nbytes / t_attn / 1e9
+        # the bound is the roof whose ideal time is longer at this arithmetic intensity
+        hbm_bound = nbytes / (PEAK_HBM_GBS * 1e9) > flop / (peak * 1e12)
+        tr = measured_traffic(spec.name)
+        traffic = tr["traffic_bytes"] if tr else None
+        if hbm_bound:
+            roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
+        else:
+            roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
+        roofline.update({
+            "kernel": "attn_kernel",
+            "algorithmic_flop": flop, "algorithmic_bytes": nbytes,
+            "mfma_view": {"achieved_tflops": round(tflops, 2), "peak": peak,
+                          "frac": round(tflops / peak, 4)},
+            "hbm_view": {"achieved_gbs": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)},
+            "source_sha256": source_hash(),
+        })
 
     res = {
         "metric": METRIC,
@@ -155,7 +226,7 @@ def main():
         "data": "synthetic (seeded, N(0,1)/sqrt(d) inputs; no dataset)",
         "config": {"workload": describe(spec), "global_batch": spec.B, "seq_len": spec.n,
                    "heads": spec.H, "head_dim": spec.d, "window": spec.window,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "timing": "warm (back to back)"},
         "tflops_per_s": round(flop / (elapsed / args.steps) / 1e12, 2),
         "pct_mfma_peak": round(100 * flop / (elapsed / args.steps) / 1e12 / peak, 2),
         "kernel_us": kernels,

@@ -47,7 +47,7 @@ namespace lwk {
 
 constexpr int D = 64;          // head dim (fixed)
 constexpr int KT = 32;         // keys per tile
-constexpr int NW = 2;          // waves per workgroup
+constexpr int NW = 4;          // waves per workgroup
 constexpr int NT = 64 * NW;    // threads per workgroup
 constexpr int ROWS_WG = 32 * NW;
 constexpr int MAXH_ARG = 32;   // per-head tables passed by value up to this many heads
@@ -81,6 +81,7 @@ struct Params {
   int32_t mask_vec;        // masks 16-byte aligned and n % 4 == 0
   int32_t uni_stride;      // > 0: every head has this stride
   int32_t blocks_per_head; // band workgroups of one head when uni_stride > 0
+  int32_t band_fast;       // band workgroups may take the bf16 fast path
   float c;                 // scale * log2(e)
   int32_t hs[MAXH_ARG];    // head_stride by value when H <= MAXH_ARG
   int32_t hb[MAXH_ARG + 1];
@@ -1141,19 +1142,36 @@ __device__ __forceinline__ void fpipe(int U, bool wave_work, InfoFn info, OffFn 
 }
 
 // ---------------------------------------------------------------------------
-// Fast band workgroup: NW x 32 query rows of one (batch, head, residue class)
-// against 64 keys per step, held as two 32-key halves in the tile layout
-// above (K halves at +0 / +4 KB, V halves at +8 KB / +12 KB of a 16 KB slot).
-// With two waves every wave needs the same 64-key tiles, so the workgroup
-// steps without skew; the halves give each step two independent MFMA and
-// softmax chains.  Keys reach LDS by buffer loads issued two steps ahead
-// into a ring of three slots.
-constexpr int W_SLOT = 16384;
-constexpr int W_NSLOT = 3;
-constexpr int W_GL_OFF = W_NSLOT * W_SLOT;
-constexpr int W_JR_OFF = W_GL_OFF + GL_MAX * 4;
-constexpr int W_SMEM = W_JR_OFF + GL_MAX * 4;
-constexpr int W_CH = 512 / NT;          // 16-byte chunks per thread per 8 KB array of a step
+// Band workgroups on the bf16 fast path (the real tokens of the batch row form
+// a prefix).  Each of the NW waves owns 32 query rows of a residue class; the
+// workgroup walks the union of their windows in steps of 64 subsequence keys
+// (two 32-key halves), then the global columns, 64 at a time.
+//
+// Per wave, a step u runs in two phases, each pairing the softmax of one half
+// on the VALU with eight MFMAs on the matrix cores, interleaved:
+//   phase A: softmax of half 0 of u  |  QK^T of half 1 of u, PV of half 1 of u-1
+//   phase B: softmax of half 1 of u  |  QK^T of half 0 of u+1, PV of half 0 of u
+// so every MFMA consumes results that were computed a phase earlier.  K and V
+// of a step go to LDS by buffer-to-LDS loads in two rings of four slots: the
+// batch issued at step u carries K of step u+3 and V of step u+2, and step u
+// waits for the batch of step u-2, so every load has two steps to land.
+//
+// Softmax bookkeeping: p = 2^(c*s - m) with a per-row offset m (log2 units)
+// that starts at the row's score against its own key.  Every local row attends
+// to itself, so its running sum is at least about 1 and cannot underflow; m
+// only moves when a half's probabilities of a row sum above SUM_HI, and then
+// jumps to the half's maximum while the accumulators are rescaled.  So the
+// common half computes no maximum at all, and every probability stays below
+// SUM_HI.
+constexpr int B_STEP = 8192;            // K (or V) of one step: keys 0-31 | keys 32-63
+constexpr int B_NSLOT = 4;
+constexpr int B_V_OFF = B_NSLOT * B_STEP;
+constexpr int B_GL_OFF = 2 * B_NSLOT * B_STEP;
+constexpr int B_JR_OFF = B_GL_OFF + GL_MAX * 4;
+constexpr int B_SMEM = B_JR_OFF + GL_MAX * 4;
+constexpr int B_CH = 512 / NT;          // 16-byte chunks per thread per 8 KB array of a step
+constexpr float SUM_HI = 16384.0f;      // 2^14
+static_assert(B_CH == 2, "each thread stages two chunks of every 8 KB array");
 
 // s_waitcnt vmcnt(N): at most N of this wave's loads outstanding.
 template <int N>
@@ -1162,46 +1180,99 @@ __device__ __forceinline__ void wait_loads() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Softmax over the two halves of a step (one running max per row).
-__device__ __forceinline__ void softmax2_bf16(Softmax& sm, const f32x16& sa, const f32x16& sb,
-                                              float c, bf16x8 (&pa)[2], bf16x8 (&pbb)[2]) {
-  float mx = max3f(sa[0], sa[1], sa[2]);
+// One 16-byte buffer load per lane into LDS at m0 = lds_base + IMM (lane l
+// writes m0 + 16 l).
+template <int IMM>
+__device__ __forceinline__ void dma16i(i32x4 desc, int voff, uint32_t lds_base) {
+  asm volatile(
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(desc), "s"(lds_base), "n"(IMM)
+      : "memory", "m0", "scc");
+}
+
+__device__ __forceinline__ int floordiv(int a, int b) {   // b > 0
+  return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+// Excluded scores become -inf: bit k of m (key k of a 32-key half) keeps
+// score k; this lane's registers hold keys 8(r/4) + 4h + r%4.
+__device__ __forceinline__ void mask_half(f32x16& sc, uint32_t m, int h32) {
+  const uint32_t m4 = m >> (4 * h32);
 #pragma unroll
-  for (int r = 3; r < 15; r += 2) mx = max3f(mx, sa[r], sa[r + 1]);
-  mx = max3f(mx, sa[15], sb[0]);
-#pragma unroll
-  for (int r = 1; r < 15; r += 2) mx = max3f(mx, sb[r], sb[r + 1]);
-  mx = max3f(mx, sb[15], sb[15]);
-  mx = half_max(mx);
-  const float mnew = fmaxf(sm.m, mx * c);
-  if (__any(mnew > sm.m + TAU)) {
-    const float alpha = __builtin_amdgcn_exp2f(sm.m - mnew);
-    sm.l *= alpha;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { sm.o[0][r] *= alpha; sm.o[1][r] *= alpha; }
-    sm.m = mnew;
+  for (int r = 0; r < 16; ++r) {
+    const int bit = 8 * (r >> 2) + (r & 3);
+    const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)m4, bit, 1);   // 0 or ~0
+    sc[r] = __uint_as_float((__float_as_uint(sc[r]) & keep) | (0xFF800000u & ~keep));
   }
+}
+
+struct BandRow {
+  f32x16 o[2];   // O^T accumulators: d = 32 db + 8 (r/4) + 4 h + r%4 of query lane%32
+  float m;       // offset of the exponent, log2 units (same in both half-lanes)
+  float l;       // this lane's share of the row sum
+};
+
+// Probabilities of one 32-key half (bf16, as PV multiplies them) and this
+// lane's share of their sum.
+__device__ __forceinline__ float band_exp_half(const f32x16& s, float c, float m, bf16x8 (&pb)[2]) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float acc_a = sm.l, acc_b = 0.f;
+  float acc = 0.f;
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      bf16x2 xa, xb;
-      xa[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sa[8 * c2 + e], c, -sm.m));
-      xa[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sa[8 * c2 + e + 1], c, -sm.m));
-      xb[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sb[8 * c2 + e], c, -sm.m));
-      xb[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sb[8 * c2 + e + 1], c, -sm.m));
-      pa[c2][e] = xa[0];
-      pa[c2][e + 1] = xa[1];
-      pbb[c2][e] = xb[0];
-      pbb[c2][e + 1] = xb[1];
-      acc_a = __builtin_amdgcn_fdot2_f32_bf16(xa, ones, acc_a, false);
-      acc_b = __builtin_amdgcn_fdot2_f32_bf16(xb, ones, acc_b, false);
+      bf16x2 x;
+      x[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e], c, -m));
+      x[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e + 1], c, -m));
+      pb[c2][e] = x[0];
+      pb[c2][e + 1] = x[1];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(x, ones, acc, false);
     }
   }
-  sm.l = acc_a + acc_b;
+  return acc;
+}
+
+// The rare half: some row's probabilities summed above SUM_HI.  Rows that
+// qualify move their offset to the half's maximum, rescale what they have
+// accumulated and recompute the half.
+__device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float c, bf16x8 (&pb)[2],
+                                            float& ts) {
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  mx = half_max(mx);
+  const float tsrow = half_sum(ts);     // both half-lanes of the row
+  float delta = 0.f;
+  if (mx != -INFINITY && tsrow > SUM_HI) delta = mx * c - st.m;
+  const float alpha = __builtin_amdgcn_exp2f(-delta);
+  st.l *= alpha;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { st.o[0][r] *= alpha; st.o[1][r] *= alpha; }
+  st.m += delta;
+  ts = band_exp_half(s, c, st.m, pb);
+}
+
+__device__ __forceinline__ bf16x8 vfrag(const uint8_t* vt, int off) {
+  const s16x4 lo = tr_read(vt + off);
+  const s16x4 hi = tr_read(vt + off + 1024);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Scheduling template for one phase: the 12 LDS reads that feed its MFMAs
+// first, softmax VALU work while they land, then the 8 MFMAs spaced by the
+// rest of the VALU work.
+__device__ __forceinline__ void interleave_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);   // VALU
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+  }
 }
 
 __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, int nv,
@@ -1220,67 +1291,131 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   const int R0 = local * ROWS_WG;
   const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
   const int nrv = nv > rho ? (nv - rho + s - 1) / s : 0;   // subsequence keys that are real tokens
-
-  // band tiles of 64 keys: tile t holds subsequence keys kb + 64t .. kb + 64t + 63
   const int r = p.r;
+
+  // band steps: step u holds subsequence keys kb0 + 64 u .. + 63
   const int kb = R0 - r;
   const int T = (ROWS_WG - 1 + 2 * r) / 64 + 1;
   const int t_lo = (-kb - 63 > 0) ? (-kb - 63 + 63) / 64 : 0;
-  int t_hi = (nr - 1 - kb) / 64;
+  int t_hi = nrv - 1 - kb >= 0 ? (nrv - 1 - kb) / 64 : -1;
   if (t_hi > T - 1) t_hi = T - 1;
-  const int nband = t_hi - t_lo + 1;
+  const int nband = R0 < nrv && t_hi >= t_lo ? t_hi - t_lo + 1 : 0;
   int g = p.gcnt[b];
   if (g > p.max_global) g = p.max_global;
   const int gmain = g < GL_MAX ? g : GL_MAX;
-  const int ngt = (gmain + 63) / 64;
+  const int ngt = R0 < nrv ? (gmain + 63) / 64 : 0;
   const int U = nband + ngt;
+  const int kb0 = kb + 64 * t_lo;
 
   const int R0w = R0 + 32 * wave;
   const int my_i = R0w + qi;
   const bool row_in = my_i < nr;
   const int my_pos = rho + (row_in ? my_i : 0) * s;
   const uint8_t my_fl = p.flags[(int64_t)b * n + my_pos];
-  QOp<true> qo;
-  qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
-  Softmax sm;
-  sm.init();
-  FLane fl;
-  fl.init(lane);
   const bool wave_work = __any(row_in && (my_fl & 3) == 1);
 
-  int32_t* gl = reinterpret_cast<int32_t*>(smem + W_GL_OFF);
-  int32_t* jr = reinterpret_cast<int32_t*>(smem + W_JR_OFF);
+  // this wave's band steps with any key of its windows [ua, ub], and those
+  // with every key inside all of its rows' windows [fa, fb]
+  const int lo_w = R0w - r > 0 ? R0w - r : 0;
+  const int hi_w = (R0w + 31 + r < nrv - 1) ? R0w + 31 + r : nrv - 1;
+  const int ua = wave_work ? floordiv(lo_w - kb0, 64) : 1 << 30;
+  const int ub = wave_work ? floordiv(hi_w - kb0, 64) : -1;
+  const int fl_lo = (R0w + 31 - r > 0) ? R0w + 31 - r : 0;
+  const int fl_hi = (R0w + r < nrv - 1) ? R0w + r : nrv - 1;
+  const int fa = floordiv(fl_lo - kb0 + 63, 64);
+  const int fb = floordiv(fl_hi - 63 - kb0, 64);
+  auto active = [&](int u) {
+    return u >= 0 && u < U && (u < nband ? (u >= ua && u <= ub) : (bool)wave_work);
+  };
+
+  QOp<true> qo;
+  qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
+  // Take Q out of the compiler's view of outstanding loads here: the loop
+  // below issues buffer-to-LDS loads the compiler does not count, so a wait it
+  // placed for Q inside the loop would also wait for those.
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
+  BandRow st;
+  {
+    // the row's own score sets the initial offset (this lane's 32 channels,
+    // then both half-lanes)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uint8_t* krow = p.K + (head + my_pos) * RB + 64 * h32;
+    float sd = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * cc);
+      const bf16x8 k8 = __builtin_bit_cast(bf16x8, kv);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 a = {qo.q[cc][e], qo.q[cc][e + 1]};
+        const bf16x2 bb = {k8[e], k8[e + 1]};
+        sd = __builtin_amdgcn_fdot2_f32_bf16(a, bb, sd, false);
+      }
+    }
+    st.m = half_sum(sd) * p.c;
+    asm volatile("" : "+v"(st.m));
+  }
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { st.o[0][i] = 0.f; st.o[1][i] = 0.f; }
+  FLane fl;
+  fl.init(lane);
+  const float c = p.c;
+
+  int32_t* gl = reinterpret_cast<int32_t*>(smem + B_GL_OFF);
+  int32_t* jr = reinterpret_cast<int32_t*>(smem + B_JR_OFF);
   const i32x4 dk = make_desc(p.K + head * RB, nv * RB);
   const i32x4 dv = make_desc(p.V + head * RB, nv * RB);
-  // thread tid stages chunks q = tid + NT*e of each 8 KB array: key row q/8 of
-  // the step (half q/256), physical chunk q%8
-  int ck16[W_CH], cv16[W_CH], srow[W_CH];
+  // thread (wave w, lane l) stages chunk q = (2 w + e) 64 + l of each 8 KB
+  // array: key row q / 8 of the step, physical chunk q % 8
+  int kbase[B_CH], vbase[B_CH];
+  const int step_b = 64 * s * RB;
+  auto chunk = [&](int e, int& srow, int& ck16, int& cv16) {
+    const int q = (B_CH * wave + e) * 64 + lane;
+    srow = q >> 3;
+    ck16 = ((q & 7) ^ swz_k(srow & 31)) * 16;
+    cv16 = ((q & 7) ^ swz_v(srow & 31)) * 16;
+  };
 #pragma unroll
-  for (int e = 0; e < W_CH; ++e) {
-    const int q = tid + NT * e;
-    srow[e] = q >> 3;
-    ck16[e] = ((q & 7) ^ swz_k(srow[e] & 31)) * 16;
-    cv16[e] = ((q & 7) ^ swz_v(srow[e] & 31)) * 16;
+  for (int e = 0; e < B_CH; ++e) {
+    int srow, ck16, cv16;
+    chunk(e, srow, ck16, cv16);
+    const int rowoff = (rho + (kb0 + srow) * s) * RB;
+    kbase[e] = rowoff + ck16;
+    vbase[e] = rowoff + cv16;
   }
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
-  const uint32_t lds0 =
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + wave * 1024;
-  auto issue = [&](int u) {
-    const uint32_t base = lds0 + (u % W_NSLOT) * W_SLOT;
+  const uint32_t lds_w = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) +
+                         wave * (B_CH * 1024);
+  // K (is_v false) or V of step t into its ring slot
+  auto issue = [&](int t, bool is_v) {
+    const uint32_t base = lds_w + (is_v ? B_V_OFF : 0) + (t % B_NSLOT) * B_STEP;
+    int off[B_CH];
+    if (t < nband) {
+      const int adv = t * step_b;
 #pragma unroll
-    for (int e = 0; e < W_CH; ++e) {
-      int rowoff;
-      bool in = true;
-      if (u < nband) {
-        rowoff = (rho + (kb + (t_lo + u) * 64 + srow[e]) * s) * RB;
-      } else {
-        const int idx = (u - nband) * 64 + srow[e];
-        in = idx < gmain;
-        rowoff = gl[in ? idx : 0] * RB;
+      for (int e = 0; e < B_CH; ++e) off[e] = (is_v ? vbase[e] : kbase[e]) + adv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < B_CH; ++e) {
+        int srow, ck16, cv16;
+        chunk(e, srow, ck16, cv16);
+        const int idx = (t - nband) * 64 + srow;
+        const bool in = idx < gmain;
+        const int rowoff = gl[in ? idx : 0] * RB;
+        off[e] = in ? rowoff + (is_v ? cv16 : ck16) : OOB_OFF;
       }
-      dma16(dk, in ? rowoff + ck16[e] : OOB_OFF, base + e * NT * 16);
-      dma16(dv, in ? rowoff + cv16[e] : OOB_OFF, base + 8192 + e * NT * 16);
     }
+    const i32x4 d = is_v ? dv : dk;
+    dma16i<0>(d, off[0], base);
+    dma16i<1024>(d, off[1], base);
+  };
+  // the batch of step t: K of step t+3 and V of step t+2 (those that exist);
+  // two loads per thread for each
+  auto batch = [&](int t) {
+    if (t + 3 < U) issue(t + 3, false);
+    if (t + 2 >= 0 && t + 2 < U) issue(t + 2, true);
   };
   auto fill = [&]() {
     for (int j = tid; j < gmain; j += NT) {
@@ -1290,90 +1425,177 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
       jr[j] = (dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
     }
   };
-  // the list must be in LDS before the first global-column tile is issued
-  const bool early_fill = nband < 2 && ngt > 0;
+  auto kslot = [&](int t) { return smem + (t % B_NSLOT) * B_STEP; };
+  auto vslot = [&](int t) { return smem + B_V_OFF + (t % B_NSLOT) * B_STEP; };
+  // QK^T of one half of a step; PV of one half of a step
+  auto qk_half = [&](f32x16& sx, const uint8_t* ks) {
+    f32x16 a = {};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+      a = mfma_bf16(*reinterpret_cast<const bf16x8*>(ks + fl.k[cc]), qo.q[cc], a);
+    sx = a;
+  };
+  auto pv_half = [&](const bf16x8 (&pb)[2], const uint8_t* vs) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        st.o[db] = mfma_bf16(vfrag(vs, fl.v[db] + c2 * 2048), pb[c2], st.o[db]);
+  };
+  // the MFMAs of a phase: QK^T of one half into sq and PV of one half, the
+  // two chains alternating so that no MFMA waits on the one just before it
+  auto phase_mfma = [&](f32x16& sq, const uint8_t* ks, const bf16x8 (&pp)[2], const uint8_t* vs) {
+    bf16x8 kf[4], vf[2][2];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(ks + fl.k[cc]);
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) vf[c2][db] = vfrag(vs, fl.v[db] + c2 * 2048);
+    f32x16 a = {};
+    a = mfma_bf16(kf[0], qo.q[0], a);
+    st.o[0] = mfma_bf16(vf[0][0], pp[0], st.o[0]);
+    a = mfma_bf16(kf[1], qo.q[1], a);
+    st.o[1] = mfma_bf16(vf[0][1], pp[0], st.o[1]);
+    a = mfma_bf16(kf[2], qo.q[2], a);
+    st.o[0] = mfma_bf16(vf[1][0], pp[1], st.o[0]);
+    a = mfma_bf16(kf[3], qo.q[3], a);
+    st.o[1] = mfma_bf16(vf[1][1], pp[1], st.o[1]);
+    sq = a;
+  };
+  auto mask_of = [&](int u, int hf) {
+    uint32_t m;
+    if (u < nband) {
+      const int j0 = kb0 + 64 * u + 32 * hf;
+      m = bit_range(-j0, nrv - j0) & bit_range_v(my_i - r - j0, my_i + r - j0 + 1);
+    } else {
+      FTile ti;
+      ti.act = true;
+      ti.kind = 2;
+      ti.j0 = (u - nband) * 64 + 32 * hf;
+      ti.okb = bit_range(0, gmain - ti.j0);
+      m = lane_mask(ti, my_i, r, jr + ti.j0, lane);
+    }
+    return m;
+  };
+  auto soft_half = [&](f32x16& sx, bf16x8 (&pb)[2]) {
+    float ts = band_exp_half(sx, c, st.m, pb);
+    if (__builtin_expect(__any(ts > SUM_HI), 0))
+      band_rebase(st, sx, c, pb, ts);
+    st.l += ts;
+  };
+
+  // prologue: the batches of steps -3, -2, -1 (K of 0, 1, 2; V of 0, 1) in
+  // flight, K of step 0 resident
+  const bool early_fill = nband < B_NSLOT - 1 && ngt > 0;
   if (early_fill) {
     fill();
     __syncthreads();
   }
-  issue(0);
-  if (U > 1) issue(1);
+  batch(-3);
+  batch(-2);
+  batch(-1);
   if (!early_fill) fill();
-  if (U > 1)
-    wait_loads<2 * W_CH>();   // tile 0 landed (tile 1's 2*W_CH loads may still fly)
-  else
-    wait_loads<0>();
+  {
+    const int later = 2 * ((1 < U) + (0 < U) + (2 < U) + (1 < U));   // loads of batches -2, -1
+    if (later >= 8)
+      wait_loads<8>();
+    else if (later >= 6)
+      wait_loads<6>();
+    else if (later >= 4)
+      wait_loads<4>();
+    else if (later >= 2)
+      wait_loads<2>();
+    else
+      wait_loads<0>();
+  }
   __syncthreads();
 
-  for (int u = 0; u < U; ++u) {
-    if (u + 2 < U) issue(u + 2);
-    const uint8_t* sl = smem + (u % W_NSLOT) * W_SLOT;
-    if (wave_work) {
-      // per-half masks (wave-uniform)
-      int kind[2], j0[2];
-      uint32_t okb[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        if (u < nband) {
-          j0[hf] = kb + (t_lo + u) * 64 + 32 * hf;
-          okb[hf] = bit_range(-j0[hf], nrv - j0[hf]);
-          const bool inside = j0[hf] >= R0w + 31 - r && j0[hf] + 31 <= R0w + r;
-          kind[hf] = (inside && okb[hf] == 0xFFFFFFFFu) ? 0 : 1;
-        } else {
-          j0[hf] = (u - nband) * 64 + 32 * hf;
-          okb[hf] = bit_range(0, gmain - j0[hf]);
-          kind[hf] = 2;
-        }
-      }
-      // QK^T of both halves, chains interleaved
-      f32x16 sa = {}, sb = {};
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        sa = mfma_bf16(*reinterpret_cast<const bf16x8*>(sl + fl.k[cc]), qo.q[cc], sa);
-        sb = mfma_bf16(*reinterpret_cast<const bf16x8*>(sl + 4096 + fl.k[cc]), qo.q[cc], sb);
-      }
-      if (kind[0] != 0) {
-        FTile ti;
-        ti.act = true; ti.kind = kind[0]; ti.okb = okb[0]; ti.j0 = j0[0];
-        apply_mask(sa, lane_mask(ti, my_i, r, jr + (kind[0] == 2 ? j0[0] : 0), lane), lane);
-      }
-      if (kind[1] != 0) {
-        FTile ti;
-        ti.act = true; ti.kind = kind[1]; ti.okb = okb[1]; ti.j0 = j0[1];
-        apply_mask(sb, lane_mask(ti, my_i, r, jr + (kind[1] == 2 ? j0[1] : 0), lane), lane);
-      }
-      bf16x8 pa[2], pbb[2];
-      softmax2_bf16(sm, sa, sb, p.c, pa, pbb);
-      // PV of both halves, alternating accumulators
-      const uint8_t* va = sl + 8192;
-      const uint8_t* vb = sl + 8192 + 4096;
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const s16x4 lo = tr_read(va + fl.v[db] + c2 * 2048);
-          const s16x4 hi = tr_read(va + fl.v[db] + c2 * 2048 + 1024);
-          sm.o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
-                               pa[c2], sm.o[db]);
-        }
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const s16x4 lo = tr_read(vb + fl.v[db] + c2 * 2048);
-          const s16x4 hi = tr_read(vb + fl.v[db] + c2 * 2048 + 1024);
-          sm.o[db] = mfma_bf16(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
-                               pbb[c2], sm.o[db]);
-        }
-      }
-    }
-    if (u + 2 < U)
-      wait_loads<2 * W_CH>();   // tile u+1 landed; tile u+2 may still fly
+  f32x16 sx, sy;           // the two halves of the step being softmaxed
+  bf16x8 pa[2], pb[2];     // probabilities of half 0 / half 1
+  if (active(0)) qk_half(sx, kslot(0));
+
+  // steps [P0, P1] need no branch: this wave is active in them and in their
+  // neighbours, and their keys lie inside every window of the wave
+  int P0 = ua + 1 > fa ? ua + 1 : fa;
+  if (P0 < 1) P0 = 1;
+  int P1 = ub - 1 < fb ? ub - 1 : fb;
+  if (P1 > nband - 2) P1 = nband - 2;
+  if (P1 > U - 2) P1 = U - 2;   // when P1 < P0 the middle loop below runs no step
+
+  auto head_of_step = [&](int u) {
+    // the batch of step u-2 (K of u+1, V of u) has landed everywhere; the
+    // slots the batch of step u overwrites were last read in step u-1
+    const int later = 2 * ((u + 2 < U) + (u + 1 < U));   // loads of batch u-1
+    if (later == 4)
+      wait_loads<4>();
+    else if (later == 2)
+      wait_loads<2>();
     else
       wait_loads<0>();
     __syncthreads();
+    batch(u);
+  };
+  auto slow_step = [&](int u) {
+    head_of_step(u);
+    const uint8_t* kc = kslot(u);
+    const uint8_t* kn = kslot(u + 1);
+    const uint8_t* vp = vslot(u + B_NSLOT - 1);
+    const uint8_t* vc = vslot(u);
+    const bool a_prev = active(u - 1), a_cur = active(u), a_next = active(u + 1);
+    const bool masked = u < fa || u > fb || u >= nband;
+    // phase A
+    if (a_cur && masked) mask_half(sx, mask_of(u, 0), h32);
+    if (a_cur) qk_half(sy, kc + 4096);
+    if (a_prev) pv_half(pb, vp + 4096);
+    if (a_cur) soft_half(sx, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase B
+    if (a_cur && masked) mask_half(sy, mask_of(u, 1), h32);
+    if (a_next) qk_half(sx, kn);
+    if (a_cur) pv_half(pa, vc);
+    if (a_cur) soft_half(sy, pb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int u = 0;
+  for (; u < P0 && u < U; ++u) slow_step(u);
+  for (; u <= P1; ++u) {
+    head_of_step(u);
+    const uint8_t* kc = kslot(u);
+    const uint8_t* kn = kslot(u + 1);
+    const uint8_t* vp = vslot(u + B_NSLOT - 1);
+    const uint8_t* vc = vslot(u);
+    // phase A
+    phase_mfma(sy, kc + 4096, pb, vp + 4096);
+    {
+      float ts = band_exp_half(sx, c, st.m, pa);
+      interleave_hint();
+      if (__builtin_expect(__any(ts > SUM_HI), 0))
+        band_rebase(st, sx, c, pa, ts);
+      st.l += ts;
+    }
+    // phase B
+    phase_mfma(sx, kn, pa, vc);
+    {
+      float ts = band_exp_half(sy, c, st.m, pb);
+      interleave_hint();
+      if (__builtin_expect(__any(ts > SUM_HI), 0))
+        band_rebase(st, sy, c, pb, ts);
+      st.l += ts;
+    }
   }
+  for (; u < U; ++u) slow_step(u);
+  // PV of half 1 of the last step (its V landed with the batch of step U-3)
+  if (active(U - 1)) pv_half(pb, vslot(U - 1) + 4096);
 
-  if (g > GL_MAX) {
-    // global columns past the LDS copy, 32 at a time through the first slot
+  if (g > GL_MAX && R0 < nrv) {
+    // global columns past the LDS copy, 32 at a time through the first K and
+    // V slots (the older Softmax helpers keep the same offset convention)
+    Softmax sm;
+    sm.m = st.m;
+    sm.l = st.l;
+    sm.o[0] = st.o[0];
+    sm.o[1] = st.o[1];
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * RB, nv * RB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * RB, nv * RB);
     const int U2 = (g - GL_MAX + KT - 1) / KT;
@@ -1388,15 +1610,13 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
         jr[j] = (idx < g && dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
       }
       __syncthreads();
-#pragma unroll
-      for (int e = 0; e < W_CH / 2; ++e) {
-        const int q = tid + NT * e;            // chunk of the 32-key tile
+      for (int q = tid; q < 256; q += NT) {     // chunk of the 32-key tile
         const int row = q >> 3;
         const bool in = jb + row < g;
         const int rowoff = gl[row] * RB;
         const int k16 = ((q & 7) ^ swz_k(row)) * 16, v16 = ((q & 7) ^ swz_v(row)) * 16;
         *reinterpret_cast<uint4*>(smem + q * 16) = bload(rk, in ? rowoff + k16 : OOB_OFF);
-        *reinterpret_cast<uint4*>(smem + 8192 + q * 16) = bload(rv, in ? rowoff + v16 : OOB_OFF);
+        *reinterpret_cast<uint4*>(smem + B_V_OFF + q * 16) = bload(rv, in ? rowoff + v16 : OOB_OFF);
       }
       __syncthreads();
       if (wave_work) {
@@ -1407,16 +1627,20 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
         ti.j0 = 0;
         f32x16 sc = fqk(qo, smem, fl);
         apply_mask(sc, lane_mask(ti, my_i, r, jr, lane), lane);
-        bf16x8 pb[2];
-        softmax_bf16(sm, sc, p.c, pb);
-        fpv(sm.o, pb, smem + 8192, fl);
+        bf16x8 pq[2];
+        softmax_bf16(sm, sc, c, pq);
+        fpv(sm.o, pq, smem + B_V_OFF, fl);
       }
     }
+    st.m = sm.m;
+    st.l = sm.l;
+    st.o[0] = sm.o[0];
+    st.o[1] = sm.o[1];
   }
 
   // normalise and store (global rows are written by the merge kernel, padded
   // rows get exact zeros)
-  const float lt = sm.l + __shfl_xor(sm.l, 32);
+  const float lt = half_sum(st.l);
   if (row_in && (my_fl & 2) == 0) {
     const bool valid = (my_fl & 1) != 0;
     const float inv = valid ? 1.0f / lt : 0.0f;
@@ -1427,7 +1651,7 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
       for (int a = 0; a < 4; ++a) {
         float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = valid ? sm.o[db][4 * a + e] * inv : 0.0f;
+        for (int e = 0; e < 4; ++e) v[e] = valid ? st.o[db][4 * a + e] * inv : 0.0f;
         store_row4<true>(orow + (32 * db + 8 * a + 4 * h32) * 2, v);
       }
     }
@@ -1511,7 +1735,7 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
 
 template <bool BF>
 constexpr int smem_bytes() {
-  constexpr int f = F_SMEM > W_SMEM ? F_SMEM : W_SMEM;
+  constexpr int f = F_SMEM > B_SMEM ? F_SMEM : B_SMEM;
   return (BF && f > smem_bytes_general<BF>()) ? f : smem_bytes_general<BF>();
 }
 
@@ -1569,7 +1793,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
     if constexpr (BF) {
       const int nv = p.vlen[b];
-      if (nv >= 0) {
+      if (nv >= 0 && p.band_fast) {
         band_wg_fast(p, b, h, local, s, nv, smem);
         return;
       }

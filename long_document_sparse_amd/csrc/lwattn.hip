@@ -42,6 +42,7 @@ struct lwattn_plan_s {
   int nqt = 0, nqg = 0, nsplit = 0, ksplit = 0;
   int n_glob_wg = 0, n_band_wg = 0, blocks_per_b = 0;
   int uni_stride = 0, blocks_per_head = 0;
+  int band_fast = 0;
   std::vector<int32_t> stride_host, blk_host;
   size_t smem = 0;
   // workspace
@@ -152,13 +153,29 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   p->uni_stride = uni ? stride[0] : 0;
   p->blocks_per_head = uni ? blk[1] : 0;
   const int64_t nband = (int64_t)B * blk[H];
-  // global-row geometry
+  // band workgroups may take the bf16 fast path when every subsequence key
+  // they stage has a byte offset that fits in 32 bits
+  int smax = 1;
+  for (int h = 0; h < H; ++h) smax = std::max(smax, stride[h]);
+  p->band_fast = (cfg->dtype == LWATTN_BF16 && (int64_t)n + 128 * (int64_t)smax < ((int64_t)1 << 24)) ? 1 : 0;
+  // global-row geometry: the key slices are sized so that the global-row
+  // workgroups fill what the band workgroups leave of the last round of
+  // workgroup slots (two per compute unit), with at least 64 of them
+  int ncu = 256;
+  {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, hip_device) == hipSuccess && prop.multiProcessorCount > 0)
+      ncu = prop.multiProcessorCount;
+  }
+  const int64_t slots = 2 * (int64_t)ncu;
   p->nqt = ceil_div(cfg->max_global, 32);
   p->nqg = ceil_div(p->nqt, lwk::NW);
   int64_t nglob = 0;
   if (p->nqt > 0 && n > 0 && B > 0 && H > 0) {
     const int64_t units = (int64_t)B * H * p->nqg;
-    int64_t want = (512 + units - 1) / units;
+    int64_t target = slots - nband % slots;
+    if (target < 64) target = 64;
+    int64_t want = (target + units - 1) / units;
     const int64_t maxs = (n + 127) / 128;
     if (want > maxs) want = maxs;
     if (want < 1) want = 1;
@@ -264,6 +281,7 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   prm.mask_vec = ((((uintptr_t)lmask | (uintptr_t)gmask) & 15u) == 0 && (c.n % 4) == 0) ? 1 : 0;
   prm.uni_stride = p->uni_stride;
   prm.blocks_per_head = p->blocks_per_head;
+  prm.band_fast = p->band_fast;
   for (int h = 0; h < lwk::MAXH_ARG; ++h) prm.hs[h] = h < c.H ? p->stride_host[h] : 0;
   for (int h = 0; h <= lwk::MAXH_ARG; ++h) prm.hb[h] = h <= c.H ? p->blk_host[h] : 0;
 

@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the Longformer window + global attention forward on one MI355X.
 
-One step = one lwattn_forward (global-index compaction, band + global-row
-attention, global-row merge) over one batch of seeded synthetic input that is
+One step = one lwattn_forward (global-index compaction, then the attention
+kernel: band rows, global rows and the merge of their key slices) over one
+batch of seeded synthetic input that is
 already resident in device memory.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload base]

@@ -133,8 +133,8 @@ lwattn_status lwattn_sync_status(lwattn_plan_t plan, hipStream_t stream);
  * forwards are kept).  lwattn_timing_read synchronizes on the recorded events
  * and returns, per kernel of the forward, the summed duration in milliseconds
  * (ms[k] for k < *nkernels, at most `cap`) and the number of recorded forwards.
- * Kernel order: 0 = global-index compaction, 1 = attention (local and global
- * rows), 2 = global-row merge. */
+ * Kernel order: 0 = global-index compaction, 1 = attention (local rows, and
+ * global rows including the merge of their key slices). */
 lwattn_status lwattn_timing_enable(lwattn_plan_t plan, int32_t max_calls);
 lwattn_status lwattn_timing_read(lwattn_plan_t plan, float* ms, int32_t cap,
                                  int32_t* nkernels, int32_t* ncalls);

@@ -71,6 +71,7 @@ struct Params {
   int32_t* vlen;           // [B]: number of real tokens if they form a prefix, else -1
   float* part_o;           // [B][H][nqt][nsplit][32][64]
   float* part_ml;          // [B][H][nqt][nsplit][32][2]
+  int32_t* tile_cnt;       // [B][H][nqt]: finished key slices of a query tile (0 between forwards)
   const int32_t* head_stride;  // [H]: dilation gap + 1 (device copy, any H)
   const int32_t* head_blk;     // [H+1]: prefix of band workgroups per batch row
   int32_t B, H, n, r;      // r = min(window/2, n)
@@ -718,6 +719,76 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
   }
 }
 
+// Global-row merge, fused into the attention kernel.  Every (b, h, query
+// tile) has a counter of finished key slices; the wave that finishes the last
+// slice of a tile combines the nsplit partial results of its 32 rows (the
+// log-sum-exp merge of split softmax) and writes them, then re-arms the
+// counter for the next forward.  Lane l merges row l % 32, channels
+// 32 (l / 32) .. +31.
+template <bool BF>
+__device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g, int lane) {
+  __threadfence();                                   // this slice's partial rows are visible
+  int32_t* cnt = p.tile_cnt + ((int64_t)b * p.H + h) * p.nqt + qt;
+  int old = 0;
+  if (lane == 0) old = atomicAdd(cnt, 1);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old != p.nsplit - 1) return;
+  __threadfence();                                   // every slice's partial rows are visible
+  const int q = lane & 31, ch = lane >> 5;
+  const int idx = qt * 32 + q;
+  if (idx < g) {
+    const int64_t base = (((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit;
+    const int ns = p.nsplit;
+    constexpr int U1 = 16, U2 = 4;
+    float mstar = -INFINITY;
+    for (int s0 = 0; s0 < ns; s0 += U1) {
+      float mv[U1];
+#pragma unroll
+      for (int e = 0; e < U1; ++e)
+        mv[e] = (s0 + e < ns) ? __builtin_nontemporal_load(p.part_ml + ((base + s0 + e) * 32 + q) * 2) : -INFINITY;
+#pragma unroll
+      for (int e = 0; e < U1; ++e) mstar = fmaxf(mstar, mv[e]);
+    }
+    float L = 0.f, acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += U2) {
+      float2 ml[U2];
+      float4 o[U2][8];
+#pragma unroll
+      for (int e = 0; e < U2; ++e) {
+        const bool in = s0 + e < ns;
+        const int64_t pi = (base + (in ? s0 + e : s0)) * 32 + q;
+        ml[e] = *reinterpret_cast<const float2*>(p.part_ml + pi * 2);
+        if (!in) ml[e] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[e][k] = *reinterpret_cast<const float4*>(p.part_o + pi * D + 32 * ch + 4 * k);
+      }
+#pragma unroll
+      for (int e = 0; e < U2; ++e) {
+        const float w = __builtin_amdgcn_exp2f(ml[e].x - mstar);
+        L += w * ml[e].y;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          acc[4 * k + 0] += w * o[e][k].x;
+          acc[4 * k + 1] += w * o[e][k].y;
+          acc[4 * k + 2] += w * o[e][k].z;
+          acc[4 * k + 3] += w * o[e][k].w;
+        }
+      }
+    }
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] *= inv;
+    constexpr int RB = D * Lay<BF>::ELT;
+    const int pos = p.gidx[(int64_t)b * p.n + idx];
+    uint8_t* orow = p.O + (((int64_t)b * p.H + h) * p.n + pos) * RB + 32 * ch * Lay<BF>::ELT;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) store_row4<BF>(orow + 4 * k * Lay<BF>::ELT, acc + 4 * k);
+  }
+  if (lane == 0) *cnt = 0;
+}
+
 template <bool BF>
 __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t* smem) {
   constexpr int RB = D * Lay<BF>::ELT;
@@ -782,6 +853,7 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
       p.part_ml[pidx * 2 + 1] = lt;
     }
   }
+  if (wave_work) finish_global_tile<BF>(p, b, h, qt, g, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1213,6 +1285,7 @@ struct BandRow {
   f32x16 o[2];   // O^T accumulators: d = 32 db + 8 (r/4) + 4 h + r%4 of query lane%32
   float m;       // offset of the exponent, log2 units (same in both half-lanes)
   float l;       // this lane's share of the row sum
+  bool first;    // the offset is still to be set from the first half with a live key
 };
 
 // Probabilities of one 32-key half (bf16, as PV multiplies them) and this
@@ -1236,9 +1309,9 @@ __device__ __forceinline__ float band_exp_half(const f32x16& s, float c, float m
   return acc;
 }
 
-// The rare half: some row's probabilities summed above SUM_HI.  Rows that
-// qualify move their offset to the half's maximum, rescale what they have
-// accumulated and recompute the half.
+// The rare half: some row's probabilities summed above SUM_HI, or a row's
+// offset is still unset.  Such rows move their offset to the half's maximum,
+// rescale what they have accumulated and recompute the half.
 __device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float c, bf16x8 (&pb)[2],
                                             float& ts) {
   float mx = s[0];
@@ -1247,8 +1320,11 @@ __device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float 
   mx = half_max(mx);
   const float tsrow = half_sum(ts);     // both half-lanes of the row
   float delta = 0.f;
-  if (mx != -INFINITY && tsrow > SUM_HI) delta = mx * c - st.m;
-  const float alpha = __builtin_amdgcn_exp2f(-delta);
+  const bool live = mx != -INFINITY;
+  if (live && (tsrow > SUM_HI || st.first)) delta = mx * c - st.m;
+  // nothing has been accumulated while the offset is unset
+  const float alpha = st.first ? 1.0f : __builtin_amdgcn_exp2f(-delta);
+  st.first = st.first && !live;
   st.l *= alpha;
 #pragma unroll
   for (int r = 0; r < 16; ++r) { st.o[0][r] *= alpha; st.o[1][r] *= alpha; }
@@ -1273,6 +1349,170 @@ __device__ __forceinline__ void interleave_hint() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
   }
+}
+
+// Where thread (wave w, lane l) stages its two 16-byte chunks q = (2 w + e) 64
+// + l of each 8 KB array of a step: key row q / 8, physical chunk q % 8, the
+// logical chunk that sits there (K and V swizzles).
+__device__ __forceinline__ void stage_chunk(int wave, int lane, int e, int& srow, int& ck16, int& cv16) {
+  const int q = (B_CH * wave + e) * 64 + lane;
+  srow = q >> 3;
+  ck16 = ((q & 7) ^ swz_k(srow & 31)) * 16;
+  cv16 = ((q & 7) ^ swz_v(srow & 31)) * 16;
+}
+
+// The half-step pipeline over U steps of 64 keys, shared by band and global
+// workgroups.  Policy callbacks:
+//   issue(t, is_v)  stage K (is_v false) or V of step t into its ring slot
+//   active(u)       this wave computes on step u
+//   masked(u)       step u needs a per-row key mask; mask_of(u, hf) is this
+//                   lane's allowed keys of half hf (bit k = key k)
+//   pre()           runs while the prologue loads are in flight
+// P0..P1 are the steps that need no branch: the wave is active in them and in
+// both neighbours, and no key is masked.
+template <class Issue, class Active, class Masked, class MaskOf, class Pre>
+__device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& issue,
+                                          const Active& active, const Masked& masked,
+                                          const MaskOf& mask_of, const Pre& pre, const QOp<true>& qo,
+                                          const FLane& fl, BandRow& st, float c, int h32,
+                                          uint8_t* smem) {
+  // the batch of step t: K of step t+3 and V of step t+2 (those that exist);
+  // two loads per thread for each
+  auto batch = [&](int t) {
+    if (t + 3 < U) issue(t + 3, false);
+    if (t + 2 >= 0 && t + 2 < U) issue(t + 2, true);
+  };
+  auto kslot = [&](int t) { return smem + (t % B_NSLOT) * B_STEP; };
+  auto vslot = [&](int t) { return smem + B_V_OFF + (t % B_NSLOT) * B_STEP; };
+  // QK^T of one half of a step; PV of one half of a step
+  auto qk_half = [&](f32x16& sx, const uint8_t* ks) {
+    f32x16 a = {};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+      a = mfma_bf16(*reinterpret_cast<const bf16x8*>(ks + fl.k[cc]), qo.q[cc], a);
+    sx = a;
+  };
+  auto pv_half = [&](const bf16x8 (&pb)[2], const uint8_t* vs) {
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        st.o[db] = mfma_bf16(vfrag(vs, fl.v[db] + c2 * 2048), pb[c2], st.o[db]);
+  };
+  // the MFMAs of a phase: QK^T of one half into sq and PV of one half, the
+  // two chains alternating so that no MFMA waits on the one just before it
+  auto phase_mfma = [&](f32x16& sq, const uint8_t* ks, const bf16x8 (&pp)[2], const uint8_t* vs) {
+    bf16x8 kf[4], vf[2][2];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(ks + fl.k[cc]);
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) vf[c2][db] = vfrag(vs, fl.v[db] + c2 * 2048);
+    f32x16 a = {};
+    a = mfma_bf16(kf[0], qo.q[0], a);
+    st.o[0] = mfma_bf16(vf[0][0], pp[0], st.o[0]);
+    a = mfma_bf16(kf[1], qo.q[1], a);
+    st.o[1] = mfma_bf16(vf[0][1], pp[0], st.o[1]);
+    a = mfma_bf16(kf[2], qo.q[2], a);
+    st.o[0] = mfma_bf16(vf[1][0], pp[1], st.o[0]);
+    a = mfma_bf16(kf[3], qo.q[3], a);
+    st.o[1] = mfma_bf16(vf[1][1], pp[1], st.o[1]);
+    sq = a;
+  };
+  auto soft_half = [&](f32x16& sx, bf16x8 (&pb)[2]) {
+    float ts = band_exp_half(sx, c, st.m, pb);
+    if (__builtin_expect(__any(ts > SUM_HI || st.first), 0)) band_rebase(st, sx, c, pb, ts);
+    st.l += ts;
+  };
+
+  // prologue: the batches of steps -3, -2, -1 (K of 0, 1, 2; V of 0, 1) in
+  // flight, K of step 0 resident
+  batch(-3);
+  batch(-2);
+  batch(-1);
+  pre();
+  {
+    const int later = 2 * ((1 < U) + (0 < U) + (2 < U) + (1 < U));   // loads of batches -2, -1
+    if (later >= 8)
+      wait_loads<8>();
+    else if (later >= 6)
+      wait_loads<6>();
+    else if (later >= 4)
+      wait_loads<4>();
+    else if (later >= 2)
+      wait_loads<2>();
+    else
+      wait_loads<0>();
+  }
+  __syncthreads();
+
+  f32x16 sx, sy;           // the two halves of the step being softmaxed
+  bf16x8 pa[2], pb[2];     // probabilities of half 0 / half 1
+  if (active(0)) qk_half(sx, kslot(0));
+
+  auto head_of_step = [&](int u) {
+    // the batch of step u-2 (K of u+1, V of u) has landed everywhere; the
+    // slots the batch of step u overwrites were last read in step u-1
+    const int later = 2 * ((u + 2 < U) + (u + 1 < U));   // loads of batch u-1
+    if (later == 4)
+      wait_loads<4>();
+    else if (later == 2)
+      wait_loads<2>();
+    else
+      wait_loads<0>();
+    __syncthreads();
+    batch(u);
+  };
+  auto slow_step = [&](int u) {
+    head_of_step(u);
+    const uint8_t* kc = kslot(u);
+    const uint8_t* kn = kslot(u + 1);
+    const uint8_t* vp = vslot(u + B_NSLOT - 1);
+    const uint8_t* vc = vslot(u);
+    const bool a_prev = active(u - 1), a_cur = active(u), a_next = active(u + 1);
+    const bool msk = masked(u);
+    // phase A
+    if (a_cur && msk) mask_half(sx, mask_of(u, 0), h32);
+    if (a_cur) qk_half(sy, kc + 4096);
+    if (a_prev) pv_half(pb, vp + 4096);
+    if (a_cur) soft_half(sx, pa);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase B
+    if (a_cur && msk) mask_half(sy, mask_of(u, 1), h32);
+    if (a_next) qk_half(sx, kn);
+    if (a_cur) pv_half(pa, vc);
+    if (a_cur) soft_half(sy, pb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int u = 0;
+  for (; u < P0 && u < U; ++u) slow_step(u);
+  for (; u <= P1; ++u) {   // runs no step when P1 < P0
+    head_of_step(u);
+    const uint8_t* kc = kslot(u);
+    const uint8_t* kn = kslot(u + 1);
+    const uint8_t* vp = vslot(u + B_NSLOT - 1);
+    const uint8_t* vc = vslot(u);
+    // phase A
+    phase_mfma(sy, kc + 4096, pb, vp + 4096);
+    {
+      float ts = band_exp_half(sx, c, st.m, pa);
+      interleave_hint();
+      if (__builtin_expect(__any(ts > SUM_HI), 0)) band_rebase(st, sx, c, pa, ts);
+      st.l += ts;
+    }
+    // phase B
+    phase_mfma(sx, kn, pa, vc);
+    {
+      float ts = band_exp_half(sy, c, st.m, pb);
+      interleave_hint();
+      if (__builtin_expect(__any(ts > SUM_HI), 0)) band_rebase(st, sy, c, pb, ts);
+      st.l += ts;
+    }
+  }
+  for (; u < U; ++u) slow_step(u);
+  // PV of half 1 of the last step (its V landed with the batch of step U-3)
+  if (active(U - 1)) pv_half(pb, vslot(U - 1) + 4096);
 }
 
 __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, int nv,
@@ -1327,6 +1567,14 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   auto active = [&](int u) {
     return u >= 0 && u < U && (u < nband ? (u >= ua && u <= ub) : (bool)wave_work);
   };
+  auto masked = [&](int u) { return u < fa || u > fb || u >= nband; };
+  // steps [P0, P1] need no branch: this wave is active in them and in their
+  // neighbours, and their keys lie inside every window of the wave
+  int P0 = ua + 1 > fa ? ua + 1 : fa;
+  if (P0 < 1) P0 = 1;
+  int P1 = ub - 1 < fb ? ub - 1 : fb;
+  if (P1 > nband - 2) P1 = nband - 2;
+  if (P1 > U - 2) P1 = U - 2;
 
   QOp<true> qo;
   qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
@@ -1357,6 +1605,7 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     asm volatile("" : "+v"(st.m));
   }
   st.l = 0.f;
+  st.first = false;
 #pragma unroll
   for (int i = 0; i < 16; ++i) { st.o[0][i] = 0.f; st.o[1][i] = 0.f; }
   FLane fl;
@@ -1367,20 +1616,12 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   int32_t* jr = reinterpret_cast<int32_t*>(smem + B_JR_OFF);
   const i32x4 dk = make_desc(p.K + head * RB, nv * RB);
   const i32x4 dv = make_desc(p.V + head * RB, nv * RB);
-  // thread (wave w, lane l) stages chunk q = (2 w + e) 64 + l of each 8 KB
-  // array: key row q / 8 of the step, physical chunk q % 8
   int kbase[B_CH], vbase[B_CH];
   const int step_b = 64 * s * RB;
-  auto chunk = [&](int e, int& srow, int& ck16, int& cv16) {
-    const int q = (B_CH * wave + e) * 64 + lane;
-    srow = q >> 3;
-    ck16 = ((q & 7) ^ swz_k(srow & 31)) * 16;
-    cv16 = ((q & 7) ^ swz_v(srow & 31)) * 16;
-  };
 #pragma unroll
   for (int e = 0; e < B_CH; ++e) {
     int srow, ck16, cv16;
-    chunk(e, srow, ck16, cv16);
+    stage_chunk(wave, lane, e, srow, ck16, cv16);
     const int rowoff = (rho + (kb0 + srow) * s) * RB;
     kbase[e] = rowoff + ck16;
     vbase[e] = rowoff + cv16;
@@ -1388,7 +1629,8 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
   const uint32_t lds_w = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) +
                          wave * (B_CH * 1024);
-  // K (is_v false) or V of step t into its ring slot
+  // K (is_v false) or V of step t into its ring slot: band steps are strided
+  // subsequence rows, global steps the listed global positions
   auto issue = [&](int t, bool is_v) {
     const uint32_t base = lds_w + (is_v ? B_V_OFF : 0) + (t % B_NSLOT) * B_STEP;
     int off[B_CH];
@@ -1400,7 +1642,7 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
 #pragma unroll
       for (int e = 0; e < B_CH; ++e) {
         int srow, ck16, cv16;
-        chunk(e, srow, ck16, cv16);
+        stage_chunk(wave, lane, e, srow, ck16, cv16);
         const int idx = (t - nband) * 64 + srow;
         const bool in = idx < gmain;
         const int rowoff = gl[in ? idx : 0] * RB;
@@ -1411,12 +1653,6 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     dma16i<0>(d, off[0], base);
     dma16i<1024>(d, off[1], base);
   };
-  // the batch of step t: K of step t+3 and V of step t+2 (those that exist);
-  // two loads per thread for each
-  auto batch = [&](int t) {
-    if (t + 3 < U) issue(t + 3, false);
-    if (t + 2 >= 0 && t + 2 < U) issue(t + 2, true);
-  };
   auto fill = [&]() {
     for (int j = tid; j < gmain; j += NT) {
       const int pos = gidx_b[j];
@@ -1424,44 +1660,6 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
       gl[j] = pos;
       jr[j] = (dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
     }
-  };
-  auto kslot = [&](int t) { return smem + (t % B_NSLOT) * B_STEP; };
-  auto vslot = [&](int t) { return smem + B_V_OFF + (t % B_NSLOT) * B_STEP; };
-  // QK^T of one half of a step; PV of one half of a step
-  auto qk_half = [&](f32x16& sx, const uint8_t* ks) {
-    f32x16 a = {};
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-      a = mfma_bf16(*reinterpret_cast<const bf16x8*>(ks + fl.k[cc]), qo.q[cc], a);
-    sx = a;
-  };
-  auto pv_half = [&](const bf16x8 (&pb)[2], const uint8_t* vs) {
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-        st.o[db] = mfma_bf16(vfrag(vs, fl.v[db] + c2 * 2048), pb[c2], st.o[db]);
-  };
-  // the MFMAs of a phase: QK^T of one half into sq and PV of one half, the
-  // two chains alternating so that no MFMA waits on the one just before it
-  auto phase_mfma = [&](f32x16& sq, const uint8_t* ks, const bf16x8 (&pp)[2], const uint8_t* vs) {
-    bf16x8 kf[4], vf[2][2];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(ks + fl.k[cc]);
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-      for (int db = 0; db < 2; ++db) vf[c2][db] = vfrag(vs, fl.v[db] + c2 * 2048);
-    f32x16 a = {};
-    a = mfma_bf16(kf[0], qo.q[0], a);
-    st.o[0] = mfma_bf16(vf[0][0], pp[0], st.o[0]);
-    a = mfma_bf16(kf[1], qo.q[1], a);
-    st.o[1] = mfma_bf16(vf[0][1], pp[0], st.o[1]);
-    a = mfma_bf16(kf[2], qo.q[2], a);
-    st.o[0] = mfma_bf16(vf[1][0], pp[1], st.o[0]);
-    a = mfma_bf16(kf[3], qo.q[3], a);
-    st.o[1] = mfma_bf16(vf[1][1], pp[1], st.o[1]);
-    sq = a;
   };
   auto mask_of = [&](int u, int hf) {
     uint32_t m;
@@ -1478,115 +1676,17 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     }
     return m;
   };
-  auto soft_half = [&](f32x16& sx, bf16x8 (&pb)[2]) {
-    float ts = band_exp_half(sx, c, st.m, pb);
-    if (__builtin_expect(__any(ts > SUM_HI), 0))
-      band_rebase(st, sx, c, pb, ts);
-    st.l += ts;
-  };
 
-  // prologue: the batches of steps -3, -2, -1 (K of 0, 1, 2; V of 0, 1) in
-  // flight, K of step 0 resident
+  // the global-position list must be in LDS before a global step is staged
   const bool early_fill = nband < B_NSLOT - 1 && ngt > 0;
   if (early_fill) {
     fill();
     __syncthreads();
   }
-  batch(-3);
-  batch(-2);
-  batch(-1);
-  if (!early_fill) fill();
-  {
-    const int later = 2 * ((1 < U) + (0 < U) + (2 < U) + (1 < U));   // loads of batches -2, -1
-    if (later >= 8)
-      wait_loads<8>();
-    else if (later >= 6)
-      wait_loads<6>();
-    else if (later >= 4)
-      wait_loads<4>();
-    else if (later >= 2)
-      wait_loads<2>();
-    else
-      wait_loads<0>();
-  }
-  __syncthreads();
-
-  f32x16 sx, sy;           // the two halves of the step being softmaxed
-  bf16x8 pa[2], pb[2];     // probabilities of half 0 / half 1
-  if (active(0)) qk_half(sx, kslot(0));
-
-  // steps [P0, P1] need no branch: this wave is active in them and in their
-  // neighbours, and their keys lie inside every window of the wave
-  int P0 = ua + 1 > fa ? ua + 1 : fa;
-  if (P0 < 1) P0 = 1;
-  int P1 = ub - 1 < fb ? ub - 1 : fb;
-  if (P1 > nband - 2) P1 = nband - 2;
-  if (P1 > U - 2) P1 = U - 2;   // when P1 < P0 the middle loop below runs no step
-
-  auto head_of_step = [&](int u) {
-    // the batch of step u-2 (K of u+1, V of u) has landed everywhere; the
-    // slots the batch of step u overwrites were last read in step u-1
-    const int later = 2 * ((u + 2 < U) + (u + 1 < U));   // loads of batch u-1
-    if (later == 4)
-      wait_loads<4>();
-    else if (later == 2)
-      wait_loads<2>();
-    else
-      wait_loads<0>();
-    __syncthreads();
-    batch(u);
+  auto pre = [&]() {
+    if (!early_fill) fill();
   };
-  auto slow_step = [&](int u) {
-    head_of_step(u);
-    const uint8_t* kc = kslot(u);
-    const uint8_t* kn = kslot(u + 1);
-    const uint8_t* vp = vslot(u + B_NSLOT - 1);
-    const uint8_t* vc = vslot(u);
-    const bool a_prev = active(u - 1), a_cur = active(u), a_next = active(u + 1);
-    const bool masked = u < fa || u > fb || u >= nband;
-    // phase A
-    if (a_cur && masked) mask_half(sx, mask_of(u, 0), h32);
-    if (a_cur) qk_half(sy, kc + 4096);
-    if (a_prev) pv_half(pb, vp + 4096);
-    if (a_cur) soft_half(sx, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    // phase B
-    if (a_cur && masked) mask_half(sy, mask_of(u, 1), h32);
-    if (a_next) qk_half(sx, kn);
-    if (a_cur) pv_half(pa, vc);
-    if (a_cur) soft_half(sy, pb);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  int u = 0;
-  for (; u < P0 && u < U; ++u) slow_step(u);
-  for (; u <= P1; ++u) {
-    head_of_step(u);
-    const uint8_t* kc = kslot(u);
-    const uint8_t* kn = kslot(u + 1);
-    const uint8_t* vp = vslot(u + B_NSLOT - 1);
-    const uint8_t* vc = vslot(u);
-    // phase A
-    phase_mfma(sy, kc + 4096, pb, vp + 4096);
-    {
-      float ts = band_exp_half(sx, c, st.m, pa);
-      interleave_hint();
-      if (__builtin_expect(__any(ts > SUM_HI), 0))
-        band_rebase(st, sx, c, pa, ts);
-      st.l += ts;
-    }
-    // phase B
-    phase_mfma(sx, kn, pa, vc);
-    {
-      float ts = band_exp_half(sy, c, st.m, pb);
-      interleave_hint();
-      if (__builtin_expect(__any(ts > SUM_HI), 0))
-        band_rebase(st, sy, c, pb, ts);
-      st.l += ts;
-    }
-  }
-  for (; u < U; ++u) slow_step(u);
-  // PV of half 1 of the last step (its V landed with the batch of step U-3)
-  if (active(U - 1)) pv_half(pb, vslot(U - 1) + 4096);
+  half_pipe(U, P0, P1, issue, active, masked, mask_of, pre, qo, fl, st, c, h32, smem);
 
   if (g > GL_MAX && R0 < nrv) {
     // global columns past the LDS copy, 32 at a time through the first K and
@@ -1638,8 +1738,8 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     st.o[1] = sm.o[1];
   }
 
-  // normalise and store (global rows are written by the merge kernel, padded
-  // rows get exact zeros)
+  // normalise and store (global rows are written by the merge of their key
+  // slices, padded rows get exact zeros)
   const float lt = half_sum(st.l);
   if (row_in && (my_fl & 2) == 0) {
     const bool valid = (my_fl & 1) != 0;
@@ -1658,6 +1758,12 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   }
 }
 
+// Global-row workgroups on the bf16 fast path: up to NW query tiles of 32
+// global rows (one per wave) against one key slice [j_start, j_end), through
+// the same pipeline; each wave leaves an unnormalised partial result (offset,
+// sum, O) that the merge of the tile's key slices combines.  The rows' offsets
+// are set from the maximum of their first half (there is no own key in a
+// slice to anchor them).
 __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, int nv,
                                uint8_t* smem) {
   constexpr int RB = 128;
@@ -1677,8 +1783,14 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   const int qpos = gidx_b[qok ? qidx : 0];
   QOp<true> qo;
   qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
-  Softmax sm;
-  sm.init();
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
+  BandRow st;
+  st.m = 0.f;
+  st.l = 0.f;
+  st.first = true;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { st.o[0][i] = 0.f; st.o[1][i] = 0.f; }
   FLane fl;
   fl.init(lane);
 
@@ -1686,37 +1798,40 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   int j_end = j_start + p.ksplit;
   if (j_end > n) j_end = n;
   const int j_use = j_end < nv ? j_end : nv;        // keys of the slice that are real tokens
-  const int U = (j_end - j_start + KT - 1) / KT;
+  const int U = j_use > j_start ? (j_use - j_start + 63) / 64 : 0;
   const i32x4 dk = make_desc(p.Kg + head * RB, nv * RB);
   const i32x4 dv = make_desc(p.Vg + head * RB, nv * RB);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.Kg + head * RB, nv * RB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.Vg + head * RB, nv * RB);
-  int ck16[FCH], cv16[FCH], off0[FCH];
+  int kbase[B_CH], vbase[B_CH];
 #pragma unroll
-  for (int e = 0; e < FCH; ++e) {
-    const int q = tid + NT * e;
-    const int srow = q >> 3;
-    ck16[e] = ((q & 7) ^ swz_k(srow)) * 16;
-    cv16[e] = ((q & 7) ^ swz_v(srow)) * 16;
-    off0[e] = (j_start + srow) * RB;
+  for (int e = 0; e < B_CH; ++e) {
+    int srow, ck16, cv16;
+    stage_chunk(wave, lane, e, srow, ck16, cv16);
+    const int rowoff = (j_start + srow) * RB;
+    kbase[e] = rowoff + ck16;
+    vbase[e] = rowoff + cv16;
   }
-  auto offs = [&](int u, int e, int& ok, int& ov) {
-    const int rowoff = off0[e] + u * KT * RB;
-    ok = rowoff + ck16[e];
-    ov = rowoff + cv16[e];
+  const uint32_t lds_w = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) +
+                         wave * (B_CH * 1024);
+  auto issue = [&](int t, bool is_v) {
+    const uint32_t base = lds_w + (is_v ? B_V_OFF : 0) + (t % B_NSLOT) * B_STEP;
+    const int adv = t * 64 * RB;
+    const i32x4 d = is_v ? dv : dk;
+    dma16i<0>(d, (is_v ? vbase[0] : kbase[0]) + adv, base);
+    dma16i<1024>(d, (is_v ? vbase[1] : kbase[1]) + adv, base);
   };
-  auto info = [&](int u) {
-    FTile ti;
-    ti.act = true;
-    ti.j0 = j_start + u * KT;
-    ti.okb = bit_range(0, j_use - ti.j0);
-    ti.kind = ti.okb == 0xFFFFFFFFu ? 0 : 3;
-    return ti;
-  };
+  auto active = [&](int u) { return u >= 0 && u < U && wave_work; };
+  // only the last step can hold keys past the slice's real tokens
+  auto masked = [&](int u) { return j_start + 64 * u + 64 > j_use; };
+  auto mask_of = [&](int u, int hf) { return bit_range(0, j_use - (j_start + 64 * u + 32 * hf)); };
   auto nothing = []() {};
-  fpipe(U, wave_work, info, offs, nothing, dk, dv, rk, rv, qo, sm, fl, lane, p.c, 0, 0, nullptr, smem);
+  // step 0 sets the offsets (slow path); the masked last step is slow too
+  const int P0 = 1;
+  int P1 = (j_use - j_start) / 64 - 1;   // last step whose 64 keys are all real
+  if (P1 > U - 2) P1 = U - 2;
+  if (!wave_work) P1 = 0;
+  half_pipe(U, P0, P1, issue, active, masked, mask_of, nothing, qo, fl, st, p.c, h32, smem);
 
-  const float lt = sm.l + __shfl_xor(sm.l, 32);
+  const float lt = half_sum(st.l);
   if (qok) {
     const int64_t pidx = ((((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp) * 32 + qi;
     float* po = p.part_o + pidx * D;
@@ -1725,12 +1840,14 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
 #pragma unroll
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<float4*>(po + 32 * db + 8 * a + 4 * h32) =
-            make_float4(sm.o[db][4 * a], sm.o[db][4 * a + 1], sm.o[db][4 * a + 2], sm.o[db][4 * a + 3]);
+            make_float4(st.o[db][4 * a], st.o[db][4 * a + 1], st.o[db][4 * a + 2], st.o[db][4 * a + 3]);
     if (h32 == 0) {
-      p.part_ml[pidx * 2 + 0] = sm.m;
+      // a slice with no real key leaves an empty partial
+      p.part_ml[pidx * 2 + 0] = st.first ? -INFINITY : st.m;
       p.part_ml[pidx * 2 + 1] = lt;
     }
   }
+  if (wave_work) finish_global_tile<true>(p, b, h, qt, g, lane);
 }
 
 template <bool BF>
@@ -1800,69 +1917,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     }
     band_wg<BF>(p, b, h, local, s, smem);
   }
-}
-
-// ---------------------------------------------------------------------------
-// Kernel 3: merge of the global-row partials.  One workgroup per (b, h, tile
-// of 32 global rows); 8 threads per row, each owning 8 of the 64 channels.
-// The split loop is unrolled so that its loads are in flight together.
-constexpr int MERGE_UNROLL = 8;
-template <bool BF>
-__global__ __launch_bounds__(256) void merge_kernel(Params p) {
-  const int wg = blockIdx.x;
-  const int qt = wg % p.nqt;
-  const int bh = wg / p.nqt;
-  const int b = bh / p.H;
-  int g = p.gcnt[b];
-  if (g > p.max_global) g = p.max_global;
-  const int q = threadIdx.x >> 3, seg = threadIdx.x & 7;
-  const int idx = qt * 32 + q;
-  if (idx >= g) return;
-  const int pos = p.gidx[(int64_t)b * p.n + idx];
-  const int64_t base = ((int64_t)bh * p.nqt + qt) * p.nsplit;
-  const int ns = p.nsplit;
-  float mstar = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += MERGE_UNROLL) {
-    float mv[MERGE_UNROLL];
-#pragma unroll
-    for (int e = 0; e < MERGE_UNROLL; ++e)
-      mv[e] = (s0 + e < ns) ? p.part_ml[((base + s0 + e) * 32 + q) * 2] : -INFINITY;
-#pragma unroll
-    for (int e = 0; e < MERGE_UNROLL; ++e) mstar = fmaxf(mstar, mv[e]);
-  }
-  float L = 0.f;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s0 = 0; s0 < ns; s0 += MERGE_UNROLL) {
-    float2 ml[MERGE_UNROLL];
-    float4 a[MERGE_UNROLL], c[MERGE_UNROLL];
-#pragma unroll
-    for (int e = 0; e < MERGE_UNROLL; ++e) {
-      if (s0 + e < ns) {
-        const int64_t pi = (base + s0 + e) * 32 + q;
-        ml[e] = *reinterpret_cast<const float2*>(p.part_ml + pi * 2);
-        a[e] = *reinterpret_cast<const float4*>(p.part_o + pi * D + seg * 8);
-        c[e] = *reinterpret_cast<const float4*>(p.part_o + pi * D + seg * 8 + 4);
-      } else {
-        ml[e] = make_float2(-INFINITY, 0.f);
-        a[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-        c[e] = a[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < MERGE_UNROLL; ++e) {
-      const float w = __builtin_amdgcn_exp2f(ml[e].x - mstar);
-      L += w * ml[e].y;
-      acc[0] += w * a[e].x; acc[1] += w * a[e].y; acc[2] += w * a[e].z; acc[3] += w * a[e].w;
-      acc[4] += w * c[e].x; acc[5] += w * c[e].y; acc[6] += w * c[e].z; acc[7] += w * c[e].w;
-    }
-  }
-  const float inv = 1.0f / L;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] *= inv;
-  constexpr int RB = D * Lay<BF>::ELT;
-  uint8_t* orow = p.O + ((int64_t)bh * p.n + pos) * RB + seg * 8 * Lay<BF>::ELT;
-  store_row4<BF>(orow, acc);
-  store_row4<BF>(orow + 4 * Lay<BF>::ELT, acc + 4);
 }
 
 }  // namespace lwk

@@ -19,7 +19,7 @@
 
 namespace {
 
-constexpr int kNumKernels = 3;
+constexpr int kNumKernels = 2;
 
 // LWATTN_DEBUG=1 in the environment prints every failing HIP call to stderr.
 bool hip_ok(hipError_t e, const char* what) {
@@ -53,6 +53,7 @@ struct lwattn_plan_s {
   int32_t* vlen = nullptr;
   float* part_o = nullptr;
   float* part_ml = nullptr;
+  int32_t* tile_cnt = nullptr;
   int32_t* head_stride = nullptr;
   int32_t* head_blk = nullptr;
   // timing
@@ -70,6 +71,7 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->vlen);
   (void)hipFree(p->part_o);
   (void)hipFree(p->part_ml);
+  (void)hipFree(p->tile_cnt);
   (void)hipFree(p->head_stride);
   (void)hipFree(p->head_blk);
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
@@ -179,7 +181,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
     const int64_t maxs = (n + 127) / 128;
     if (want > maxs) want = maxs;
     if (want < 1) want = 1;
-    p->ksplit = ceil_div(ceil_div(n, want), 32) * 32;
+    p->ksplit = ceil_div(ceil_div(n, want), 64) * 64;   // whole 64-key steps
     p->nsplit = ceil_div(n, p->ksplit);
     nglob = units * p->nsplit;
   }
@@ -208,6 +210,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   const size_t nparts = (size_t)B * H * p->nqt * (p->nsplit > 0 ? p->nsplit : 0) * 32;
   alloc((void**)&p->part_o, nparts * lwk::D * 4);
   alloc((void**)&p->part_ml, nparts * 2 * 4);
+  alloc((void**)&p->tile_cnt, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4);
   alloc((void**)&p->head_stride, (size_t)H * 4);
   alloc((void**)&p->head_blk, (size_t)(H + 1) * 4);
   if (!ok) {
@@ -217,7 +220,9 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   if ((H > 0 && !hip_ok(hipMemcpy(p->head_stride, stride.data(), (size_t)H * 4, hipMemcpyHostToDevice), "hipMemcpy")) ||
       !hip_ok(hipMemcpy(p->head_blk, blk.data(), (size_t)(H + 1) * 4, hipMemcpyHostToDevice), "hipMemcpy") ||
       (B > 0 && !hip_ok(hipMemset(p->status, 0, (size_t)B * 4), "hipMemset")) ||
-      (B > 0 && !hip_ok(hipMemset(p->gcnt, 0, (size_t)B * 4), "hipMemset"))) {
+      (B > 0 && !hip_ok(hipMemset(p->gcnt, 0, (size_t)B * 4), "hipMemset")) ||
+      !hip_ok(hipMemset(p->tile_cnt, 0, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4), "hipMemset") ||
+      !hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize")) {
     free_plan(p);
     return LWATTN_E_DEVICE;
   }
@@ -263,6 +268,7 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   prm.vlen = p->vlen;
   prm.part_o = p->part_o;
   prm.part_ml = p->part_ml;
+  prm.tile_cnt = p->tile_cnt;
   prm.head_stride = p->head_stride;
   prm.head_blk = p->head_blk;
   prm.B = c.B;
@@ -301,18 +307,7 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   if (timed && !hip_ok(hipEventRecord(ev[2], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
 
-  if (p->nqt > 0) {
-    const int mgrid = c.B * c.H * p->nqt;
-    if (c.dtype == LWATTN_BF16)
-      hipLaunchKernelGGL(lwk::merge_kernel<true>, dim3(mgrid), dim3(256), 0, stream, prm);
-    else
-      hipLaunchKernelGGL(lwk::merge_kernel<false>, dim3(mgrid), dim3(256), 0, stream, prm);
-    if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-  }
-  if (timed) {
-    if (!hip_ok(hipEventRecord(ev[3], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
-    ++p->timing_calls;
-  }
+  if (timed) ++p->timing_calls;
   return LWATTN_OK;
 }
 
@@ -364,7 +359,7 @@ lwattn_status lwattn_timing_read(lwattn_plan_t p, float* ms, int32_t cap, int32_
                                  int32_t* ncalls) {
   if (!p || !nkernels || !ncalls || (cap > 0 && !ms)) return LWATTN_E_INVALID;
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
-  float tot[kNumKernels] = {0.f, 0.f, 0.f};
+  float tot[kNumKernels] = {0.f, 0.f};
   for (int call = 0; call < p->timing_calls; ++call) {
     hipEvent_t* ev = &p->events[(size_t)call * (kNumKernels + 1)];
     if (!hip_ok(hipEventSynchronize(ev[kNumKernels]), "hipEventSynchronize")) return LWATTN_E_DEVICE;

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "liblwattn.so")
 
 LWATTN_F32, LWATTN_BF16 = 0, 1
 OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_DEVICE, E_TOO_MANY_GLOBALS = range(6)
-KERNELS = ("compact", "attention", "merge")
+KERNELS = ("compact", "attention")
 
 # (name, restype, argtypes) of every exported function, in header order
 _c_p = ctypes.c_void_p

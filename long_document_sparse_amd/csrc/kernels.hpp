@@ -1338,18 +1338,25 @@ __device__ __forceinline__ bf16x8 vfrag(const uint8_t* vt, int off) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Scheduling template for one phase: the 12 LDS reads that feed its MFMAs
-// first, softmax VALU work while they land, then the 8 MFMAs spaced by the
-// rest of the VALU work.
+// Scheduling template for one phase: softmax VALU work first (while this
+// phase's MFMA operands finish landing), the 8 MFMAs spaced by the rest of it,
+// then the 12 LDS reads of the next phase's MFMA operands.
 __device__ __forceinline__ void interleave_hint() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // LDS reads
-  __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);   // VALU
+  __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);   // VALU while the operands land
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // LDS reads of the next phase
 }
+
+// MFMA operands of one phase: K of one half (A of QK^T) and V^T of one half
+// (A of PV), read from LDS one phase ahead.
+struct PhaseOps {
+  bf16x8 kf[4];
+  bf16x8 vf[2][2];
+};
 
 // Where thread (wave w, lane l) stages its two 16-byte chunks q = (2 w + e) 64
 // + l of each 8 KB array of a step: key row q / 8, physical chunk q % 8, the
@@ -1399,25 +1406,26 @@ __device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& is
       for (int db = 0; db < 2; ++db)
         st.o[db] = mfma_bf16(vfrag(vs, fl.v[db] + c2 * 2048), pb[c2], st.o[db]);
   };
-  // the MFMAs of a phase: QK^T of one half into sq and PV of one half, the
-  // two chains alternating so that no MFMA waits on the one just before it
-  auto phase_mfma = [&](f32x16& sq, const uint8_t* ks, const bf16x8 (&pp)[2], const uint8_t* vs) {
-    bf16x8 kf[4], vf[2][2];
+  auto load_ops = [&](PhaseOps& ops, const uint8_t* ks, const uint8_t* vs) {
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(ks + fl.k[cc]);
+    for (int cc = 0; cc < 4; ++cc) ops.kf[cc] = *reinterpret_cast<const bf16x8*>(ks + fl.k[cc]);
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int db = 0; db < 2; ++db) vf[c2][db] = vfrag(vs, fl.v[db] + c2 * 2048);
+      for (int db = 0; db < 2; ++db) ops.vf[c2][db] = vfrag(vs, fl.v[db] + c2 * 2048);
+  };
+  // the MFMAs of a phase: QK^T of one half into sq and PV of one half, the
+  // two chains alternating so that no MFMA waits on the one just before it
+  auto phase_mfma = [&](f32x16& sq, const PhaseOps& ops, const bf16x8 (&pp)[2]) {
     f32x16 a = {};
-    a = mfma_bf16(kf[0], qo.q[0], a);
-    st.o[0] = mfma_bf16(vf[0][0], pp[0], st.o[0]);
-    a = mfma_bf16(kf[1], qo.q[1], a);
-    st.o[1] = mfma_bf16(vf[0][1], pp[0], st.o[1]);
-    a = mfma_bf16(kf[2], qo.q[2], a);
-    st.o[0] = mfma_bf16(vf[1][0], pp[1], st.o[0]);
-    a = mfma_bf16(kf[3], qo.q[3], a);
-    st.o[1] = mfma_bf16(vf[1][1], pp[1], st.o[1]);
+    st.o[0] = mfma_bf16(ops.vf[0][0], pp[0], st.o[0]);
+    a = mfma_bf16(ops.kf[0], qo.q[0], a);
+    st.o[1] = mfma_bf16(ops.vf[0][1], pp[0], st.o[1]);
+    a = mfma_bf16(ops.kf[1], qo.q[1], a);
+    st.o[0] = mfma_bf16(ops.vf[1][0], pp[1], st.o[0]);
+    a = mfma_bf16(ops.kf[2], qo.q[2], a);
+    st.o[1] = mfma_bf16(ops.vf[1][1], pp[1], st.o[1]);
+    a = mfma_bf16(ops.kf[3], qo.q[3], a);
     sq = a;
   };
   auto soft_half = [&](f32x16& sx, bf16x8 (&pb)[2]) {
@@ -1487,28 +1495,56 @@ __device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& is
   };
   int u = 0;
   for (; u < P0 && u < U; ++u) slow_step(u);
+  // Branch-free steps.  Phase A of step u multiplies K of half 1 of u and V of
+  // half 1 of u-1; phase B, K of half 0 of u+1 and V of half 0 of u.  Each
+  // phase reads the operands of the next one once its own MFMAs are issued:
+  // those slots were filled by batches already waited for, and the batch of
+  // the next step writes other slots.
+  // A half whose probabilities overflow SUM_HI leaves the loop: the rescale
+  // of O happens outside it (keeping O in place through the loop), and the
+  // remaining steps run on the slow path.
+  PhaseOps ops;
+  if (u <= P1) load_ops(ops, kslot(u) + 4096, vslot(u + B_NSLOT - 1) + 4096);
+  int rare_at = 0;
+  float ts_rare = 0.f;
   for (; u <= P1; ++u) {   // runs no step when P1 < P0
     head_of_step(u);
-    const uint8_t* kc = kslot(u);
-    const uint8_t* kn = kslot(u + 1);
-    const uint8_t* vp = vslot(u + B_NSLOT - 1);
-    const uint8_t* vc = vslot(u);
     // phase A
-    phase_mfma(sy, kc + 4096, pb, vp + 4096);
-    {
-      float ts = band_exp_half(sx, c, st.m, pa);
-      interleave_hint();
-      if (__builtin_expect(__any(ts > SUM_HI), 0)) band_rebase(st, sx, c, pa, ts);
-      st.l += ts;
+    phase_mfma(sy, ops, pb);
+    float ts = band_exp_half(sx, c, st.m, pa);
+    load_ops(ops, kslot(u + 1), vslot(u));
+    interleave_hint();
+    if (__builtin_expect(__any(ts > SUM_HI), 0)) {
+      rare_at = 1;
+      ts_rare = ts;
+      break;
     }
+    st.l += ts;
     // phase B
-    phase_mfma(sx, kn, pa, vc);
-    {
-      float ts = band_exp_half(sy, c, st.m, pb);
-      interleave_hint();
-      if (__builtin_expect(__any(ts > SUM_HI), 0)) band_rebase(st, sy, c, pb, ts);
-      st.l += ts;
+    phase_mfma(sx, ops, pa);
+    ts = band_exp_half(sy, c, st.m, pb);
+    if (u + 1 <= P1) load_ops(ops, kslot(u + 1) + 4096, vslot(u) + 4096);
+    interleave_hint();
+    if (__builtin_expect(__any(ts > SUM_HI), 0)) {
+      rare_at = 2;
+      ts_rare = ts;
+      break;
     }
+    st.l += ts;
+  }
+  if (rare_at == 1) {
+    // half 0 of step u overflowed: rescale, then phase B of step u
+    band_rebase(st, sx, c, pa, ts_rare);
+    st.l += ts_rare;
+    qk_half(sx, kslot(u + 1));
+    pv_half(pa, vslot(u));
+    soft_half(sy, pb);
+    ++u;
+  } else if (rare_at == 2) {
+    // half 1 of step u overflowed
+    band_rebase(st, sy, c, pb, ts_rare);
+    st.l += ts_rare;
+    ++u;
   }
   for (; u < U; ++u) slow_step(u);
   // PV of half 1 of the last step (its V landed with the batch of step U-3)

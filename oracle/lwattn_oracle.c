@@ -20,7 +20,7 @@
  *     query is zeroed; the global token indices are the stable partition of
  *     the global flags (global_idx, global_token_nums).
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   window  : keys i + k*s for -w/2 <= k <= w/2, with s = gap + 1 (the dilation
  *             value is the number of skipped positions between taps); keys
  *             outside [0, n) do not exist.

@@ -863,29 +863,16 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
 // Keys are fetched with buffer loads whose range is the nv real rows of the
 // (batch, head), so the hardware returns zeros for every key before the start,
 // past the end or in the padded tail -- no clamping, no flag loads, no zeroing
-// selects.  Validity of the 32 keys of a tile is then pure scalar arithmetic.
+// selects.  Validity of the keys of a tile is then pure scalar arithmetic.
 // K and V tiles are stored row-major (128 B rows) with 16-byte chunks XOR-
-// swizzled per row: thread t writes physical chunk t (conflict-free b128
-// stores).  The QK^T A operand is a b128 read per lane; the PV A operand
+// swizzled per row, so that the b128 reads of the QK^T A operand and the
+// transposing reads of the PV A operand are free of bank conflicts; a
+// buffer-to-LDS load writes 64 consecutive physical chunks, each lane fetching
+// the logical chunk that belongs there.  The PV A operand
 // (V^T, four consecutive keys at one d per lane) comes from ds_read_b64_tr_b16:
 // within a 16-lane group, source lane 4e+q reads V[k0+e][d0+4q .. +3] and
 // output lane i receives V[k0+e][d0+i] for e = 0..3.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-constexpr int FK_OFF = 0;                       // K tile, 32 x 128 B
-constexpr int FV_OFF = 4096;                    // V tile, 32 x 128 B
-constexpr int FSLOT = 8192;
-#ifndef LW_F_DIST
-#define LW_F_DIST 4
-#endif
-#ifndef LW_STAGE_REGS
-#define LW_STAGE_REGS 1   // 1: stage K/V through registers; 0: buffer loads straight into LDS
-#endif
-constexpr int F_DIST = LW_F_DIST;               // tiles u+2 .. u+F_DIST are in flight during step u
-constexpr int F_NSLOT = F_DIST + 1;             // LDS ring: tiles u .. u+F_DIST
-constexpr int F_GL_OFF = F_NSLOT * FSLOT;       // int32[GL_MAX]: global positions
-constexpr int F_JR_OFF = F_GL_OFF + GL_MAX * 4; // int32[GL_MAX]: their window index (or JREL_NONE)
-constexpr int F_SMEM = F_JR_OFF + GL_MAX * 4;
-constexpr int FCH = 256 / NT;                   // 16-byte chunks per thread per 4 KB tile array
 constexpr int OOB_OFF = 0x7FFFFF00;             // a buffer offset past any range
 
 __device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
@@ -897,10 +884,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-
-struct FStage {
-  uint4 k[256 / (64 * NW)], v[256 / (64 * NW)];   // FCH chunks of K and of V
-};
 
 // Per-lane LDS byte offsets used by the compute of every tile.
 struct FLane {
@@ -1074,144 +1057,7 @@ __device__ __forceinline__ i32x4 make_desc(const void* base, int bytes) {
   return d;
 }
 
-// One 16-byte buffer load per lane straight into LDS: lane l writes
-// lds_base + 16*l.  Written as inline asm so that the compiler does not wait
-// for it before every LDS read; the pipeline below waits explicitly.  The
-// instruction has no register destination.
-__device__ __forceinline__ void dma16(i32x4 desc, int voff, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(desc), "s"(lds_base)
-      : "memory", "m0");
-}
-// Wait until at most c tiles' loads (2*FCH per tile and thread) are outstanding.
-template <int C>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(2 * FCH * C <= 63, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * FCH * C) : "memory");
-}
-__device__ __forceinline__ void wait_tiles(int c) {
-  static_assert(F_DIST <= 8, "wait_tiles covers up to 6 tiles in flight");
-  switch (c < 0 ? 0 : c) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<1>(); break;
-    case 2: wait_vm<2>(); break;
-    case 3: wait_vm<3>(); break;
-    case 4: wait_vm<4>(); break;
-    case 5: wait_vm<5>(); break;
-    default: wait_vm<6>(); break;
-  }
-}
 
-// Software-pipelined tile loop.  Tile t goes, by buffer-to-LDS loads, into
-// LDS slot t % F_NSLOT, issued F_DIST steps ahead of its first use (the ring
-// has F_DIST + 1 slots).  Step u issues the QK^T MFMAs of tile u+1 first, runs
-// the softmax of tile u on the VALU while they execute, then the PV MFMAs of
-// tile u; before the barrier it waits for tile u+2, which step u+1 reads.  The
-// loop is unrolled by two so the score registers alternate without copies.
-template <class InfoFn, class OffFn, class PreFn>
-__device__ __forceinline__ void fpipe(int U, bool wave_work, InfoFn info, OffFn offs, PreFn pre,
-                                      i32x4 dk, i32x4 dv, __amdgpu_buffer_rsrc_t rk,
-                                      __amdgpu_buffer_rsrc_t rv, const QOp<true>& qo, Softmax& sm,
-                                      const FLane& fl, int lane, float c, int my_i, int r,
-                                      const int32_t* jr, uint8_t* smem) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t lds0 =
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) + wave * 1024;
-  auto slot = [&](int u) { return smem + (u % F_NSLOT) * FSLOT; };
-  [[maybe_unused]] auto issue = [&](int u) {
-    const uint32_t base = lds0 + (u % F_NSLOT) * FSLOT;
-#pragma unroll
-    for (int e = 0; e < FCH; ++e) {
-      int ok, ov;
-      offs(u, e, ok, ov);
-      dma16(dk, ok, base + FK_OFF + e * NT * 16);
-      dma16(dv, ov, base + FV_OFF + e * NT * 16);
-    }
-  };
-#if LW_STAGE_REGS
-  // Register staging: tile t is loaded into register set t % 2 two steps
-  // before its LDS store, stored into slot t % F_NSLOT one step before use.
-  FStage rs[2];
-  auto rload = [&](FStage& set, int u) {
-#pragma unroll
-    for (int e = 0; e < FCH; ++e) {
-      int ok, ov;
-      offs(u, e, ok, ov);
-      set.k[e] = bload(rk, ok);
-      set.v[e] = bload(rv, ov);
-    }
-  };
-  auto rstore = [&](const FStage& set, int u) {
-    uint8_t* sl = slot(u);
-#pragma unroll
-    for (int e = 0; e < FCH; ++e) {
-      *reinterpret_cast<uint4*>(sl + FK_OFF + (threadIdx.x + NT * e) * 16) = set.k[e];
-      *reinterpret_cast<uint4*>(sl + FV_OFF + (threadIdx.x + NT * e) * 16) = set.v[e];
-    }
-  };
-  rload(rs[0], 0);
-  if (U > 1) rload(rs[1], 1);
-  pre();
-  rstore(rs[0], 0);
-  if (U > 1) rstore(rs[1], 1);
-  if (U > 2) rload(rs[0], 2);
-  if (U > 3) rload(rs[1], 3);
-  __syncthreads();
-#else
-  const int last0 = U - 1 < F_DIST ? U - 1 : F_DIST;
-  for (int v = 0; v <= last0; ++v) issue(v);
-  pre();
-  wait_tiles(last0 - 1);           // tiles 0 and 1 have landed
-  __syncthreads();
-#endif
-  FTile cur = info(0);
-  f32x16 S0, S1;
-  if (wave_work && cur.act) S0 = fqk(qo, slot(0) + FK_OFF, fl);
-  auto step = [&](int u, f32x16& Sin, f32x16& Sout, FStage& R) {
-#if !LW_STAGE_REGS
-    if (u >= 1 && u + F_DIST < U) issue(u + F_DIST);
-#endif
-    FTile nxt;
-    nxt.act = false;
-    nxt.kind = 0;
-    nxt.okb = 0;
-    nxt.j0 = 0;
-    if (u + 1 < U) nxt = info(u + 1);
-    if (wave_work && nxt.act) Sout = fqk(qo, slot(u + 1) + FK_OFF, fl);
-    if (wave_work && cur.act) {
-      if (cur.kind != 0)
-        apply_mask(Sin, lane_mask(cur, my_i, r, jr + (cur.kind == 2 ? cur.j0 : 0), lane), lane);
-      bf16x8 pb[2];
-      softmax_bf16(sm, Sin, c, pb);
-      fpv(sm.o, pb, slot(u) + FV_OFF, fl);
-    }
-#if LW_STAGE_REGS
-    if (u + 2 < U) rstore(R, u + 2);     // R holds tile u+2
-    __syncthreads();
-    if (u + 4 < U) rload(R, u + 4);
-#else
-    const int last = U - 1 < u + F_DIST ? U - 1 : u + F_DIST;
-    wait_tiles(last - (u + 2));
-    __syncthreads();
-#endif
-    cur = nxt;
-  };
-#if LW_STAGE_REGS
-  FStage& RA = rs[0];
-  FStage& RB = rs[1];
-#else
-  FStage RA, RB;
-#endif
-  for (int u = 0; u < U; u += 2) {
-    step(u, S0, S1, RA);
-    if (u + 1 >= U) break;
-    step(u + 1, S1, S0, RB);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Band workgroups on the bf16 fast path (the real tokens of the batch row form
@@ -1375,14 +1221,17 @@ __device__ __forceinline__ void stage_chunk(int wave, int lane, int e, int& srow
 //   masked(u)       step u needs a per-row key mask; mask_of(u, hf) is this
 //                   lane's allowed keys of half hf (bit k = key k)
 //   pre()           runs while the prologue loads are in flight
-// P0..P1 are the steps that need no branch: the wave is active in them and in
-// both neighbours, and no key is masked.
+// An idle wave (no row of its own) only stages its share and keeps the
+// barriers.  Every step runs the same interleaved schedule; a step that is masked (or
+// where this wave has no key at all: masked(u) covers those, and their mask
+// is empty) applies its mask to the scores first, so its probabilities are
+// exactly zero where excluded.
 template <class Issue, class Active, class Masked, class MaskOf, class Pre>
-__device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& issue,
+__device__ __forceinline__ void half_pipe(int U, bool idle, const Issue& issue,
                                           const Active& active, const Masked& masked,
-                                          const MaskOf& mask_of, const Pre& pre, const QOp<true>& qo,
-                                          const FLane& fl, BandRow& st, float c, int h32,
-                                          uint8_t* smem) {
+                                          const MaskOf& mask_of, const Pre& pre,
+                                          const QOp<true>& qo, const FLane& fl, BandRow& st,
+                                          float c, int h32, uint8_t* smem) {
   // the batch of step t: K of step t+3 and V of step t+2 (those that exist);
   // two loads per thread for each
   auto batch = [&](int t) {
@@ -1439,6 +1288,8 @@ __device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& is
   batch(-3);
   batch(-2);
   batch(-1);
+  for (int i = threadIdx.x; i < B_STEP / 16; i += NT)   // V slot of "step -1"
+    reinterpret_cast<uint4*>(smem + B_V_OFF + (B_NSLOT - 1) * B_STEP)[i] = make_uint4(0, 0, 0, 0);
   pre();
   {
     const int later = 2 * ((1 < U) + (0 < U) + (2 < U) + (1 < U));   // loads of batches -2, -1
@@ -1457,7 +1308,25 @@ __device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& is
 
   f32x16 sx, sy;           // the two halves of the step being softmaxed
   bf16x8 pa[2], pb[2];     // probabilities of half 0 / half 1
-  if (active(0)) qk_half(sx, kslot(0));
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { pa[c2][e] = (__bf16)0.0f; pb[c2][e] = (__bf16)0.0f; }
+  }
+  if (U > 0) qk_half(sx, kslot(0));
+  if (st.first && U > 0) {
+    // rows without an anchor take the maximum of the allowed keys of their
+    // first half as offset
+    if (masked(0)) mask_half(sx, mask_of(0, 0), h32);
+    float mx = sx[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sx[r]);
+    mx = half_max(mx);
+    if (mx != -INFINITY) {
+      st.m = mx * c;
+      st.first = false;
+    }
+  }
 
   auto head_of_step = [&](int u) {
     // the batch of step u-2 (K of u+1, V of u) has landed everywhere; the
@@ -1493,22 +1362,29 @@ __device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& is
     if (a_cur) soft_half(sy, pb);
     __builtin_amdgcn_sched_barrier(0);
   };
-  int u = 0;
-  for (; u < P0 && u < U; ++u) slow_step(u);
-  // Branch-free steps.  Phase A of step u multiplies K of half 1 of u and V of
-  // half 1 of u-1; phase B, K of half 0 of u+1 and V of half 0 of u.  Each
-  // phase reads the operands of the next one once its own MFMAs are issued:
-  // those slots were filled by batches already waited for, and the batch of
-  // the next step writes other slots.
-  // A half whose probabilities overflow SUM_HI leaves the loop: the rescale
-  // of O happens outside it (keeping O in place through the loop), and the
-  // remaining steps run on the slow path.
+
+  // Phase A of step u multiplies K of half 1 of u and V of half 1 of u-1;
+  // phase B, K of half 0 of u+1 and V of half 0 of u.  Each phase reads the
+  // operands of the next one once its own MFMAs are issued: those slots were
+  // filled by batches already waited for, and the batch of the next step
+  // writes other slots.  Step 0's phase A reads the V slot of "step -1",
+  // zeroed above, against probabilities that are zero.  A half whose
+  // probabilities overflow SUM_HI leaves the loop: the rescale of O happens
+  // outside it (keeping O in place through the loop), and the remaining steps
+  // run on the slow path.
+  if (idle) {
+    for (int u = 0; u < U; ++u) head_of_step(u);
+    return;
+  }
   PhaseOps ops;
-  if (u <= P1) load_ops(ops, kslot(u) + 4096, vslot(u + B_NSLOT - 1) + 4096);
+  if (U > 0) load_ops(ops, kslot(0) + 4096, vslot(B_NSLOT - 1) + 4096);
   int rare_at = 0;
   float ts_rare = 0.f;
-  for (; u <= P1; ++u) {   // runs no step when P1 < P0
+  int u = 0;
+  for (; u < U; ++u) {
     head_of_step(u);
+    const bool msk = masked(u);
+    if (msk) mask_half(sx, mask_of(u, 0), h32);
     // phase A
     phase_mfma(sy, ops, pb);
     float ts = band_exp_half(sx, c, st.m, pa);
@@ -1520,10 +1396,11 @@ __device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& is
       break;
     }
     st.l += ts;
+    if (msk) mask_half(sy, mask_of(u, 1), h32);
     // phase B
     phase_mfma(sx, ops, pa);
     ts = band_exp_half(sy, c, st.m, pb);
-    if (u + 1 <= P1) load_ops(ops, kslot(u + 1) + 4096, vslot(u) + 4096);
+    if (u + 1 < U) load_ops(ops, kslot(u + 1) + 4096, vslot(u) + 4096);
     interleave_hint();
     if (__builtin_expect(__any(ts > SUM_HI), 0)) {
       rare_at = 2;
@@ -1536,7 +1413,8 @@ __device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& is
     // half 0 of step u overflowed: rescale, then phase B of step u
     band_rebase(st, sx, c, pa, ts_rare);
     st.l += ts_rare;
-    qk_half(sx, kslot(u + 1));
+    if (masked(u)) mask_half(sy, mask_of(u, 1), h32);
+    if (u + 1 < U) qk_half(sx, kslot(u + 1));
     pv_half(pa, vslot(u));
     soft_half(sy, pb);
     ++u;
@@ -1548,7 +1426,7 @@ __device__ __forceinline__ void half_pipe(int U, int P0, int P1, const Issue& is
   }
   for (; u < U; ++u) slow_step(u);
   // PV of half 1 of the last step (its V landed with the batch of step U-3)
-  if (active(U - 1)) pv_half(pb, vslot(U - 1) + 4096);
+  if (U > 0) pv_half(pb, vslot(U - 1) + 4096);
 }
 
 __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, int nv,
@@ -1604,13 +1482,6 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     return u >= 0 && u < U && (u < nband ? (u >= ua && u <= ub) : (bool)wave_work);
   };
   auto masked = [&](int u) { return u < fa || u > fb || u >= nband; };
-  // steps [P0, P1] need no branch: this wave is active in them and in their
-  // neighbours, and their keys lie inside every window of the wave
-  int P0 = ua + 1 > fa ? ua + 1 : fa;
-  if (P0 < 1) P0 = 1;
-  int P1 = ub - 1 < fb ? ub - 1 : fb;
-  if (P1 > nband - 2) P1 = nband - 2;
-  if (P1 > U - 2) P1 = U - 2;
 
   QOp<true> qo;
   qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
@@ -1722,7 +1593,7 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   auto pre = [&]() {
     if (!early_fill) fill();
   };
-  half_pipe(U, P0, P1, issue, active, masked, mask_of, pre, qo, fl, st, c, h32, smem);
+  half_pipe(U, !wave_work, issue, active, masked, mask_of, pre, qo, fl, st, c, h32, smem);
 
   if (g > GL_MAX && R0 < nrv) {
     // global columns past the LDS copy, 32 at a time through the first K and
@@ -1860,12 +1731,7 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   auto masked = [&](int u) { return j_start + 64 * u + 64 > j_use; };
   auto mask_of = [&](int u, int hf) { return bit_range(0, j_use - (j_start + 64 * u + 32 * hf)); };
   auto nothing = []() {};
-  // step 0 sets the offsets (slow path); the masked last step is slow too
-  const int P0 = 1;
-  int P1 = (j_use - j_start) / 64 - 1;   // last step whose 64 keys are all real
-  if (P1 > U - 2) P1 = U - 2;
-  if (!wave_work) P1 = 0;
-  half_pipe(U, P0, P1, issue, active, masked, mask_of, nothing, qo, fl, st, p.c, h32, smem);
+  half_pipe(U, !wave_work, issue, active, masked, mask_of, nothing, qo, fl, st, p.c, h32, smem);
 
   const float lt = half_sum(st.l);
   if (qok) {
@@ -1888,8 +1754,7 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
 
 template <bool BF>
 constexpr int smem_bytes() {
-  constexpr int f = F_SMEM > B_SMEM ? F_SMEM : B_SMEM;
-  return (BF && f > smem_bytes_general<BF>()) ? f : smem_bytes_general<BF>();
+  return (BF && B_SMEM > smem_bytes_general<BF>()) ? B_SMEM : smem_bytes_general<BF>();
 }
 
 // The logical workgroup order keeps neighbouring query blocks of one head on

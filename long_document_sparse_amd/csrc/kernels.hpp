@@ -1220,14 +1220,15 @@ __device__ __forceinline__ void stage_chunk(int wave, int lane, int e, int& srow
 //   active(u)       this wave computes on step u
 //   masked(u)       step u needs a per-row key mask; mask_of(u, hf) is this
 //                   lane's allowed keys of half hf (bit k = key k)
-//   pre()           runs while the prologue loads are in flight
-// An idle wave (no row of its own) only stages its share and keeps the
-// barriers.  Every step runs the same interleaved schedule; a step that is masked (or
+//   pre()           runs while the prologue loads are in flight (it loads the
+//                   rows' queries and sets their offsets)
+//   idle()          (after pre) this wave has no row of its own: it only stages
+//                   its share and keeps the barriers  Every step runs the same interleaved schedule; a step that is masked (or
 // where this wave has no key at all: masked(u) covers those, and their mask
 // is empty) applies its mask to the scores first, so its probabilities are
 // exactly zero where excluded.
-template <class Issue, class Active, class Masked, class MaskOf, class Pre>
-__device__ __forceinline__ void half_pipe(int U, bool idle, const Issue& issue,
+template <class Idle, class Issue, class Active, class Masked, class MaskOf, class Pre>
+__device__ __forceinline__ void half_pipe(int U, const Idle& idle, const Issue& issue,
                                           const Active& active, const Masked& masked,
                                           const MaskOf& mask_of, const Pre& pre,
                                           const QOp<true>& qo, const FLane& fl, BandRow& st,
@@ -1372,7 +1373,7 @@ __device__ __forceinline__ void half_pipe(int U, bool idle, const Issue& issue,
   // probabilities overflow SUM_HI leaves the loop: the rescale of O happens
   // outside it (keeping O in place through the loop), and the remaining steps
   // run on the slow path.
-  if (idle) {
+  if (idle()) {
     for (int u = 0; u < U; ++u) head_of_step(u);
     return;
   }
@@ -1465,15 +1466,15 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   const int my_i = R0w + qi;
   const bool row_in = my_i < nr;
   const int my_pos = rho + (row_in ? my_i : 0) * s;
-  const uint8_t my_fl = p.flags[(int64_t)b * n + my_pos];
-  const bool wave_work = __any(row_in && (my_fl & 3) == 1);
+  uint8_t my_fl = 0;         // loaded while the first keys are in flight
+  bool wave_work = false;    // the wave has a local row
 
   // this wave's band steps with any key of its windows [ua, ub], and those
   // with every key inside all of its rows' windows [fa, fb]
   const int lo_w = R0w - r > 0 ? R0w - r : 0;
   const int hi_w = (R0w + 31 + r < nrv - 1) ? R0w + 31 + r : nrv - 1;
-  const int ua = wave_work ? floordiv(lo_w - kb0, 64) : 1 << 30;
-  const int ub = wave_work ? floordiv(hi_w - kb0, 64) : -1;
+  const int ua = floordiv(lo_w - kb0, 64);
+  const int ub = floordiv(hi_w - kb0, 64);
   const int fl_lo = (R0w + 31 - r > 0) ? R0w + 31 - r : 0;
   const int fl_hi = (R0w + r < nrv - 1) ? R0w + r : nrv - 1;
   const int fa = floordiv(fl_lo - kb0 + 63, 64);
@@ -1484,14 +1485,16 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   auto masked = [&](int u) { return u < fa || u > fb || u >= nband; };
 
   QOp<true> qo;
-  qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
-  // Take Q out of the compiler's view of outstanding loads here: the loop
-  // below issues buffer-to-LDS loads the compiler does not count, so a wait it
-  // placed for Q inside the loop would also wait for those.
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
   BandRow st;
-  {
+  auto load_rows = [&]() {
+    my_fl = p.flags[(int64_t)b * n + my_pos];
+    wave_work = __any(row_in && (my_fl & 3) == 1);
+    qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
+    // Take Q out of the compiler's view of outstanding loads here: the loop
+    // below issues buffer-to-LDS loads the compiler does not count, so a wait
+    // it placed for Q inside the loop would also wait for those.
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
     // the row's own score sets the initial offset (this lane's 32 channels,
     // then both half-lanes)
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -1510,7 +1513,7 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     }
     st.m = half_sum(sd) * p.c;
     asm volatile("" : "+v"(st.m));
-  }
+  };
   st.l = 0.f;
   st.first = false;
 #pragma unroll
@@ -1591,9 +1594,11 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     __syncthreads();
   }
   auto pre = [&]() {
+    load_rows();
     if (!early_fill) fill();
   };
-  half_pipe(U, !wave_work, issue, active, masked, mask_of, pre, qo, fl, st, c, h32, smem);
+  auto idle = [&]() { return !wave_work; };
+  half_pipe(U, idle, issue, active, masked, mask_of, pre, qo, fl, st, c, h32, smem);
 
   if (g > GL_MAX && R0 < nrv) {
     // global columns past the LDS copy, 32 at a time through the first K and
@@ -1687,11 +1692,13 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
   const int qidx = qt * 32 + qi;
   const bool qok = wave_work && qidx < g;
-  const int qpos = gidx_b[qok ? qidx : 0];
   QOp<true> qo;
-  qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
+  auto load_rows = [&]() {   // while the first keys are in flight
+    const int qpos = gidx_b[qok ? qidx : 0];
+    qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
+    for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
+  };
   BandRow st;
   st.m = 0.f;
   st.l = 0.f;
@@ -1730,8 +1737,8 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   // only the last step can hold keys past the slice's real tokens
   auto masked = [&](int u) { return j_start + 64 * u + 64 > j_use; };
   auto mask_of = [&](int u, int hf) { return bit_range(0, j_use - (j_start + 64 * u + 32 * hf)); };
-  auto nothing = []() {};
-  half_pipe(U, !wave_work, issue, active, masked, mask_of, nothing, qo, fl, st, p.c, h32, smem);
+  auto idle = [&]() { return !wave_work; };
+  half_pipe(U, idle, issue, active, masked, mask_of, load_rows, qo, fl, st, p.c, h32, smem);
 
   const float lt = half_sum(st.l);
   if (qok) {

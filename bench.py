@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the Longformer window + global attention forward on one MI355X.
 
-One step = one lwattn_forward (global-index compaction, then the attention
-kernel: band rows, global rows and the merge of their key slices) over one
-batch of seeded synthetic input that is
-already resident in device memory.  Prints ONE JSON line.
+One step = one lwattn_forward, a single kernel launch (global-index
+compaction, band rows, global rows and the merge of their key slices), over
+one batch of seeded synthetic input that is already resident in device
+memory.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload base]
                   [--no-cpu-baseline] [--no-timing] [--copy-probe MIB]
@@ -14,7 +14,9 @@ dilation, one global token at position 0, bf16 storage, fp32 accumulation.
 
 Timing is "warm": forwards run back to back, so inputs that fit the 256 MB
 last-level cache stay there between steps.  Per-kernel durations come from
-HIP events that the library records on the stream the kernels run on.
+HIP events that the library records on the stream the kernel runs on, around
+the kernel of every fourth forward of the timed loop (recording them on every
+forward would make the host, not the GPU, set the pace of the loop).
 
 --copy-probe runs, after the timed loop, a plain device-to-device copy of the
 given size a few times; a counter pass over the same command then gives the
@@ -34,6 +36,7 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
+TIMING_EVERY = 4
 METRIC = "window+global attn fwd tokens/s & TFLOP/s (% bf16 MFMA peak), n=4096 w=512"
 KERNEL_SOURCES = ("long_document_sparse_amd/csrc/kernels.hpp",
                   "long_document_sparse_amd/csrc/lwattn.hip")
@@ -158,7 +161,8 @@ def main():
         raise SystemExit(f"forward failed: {lwattn.strerror(st)}")
 
     if not args.no_timing:
-        plan.timing_enable(args.steps)
+        # per-kernel events on every TIMING_EVERY-th forward of the timed loop
+        plan.timing_enable(args.steps, every=TIMING_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):

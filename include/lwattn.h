@@ -103,7 +103,10 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
  * Returns LWATTN_E_INVALID before launching anything if the plan or a pointer
  * is null or misaligned, LWATTN_E_DEVICE if a launch fails.  Data-dependent
  * errors (too many global tokens) are reported by lwattn_sync_status; O is
- * then undefined.  One plan serves one stream at a time. */
+ * then undefined.  One plan serves one stream at a time: its workspace
+ * (flags, global-index lists, per-row readiness words, merge counters) is
+ * shared by all its forwards, so forwards of one plan that overlap on two
+ * streams race.  The forward is a single kernel launch. */
 lwattn_status lwattn_forward(lwattn_plan_t plan,
                              const void* Q, const void* K, const void* V,
                              const void* Qg, const void* Kg, const void* Vg,
@@ -125,7 +128,10 @@ lwattn_status lwattn_global_index(lwattn_plan_t plan, int32_t* gidx, int32_t* gc
 
 /* Synchronizes `stream`, then reports the device-side status of the last
  * forward: LWATTN_E_TOO_MANY_GLOBALS if any row exceeded max_global, else
- * LWATTN_OK (or LWATTN_E_DEVICE if a HIP call failed). */
+ * LWATTN_OK.  LWATTN_E_DEVICE if a HIP call failed, or if in any forward
+ * since lwattn_plan a workgroup timed out waiting for the compaction of its
+ * batch row (its output rows were then not written); that state is sticky
+ * and the plan should be destroyed. */
 lwattn_status lwattn_sync_status(lwattn_plan_t plan, hipStream_t stream);
 
 /* Kernel timing for measurement.  While enabled, every forward records HIP
@@ -133,9 +139,14 @@ lwattn_status lwattn_sync_status(lwattn_plan_t plan, hipStream_t stream);
  * forwards are kept).  lwattn_timing_read synchronizes on the recorded events
  * and returns, per kernel of the forward, the summed duration in milliseconds
  * (ms[k] for k < *nkernels, at most `cap`) and the number of recorded forwards.
- * Kernel order: 0 = global-index compaction, 1 = attention (local rows, and
- * global rows including the merge of their key slices). */
+ * A forward is one kernel (*nkernels = 1): the global-index compaction, the
+ * local rows and the global rows including the merge of their key slices. */
 lwattn_status lwattn_timing_enable(lwattn_plan_t plan, int32_t max_calls);
+/* Record the events of every `every`-th forward only (every >= 1; 1 after
+ * lwattn_plan), so that recording adds little host work to a timed loop of
+ * back-to-back forwards.  Counting restarts at lwattn_timing_enable.
+ * LWATTN_E_INVALID for a null plan or every < 1. */
+lwattn_status lwattn_timing_every(lwattn_plan_t plan, int32_t every);
 lwattn_status lwattn_timing_read(lwattn_plan_t plan, float* ms, int32_t cap,
                                  int32_t* nkernels, int32_t* ncalls);
 lwattn_status lwattn_timing_disable(lwattn_plan_t plan);

@@ -1,21 +1,21 @@
 // kernels.hpp -- gfx950 kernels of the Longformer window + global attention
 // forward.  Included once, by lwattn.hip.
 //
-// Three kernels run per forward, in order on one stream:
-//   compact_kernel  one workgroup per batch row: padding / global flags per
-//                   position and the ascending global-index list (wave ballot
-//                   + prefix count), the FasterTransformer guide's
-//                   global_idx / global_token_nums partition.
-//   attn_kernel     one grid with two kinds of workgroups:
-//                   * global-row workgroups: the global queries of one
-//                     (batch, head) against one slice of all keys under
-//                     Qg/Kg/Vg, written as an unnormalised softmax partial
-//                     (running max, running sum, weighted value sum);
-//                   * band workgroups: 128 query rows of one (batch, head,
-//                     residue class of the dilation) against their window
-//                     keys and the global keys under Q/K/V, one online
-//                     softmax per row, the output row written directly.
-//   merge_kernel    log-sum-exp merge of the global-row partials.
+// One kernel, attn_kernel, runs per forward.  Its grid holds three kinds of
+// workgroups, in dispatch order:
+//   * compaction workgroups, one per batch row: padding / global flags per
+//     position, the ascending global-index list (wave ballot + prefix count;
+//     the FasterTransformer guide's global_idx / global_token_nums partition)
+//     and the length of the row's real-token prefix, published to the rest of
+//     the grid through a per-row epoch word;
+//   * band workgroups: 128 query rows of one (batch, head, residue class of
+//     the dilation) against their window keys and the global keys under
+//     Q/K/V, one online softmax per row, the output row written directly;
+//   * global-row workgroups: the global queries of one (batch, head) against
+//     one slice of all keys under Qg/Kg/Vg, written as an unnormalised softmax
+//     partial (running max, running sum, weighted value sum); the last slice
+//     of a query tile to finish merges all of them (log-sum-exp) and writes
+//     the output rows.
 //
 // Method sources: "LongFormer: The Long-Document Transformer" notes, sections
 // "Sliding Window", "Dilated Sliding Window" and "Global Attention" (banded
@@ -31,8 +31,8 @@
 // stay in registers and are the B operand of O^T += V^T * P^T; V is stored
 // transposed in LDS so that each lane reads runs of 4 keys at one d.
 //
-// Staging.  Every thread of a workgroup loads one 16-byte chunk of K and of V
-// per tile (two for float32) into registers two tiles ahead of its use and
+// Staging (general path: rows with scattered padding, float32 storage).
+// Every thread of a workgroup loads one 16-byte chunk of K and of V per tile (two for float32) into registers two tiles ahead of its use and
 // writes them to one of two LDS slots one step ahead, so a global load has two
 // compute steps to arrive.  Key positions are computed, not loaded; the
 // padding flag of a key is loaded beside its K/V chunk and padded keys are
@@ -72,6 +72,10 @@ struct Params {
   float* part_o;           // [B][H][nqt][nsplit][32][64]
   float* part_ml;          // [B][H][nqt][nsplit][32][2]
   int32_t* tile_cnt;       // [B][H][nqt]: finished key slices of a query tile (0 between forwards)
+  int32_t* ready;          // [B]: epoch of the last forward whose compaction of the row is done
+  int32_t* fault;          // sticky: set when a workgroup gave up waiting for its row
+  int32_t epoch;           // this forward's number (> 0)
+  int32_t n_comp_wg;       // compaction workgroups at the head of the attention launch (= B)
   const int32_t* head_stride;  // [H]: dilation gap + 1 (device copy, any H)
   const int32_t* head_blk;     // [H+1]: prefix of band workgroups per batch row
   int32_t B, H, n, r;      // r = min(window/2, n)
@@ -426,74 +430,83 @@ struct Softmax {
 };
 
 // ---------------------------------------------------------------------------
-// Kernel 1: flags + global-index compaction, one workgroup per batch row.
-// Each thread takes 4 consecutive positions per pass (one float4 of each
-// mask); a wave's 256 positions are counted with 4 ballots.
-constexpr int CT = 1024;
-constexpr int CPT = 4;
-// exclusive prefix over the wave of a per-lane count in [0, 7], and the wave total
-__device__ __forceinline__ void wave_count(int mine, int lane, int& before, int& total) {
+// Compaction, inside the attention launch: workgroup b (of the first B) does
+// batch row b with NT threads, 16 consecutive positions per thread and pass
+// (four float4 of each mask), counting a wave's globals with 5 ballots (per-
+// thread counts are 0..16), then publishes the row by storing this forward's
+// epoch into ready[b].  Every other workgroup of the launch waits for the
+// epoch of its row before reading what the compaction wrote.
+constexpr int C_PT = 16;
+__device__ __forceinline__ void wave_count5(int mine, int lane, int& before, int& total) {
   before = 0;
   total = 0;
 #pragma unroll
-  for (int bit = 0; bit < 3; ++bit) {
+  for (int bit = 0; bit < 5; ++bit) {
     const uint64_t bal = __ballot((mine >> bit) & 1);
     before += __popcll(bal & ((1ull << lane) - 1ull)) << bit;
     total += __popcll(bal) << bit;
   }
 }
-__global__ __launch_bounds__(CT) void compact_kernel(Params p) {
-  __shared__ int wsum[CT / 64];
-  __shared__ int vsum[CT / 64];
-  __shared__ int first_pad;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+__device__ void compact_row(const Params& p, int b, uint8_t* smem) {
+  int* wsum = reinterpret_cast<int*>(smem);            // [NW] globals per wave
+  int* vsum = wsum + NW;                               // [NW] real tokens per wave
+  int* first_pad = vsum + NW;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = p.n;
   const float* lm = p.lmask + (int64_t)b * n;
   const float* gm = p.gmask + (int64_t)b * n;
   uint8_t* fl = p.flags + (int64_t)b * n;
   int32_t* gi = p.gidx + (int64_t)b * n;
-  if (tid == 0) first_pad = n;
+  if (tid == 0) *first_pad = n;
   __syncthreads();
   int carry = 0, nvalid = 0;
   const bool vec = p.mask_vec != 0;   // masks 16-byte aligned and n % 4 == 0
-  for (int base = 0; base < n; base += CT * CPT) {
-    const int j0 = base + tid * CPT;
-    float lv[CPT], gv[CPT];
-    if (vec && j0 + CPT <= n) {
-      const float4 a = *reinterpret_cast<const float4*>(lm + j0);
-      const float4 c = *reinterpret_cast<const float4*>(gm + j0);
-      lv[0] = a.x; lv[1] = a.y; lv[2] = a.z; lv[3] = a.w;
-      gv[0] = c.x; gv[1] = c.y; gv[2] = c.z; gv[3] = c.w;
+  for (int base = 0; base < n; base += NT * C_PT) {
+    const int j0 = base + tid * C_PT;
+    float lv[C_PT], gv[C_PT];
+    if (vec && j0 + C_PT <= n) {
+#pragma unroll
+      for (int k = 0; k < C_PT / 4; ++k) {
+        const float4 a = *reinterpret_cast<const float4*>(lm + j0 + 4 * k);
+        const float4 c = *reinterpret_cast<const float4*>(gm + j0 + 4 * k);
+        lv[4 * k] = a.x; lv[4 * k + 1] = a.y; lv[4 * k + 2] = a.z; lv[4 * k + 3] = a.w;
+        gv[4 * k] = c.x; gv[4 * k + 1] = c.y; gv[4 * k + 2] = c.z; gv[4 * k + 3] = c.w;
+      }
     } else {
 #pragma unroll
-      for (int e = 0; e < CPT; ++e) {
+      for (int e = 0; e < C_PT; ++e) {
         lv[e] = (j0 + e < n) ? lm[j0 + e] : 0.0f;
         gv[e] = (j0 + e < n) ? gm[j0 + e] : 0.0f;
       }
     }
-    bool g[CPT];
-    uint32_t packed = 0;
+    uint32_t gbits = 0, packed[C_PT / 4];
     int mine = 0, myvalid = 0, mypad = n;
 #pragma unroll
-    for (int e = CPT - 1; e >= 0; --e) {
+    for (int k = 0; k < C_PT / 4; ++k) packed[k] = 0;
+#pragma unroll
+    for (int e = C_PT - 1; e >= 0; --e) {
       const bool v = lv[e] != 0.0f;
-      g[e] = v && (gv[e] != 0.0f);
-      packed |= (uint32_t)((v ? 1 : 0) | (g[e] ? 2 : 0)) << (8 * e);
-      mine += g[e] ? 1 : 0;
+      const bool g = v && (gv[e] != 0.0f);
+      packed[e / 4] |= (uint32_t)((v ? 1 : 0) | (g ? 2 : 0)) << (8 * (e % 4));
+      gbits |= (uint32_t)(g ? 1 : 0) << e;
+      mine += g ? 1 : 0;
       myvalid += v ? 1 : 0;
       if (!v && j0 + e < n) mypad = j0 + e;
     }
-    if ((n % 4) == 0 && j0 + CPT <= n) {
-      *reinterpret_cast<uint32_t*>(fl + j0) = packed;   // 4-byte aligned: b*n and j0 are multiples of 4
+    if ((n % 4) == 0 && j0 + C_PT <= n) {
+#pragma unroll
+      for (int k = 0; k < C_PT / 4; ++k)
+        *reinterpret_cast<uint32_t*>(fl + j0 + 4 * k) = packed[k];   // 4-byte aligned
     } else {
 #pragma unroll
-      for (int e = 0; e < CPT; ++e)
-        if (j0 + e < n) fl[j0 + e] = (uint8_t)(packed >> (8 * e));
+      for (int e = 0; e < C_PT; ++e)
+        if (j0 + e < n) fl[j0 + e] = (uint8_t)(packed[e / 4] >> (8 * (e % 4)));
     }
-    if (mypad < n) atomicMin(&first_pad, mypad);
+    if (mypad < n) atomicMin(first_pad, mypad);
     int before, wtot, vb, vtot;
-    wave_count(mine, lane, before, wtot);
-    wave_count(myvalid, lane, vb, vtot);
+    wave_count5(mine, lane, before, wtot);
+    wave_count5(myvalid, lane, vb, vtot);
     if (lane == 0) {
       wsum[wave] = wtot;
       vsum[wave] = vtot;
@@ -501,30 +514,83 @@ __global__ __launch_bounds__(CT) void compact_kernel(Params p) {
     __syncthreads();
     int wpre = 0, tot = 0, vt = 0;
 #pragma unroll
-    for (int w = 0; w < CT / 64; ++w) {
-      const int c = wsum[w];
-      wpre += (w < wave) ? c : 0;
-      tot += c;
+    for (int w = 0; w < NW; ++w) {
+      const int cw = wsum[w];
+      wpre += (w < wave) ? cw : 0;
+      tot += cw;
       vt += vsum[w];
     }
     int k = carry + wpre + before;
-#pragma unroll
-    for (int e = 0; e < CPT; ++e)
-      if (g[e]) gi[k++] = j0 + e;
+    while (gbits) {
+      const int e = __builtin_ctz(gbits);
+      gbits &= gbits - 1;
+      gi[k++] = j0 + e;
+    }
     carry += tot;
     nvalid += vt;
     __syncthreads();
   }
-  for (int k = carry + tid; k < n; k += CT) gi[k] = -1;
+  for (int k = carry + tid; k < n; k += NT) gi[k] = -1;
   if (tid == 0) {
     p.gcnt[b] = carry;
     p.status[b] = carry > p.max_global ? 1 : 0;
-    p.vlen[b] = (first_pad == nvalid) ? nvalid : -1;   // real tokens form the prefix [0, nvalid)
+    p.vlen[b] = (*first_pad == nvalid) ? nvalid : -1;   // real tokens form the prefix [0, nvalid)
   }
+  // the row's flags, list, count and prefix length are written back before
+  // the epoch is published (a release; no acquire, which would invalidate
+  // this XCD's caches)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) __hip_atomic_store(p.ready + b, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Reads of what other workgroups of the launch wrote (the compaction's
+// outputs, global-row partials) on the fast paths are agent-scope relaxed
+// atomic loads: they compile to loads that are coherent across the XCDs
+// (sc1) and so need no acquire fence, whose cache invalidation costs
+// microseconds when hundreds of workgroups issue it at once.  They are issued
+// only after the epoch (or the slice counter) has been seen, behind a barrier,
+// so they observe what the release published.
+__device__ __forceinline__ int coherent_load(const int32_t* ptr) {
+  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_loadf(const float* ptr) {
+  return __builtin_bit_cast(float, coherent_load(reinterpret_cast<const int32_t*>(ptr)));
+}
+
+// Wait until batch row b is compacted for this forward.  The compaction
+// workgroups come first in dispatch order, so they run; the wait is bounded
+// all the same, and a row that never becomes ready is reported in the sticky
+// fault word (the workgroup then skips its work) instead of hanging the
+// launch.  One thread polls with relaxed loads and sleeps between polls; the
+// barrier passes what it saw on to the rest of the workgroup.  Callers that
+// read the compaction's outputs with plain loads (the general paths) ask for
+// an agent-scope acquire fence in every wave as well.
+// The limit allows at least ~2^18 polls (each sleeps >= 128 clocks) plus
+// n / 4 for the compaction of long rows, far beyond the time it takes.
+constexpr int READY_SPIN_BASE = 1 << 18;
+__device__ __forceinline__ bool wait_ready(const Params& p, int b, bool acquire) {
+  __shared__ int s_ok;
+  if (threadIdx.x == 0) {
+    const int limit = READY_SPIN_BASE + (p.n >> 2);
+    int spins = 0, good = 1;
+    while (coherent_load(p.ready + b) != p.epoch) {
+      if (++spins > limit) {
+        good = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (!good) atomicOr(p.fault, 1);
+    s_ok = good;
+  }
+  __syncthreads();
+  if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return s_ok != 0;
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: attention.
+// Attention.
 // mask_kind: 0 none, 1 window tile (key usable and |i - j| <= r),
 //            2 global columns (usable and not already in the row's window),
 //            3 key usable only.  Every mask is a select, never a branch.
@@ -727,25 +793,30 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
 // 32 (l / 32) .. +31.
 template <bool BF>
 __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g, int lane) {
-  __threadfence();                                   // this slice's partial rows are visible
+  // this slice's partial rows are written back before it is counted; the
+  // wave that counts the last slice reads all of them with coherent loads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   int32_t* cnt = p.tile_cnt + ((int64_t)b * p.H + h) * p.nqt + qt;
   int old = 0;
   if (lane == 0) old = atomicAdd(cnt, 1);
   old = __builtin_amdgcn_readfirstlane(old);
   if (old != p.nsplit - 1) return;
-  __threadfence();                                   // every slice's partial rows are visible
   const int q = lane & 31, ch = lane >> 5;
   const int idx = qt * 32 + q;
   if (idx < g) {
     const int64_t base = (((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit;
     const int ns = p.nsplit;
+    // this tile's partial O rows, read through a buffer range with the sc1
+    // (agent-coherent) cache policy
+    const __amdgpu_buffer_rsrc_t ro =
+        __builtin_amdgcn_make_buffer_rsrc(p.part_o + base * 32 * D, (short)0, ns * 32 * D * 4, 0x00020000);
     constexpr int U1 = 16, U2 = 4;
     float mstar = -INFINITY;
     for (int s0 = 0; s0 < ns; s0 += U1) {
       float mv[U1];
 #pragma unroll
       for (int e = 0; e < U1; ++e)
-        mv[e] = (s0 + e < ns) ? __builtin_nontemporal_load(p.part_ml + ((base + s0 + e) * 32 + q) * 2) : -INFINITY;
+        mv[e] = (s0 + e < ns) ? coherent_loadf(p.part_ml + ((base + s0 + e) * 32 + q) * 2) : -INFINITY;
 #pragma unroll
       for (int e = 0; e < U1; ++e) mstar = fmaxf(mstar, mv[e]);
     }
@@ -758,11 +829,14 @@ __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g,
 #pragma unroll
       for (int e = 0; e < U2; ++e) {
         const bool in = s0 + e < ns;
-        const int64_t pi = (base + (in ? s0 + e : s0)) * 32 + q;
-        ml[e] = *reinterpret_cast<const float2*>(p.part_ml + pi * 2);
+        const int sl = in ? s0 + e : s0;
+        const int64_t pi = (base + sl) * 32 + q;
+        ml[e] = make_float2(coherent_loadf(p.part_ml + pi * 2), coherent_loadf(p.part_ml + pi * 2 + 1));
         if (!in) ml[e] = make_float2(-INFINITY, 0.f);
+        const int ob = ((sl * 32 + q) * D + 32 * ch) * 4;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) o[e][k] = *reinterpret_cast<const float4*>(p.part_o + pi * D + 32 * ch + 4 * k);
+        for (int k = 0; k < 8; ++k)
+          o[e][k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, ob + 16 * k, 0, 16));
       }
 #pragma unroll
       for (int e = 0; e < U2; ++e) {
@@ -781,7 +855,7 @@ __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g,
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] *= inv;
     constexpr int RB = D * Lay<BF>::ELT;
-    const int pos = p.gidx[(int64_t)b * p.n + idx];
+    const int pos = coherent_load(p.gidx + (int64_t)b * p.n + idx);
     uint8_t* orow = p.O + (((int64_t)b * p.H + h) * p.n + pos) * RB + 32 * ch * Lay<BF>::ELT;
 #pragma unroll
     for (int k = 0; k < 8; ++k) store_row4<BF>(orow + 4 * k * Lay<BF>::ELT, acc + 4 * k);
@@ -857,12 +931,14 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
 }
 
 // ---------------------------------------------------------------------------
-// Fast path for bf16 storage and batch rows whose real tokens are a prefix
-// [0, nv) (no padding, or a padded tail): the common case.
+// Fast path for bf16 storage where the real tokens among the keys a workgroup
+// reads are a prefix of them (no padding, or a padded tail): the common case.
+// A band workgroup checks this over its own key range; a global-row
+// workgroup takes it when the whole batch row's real tokens are [0, nv).
 //
-// Keys are fetched with buffer loads whose range is the nv real rows of the
-// (batch, head), so the hardware returns zeros for every key before the start,
-// past the end or in the padded tail -- no clamping, no flag loads, no zeroing
+// Keys are fetched with buffer loads whose range ends at the first padded
+// row, so the hardware returns zeros for every key before the start, past the
+// end or in the padded tail -- no clamping, no flag loads, no zeroing
 // selects.  Validity of the keys of a tile is then pure scalar arithmetic.
 // K and V tiles are stored row-major (128 B rows) with 16-byte chunks XOR-
 // swizzled per row, so that the b128 reads of the QK^T A operand and the
@@ -1228,7 +1304,7 @@ __device__ __forceinline__ void stage_chunk(int wave, int lane, int e, int& srow
 // is empty) applies its mask to the scores first, so its probabilities are
 // exactly zero where excluded.
 template <class Idle, class Issue, class Active, class Masked, class MaskOf, class Pre>
-__device__ __forceinline__ void half_pipe(int U, const Idle& idle, const Issue& issue,
+__device__ __forceinline__ void half_pipe(const int& U, const Idle& idle, const Issue& issue,
                                           const Active& active, const Masked& masked,
                                           const MaskOf& mask_of, const Pre& pre,
                                           const QOp<true>& qo, const FLane& fl, BandRow& st,
@@ -1430,8 +1506,15 @@ __device__ __forceinline__ void half_pipe(int U, const Idle& idle, const Issue& 
   if (U > 0) pv_half(pb, vslot(U - 1) + 4096);
 }
 
-__device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, int nv,
-                             uint8_t* smem) {
+// Band workgroup on the fast path.  It does not wait for the compaction of its
+// batch row before it starts: the padding of the keys its band steps can read
+// and of its own rows comes straight from the local attention mask, and the
+// row's global-position list is needed only for the global columns, which
+// follow the band steps; the wait for it sits after the first key batches are
+// issued.  Returns false, having written nothing, when the real tokens among
+// those keys are not a prefix of them; the general path then takes the
+// workgroup.
+__device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, uint8_t* smem) {
   constexpr int RB = 128;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -1445,29 +1528,75 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   }
   const int R0 = local * ROWS_WG;
   const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
-  const int nrv = nv > rho ? (nv - rho + s - 1) / s : 0;   // subsequence keys that are real tokens
   const int r = p.r;
 
   // band steps: step u holds subsequence keys kb0 + 64 u .. + 63
   const int kb = R0 - r;
   const int T = (ROWS_WG - 1 + 2 * r) / 64 + 1;
   const int t_lo = (-kb - 63 > 0) ? (-kb - 63 + 63) / 64 : 0;
-  int t_hi = nrv - 1 - kb >= 0 ? (nrv - 1 - kb) / 64 : -1;
-  if (t_hi > T - 1) t_hi = T - 1;
-  const int nband = R0 < nrv && t_hi >= t_lo ? t_hi - t_lo + 1 : 0;
-  int g = p.gcnt[b];
-  if (g > p.max_global) g = p.max_global;
-  const int gmain = g < GL_MAX ? g : GL_MAX;
-  const int ngt = R0 < nrv ? (gmain + 63) / 64 : 0;
-  const int U = nband + ngt;
   const int kb0 = kb + 64 * t_lo;
 
   const int R0w = R0 + 32 * wave;
   const int my_i = R0w + qi;
   const bool row_in = my_i < nr;
   const int my_pos = rho + (row_in ? my_i : 0) * s;
-  uint8_t my_fl = 0;         // loaded while the first keys are in flight
-  bool wave_work = false;    // the wave has a local row
+
+  // Padding of the subsequence keys [sc_lo, sc_hi) that any band step can
+  // read, and the flags of this lane's row, from the masks.
+  const float* lmb = p.lmask + (int64_t)b * n;
+  const float* gmb = p.gmask + (int64_t)b * n;
+  const float l_row = row_in ? lmb[my_pos] : 0.0f;
+  const float g_row = row_in ? gmb[my_pos] : 0.0f;
+  const int sc_lo = kb0 > 0 ? kb0 : 0;
+  const int sc_hi = kb + 64 * T < nr ? kb + 64 * T : nr;
+  int first = nr, ninv = 0;
+  for (int i0 = sc_lo + tid; i0 < sc_hi; i0 += 4 * NT) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e * NT;
+      v[e] = i < sc_hi ? lmb[rho + i * s] : 1.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool pad = v[e] == 0.0f;
+      const int i = i0 + e * NT;
+      first = pad && i < first ? i : first;
+      ninv += pad ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int f2 = __shfl_xor(first, o);
+    first = f2 < first ? f2 : first;
+    ninv += __shfl_xor(ninv, o);
+  }
+  __shared__ int s_pad[2 * NW];
+  if (lane == 0) {
+    s_pad[2 * wave] = first;
+    s_pad[2 * wave + 1] = ninv;
+  }
+  __syncthreads();
+  first = nr;
+  ninv = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    first = s_pad[2 * w] < first ? s_pad[2 * w] : first;
+    ninv += s_pad[2 * w + 1];
+  }
+  // real tokens among the readable keys must be exactly [.., first)
+  if (ninv != 0 && ninv != sc_hi - first) return false;
+  const int nrv = first;                                 // subsequence keys below are real
+  const int nv_pos = ninv ? rho + first * s : n;         // positions below are readable
+
+  int t_hi = nrv - 1 - kb >= 0 ? (nrv - 1 - kb) / 64 : -1;
+  if (t_hi > T - 1) t_hi = T - 1;
+  const int nband = R0 < nrv && t_hi >= t_lo ? t_hi - t_lo + 1 : 0;
+  // the global columns, known once the row's compaction is visible
+  int g = 0, gmain = 0, U = nband;
+
+  const uint8_t my_fl = (uint8_t)((l_row != 0.0f ? 1 : 0) | (l_row != 0.0f && g_row != 0.0f ? 2 : 0));
+  const bool wave_work = __any(row_in && (my_fl & 3) == 1);   // the wave has a local row
 
   // this wave's band steps with any key of its windows [ua, ub], and those
   // with every key inside all of its rows' windows [fa, fb]
@@ -1480,15 +1609,13 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   const int fa = floordiv(fl_lo - kb0 + 63, 64);
   const int fb = floordiv(fl_hi - 63 - kb0, 64);
   auto active = [&](int u) {
-    return u >= 0 && u < U && (u < nband ? (u >= ua && u <= ub) : (bool)wave_work);
+    return u >= 0 && u < U && (u < nband ? (u >= ua && u <= ub) : wave_work);
   };
   auto masked = [&](int u) { return u < fa || u > fb || u >= nband; };
 
   QOp<true> qo;
   BandRow st;
   auto load_rows = [&]() {
-    my_fl = p.flags[(int64_t)b * n + my_pos];
-    wave_work = __any(row_in && (my_fl & 3) == 1);
     qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
     // Take Q out of the compiler's view of outstanding loads here: the loop
     // below issues buffer-to-LDS loads the compiler does not count, so a wait
@@ -1524,8 +1651,8 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
 
   int32_t* gl = reinterpret_cast<int32_t*>(smem + B_GL_OFF);
   int32_t* jr = reinterpret_cast<int32_t*>(smem + B_JR_OFF);
-  const i32x4 dk = make_desc(p.K + head * RB, nv * RB);
-  const i32x4 dv = make_desc(p.V + head * RB, nv * RB);
+  const i32x4 dk = make_desc(p.K + head * RB, nv_pos * RB);
+  const i32x4 dv = make_desc(p.V + head * RB, nv_pos * RB);
   int kbase[B_CH], vbase[B_CH];
   const int step_b = 64 * s * RB;
 #pragma unroll
@@ -1540,15 +1667,18 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
   const uint32_t lds_w = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem) +
                          wave * (B_CH * 1024);
   // K (is_v false) or V of step t into its ring slot: band steps are strided
-  // subsequence rows, global steps the listed global positions
+  // subsequence rows, global steps the listed global positions (real tokens
+  // anywhere in the row, so read through a range over all n rows)
   auto issue = [&](int t, bool is_v) {
     const uint32_t base = lds_w + (is_v ? B_V_OFF : 0) + (t % B_NSLOT) * B_STEP;
     int off[B_CH];
+    i32x4 d = is_v ? dv : dk;
     if (t < nband) {
       const int adv = t * step_b;
 #pragma unroll
       for (int e = 0; e < B_CH; ++e) off[e] = (is_v ? vbase[e] : kbase[e]) + adv;
     } else {
+      d[2] = n * RB;
 #pragma unroll
       for (int e = 0; e < B_CH; ++e) {
         int srow, ck16, cv16;
@@ -1559,13 +1689,12 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
         off[e] = in ? rowoff + (is_v ? cv16 : ck16) : OOB_OFF;
       }
     }
-    const i32x4 d = is_v ? dv : dk;
     dma16i<0>(d, off[0], base);
     dma16i<1024>(d, off[1], base);
   };
   auto fill = [&]() {
     for (int j = tid; j < gmain; j += NT) {
-      const int pos = gidx_b[j];
+      const int pos = coherent_load(gidx_b + j);
       const int dp = pos - rho;
       gl[j] = pos;
       jr[j] = (dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
@@ -1587,15 +1716,29 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     return m;
   };
 
-  // the global-position list must be in LDS before a global step is staged
-  const bool early_fill = nband < B_NSLOT - 1 && ngt > 0;
+  // the global columns: wait for the row's compaction, then count them
+  auto learn_globals = [&]() {
+    if (wait_ready(p, b, false)) {
+      g = coherent_load(p.gcnt + b);
+      if (g > p.max_global) g = p.max_global;
+    }
+    gmain = g < GL_MAX ? g : GL_MAX;
+    U = nband + (R0 < nrv ? (gmain + 63) / 64 : 0);
+  };
+  // the global-position list must be in LDS before a global step is staged;
+  // with fewer band steps than the prologue stages, that is before it
+  const bool early_fill = nband < B_NSLOT - 1;
   if (early_fill) {
+    learn_globals();
     fill();
     __syncthreads();
   }
   auto pre = [&]() {
     load_rows();
-    if (!early_fill) fill();
+    if (!early_fill) {
+      learn_globals();
+      fill();
+    }
   };
   auto idle = [&]() { return !wave_work; };
   half_pipe(U, idle, issue, active, masked, mask_of, pre, qo, fl, st, c, h32, smem);
@@ -1608,15 +1751,15 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
     sm.l = st.l;
     sm.o[0] = st.o[0];
     sm.o[1] = st.o[1];
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * RB, nv * RB);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * RB, nv * RB);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * RB, n * RB);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * RB, n * RB);
     const int U2 = (g - GL_MAX + KT - 1) / KT;
     for (int u2 = 0; u2 < U2; ++u2) {
       __syncthreads();
       const int jb = GL_MAX + u2 * KT;
       for (int j = tid; j < KT; j += NT) {
         const int idx = jb + j;
-        const int pos = idx < g ? gidx_b[idx] : 0;
+        const int pos = idx < g ? coherent_load(gidx_b + idx) : 0;
         const int dp = pos - rho;
         gl[j] = pos;
         jr[j] = (idx < g && dp >= 0 && dp % s == 0) ? dp / s : JREL_NONE;
@@ -1668,6 +1811,7 @@ __device__ void band_wg_fast(const Params& p, int b, int h, int local, int s, in
       }
     }
   }
+  return true;
 }
 
 // Global-row workgroups on the bf16 fast path: up to NW query tiles of 32
@@ -1681,7 +1825,7 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   constexpr int RB = 128;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  int g = p.gcnt[b];
+  int g = coherent_load(p.gcnt + b);
   if (g > p.max_global) g = p.max_global;
   const int nqt_b = (g + 31) / 32;
   if (qg * NW >= nqt_b) return;                     // uniform over the workgroup
@@ -1694,7 +1838,7 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   const bool qok = wave_work && qidx < g;
   QOp<true> qo;
   auto load_rows = [&]() {   // while the first keys are in flight
-    const int qpos = gidx_b[qok ? qidx : 0];
+    const int qpos = coherent_load(gidx_b + (qok ? qidx : 0));
     qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
@@ -1773,12 +1917,19 @@ __device__ __forceinline__ int xcd_remap(int pid, int count) {
   return x * q + (x < rem ? x : rem) + idx;
 }
 
-// Band workgroups come first in dispatch order (they are the long ones);
-// global-row workgroups fill the gaps behind them.
+// Dispatch order: the compaction workgroups (one per batch row, padded to a
+// multiple of 8 so that the band workgroups behind them keep their XCD
+// placement), then the band workgroups (the long ones), then the global-row
+// workgroups that fill the gaps behind them.
 template <bool BF>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int bid = blockIdx.x;
+  int bid = blockIdx.x;
+  if (bid < p.n_comp_wg) {
+    if (bid < p.B) compact_row(p, bid, smem);
+    return;
+  }
+  bid -= p.n_comp_wg;
   if (bid >= p.n_band_wg) {
     const int lg = bid - p.n_band_wg;
     if (lg >= p.B * p.H * p.nqg * p.nsplit) return;
@@ -1788,13 +1939,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     t /= p.nqg;
     const int h = t % p.H;
     const int b = t / p.H;
+    if (!wait_ready(p, b, false)) return;
     if constexpr (BF) {
-      const int nv = p.vlen[b];
+      const int nv = coherent_load(p.vlen + b);
       if (nv >= 0) {
         global_wg_fast(p, b, h, qg, sp, nv, smem);
         return;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the general path reads with plain loads
     global_wg<BF>(p, b, h, qg, sp, smem);
   } else {
     const int lb = xcd_remap(bid, p.n_band_wg);
@@ -1817,12 +1970,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
       s = p.head_stride[h];
     }
     if constexpr (BF) {
-      const int nv = p.vlen[b];
-      if (nv >= 0 && p.band_fast) {
-        band_wg_fast(p, b, h, local, s, nv, smem);
-        return;
-      }
+      if (p.band_fast && band_wg_fast(p, b, h, local, s, smem)) return;
     }
+    if (!wait_ready(p, b, true)) return;
     band_wg<BF>(p, b, h, local, s, smem);
   }
 }

@@ -19,7 +19,7 @@
 
 namespace {
 
-constexpr int kNumKernels = 2;
+constexpr int kNumKernels = 1;
 
 // LWATTN_DEBUG=1 in the environment prints every failing HIP call to stderr.
 bool hip_ok(hipError_t e, const char* what) {
@@ -40,7 +40,7 @@ struct lwattn_plan_s {
   int device = 0;
   // geometry
   int nqt = 0, nqg = 0, nsplit = 0, ksplit = 0;
-  int n_glob_wg = 0, n_band_wg = 0, blocks_per_b = 0;
+  int n_comp_wg = 0, n_glob_wg = 0, n_band_wg = 0, blocks_per_b = 0;
   int uni_stride = 0, blocks_per_head = 0;
   int band_fast = 0;
   std::vector<int32_t> stride_host, blk_host;
@@ -54,11 +54,16 @@ struct lwattn_plan_s {
   float* part_o = nullptr;
   float* part_ml = nullptr;
   int32_t* tile_cnt = nullptr;
+  int32_t* ready = nullptr;   // [B] epoch of the last compaction of each batch row
+  int32_t* fault = nullptr;   // sticky: a workgroup gave up waiting for its row
+  int32_t epoch = 0;          // forwards launched (kept in 1 .. INT32_MAX - 1)
   int32_t* head_stride = nullptr;
   int32_t* head_blk = nullptr;
   // timing
   int timing_cap = 0;
   int timing_calls = 0;
+  int timing_every = 1;    // record the events of every k-th forward
+  int64_t timing_seen = 0; // forwards since timing was enabled
   std::vector<hipEvent_t> events;   // (kNumKernels + 1) per recorded forward
 };
 
@@ -72,6 +77,8 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->part_o);
   (void)hipFree(p->part_ml);
   (void)hipFree(p->tile_cnt);
+  (void)hipFree(p->ready);
+  (void)hipFree(p->fault);
   (void)hipFree(p->head_stride);
   (void)hipFree(p->head_blk);
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
@@ -160,9 +167,12 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   int smax = 1;
   for (int h = 0; h < H; ++h) smax = std::max(smax, stride[h]);
   p->band_fast = (cfg->dtype == LWATTN_BF16 && (int64_t)n + 128 * (int64_t)smax < ((int64_t)1 << 24)) ? 1 : 0;
+  // compaction workgroups lead the grid, padded to a multiple of 8 so that the
+  // band workgroups behind them keep their XCD placement
+  const int64_t ncomp = ((int64_t)B + 7) / 8 * 8;
   // global-row geometry: the key slices are sized so that the global-row
-  // workgroups fill what the band workgroups leave of the last round of
-  // workgroup slots (two per compute unit), with at least 64 of them
+  // workgroups fill what the compaction and band workgroups leave of the last
+  // round of workgroup slots (two per compute unit), with at least 64 of them
   int ncu = 256;
   {
     hipDeviceProp_t prop;
@@ -175,7 +185,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   int64_t nglob = 0;
   if (p->nqt > 0 && n > 0 && B > 0 && H > 0) {
     const int64_t units = (int64_t)B * H * p->nqg;
-    int64_t target = slots - nband % slots;
+    int64_t target = slots - (ncomp + nband) % slots;
     if (target < 64) target = 64;
     int64_t want = (target + units - 1) / units;
     const int64_t maxs = (n + 127) / 128;
@@ -186,10 +196,11 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
     nglob = units * p->nsplit;
   }
   const int64_t nglob_pad = (nglob + 7) / 8 * 8;
-  if (nband + nglob_pad > INT32_MAX) {
+  if (ncomp + nband + nglob_pad > INT32_MAX) {
     free_plan(p);
     return LWATTN_E_INVALID;
   }
+  p->n_comp_wg = (int)ncomp;
   p->n_band_wg = (int)nband;
   p->n_glob_wg = (int)nglob_pad;
   p->smem = cfg->dtype == LWATTN_BF16 ? lwk::smem_bytes<true>() : lwk::smem_bytes<false>();
@@ -211,6 +222,8 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->part_o, nparts * lwk::D * 4);
   alloc((void**)&p->part_ml, nparts * 2 * 4);
   alloc((void**)&p->tile_cnt, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4);
+  alloc((void**)&p->ready, (size_t)B * 4);
+  alloc((void**)&p->fault, 4);
   alloc((void**)&p->head_stride, (size_t)H * 4);
   alloc((void**)&p->head_blk, (size_t)(H + 1) * 4);
   if (!ok) {
@@ -222,6 +235,8 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
       (B > 0 && !hip_ok(hipMemset(p->status, 0, (size_t)B * 4), "hipMemset")) ||
       (B > 0 && !hip_ok(hipMemset(p->gcnt, 0, (size_t)B * 4), "hipMemset")) ||
       !hip_ok(hipMemset(p->tile_cnt, 0, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4), "hipMemset") ||
+      (B > 0 && !hip_ok(hipMemset(p->ready, 0, (size_t)B * 4), "hipMemset")) ||
+      !hip_ok(hipMemset(p->fault, 0, 4), "hipMemset") ||
       !hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize")) {
     free_plan(p);
     return LWATTN_E_DEVICE;
@@ -269,6 +284,11 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   prm.part_o = p->part_o;
   prm.part_ml = p->part_ml;
   prm.tile_cnt = p->tile_cnt;
+  prm.ready = p->ready;
+  prm.fault = p->fault;
+  p->epoch = p->epoch >= INT32_MAX - 1 ? 1 : p->epoch + 1;
+  prm.epoch = p->epoch;
+  prm.n_comp_wg = p->n_comp_wg;
   prm.head_stride = p->head_stride;
   prm.head_blk = p->head_blk;
   prm.B = c.B;
@@ -291,21 +311,21 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   for (int h = 0; h < lwk::MAXH_ARG; ++h) prm.hs[h] = h < c.H ? p->stride_host[h] : 0;
   for (int h = 0; h <= lwk::MAXH_ARG; ++h) prm.hb[h] = h <= c.H ? p->blk_host[h] : 0;
 
-  const bool timed = p->timing_cap > 0 && p->timing_calls < p->timing_cap;
+  bool timed = false;
+  if (p->timing_cap > 0 && p->timing_calls < p->timing_cap) {
+    timed = (p->timing_seen % p->timing_every) == 0;
+    ++p->timing_seen;
+  }
   hipEvent_t* ev = timed ? &p->events[(size_t)p->timing_calls * (kNumKernels + 1)] : nullptr;
   if (timed && !hip_ok(hipEventRecord(ev[0], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
 
-  hipLaunchKernelGGL(lwk::compact_kernel, dim3(c.B), dim3(lwk::CT), 0, stream, prm);
-  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-  if (timed && !hip_ok(hipEventRecord(ev[1], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
-
-  const int grid = p->n_glob_wg + p->n_band_wg;
+  const int grid = p->n_comp_wg + p->n_band_wg + p->n_glob_wg;
   if (c.dtype == LWATTN_BF16)
     hipLaunchKernelGGL(lwk::attn_kernel<true>, dim3(grid), dim3(lwk::NT), p->smem, stream, prm);
   else
     hipLaunchKernelGGL(lwk::attn_kernel<false>, dim3(grid), dim3(lwk::NT), p->smem, stream, prm);
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-  if (timed && !hip_ok(hipEventRecord(ev[2], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
+  if (timed && !hip_ok(hipEventRecord(ev[1], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
 
   if (timed) ++p->timing_calls;
   return LWATTN_OK;
@@ -329,6 +349,9 @@ lwattn_status lwattn_sync_status(lwattn_plan_t p, hipStream_t stream) {
   if (!hip_ok(hipStreamSynchronize(stream), "hipStreamSynchronize")) return LWATTN_E_DEVICE;
   const int B = p->cfg.B;
   if (B == 0) return LWATTN_OK;
+  int32_t fault = 0;
+  if (!hip_ok(hipMemcpy(&fault, p->fault, 4, hipMemcpyDeviceToHost), "hipMemcpy")) return LWATTN_E_DEVICE;
+  if (fault) return LWATTN_E_DEVICE;
   std::vector<int32_t> st(B);
   if (!hip_ok(hipMemcpy(st.data(), p->status, (size_t)B * 4, hipMemcpyDeviceToHost), "hipMemcpy"))
     return LWATTN_E_DEVICE;
@@ -344,6 +367,7 @@ lwattn_status lwattn_timing_enable(lwattn_plan_t p, int32_t max_calls) {
   p->events.clear();
   p->timing_cap = 0;
   p->timing_calls = 0;
+  p->timing_seen = 0;
   const size_t ne = (size_t)max_calls * (kNumKernels + 1);
   p->events.reserve(ne);
   for (size_t i = 0; i < ne; ++i) {
@@ -355,11 +379,18 @@ lwattn_status lwattn_timing_enable(lwattn_plan_t p, int32_t max_calls) {
   return LWATTN_OK;
 }
 
+lwattn_status lwattn_timing_every(lwattn_plan_t p, int32_t every) {
+  if (!p || every < 1) return LWATTN_E_INVALID;
+  p->timing_every = every;
+  p->timing_seen = 0;
+  return LWATTN_OK;
+}
+
 lwattn_status lwattn_timing_read(lwattn_plan_t p, float* ms, int32_t cap, int32_t* nkernels,
                                  int32_t* ncalls) {
   if (!p || !nkernels || !ncalls || (cap > 0 && !ms)) return LWATTN_E_INVALID;
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
-  float tot[kNumKernels] = {0.f, 0.f};
+  float tot[kNumKernels] = {};
   for (int call = 0; call < p->timing_calls; ++call) {
     hipEvent_t* ev = &p->events[(size_t)call * (kNumKernels + 1)];
     if (!hip_ok(hipEventSynchronize(ev[kNumKernels]), "hipEventSynchronize")) return LWATTN_E_DEVICE;

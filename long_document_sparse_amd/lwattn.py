@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "liblwattn.so")
 
 LWATTN_F32, LWATTN_BF16 = 0, 1
 OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_DEVICE, E_TOO_MANY_GLOBALS = range(6)
-KERNELS = ("compact", "attention")
+KERNELS = ("attention",)
 
 # (name, restype, argtypes) of every exported function, in header order
 _c_p = ctypes.c_void_p
@@ -42,6 +42,7 @@ SIGNATURES = [
     ("lwattn_global_index", ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
     ("lwattn_sync_status", ctypes.c_int, [_c_p, _c_p]),
     ("lwattn_timing_enable", ctypes.c_int, [_c_p, _i32]),
+    ("lwattn_timing_every", ctypes.c_int, [_c_p, _i32]),
     ("lwattn_timing_read", ctypes.c_int, [_c_p, ctypes.POINTER(ctypes.c_float), _i32,
                                           ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     ("lwattn_timing_disable", ctypes.c_int, [_c_p]),
@@ -191,10 +192,15 @@ class Plan:
     def sync_status(self, stream=None) -> int:
         return int(self.lib.lwattn_sync_status(self.handle, _stream_handle(stream)))
 
-    def timing_enable(self, max_calls: int):
+    def timing_enable(self, max_calls: int, every: int = 1):
+        """Record per-kernel events for up to max_calls forwards, on every
+        `every`-th forward."""
         st = self.lib.lwattn_timing_enable(self.handle, int(max_calls))
         if st != OK:
             raise LwattnError(st, "lwattn_timing_enable")
+        st = self.lib.lwattn_timing_every(self.handle, int(every))
+        if st != OK:
+            raise LwattnError(st, "lwattn_timing_every")
 
     def timing_read(self):
         """({kernel: total ms}, calls) over the forwards recorded since timing_enable."""

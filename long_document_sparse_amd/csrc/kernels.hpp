@@ -1260,17 +1260,21 @@ __device__ __forceinline__ bf16x8 vfrag(const uint8_t* vt, int off) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Scheduling template for one phase: softmax VALU work first (while this
-// phase's MFMA operands finish landing), the 8 MFMAs spaced by the rest of it,
-// then the 12 LDS reads of the next phase's MFMA operands.
+// Scheduling template for one phase: each of the 8 MFMAs followed by the LDS
+// read(s) of the operand that replaces its own (two transposing reads for a
+// V^T fragment, one for a K fragment) and a share of the softmax VALU work,
+// then the rest of the softmax.
 __device__ __forceinline__ void interleave_hint() {
-  __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);   // VALU while the operands land
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // PV MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // its V^T fragment for the next phase
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // 6 VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // QK^T MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // its K fragment for the next phase
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // 6 VALU
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // LDS reads of the next phase
+  __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);             // the rest of the softmax
 }
 
 // MFMA operands of one phase: K of one half (A of QK^T) and V^T of one half
@@ -1352,6 +1356,31 @@ __device__ __forceinline__ void half_pipe(const int& U, const Idle& idle, const 
     a = mfma_bf16(ops.kf[2], qo.q[2], a);
     st.o[1] = mfma_bf16(ops.vf[1][1], pp[1], st.o[1]);
     a = mfma_bf16(ops.kf[3], qo.q[3], a);
+    sq = a;
+  };
+  // the same MFMAs, each followed by the LDS read of the operand that
+  // replaces its own in the next phase (K rows at ks, V^T at vs): the reads
+  // leave in a stream across the phase instead of in one burst, and the
+  // registers of an operand are reused as soon as its MFMA has taken it
+  auto phase_mfma_next = [&](f32x16& sq, PhaseOps& ops, const bf16x8 (&pp)[2], const uint8_t* ks,
+                             const uint8_t* vs) {
+    f32x16 a = {};
+    st.o[0] = mfma_bf16(ops.vf[0][0], pp[0], st.o[0]);
+    ops.vf[0][0] = vfrag(vs, fl.v[0]);
+    a = mfma_bf16(ops.kf[0], qo.q[0], a);
+    ops.kf[0] = *reinterpret_cast<const bf16x8*>(ks + fl.k[0]);
+    st.o[1] = mfma_bf16(ops.vf[0][1], pp[0], st.o[1]);
+    ops.vf[0][1] = vfrag(vs, fl.v[1]);
+    a = mfma_bf16(ops.kf[1], qo.q[1], a);
+    ops.kf[1] = *reinterpret_cast<const bf16x8*>(ks + fl.k[1]);
+    st.o[0] = mfma_bf16(ops.vf[1][0], pp[1], st.o[0]);
+    ops.vf[1][0] = vfrag(vs, fl.v[0] + 2048);
+    a = mfma_bf16(ops.kf[2], qo.q[2], a);
+    ops.kf[2] = *reinterpret_cast<const bf16x8*>(ks + fl.k[2]);
+    st.o[1] = mfma_bf16(ops.vf[1][1], pp[1], st.o[1]);
+    ops.vf[1][1] = vfrag(vs, fl.v[1] + 2048);
+    a = mfma_bf16(ops.kf[3], qo.q[3], a);
+    ops.kf[3] = *reinterpret_cast<const bf16x8*>(ks + fl.k[3]);
     sq = a;
   };
   auto soft_half = [&](f32x16& sx, bf16x8 (&pb)[2]) {
@@ -1463,9 +1492,8 @@ __device__ __forceinline__ void half_pipe(const int& U, const Idle& idle, const 
     const bool msk = masked(u);
     if (msk) mask_half(sx, mask_of(u, 0), h32);
     // phase A
-    phase_mfma(sy, ops, pb);
+    phase_mfma_next(sy, ops, pb, kslot(u + 1), vslot(u));
     float ts = band_exp_half(sx, c, st.m, pa);
-    load_ops(ops, kslot(u + 1), vslot(u));
     interleave_hint();
     if (__builtin_expect(__any(ts > SUM_HI), 0)) {
       rare_at = 1;
@@ -1474,10 +1502,10 @@ __device__ __forceinline__ void half_pipe(const int& U, const Idle& idle, const 
     }
     st.l += ts;
     if (msk) mask_half(sy, mask_of(u, 1), h32);
-    // phase B
-    phase_mfma(sx, ops, pa);
+    // phase B (the operands read for step u+1 = U are never used; the reads
+    // stay inside the ring)
+    phase_mfma_next(sx, ops, pa, kslot(u + 1) + 4096, vslot(u) + 4096);
     ts = band_exp_half(sy, c, st.m, pb);
-    if (u + 1 < U) load_ops(ops, kslot(u + 1) + 4096, vslot(u) + 4096);
     interleave_hint();
     if (__builtin_expect(__any(ts > SUM_HI), 0)) {
       rare_at = 2;
@@ -1547,6 +1575,20 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   const float* gmb = p.gmask + (int64_t)b * n;
   const float l_row = row_in ? lmb[my_pos] : 0.0f;
   const float g_row = row_in ? gmb[my_pos] : 0.0f;
+  // this lane's query row and its own key row (the initial offset), in the
+  // same round trip as the masks
+  QOp<true> qo;
+  qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
+  uint4 kdiag[4];
+  {
+    const uint8_t* krow = p.K + (head + my_pos) * RB + 64 * h32;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) kdiag[cc] = *reinterpret_cast<const uint4*>(krow + 16 * cc);
+  }
+  // the output row, kept in registers: reloading the pointer at the end
+  // would be a scalar load that misses by then
+  uint64_t orow_bits = (uint64_t)(uintptr_t)(p.O + (head + my_pos) * RB);
+  asm volatile("" : "+v"(orow_bits));
   const int sc_lo = kb0 > 0 ? kb0 : 0;
   const int sc_hi = kb + 64 * T < nr ? kb + 64 * T : nr;
   int first = nr, ninv = 0;
@@ -1613,24 +1655,21 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   };
   auto masked = [&](int u) { return u < fa || u > fb || u >= nband; };
 
-  QOp<true> qo;
-  BandRow st;
-  auto load_rows = [&]() {
-    qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
-    // Take Q out of the compiler's view of outstanding loads here: the loop
-    // below issues buffer-to-LDS loads the compiler does not count, so a wait
-    // it placed for Q inside the loop would also wait for those.
+  // Q is complete here (the scan waited for every load): take it out of the
+  // compiler's view of outstanding loads, since the loop below issues
+  // buffer-to-LDS loads the compiler does not count, and a wait it placed for
+  // Q inside the loop would also wait for those.
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
+  for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
+  BandRow st;
+  {
     // the row's own score sets the initial offset (this lane's 32 channels,
     // then both half-lanes)
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const uint8_t* krow = p.K + (head + my_pos) * RB + 64 * h32;
     float sd = 0.f;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * cc);
-      const bf16x8 k8 = __builtin_bit_cast(bf16x8, kv);
+      const bf16x8 k8 = __builtin_bit_cast(bf16x8, kdiag[cc]);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const bf16x2 a = {qo.q[cc][e], qo.q[cc][e + 1]};
@@ -1640,7 +1679,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
     }
     st.m = half_sum(sd) * p.c;
     asm volatile("" : "+v"(st.m));
-  };
+  }
   st.l = 0.f;
   st.first = false;
 #pragma unroll
@@ -1734,7 +1773,6 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
     __syncthreads();
   }
   auto pre = [&]() {
-    load_rows();
     if (!early_fill) {
       learn_globals();
       fill();
@@ -1799,7 +1837,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   if (row_in && (my_fl & 2) == 0) {
     const bool valid = (my_fl & 1) != 0;
     const float inv = valid ? 1.0f / lt : 0.0f;
-    uint8_t* orow = p.O + (head + my_pos) * RB;
+    uint8_t* orow = reinterpret_cast<uint8_t*>((uintptr_t)orow_bits);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll

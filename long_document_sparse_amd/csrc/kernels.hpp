@@ -1307,8 +1307,14 @@ __device__ __forceinline__ void stage_chunk(int wave, int lane, int e, int& srow
 // where this wave has no key at all: masked(u) covers those, and their mask
 // is empty) applies its mask to the scores first, so its probabilities are
 // exactly zero where excluded.
-template <class Idle, class Issue, class Active, class Masked, class MaskOf, class Pre>
-__device__ __forceinline__ void half_pipe(const int& U, const Idle& idle, const Issue& issue,
+//
+// Steps plain_lo..plain_hi are "plain" for this wave: active, without a masked
+// key, and with both loads of their batch band steps (issue_band).  Their head
+// is lean: a fixed load wait and no mask or issue-kind tests.
+template <class Idle, class Issue, class IssueBand, class Active, class Masked, class MaskOf,
+          class Pre>
+__device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_hi, const Idle& idle,
+                                          const Issue& issue, const IssueBand& issue_band,
                                           const Active& active, const Masked& masked,
                                           const MaskOf& mask_of, const Pre& pre,
                                           const QOp<true>& qo, const FLane& fl, BandRow& st,
@@ -1488,8 +1494,17 @@ __device__ __forceinline__ void half_pipe(const int& U, const Idle& idle, const 
   float ts_rare = 0.f;
   int u = 0;
   for (; u < U; ++u) {
-    head_of_step(u);
-    const bool msk = masked(u);
+    const bool plain = u >= plain_lo && u <= plain_hi;
+    if (plain) {
+      // batch u-2 has landed (the 4 loads of batch u-1 may still fly)
+      wait_loads<4>();
+      __syncthreads();
+      issue_band(u + 3, false);
+      issue_band(u + 2, true);
+    } else {
+      head_of_step(u);
+    }
+    const bool msk = !plain && masked(u);
     if (msk) mask_half(sx, mask_of(u, 0), h32);
     // phase A
     phase_mfma_next(sy, ops, pb, kslot(u + 1), vslot(u));
@@ -1731,6 +1746,13 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
     dma16i<0>(d, off[0], base);
     dma16i<1024>(d, off[1], base);
   };
+  auto issue_band = [&](int t, bool is_v) {   // t < nband
+    const uint32_t base = lds_w + (is_v ? B_V_OFF : 0) + (t % B_NSLOT) * B_STEP;
+    const int adv = t * step_b;
+    const i32x4 d = is_v ? dv : dk;
+    dma16i<0>(d, (is_v ? vbase[0] : kbase[0]) + adv, base);
+    dma16i<1024>(d, (is_v ? vbase[1] : kbase[1]) + adv, base);
+  };
   auto fill = [&]() {
     for (int j = tid; j < gmain; j += NT) {
       const int pos = coherent_load(gidx_b + j);
@@ -1779,7 +1801,12 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
     }
   };
   auto idle = [&]() { return !wave_work; };
-  half_pipe(U, idle, issue, active, masked, mask_of, pre, qo, fl, st, c, h32, smem);
+  // plain steps of this wave: every key inside all of its rows' windows, and
+  // the batch (K of u+3, V of u+2) made of band steps
+  const int plain_lo = fa > 0 ? fa : 0;
+  const int plain_hi = fb < nband - 4 ? fb : nband - 4;
+  half_pipe(U, plain_lo, plain_hi, idle, issue, issue_band, active, masked, mask_of, pre, qo, fl,
+            st, c, h32, smem);
 
   if (g > GL_MAX && R0 < nrv) {
     // global columns past the LDS copy, 32 at a time through the first K and
@@ -1920,7 +1947,8 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   auto masked = [&](int u) { return j_start + 64 * u + 64 > j_use; };
   auto mask_of = [&](int u, int hf) { return bit_range(0, j_use - (j_start + 64 * u + 32 * hf)); };
   auto idle = [&]() { return !wave_work; };
-  half_pipe(U, idle, issue, active, masked, mask_of, load_rows, qo, fl, st, p.c, h32, smem);
+  half_pipe(U, 1, 0, idle, issue, issue, active, masked, mask_of, load_rows, qo, fl, st, p.c, h32,
+            smem);
 
   const float lt = half_sum(st.l);
   if (qok) {

@@ -13,10 +13,11 @@ The default workload is "base": B=1, H=12, n=4096, d=64, w=512 (+-256), no
 dilation, one global token at position 0, bf16 storage, fp32 accumulation.
 
 Timing is "warm": forwards run back to back, so inputs that fit the 256 MB
-last-level cache stay there between steps.  Per-kernel durations come from
-HIP events that the library records on the stream the kernel runs on, around
-the kernel of every fourth forward of the timed loop (recording them on every
-forward would make the host, not the GPU, set the pace of the loop).
+last-level cache stay there between steps.  Kernel durations come from HIP
+events that the dispatch of the attention kernel itself records at the start
+and the end of its execution, on every fourth forward of the timed loop
+(recording them on every forward would make the host, not the GPU, set the
+pace of the loop).
 
 --copy-probe runs, after the timed loop, a plain device-to-device copy of the
 given size a few times; a counter pass over the same command then gives the

@@ -134,9 +134,10 @@ lwattn_status lwattn_global_index(lwattn_plan_t plan, int32_t* gidx, int32_t* gc
  * and the plan should be destroyed. */
 lwattn_status lwattn_sync_status(lwattn_plan_t plan, hipStream_t stream);
 
-/* Kernel timing for measurement.  While enabled, every forward records HIP
- * events around each of its kernel launches on its stream (up to `max_calls`
- * forwards are kept).  lwattn_timing_read synchronizes on the recorded events
+/* Kernel timing for measurement.  While enabled, every forward's kernel is
+ * launched with a pair of HIP events that its dispatch records at the start
+ * and the end of the kernel's execution (hipExtLaunchKernel; up to
+ * `max_calls` forwards are kept).  lwattn_timing_read synchronizes on the recorded events
  * and returns, per kernel of the forward, the summed duration in milliseconds
  * (ms[k] for k < *nkernels, at most `cap`) and the number of recorded forwards.
  * A forward is one kernel (*nkernels = 1): the global-index compaction, the

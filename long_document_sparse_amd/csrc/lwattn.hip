@@ -4,6 +4,7 @@
 // A plan validates the configuration once, derives the launch geometry and
 // owns the device workspace; a forward only enqueues three kernels on the
 // caller's stream (see kernels.hpp) and never allocates or synchronizes.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -316,16 +317,21 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
     timed = (p->timing_seen % p->timing_every) == 0;
     ++p->timing_seen;
   }
-  hipEvent_t* ev = timed ? &p->events[(size_t)p->timing_calls * (kNumKernels + 1)] : nullptr;
-  if (timed && !hip_ok(hipEventRecord(ev[0], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
-
+  // timed forwards take their events from the dispatch itself (start and end
+  // of the kernel's execution), untimed ones launch plainly
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  if (timed) {
+    ev0 = p->events[(size_t)p->timing_calls * (kNumKernels + 1)];
+    ev1 = p->events[(size_t)p->timing_calls * (kNumKernels + 1) + 1];
+  }
   const int grid = p->n_comp_wg + p->n_band_wg + p->n_glob_wg;
   if (c.dtype == LWATTN_BF16)
-    hipLaunchKernelGGL(lwk::attn_kernel<true>, dim3(grid), dim3(lwk::NT), p->smem, stream, prm);
+    hipExtLaunchKernelGGL(lwk::attn_kernel<true>, dim3(grid), dim3(lwk::NT), (uint32_t)p->smem, stream,
+                          ev0, ev1, 0u, prm);
   else
-    hipLaunchKernelGGL(lwk::attn_kernel<false>, dim3(grid), dim3(lwk::NT), p->smem, stream, prm);
+    hipExtLaunchKernelGGL(lwk::attn_kernel<false>, dim3(grid), dim3(lwk::NT), (uint32_t)p->smem, stream,
+                          ev0, ev1, 0u, prm);
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-  if (timed && !hip_ok(hipEventRecord(ev[1], stream), "hipEventRecord")) return LWATTN_E_DEVICE;
 
   if (timed) ++p->timing_calls;
   return LWATTN_OK;

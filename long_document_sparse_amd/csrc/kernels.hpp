@@ -1162,7 +1162,9 @@ constexpr int B_NSLOT = 4;
 constexpr int B_V_OFF = B_NSLOT * B_STEP;
 constexpr int B_GL_OFF = 2 * B_NSLOT * B_STEP;
 constexpr int B_JR_OFF = B_GL_OFF + GL_MAX * 4;
-constexpr int B_SMEM = B_JR_OFF + GL_MAX * 4;
+constexpr int B_GH_OFF = B_JR_OFF + GL_MAX * 4;   // up to 32 global keys: K half | V half
+constexpr int B_GH_MAX = 32;
+constexpr int B_SMEM = B_GH_OFF + 2 * (B_STEP / 2);
 constexpr int B_CH = 512 / NT;          // 16-byte chunks per thread per 8 KB array of a step
 constexpr float SUM_HI = 16384.0f;      // 2^14
 static_assert(B_CH == 2, "each thread stages two chunks of every 8 KB array");
@@ -1311,12 +1313,17 @@ __device__ __forceinline__ void stage_chunk(int wave, int lane, int e, int& srow
 // Steps plain_lo..plain_hi are "plain" for this wave: active, without a masked
 // key, and with both loads of their batch band steps (issue_band).  Their head
 // is lean: a fixed load wait and no mask or issue-kind tests.
+//
+// With extra_half, after the last step the wave takes one more 32-key half
+// whose K and V sit at smem + B_GH_OFF (K half, then V half) under the lane
+// mask extra_mask() -- the few global columns of band rows.
 template <class Idle, class Issue, class IssueBand, class Active, class Masked, class MaskOf,
-          class Pre>
+          class Pre, class ExtraMask>
 __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_hi, const Idle& idle,
                                           const Issue& issue, const IssueBand& issue_band,
                                           const Active& active, const Masked& masked,
                                           const MaskOf& mask_of, const Pre& pre,
+                                          const bool& extra_half, const ExtraMask& extra_mask,
                                           const QOp<true>& qo, const FLane& fl, BandRow& st,
                                           float c, int h32, uint8_t* smem) {
   // the batch of step t: K of step t+3 and V of step t+2 (those that exist);
@@ -1547,6 +1554,16 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
   for (; u < U; ++u) slow_step(u);
   // PV of half 1 of the last step (its V landed with the batch of step U-3)
   if (U > 0) pv_half(pb, vslot(U - 1) + 4096);
+  if (extra_half) {
+    // staged before the loop; every step's wait and barrier has passed since
+    const uint8_t* gk = smem + B_GH_OFF;
+    f32x16 sg;
+    qk_half(sg, gk);
+    mask_half(sg, extra_mask(), h32);
+    bf16x8 pg[2];
+    soft_half(sg, pg);
+    pv_half(pg, gk + B_STEP / 2);
+  }
 }
 
 // Band workgroup on the fast path.  It does not wait for the compaction of its
@@ -1777,14 +1794,43 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
     return m;
   };
 
-  // the global columns: wait for the row's compaction, then count them
+  // the global columns: wait for the row's compaction, then count them; up to
+  // 32 of them take one extra half after the band steps (their K and V
+  // staged once, below), more take whole pipeline steps
+  bool gh = false;
   auto learn_globals = [&]() {
     if (wait_ready(p, b, false)) {
       g = coherent_load(p.gcnt + b);
       if (g > p.max_global) g = p.max_global;
     }
     gmain = g < GL_MAX ? g : GL_MAX;
-    U = nband + (R0 < nrv ? (gmain + 63) / 64 : 0);
+    gh = R0 < nrv && gmain > 0 && gmain <= B_GH_MAX;
+    U = nband + (R0 < nrv && !gh ? (gmain + 63) / 64 : 0);
+  };
+  // K and V rows of the <= 32 global keys into the extra half (waves 0 and 1
+  // stage its 32 rows, two chunks per lane per array), after gl[] is visible
+  auto stage_gh = [&]() {
+    if (wave < 2) {
+      i32x4 d = dk;
+      d[2] = n * RB;
+      i32x4 e = dv;
+      e[2] = n * RB;
+      const uint32_t base = lds_w + (uint32_t)B_GH_OFF;   // this wave's 2 KB of the K half
+      int offk[B_CH], offv[B_CH];
+#pragma unroll
+      for (int c2 = 0; c2 < B_CH; ++c2) {
+        int srow, ck16, cv16;
+        stage_chunk(wave, lane, c2, srow, ck16, cv16);
+        const bool in = srow < gmain;
+        const int rowoff = gl[in ? srow : 0] * RB;
+        offk[c2] = in ? rowoff + ck16 : OOB_OFF;
+        offv[c2] = in ? rowoff + cv16 : OOB_OFF;
+      }
+      dma16i<0>(d, offk[0], base);
+      dma16i<1024>(d, offk[1], base);
+      dma16i<0>(e, offv[0], base + B_STEP / 2);
+      dma16i<1024>(e, offv[1], base + B_STEP / 2);
+    }
   };
   // the global-position list must be in LDS before a global step is staged;
   // with fewer band steps than the prologue stages, that is before it
@@ -1793,20 +1839,33 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
     learn_globals();
     fill();
     __syncthreads();
+    if (gh) stage_gh();
   }
   auto pre = [&]() {
     if (!early_fill) {
       learn_globals();
       fill();
+      if (gh) {
+        __syncthreads();
+        stage_gh();
+      }
     }
+  };
+  auto gh_mask = [&]() {
+    FTile ti;
+    ti.act = true;
+    ti.kind = 2;
+    ti.j0 = 0;
+    ti.okb = bit_range(0, gmain);
+    return lane_mask(ti, my_i, r, jr, lane);
   };
   auto idle = [&]() { return !wave_work; };
   // plain steps of this wave: every key inside all of its rows' windows, and
   // the batch (K of u+3, V of u+2) made of band steps
   const int plain_lo = fa > 0 ? fa : 0;
   const int plain_hi = fb < nband - 4 ? fb : nband - 4;
-  half_pipe(U, plain_lo, plain_hi, idle, issue, issue_band, active, masked, mask_of, pre, qo, fl,
-            st, c, h32, smem);
+  half_pipe(U, plain_lo, plain_hi, idle, issue, issue_band, active, masked, mask_of, pre, gh, gh_mask,
+            qo, fl, st, c, h32, smem);
 
   if (g > GL_MAX && R0 < nrv) {
     // global columns past the LDS copy, 32 at a time through the first K and
@@ -1947,8 +2006,9 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   auto masked = [&](int u) { return j_start + 64 * u + 64 > j_use; };
   auto mask_of = [&](int u, int hf) { return bit_range(0, j_use - (j_start + 64 * u + 32 * hf)); };
   auto idle = [&]() { return !wave_work; };
-  half_pipe(U, 1, 0, idle, issue, issue, active, masked, mask_of, load_rows, qo, fl, st, p.c, h32,
-            smem);
+  const bool no_extra = false;
+  half_pipe(U, 1, 0, idle, issue, issue, active, masked, mask_of, load_rows, no_extra,
+            [] { return 0u; }, qo, fl, st, p.c, h32, smem);
 
   const float lt = half_sum(st.l);
   if (qok) {

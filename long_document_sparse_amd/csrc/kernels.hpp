@@ -4,10 +4,10 @@
 // One kernel, attn_kernel, runs per forward.  Its grid holds three kinds of
 // workgroups, in dispatch order:
 //   * compaction workgroups, one per batch row: padding / global flags per
-//     position, the ascending global-index list (wave ballot + prefix count;
-//     the FasterTransformer guide's global_idx / global_token_nums partition)
-//     and the length of the row's real-token prefix, published to the rest of
-//     the grid through a per-row epoch word;
+//     position and the ascending global-index list with its count (wave
+//     ballot + prefix count; the FasterTransformer guide's global_idx /
+//     global_token_nums partition), published to the rest of the grid through
+//     a per-row epoch word;
 //   * band workgroups: 128 query rows of one (batch, head, residue class of
 //     the dilation) against their window keys and the global keys under
 //     Q/K/V, one online softmax per row, the output row written directly;
@@ -68,7 +68,6 @@ struct Params {
   int32_t* gidx;           // [B][n]
   int32_t* gcnt;           // [B]
   int32_t* status;         // [B]: 1 if the row has more than max_global globals
-  int32_t* vlen;           // [B]: number of real tokens if they form a prefix, else -1
   float* part_o;           // [B][H][nqt][nsplit][32][64]
   float* part_ml;          // [B][H][nqt][nsplit][32][2]
   int32_t* tile_cnt;       // [B][H][nqt]: finished key slices of a query tile (0 between forwards)
@@ -450,17 +449,13 @@ __device__ __forceinline__ void wave_count5(int mine, int lane, int& before, int
 
 __device__ void compact_row(const Params& p, int b, uint8_t* smem) {
   int* wsum = reinterpret_cast<int*>(smem);            // [NW] globals per wave
-  int* vsum = wsum + NW;                               // [NW] real tokens per wave
-  int* first_pad = vsum + NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = p.n;
   const float* lm = p.lmask + (int64_t)b * n;
   const float* gm = p.gmask + (int64_t)b * n;
   uint8_t* fl = p.flags + (int64_t)b * n;
   int32_t* gi = p.gidx + (int64_t)b * n;
-  if (tid == 0) *first_pad = n;
-  __syncthreads();
-  int carry = 0, nvalid = 0;
+  int carry = 0;
   const bool vec = p.mask_vec != 0;   // masks 16-byte aligned and n % 4 == 0
   for (int base = 0; base < n; base += NT * C_PT) {
     const int j0 = base + tid * C_PT;
@@ -481,7 +476,7 @@ __device__ void compact_row(const Params& p, int b, uint8_t* smem) {
       }
     }
     uint32_t gbits = 0, packed[C_PT / 4];
-    int mine = 0, myvalid = 0, mypad = n;
+    int mine = 0;
 #pragma unroll
     for (int k = 0; k < C_PT / 4; ++k) packed[k] = 0;
 #pragma unroll
@@ -491,8 +486,6 @@ __device__ void compact_row(const Params& p, int b, uint8_t* smem) {
       packed[e / 4] |= (uint32_t)((v ? 1 : 0) | (g ? 2 : 0)) << (8 * (e % 4));
       gbits |= (uint32_t)(g ? 1 : 0) << e;
       mine += g ? 1 : 0;
-      myvalid += v ? 1 : 0;
-      if (!v && j0 + e < n) mypad = j0 + e;
     }
     if ((n % 4) == 0 && j0 + C_PT <= n) {
 #pragma unroll
@@ -503,22 +496,16 @@ __device__ void compact_row(const Params& p, int b, uint8_t* smem) {
       for (int e = 0; e < C_PT; ++e)
         if (j0 + e < n) fl[j0 + e] = (uint8_t)(packed[e / 4] >> (8 * (e % 4)));
     }
-    if (mypad < n) atomicMin(first_pad, mypad);
-    int before, wtot, vb, vtot;
+    int before, wtot;
     wave_count5(mine, lane, before, wtot);
-    wave_count5(myvalid, lane, vb, vtot);
-    if (lane == 0) {
-      wsum[wave] = wtot;
-      vsum[wave] = vtot;
-    }
+    if (lane == 0) wsum[wave] = wtot;
     __syncthreads();
-    int wpre = 0, tot = 0, vt = 0;
+    int wpre = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const int cw = wsum[w];
       wpre += (w < wave) ? cw : 0;
       tot += cw;
-      vt += vsum[w];
     }
     int k = carry + wpre + before;
     while (gbits) {
@@ -527,16 +514,14 @@ __device__ void compact_row(const Params& p, int b, uint8_t* smem) {
       gi[k++] = j0 + e;
     }
     carry += tot;
-    nvalid += vt;
     __syncthreads();
   }
   for (int k = carry + tid; k < n; k += NT) gi[k] = -1;
   if (tid == 0) {
     p.gcnt[b] = carry;
     p.status[b] = carry > p.max_global ? 1 : 0;
-    p.vlen[b] = (*first_pad == nvalid) ? nvalid : -1;   // real tokens form the prefix [0, nvalid)
   }
-  // the row's flags, list, count and prefix length are written back before
+  // the row's flags, list and count are written back before
   // the epoch is published (a release; no acquire, which would invalidate
   // this XCD's caches)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -933,8 +918,8 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
 // ---------------------------------------------------------------------------
 // Fast path for bf16 storage where the real tokens among the keys a workgroup
 // reads are a prefix of them (no padding, or a padded tail): the common case.
-// A band workgroup checks this over its own key range; a global-row
-// workgroup takes it when the whole batch row's real tokens are [0, nv).
+// Each workgroup checks this itself, from the mask, over the keys it reads
+// (a band workgroup over its band, a global-row workgroup over its slice).
 //
 // Keys are fetched with buffer loads whose range ends at the first padded
 // row, so the hardware returns zeros for every key before the start, past the
@@ -1136,10 +1121,11 @@ __device__ __forceinline__ i32x4 make_desc(const void* base, int bytes) {
 
 
 // ---------------------------------------------------------------------------
-// Band workgroups on the bf16 fast path (the real tokens of the batch row form
-// a prefix).  Each of the NW waves owns 32 query rows of a residue class; the
-// workgroup walks the union of their windows in steps of 64 subsequence keys
-// (two 32-key halves), then the global columns, 64 at a time.
+// Band workgroups on the bf16 fast path (the real tokens among their keys
+// form a prefix).  Each of the NW waves owns 32 query rows of a residue class;
+// the workgroup walks the union of their windows in steps of 64 subsequence
+// keys (two 32-key halves), then the global columns: up to 32 as one extra
+// half, more 64 at a time.
 //
 // Per wave, a step u runs in two phases, each pairing the softmax of one half
 // on the VALU with eight MFMAs on the matrix cores, interleaved:
@@ -1213,8 +1199,12 @@ struct BandRow {
 };
 
 // Probabilities of one 32-key half (bf16, as PV multiplies them) and this
-// lane's share of their sum.
-__device__ __forceinline__ float band_exp_half(const f32x16& s, float c, float m, bf16x8 (&pb)[2]) {
+// lane's share of their sum.  The scores arrive already scaled and offset
+// (c s - m0: Q is pre-scaled by c and the QK^T accumulator starts at -m0), so
+// p = 2^(s - x) with x the part of the row's offset beyond m0 -- zero until a
+// rebase, and then the subtraction is only paid off the fast loop.
+template <bool OFF>
+__device__ __forceinline__ float band_exp_half(const f32x16& s, float x, bf16x8 (&pb)[2]) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float acc = 0.f;
@@ -1222,12 +1212,12 @@ __device__ __forceinline__ float band_exp_half(const f32x16& s, float c, float m
   for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      bf16x2 x;
-      x[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e], c, -m));
-      x[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e + 1], c, -m));
-      pb[c2][e] = x[0];
-      pb[c2][e + 1] = x[1];
-      acc = __builtin_amdgcn_fdot2_f32_bf16(x, ones, acc, false);
+      bf16x2 q;
+      q[0] = (__bf16)__builtin_amdgcn_exp2f(OFF ? s[8 * c2 + e] - x : s[8 * c2 + e]);
+      q[1] = (__bf16)__builtin_amdgcn_exp2f(OFF ? s[8 * c2 + e + 1] - x : s[8 * c2 + e + 1]);
+      pb[c2][e] = q[0];
+      pb[c2][e + 1] = q[1];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(q, ones, acc, false);
     }
   }
   return acc;
@@ -1235,9 +1225,10 @@ __device__ __forceinline__ float band_exp_half(const f32x16& s, float c, float m
 
 // The rare half: some row's probabilities summed above SUM_HI, or a row's
 // offset is still unset.  Such rows move their offset to the half's maximum,
-// rescale what they have accumulated and recompute the half.
-__device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float c, bf16x8 (&pb)[2],
-                                            float& ts) {
+// rescale what they have accumulated and recompute the half.  s is relative
+// to the row's m0.
+__device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float m0,
+                                            bf16x8 (&pb)[2], float& ts) {
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -1245,7 +1236,7 @@ __device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float 
   const float tsrow = half_sum(ts);     // both half-lanes of the row
   float delta = 0.f;
   const bool live = mx != -INFINITY;
-  if (live && (tsrow > SUM_HI || st.first)) delta = mx * c - st.m;
+  if (live && (tsrow > SUM_HI || st.first)) delta = (m0 + mx) - st.m;
   // nothing has been accumulated while the offset is unset
   const float alpha = st.first ? 1.0f : __builtin_amdgcn_exp2f(-delta);
   st.first = st.first && !live;
@@ -1253,7 +1244,17 @@ __device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float 
 #pragma unroll
   for (int r = 0; r < 16; ++r) { st.o[0][r] *= alpha; st.o[1][r] *= alpha; }
   st.m += delta;
-  ts = band_exp_half(s, c, st.m, pb);
+  ts = band_exp_half<true>(s, st.m - m0, pb);
+}
+
+// Q scaled by c = scale log2(e) once, so that QK^T yields the exponent's
+// argument directly (the scaled value is rounded to bf16, a relative change of
+// at most 2^-9 per element).
+__device__ __forceinline__ void scale_q(QOp<true>& qo, float c) {
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qo.q[cc][e] = (__bf16)((float)qo.q[cc][e] * c);
 }
 
 __device__ __forceinline__ bf16x8 vfrag(const uint8_t* vt, int off) {
@@ -1325,7 +1326,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
                                           const MaskOf& mask_of, const Pre& pre,
                                           const bool& extra_half, const ExtraMask& extra_mask,
                                           const QOp<true>& qo, const FLane& fl, BandRow& st,
-                                          float c, int h32, uint8_t* smem) {
+                                          int h32, uint8_t* smem) {
   // the batch of step t: K of step t+3 and V of step t+2 (those that exist);
   // two loads per thread for each
   auto batch = [&](int t) {
@@ -1335,8 +1336,15 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
   auto kslot = [&](int t) { return smem + (t % B_NSLOT) * B_STEP; };
   auto vslot = [&](int t) { return smem + B_V_OFF + (t % B_NSLOT) * B_STEP; };
   // QK^T of one half of a step; PV of one half of a step
+  // the row's fixed exponent offset, folded into every QK^T accumulator (so
+  // that the scores come out as c s - m0); set again after the first-half
+  // maximum of rows without an anchor
+  float m0 = st.m;
+  f32x16 mvec;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mvec[i] = -m0;
   auto qk_half = [&](f32x16& sx, const uint8_t* ks) {
-    f32x16 a = {};
+    f32x16 a = mvec;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
       a = mfma_bf16(*reinterpret_cast<const bf16x8*>(ks + fl.k[cc]), qo.q[cc], a);
@@ -1358,26 +1366,14 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
       for (int db = 0; db < 2; ++db) ops.vf[c2][db] = vfrag(vs, fl.v[db] + c2 * 2048);
   };
   // the MFMAs of a phase: QK^T of one half into sq and PV of one half, the
-  // two chains alternating so that no MFMA waits on the one just before it
-  auto phase_mfma = [&](f32x16& sq, const PhaseOps& ops, const bf16x8 (&pp)[2]) {
-    f32x16 a = {};
-    st.o[0] = mfma_bf16(ops.vf[0][0], pp[0], st.o[0]);
-    a = mfma_bf16(ops.kf[0], qo.q[0], a);
-    st.o[1] = mfma_bf16(ops.vf[0][1], pp[0], st.o[1]);
-    a = mfma_bf16(ops.kf[1], qo.q[1], a);
-    st.o[0] = mfma_bf16(ops.vf[1][0], pp[1], st.o[0]);
-    a = mfma_bf16(ops.kf[2], qo.q[2], a);
-    st.o[1] = mfma_bf16(ops.vf[1][1], pp[1], st.o[1]);
-    a = mfma_bf16(ops.kf[3], qo.q[3], a);
-    sq = a;
-  };
-  // the same MFMAs, each followed by the LDS read of the operand that
-  // replaces its own in the next phase (K rows at ks, V^T at vs): the reads
+  // two chains alternating so that no MFMA waits on the one just before it,
+  // each followed by the LDS read of the operand that replaces its own in the
+  // next phase (K rows at ks, V^T at vs): the reads
   // leave in a stream across the phase instead of in one burst, and the
   // registers of an operand are reused as soon as its MFMA has taken it
   auto phase_mfma_next = [&](f32x16& sq, PhaseOps& ops, const bf16x8 (&pp)[2], const uint8_t* ks,
                              const uint8_t* vs) {
-    f32x16 a = {};
+    f32x16 a = mvec;
     st.o[0] = mfma_bf16(ops.vf[0][0], pp[0], st.o[0]);
     ops.vf[0][0] = vfrag(vs, fl.v[0]);
     a = mfma_bf16(ops.kf[0], qo.q[0], a);
@@ -1397,8 +1393,8 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     sq = a;
   };
   auto soft_half = [&](f32x16& sx, bf16x8 (&pb)[2]) {
-    float ts = band_exp_half(sx, c, st.m, pb);
-    if (__builtin_expect(__any(ts > SUM_HI || st.first), 0)) band_rebase(st, sx, c, pb, ts);
+    float ts = band_exp_half<true>(sx, st.m - m0, pb);
+    if (__builtin_expect(__any(ts > SUM_HI || st.first), 0)) band_rebase(st, sx, m0, pb, ts);
     st.l += ts;
   };
 
@@ -1442,9 +1438,15 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sx[r]);
     mx = half_max(mx);
     if (mx != -INFINITY) {
-      st.m = mx * c;
+      st.m = m0 + mx;
       st.first = false;
     }
+    // from here on the offset in the accumulator is the row's offset
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sx[r] -= st.m - m0;
+    m0 = st.m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mvec[i] = -m0;
   }
 
   auto head_of_step = [&](int u) {
@@ -1515,7 +1517,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     if (msk) mask_half(sx, mask_of(u, 0), h32);
     // phase A
     phase_mfma_next(sy, ops, pb, kslot(u + 1), vslot(u));
-    float ts = band_exp_half(sx, c, st.m, pa);
+    float ts = band_exp_half<false>(sx, 0.f, pa);   // st.m == m0 in this loop
     interleave_hint();
     if (__builtin_expect(__any(ts > SUM_HI), 0)) {
       rare_at = 1;
@@ -1527,7 +1529,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     // phase B (the operands read for step u+1 = U are never used; the reads
     // stay inside the ring)
     phase_mfma_next(sx, ops, pa, kslot(u + 1) + 4096, vslot(u) + 4096);
-    ts = band_exp_half(sy, c, st.m, pb);
+    ts = band_exp_half<false>(sy, 0.f, pb);
     interleave_hint();
     if (__builtin_expect(__any(ts > SUM_HI), 0)) {
       rare_at = 2;
@@ -1538,7 +1540,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
   }
   if (rare_at == 1) {
     // half 0 of step u overflowed: rescale, then phase B of step u
-    band_rebase(st, sx, c, pa, ts_rare);
+    band_rebase(st, sx, m0, pa, ts_rare);
     st.l += ts_rare;
     if (masked(u)) mask_half(sy, mask_of(u, 1), h32);
     if (u + 1 < U) qk_half(sx, kslot(u + 1));
@@ -1547,7 +1549,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     ++u;
   } else if (rare_at == 2) {
     // half 1 of step u overflowed
-    band_rebase(st, sy, c, pb, ts_rare);
+    band_rebase(st, sy, m0, pb, ts_rare);
     st.l += ts_rare;
     ++u;
   }
@@ -1563,6 +1565,50 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     bf16x8 pg[2];
     soft_half(sg, pg);
     pv_half(pg, gk + B_STEP / 2);
+  }
+}
+
+// Padding of the positions rho + i s, i in [lo, hi), read from the local
+// attention mask by the whole workgroup: the first padded index (none_val if
+// there is none) and the number of padded ones.  Ends with a barrier.
+__device__ __forceinline__ void pad_scan(const float* lmb, int rho, int s, int lo, int hi,
+                                         int none_val, int& first, int& ninv) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  first = none_val;
+  ninv = 0;
+  for (int i0 = lo + tid; i0 < hi; i0 += 4 * NT) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e * NT;
+      v[e] = i < hi ? lmb[rho + i * s] : 1.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool pad = v[e] == 0.0f;
+      const int i = i0 + e * NT;
+      first = pad && i < first ? i : first;
+      ninv += pad ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const int f2 = __shfl_xor(first, o);
+    first = f2 < first ? f2 : first;
+    ninv += __shfl_xor(ninv, o);
+  }
+  __shared__ int s_pad[2 * NW];
+  if (lane == 0) {
+    s_pad[2 * wave] = first;
+    s_pad[2 * wave + 1] = ninv;
+  }
+  __syncthreads();
+  first = none_val;
+  ninv = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    first = s_pad[2 * w] < first ? s_pad[2 * w] : first;
+    ninv += s_pad[2 * w + 1];
   }
 }
 
@@ -1623,41 +1669,8 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   asm volatile("" : "+v"(orow_bits));
   const int sc_lo = kb0 > 0 ? kb0 : 0;
   const int sc_hi = kb + 64 * T < nr ? kb + 64 * T : nr;
-  int first = nr, ninv = 0;
-  for (int i0 = sc_lo + tid; i0 < sc_hi; i0 += 4 * NT) {
-    float v[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = i0 + e * NT;
-      v[e] = i < sc_hi ? lmb[rho + i * s] : 1.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool pad = v[e] == 0.0f;
-      const int i = i0 + e * NT;
-      first = pad && i < first ? i : first;
-      ninv += pad ? 1 : 0;
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const int f2 = __shfl_xor(first, o);
-    first = f2 < first ? f2 : first;
-    ninv += __shfl_xor(ninv, o);
-  }
-  __shared__ int s_pad[2 * NW];
-  if (lane == 0) {
-    s_pad[2 * wave] = first;
-    s_pad[2 * wave + 1] = ninv;
-  }
-  __syncthreads();
-  first = nr;
-  ninv = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    first = s_pad[2 * w] < first ? s_pad[2 * w] : first;
-    ninv += s_pad[2 * w + 1];
-  }
+  int first, ninv;
+  pad_scan(lmb, rho, s, sc_lo, sc_hi, nr, first, ninv);
   // real tokens among the readable keys must be exactly [.., first)
   if (ninv != 0 && ninv != sc_hi - first) return false;
   const int nrv = first;                                 // subsequence keys below are real
@@ -1691,6 +1704,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   // compiler's view of outstanding loads, since the loop below issues
   // buffer-to-LDS loads the compiler does not count, and a wait it placed for
   // Q inside the loop would also wait for those.
+  scale_q(qo, p.c);
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
   BandRow st;
@@ -1709,7 +1723,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
         sd = __builtin_amdgcn_fdot2_f32_bf16(a, bb, sd, false);
       }
     }
-    st.m = half_sum(sd) * p.c;
+    st.m = half_sum(sd);   // Q carries the factor c
     asm volatile("" : "+v"(st.m));
   }
   st.l = 0.f;
@@ -1718,7 +1732,6 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   for (int i = 0; i < 16; ++i) { st.o[0][i] = 0.f; st.o[1][i] = 0.f; }
   FLane fl;
   fl.init(lane);
-  const float c = p.c;
 
   int32_t* gl = reinterpret_cast<int32_t*>(smem + B_GL_OFF);
   int32_t* jr = reinterpret_cast<int32_t*>(smem + B_JR_OFF);
@@ -1865,7 +1878,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   const int plain_lo = fa > 0 ? fa : 0;
   const int plain_hi = fb < nband - 4 ? fb : nband - 4;
   half_pipe(U, plain_lo, plain_hi, idle, issue, issue_band, active, masked, mask_of, pre, gh, gh_mask,
-            qo, fl, st, c, h32, smem);
+            qo, fl, st, h32, smem);
 
   if (g > GL_MAX && R0 < nrv) {
     // global columns past the LDS copy, 32 at a time through the first K and
@@ -1904,10 +1917,10 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
         ti.kind = 2;
         ti.okb = bit_range(0, g - jb);
         ti.j0 = 0;
-        f32x16 sc = fqk(qo, smem, fl);
+        f32x16 sc = fqk(qo, smem, fl);   // Q carries the factor c
         apply_mask(sc, lane_mask(ti, my_i, r, jr, lane), lane);
         bf16x8 pq[2];
-        softmax_bf16(sm, sc, c, pq);
+        softmax_bf16(sm, sc, 1.0f, pq);
         fpv(sm.o, pq, smem + B_V_OFF, fl);
       }
     }
@@ -1943,29 +1956,49 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
 // the same pipeline; each wave leaves an unnormalised partial result (offset,
 // sum, O) that the merge of the tile's key slices combines.  The rows' offsets
 // are set from the maximum of their first half (there is no own key in a
-// slice to anchor them).
-__device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, int nv,
-                               uint8_t* smem) {
+// slice to anchor them).  Like the band path, the workgroup reads the padding
+// of its slice from the mask and issues its first key batches before it waits
+// for the row's compaction (which names its query rows).  Returns false,
+// having written nothing, when the slice's real tokens are not a prefix of it.
+__device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, uint8_t* smem) {
   constexpr int RB = 128;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  int g = coherent_load(p.gcnt + b);
-  if (g > p.max_global) g = p.max_global;
-  const int nqt_b = (g + 31) / 32;
-  if (qg * NW >= nqt_b) return;                     // uniform over the workgroup
-  const int qt = qg * NW + wave;
-  const bool wave_work = qt < nqt_b;
   const int n = p.n;
   const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
-  const int qidx = qt * 32 + qi;
-  const bool qok = wave_work && qidx < g;
+  const int j_start = sp * p.ksplit;
+  int j_end = j_start + p.ksplit;
+  if (j_end > n) j_end = n;
+  int first, ninv;
+  pad_scan(p.lmask + (int64_t)b * n, 0, 1, j_start, j_end, j_end, first, ninv);
+  if (ninv != 0 && ninv != j_end - first) return false;
+  const int j_use = first;                          // keys of the slice that are real tokens
+  int U = j_use > j_start ? (j_use - j_start + 63) / 64 : 0;
+
+  // the query tiles, known once the row's compaction is visible
+  int g = 0, qt = 0;
+  bool wave_work = false, qok = false;
   QOp<true> qo;
   auto load_rows = [&]() {   // while the first keys are in flight
-    const int qpos = coherent_load(gidx_b + (qok ? qidx : 0));
-    qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
+    if (wait_ready(p, b, false)) {
+      g = coherent_load(p.gcnt + b);
+      if (g > p.max_global) g = p.max_global;
+    }
+    const int nqt_b = (g + 31) / 32;
+    if (qg * NW >= nqt_b) {                         // no query tile here: drain and leave
+      U = 0;
+      return;
+    }
+    qt = qg * NW + wave;
+    wave_work = qt < nqt_b;
+    const int qidx = qt * 32 + qi;
+    qok = wave_work && qidx < g;
+    const int qpos = qok ? coherent_load(gidx_b + qidx) : 0;
+    qo.load(p.Qg + (head + qpos) * RB, qok, h32);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
+    scale_q(qo, p.c);
   };
   BandRow st;
   st.m = 0.f;
@@ -1976,13 +2009,8 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   FLane fl;
   fl.init(lane);
 
-  const int j_start = sp * p.ksplit;
-  int j_end = j_start + p.ksplit;
-  if (j_end > n) j_end = n;
-  const int j_use = j_end < nv ? j_end : nv;        // keys of the slice that are real tokens
-  const int U = j_use > j_start ? (j_use - j_start + 63) / 64 : 0;
-  const i32x4 dk = make_desc(p.Kg + head * RB, nv * RB);
-  const i32x4 dv = make_desc(p.Vg + head * RB, nv * RB);
+  const i32x4 dk = make_desc(p.Kg + head * RB, j_use * RB);
+  const i32x4 dv = make_desc(p.Vg + head * RB, j_use * RB);
   int kbase[B_CH], vbase[B_CH];
 #pragma unroll
   for (int e = 0; e < B_CH; ++e) {
@@ -2008,7 +2036,7 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
   auto idle = [&]() { return !wave_work; };
   const bool no_extra = false;
   half_pipe(U, 1, 0, idle, issue, issue, active, masked, mask_of, load_rows, no_extra,
-            [] { return 0u; }, qo, fl, st, p.c, h32, smem);
+            [] { return 0u; }, qo, fl, st, h32, smem);
 
   const float lt = half_sum(st.l);
   if (qok) {
@@ -2027,6 +2055,7 @@ __device__ void global_wg_fast(const Params& p, int b, int h, int qg, int sp, in
     }
   }
   if (wave_work) finish_global_tile<true>(p, b, h, qt, g, lane);
+  return true;
 }
 
 template <bool BF>
@@ -2065,15 +2094,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     t /= p.nqg;
     const int h = t % p.H;
     const int b = t / p.H;
-    if (!wait_ready(p, b, false)) return;
     if constexpr (BF) {
-      const int nv = coherent_load(p.vlen + b);
-      if (nv >= 0) {
-        global_wg_fast(p, b, h, qg, sp, nv, smem);
-        return;
-      }
+      if (global_wg_fast(p, b, h, qg, sp, smem)) return;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the general path reads with plain loads
+    if (!wait_ready(p, b, true)) return;
     global_wg<BF>(p, b, h, qg, sp, smem);
   } else {
     const int lb = xcd_remap(bid, p.n_band_wg);

@@ -51,7 +51,6 @@ struct lwattn_plan_s {
   int32_t* gidx = nullptr;
   int32_t* gcnt = nullptr;
   int32_t* status = nullptr;
-  int32_t* vlen = nullptr;
   float* part_o = nullptr;
   float* part_ml = nullptr;
   int32_t* tile_cnt = nullptr;
@@ -74,7 +73,6 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->gidx);
   (void)hipFree(p->gcnt);
   (void)hipFree(p->status);
-  (void)hipFree(p->vlen);
   (void)hipFree(p->part_o);
   (void)hipFree(p->part_ml);
   (void)hipFree(p->tile_cnt);
@@ -218,7 +216,6 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->gidx, bn * 4);
   alloc((void**)&p->gcnt, (size_t)B * 4);
   alloc((void**)&p->status, (size_t)B * 4);
-  alloc((void**)&p->vlen, (size_t)B * 4);
   const size_t nparts = (size_t)B * H * p->nqt * (p->nsplit > 0 ? p->nsplit : 0) * 32;
   alloc((void**)&p->part_o, nparts * lwk::D * 4);
   alloc((void**)&p->part_ml, nparts * 2 * 4);
@@ -281,7 +278,6 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   prm.gidx = p->gidx;
   prm.gcnt = p->gcnt;
   prm.status = p->status;
-  prm.vlen = p->vlen;
   prm.part_o = p->part_o;
   prm.part_ml = p->part_ml;
   prm.tile_cnt = p->tile_cnt;

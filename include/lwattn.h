@@ -152,6 +152,14 @@ lwattn_status lwattn_timing_read(lwattn_plan_t plan, float* ms, int32_t cap,
                                  int32_t* nkernels, int32_t* ncalls);
 lwattn_status lwattn_timing_disable(lwattn_plan_t plan);
 
+/* Testing aid for the failure path of the in-kernel wait (for test code only).
+ * In the next forward of `plan`, the row compactions publish a number the
+ * other workgroups do not wait for, and their waits give up after 64 polls:
+ * every workgroup still exits normally, O is undefined, and
+ * lwattn_sync_status reports LWATTN_E_DEVICE from then on (the plan is then
+ * to be destroyed).  LWATTN_E_INVALID for a null plan. */
+lwattn_status lwattn_test_inject_wait_timeout(lwattn_plan_t plan);
+
 /* Static description of a status code. */
 const char* lwattn_strerror(lwattn_status s);
 

@@ -73,7 +73,9 @@ struct Params {
   int32_t* tile_cnt;       // [B][H][nqt]: finished key slices of a query tile (0 between forwards)
   int32_t* ready;          // [B]: epoch of the last forward whose compaction of the row is done
   int32_t* fault;          // sticky: set when a workgroup gave up waiting for its row
-  int32_t epoch;           // this forward's number (> 0)
+  int32_t epoch;           // this forward's number (> 0): what every workgroup waits for
+  int32_t publish;         // what the compaction publishes (= epoch, except in a fault test)
+  int32_t spin_limit;      // polls before a wait for a row gives up
   int32_t n_comp_wg;       // compaction workgroups at the head of the attention launch (= B)
   const int32_t* head_stride;  // [H]: dilation gap + 1 (device copy, any H)
   const int32_t* head_blk;     // [H+1]: prefix of band workgroups per batch row
@@ -526,7 +528,7 @@ __device__ void compact_row(const Params& p, int b, uint8_t* smem) {
   // this XCD's caches)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(p.ready + b, p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(p.ready + b, p.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Reads of what other workgroups of the launch wrote (the compaction's
@@ -551,16 +553,15 @@ __device__ __forceinline__ float coherent_loadf(const float* ptr) {
 // barrier passes what it saw on to the rest of the workgroup.  Callers that
 // read the compaction's outputs with plain loads (the general paths) ask for
 // an agent-scope acquire fence in every wave as well.
-// The limit allows at least ~2^18 polls (each sleeps >= 128 clocks) plus
-// n / 4 for the compaction of long rows, far beyond the time it takes.
-constexpr int READY_SPIN_BASE = 1 << 18;
+// The limit (p.spin_limit, set by the host) allows at least ~2^18 polls (each
+// sleeps >= 128 clocks) plus n / 4 for the compaction of long rows, far beyond
+// the time it takes.
 __device__ __forceinline__ bool wait_ready(const Params& p, int b, bool acquire) {
   __shared__ int s_ok;
   if (threadIdx.x == 0) {
-    const int limit = READY_SPIN_BASE + (p.n >> 2);
     int spins = 0, good = 1;
     while (coherent_load(p.ready + b) != p.epoch) {
-      if (++spins > limit) {
+      if (++spins > p.spin_limit) {
         good = 0;
         break;
       }

@@ -57,6 +57,7 @@ struct lwattn_plan_s {
   int32_t* ready = nullptr;   // [B] epoch of the last compaction of each batch row
   int32_t* fault = nullptr;   // sticky: a workgroup gave up waiting for its row
   int32_t epoch = 0;          // forwards launched (kept in 1 .. INT32_MAX - 1)
+  bool inject_timeout = false; // fault test: the next forward's waits give up
   int32_t* head_stride = nullptr;
   int32_t* head_blk = nullptr;
   // timing
@@ -285,6 +286,15 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   prm.fault = p->fault;
   p->epoch = p->epoch >= INT32_MAX - 1 ? 1 : p->epoch + 1;
   prm.epoch = p->epoch;
+  prm.publish = p->epoch;
+  prm.spin_limit = (1 << 18) + (int32_t)(c.n >> 2);
+  if (p->inject_timeout) {
+    // the rows are published under another number and nobody waits long:
+    // every waiting workgroup gives up, sets the fault word and skips its work
+    p->inject_timeout = false;
+    prm.publish = -1;
+    prm.spin_limit = 64;
+  }
   prm.n_comp_wg = p->n_comp_wg;
   prm.head_stride = p->head_stride;
   prm.head_blk = p->head_blk;
@@ -405,6 +415,12 @@ lwattn_status lwattn_timing_read(lwattn_plan_t p, float* ms, int32_t cap, int32_
   for (int k = 0; k < kNumKernels && k < cap; ++k) ms[k] = tot[k];
   *nkernels = kNumKernels;
   *ncalls = p->timing_calls;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_test_inject_wait_timeout(lwattn_plan_t p) {
+  if (!p) return LWATTN_E_INVALID;
+  p->inject_timeout = true;
   return LWATTN_OK;
 }
 

@@ -46,6 +46,7 @@ SIGNATURES = [
     ("lwattn_timing_read", ctypes.c_int, [_c_p, ctypes.POINTER(ctypes.c_float), _i32,
                                           ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     ("lwattn_timing_disable", ctypes.c_int, [_c_p]),
+    ("lwattn_test_inject_wait_timeout", ctypes.c_int, [_c_p]),
     ("lwattn_strerror", ctypes.c_char_p, [ctypes.c_int]),
 ]
 

@@ -78,6 +78,7 @@ def test_null_config_and_plan_arguments_are_rejected():
     assert lib.lwattn_sync_status(None, None) == lw.E_INVALID
     assert lib.lwattn_timing_enable(None, 4) == lw.E_INVALID
     assert lib.lwattn_timing_every(None, 2) == lw.E_INVALID
+    assert lib.lwattn_test_inject_wait_timeout(None) == lw.E_INVALID
     assert lib.lwattn_timing_disable(None) == lw.E_INVALID
     nk, nc = ctypes.c_int32(), ctypes.c_int32()
     assert lib.lwattn_timing_read(None, None, 0, ctypes.byref(nk), ctypes.byref(nc)) == lw.E_INVALID

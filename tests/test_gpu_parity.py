@@ -158,6 +158,33 @@ def test_too_many_globals_is_reported():
     assert st == lw.OK
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_wait_timeout_is_reported_not_hung(dtype):
+    """The in-kernel wait for a row's compaction is bounded: when the rows are
+    published under a number nobody waits for and the poll limit is tiny (the
+    library's fault-test hook), every workgroup still exits and the fault is
+    reported, stickily; the same inputs on a fresh plan are correct."""
+    spec = workloads.custom(2, 3, 700, 64, 128, dtype, [0, 1, 0], seed=9, n_global=5,
+                            pad_mode="per_batch", pad_lo=0, pad_hi=100)
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec)
+    lib = lw.load_library()
+    assert lib.lwattn_test_inject_wait_timeout(plan.handle) == lw.OK
+    out, st = run(plan, ts, lm, gm)
+    assert st == lw.E_DEVICE
+    out, st = run(plan, ts, lm, gm)          # the fault word is sticky
+    assert st == lw.E_DEVICE
+    plan.close()
+    fresh = make_plan(spec)
+    out, st = run(fresh, ts, lm, gm)
+    assert st == lw.OK
+    want = oracle.forward(*x.tensors(), x.lmask, x.gmask, spec.window, spec.dilation, spec.scale)
+    got = out.float().cpu().numpy().astype(np.float64)
+    tol = 2e-2 if dtype == "bf16" else 1e-4
+    assert float(np.max(np.abs(got - want))) <= tol
+
+
 def test_empty_problem_and_bad_pointers():
     plan = lw.Plan(0, 2, 128, 64, 16, [0, 0], 4, 0.125, "bf16")
     e = torch.empty((0, 2, 128, 64), dtype=torch.bfloat16, device="cuda:0")

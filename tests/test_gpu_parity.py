@@ -222,6 +222,30 @@ def test_mixed_prefix_and_scattered_padding_in_one_call():
     assert np.max(np.abs(got - want)) <= TOL_ABS["bf16"]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_more_global_columns_than_the_lds_list(dtype):
+    """600 global tokens in a row that also has local rows: local rows take the
+    first 512 global columns from the LDS list and the rest 32 at a time; 19
+    global query tiles need several global-row workgroups per slice."""
+    spec = workloads.custom(1, 2, 2048, 64, 128, dtype, [0, 1], seed=12, n_global=600,
+                            global_mode="random", pad_mode="per_batch", pad_lo=0, pad_hi=200,
+                            max_global=600)
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec)
+    out, st = run(plan, ts, lm, gm)
+    assert st == lw.OK
+    gidx, gcnt = plan.global_index()
+    og, oc = oracle.compact(x.lmask, x.gmask)
+    assert np.array_equal(gcnt.cpu().numpy(), oc) and int(oc[0]) > 512
+    assert np.array_equal(gidx.cpu().numpy(), og)
+    want = oracle.forward(*x.tensors(), x.lmask, x.gmask, spec.window, spec.dilation, spec.scale)
+    got = to_np64(out)
+    err = float(np.max(np.abs(got - want)))
+    say(f"600 globals {dtype}: max abs err {err:.3e}")
+    assert err <= TOL_ABS[dtype]
+
+
 def test_all_padded_and_all_global_rows():
     B, H, n = 2, 2, 200
     spec = workloads.custom(B, H, n, 64, 16, "bf16", [0, 1], seed=7, n_global=0)

@@ -246,6 +246,25 @@ def test_more_global_columns_than_the_lds_list(dtype):
     assert err <= TOL_ABS[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_more_heads_than_the_kernel_argument_tables(dtype):
+    """40 heads with mixed dilation: band workgroups find their head through the
+    device-side per-head tables instead of the kernel-argument copy."""
+    H = 40
+    spec = workloads.custom(1, H, 256, 64, 32, dtype, [h % 3 for h in range(H)], seed=13,
+                            n_global=3, pad_mode="per_batch", pad_lo=0, pad_hi=40)
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec)
+    out, st = run(plan, ts, lm, gm)
+    assert st == lw.OK
+    want = oracle.forward(*x.tensors(), x.lmask, x.gmask, spec.window, spec.dilation, spec.scale)
+    got = to_np64(out)
+    err = float(np.max(np.abs(got - want)))
+    say(f"40 heads {dtype}: max abs err {err:.3e}")
+    assert err <= TOL_ABS[dtype]
+
+
 def test_all_padded_and_all_global_rows():
     B, H, n = 2, 2, 200
     spec = workloads.custom(B, H, n, 64, 16, "bf16", [0, 1], seed=7, n_global=0)

@@ -98,8 +98,8 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
  *                         positions are read.
  *   local_attn_mask     : device float32 [B,n]; != 0 marks a real token.
  *   global_attn_mask    : device float32 [B,n]; != 0 marks a global token.
- *   O                   : device, [B,H,n,d], dtype; every row is written.  Must
- *                         not overlap any input.
+ *   O                   : device, [B,H,n,d], dtype, 16-byte aligned; every row
+ *                         is written.  Must not overlap any input.
  * Returns LWATTN_E_INVALID before launching anything if the plan or a pointer
  * is null or misaligned, LWATTN_E_DEVICE if a launch fails.  Data-dependent
  * errors (too many global tokens) are reported by lwattn_sync_status; O is

@@ -774,11 +774,14 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
 // Global-row merge, fused into the attention kernel.  Every (b, h, query
 // tile) has a counter of finished key slices; the wave that finishes the last
 // slice of a tile combines the nsplit partial results of its 32 rows (the
-// log-sum-exp merge of split softmax) and writes them, then re-arms the
-// counter for the next forward.  Lane l merges row l % 32, channels
-// 32 (l / 32) .. +31.
+// log-sum-exp merge of split softmax, taken online: a running maximum, the
+// running sum and output rescaled as each partial arrives) and writes them,
+// then re-arms the counter for the next forward.  Lane l merges row l % 32,
+// channels 32 (l / 32) .. +31; pos is that row's sequence position.  The
+// partials are streamed two chunks deep, so the merge waits for about one
+// memory round trip instead of one per chunk.
 template <bool BF>
-__device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g, int lane) {
+__device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g, int lane, int pos) {
   // this slice's partial rows are written back before it is counted; the
   // wave that counts the last slice reads all of them with coherent loads
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -792,56 +795,64 @@ __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g,
   if (idx < g) {
     const int64_t base = (((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit;
     const int ns = p.nsplit;
-    // this tile's partial O rows, read through a buffer range with the sc1
+    // this tile's partials, read through buffer ranges with the sc1
     // (agent-coherent) cache policy
     const __amdgpu_buffer_rsrc_t ro =
         __builtin_amdgcn_make_buffer_rsrc(p.part_o + base * 32 * D, (short)0, ns * 32 * D * 4, 0x00020000);
-    constexpr int U1 = 16, U2 = 4;
-    float mstar = -INFINITY;
-    for (int s0 = 0; s0 < ns; s0 += U1) {
-      float mv[U1];
+    const __amdgpu_buffer_rsrc_t rml =
+        __builtin_amdgcn_make_buffer_rsrc(p.part_ml + base * 32 * 2, (short)0, ns * 32 * 2 * 4, 0x00020000);
+    constexpr int U = 2;   // partials per chunk
+    struct Chunk {
+      float2 ml[U];
+      float4 o[U][8];
+    };
+    // partials past ns read as zeros through the ranges and are skipped
+    auto load = [&](int s0, Chunk& c) {
 #pragma unroll
-      for (int e = 0; e < U1; ++e)
-        mv[e] = (s0 + e < ns) ? coherent_loadf(p.part_ml + ((base + s0 + e) * 32 + q) * 2) : -INFINITY;
-#pragma unroll
-      for (int e = 0; e < U1; ++e) mstar = fmaxf(mstar, mv[e]);
-    }
-    float L = 0.f, acc[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += U2) {
-      float2 ml[U2];
-      float4 o[U2][8];
-#pragma unroll
-      for (int e = 0; e < U2; ++e) {
-        const bool in = s0 + e < ns;
-        const int sl = in ? s0 + e : s0;
-        const int64_t pi = (base + sl) * 32 + q;
-        ml[e] = make_float2(coherent_loadf(p.part_ml + pi * 2), coherent_loadf(p.part_ml + pi * 2 + 1));
-        if (!in) ml[e] = make_float2(-INFINITY, 0.f);
+      for (int e = 0; e < U; ++e) {
+        const int sl = s0 + e;
+        c.ml[e] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rml, (sl * 32 + q) * 8, 0, 16));
         const int ob = ((sl * 32 + q) * D + 32 * ch) * 4;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          o[e][k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, ob + 16 * k, 0, 16));
+          c.o[e][k] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, ob + 16 * k, 0, 16));
       }
+    };
+    float mrun = -INFINITY, L = 0.f, acc[32];
 #pragma unroll
-      for (int e = 0; e < U2; ++e) {
-        const float w = __builtin_amdgcn_exp2f(ml[e].x - mstar);
-        L += w * ml[e].y;
+    for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+    auto merge = [&](int s0, const Chunk& c) {
+#pragma unroll
+      for (int e = 0; e < U; ++e) {
+        // an empty slice (no real key) carries offset -inf
+        const bool live = s0 + e < ns && c.ml[e].x != -INFINITY;
+        const float mn = live ? fmaxf(mrun, c.ml[e].x) : mrun;
+        const float wa = live ? __builtin_amdgcn_exp2f(mrun - mn) : 1.0f;
+        const float wb = live ? __builtin_amdgcn_exp2f(c.ml[e].x - mn) : 0.0f;
+        L = wa * L + wb * c.ml[e].y;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          acc[4 * k + 0] += w * o[e][k].x;
-          acc[4 * k + 1] += w * o[e][k].y;
-          acc[4 * k + 2] += w * o[e][k].z;
-          acc[4 * k + 3] += w * o[e][k].w;
+          acc[4 * k + 0] = wa * acc[4 * k + 0] + wb * c.o[e][k].x;
+          acc[4 * k + 1] = wa * acc[4 * k + 1] + wb * c.o[e][k].y;
+          acc[4 * k + 2] = wa * acc[4 * k + 2] + wb * c.o[e][k].z;
+          acc[4 * k + 3] = wa * acc[4 * k + 3] + wb * c.o[e][k].w;
         }
+        mrun = mn;
       }
+    };
+    Chunk ca, cb;
+    load(0, ca);
+    for (int s0 = 0; s0 < ns; s0 += 2 * U) {
+      if (s0 + U < ns) load(s0 + U, cb);
+      merge(s0, ca);
+      if (s0 + U >= ns) break;
+      if (s0 + 2 * U < ns) load(s0 + 2 * U, ca);
+      merge(s0 + U, cb);
     }
     const float inv = 1.0f / L;
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] *= inv;
     constexpr int RB = D * Lay<BF>::ELT;
-    const int pos = coherent_load(p.gidx + (int64_t)b * p.n + idx);
     uint8_t* orow = p.O + (((int64_t)b * p.H + h) * p.n + pos) * RB + 32 * ch * Lay<BF>::ELT;
 #pragma unroll
     for (int k = 0; k < 8; ++k) store_row4<BF>(orow + 4 * k * Lay<BF>::ELT, acc + 4 * k);
@@ -913,7 +924,7 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
       p.part_ml[pidx * 2 + 1] = lt;
     }
   }
-  if (wave_work) finish_global_tile<BF>(p, b, h, qt, g, lane);
+  if (wave_work) finish_global_tile<BF>(p, b, h, qt, g, lane, qpos);
 }
 
 // ---------------------------------------------------------------------------
@@ -1932,21 +1943,37 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   }
 
   // normalise and store (global rows are written by the merge of their key
-  // slices, padded rows get exact zeros)
+  // slices, padded rows get exact zeros).  The wave's 32 rows are staged in
+  // LDS (free once every wave is past the ring) and leave as whole 128-byte
+  // rows, eight lanes per row, with the agent-scope write-through policy: the
+  // lines are not left dirty in L2 for the end of the kernel (or a global
+  // merge's release) to write back, and no line is written in pieces.
   const float lt = half_sum(st.l);
-  if (row_in && (my_fl & 2) == 0) {
-    const bool valid = (my_fl & 1) != 0;
-    const float inv = valid ? 1.0f / lt : 0.0f;
-    uint8_t* orow = reinterpret_cast<uint8_t*>((uintptr_t)orow_bits);
+  const bool keep = row_in && (my_fl & 2) == 0;
+  const bool valid = (my_fl & 1) != 0;
+  const float inv = valid ? 1.0f / lt : 0.0f;
+  __syncthreads();
+  uint8_t* stg = smem + wave * 4096;   // 32 rows x 128 bytes, 16-byte chunks swizzled by row
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+  for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        float v[4];
+    for (int a = 0; a < 4; ++a) {
+      bf16x4 t;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = valid ? st.o[db][4 * a + e] * inv : 0.0f;
-        store_row4<true>(orow + (32 * db + 8 * a + 4 * h32) * 2, v);
-      }
+      for (int e = 0; e < 4; ++e) t[e] = (__bf16)(valid ? st.o[db][4 * a + e] * inv : 0.0f);
+      const int chunk = (4 * db + a) ^ (qi & 7);
+      *reinterpret_cast<bf16x4*>(stg + qi * 128 + chunk * 16 + h32 * 8) = t;
+    }
+  }
+  const uint32_t or_lo = (uint32_t)orow_bits, or_hi = (uint32_t)(orow_bits >> 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * i + (lane >> 3), c = lane & 7;
+    const i32x4 v = *reinterpret_cast<const i32x4*>(stg + row * 128 + ((c ^ (row & 7)) * 16));
+    const uint64_t rt = ((uint64_t)(uint32_t)__shfl((int)or_hi, row) << 32) | (uint32_t)__shfl((int)or_lo, row);
+    if (__shfl(keep ? 1 : 0, row)) {
+      uint8_t* dst = reinterpret_cast<uint8_t*>((uintptr_t)rt) + c * 16;
+      asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(v) : "memory");
     }
   }
   return true;
@@ -1978,7 +2005,7 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
   int U = j_use > j_start ? (j_use - j_start + 63) / 64 : 0;
 
   // the query tiles, known once the row's compaction is visible
-  int g = 0, qt = 0;
+  int g = 0, qt = 0, qpos_row = 0;
   bool wave_work = false, qok = false;
   QOp<true> qo;
   auto load_rows = [&]() {   // while the first keys are in flight
@@ -1996,6 +2023,7 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
     const int qidx = qt * 32 + qi;
     qok = wave_work && qidx < g;
     const int qpos = qok ? coherent_load(gidx_b + qidx) : 0;
+    qpos_row = qpos;
     qo.load(p.Qg + (head + qpos) * RB, qok, h32);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
@@ -2055,7 +2083,7 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
       p.part_ml[pidx * 2 + 1] = lt;
     }
   }
-  if (wave_work) finish_global_tile<true>(p, b, h, qt, g, lane);
+  if (wave_work) finish_global_tile<true>(p, b, h, qt, g, lane, qpos_row);
   return true;
 }
 

@@ -148,8 +148,7 @@ class Plan:
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
 
-    def forward(self, q, k, v, qg, kg, vg, lmask, gmask, out=None, stream=None):
-        """Enqueue one forward; returns O (allocated if `out` is None)."""
+    def _validate(self, q, k, v, qg, kg, vg, lmask, gmask, out):
         import torch
         tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
         for t, name in ((q, "q"), (k, "k"), (v, "v"), (qg, "qg"), (kg, "kg"), (vg, "vg")):
@@ -167,6 +166,11 @@ class Plan:
             self._check(out, "out", tdt)
             if tuple(out.shape) != self.shape:
                 raise ValueError("out has the wrong shape")
+        return out
+
+    def forward(self, q, k, v, qg, kg, vg, lmask, gmask, out=None, stream=None):
+        """Enqueue one forward; returns O (allocated if `out` is None)."""
+        out = self._validate(q, k, v, qg, kg, vg, lmask, gmask, out)
         st = self.lib.lwattn_forward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                      qg.data_ptr(), kg.data_ptr(), vg.data_ptr(),
                                      lmask.data_ptr(), gmask.data_ptr(), out.data_ptr(),
@@ -174,6 +178,24 @@ class Plan:
         if st != OK:
             raise LwattnError(st, "lwattn_forward")
         return out
+
+    def bind(self, q, k, v, qg, kg, vg, lmask, gmask, out=None, stream=None):
+        """Validate the buffers once and return a no-argument callable that
+        enqueues the same forward again (same buffers, same stream), with the
+        arguments marshalled up front: the per-call host cost is one C call.
+        The callable keeps the tensors alive and returns O."""
+        out = self._validate(q, k, v, qg, kg, vg, lmask, gmask, out)
+        fn = self.lib.lwattn_forward
+        args = (self.handle,) + tuple(ctypes.c_void_p(t.data_ptr()) for t in
+                                      (q, k, v, qg, kg, vg, lmask, gmask, out)) + (_stream_handle(stream),)
+        keep = (q, k, v, qg, kg, vg, lmask, gmask, out)
+
+        def run():
+            st = fn(*args)
+            if st != OK:
+                raise LwattnError(st, "lwattn_forward")
+            return keep[-1]
+        return run
 
     __call__ = forward
 

@@ -146,6 +146,27 @@ def test_deterministic_and_poison_invariant():
     assert torch.equal(a, c)
 
 
+def test_bound_call_repeats_the_forward():
+    """Plan.bind marshals the call once; every call of it must give exactly what
+    Plan.forward gives on the same buffers."""
+    spec = workloads.custom(1, 3, 700, 64, 96, "bf16", [0, 1, 0], seed=8, n_global=4,
+                            pad_mode="per_batch", pad_hi=90)
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec)
+    ref, st = run(plan, ts, lm, gm)
+    assert st == lw.OK
+    out = torch.full_like(ref, float("nan"))
+    step = plan.bind(*ts, lm, gm, out=out)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        got = step()
+        torch.cuda.synchronize()
+        assert got.data_ptr() == out.data_ptr()
+        assert torch.equal(got, ref)
+    assert plan.sync_status() == lw.OK
+
+
 def test_too_many_globals_is_reported():
     spec = workloads.custom(2, 2, 300, 64, 32, "f32", [0, 1], seed=6, n_global=20)
     x = workloads.generate(spec)

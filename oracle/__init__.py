@@ -72,6 +72,9 @@ def _load():
         lib.lwo_rows.restype = ctypes.c_int
         lib.lwo_forward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int32]
         lib.lwo_forward.restype = ctypes.c_int
+        lib.lwo_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p] + \
+            [ctypes.c_void_p] * 6 + [ctypes.c_int32]
+        lib.lwo_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -160,3 +163,23 @@ def rows(Q, K, V, Qg, Kg, Vg, lmask, gmask, window, row_index, dilation=None, sc
     if rc:
         raise RuntimeError(f"oracle rows failed ({rc})")
     return out
+
+
+def backward(Q, K, V, Qg, Kg, Vg, lmask, gmask, dO, window, dilation=None, scale=None,
+             threads=None):
+    """Gradients (dQ, dK, dV, dQg, dKg, dVg), float64 [B,H,n,d] each, of a loss whose
+    gradient with respect to the forward's output is dO (inputs upcast exactly to
+    double; the chain rule through the definition, see the C file)."""
+    d = np.shape(Q)[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    bound = _Bound(Q, K, V, Qg, Kg, Vg, lmask, gmask, window, dilation, scale)
+    go = _f32(dO)
+    if go.shape != bound.shape:
+        raise ValueError("dO must have the shape of the output [B,H,n,d]")
+    outs = [np.empty(bound.shape, np.float64) for _ in range(6)]
+    rc = _load().lwo_backward(ctypes.byref(bound.p), go.ctypes.data,
+                              *[o.ctypes.data for o in outs], threads or default_threads())
+    if rc:
+        raise RuntimeError(f"oracle backward failed ({rc})")
+    return tuple(outs)

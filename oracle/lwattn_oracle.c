@@ -209,3 +209,101 @@ int lwo_forward(const lwo_problem* p, double* out, int32_t threads) {
   }
   return err;
 }
+
+/* Gradient of the forward with respect to Q, K, V, Qg, Kg, Vg, given dO, the
+ * gradient of a scalar loss with respect to the output (all [B,H,n,d]).
+ *
+ * It is the chain rule through the definition above, row by row.  For a
+ * non-padded row i with allowed keys t (the same set lwo_allowed gives the
+ * forward), scores x_t = scale <q_i, k_t> and probabilities p_t = softmax(x)_t,
+ * the output O_i = sum_t p_t v_t gives, with e_t = <dO_i, v_t> and
+ * D = sum_t p_t e_t:
+ *   dx_t  = p_t (e_t - D)                  (softmax Jacobian)
+ *   dq_i  = scale * sum_t dx_t k_t         (into dQ for a local row, dQg for a global row)
+ *   dk_t += scale * dx_t q_i               (into dK, or dKg for a global row)
+ *   dv_t += p_t dO_i                       (into dV, or dVg for a global row)
+ * A local row's window keys and its global keys both use (q, k, v) = (Q, K, V);
+ * a global row uses (Qg, Kg, Vg).  Padded rows contribute nothing, and every
+ * entry no row touches stays zero.  (b, h) pairs are independent (one OpenMP
+ * task each); within a pair the rows are summed in order. */
+int lwo_backward(const lwo_problem* p, const float* dO, double* dQ, double* dK, double* dV,
+                 double* dQg, double* dKg, double* dVg, int32_t threads) {
+  const int32_t n = p->n, d = p->d;
+  const int64_t pairs = (int64_t)p->B * p->H;
+  const int64_t per = (int64_t)n * d;
+  if (threads < 1) threads = 1;
+  int err = 0;
+#pragma omp parallel num_threads(threads)
+  {
+    int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    double* prob = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double* dx = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    if (!keys || !prob || !dx) {
+#pragma omp atomic write
+      err = 2;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t bh = 0; bh < pairs; ++bh) {
+        const int32_t b = (int32_t)(bh / p->H), h = (int32_t)(bh % p->H);
+        const int64_t head = bh * per;
+        for (int64_t e = 0; e < per; ++e) {
+          dQ[head + e] = 0.0; dK[head + e] = 0.0; dV[head + e] = 0.0;
+          dQg[head + e] = 0.0; dKg[head + e] = 0.0; dVg[head + e] = 0.0;
+        }
+        const float* lm = p->lmask + (int64_t)b * n;
+        const float* gm = p->gmask + (int64_t)b * n;
+        for (int32_t i = 0; i < n; ++i) {
+          int32_t kind;
+          const int64_t cnt = lwo_allowed(lm, gm, n, p->window, p->gap[h], i, keys, &kind);
+          if (kind == LWO_PADDED || cnt == 0) continue;
+          const int glob = kind == LWO_GLOBAL;
+          const float* q = (glob ? p->Qg : p->Q) + head + (int64_t)i * d;
+          const float* kmat = (glob ? p->Kg : p->K) + head;
+          const float* vmat = (glob ? p->Vg : p->V) + head;
+          const float* go = dO + head + (int64_t)i * d;
+          double* gq = (glob ? dQg : dQ) + head + (int64_t)i * d;
+          double* gk = (glob ? dKg : dK) + head;
+          double* gv = (glob ? dVg : dV) + head;
+          /* probabilities, as in the forward */
+          double mx = -INFINITY;
+          for (int64_t t = 0; t < cnt; ++t) {
+            const float* kr = kmat + (int64_t)keys[t] * d;
+            double dot = 0.0;
+            for (int32_t c = 0; c < d; ++c) dot += (double)q[c] * (double)kr[c];
+            prob[t] = p->scale * dot;
+            if (prob[t] > mx) mx = prob[t];
+          }
+          double sum = 0.0;
+          for (int64_t t = 0; t < cnt; ++t) {
+            prob[t] = exp(prob[t] - mx);
+            sum += prob[t];
+          }
+          for (int64_t t = 0; t < cnt; ++t) prob[t] /= sum;
+          /* e_t = <dO_i, v_t>, D = sum_t p_t e_t, dx_t = p_t (e_t - D) */
+          double D = 0.0;
+          for (int64_t t = 0; t < cnt; ++t) {
+            const float* vr = vmat + (int64_t)keys[t] * d;
+            double e = 0.0;
+            for (int32_t c = 0; c < d; ++c) e += (double)go[c] * (double)vr[c];
+            dx[t] = e;
+            D += prob[t] * e;
+          }
+          for (int64_t t = 0; t < cnt; ++t) dx[t] = prob[t] * (dx[t] - D);
+          for (int64_t t = 0; t < cnt; ++t) {
+            const int64_t j = keys[t];
+            const float* kr = kmat + j * d;
+            for (int32_t c = 0; c < d; ++c) {
+              gq[c] += p->scale * dx[t] * (double)kr[c];
+              gk[j * d + c] += p->scale * dx[t] * (double)q[c];
+              gv[j * d + c] += prob[t] * (double)go[c];
+            }
+          }
+        }
+      }
+    }
+    free(keys);
+    free(prob);
+    free(dx);
+  }
+  return err;
+}

@@ -113,6 +113,38 @@ lwattn_status lwattn_forward(lwattn_plan_t plan,
                              const float* local_attn_mask, const float* global_attn_mask,
                              void* O, hipStream_t stream);
 
+/* Enqueues the backward of one forward on `stream` (asynchronous; no
+ * allocation, no host sync): the gradients of a loss with respect to Q, K, V,
+ * Qg, Kg, Vg, given dO = dLoss/dO.  It differentiates the operation that
+ * lwattn_forward computes (LongFormer notes, sections "Sliding Window",
+ * "Dilated Sliding Window" and "Global Attention"): with P the softmax of a
+ * row over its allowed keys, dP_ij = <dO_i, v_j> and D_i = <dO_i, O_i>,
+ *   dS_ij = P_ij (dP_ij - D_i),  dq_i = scale sum_j dS_ij k_j,
+ *   dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dO_i,
+ * over (Q, K, V) for a local row's window and global keys and (Qg, Kg, Vg) for
+ * a global row.
+ *   Q .. Vg, masks      : the forward's inputs (same layouts and rules).
+ *   O                   : device [B,H,n,d], dtype: the forward's output for them.
+ *   dO                  : device [B,H,n,d], dtype; rows of padded positions are
+ *                         not read.
+ *   dQ, dK, dV, dQg, dKg, dVg : device [B,H,n,d], dtype; every element is
+ *                         written (zero where no path reaches it).  They must
+ *                         not overlap each other or any input.
+ * All pointers 16-byte aligned.  Arithmetic in fp32 (bf16 storage is widened
+ * on load and rounded RNE on store).  Three kernel launches: the global-index
+ * compaction, dQ/dQg (which leaves each row's log-sum-exp and D in the plan's
+ * workspace), then dK/dV/dKg/dVg.  Errors as for lwattn_forward; too many
+ * global tokens is reported by lwattn_sync_status.  Shares the plan's
+ * workspace with lwattn_forward: a forward and a backward of one plan must
+ * not overlap (same stream, or ordered). */
+lwattn_status lwattn_backward(lwattn_plan_t plan,
+                              const void* Q, const void* K, const void* V,
+                              const void* Qg, const void* Kg, const void* Vg,
+                              const float* local_attn_mask, const float* global_attn_mask,
+                              const void* O, const void* dO,
+                              void* dQ, void* dK, void* dV, void* dQg, void* dKg, void* dVg,
+                              hipStream_t stream);
+
 /* Frees the plan and its workspace.  NULL is a no-op. */
 lwattn_status lwattn_destroy(lwattn_plan_t plan);
 

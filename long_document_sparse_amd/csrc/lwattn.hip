@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "backward.hpp"
 #include "lwattn.h"
 
 namespace {
@@ -60,6 +61,10 @@ struct lwattn_plan_s {
   bool inject_timeout = false; // fault test: the next forward's waits give up
   int32_t* head_stride = nullptr;
   int32_t* head_blk = nullptr;
+  // backward: 64-row blocks per head (all residue classes), per-row statistics
+  int32_t* head_blk64 = nullptr;
+  int blocks64_per_b = 0;
+  float2* stats = nullptr;
   // timing
   int timing_cap = 0;
   int timing_calls = 0;
@@ -81,6 +86,8 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->fault);
   (void)hipFree(p->head_stride);
   (void)hipFree(p->head_blk);
+  (void)hipFree(p->head_blk64);
+  (void)hipFree(p->stats);
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
   delete p;
 }
@@ -143,17 +150,21 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   p->cfg.dilation = nullptr;   // the plan keeps its own copy
 
   // band geometry: per head, sum over residue classes of ceil(n_rho / 128)
-  std::vector<int32_t> stride(H), blk(H + 1, 0);
+  // (forward) and of ceil(n_rho / 64) (backward)
+  std::vector<int32_t> stride(H), blk(H + 1, 0), blk64(H + 1, 0);
   for (int h = 0; h < H; ++h) {
     const int s = p->gap[h] + 1;
     stride[h] = s;
-    int64_t nb = 0;
+    int64_t nb = 0, nb64 = 0;
     for (int rho = 0; rho < s && rho < n; ++rho) {
       const int64_t nr = ((int64_t)n - rho + s - 1) / s;
       nb += (nr + lwk::ROWS_WG - 1) / lwk::ROWS_WG;
+      nb64 += (nr + lwk::bw::T - 1) / lwk::bw::T;
     }
     blk[h + 1] = blk[h] + (int32_t)nb;
+    blk64[h + 1] = blk64[h] + (int32_t)nb64;
   }
+  p->blocks64_per_b = blk64[H];
   p->blocks_per_b = blk[H];
   p->stride_host = stride;
   p->blk_host = blk;
@@ -225,12 +236,15 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->fault, 4);
   alloc((void**)&p->head_stride, (size_t)H * 4);
   alloc((void**)&p->head_blk, (size_t)(H + 1) * 4);
+  alloc((void**)&p->head_blk64, (size_t)(H + 1) * 4);
+  alloc((void**)&p->stats, (size_t)B * H * n * sizeof(float2));
   if (!ok) {
     free_plan(p);
     return LWATTN_E_NOMEM;
   }
   if ((H > 0 && !hip_ok(hipMemcpy(p->head_stride, stride.data(), (size_t)H * 4, hipMemcpyHostToDevice), "hipMemcpy")) ||
       !hip_ok(hipMemcpy(p->head_blk, blk.data(), (size_t)(H + 1) * 4, hipMemcpyHostToDevice), "hipMemcpy") ||
+      !hip_ok(hipMemcpy(p->head_blk64, blk64.data(), (size_t)(H + 1) * 4, hipMemcpyHostToDevice), "hipMemcpy") ||
       (B > 0 && !hip_ok(hipMemset(p->status, 0, (size_t)B * 4), "hipMemset")) ||
       (B > 0 && !hip_ok(hipMemset(p->gcnt, 0, (size_t)B * 4), "hipMemset")) ||
       !hip_ok(hipMemset(p->tile_cnt, 0, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4), "hipMemset") ||
@@ -340,6 +354,91 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
 
   if (timed) ++p->timing_calls;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, const void* V,
+                              const void* Qg, const void* Kg, const void* Vg,
+                              const float* lmask, const float* gmask, const void* O, const void* dO,
+                              void* dQ, void* dK, void* dV, void* dQg, void* dKg, void* dVg,
+                              hipStream_t stream) {
+  if (!p) return LWATTN_E_INVALID;
+  const lwattn_config& c = p->cfg;
+  if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
+  const void* ptrs[] = {Q, K, V, Qg, Kg, Vg, O, dO, dQ, dK, dV, dQg, dKg, dVg};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return LWATTN_E_INVALID;
+  if (!lmask || !gmask || ((uintptr_t)lmask & 3u) || ((uintptr_t)gmask & 3u)) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+
+  // 1. the global-index compaction (published under a fresh epoch, so that the
+  //    next forward's waits still see a new number)
+  lwk::Params cp;
+  std::memset(&cp, 0, sizeof(cp));
+  cp.lmask = lmask;
+  cp.gmask = gmask;
+  cp.flags = p->flags;
+  cp.gidx = p->gidx;
+  cp.gcnt = p->gcnt;
+  cp.status = p->status;
+  cp.ready = p->ready;
+  cp.fault = p->fault;
+  p->epoch = p->epoch >= INT32_MAX - 1 ? 1 : p->epoch + 1;
+  cp.epoch = p->epoch;
+  cp.publish = p->epoch;
+  cp.B = c.B;
+  cp.H = c.H;
+  cp.n = c.n;
+  cp.max_global = c.max_global;
+  cp.mask_vec = ((((uintptr_t)lmask | (uintptr_t)gmask) & 15u) == 0 && (c.n % 4) == 0) ? 1 : 0;
+  hipLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream, cp);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+
+  lwk::bw::BwParams bp;
+  bp.Q = (const uint8_t*)Q;
+  bp.K = (const uint8_t*)K;
+  bp.V = (const uint8_t*)V;
+  bp.Qg = (const uint8_t*)Qg;
+  bp.Kg = (const uint8_t*)Kg;
+  bp.Vg = (const uint8_t*)Vg;
+  bp.O = (const uint8_t*)O;
+  bp.dO = (const uint8_t*)dO;
+  bp.dQ = (uint8_t*)dQ;
+  bp.dK = (uint8_t*)dK;
+  bp.dV = (uint8_t*)dV;
+  bp.dQg = (uint8_t*)dQg;
+  bp.dKg = (uint8_t*)dKg;
+  bp.dVg = (uint8_t*)dVg;
+  bp.lmask = lmask;
+  bp.gmask = gmask;
+  bp.gidx = p->gidx;
+  bp.gcnt = p->gcnt;
+  bp.head_stride = p->head_stride;
+  bp.head_blk = p->head_blk64;
+  bp.stats = p->stats;
+  bp.B = c.B;
+  bp.H = c.H;
+  bp.n = c.n;
+  bp.r = (int)std::min<int64_t>(c.window / 2, c.n);
+  bp.max_global = c.max_global;
+  bp.ntg = (c.max_global + lwk::bw::T - 1) / lwk::bw::T;
+  bp.blocks_per_b = p->blocks64_per_b;
+  bp.scale = c.scale;
+  const int64_t grid = (int64_t)c.B * p->blocks64_per_b + (int64_t)c.B * c.H * bp.ntg;
+  if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
+  // 2. dQ, dQg and the rows' statistics; 3. dK, dV, dKg, dVg
+  if (c.dtype == LWATTN_BF16) {
+    (void)hipFuncSetAttribute((const void*)lwk::bw::dq_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DQ_SMEM);
+    (void)hipFuncSetAttribute((const void*)lwk::bw::dkv_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DKV_SMEM);
+    hipLaunchKernelGGL(lwk::bw::dq_kernel<true>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DQ_SMEM, stream, bp);
+    hipLaunchKernelGGL(lwk::bw::dkv_kernel<true>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DKV_SMEM, stream, bp);
+  } else {
+    (void)hipFuncSetAttribute((const void*)lwk::bw::dq_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DQ_SMEM);
+    (void)hipFuncSetAttribute((const void*)lwk::bw::dkv_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DKV_SMEM);
+    hipLaunchKernelGGL(lwk::bw::dq_kernel<false>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DQ_SMEM, stream, bp);
+    hipLaunchKernelGGL(lwk::bw::dkv_kernel<false>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DKV_SMEM, stream, bp);
+  }
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   return LWATTN_OK;
 }
 

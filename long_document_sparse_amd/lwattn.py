@@ -38,6 +38,7 @@ SIGNATURES = [
     ("lwattn_check_config", ctypes.c_int, [ctypes.POINTER(Config)]),
     ("lwattn_plan", ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_int, ctypes.POINTER(_c_p)]),
     ("lwattn_forward", ctypes.c_int, [_c_p] * 9 + [_c_p, _c_p]),
+    ("lwattn_backward", ctypes.c_int, [_c_p] * 17 + [_c_p]),
     ("lwattn_destroy", ctypes.c_int, [_c_p]),
     ("lwattn_global_index", ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
     ("lwattn_sync_status", ctypes.c_int, [_c_p, _c_p]),
@@ -178,6 +179,30 @@ class Plan:
         if st != OK:
             raise LwattnError(st, "lwattn_forward")
         return out
+
+    def backward(self, q, k, v, qg, kg, vg, lmask, gmask, o, do, grads=None, stream=None):
+        """Enqueue the backward of the forward that produced `o`; returns
+        (dQ, dK, dV, dQg, dKg, dVg), allocated if `grads` is None."""
+        import torch
+        self._validate(q, k, v, qg, kg, vg, lmask, gmask, o)
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        self._check(do, "do", tdt)
+        if tuple(do.shape) != self.shape:
+            raise ValueError("do has the wrong shape")
+        if grads is None:
+            grads = tuple(torch.empty(self.shape, dtype=tdt, device=q.device) for _ in range(6))
+        for t, name in zip(grads, ("dq", "dk", "dv", "dqg", "dkg", "dvg")):
+            self._check(t, name, tdt)
+            if tuple(t.shape) != self.shape:
+                raise ValueError(f"{name} has the wrong shape")
+        st = self.lib.lwattn_backward(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      qg.data_ptr(), kg.data_ptr(), vg.data_ptr(),
+                                      lmask.data_ptr(), gmask.data_ptr(), o.data_ptr(),
+                                      do.data_ptr(), *[t.data_ptr() for t in grads],
+                                      _stream_handle(stream))
+        if st != OK:
+            raise LwattnError(st, "lwattn_backward")
+        return grads
 
     def bind(self, q, k, v, qg, kg, vg, lmask, gmask, out=None, stream=None):
         """Validate the buffers once and return a no-argument callable that

@@ -1,0 +1,93 @@
+"""GPU parity of the backward (lwattn_backward through the C ABI) against the
+oracle's backward, element by element over all six gradients.
+
+Tolerance, derived from the arithmetic: both sides see the same stored inputs;
+the HIP path computes in fp32 (scores, exp, every sum over up to n rows or keys)
+and rounds the gradients to the storage type, the oracle in fp64.  Per tensor,
+relative to its largest entry: fp32 storage |err| <= 1e-4 * max |g|; bf16
+storage (output rounding alone is 2^-9 relative) |err| <= 2e-2 * max |g|.  A
+tensor that no path reaches must be exactly zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import make_plan, say, to_dev, to_np64
+from long_document_sparse_amd import lwattn as lw
+from long_document_sparse_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("dQ", "dK", "dV", "dQg", "dKg", "dVg")
+
+CASES = [
+    # (B, H, n, window, dtype, dilation, n_global, global_mode, pad_mode, pad_hi)
+    (1, 2, 200, 64, "f32", [0, 1], 1, "first", "none", 0),
+    (2, 2, 333, 40, "bf16", [0, 2], 5, "random", "per_batch", 80),
+    (1, 3, 300, 128, "f32", [0, 1, 3], 70, "random", "per_batch", 60),   # two global tiles
+    (2, 2, 130, 400, "bf16", [0, 0], 3, "first", "none", 0),             # window > n
+    (1, 2, 257, 16, "f32", [1, 4], 0, "first", "scatter", 40),           # no globals, scattered pads
+    (1, 1, 65, 8, "bf16", [0], 65, "first", "none", 0),                  # every token global
+]
+
+
+def _grad_out(x, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal(x.tensors()[0].shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}n{c[2]}w{c[3]}{c[4]}g{c[6]}{c[8]}")
+def test_backward_matches_oracle(case):
+    B, H, n, window, dtype, dil, ng, gmode, pmode, phi = case
+    spec = workloads.custom(B, H, n, 64, window, dtype, dil, seed=21, n_global=ng,
+                            global_mode=gmode, pad_mode=pmode, pad_hi=phi)
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec, max_global=max(ng, 1))
+    o = torch.empty_like(ts[0])
+    plan(*ts, lm, gm, out=o)
+    go_np = _grad_out(x, 3)
+    tdt = ts[0].dtype
+    go = torch.from_numpy(go_np).to(ts[0].device).to(tdt)
+    grads = tuple(torch.full_like(ts[0], float("nan")) for _ in range(6))
+    plan.backward(*ts, lm, gm, o, go, grads=grads)
+    assert plan.sync_status() == lw.OK
+    # the oracle sees exactly the stored values (bf16 inputs widened)
+    ins = [to_np64(t) for t in ts]
+    go_seen = to_np64(go)
+    want = oracle.backward(*ins, x.lmask, x.gmask, go_seen, spec.window, spec.dilation, spec.scale)
+    for name, g, w in zip(NAMES, grads, want):
+        got = to_np64(g)
+        assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+        err = float(np.max(np.abs(got - w)))
+        ref = float(np.max(np.abs(w)))
+        say(f"{name}: max abs err {err:.3e}, max |g| {ref:.3e}")
+        if ref == 0.0:
+            assert err == 0.0, name
+        else:
+            assert err <= TOL[dtype] * ref, name
+
+
+def test_backward_base_size_bf16():
+    """The benchmark's configuration (B=1, H=12, n=4096, w=512, one global token
+    at the start, bf16), every element of every gradient."""
+    spec = workloads.named("base")
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec)
+    o = torch.empty_like(ts[0])
+    plan(*ts, lm, gm, out=o)
+    go = torch.from_numpy(_grad_out(x, 4)).to(ts[0].device).to(ts[0].dtype)
+    grads = plan.backward(*ts, lm, gm, o, go)
+    assert plan.sync_status() == lw.OK
+    want = oracle.backward(*[to_np64(t) for t in ts], x.lmask, x.gmask, to_np64(go),
+                           spec.window, spec.dilation, spec.scale)
+    for name, g, w in zip(NAMES, grads, want):
+        got = to_np64(g)
+        err = float(np.max(np.abs(got - w)))
+        ref = float(np.max(np.abs(w)))
+        say(f"base {name}: max abs err {err:.3e}, max |g| {ref:.3e}")
+        assert np.all(np.isfinite(got))
+        assert err <= TOL["bf16"] * ref, name

@@ -8,6 +8,7 @@ memory.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload base]
                   [--no-cpu-baseline] [--no-timing] [--copy-probe MIB]
+                  [--pass forward|backward]
 
 The default workload is "base": B=1, H=12, n=4096, d=64, w=512 (+-256), no
 dilation, one global token at position 0, bf16 storage, fp32 accumulation.
@@ -18,6 +19,12 @@ events that the dispatch of the attention kernel itself records at the start
 and the end of its execution, on every fourth forward of the timed loop
 (recording them on every forward would make the host, not the GPU, set the
 pace of the loop).
+
+--pass backward times lwattn_backward instead (dQ, dK, dV, dQg, dKg, dVg of a
+seeded dO, after one forward for O) and prints its own line: its three
+launches are timed together with events on the stream around the timed loop,
+its roofline is the fp32 vector-ALU one (the kernels compute in fp32 on the
+VALU), and its CPU baseline is the oracle's backward.
 
 --copy-probe runs, after the timed loop, a plain device-to-device copy of the
 given size a few times; a counter pass over the same command then gives the
@@ -36,9 +43,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense MFMA
+PEAK_FP32_VECTOR = 157.3                          # MI355X fp32 vector ALU, TFLOP/s
 PEAK_HBM_GBS = 8000.0
 TIMING_EVERY = 4
 METRIC = "window+global attn fwd tokens/s & TFLOP/s (% bf16 MFMA peak), n=4096 w=512"
+METRIC_BWD = "window+global attn bwd tokens/s & TFLOP/s (% fp32 vector peak), n=4096 w=512"
 KERNEL_SOURCES = ("long_document_sparse_amd/csrc/kernels.hpp",
                   "long_document_sparse_amd/csrc/lwattn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.txt")
@@ -122,6 +131,103 @@ def cpu_baseline(x, budget_s=12.0):
             "sample": sample}
 
 
+def cpu_baseline_backward(x, go, budget_s=12.0):
+    """The oracle's backward, as it is, on the host cores, repeated over the
+    whole problem for about budget_s seconds."""
+    import oracle
+    spec = x.spec
+    threads = oracle.default_threads()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    args = (*x.tensors(), x.lmask, x.gmask, go, spec.window, spec.dilation, spec.scale)
+    reps, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        oracle.backward(*args, threads=threads)
+        t += time.perf_counter() - t0
+        reps += 1
+    value = spec.B * spec.n * reps / t
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole backward, repeated {reps} times ({t:.2f} s)"}
+
+
+def run_backward(args, spec, x, ts, lm, gm, plan):
+    """--pass backward: one JSON line for lwattn_backward."""
+    import numpy as np
+    import torch
+    from long_document_sparse_amd import flops as fl
+    from long_document_sparse_amd import lwattn
+    dev = ts[0].device
+    o = torch.empty_like(ts[0])
+    plan(*ts, lm, gm, out=o)
+    go_np = np.random.default_rng(spec.seed + 101).standard_normal(ts[0].shape).astype(np.float32)
+    go = torch.from_numpy(go_np).to(dev).to(ts[0].dtype)
+    grads = tuple(torch.empty_like(ts[0]) for _ in range(6))
+    step = plan.bind_backward(*ts, lm, gm, o, go, grads)
+    for _ in range(args.warmup):
+        step()
+    st = plan.sync_status()
+    if st != lwattn.OK:
+        raise SystemExit(f"backward failed: {lwattn.strerror(st)}")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = plan.sync_status()
+    if st != lwattn.OK:
+        raise SystemExit(f"backward failed: {lwattn.strerror(st)}")
+    t_call = e0.elapsed_time(e1) * 1e-3 / args.steps        # s per backward, on the stream
+    flop = fl.backward_flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
+    nbytes = fl.backward_bytes(x.lmask, x.gmask, spec.H, spec.d, 2 if spec.dtype == "bf16" else 4)
+    tflops = flop / t_call / 1e12
+    gbs = nbytes / t_call / 1e9
+    alu_bound = flop / (PEAK_FP32_VECTOR * 1e12) > nbytes / (PEAK_HBM_GBS * 1e9)
+    roofline = ({"bound": "alu", "achieved": round(tflops, 2), "peak": PEAK_FP32_VECTOR,
+                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_VECTOR, 4), "traffic": None}
+                if alu_bound else
+                {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None})
+    roofline.update({"kernel": "backward (compact_kernel + dq_kernel + dkv_kernel)",
+                     "algorithmic_flop": flop, "algorithmic_bytes": nbytes,
+                     "alu_view": {"achieved_tflops": round(tflops, 2), "peak": PEAK_FP32_VECTOR,
+                                  "frac": round(tflops / PEAK_FP32_VECTOR, 4)},
+                     "hbm_view": {"achieved_gbs": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                  "frac": round(gbs / PEAK_HBM_GBS, 4)},
+                     "source_sha256": source_hash()})
+    tokens = spec.B * spec.n
+    res = {
+        "metric": METRIC_BWD,
+        "value": round(tokens / (elapsed / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded, N(0,1)/sqrt(d) inputs, N(0,1) dO; no dataset)",
+        "config": {"workload": describe(spec) + "; backward", "global_batch": spec.B,
+                   "seq_len": spec.n, "heads": spec.H, "head_dim": spec.d, "window": spec.window,
+                   "parallelism": "single GPU", "timing": "warm (back to back)"},
+        "tflops_per_s": round(flop / (elapsed / args.steps) / 1e12, 2),
+        "us_per_backward_on_stream": round(t_call * 1e6, 2),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_backward(x, go_np.astype(np.float32) if spec.dtype == "f32"
+                                                    else go.float().cpu().numpy())
+    plan.close()
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +237,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel HIP events (roofline fields become null)")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                    help="time the forward (default) or the backward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device to device 5 times (counter calibration)")
     args = ap.parse_args()
@@ -154,6 +262,9 @@ def main():
     out = torch.empty_like(ts[0])
     plan = lwattn.Plan(spec.B, spec.H, spec.n, spec.d, spec.window, spec.dilation,
                        spec.max_global, spec.scale, spec.dtype)
+    if args.which == "backward":
+        run_backward(args, spec, x, ts, lm, gm, plan)
+        return
 
     # the buffers are validated and the call marshalled once; every step
     # below is one lwattn_forward

@@ -116,27 +116,35 @@ __device__ __forceinline__ void load_tile(float* dst, const uint8_t* head, const
   }
 }
 
-// c[i][j] += sum_k A[rg + 16 i][k] * B[cg + 16 j][k] over k < 64 (A and B row-major).
-__device__ __forceinline__ void gemm_abt(const float* A, const float* B, float (&c)[4][4]) {
+// c[i][j] += sum_k A[rg + 16 i][k] * B[cg + 16 j][k] over k < kmax (A and B
+// row-major), for i < ni and j < nj: a tile with few live rows (a tile of
+// global rows or keys) takes ni or nj = ceil(live / 16) and kmax = the live
+// rows rounded up to 4.  The bounds are workgroup-uniform.
+__device__ __forceinline__ void gemm_abt(const float* A, const float* B, float (&c)[4][4],
+                                         int ni = 4, int nj = 4, int kmax = T) {
   const int t = threadIdx.x, rg = t >> 4, cg = t & 15;
-#pragma unroll 4
-  for (int k = 0; k < T; k += 4) {
+  for (int k = 0; k < kmax; k += 4) {
     float4 a[4], bv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4*>(A + (rg + 16 * i) * LS + k);
+    for (int i = 0; i < 4; ++i)
+      if (i < ni) a[i] = *reinterpret_cast<const float4*>(A + (rg + 16 * i) * LS + k);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = *reinterpret_cast<const float4*>(B + (cg + 16 * j) * LS + k);
+    for (int j = 0; j < 4; ++j)
+      if (j < nj) bv[j] = *reinterpret_cast<const float4*>(B + (cg + 16 * j) * LS + k);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[i][j] = fmaf(a[i].x, bv[j].x, c[i][j]);
-        c[i][j] = fmaf(a[i].y, bv[j].y, c[i][j]);
-        c[i][j] = fmaf(a[i].z, bv[j].z, c[i][j]);
-        c[i][j] = fmaf(a[i].w, bv[j].w, c[i][j]);
-      }
+      for (int j = 0; j < 4; ++j)
+        if (i < ni && j < nj) {
+          c[i][j] = fmaf(a[i].x, bv[j].x, c[i][j]);
+          c[i][j] = fmaf(a[i].y, bv[j].y, c[i][j]);
+          c[i][j] = fmaf(a[i].z, bv[j].z, c[i][j]);
+          c[i][j] = fmaf(a[i].w, bv[j].w, c[i][j]);
+        }
   }
 }
+
+__device__ __forceinline__ int groups16(int live) { return live >= T ? 4 : (live + 15) / 16; }
 
 __device__ __forceinline__ void zero(float (&c)[4][4]) {
 #pragma unroll
@@ -355,6 +363,7 @@ __device__ void dq_global(const BwParams& p, int b, int h, int gt, float* sm, Me
   int g = p.gcnt[b];
   if (g > p.max_global) g = p.max_global;
   if (T * gt >= g) return;
+  const int ni = groups16(g - T * gt);   // row groups with a live global row
   if (t < T) {
     const int idx = T * gt + t;
     const int ps = idx < g ? p.gidx[(int64_t)b * n + idx] : -1;
@@ -395,7 +404,7 @@ __device__ void dq_global(const BwParams& p, int b, int h, int gt, float* sm, Me
     __syncthreads();
     float c[4][4];
     zero(c);
-    gemm_abt(tQ, tK, c);
+    gemm_abt(tQ, tK, c, ni);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float mx = m[i];
@@ -436,8 +445,8 @@ __device__ void dq_global(const BwParams& p, int b, int h, int gt, float* sm, Me
     float c[4][4], e[4][4];
     zero(c);
     zero(e);
-    gemm_abt(tQ, tK, c);
-    gemm_abt(tdO, tV, e);
+    gemm_abt(tQ, tK, c, ni);
+    gemm_abt(tdO, tV, e, ni);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = rg + 16 * i;
@@ -450,7 +459,7 @@ __device__ void dq_global(const BwParams& p, int b, int h, int gt, float* sm, Me
     }
     put(tS, c);
     __syncthreads();
-    gemm_abt(tS, tKt, acc);
+    gemm_abt(tS, tKt, acc, ni);
   }
   __syncthreads();
 #pragma unroll
@@ -469,9 +478,12 @@ __device__ void dq_global(const BwParams& p, int b, int h, int gt, float* sm, Me
 // One sweep of a key tile (kpos/kkind set, K-side tiles tK, tV staged) over
 // query-row tiles: accK += dS^T Q, accV += P^T dO.  set_rows(qt) fills
 // rpos/rkind/lse/dd of row tile qt; allowed(qt, key, row) is the mask.
-template <bool BF, class SetRows, class Allowed>
+// ni: key groups with a live key; live_rows(qt): live rows of row tile qt
+// (rows past them are dead in every row tile but the last).
+template <bool BF, class SetRows, class Allowed, class LiveRows>
 __device__ __forceinline__ void kv_sweep(const BwParams& p, const uint8_t* Qsrc, int64_t hoff, int nq,
-                                         const SetRows& set_rows, const Allowed& allowed, float* sm,
+                                         const SetRows& set_rows, const Allowed& allowed,
+                                         const LiveRows& live_rows, int ni, float* sm,
                                          Meta& mt, float (&accK)[4][4], float (&accV)[4][4]) {
   float* tK = sm;
   float* tV = sm + TILE;
@@ -491,11 +503,13 @@ __device__ __forceinline__ void kv_sweep(const BwParams& p, const uint8_t* Qsrc,
     load_tile<BF>(tQt, Qsrc + hoff, mt.rpos, true);
     load_tile<BF>(tdOt, p.dO + hoff, mt.rpos, true);
     __syncthreads();
+    const int lr = live_rows(qt);
+    const int nj = groups16(lr), kr = lr >= T ? T : (lr + 3) & ~3;
     float c[4][4], e[4][4];
     zero(c);
     zero(e);
-    gemm_abt(tK, tQ, c);     // S^T [key][row]
-    gemm_abt(tV, tdO, e);    // dP^T [key][row]
+    gemm_abt(tK, tQ, c, ni, nj);     // S^T [key][row]
+    gemm_abt(tV, tdO, e, ni, nj);    // dP^T [key][row]
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = cg + 16 * j;
@@ -510,8 +524,8 @@ __device__ __forceinline__ void kv_sweep(const BwParams& p, const uint8_t* Qsrc,
     put(tP, c);
     put(tdS, e);
     __syncthreads();
-    gemm_abt(tP, tdOt, accV);    // [key][d] += sum_row P^T dO
-    gemm_abt(tdS, tQt, accK);    // [key][d] += sum_row dS^T Q
+    gemm_abt(tP, tdOt, accV, ni, 4, kr);    // [key][d] += sum_row P^T dO
+    gemm_abt(tdS, tQt, accK, ni, 4, kr);    // [key][d] += sum_row dS^T Q
   }
 }
 
@@ -565,7 +579,7 @@ __device__ void dkv_window(const BwParams& p, int b, int h, int rho, int blk, fl
   float accK[4][4], accV[4][4];
   zero(accK);
   zero(accV);
-  kv_sweep<BF>(p, p.Q, hoff, nwin, win_rows, win_ok, sm, mt, accK, accV);
+  kv_sweep<BF>(p, p.Q, hoff, nwin, win_rows, win_ok, [](int) { return T; }, 4, sm, mt, accK, accV);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -601,7 +615,8 @@ __device__ void dkv_window(const BwParams& p, int b, int h, int rho, int blk, fl
   zero(accK);
   zero(accV);
   const int nq = (g + T - 1) / T;
-  kv_sweep<BF>(p, p.Qg, hoff, nq, glob_rows, glob_ok, sm, mt, accK, accV);
+  kv_sweep<BF>(p, p.Qg, hoff, nq, glob_rows, glob_ok, [&](int qt) { return g - T * qt; }, 4, sm, mt,
+               accK, accV);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -662,7 +677,8 @@ __device__ void dkv_global_keys(const BwParams& p, int b, int h, int gt, float* 
   float accK[4][4], accV[4][4];
   zero(accK);
   zero(accV);
-  kv_sweep<BF>(p, p.Q, hoff, (n + T - 1) / T, all_rows, ok, sm, mt, accK, accV);
+  kv_sweep<BF>(p, p.Q, hoff, (n + T - 1) / T, all_rows, ok, [](int) { return T; }, groups16(g - T * gt),
+               sm, mt, accK, accV);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -700,19 +716,20 @@ __device__ __forceinline__ void decode_block(const BwParams& p, int lb, int& b, 
 constexpr int DQ_SMEM = 6 * TILE * 4;
 constexpr int DKV_SMEM = 8 * TILE * 4;
 
+// Grid order: the global-row (or global-key) tiles first, each of which
+// walks the whole sequence, then the residue-class blocks.
 template <bool BF>
 __global__ __launch_bounds__(NTH) void dq_kernel(BwParams p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   __shared__ Meta mt;
-  const int nloc = p.B * p.blocks_per_b;
+  const int nglob = p.B * p.H * p.ntg;
   const int bid = blockIdx.x;
-  if (bid < nloc) {
+  if (bid >= nglob) {
     int b, h, rho, blk;
-    decode_block(p, bid, b, h, rho, blk);
+    decode_block(p, bid - nglob, b, h, rho, blk);
     dq_local<BF>(p, b, h, rho, blk, sm, mt);
   } else {
-    const int lg = bid - nloc;
-    const int gt = lg % p.ntg, bh = lg / p.ntg;
+    const int gt = bid % p.ntg, bh = bid / p.ntg;
     dq_global<BF>(p, bh / p.H, bh % p.H, gt, sm, mt);
   }
 }
@@ -721,15 +738,14 @@ template <bool BF>
 __global__ __launch_bounds__(NTH) void dkv_kernel(BwParams p) {
   extern __shared__ __attribute__((aligned(16))) float sm[];
   __shared__ Meta mt;
-  const int nloc = p.B * p.blocks_per_b;
+  const int nglob = p.B * p.H * p.ntg;
   const int bid = blockIdx.x;
-  if (bid < nloc) {
+  if (bid >= nglob) {
     int b, h, rho, blk;
-    decode_block(p, bid, b, h, rho, blk);
+    decode_block(p, bid - nglob, b, h, rho, blk);
     dkv_window<BF>(p, b, h, rho, blk, sm, mt);
   } else {
-    const int lg = bid - nloc;
-    const int gt = lg % p.ntg, bh = lg / p.ntg;
+    const int gt = bid % p.ntg, bh = bid / p.ntg;
     dkv_global_keys<BF>(p, bh / p.H, bh % p.H, gt, sm, mt);
   }
 }

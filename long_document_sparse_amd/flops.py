@@ -78,3 +78,29 @@ def hbm_bytes(lmask, gmask, H: int, d: int, elt: int) -> int:
         total += H * rows * d * elt
     total += 2 * 4 * v.size
     return total
+
+
+def backward_flops(lmask, gmask, window: int, dilation: Sequence[int], d: int) -> int:
+    """Algorithmic FLOPs of the backward: per allowed pair, the five d-long
+    products of the chain rule (the score q.k, dP = dO.v, and the dq, dk, dv
+    accumulations), 10*d FLOPs.  Recomputation the kernels do on top (the
+    scores and dP evaluated a second time for the key gradients, the
+    log-sum-exp pass) is not counted."""
+    return 10 * d * pairs(lmask, gmask, window, dilation)
+
+
+def backward_bytes(lmask, gmask, H: int, d: int, elt: int) -> int:
+    """Each row the backward must read once (Q at local rows, Qg at global rows,
+    K, V at valid rows, Kg, Vg at valid rows when there is a global token, O and
+    dO at valid rows) and the six gradients written at every row, plus the
+    masks."""
+    v, g = _flags(lmask, gmask)
+    n = v.shape[1]
+    total = 0
+    for b in range(v.shape[0]):
+        nv = int(v[b].sum())
+        ng = int(g[b].sum())
+        reads = (nv - ng) + ng + 2 * nv + (2 * nv if ng > 0 else 0) + 2 * nv
+        total += H * (reads + 6 * n) * d * elt
+    total += 2 * 4 * v.size
+    return total

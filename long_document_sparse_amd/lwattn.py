@@ -204,6 +204,23 @@ class Plan:
             raise LwattnError(st, "lwattn_backward")
         return grads
 
+    def bind_backward(self, q, k, v, qg, kg, vg, lmask, gmask, o, do, grads, stream=None):
+        """Like bind, for the backward: validates once, returns a no-argument
+        callable that enqueues lwattn_backward into `grads` again."""
+        self.backward(q, k, v, qg, kg, vg, lmask, gmask, o, do, grads=grads, stream=stream)
+        fn = self.lib.lwattn_backward
+        args = (self.handle,) + tuple(ctypes.c_void_p(t.data_ptr()) for t in
+                                      (q, k, v, qg, kg, vg, lmask, gmask, o, do, *grads)) + \
+            (_stream_handle(stream),)
+        keep = (q, k, v, qg, kg, vg, lmask, gmask, o, do, grads)
+
+        def run():
+            st = fn(*args)
+            if st != OK:
+                raise LwattnError(st, "lwattn_backward")
+            return keep[-1]
+        return run
+
     def bind(self, q, k, v, qg, kg, vg, lmask, gmask, out=None, stream=None):
         """Validate the buffers once and return a no-argument callable that
         enqueues the same forward again (same buffers, same stream), with the

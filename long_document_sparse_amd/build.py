@@ -8,7 +8,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "lwattn.hip")
-DEPS = [SRC, os.path.join(PKG, "csrc", "kernels.hpp"), os.path.join(ROOT, "include", "lwattn.h")]
+DEPS = [SRC, os.path.join(PKG, "csrc", "kernels.hpp"), os.path.join(PKG, "csrc", "backward.hpp"),
+        os.path.join(ROOT, "include", "lwattn.h")]
 LIB = os.path.join(PKG, "liblwattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -44,6 +44,9 @@ struct BwParams {
   const int32_t* head_stride;   // [H] dilation stride
   const int32_t* head_blk;      // [H+1] prefix over heads of 64-row blocks (all residue classes)
   float2* stats;                // [B,H,n] (log-sum-exp, D) of every non-padded row
+  float* gq;                    // [B,H,max_global,gsplit,68] per-chunk dQg sums, max, sum of exp
+  float* gk;                    // [B,H,max_global,gsplit,128] per-chunk dK, dV sums of global keys
+  int gsplit, gchunk;           // position chunks of the global rows' / keys' sums, chunk length
   int B, H, n, r, max_global, ntg, blocks_per_b;
   float scale;
 };
@@ -178,7 +181,7 @@ __device__ __forceinline__ void store_tile(uint8_t* head, const float* src, cons
 }
 
 // Shared per-tile bookkeeping in LDS.
-struct Meta {
+struct alignas(16) Meta {
   int rpos[T], kpos[T];
   uint8_t rkind[T], kkind[T], rkeep[T], kkeep[T];
   float lse[T], dd[T];
@@ -749,6 +752,731 @@ __global__ __launch_bounds__(NTH) void dkv_kernel(BwParams p) {
     dkv_global_keys<BF>(p, bh / p.H, bh % p.H, gt, sm, mt);
   }
 }
+
+// ---------------------------------------------------------------------------
+// bf16 storage: the residue-class blocks on the matrix cores.  Four waves per
+// workgroup; wave w owns a 32 x 32 quadrant of every 64-row x 64-key tile pair.
+// The products use v_mfma_f32_32x32x16_bf16 with the operand layouts of the
+// forward: A and B fragments hold X[row][32 h + 8 c .. +8] for lane row l % 32,
+// h = l / 32, over four k-chunks c; an accumulator register r of lane l is
+// element (8 (r / 4) + 4 h + r % 4, l % 32).  A product whose contraction runs
+// over the accumulator's rows (dQ^T = K^T dS^T, dK^T = Q^T dS, dV^T = dO^T P)
+// takes the scores straight from the registers as its B operand (rounded to
+// bf16, in the accumulator's row order) and the other side through the
+// transposing LDS read, whose addressing yields the same row order.
+//
+// Tiles are bf16 in LDS, 128-byte rows of eight 16-byte chunks; logical chunk
+// c of row R sits at physical chunk c ^ swz(R).  swz gives rows 0..7 distinct
+// values, so the eight rows of a b128 row read hit distinct banks, and it maps
+// rows e = 0..3 (and 4..7) to even offsets 2e (xor 1), so the four rows of a
+// transposing read take four distinct 32-byte chunk pairs.
+namespace mk {
+
+constexpr int TB = T * 128;   // bytes of one bf16 tile
+
+__device__ __forceinline__ int swz(int row) { return (2 * (row & 3)) ^ ((row >> 2) & 1); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)ptr);
+}
+
+// A synchronous tile load (global -> registers -> LDS), swizzled.
+__device__ __forceinline__ void load_tile_bf(uint8_t* dst, const uint8_t* head, const int* pos) {
+  const int t = threadIdx.x, row = t >> 2, q = t & 3;
+  const int ps = pos[row];
+  uint4 a = make_uint4(0, 0, 0, 0), c = a;
+  if (ps >= 0) {
+    const uint8_t* src = head + (int64_t)ps * 128 + q * 32;
+    a = *reinterpret_cast<const uint4*>(src);
+    c = *reinterpret_cast<const uint4*>(src + 16);
+  }
+  const int sw = swz(row);
+  *reinterpret_cast<uint4*>(dst + row * 128 + ((2 * q) ^ sw) * 16) = a;
+  *reinterpret_cast<uint4*>(dst + row * 128 + ((2 * q + 1) ^ sw) * 16) = c;
+}
+
+// This wave's 16 rows of a 64-row tile, straight from global memory into LDS
+// at `tile` (an LDS address): lane l fills chunk l % 8 of rows R0 = 16 w + l / 8
+// and R0 + 8, whose positions are p0 and p1 (negative: a zero row).  d covers
+// the head's n rows.
+__device__ __forceinline__ int dma_row0(int w, int lane) { return 16 * w + (lane >> 3); }
+
+__device__ __forceinline__ void dma_tile(const i32x4& d, uint32_t tile, int w, int lane, int p0, int p1) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(tile + w * 2048);
+  const int R0 = dma_row0(w, lane);
+  const int c16 = ((lane & 7) ^ swz(R0)) * 16;   // swz(R0 + 8) = swz(R0)
+  dma16i<0>(d, p0 >= 0 ? p0 * 128 + c16 : OOB_OFF, base);
+  dma16i<1024>(d, p1 >= 0 ? p1 * 128 + c16 : OOB_OFF, base);
+}
+
+// s_waitcnt vmcnt(0) through the builtin, which the compiler's own wait
+// placement sees: after it, no load of this wave is taken as outstanding (an
+// inline-asm wait would leave the compiler waiting again before the first use
+// of an older load, and so also for the tile loads issued after it).
+__device__ __forceinline__ void wait_all_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0, expcnt 7, lgkmcnt 15: loads only
+}
+
+// A or B fragment c of row `row` of a [row][d] tile
+__device__ __forceinline__ bf16x8 frag_row(const uint8_t* tile, int row, int h, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * 128 + (((4 * h + c) ^ swz(row)) * 16));
+}
+
+// The four fragments of one row in global memory (zeros for pos < 0).
+__device__ __forceinline__ void row_frags(bf16x8 (&f)[4], const uint8_t* head, int pos, int h) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (pos >= 0) v = *reinterpret_cast<const uint4*>(head + (int64_t)pos * 128 + (32 * h + 8 * c) * 2);
+    f[c] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// A fragment of X^T for d block db and k-chunk c2 (rows of the tile at
+// `tile`): lane l gets X[row(j)][32 db + l % 32] for rows 16 c2 + 4 h + j
+// (j < 4) and 16 c2 + 8 + 4 h + j - 4 (j >= 4).  Every row read by a lane has
+// row % 4 = e and (row / 4) % 2 = h, so one swizzle serves all of them.
+__device__ __forceinline__ bf16x8 frag_tr(const uint8_t* tile, int c2, int db, int lane) {
+  const int h = lane >> 5, g1 = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
+  const int chunk = (4 * db + 2 * g1 + (q >> 1)) ^ (2 * e) ^ h;
+  const uint8_t* a = tile + c2 * 2048 + (4 * h + e) * 128 + chunk * 16 + (q & 1) * 8;
+  const s16x4 lo = tr_read(a);
+  const s16x4 hi = tr_read(a + 1024);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// B fragment for k-chunk c2 taken from an accumulator (its rows 16 c2 ..).
+__device__ __forceinline__ bf16x8 acc_frag(const f32x16& x, int c2) {
+  bf16x8 f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (__bf16)x[8 * c2 + j];
+  return f;
+}
+
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Row pieces of a [.][64] gradient held as two d-block accumulators (element
+// (d, l % 32)) to global memory: lane writes d = 32 db + 8 a + 4 h .. +3.
+__device__ __forceinline__ void store_dT(uint8_t* rowptr, const f32x16 (&x)[2], float mul, int h) {
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (__bf16)(x[db][4 * a + e] * mul);
+      *reinterpret_cast<bf16x4*>(rowptr + (32 * db + 8 * a + 4 * h) * 2) = v;
+    }
+}
+
+// <dO, O> of a row whose dO fragments are at hand (both half-lanes get it).
+__device__ __forceinline__ float row_dot(const bf16x8 (&df)[4], const uint8_t* O, int pos, int h) {
+  bf16x8 of[4];
+  row_frags(of, O, pos, h);
+  float a = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaf((float)df[c][e], (float)of[c][e], a);
+  return half_sum(a);
+}
+
+// Tile metadata fetched one tile ahead: raw values in registers (threads
+// 0..63, one tile row or key each), turned into a Meta entry once they land.
+struct MetaRegs {
+  int pos;
+  float lv, gv;   // masks at pos (zero when pos < 0)
+  float2 st;      // (log-sum-exp, D) at pos, where wanted
+};
+
+// lm, gm: the batch row's masks; st: the head's statistics (or null).
+__device__ __forceinline__ void fetch_meta(MetaRegs& mr, const float* lm, const float* gm, const float2* st,
+                                           int pos, bool masks) {
+  mr.pos = pos;
+  mr.lv = 0.0f;
+  mr.gv = 0.0f;
+  mr.st = make_float2(0.0f, 0.0f);
+  if (pos >= 0) {
+    if (masks) {
+      mr.lv = lm[pos];
+      mr.gv = gm[pos];
+    }
+    if (st) mr.st = st[pos];
+  }
+}
+
+// Kind of the fetched position: from the masks, or 1 (global) without them.
+__device__ __forceinline__ uint8_t meta_kind(const MetaRegs& mr, bool masks) {
+  if (mr.pos < 0) return 0;
+  if (!masks) return 1;
+  if (mr.lv == 0.0f) return 0;
+  return mr.gv != 0.0f ? 1 : 2;
+}
+
+constexpr int DQ_SMEM = 4 * TB + 2 * 64 * 34 * 4;   // two K, V tile pairs; the key quadrants' merge
+constexpr int DKV_SMEM = 4 * TB + 2 * 64 * 64 * 4;  // two Q, dO tile pairs; the row quadrants' sums
+
+// dQ of the 64 rows I0 .. of residue class rho of (b, h), in one pass over the
+// key tiles (the window's, then the global keys') with a running softmax per
+// row: dQ = scale (sum_k e^(s_k - m) (dP_k - D) K_k) / (sum_k e^(s_k - m)),
+// m the running maximum.  Also writes zero dQ rows for the block's non-local
+// rows, zero dQg rows for its non-global rows, and (log-sum-exp, D) of its
+// local rows.
+__device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint8_t* sm, Meta (&mt)[2]) {
+  float* xch = reinterpret_cast<float*>(sm + 4 * TB);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, rq = w & 1, kq = w >> 1;
+  const int h32 = lane >> 5, qi = lane & 31;
+  const int n = p.n, s = p.head_stride[h], r = p.r;
+  const int nr = (n - rho + s - 1) / s;
+  const int I0 = blk * T;
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t hoff = bh * n * 128;
+  int g = p.gcnt[b];
+  if (g > p.max_global) g = p.max_global;
+  const int32_t* gidx = p.gidx + (int64_t)b * n;
+  const int nwin = (T + 2 * r + T - 1) / T;
+  const int ntot = nwin + (g + T - 1) / T;
+  auto key_pos = [&](int kt, int R) {
+    if (kt < nwin) {
+      const int jp = I0 - r + T * kt + R;
+      return jp >= 0 && jp < nr ? rho + jp * s : -1;
+    }
+    const int idx = T * (kt - nwin) + R;
+    return idx < g ? gidx[idx] : -1;
+  };
+  const i32x4 dK = make_desc(p.K + hoff, n * 128);
+  const i32x4 dV = make_desc(p.V + hoff, n * 128);
+  const uint32_t lds0 = lds_addr(sm);
+  const float* lm = p.lmask + (int64_t)b * n;
+  const float* gm = p.gmask + (int64_t)b * n;
+  MetaRegs mr;
+  auto prefetch = [&](int kt) {
+    // every position first (global tiles read them from the index), then
+    // the tiles, then the metadata
+    const int R0 = dma_row0(w, lane);
+    const int p0 = key_pos(kt, R0), p1 = key_pos(kt, R0 + 8);
+    const int pm = t < T ? key_pos(kt, t) : -1;
+    const uint32_t buf = lds0 + (kt & 1) * 2 * TB;
+    dma_tile(dK, buf, w, lane, p0, p1);
+    dma_tile(dV, buf + TB, w, lane, p0, p1);
+    if (t < T) fetch_meta(mr, lm, gm, nullptr, pm, kt < nwin);
+  };
+  if (ntot > 0) prefetch(0);
+
+  const int row = 32 * rq + qi;
+  const int rps = I0 + row < nr ? rho + (I0 + row) * s : -1;
+  const uint8_t rkd = kind_of(p, b, rps);
+  const bool rlocal = rkd == 2;
+  bf16x8 qf[4], df[4];
+  row_frags(qf, p.Q + hoff, rps, h32);
+  row_frags(df, p.dO + hoff, rps, h32);
+  const float dsum = row_dot(df, p.O + hoff, rps, h32);
+
+  float m = -INFINITY, l = 0.0f;
+  f32x16 acc[2] = {};
+  for (int kt = 0; kt < ntot; ++kt) {
+    const int cur = kt & 1;
+    wait_all_loads();
+    if (t < T) {
+      mt[cur].kpos[t] = mr.pos;
+      mt[cur].kkind[t] = meta_kind(mr, kt < nwin);
+    }
+    __syncthreads();
+    if (kt + 1 < ntot) prefetch(kt + 1);
+    const uint8_t* tK = sm + cur * 2 * TB;
+    const uint8_t* tV = tK + TB;
+    f32x16 x = {}, e = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      x = mfma_bf16(frag_row(tK, 32 * kq + qi, h32, c), qf[c], x);
+      e = mfma_bf16(frag_row(tV, 32 * kq + qi, h32, c), df[c], e);
+    }
+    // key acc_row(i) of the quadrant: allowed if of the tile's kind (local in
+    // the window, global after it) and, in the window, within r of the row
+    bool ok[16];
+    {
+      const bool win = kt < nwin;
+      const uint32_t want = win ? 2u : 1u;
+      const int base = T * kt - r - row + 32 * kq + 4 * h32 + r;   // key index minus row index, plus r
+      const uint32_t span = win ? (uint32_t)(2 * r) : 0xFFFFFFFFu;
+      const uint8_t* kk = mt[cur].kkind + 32 * kq + 4 * h32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kw = *reinterpret_cast<const uint32_t*>(kk + 8 * j);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          ok[4 * j + u] = rlocal && ((kw >> (8 * u)) & 0xFFu) == want &&
+                          (uint32_t)(base + 8 * j + u) <= span;
+      }
+    }
+    float mx = m;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (ok[i]) mx = fmaxf(mx, p.scale * x[i]);
+    mx = half_max(mx);   // one running max for both halves of the row
+    const float alpha = m == -INFINITY ? 0.0f : __expf(m - mx);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pr = ok[i] ? __expf(p.scale * x[i] - mx) : 0.0f;
+      l += pr;
+      x[i] = pr * (e[i] - dsum);
+    }
+    m = mx;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const bf16x8 bs = acc_frag(x, c2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) acc[db] = mfma_bf16(frag_tr(tK + 32 * kq * 128, c2, db, lane), bs, acc[db]);
+    }
+  }
+  l = half_sum(l);
+  // merge the two key quadrants
+  __syncthreads();
+  float* xr = xch + (rq * 64 + lane) * 34;
+  if (kq == 1) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xr[db * 16 + i] = acc[db][i];
+    xr[32] = m;
+    xr[33] = l;
+  }
+  __syncthreads();
+  if (kq == 0 && rps >= 0) {
+    const float m2 = xr[32], l2 = xr[33];
+    const float mm = fmaxf(m, m2);
+    const float a1 = m == -INFINITY ? 0.0f : __expf(m - mm);
+    const float a2 = m2 == -INFINITY ? 0.0f : __expf(m2 - mm);
+    const float L = l * a1 + l2 * a2;
+    const float mul = rlocal && L > 0.0f ? p.scale / L : 0.0f;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] = acc[db][i] * a1 + xr[db * 16 + i] * a2;
+    store_dT(p.dQ + hoff + (int64_t)rps * 128, acc, mul, h32);
+    if (rkd != 1) {
+      const f32x16 z[2] = {};
+      store_dT(p.dQg + hoff + (int64_t)rps * 128, z, 0.0f, h32);
+    }
+    if (rlocal && h32 == 0) p.stats[bh * n + rps] = make_float2(L > 0.0f ? mm + __logf(L) : INFINITY, dsum);
+  }
+}
+
+// dK^T, dV^T accumulators of one key quadrant (lane = key) over the rows of
+// a 64-row tile: S = Q K^T and dP = dO V^T with rows in the accumulator's
+// order; P = exp(scale S - lse(row)) where the pair is allowed (0 elsewhere),
+// dS = P (dP - D).  A pair is allowed when kok (the key's side holds), the
+// row's kind is `want`, and base + (row index in the tile) taken from it, as
+// an unsigned number, is at most span (the window's reach; all ones: no limit).
+__device__ __forceinline__ void kv_tile(f32x16 (&dk)[2], f32x16 (&dv)[2], const uint8_t* tQ,
+                                        const uint8_t* tdO, const bf16x8 (&kf)[4], const bf16x8 (&vf)[4],
+                                        const Meta& mt, float scale, int rq, int lane, bool kok,
+                                        uint32_t want, int base, uint32_t span) {
+  const int h32 = lane >> 5, qi = lane & 31;
+  f32x16 x = {}, e = {};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    x = mfma_bf16(frag_row(tQ, 32 * rq + qi, h32, c), kf[c], x);
+    e = mfma_bf16(frag_row(tdO, 32 * rq + qi, h32, c), vf[c], e);
+  }
+  f32x16 pp;
+  const int r0 = 32 * rq + 4 * h32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(mt.rkind + r0 + 8 * j);
+    const float4 ls = *reinterpret_cast<const float4*>(mt.lse + r0 + 8 * j);
+    const float4 dd = *reinterpret_cast<const float4*>(mt.dd + r0 + 8 * j);
+    const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, ddv[4] = {dd.x, dd.y, dd.z, dd.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * j + u;
+      const bool ok = kok && ((kw >> (8 * u)) & 0xFFu) == want && (uint32_t)(base - (r0 + 8 * j + u)) <= span;
+      const float pr = ok ? __expf(scale * x[i] - lsv[u]) : 0.0f;
+      pp[i] = pr;
+      x[i] = pr * (e[i] - ddv[u]);
+    }
+  }
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    const bf16x8 bs = acc_frag(x, c2), bp = acc_frag(pp, c2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      dk[db] = mfma_bf16(frag_tr(tQ + 32 * rq * 128, c2, db, lane), bs, dk[db]);
+      dv[db] = mfma_bf16(frag_tr(tdO + 32 * rq * 128, c2, db, lane), bp, dv[db]);
+    }
+  }
+}
+
+// Adds the row-quadrant-1 waves' dK^T, dV^T to the row-quadrant-0 waves'
+// (through LDS); returns true in the waves that then hold the sums.
+__device__ __forceinline__ bool sum_row_quadrants(f32x16 (&dk)[2], f32x16 (&dv)[2], float* xch, int rq,
+                                                  int kq, int lane) {
+  __syncthreads();
+  float* x = xch + (kq * 64 + lane) * 64;
+  if (rq == 1) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        x[db * 16 + i] = dk[db][i];
+        x[32 + db * 16 + i] = dv[db][i];
+      }
+  }
+  __syncthreads();
+  if (rq != 0) return false;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[db][i] += x[db * 16 + i];
+      dv[db][i] += x[32 + db * 16 + i];
+    }
+  return true;
+}
+
+// dK, dV (window part) and dKg, dVg of the 64 keys J0 .. of residue class rho
+// of (b, h), in one pass over the row tiles: the window's (with Q and the
+// local rows' statistics), then the global rows' (with Qg and theirs).  The
+// statistics must be in place.
+__device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uint8_t* sm, Meta (&mt)[2]) {
+  float* xch = reinterpret_cast<float*>(sm + 4 * TB);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, kq = w & 1, rq = w >> 1;
+  const int h32 = lane >> 5, qi = lane & 31;
+  const int n = p.n, s = p.head_stride[h], r = p.r;
+  const int nr = (n - rho + s - 1) / s;
+  const int J0 = blk * T;
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t hoff = bh * n * 128;
+  int g = p.gcnt[b];
+  if (g > p.max_global) g = p.max_global;
+  const int32_t* gidx = p.gidx + (int64_t)b * n;
+  const int nwin = (T + 2 * r + T - 1) / T;
+  const int ntot = nwin + (g + T - 1) / T;
+  auto row_pos = [&](int qt, int R) {
+    if (qt < nwin) {
+      const int ip = J0 - r + T * qt + R;
+      return ip >= 0 && ip < nr ? rho + ip * s : -1;
+    }
+    const int idx = T * (qt - nwin) + R;
+    return idx < g ? gidx[idx] : -1;
+  };
+  const i32x4 dQd = make_desc(p.Q + hoff, n * 128);
+  const i32x4 dQgd = make_desc(p.Qg + hoff, n * 128);
+  const i32x4 dOd = make_desc(p.dO + hoff, n * 128);
+  const uint32_t lds0 = lds_addr(sm);
+  const float* lm = p.lmask + (int64_t)b * n;
+  const float* gm = p.gmask + (int64_t)b * n;
+  const float2* st = p.stats + bh * n;
+  MetaRegs mr;
+  auto prefetch = [&](int qt) {
+    const int R0 = dma_row0(w, lane);
+    const int p0 = row_pos(qt, R0), p1 = row_pos(qt, R0 + 8);
+    const int pm = t < T ? row_pos(qt, t) : -1;
+    const uint32_t buf = lds0 + (qt & 1) * 2 * TB;
+    dma_tile(qt < nwin ? dQd : dQgd, buf, w, lane, p0, p1);
+    dma_tile(dOd, buf + TB, w, lane, p0, p1);
+    if (t < T) fetch_meta(mr, lm, gm, st, pm, qt < nwin);
+  };
+  if (ntot > 0) prefetch(0);
+
+  const int key = 32 * kq + qi;
+  const int kps = J0 + key < nr ? rho + (J0 + key) * s : -1;
+  const uint8_t kkd = kind_of(p, b, kps);
+  bf16x8 kf[4], vf[4];
+  row_frags(kf, p.K + hoff, kps, h32);
+  row_frags(vf, p.V + hoff, kps, h32);
+  f32x16 dk[2] = {}, dv[2] = {};
+  auto finish_window = [&]() {
+    // global keys' dK, dV come from the chunk sums
+    if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0 && kkd != 1) {
+      store_dT(p.dK + hoff + (int64_t)kps * 128, dk, p.scale, h32);
+      store_dT(p.dV + hoff + (int64_t)kps * 128, dv, 1.0f, h32);
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      dk[db] = f32x16{};
+      dv[db] = f32x16{};
+    }
+    row_frags(kf, p.Kg + hoff, kps, h32);
+    row_frags(vf, p.Vg + hoff, kps, h32);
+  };
+  auto step = [&](int qt) {
+    const int cur = qt & 1;
+    wait_all_loads();
+    if (t < T) {
+      const uint8_t kd = meta_kind(mr, qt < nwin);
+      const bool keep = qt < nwin ? kd == 2 : kd == 1;
+      mt[cur].rkind[t] = kd;
+      mt[cur].lse[t] = keep ? mr.st.x : 0.0f;
+      mt[cur].dd[t] = keep ? mr.st.y : 0.0f;
+    }
+    __syncthreads();
+    if (qt + 1 < ntot) prefetch(qt + 1);
+    const uint8_t* tQ = sm + cur * 2 * TB;
+    const uint8_t* tdO = tQ + TB;
+    // window: key index minus row index (subsequence) within [-r, r]
+    const bool win = qt < nwin;
+    kv_tile(dk, dv, tQ, tdO, kf, vf, mt[cur], p.scale, rq, lane, win ? kkd == 2 : kkd != 0, win ? 2u : 1u,
+            2 * r + key - T * qt, win ? (uint32_t)(2 * r) : 0xFFFFFFFFu);
+  };
+  // the window's row tiles; then the global rows' tiles (Kg, Vg fragments)
+  for (int qt = 0; qt < nwin; ++qt) step(qt);
+  finish_window();
+  for (int qt = nwin; qt < ntot; ++qt) step(qt);
+  if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0) {
+    store_dT(p.dKg + hoff + (int64_t)kps * 128, dk, p.scale, h32);
+    store_dT(p.dVg + hoff + (int64_t)kps * 128, dv, 1.0f, h32);
+  }
+}
+
+// Sums over one chunk of positions P0 .. P1-1 for global tile gt of (b, h):
+// (1) the global rows' dQg^T = Kg^T dS^T with a chunk-local running max (an
+// online softmax over the chunk's real keys), with the max and the sum of
+// exponentials, and (2) the global keys' dK^T = Q^T dS, dV^T = dO^T P over the
+// chunk's local rows (their statistics must be in place).
+constexpr int GS_SMEM = 2 * TB + 2 * 64 * 64 * 4;
+
+__device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, uint8_t* sm, Meta& mt) {
+  uint8_t* tA = sm;
+  uint8_t* tB = sm + TB;
+  float* xch = reinterpret_cast<float*>(sm + 2 * TB);
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int h32 = lane >> 5, qi = lane & 31;
+  const int n = p.n;
+  const int64_t bh = (int64_t)b * p.H + h;
+  const int64_t hoff = bh * n * 128;
+  const int64_t soff = bh * n;
+  int g = p.gcnt[b];
+  if (g > p.max_global) g = p.max_global;
+  if (T * gt >= g) return;
+  const int P0 = sp * p.gchunk;
+  const int P1 = P0 + p.gchunk < n ? P0 + p.gchunk : n;
+  if (t < T) {
+    const int idx = T * gt + t;
+    mt.rpos[t] = idx < g ? p.gidx[(int64_t)b * n + idx] : -1;
+  }
+  __syncthreads();
+  {
+    // (1) wave w: global rows 32 (w & 1) + lane % 32 (lane = row), keys 32 (w >> 1) ..
+    const int rq = w & 1, kq = w >> 1;
+    const int row = 32 * rq + qi;
+    const int gps = mt.rpos[row];
+    bf16x8 qf[4], df[4];
+    row_frags(qf, p.Qg + hoff, gps, h32);
+    row_frags(df, p.dO + hoff, gps, h32);
+    float dsum;
+    {
+      bf16x8 of[4];
+      row_frags(of, p.O + hoff, gps, h32);
+      float a = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf((float)df[c][e], (float)of[c][e], a);
+      dsum = half_sum(a);
+    }
+    float m = -INFINITY, l = 0.0f;
+    f32x16 acc[2] = {};
+    for (int P = P0; P < P1; P += T) {
+      __syncthreads();
+      if (t < T) {
+        const int ps = P + t < P1 ? P + t : -1;
+        mt.kpos[t] = ps;
+        mt.kkind[t] = kind_of(p, b, ps);
+      }
+      __syncthreads();
+      load_tile_bf(tA, p.Kg + hoff, mt.kpos);
+      load_tile_bf(tB, p.Vg + hoff, mt.kpos);
+      __syncthreads();
+      f32x16 x = {}, e = {};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        x = mfma_bf16(frag_row(tA, 32 * kq + qi, h32, c), qf[c], x);
+        e = mfma_bf16(frag_row(tB, 32 * kq + qi, h32, c), df[c], e);
+      }
+      float mx = m;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (gps >= 0 && mt.kkind[32 * kq + acc_row(i, h32)] != 0) mx = fmaxf(mx, p.scale * x[i]);
+      mx = half_max(mx);   // one running max for both halves of the row
+      const float alpha = m == -INFINITY ? 0.0f : __expf(m - mx);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool ok = gps >= 0 && mt.kkind[32 * kq + acc_row(i, h32)] != 0;
+        const float pr = ok ? __expf(p.scale * x[i] - mx) : 0.0f;
+        l += pr;
+        x[i] = pr * (e[i] - dsum);
+      }
+      m = mx;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const bf16x8 bs = acc_frag(x, c2);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) acc[db] = mfma_bf16(frag_tr(tA + 32 * kq * 128, c2, db, lane), bs, acc[db]);
+      }
+    }
+    l = half_sum(l);
+    // merge the two key quadrants
+    __syncthreads();
+    float* x = xch + (rq * 64 + lane) * 34;
+    if (kq == 1) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[db * 16 + i] = acc[db][i];
+      x[32] = m;
+      x[33] = l;
+    }
+    __syncthreads();
+    if (kq == 0 && gps >= 0) {
+      const float m2 = x[32], l2 = x[33];
+      const float mm = fmaxf(m, m2);
+      const float a1 = m == -INFINITY ? 0.0f : __expf(m - mm);
+      const float a2 = m2 == -INFINITY ? 0.0f : __expf(m2 - mm);
+      float* dst = p.gq + ((bh * p.max_global + T * gt + row) * p.gsplit + sp) * 68;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float4 v;
+          v.x = acc[db][4 * a + 0] * a1 + x[db * 16 + 4 * a + 0] * a2;
+          v.y = acc[db][4 * a + 1] * a1 + x[db * 16 + 4 * a + 1] * a2;
+          v.z = acc[db][4 * a + 2] * a1 + x[db * 16 + 4 * a + 2] * a2;
+          v.w = acc[db][4 * a + 3] * a1 + x[db * 16 + 4 * a + 3] * a2;
+          *reinterpret_cast<float4*>(dst + 32 * db + 8 * a + 4 * h32) = v;
+        }
+      if (h32 == 0) {
+        dst[64] = mm;
+        dst[65] = l * a1 + l2 * a2;
+      }
+    }
+  }
+  // (2) wave w: global keys 32 (w & 1) + lane % 32 (lane = key), rows 32 (w >> 1) ..
+  __syncthreads();
+  {
+    const int kq = w & 1, rq = w >> 1;
+    const int key = 32 * kq + qi;
+    const int kps = mt.rpos[key];   // the tile's global positions, now as keys
+    bf16x8 kf[4], vf[4];
+    row_frags(kf, p.K + hoff, kps, h32);
+    row_frags(vf, p.V + hoff, kps, h32);
+    f32x16 dk[2] = {}, dv[2] = {};
+    __syncthreads();   // every wave has read rpos
+    for (int P = P0; P < P1; P += T) {
+      __syncthreads();
+      if (t < T) {
+        const int ps = P + t < P1 ? P + t : -1;
+        const uint8_t kd = kind_of(p, b, ps);
+        mt.rkind[t] = kd;
+        mt.kpos[t] = ps;
+        float2 st = make_float2(0.0f, 0.0f);
+        if (kd == 2) st = p.stats[soff + ps];
+        mt.lse[t] = st.x;
+        mt.dd[t] = st.y;
+      }
+      __syncthreads();
+      load_tile_bf(tA, p.Q + hoff, mt.kpos);
+      load_tile_bf(tB, p.dO + hoff, mt.kpos);
+      __syncthreads();
+      kv_tile(dk, dv, tA, tB, kf, vf, mt, p.scale, rq, lane, kps >= 0, 2u, 0, 0xFFFFFFFFu);
+    }
+    if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0) {
+      float* dst = p.gk + ((bh * p.max_global + T * gt + key) * p.gsplit + sp) * 128;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int d = 32 * db + 8 * a + 4 * h32;
+          *reinterpret_cast<float4*>(dst + d) =
+              make_float4(dk[db][4 * a], dk[db][4 * a + 1], dk[db][4 * a + 2], dk[db][4 * a + 3]);
+          *reinterpret_cast<float4*>(dst + 64 + d) =
+              make_float4(dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]);
+        }
+    }
+  }
+}
+
+__global__ __launch_bounds__(NTH) void dq_kernel(BwParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
+  __shared__ Meta mt[2];
+  int b, h, rho, blk;
+  decode_block(p, blockIdx.x, b, h, rho, blk);
+  dq_local(p, b, h, rho, blk, sm, mt);
+}
+
+__global__ __launch_bounds__(NTH) void dkv_kernel(BwParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
+  __shared__ Meta mt[2];
+  int b, h, rho, blk;
+  decode_block(p, blockIdx.x, b, h, rho, blk);
+  dkv_local(p, b, h, rho, blk, sm, mt);
+}
+
+__global__ __launch_bounds__(NTH) void global_chunk_kernel(BwParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
+  __shared__ Meta mt;
+  const int sp = blockIdx.x % p.gsplit, rest = blockIdx.x / p.gsplit;
+  const int gt = rest % p.ntg, bh = rest / p.ntg;
+  global_chunk(p, bh / p.H, bh % p.H, gt, sp, sm, mt);
+}
+
+// One wave per (b, h, global index): combines the chunk sums into dQg (and
+// the row's log-sum-exp and D) and the global key's dK, dV.  Lane = d.
+__global__ __launch_bounds__(NTH) void global_merge_kernel(BwParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * (NTH / 64) + (threadIdx.x >> 6);
+  if (item >= (int64_t)p.B * p.H * p.max_global) return;
+  const int gi = (int)(item % p.max_global);
+  const int64_t bh = item / p.max_global;
+  const int b = (int)(bh / p.H);
+  int g = p.gcnt[b];
+  if (g > p.max_global) g = p.max_global;
+  if (gi >= g) return;
+  const int n = p.n;
+  const int pos = p.gidx[(int64_t)b * n + gi];
+  const float* q = p.gq + item * p.gsplit * 68;
+  // lane-parallel maximum over the chunks, then independent loads per chunk
+  float mm = -INFINITY;
+  for (int sp = lane; sp < p.gsplit; sp += 64) mm = fmaxf(mm, q[sp * 68 + 64]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o));
+  float L = 0.0f, a = 0.0f;
+#pragma unroll 8
+  for (int sp = 0; sp < p.gsplit; ++sp) {
+    const float m = q[sp * 68 + 64];
+    const float f = m == -INFINITY ? 0.0f : __expf(m - mm);
+    L = fmaf(q[sp * 68 + 65], f, L);
+    a = fmaf(q[sp * 68 + lane], f, a);
+  }
+  const float* k = p.gk + item * p.gsplit * 128;
+  float sk = 0.0f, sv = 0.0f;
+#pragma unroll 8
+  for (int sp = 0; sp < p.gsplit; ++sp) {
+    sk += k[sp * 128 + lane];
+    sv += k[sp * 128 + 64 + lane];
+  }
+  const int64_t ro = (bh * n + pos) * 128 + lane * 2;
+  const float dov = (float)*reinterpret_cast<const __bf16*>(p.dO + ro);
+  float dd = dov * (float)*reinterpret_cast<const __bf16*>(p.O + ro);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dd += __shfl_xor(dd, o);
+  *reinterpret_cast<__bf16*>(p.dQg + ro) = (__bf16)(L > 0.0f ? p.scale * a / L : 0.0f);
+  *reinterpret_cast<__bf16*>(p.dK + ro) = (__bf16)(p.scale * sk);
+  *reinterpret_cast<__bf16*>(p.dV + ro) = (__bf16)sv;
+  if (lane == 0) p.stats[bh * n + pos] = make_float2(L > 0.0f ? mm + __logf(L) : INFINITY, dd);
+}
+
+}  // namespace mk
 
 // The forward's compaction workgroup, on its own.
 __global__ __launch_bounds__(NT) void compact_kernel(Params p) {

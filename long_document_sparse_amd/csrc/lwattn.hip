@@ -65,6 +65,10 @@ struct lwattn_plan_s {
   int32_t* head_blk64 = nullptr;
   int blocks64_per_b = 0;
   float2* stats = nullptr;
+  // bf16 backward: the global rows' and global keys' sums over position chunks
+  int gsplit = 0, gchunk = 0;
+  float* gq = nullptr;
+  float* gk = nullptr;
   // timing
   int timing_cap = 0;
   int timing_calls = 0;
@@ -88,6 +92,8 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->head_blk);
   (void)hipFree(p->head_blk64);
   (void)hipFree(p->stats);
+  (void)hipFree(p->gq);
+  (void)hipFree(p->gk);
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
   delete p;
 }
@@ -238,6 +244,20 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->head_blk, (size_t)(H + 1) * 4);
   alloc((void**)&p->head_blk64, (size_t)(H + 1) * 4);
   alloc((void**)&p->stats, (size_t)B * H * n * sizeof(float2));
+  if (cfg->dtype == LWATTN_BF16 && cfg->max_global > 0 && n > 0) {
+    // the positions of a head are cut into chunks of whole 64-row tiles, at
+    // least four tiles each, as many as bring the workgroups of the chunk sums
+    // (one per batch row, head, 64 global rows and chunk) to about 1024
+    const int64_t ntile = ((int64_t)n + lwk::bw::T - 1) / lwk::bw::T;
+    const int64_t units = (int64_t)B * H * ceil_div(cfg->max_global, lwk::bw::T);
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>((ntile + 3) / 4, (1024 + units - 1) / units));
+    const int64_t tiles = (ntile + want - 1) / want;
+    p->gchunk = (int)(tiles * lwk::bw::T);
+    p->gsplit = (int)((ntile + tiles - 1) / tiles);
+    const size_t rows = (size_t)B * H * cfg->max_global * p->gsplit;
+    alloc((void**)&p->gq, rows * 68 * 4);
+    alloc((void**)&p->gk, rows * 128 * 4);
+  }
   if (!ok) {
     free_plan(p);
     return LWATTN_E_NOMEM;
@@ -416,6 +436,10 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   bp.head_stride = p->head_stride;
   bp.head_blk = p->head_blk64;
   bp.stats = p->stats;
+  bp.gq = p->gq;
+  bp.gk = p->gk;
+  bp.gsplit = p->gsplit;
+  bp.gchunk = p->gchunk;
   bp.B = c.B;
   bp.H = c.H;
   bp.n = c.n;
@@ -426,13 +450,27 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   bp.scale = c.scale;
   const int64_t grid = (int64_t)c.B * p->blocks64_per_b + (int64_t)c.B * c.H * bp.ntg;
   if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
-  // 2. dQ, dQg and the rows' statistics; 3. dK, dV, dKg, dVg
   if (c.dtype == LWATTN_BF16) {
-    (void)hipFuncSetAttribute((const void*)lwk::bw::dq_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DQ_SMEM);
-    (void)hipFuncSetAttribute((const void*)lwk::bw::dkv_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DKV_SMEM);
-    hipLaunchKernelGGL(lwk::bw::dq_kernel<true>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DQ_SMEM, stream, bp);
-    hipLaunchKernelGGL(lwk::bw::dkv_kernel<true>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DKV_SMEM, stream, bp);
+    // 2. dQ, dQg (zero) and the local rows' statistics; 3. the chunk sums of
+    // the global rows and keys; 4. their merge: dQg, the global rows'
+    // statistics, the global keys' dK, dV; 5. dK, dV (window), dKg, dVg
+    namespace mk = lwk::bw::mk;
+    const int64_t nblk = (int64_t)c.B * p->blocks64_per_b;
+    const int64_t nchunk = (int64_t)c.B * c.H * bp.ntg * p->gsplit;
+    const int64_t nmerge = ((int64_t)c.B * c.H * c.max_global + 3) / 4;
+    // tiles are read through 32-bit buffer offsets over a head's n rows
+    if (nchunk > INT32_MAX || nmerge > INT32_MAX || (int64_t)c.n * 128 >= lwk::OOB_OFF)
+      return LWATTN_E_UNSUPPORTED;
+    (void)hipFuncSetAttribute((const void*)mk::dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DQ_SMEM);
+    (void)hipFuncSetAttribute((const void*)mk::dkv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DKV_SMEM);
+    hipLaunchKernelGGL(mk::dq_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DQ_SMEM, stream, bp);
+    if (nchunk > 0) {
+      hipLaunchKernelGGL(mk::global_chunk_kernel, dim3((uint32_t)nchunk), dim3(lwk::bw::NTH), mk::GS_SMEM, stream, bp);
+      hipLaunchKernelGGL(mk::global_merge_kernel, dim3((uint32_t)nmerge), dim3(lwk::bw::NTH), 0, stream, bp);
+    }
+    hipLaunchKernelGGL(mk::dkv_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DKV_SMEM, stream, bp);
   } else {
+    // 2. dQ, dQg and the rows' statistics; 3. dK, dV, dKg, dVg
     (void)hipFuncSetAttribute((const void*)lwk::bw::dq_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DQ_SMEM);
     (void)hipFuncSetAttribute((const void*)lwk::bw::dkv_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DKV_SMEM);
     hipLaunchKernelGGL(lwk::bw::dq_kernel<false>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DQ_SMEM, stream, bp);

@@ -43,7 +43,8 @@ struct BwParams {
   const int32_t* gcnt;          // [B]
   const int32_t* head_stride;   // [H] dilation stride
   const int32_t* head_blk;      // [H+1] prefix over heads of 64-row blocks (all residue classes)
-  float2* stats;                // [B,H,n] (log-sum-exp, D) of every non-padded row
+  float2* stats;                // [B,H,n] (log-sum-exp, D) of every non-padded row; the bf16
+                                // kernels keep the log-sum-exp in log2 units
   float* gq;                    // [B,H,max_global,gsplit,68] per-chunk dQg sums, max, sum of exp
   float* gk;                    // [B,H,max_global,gsplit,128] per-chunk dK, dV sums of global keys
   int gsplit, gchunk;           // position chunks of the global rows' / keys' sums, chunk length
@@ -185,6 +186,7 @@ struct alignas(16) Meta {
   int rpos[T], kpos[T];
   uint8_t rkind[T], kkind[T], rkeep[T], kkeep[T];
   float lse[T], dd[T];
+  uint32_t okm[2];   // matrix-core kernels: bit k of word q: tile row / key 32 q + k counts
 };
 
 // Every key tile a block of 64 query rows visits: window tiles (kt < nwin),
@@ -766,33 +768,21 @@ __global__ __launch_bounds__(NTH) void dkv_kernel(BwParams p) {
 // transposing LDS read, whose addressing yields the same row order.
 //
 // Tiles are bf16 in LDS, 128-byte rows of eight 16-byte chunks; logical chunk
-// c of row R sits at physical chunk c ^ swz(R).  swz gives rows 0..7 distinct
-// values, so the eight rows of a b128 row read hit distinct banks, and it maps
-// rows e = 0..3 (and 4..7) to even offsets 2e (xor 1), so the four rows of a
-// transposing read take four distinct 32-byte chunk pairs.
+// c of row R sits at physical chunk c ^ swz(R), swz(R) = 2 (R % 4) ^ bit 2 of R
+// ^ 2 bit 3 of R.  Row reads (16 bytes a lane, rows R0 .. R0+15 at one
+// logical chunk): swz differs across any 8 aligned consecutive rows and across
+// the 8 rows of one parity among 16, so a 128- or a 256-byte bank cycle holds
+// distinct chunks.  Transposing reads (8 bytes a lane, rows 4h .. 4h+3 at four
+// chunks): swz / 2 takes four distinct values on those rows, and bit 2 of swz
+// differs between rows of equal parity, so both bank widths stay free too.
 namespace mk {
 
 constexpr int TB = T * 128;   // bytes of one bf16 tile
 
-__device__ __forceinline__ int swz(int row) { return (2 * (row & 3)) ^ ((row >> 2) & 1); }
+__device__ __forceinline__ int swz(int row) { return (2 * (row & 3)) ^ ((row >> 2) & 1) ^ (((row >> 3) & 1) << 1); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)ptr);
-}
-
-// A synchronous tile load (global -> registers -> LDS), swizzled.
-__device__ __forceinline__ void load_tile_bf(uint8_t* dst, const uint8_t* head, const int* pos) {
-  const int t = threadIdx.x, row = t >> 2, q = t & 3;
-  const int ps = pos[row];
-  uint4 a = make_uint4(0, 0, 0, 0), c = a;
-  if (ps >= 0) {
-    const uint8_t* src = head + (int64_t)ps * 128 + q * 32;
-    a = *reinterpret_cast<const uint4*>(src);
-    c = *reinterpret_cast<const uint4*>(src + 16);
-  }
-  const int sw = swz(row);
-  *reinterpret_cast<uint4*>(dst + row * 128 + ((2 * q) ^ sw) * 16) = a;
-  *reinterpret_cast<uint4*>(dst + row * 128 + ((2 * q + 1) ^ sw) * 16) = c;
 }
 
 // This wave's 16 rows of a 64-row tile, straight from global memory into LDS
@@ -804,9 +794,9 @@ __device__ __forceinline__ int dma_row0(int w, int lane) { return 16 * w + (lane
 __device__ __forceinline__ void dma_tile(const i32x4& d, uint32_t tile, int w, int lane, int p0, int p1) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(tile + w * 2048);
   const int R0 = dma_row0(w, lane);
-  const int c16 = ((lane & 7) ^ swz(R0)) * 16;   // swz(R0 + 8) = swz(R0)
+  const int c16 = ((lane & 7) ^ swz(R0)) * 16;   // swz(R0 + 8) = swz(R0) ^ 2
   dma16i<0>(d, p0 >= 0 ? p0 * 128 + c16 : OOB_OFF, base);
-  dma16i<1024>(d, p1 >= 0 ? p1 * 128 + c16 : OOB_OFF, base);
+  dma16i<1024>(d, p1 >= 0 ? p1 * 128 + (c16 ^ 32) : OOB_OFF, base);
 }
 
 // s_waitcnt vmcnt(0) through the builtin, which the compiler's own wait
@@ -835,13 +825,14 @@ __device__ __forceinline__ void row_frags(bf16x8 (&f)[4], const uint8_t* head, i
 // A fragment of X^T for d block db and k-chunk c2 (rows of the tile at
 // `tile`): lane l gets X[row(j)][32 db + l % 32] for rows 16 c2 + 4 h + j
 // (j < 4) and 16 c2 + 8 + 4 h + j - 4 (j >= 4).  Every row read by a lane has
-// row % 4 = e and (row / 4) % 2 = h, so one swizzle serves all of them.
+// row % 4 = e and (row / 4) % 2 = h; bit 3 of the row tells the two reads
+// apart (their swizzles differ by 2).
 __device__ __forceinline__ bf16x8 frag_tr(const uint8_t* tile, int c2, int db, int lane) {
   const int h = lane >> 5, g1 = (lane >> 4) & 1, e = (lane >> 2) & 3, q = lane & 3;
   const int chunk = (4 * db + 2 * g1 + (q >> 1)) ^ (2 * e) ^ h;
-  const uint8_t* a = tile + c2 * 2048 + (4 * h + e) * 128 + chunk * 16 + (q & 1) * 8;
-  const s16x4 lo = tr_read(a);
-  const s16x4 hi = tr_read(a + 1024);
+  const uint8_t* a = tile + c2 * 2048 + (4 * h + e) * 128 + (q & 1) * 8;
+  const s16x4 lo = tr_read(a + chunk * 16);
+  const s16x4 hi = tr_read(a + 1024 + (chunk ^ 2) * 16);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -913,8 +904,114 @@ __device__ __forceinline__ uint8_t meta_kind(const MetaRegs& mr, bool masks) {
   return mr.gv != 0.0f ? 1 : 2;
 }
 
-constexpr int DQ_SMEM = 4 * TB + 2 * 64 * 34 * 4;   // two K, V tile pairs; the key quadrants' merge
+constexpr int DQ_SMEM = 4 * TB + 2 * 64 * 34 * 4;   // two K, V tile pairs; the key quadrants' merge (34 floats a row)
 constexpr int DKV_SMEM = 4 * TB + 2 * 64 * 64 * 4;  // two Q, dO tile pairs; the row quadrants' sums
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// Wave 0 (threads 0..63, one tile row or key each) publishes which entries of
+// the tile count: bit t of the 64-bit word.
+__device__ __forceinline__ void publish_bits(Meta& mt, bool counts) {
+  const uint64_t bits = __ballot(counts);
+  if (threadIdx.x == 0) {
+    mt.okm[0] = (uint32_t)bits;
+    mt.okm[1] = (uint32_t)(bits >> 32);
+  }
+}
+
+// True when every (row, key) pair of window tile kt (64 rows against keys
+// 64 kt - r .. of the same subsequence) lies within r: the pairs' key index
+// minus row index, plus r, spans 64 kt - 63 .. 64 kt + 63, inside [0, 2r].
+__device__ __forceinline__ bool interior_tile(int kt, int r) { return kt >= 1 && T * kt + 63 <= 2 * r; }
+
+// One key tile of a running-softmax dQ^T sum.  Lane = row, with the row's
+// fragments qf, df (B operands) and D = <dO, O>; the wave takes keys 32 kq ..
+// of the tile: S^T = K Q^T, dP^T = V dO^T.  Bit k of M: key 32 kq + k counts
+// for the lane's row (ignored when `full`, wave-uniform: every key counts).
+// Exponents are in log2 units, c = scale log2(e); the running offset m (the
+// same in both halves of the row) moves only when a score passes it by more
+// than TAU, so the terms stay below 2^TAU; l is this lane's share of the sum.
+__device__ __forceinline__ void dq_tile(f32x16 (&acc)[2], float& m, float& l, const uint8_t* tK,
+                                        const uint8_t* tV, const bf16x8 (&qf)[4], const bf16x8 (&df)[4],
+                                        float dsum, uint32_t M, bool full, float c, int kq, int lane) {
+  const int h32 = lane >> 5, qi = lane & 31;
+  f32x16 x = {}, e = {};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x = mfma_bf16(frag_row(tK, 32 * kq + qi, h32, k), qf[k], x);
+    e = mfma_bf16(frag_row(tV, 32 * kq + qi, h32, k), df[k], e);
+  }
+  if (!full) mask_half(x, M, h32);
+  float mr = x[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mr = fmaxf(mr, x[i]);
+  const float mx = half_max(mr) * c;
+  if (__any(mx > m + TAU)) {
+    const float mn = mx > m + TAU ? mx : m;
+    const float alpha = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    m = mn;
+  }
+  const float mu = m == -INFINITY ? 0.0f : m;   // no counted key yet: every term is exp2(-inf) = 0
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float pr = __builtin_amdgcn_exp2f(fmaf(x[i], c, -mu));
+    l += pr;
+    x[i] = pr * (e[i] - dsum);
+  }
+#pragma unroll
+  for (int c2 = 0; c2 < 2; ++c2) {
+    const bf16x8 bs = acc_frag(x, c2);
+#pragma unroll
+    for (int db = 0; db < 2; ++db) acc[db] = mfma_bf16(frag_tr(tK + 32 * kq * 128, c2, db, lane), bs, acc[db]);
+  }
+}
+
+// Merges the two key quadrants' running sums of each row (offsets m in log2
+// units): the kq = 1 waves hand theirs over through LDS.  Returns true in the
+// kq = 0 waves, whose acc, m and l then hold the row's (l summed over both
+// halves of the row).
+__device__ __forceinline__ bool merge_key_quadrants(f32x16 (&acc)[2], float& m, float& l, float* xch, int rq,
+                                                    int kq, int lane) {
+  l = half_sum(l);
+  __syncthreads();
+  // [rq][8 float4 of acc][lane], then [rq][lane] (m, l): consecutive lanes at
+  // consecutive addresses
+  float4* xa = reinterpret_cast<float4*>(xch) + rq * 8 * 64 + lane;
+  float2* xm = reinterpret_cast<float2*>(xch + 2 * 8 * 64 * 4) + rq * 64 + lane;
+  if (kq == 1) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        xa[(4 * db + a) * 64] = make_float4(acc[db][4 * a], acc[db][4 * a + 1], acc[db][4 * a + 2], acc[db][4 * a + 3]);
+    *xm = make_float2(m, l);
+  }
+  __syncthreads();
+  if (kq != 0) return false;
+  const float2 ml = *xm;
+  const float m2 = ml.x, l2 = ml.y;
+  const float mm = fmaxf(m, m2);
+  const float a1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mm);
+  const float a2 = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m2 - mm);
+  l = l * a1 + l2 * a2;
+  m = mm;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float4 v = xa[(4 * db + a) * 64];
+      acc[db][4 * a] = acc[db][4 * a] * a1 + v.x * a2;
+      acc[db][4 * a + 1] = acc[db][4 * a + 1] * a1 + v.y * a2;
+      acc[db][4 * a + 2] = acc[db][4 * a + 2] * a1 + v.z * a2;
+      acc[db][4 * a + 3] = acc[db][4 * a + 3] * a1 + v.w * a2;
+    }
+  return true;
+}
 
 // dQ of the 64 rows I0 .. of residue class rho of (b, h), in one pass over the
 // key tiles (the window's, then the global keys') with a running softmax per
@@ -972,131 +1069,70 @@ __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint
   row_frags(df, p.dO + hoff, rps, h32);
   const float dsum = row_dot(df, p.O + hoff, rps, h32);
 
+  const float c = p.scale * LOG2E;
+  const bool all_local = __all(rlocal);
   float m = -INFINITY, l = 0.0f;
   f32x16 acc[2] = {};
   for (int kt = 0; kt < ntot; ++kt) {
     const int cur = kt & 1;
+    const bool win = kt < nwin;
     wait_all_loads();
     if (t < T) {
-      mt[cur].kpos[t] = mr.pos;
-      mt[cur].kkind[t] = meta_kind(mr, kt < nwin);
+      // window tiles count local keys; the global tiles count global keys
+      const uint8_t kd = meta_kind(mr, win);
+      mt[cur].kkind[t] = kd;
+      publish_bits(mt[cur], kd == (win ? 2 : 1));
     }
     __syncthreads();
     if (kt + 1 < ntot) prefetch(kt + 1);
     const uint8_t* tK = sm + cur * 2 * TB;
-    const uint8_t* tV = tK + TB;
-    f32x16 x = {}, e = {};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      x = mfma_bf16(frag_row(tK, 32 * kq + qi, h32, c), qf[c], x);
-      e = mfma_bf16(frag_row(tV, 32 * kq + qi, h32, c), df[c], e);
-    }
-    // key acc_row(i) of the quadrant: allowed if of the tile's kind (local in
-    // the window, global after it) and, in the window, within r of the row
-    bool ok[16];
-    {
-      const bool win = kt < nwin;
-      const uint32_t want = win ? 2u : 1u;
-      const int base = T * kt - r - row + 32 * kq + 4 * h32 + r;   // key index minus row index, plus r
-      const uint32_t span = win ? (uint32_t)(2 * r) : 0xFFFFFFFFu;
-      const uint8_t* kk = mt[cur].kkind + 32 * kq + 4 * h32;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kw = *reinterpret_cast<const uint32_t*>(kk + 8 * j);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          ok[4 * j + u] = rlocal && ((kw >> (8 * u)) & 0xFFu) == want &&
-                          (uint32_t)(base + 8 * j + u) <= span;
-      }
-    }
-    float mx = m;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (ok[i]) mx = fmaxf(mx, p.scale * x[i]);
-    mx = half_max(mx);   // one running max for both halves of the row
-    const float alpha = m == -INFINITY ? 0.0f : __expf(m - mx);
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pr = ok[i] ? __expf(p.scale * x[i] - mx) : 0.0f;
-      l += pr;
-      x[i] = pr * (e[i] - dsum);
-    }
-    m = mx;
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      const bf16x8 bs = acc_frag(x, c2);
-#pragma unroll
-      for (int db = 0; db < 2; ++db) acc[db] = mfma_bf16(frag_tr(tK + 32 * kq * 128, c2, db, lane), bs, acc[db]);
-    }
+    // in the window, key 32 kq + k is within r of the row when key index
+    // minus row index, plus r, lies in [0, 2r]: k in [a, a + 2r]
+    const uint32_t kb = mt[cur].okm[kq];
+    const int a = row - T * kt - 32 * kq;
+    const uint32_t M = rlocal ? kb & (win ? bit_range_v(a, a + 2 * r + 1) : 0xFFFFFFFFu) : 0u;
+    const bool full = all_local && kb == 0xFFFFFFFFu && (!win || interior_tile(kt, r));
+    dq_tile(acc, m, l, tK, tK + TB, qf, df, dsum, M, full, c, kq, lane);
   }
-  l = half_sum(l);
-  // merge the two key quadrants
-  __syncthreads();
-  float* xr = xch + (rq * 64 + lane) * 34;
-  if (kq == 1) {
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) xr[db * 16 + i] = acc[db][i];
-    xr[32] = m;
-    xr[33] = l;
-  }
-  __syncthreads();
-  if (kq == 0 && rps >= 0) {
-    const float m2 = xr[32], l2 = xr[33];
-    const float mm = fmaxf(m, m2);
-    const float a1 = m == -INFINITY ? 0.0f : __expf(m - mm);
-    const float a2 = m2 == -INFINITY ? 0.0f : __expf(m2 - mm);
-    const float L = l * a1 + l2 * a2;
+  if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && rps >= 0) {
+    const float L = l, mm = m;
     const float mul = rlocal && L > 0.0f ? p.scale / L : 0.0f;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] = acc[db][i] * a1 + xr[db * 16 + i] * a2;
     store_dT(p.dQ + hoff + (int64_t)rps * 128, acc, mul, h32);
     if (rkd != 1) {
       const f32x16 z[2] = {};
       store_dT(p.dQg + hoff + (int64_t)rps * 128, z, 0.0f, h32);
     }
-    if (rlocal && h32 == 0) p.stats[bh * n + rps] = make_float2(L > 0.0f ? mm + __logf(L) : INFINITY, dsum);
+    if (rlocal && h32 == 0) p.stats[bh * n + rps] = make_float2(L > 0.0f ? mm + log2f(L) : INFINITY, dsum);
   }
 }
 
 // dK^T, dV^T accumulators of one key quadrant (lane = key) over the rows of
 // a 64-row tile: S = Q K^T and dP = dO V^T with rows in the accumulator's
-// order; P = exp(scale S - lse(row)) where the pair is allowed (0 elsewhere),
-// dS = P (dP - D).  A pair is allowed when kok (the key's side holds), the
-// row's kind is `want`, and base + (row index in the tile) taken from it, as
-// an unsigned number, is at most span (the window's reach; all ones: no limit).
+// order; P = exp2(c S - lse2(row)) (c = scale log2(e), lse2 the row's
+// log-sum-exp in log2 units, from mt.lse), dS = P (dP - D).  Bit k of M: row
+// 32 rq + k counts for the lane's key (ignored when `full`: every row counts).
 __device__ __forceinline__ void kv_tile(f32x16 (&dk)[2], f32x16 (&dv)[2], const uint8_t* tQ,
                                         const uint8_t* tdO, const bf16x8 (&kf)[4], const bf16x8 (&vf)[4],
-                                        const Meta& mt, float scale, int rq, int lane, bool kok,
-                                        uint32_t want, int base, uint32_t span) {
+                                        const Meta& mt, float c, int rq, int lane, uint32_t M, bool full) {
   const int h32 = lane >> 5, qi = lane & 31;
   f32x16 x = {}, e = {};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    x = mfma_bf16(frag_row(tQ, 32 * rq + qi, h32, c), kf[c], x);
-    e = mfma_bf16(frag_row(tdO, 32 * rq + qi, h32, c), vf[c], e);
+  for (int k = 0; k < 4; ++k) {
+    x = mfma_bf16(frag_row(tQ, 32 * rq + qi, h32, k), kf[k], x);
+    e = mfma_bf16(frag_row(tdO, 32 * rq + qi, h32, k), vf[k], e);
   }
+  if (!full) mask_half(x, M, h32);
   f32x16 pp;
   const int r0 = 32 * rq + 4 * h32;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t kw = *reinterpret_cast<const uint32_t*>(mt.rkind + r0 + 8 * j);
     const float4 ls = *reinterpret_cast<const float4*>(mt.lse + r0 + 8 * j);
     const float4 dd = *reinterpret_cast<const float4*>(mt.dd + r0 + 8 * j);
     const float lsv[4] = {ls.x, ls.y, ls.z, ls.w}, ddv[4] = {dd.x, dd.y, dd.z, dd.w};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = 4 * j + u;
-      const bool ok = kok && ((kw >> (8 * u)) & 0xFFu) == want && (uint32_t)(base - (r0 + 8 * j + u)) <= span;
-      const float pr = ok ? __expf(scale * x[i] - lsv[u]) : 0.0f;
+      const float pr = __builtin_amdgcn_exp2f(fmaf(x[i], c, -lsv[u]));
       pp[i] = pr;
       x[i] = pr * (e[i] - ddv[u]);
     }
@@ -1117,14 +1153,15 @@ __device__ __forceinline__ void kv_tile(f32x16 (&dk)[2], f32x16 (&dv)[2], const 
 __device__ __forceinline__ bool sum_row_quadrants(f32x16 (&dk)[2], f32x16 (&dv)[2], float* xch, int rq,
                                                   int kq, int lane) {
   __syncthreads();
-  float* x = xch + (kq * 64 + lane) * 64;
+  // [kq][16 float4 of dk, dv][lane]: consecutive lanes at consecutive addresses
+  float4* x = reinterpret_cast<float4*>(xch) + kq * 16 * 64 + lane;
   if (rq == 1) {
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[db * 16 + i] = dk[db][i];
-        x[32 + db * 16 + i] = dv[db][i];
+      for (int a = 0; a < 4; ++a) {
+        x[(4 * db + a) * 64] = make_float4(dk[db][4 * a], dk[db][4 * a + 1], dk[db][4 * a + 2], dk[db][4 * a + 3]);
+        x[(8 + 4 * db + a) * 64] = make_float4(dv[db][4 * a], dv[db][4 * a + 1], dv[db][4 * a + 2], dv[db][4 * a + 3]);
       }
   }
   __syncthreads();
@@ -1132,9 +1169,16 @@ __device__ __forceinline__ bool sum_row_quadrants(f32x16 (&dk)[2], f32x16 (&dv)[
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[db][i] += x[db * 16 + i];
-      dv[db][i] += x[32 + db * 16 + i];
+    for (int a = 0; a < 4; ++a) {
+      const float4 u = x[(4 * db + a) * 64], v = x[(8 + 4 * db + a) * 64];
+      dk[db][4 * a] += u.x;
+      dk[db][4 * a + 1] += u.y;
+      dk[db][4 * a + 2] += u.z;
+      dk[db][4 * a + 3] += u.w;
+      dv[db][4 * a] += v.x;
+      dv[db][4 * a + 1] += v.y;
+      dv[db][4 * a + 2] += v.z;
+      dv[db][4 * a + 3] += v.w;
     }
   return true;
 }
@@ -1191,6 +1235,8 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
   row_frags(kf, p.K + hoff, kps, h32);
   row_frags(vf, p.V + hoff, kps, h32);
   f32x16 dk[2] = {}, dv[2] = {};
+  const float c = p.scale * LOG2E;
+  const bool all_win = __all(kkd == 2), all_real = __all(kkd != 0);
   auto finish_window = [&]() {
     // global keys' dK, dV come from the chunk sums
     if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0 && kkd != 1) {
@@ -1208,21 +1254,26 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
   auto step = [&](int qt) {
     const int cur = qt & 1;
     wait_all_loads();
+    const bool win = qt < nwin;
     if (t < T) {
-      const uint8_t kd = meta_kind(mr, qt < nwin);
-      const bool keep = qt < nwin ? kd == 2 : kd == 1;
+      // window tiles count local rows; the global tiles count global rows
+      const uint8_t kd = meta_kind(mr, win);
+      const bool keep = kd == (win ? 2 : 1);
       mt[cur].rkind[t] = kd;
       mt[cur].lse[t] = keep ? mr.st.x : 0.0f;
       mt[cur].dd[t] = keep ? mr.st.y : 0.0f;
+      publish_bits(mt[cur], keep);
     }
     __syncthreads();
     if (qt + 1 < ntot) prefetch(qt + 1);
     const uint8_t* tQ = sm + cur * 2 * TB;
-    const uint8_t* tdO = tQ + TB;
-    // window: key index minus row index (subsequence) within [-r, r]
-    const bool win = qt < nwin;
-    kv_tile(dk, dv, tQ, tdO, kf, vf, mt[cur], p.scale, rq, lane, win ? kkd == 2 : kkd != 0, win ? 2u : 1u,
-            2 * r + key - T * qt, win ? (uint32_t)(2 * r) : 0xFFFFFFFFu);
+    // in the window, row 32 rq + k is within r of the key when key index
+    // minus row index, plus r, lies in [0, 2r]: k in [bk - 2r, bk]
+    const uint32_t rb = mt[cur].okm[rq];
+    const int bk = 2 * r + key - T * qt - 32 * rq;
+    const uint32_t M = win ? (kkd == 2 ? rb & bit_range_v(bk - 2 * r, bk + 1) : 0u) : (kkd != 0 ? rb : 0u);
+    const bool full = rb == 0xFFFFFFFFu && (win ? all_win && interior_tile(qt, r) : all_real);
+    kv_tile(dk, dv, tQ, tQ + TB, kf, vf, mt[cur], c, rq, lane, M, full);
   };
   // the window's row tiles; then the global rows' tiles (Kg, Vg fragments)
   for (int qt = 0; qt < nwin; ++qt) step(qt);
@@ -1238,157 +1289,114 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
 // (1) the global rows' dQg^T = Kg^T dS^T with a chunk-local running max (an
 // online softmax over the chunk's real keys), with the max and the sum of
 // exponentials, and (2) the global keys' dK^T = Q^T dS, dV^T = dO^T P over the
-// chunk's local rows (their statistics must be in place).
-constexpr int GS_SMEM = 2 * TB + 2 * 64 * 64 * 4;
+// chunk's local rows (their statistics must be in place).  One pass over the
+// chunk's tiles for each, the tiles double-buffered as in the dQ kernel.
+constexpr int GS_SMEM = 4 * TB + 2 * 64 * 64 * 4;
 
-__device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, uint8_t* sm, Meta& mt) {
-  uint8_t* tA = sm;
-  uint8_t* tB = sm + TB;
-  float* xch = reinterpret_cast<float*>(sm + 2 * TB);
+__device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, uint8_t* sm, Meta (&mt)[2]) {
+  float* xch = reinterpret_cast<float*>(sm + 4 * TB);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int h32 = lane >> 5, qi = lane & 31;
   const int n = p.n;
   const int64_t bh = (int64_t)b * p.H + h;
   const int64_t hoff = bh * n * 128;
-  const int64_t soff = bh * n;
   int g = p.gcnt[b];
   if (g > p.max_global) g = p.max_global;
   if (T * gt >= g) return;
+  const int32_t* gidx = p.gidx + (int64_t)b * n + T * gt;   // this tile's global positions
   const int P0 = sp * p.gchunk;
   const int P1 = P0 + p.gchunk < n ? P0 + p.gchunk : n;
-  if (t < T) {
-    const int idx = T * gt + t;
-    mt.rpos[t] = idx < g ? p.gidx[(int64_t)b * n + idx] : -1;
-  }
-  __syncthreads();
+  const int nt = (P1 - P0 + T - 1) / T;   // tiles per part
+  auto pos_of = [&](int st, int R) {
+    const int ps = P0 + T * (st < nt ? st : st - nt) + R;
+    return ps < P1 ? ps : -1;
+  };
+  const i32x4 dKg = make_desc(p.Kg + hoff, n * 128);
+  const i32x4 dVg = make_desc(p.Vg + hoff, n * 128);
+  const i32x4 dQd = make_desc(p.Q + hoff, n * 128);
+  const i32x4 dOd = make_desc(p.dO + hoff, n * 128);
+  const uint32_t lds0 = lds_addr(sm);
+  const float* lm = p.lmask + (int64_t)b * n;
+  const float* gm = p.gmask + (int64_t)b * n;
+  const float2* stp = p.stats + bh * n;
+  MetaRegs mr;
+  auto prefetch = [&](int st) {
+    const bool two = st >= nt;
+    const int R0 = dma_row0(w, lane);
+    const int p0 = pos_of(st, R0), p1 = pos_of(st, R0 + 8);
+    const int pm = t < T ? pos_of(st, t) : -1;
+    const uint32_t buf = lds0 + (st & 1) * 2 * TB;
+    dma_tile(two ? dQd : dKg, buf, w, lane, p0, p1);
+    dma_tile(two ? dOd : dVg, buf + TB, w, lane, p0, p1);
+    if (t < T) fetch_meta(mr, lm, gm, two ? stp : nullptr, pm, true);
+  };
+  prefetch(0);
+  // (1) wave w: global rows 32 (w & 1) + lane % 32 (lane = row), keys 32 (w >> 1) ..
   {
-    // (1) wave w: global rows 32 (w & 1) + lane % 32 (lane = row), keys 32 (w >> 1) ..
     const int rq = w & 1, kq = w >> 1;
     const int row = 32 * rq + qi;
-    const int gps = mt.rpos[row];
+    const int gps = T * gt + row < g ? gidx[row] : -1;
     bf16x8 qf[4], df[4];
     row_frags(qf, p.Qg + hoff, gps, h32);
     row_frags(df, p.dO + hoff, gps, h32);
-    float dsum;
-    {
-      bf16x8 of[4];
-      row_frags(of, p.O + hoff, gps, h32);
-      float a = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a = fmaf((float)df[c][e], (float)of[c][e], a);
-      dsum = half_sum(a);
-    }
+    const float dsum = row_dot(df, p.O + hoff, gps, h32);
+    const float c = p.scale * LOG2E;
+    const bool all_live = __all(gps >= 0);
     float m = -INFINITY, l = 0.0f;
     f32x16 acc[2] = {};
-    for (int P = P0; P < P1; P += T) {
-      __syncthreads();
+    for (int st = 0; st < nt; ++st) {
+      const int cur = st & 1;
+      wait_all_loads();
       if (t < T) {
-        const int ps = P + t < P1 ? P + t : -1;
-        mt.kpos[t] = ps;
-        mt.kkind[t] = kind_of(p, b, ps);
+        const uint8_t kd = meta_kind(mr, true);
+        mt[cur].kkind[t] = kd;
+        publish_bits(mt[cur], kd != 0);   // every real key
       }
       __syncthreads();
-      load_tile_bf(tA, p.Kg + hoff, mt.kpos);
-      load_tile_bf(tB, p.Vg + hoff, mt.kpos);
-      __syncthreads();
-      f32x16 x = {}, e = {};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        x = mfma_bf16(frag_row(tA, 32 * kq + qi, h32, c), qf[c], x);
-        e = mfma_bf16(frag_row(tB, 32 * kq + qi, h32, c), df[c], e);
-      }
-      float mx = m;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (gps >= 0 && mt.kkind[32 * kq + acc_row(i, h32)] != 0) mx = fmaxf(mx, p.scale * x[i]);
-      mx = half_max(mx);   // one running max for both halves of the row
-      const float alpha = m == -INFINITY ? 0.0f : __expf(m - mx);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const bool ok = gps >= 0 && mt.kkind[32 * kq + acc_row(i, h32)] != 0;
-        const float pr = ok ? __expf(p.scale * x[i] - mx) : 0.0f;
-        l += pr;
-        x[i] = pr * (e[i] - dsum);
-      }
-      m = mx;
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 bs = acc_frag(x, c2);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) acc[db] = mfma_bf16(frag_tr(tA + 32 * kq * 128, c2, db, lane), bs, acc[db]);
-      }
+      prefetch(st + 1);   // the first tile of part (2) follows the last of part (1)
+      const uint8_t* tK = sm + cur * 2 * TB;
+      const uint32_t kb = mt[cur].okm[kq];
+      dq_tile(acc, m, l, tK, tK + TB, qf, df, dsum, gps >= 0 ? kb : 0u, all_live && kb == 0xFFFFFFFFu, c, kq,
+              lane);
     }
-    l = half_sum(l);
-    // merge the two key quadrants
-    __syncthreads();
-    float* x = xch + (rq * 64 + lane) * 34;
-    if (kq == 1) {
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[db * 16 + i] = acc[db][i];
-      x[32] = m;
-      x[33] = l;
-    }
-    __syncthreads();
-    if (kq == 0 && gps >= 0) {
-      const float m2 = x[32], l2 = x[33];
-      const float mm = fmaxf(m, m2);
-      const float a1 = m == -INFINITY ? 0.0f : __expf(m - mm);
-      const float a2 = m2 == -INFINITY ? 0.0f : __expf(m2 - mm);
+    if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && gps >= 0) {
       float* dst = p.gq + ((bh * p.max_global + T * gt + row) * p.gsplit + sp) * 68;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          float4 v;
-          v.x = acc[db][4 * a + 0] * a1 + x[db * 16 + 4 * a + 0] * a2;
-          v.y = acc[db][4 * a + 1] * a1 + x[db * 16 + 4 * a + 1] * a2;
-          v.z = acc[db][4 * a + 2] * a1 + x[db * 16 + 4 * a + 2] * a2;
-          v.w = acc[db][4 * a + 3] * a1 + x[db * 16 + 4 * a + 3] * a2;
-          *reinterpret_cast<float4*>(dst + 32 * db + 8 * a + 4 * h32) = v;
-        }
-      if (h32 == 0) {
-        dst[64] = mm;
-        dst[65] = l * a1 + l2 * a2;
-      }
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<float4*>(dst + 32 * db + 8 * a + 4 * h32) =
+              make_float4(acc[db][4 * a], acc[db][4 * a + 1], acc[db][4 * a + 2], acc[db][4 * a + 3]);
+      if (h32 == 0) *reinterpret_cast<float2*>(dst + 64) = make_float2(m, l);
     }
   }
   // (2) wave w: global keys 32 (w & 1) + lane % 32 (lane = key), rows 32 (w >> 1) ..
-  __syncthreads();
   {
     const int kq = w & 1, rq = w >> 1;
     const int key = 32 * kq + qi;
-    const int kps = mt.rpos[key];   // the tile's global positions, now as keys
+    const int kps = T * gt + key < g ? gidx[key] : -1;
     bf16x8 kf[4], vf[4];
     row_frags(kf, p.K + hoff, kps, h32);
     row_frags(vf, p.V + hoff, kps, h32);
     f32x16 dk[2] = {}, dv[2] = {};
-    __syncthreads();   // every wave has read rpos
-    for (int P = P0; P < P1; P += T) {
-      __syncthreads();
+    const float c = p.scale * LOG2E;
+    const bool all_live = __all(kps >= 0);
+    for (int st = nt; st < 2 * nt; ++st) {
+      const int cur = st & 1;
+      wait_all_loads();
       if (t < T) {
-        const int ps = P + t < P1 ? P + t : -1;
-        const uint8_t kd = kind_of(p, b, ps);
-        mt.rkind[t] = kd;
-        mt.kpos[t] = ps;
-        float2 st = make_float2(0.0f, 0.0f);
-        if (kd == 2) st = p.stats[soff + ps];
-        mt.lse[t] = st.x;
-        mt.dd[t] = st.y;
+        const uint8_t kd = meta_kind(mr, true);
+        mt[cur].rkind[t] = kd;
+        mt[cur].lse[t] = kd == 2 ? mr.st.x : 0.0f;
+        mt[cur].dd[t] = kd == 2 ? mr.st.y : 0.0f;
+        publish_bits(mt[cur], kd == 2);   // every local row
       }
       __syncthreads();
-      load_tile_bf(tA, p.Q + hoff, mt.kpos);
-      load_tile_bf(tB, p.dO + hoff, mt.kpos);
-      __syncthreads();
-      kv_tile(dk, dv, tA, tB, kf, vf, mt, p.scale, rq, lane, kps >= 0, 2u, 0, 0xFFFFFFFFu);
+      if (st + 1 < 2 * nt) prefetch(st + 1);
+      const uint8_t* tQ = sm + cur * 2 * TB;
+      const uint32_t rb = mt[cur].okm[rq];
+      kv_tile(dk, dv, tQ, tQ + TB, kf, vf, mt[cur], c, rq, lane, kps >= 0 ? rb : 0u,
+              all_live && rb == 0xFFFFFFFFu);
     }
     if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0) {
       float* dst = p.gk + ((bh * p.max_global + T * gt + key) * p.gsplit + sp) * 128;
@@ -1424,14 +1432,15 @@ __global__ __launch_bounds__(NTH) void dkv_kernel(BwParams p) {
 
 __global__ __launch_bounds__(NTH) void global_chunk_kernel(BwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
-  __shared__ Meta mt;
+  __shared__ Meta mt[2];
   const int sp = blockIdx.x % p.gsplit, rest = blockIdx.x / p.gsplit;
   const int gt = rest % p.ntg, bh = rest / p.ntg;
   global_chunk(p, bh / p.H, bh % p.H, gt, sp, sm, mt);
 }
 
-// One wave per (b, h, global index): combines the chunk sums into dQg (and
-// the row's log-sum-exp and D) and the global key's dK, dV.  Lane = d.
+// One wave per (b, h, global index): combines the chunk sums (offsets in log2
+// units) into dQg (and the row's log-sum-exp, log2 units, and D) and the
+// global key's dK, dV.  Lane = d.
 __global__ __launch_bounds__(NTH) void global_merge_kernel(BwParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * (NTH / 64) + (threadIdx.x >> 6);
@@ -1454,7 +1463,7 @@ __global__ __launch_bounds__(NTH) void global_merge_kernel(BwParams p) {
 #pragma unroll 8
   for (int sp = 0; sp < p.gsplit; ++sp) {
     const float m = q[sp * 68 + 64];
-    const float f = m == -INFINITY ? 0.0f : __expf(m - mm);
+    const float f = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mm);
     L = fmaf(q[sp * 68 + 65], f, L);
     a = fmaf(q[sp * 68 + lane], f, a);
   }
@@ -1473,7 +1482,7 @@ __global__ __launch_bounds__(NTH) void global_merge_kernel(BwParams p) {
   *reinterpret_cast<__bf16*>(p.dQg + ro) = (__bf16)(L > 0.0f ? p.scale * a / L : 0.0f);
   *reinterpret_cast<__bf16*>(p.dK + ro) = (__bf16)(p.scale * sk);
   *reinterpret_cast<__bf16*>(p.dV + ro) = (__bf16)sv;
-  if (lane == 0) p.stats[bh * n + pos] = make_float2(L > 0.0f ? mm + __logf(L) : INFINITY, dd);
+  if (lane == 0) p.stats[bh * n + pos] = make_float2(L > 0.0f ? mm + log2f(L) : INFINITY, dd);
 }
 
 }  // namespace mk

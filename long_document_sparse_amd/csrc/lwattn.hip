@@ -245,12 +245,12 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->head_blk64, (size_t)(H + 1) * 4);
   alloc((void**)&p->stats, (size_t)B * H * n * sizeof(float2));
   if (cfg->dtype == LWATTN_BF16 && cfg->max_global > 0 && n > 0) {
-    // the positions of a head are cut into chunks of whole 64-row tiles, at
-    // least four tiles each, as many as bring the workgroups of the chunk sums
-    // (one per batch row, head, 64 global rows and chunk) to about 1024
+    // the positions of a head are cut into chunks of whole 64-row tiles, as
+    // many as bring the workgroups of the chunk sums (one per batch row, head,
+    // 64 global rows and chunk) to about 1024
     const int64_t ntile = ((int64_t)n + lwk::bw::T - 1) / lwk::bw::T;
     const int64_t units = (int64_t)B * H * ceil_div(cfg->max_global, lwk::bw::T);
-    const int64_t want = std::max<int64_t>(1, std::min<int64_t>((ntile + 3) / 4, (1024 + units - 1) / units));
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>(ntile, (1024 + units - 1) / units));
     const int64_t tiles = (ntile + want - 1) / want;
     p->gchunk = (int)(tiles * lwk::bw::T);
     p->gsplit = (int)((ntile + tiles - 1) / tiles);
@@ -463,6 +463,8 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
       return LWATTN_E_UNSUPPORTED;
     (void)hipFuncSetAttribute((const void*)mk::dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DQ_SMEM);
     (void)hipFuncSetAttribute((const void*)mk::dkv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DKV_SMEM);
+    (void)hipFuncSetAttribute((const void*)mk::global_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              mk::GS_SMEM);
     hipLaunchKernelGGL(mk::dq_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DQ_SMEM, stream, bp);
     if (nchunk > 0) {
       hipLaunchKernelGGL(mk::global_chunk_kernel, dim3((uint32_t)nchunk), dim3(lwk::bw::NTH), mk::GS_SMEM, stream, bp);

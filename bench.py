@@ -21,10 +21,12 @@ and the end of its execution, on every fourth forward of the timed loop
 pace of the loop).
 
 --pass backward times lwattn_backward instead (dQ, dK, dV, dQg, dKg, dVg of a
-seeded dO, after one forward for O) and prints its own line: its three
-launches are timed together with events on the stream around the timed loop,
-its roofline is the fp32 vector-ALU one (the kernels compute in fp32 on the
-VALU), and its CPU baseline is the oracle's backward.
+seeded dO, after one forward for O) and prints its own line: the whole call
+is timed with events on the stream around the timed loop, and each of its
+kernels with the events its dispatch records; the roofline is that of the
+longest kernel (bf16 storage: its matrix FLOPs against the bf16 matrix-core
+peak; fp32 storage: the whole call against the fp32 vector-ALU peak), and the
+CPU baseline is the oracle's backward.
 
 --copy-probe runs, after the timed loop, a plain device-to-device copy of the
 given size a few times; a counter pass over the same command then gives the
@@ -44,10 +46,11 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense MFMA
 PEAK_FP32_VECTOR = 157.3                          # MI355X fp32 vector ALU, TFLOP/s
+PEAK_BF16_MFMA = 2500.0                           # MI355X dense bf16 matrix cores, TFLOP/s
 PEAK_HBM_GBS = 8000.0
 TIMING_EVERY = 4
 METRIC = "window+global attn fwd tokens/s & TFLOP/s (% bf16 MFMA peak), n=4096 w=512"
-METRIC_BWD = "window+global attn bwd tokens/s & TFLOP/s (% fp32 vector peak), n=4096 w=512"
+METRIC_BWD = "window+global attn bwd tokens/s, n=4096 w=512"
 KERNEL_SOURCES = ("long_document_sparse_amd/csrc/kernels.hpp",
                   "long_document_sparse_amd/csrc/lwattn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_traffic.txt")
@@ -171,6 +174,10 @@ def run_backward(args, spec, x, ts, lm, gm, plan):
     if st != lwattn.OK:
         raise SystemExit(f"backward failed: {lwattn.strerror(st)}")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not args.no_timing:
+        # per-kernel events recorded by the dispatches themselves, every
+        # TIMING_EVERY-th backward of the timed loop
+        plan.timing_enable(args.steps, every=TIMING_EVERY)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
@@ -185,21 +192,27 @@ def run_backward(args, spec, x, ts, lm, gm, plan):
     t_call = e0.elapsed_time(e1) * 1e-3 / args.steps        # s per backward, on the stream
     flop = fl.backward_flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
     nbytes = fl.backward_bytes(x.lmask, x.gmask, spec.H, spec.d, 2 if spec.dtype == "bf16" else 4)
-    tflops = flop / t_call / 1e12
-    gbs = nbytes / t_call / 1e9
-    alu_bound = flop / (PEAK_FP32_VECTOR * 1e12) > nbytes / (PEAK_HBM_GBS * 1e9)
-    roofline = ({"bound": "alu", "achieved": round(tflops, 2), "peak": PEAK_FP32_VECTOR,
-                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_VECTOR, 4), "traffic": None}
-                if alu_bound else
-                {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None})
-    roofline.update({"kernel": "backward (compact_kernel + dq_kernel + dkv_kernel)",
-                     "algorithmic_flop": flop, "algorithmic_bytes": nbytes,
-                     "alu_view": {"achieved_tflops": round(tflops, 2), "peak": PEAK_FP32_VECTOR,
-                                  "frac": round(tflops / PEAK_FP32_VECTOR, 4)},
-                     "hbm_view": {"achieved_gbs": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                                  "frac": round(gbs / PEAK_HBM_GBS, 4)},
-                     "source_sha256": source_hash()})
+    roofline = None
+    if not args.no_timing:
+        tot, calls = plan.timing_read_backward()
+        plan.timing_disable()
+        kflop = fl.backward_kernel_flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
+        per = {k: v / max(calls, 1) * 1e-3 for k, v in tot.items()}     # s per launch
+        dom = max(per, key=per.get)
+        if spec.dtype == "bf16":
+            # the contractions run on bf16 matrix cores
+            achieved = kflop[dom] / per[dom] / 1e12
+            roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_MFMA,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_MFMA, 4), "traffic": None}
+        else:
+            # fp32 storage: the contractions run on the fp32 vector ALUs
+            achieved = flop / t_call / 1e12
+            roofline = {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP32_VECTOR,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_VECTOR, 4), "traffic": None}
+        roofline.update({"kernel": dom if spec.dtype == "bf16" else "backward (all kernels)",
+                         "algorithmic_flop": kflop[dom] if spec.dtype == "bf16" else flop,
+                         "kernel_us": {k: round(v * 1e6, 2) for k, v in per.items() if v > 0},
+                         "timed_calls": calls, "source_sha256": source_hash()})
     tokens = spec.B * spec.n
     res = {
         "metric": METRIC_BWD,
@@ -218,6 +231,8 @@ def run_backward(args, spec, x, ts, lm, gm, plan):
                    "seq_len": spec.n, "heads": spec.H, "head_dim": spec.d, "window": spec.window,
                    "parallelism": "single GPU", "timing": "warm (back to back)"},
         "tflops_per_s": round(flop / (elapsed / args.steps) / 1e12, 2),
+        "algorithmic_flop": flop,
+        "algorithmic_bytes": nbytes,
         "us_per_backward_on_stream": round(t_call * 1e6, 2),
         "roofline": roofline,
     }

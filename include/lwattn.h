@@ -182,6 +182,14 @@ lwattn_status lwattn_timing_enable(lwattn_plan_t plan, int32_t max_calls);
 lwattn_status lwattn_timing_every(lwattn_plan_t plan, int32_t every);
 lwattn_status lwattn_timing_read(lwattn_plan_t plan, float* ms, int32_t cap,
                                  int32_t* nkernels, int32_t* ncalls);
+/* The same for backwards (recorded while timing is enabled, every `every`-th
+ * backward, up to `max_calls`): per kernel slot, the summed duration in
+ * milliseconds over the recorded backwards.  Slots (*nkernels = 5): the
+ * global-index compaction, dQ, the chunk sums of the global rows and keys, their
+ * merge, dK/dV; a slot whose kernel a backward did not launch (fp32 storage
+ * launches slots 0, 1 and 4 only) counts zero. */
+lwattn_status lwattn_timing_read_backward(lwattn_plan_t plan, float* ms, int32_t cap,
+                                          int32_t* nkernels, int32_t* ncalls);
 lwattn_status lwattn_timing_disable(lwattn_plan_t plan);
 
 /* Testing aid for the failure path of the in-kernel wait (for test code only).

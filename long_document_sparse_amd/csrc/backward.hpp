@@ -785,18 +785,61 @@ __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t*)ptr);
 }
 
+// s_waitcnt vmcnt(N) through the builtin (loads only).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | (((N >> 4) & 3) << 14));
+}
+
+// One dword per lane straight into LDS at m0 = lds_base (lane l writes
+// lds_base + 4 l); an offset past the descriptor's range writes zero.  G tags
+// the copy of the code: the issue sequences of window tiles (positions from
+// arithmetic) and of global tiles (positions read from the index) must stay
+// apart, or the compiler's wait for the index reads would land on both.
+template <int G>
+__device__ __forceinline__ void dma4(const i32x4& desc, int voff, uint32_t lds_base) {
+  if constexpr (G == 0)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(desc), "s"(lds_base)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds ; global tile"
+                 :
+                 : "v"(voff), "s"(desc), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// 16 bytes per lane into LDS at m0 = lds_base + IMM (lane l writes 16 l on);
+// G as for dma4.
+template <int IMM, int G>
+__device__ __forceinline__ void dma16g(const i32x4& desc, int voff, uint32_t lds_base) {
+  if constexpr (G == 0)
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(desc), "s"(lds_base), "n"(IMM)
+                 : "memory", "m0", "scc");
+  else
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds ; global tile"
+                 :
+                 : "v"(voff), "s"(desc), "s"(lds_base), "n"(IMM)
+                 : "memory", "m0", "scc");
+}
+
 // This wave's 16 rows of a 64-row tile, straight from global memory into LDS
 // at `tile` (an LDS address): lane l fills chunk l % 8 of rows R0 = 16 w + l / 8
 // and R0 + 8, whose positions are p0 and p1 (negative: a zero row).  d covers
 // the head's n rows.
 __device__ __forceinline__ int dma_row0(int w, int lane) { return 16 * w + (lane >> 3); }
 
+template <int G = 0>
 __device__ __forceinline__ void dma_tile(const i32x4& d, uint32_t tile, int w, int lane, int p0, int p1) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(tile + w * 2048);
   const int R0 = dma_row0(w, lane);
   const int c16 = ((lane & 7) ^ swz(R0)) * 16;   // swz(R0 + 8) = swz(R0) ^ 2
-  dma16i<0>(d, p0 >= 0 ? p0 * 128 + c16 : OOB_OFF, base);
-  dma16i<1024>(d, p1 >= 0 ? p1 * 128 + (c16 ^ 32) : OOB_OFF, base);
+  dma16g<0, G>(d, p0 >= 0 ? p0 * 128 + c16 : OOB_OFF, base);
+  dma16g<1024, G>(d, p1 >= 0 ? p1 * 128 + (c16 ^ 32) : OOB_OFF, base);
 }
 
 // s_waitcnt vmcnt(0) through the builtin, which the compiler's own wait
@@ -805,6 +848,31 @@ __device__ __forceinline__ void dma_tile(const i32x4& d, uint32_t tile, int w, i
 // of an older load, and so also for the tile loads issued after it).
 __device__ __forceinline__ void wait_all_loads() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt 0, expcnt 7, lgkmcnt 15: loads only
+}
+
+// Per-tile metadata of the three-slot kernels: log-sum-exp (log2 units) and
+// D of the tile's rows where they count (zero elsewhere), and the bits of the
+// rows or keys that count.
+struct alignas(16) TMeta {
+  float lse[T], dd[T];
+  uint32_t okm[2], pad[2];
+};
+
+// What wave 0 stages per tile and slot, straight from global memory: the
+// masks at the tile's 64 positions, and (kernels that need them) the rows'
+// statistics.  Positions outside the tile read as zero: a zero local mask,
+// so kind 0.
+struct Stage {
+  float lm[T], gm[T];
+};
+struct StageS {
+  float lm[T], gm[T], lse[T], dd[T];
+};
+
+template <typename S>
+__device__ __forceinline__ uint8_t stage_kind(const S& sg, int t) {
+  if (sg.lm[t] == 0.0f) return 0;
+  return sg.gm[t] != 0.0f ? 1 : 2;
 }
 
 // A or B fragment c of row `row` of a [row][d] tile
@@ -904,14 +972,15 @@ __device__ __forceinline__ uint8_t meta_kind(const MetaRegs& mr, bool masks) {
   return mr.gv != 0.0f ? 1 : 2;
 }
 
-constexpr int DQ_SMEM = 4 * TB + 2 * 64 * 34 * 4;   // two K, V tile pairs; the key quadrants' merge (34 floats a row)
+constexpr int DQ_SMEM = 6 * TB + 3 * (int)sizeof(Stage);   // three K, V tile pairs, three Stage records
 constexpr int DKV_SMEM = 4 * TB + 2 * 64 * 64 * 4;  // two Q, dO tile pairs; the row quadrants' sums
 
 constexpr float LOG2E = 1.4426950408889634f;
 
 // Wave 0 (threads 0..63, one tile row or key each) publishes which entries of
 // the tile count: bit t of the 64-bit word.
-__device__ __forceinline__ void publish_bits(Meta& mt, bool counts) {
+template <typename M>
+__device__ __forceinline__ void publish_bits(M& mt, bool counts) {
   const uint64_t bits = __ballot(counts);
   if (threadIdx.x == 0) {
     mt.okm[0] = (uint32_t)bits;
@@ -1019,8 +1088,11 @@ __device__ __forceinline__ bool merge_key_quadrants(f32x16 (&acc)[2], float& m, 
 // m the running maximum.  Also writes zero dQ rows for the block's non-local
 // rows, zero dQg rows for its non-global rows, and (log-sum-exp, D) of its
 // local rows.
-__device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint8_t* sm, Meta (&mt)[2]) {
-  float* xch = reinterpret_cast<float*>(sm + 4 * TB);
+__device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint8_t* sm, TMeta (&tm)[3]) {
+  // LDS: three slots of (K tile, V tile), then three Stage records; the
+  // merge of the key quadrants reuses the slots once the tiles are done
+  Stage* stg = reinterpret_cast<Stage*>(sm + 6 * TB);
+  float* xch = reinterpret_cast<float*>(sm);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, rq = w & 1, kq = w >> 1;
   const int h32 = lane >> 5, qi = lane & 31;
   const int n = p.n, s = p.head_stride[h], r = p.r;
@@ -1043,22 +1115,34 @@ __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint
   };
   const i32x4 dK = make_desc(p.K + hoff, n * 128);
   const i32x4 dV = make_desc(p.V + hoff, n * 128);
+  const i32x4 dLm = make_desc(p.lmask + (int64_t)b * n, n * 4);
+  const i32x4 dGm = make_desc(p.gmask + (int64_t)b * n, n * 4);
   const uint32_t lds0 = lds_addr(sm);
-  const float* lm = p.lmask + (int64_t)b * n;
-  const float* gm = p.gmask + (int64_t)b * n;
-  MetaRegs mr;
-  auto prefetch = [&](int kt) {
-    // every position first (global tiles read them from the index), then
-    // the tiles, then the metadata
+  const uint32_t ldsg = lds_addr(stg);
+  // tile kt into slot kt % 3: every wave its 16 rows of K and V (4 loads),
+  // wave 0 also the masks at the 64 key positions (2 loads)
+  auto issue = [&](auto gtag, int kt, int slot) {
+    constexpr int G = decltype(gtag)::value;
     const int R0 = dma_row0(w, lane);
     const int p0 = key_pos(kt, R0), p1 = key_pos(kt, R0 + 8);
-    const int pm = t < T ? key_pos(kt, t) : -1;
-    const uint32_t buf = lds0 + (kt & 1) * 2 * TB;
-    dma_tile(dK, buf, w, lane, p0, p1);
-    dma_tile(dV, buf + TB, w, lane, p0, p1);
-    if (t < T) fetch_meta(mr, lm, gm, nullptr, pm, kt < nwin);
+    const uint32_t buf = lds0 + slot * 2 * TB;
+    dma_tile<G>(dK, buf, w, lane, p0, p1);
+    dma_tile<G>(dV, buf + TB, w, lane, p0, p1);
+    if (w == 0) {
+      const int pm = key_pos(kt, lane);
+      const int off = pm >= 0 ? pm * 4 : OOB_OFF;
+      const uint32_t sb = __builtin_amdgcn_readfirstlane(ldsg + slot * (uint32_t)sizeof(Stage));
+      dma4<G>(dLm, off, sb + offsetof(Stage, lm));
+      dma4<G>(dGm, off, sb + offsetof(Stage, gm));
+    }
   };
-  if (ntot > 0) prefetch(0);
+  auto prefetch = [&](int kt, int slot) {
+    if (kt < nwin)
+      issue(std::integral_constant<int, 0>{}, kt, slot);
+    else
+      issue(std::integral_constant<int, 1>{}, kt, slot);
+  };
+  prefetch(0, 0);
 
   const int row = 32 * rq + qi;
   const int rps = I0 + row < nr ? rho + (I0 + row) * s : -1;
@@ -1068,31 +1152,42 @@ __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint
   row_frags(qf, p.Q + hoff, rps, h32);
   row_frags(df, p.dO + hoff, rps, h32);
   const float dsum = row_dot(df, p.O + hoff, rps, h32);
+  // every load so far has landed, tile 0 too; from here on the only loads in
+  // flight are the tiles' (and, at global tiles, the index reads)
+  wait_all_loads();
+  if (ntot > 1) prefetch(1, 1);
 
   const float c = p.scale * LOG2E;
   const bool all_local = __all(rlocal);
   float m = -INFINITY, l = 0.0f;
   f32x16 acc[2] = {};
+  int cur = 0;
   for (int kt = 0; kt < ntot; ++kt) {
-    const int cur = kt & 1;
     const bool win = kt < nwin;
-    wait_all_loads();
+    // tile kt landed; tile kt + 1 may still be in flight
+    if (kt + 1 < ntot) {
+      if (w == 0)
+        wait_vm<6>();
+      else
+        wait_vm<4>();
+    } else {
+      wait_vm<0>();
+    }
     if (t < T) {
       // window tiles count local keys; the global tiles count global keys
-      const uint8_t kd = meta_kind(mr, win);
-      mt[cur].kkind[t] = kd;
-      publish_bits(mt[cur], kd == (win ? 2 : 1));
+      publish_bits(tm[cur], stage_kind(stg[cur], t) == (win ? 2 : 1));
     }
     __syncthreads();
-    if (kt + 1 < ntot) prefetch(kt + 1);
+    if (kt + 2 < ntot) prefetch(kt + 2, cur == 0 ? 2 : cur - 1);
     const uint8_t* tK = sm + cur * 2 * TB;
     // in the window, key 32 kq + k is within r of the row when key index
     // minus row index, plus r, lies in [0, 2r]: k in [a, a + 2r]
-    const uint32_t kb = mt[cur].okm[kq];
+    const uint32_t kb = tm[cur].okm[kq];
     const int a = row - T * kt - 32 * kq;
     const uint32_t M = rlocal ? kb & (win ? bit_range_v(a, a + 2 * r + 1) : 0xFFFFFFFFu) : 0u;
     const bool full = all_local && kb == 0xFFFFFFFFu && (!win || interior_tile(kt, r));
     dq_tile(acc, m, l, tK, tK + TB, qf, df, dsum, M, full, c, kq, lane);
+    cur = cur == 2 ? 0 : cur + 1;
   }
   if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && rps >= 0) {
     const float L = l, mm = m;
@@ -1414,11 +1509,13 @@ __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, ui
   }
 }
 
+// Neighbouring blocks of a head share most of their window tiles: the
+// logical block order keeps them on one XCD, whose L2 then serves the overlap.
 __global__ __launch_bounds__(NTH) void dq_kernel(BwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
-  __shared__ Meta mt[2];
+  __shared__ TMeta mt[3];
   int b, h, rho, blk;
-  decode_block(p, blockIdx.x, b, h, rho, blk);
+  decode_block(p, xcd_remap(blockIdx.x, gridDim.x), b, h, rho, blk);
   dq_local(p, b, h, rho, blk, sm, mt);
 }
 
@@ -1426,7 +1523,7 @@ __global__ __launch_bounds__(NTH) void dkv_kernel(BwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ Meta mt[2];
   int b, h, rho, blk;
-  decode_block(p, blockIdx.x, b, h, rho, blk);
+  decode_block(p, xcd_remap(blockIdx.x, gridDim.x), b, h, rho, blk);
   dkv_local(p, b, h, rho, blk, sm, mt);
 }
 

@@ -22,6 +22,9 @@
 namespace {
 
 constexpr int kNumKernels = 1;
+// backward kernel slots: compaction, dQ, chunk sums, merge, dK/dV (the fp32
+// storage path runs the compaction, dQ and dK/dV only)
+constexpr int kNumBwKernels = 5;
 
 // LWATTN_DEBUG=1 in the environment prints every failing HIP call to stderr.
 bool hip_ok(hipError_t e, const char* what) {
@@ -75,6 +78,9 @@ struct lwattn_plan_s {
   int timing_every = 1;    // record the events of every k-th forward
   int64_t timing_seen = 0; // forwards since timing was enabled
   std::vector<hipEvent_t> events;   // (kNumKernels + 1) per recorded forward
+  int bw_calls = 0;                 // backwards recorded
+  int64_t bw_seen = 0;              // backwards since timing was enabled
+  std::vector<hipEvent_t> bw_events;   // 2 kNumBwKernels per recorded backward
 };
 
 static void free_plan(lwattn_plan_s* p) {
@@ -95,6 +101,7 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->gq);
   (void)hipFree(p->gk);
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->bw_events) (void)hipEventDestroy(e);
   delete p;
 }
 
@@ -411,7 +418,18 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   cp.n = c.n;
   cp.max_global = c.max_global;
   cp.mask_vec = ((((uintptr_t)lmask | (uintptr_t)gmask) & 15u) == 0 && (c.n % 4) == 0) ? 1 : 0;
-  hipLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream, cp);
+  bool timed = false;
+  if (p->timing_cap > 0 && p->bw_calls < p->timing_cap) {
+    timed = (p->bw_seen % p->timing_every) == 0;
+    ++p->bw_seen;
+  }
+  // a timed backward launches each kernel with the pair of events its
+  // dispatch records (slot k: events 2k, 2k + 1 of the call's record)
+  auto ev = [&](int k, int e) -> hipEvent_t {
+    return timed ? p->bw_events[(size_t)p->bw_calls * 2 * kNumBwKernels + 2 * k + e] : nullptr;
+  };
+  hipExtLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream,
+                        ev(0, 0), ev(0, 1), 0u, cp);
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
 
   lwk::bw::BwParams bp;
@@ -465,20 +483,27 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
     (void)hipFuncSetAttribute((const void*)mk::dkv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DKV_SMEM);
     (void)hipFuncSetAttribute((const void*)mk::global_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               mk::GS_SMEM);
-    hipLaunchKernelGGL(mk::dq_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DQ_SMEM, stream, bp);
+    hipExtLaunchKernelGGL(mk::dq_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DQ_SMEM, stream, ev(1, 0),
+                          ev(1, 1), 0u, bp);
     if (nchunk > 0) {
-      hipLaunchKernelGGL(mk::global_chunk_kernel, dim3((uint32_t)nchunk), dim3(lwk::bw::NTH), mk::GS_SMEM, stream, bp);
-      hipLaunchKernelGGL(mk::global_merge_kernel, dim3((uint32_t)nmerge), dim3(lwk::bw::NTH), 0, stream, bp);
+      hipExtLaunchKernelGGL(mk::global_chunk_kernel, dim3((uint32_t)nchunk), dim3(lwk::bw::NTH), mk::GS_SMEM,
+                            stream, ev(2, 0), ev(2, 1), 0u, bp);
+      hipExtLaunchKernelGGL(mk::global_merge_kernel, dim3((uint32_t)nmerge), dim3(lwk::bw::NTH), 0, stream,
+                            ev(3, 0), ev(3, 1), 0u, bp);
     }
-    hipLaunchKernelGGL(mk::dkv_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DKV_SMEM, stream, bp);
+    hipExtLaunchKernelGGL(mk::dkv_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DKV_SMEM, stream,
+                          ev(4, 0), ev(4, 1), 0u, bp);
   } else {
     // 2. dQ, dQg and the rows' statistics; 3. dK, dV, dKg, dVg
     (void)hipFuncSetAttribute((const void*)lwk::bw::dq_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DQ_SMEM);
     (void)hipFuncSetAttribute((const void*)lwk::bw::dkv_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DKV_SMEM);
-    hipLaunchKernelGGL(lwk::bw::dq_kernel<false>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DQ_SMEM, stream, bp);
-    hipLaunchKernelGGL(lwk::bw::dkv_kernel<false>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DKV_SMEM, stream, bp);
+    hipExtLaunchKernelGGL(lwk::bw::dq_kernel<false>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DQ_SMEM,
+                          stream, ev(1, 0), ev(1, 1), 0u, bp);
+    hipExtLaunchKernelGGL(lwk::bw::dkv_kernel<false>, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::bw::DKV_SMEM,
+                          stream, ev(4, 0), ev(4, 1), 0u, bp);
   }
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  if (timed) ++p->bw_calls;
   return LWATTN_OK;
 }
 
@@ -515,17 +540,26 @@ lwattn_status lwattn_timing_enable(lwattn_plan_t p, int32_t max_calls) {
   if (!p || max_calls <= 0) return LWATTN_E_INVALID;
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->bw_events) (void)hipEventDestroy(e);
   p->events.clear();
+  p->bw_events.clear();
   p->timing_cap = 0;
   p->timing_calls = 0;
   p->timing_seen = 0;
-  const size_t ne = (size_t)max_calls * (kNumKernels + 1);
-  p->events.reserve(ne);
-  for (size_t i = 0; i < ne; ++i) {
-    hipEvent_t e;
-    if (!hip_ok(hipEventCreate(&e), "hipEventCreate")) return LWATTN_E_DEVICE;
-    p->events.push_back(e);
-  }
+  p->bw_calls = 0;
+  p->bw_seen = 0;
+  auto make = [&](std::vector<hipEvent_t>& v, size_t ne) {
+    v.reserve(ne);
+    for (size_t i = 0; i < ne; ++i) {
+      hipEvent_t e;
+      if (!hip_ok(hipEventCreate(&e), "hipEventCreate")) return false;
+      v.push_back(e);
+    }
+    return true;
+  };
+  if (!make(p->events, (size_t)max_calls * (kNumKernels + 1)) ||
+      !make(p->bw_events, (size_t)max_calls * 2 * kNumBwKernels))
+    return LWATTN_E_DEVICE;
   p->timing_cap = max_calls;
   return LWATTN_OK;
 }
@@ -534,6 +568,7 @@ lwattn_status lwattn_timing_every(lwattn_plan_t p, int32_t every) {
   if (!p || every < 1) return LWATTN_E_INVALID;
   p->timing_every = every;
   p->timing_seen = 0;
+  p->bw_seen = 0;
   return LWATTN_OK;
 }
 
@@ -567,9 +602,36 @@ lwattn_status lwattn_timing_disable(lwattn_plan_t p) {
   if (!p) return LWATTN_E_INVALID;
   (void)hipSetDevice(p->device);
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->bw_events) (void)hipEventDestroy(e);
   p->events.clear();
+  p->bw_events.clear();
   p->timing_cap = 0;
   p->timing_calls = 0;
+  p->bw_calls = 0;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_timing_read_backward(lwattn_plan_t p, float* ms, int32_t cap, int32_t* nkernels,
+                                          int32_t* ncalls) {
+  if (!p || !nkernels || !ncalls || (cap > 0 && !ms)) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  float tot[kNumBwKernels] = {};
+  for (int call = 0; call < p->bw_calls; ++call) {
+    hipEvent_t* ev = &p->bw_events[(size_t)call * 2 * kNumBwKernels];
+    // the dK/dV kernel ends every backward
+    if (!hip_ok(hipEventSynchronize(ev[2 * kNumBwKernels - 1]), "hipEventSynchronize")) return LWATTN_E_DEVICE;
+    for (int k = 0; k < kNumBwKernels; ++k) {
+      float t = 0.f;
+      // a kernel the call did not launch left its pair unrecorded: both are
+      // then the pair's last recording or never recorded, and count as zero
+      hipError_t e = hipEventElapsedTime(&t, ev[2 * k], ev[2 * k + 1]);
+      if (e != hipSuccess) t = 0.f;
+      tot[k] += t;
+    }
+  }
+  for (int k = 0; k < kNumBwKernels && k < cap; ++k) ms[k] = tot[k];
+  *nkernels = kNumBwKernels;
+  *ncalls = p->bw_calls;
   return LWATTN_OK;
 }
 

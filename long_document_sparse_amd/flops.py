@@ -80,6 +80,27 @@ def hbm_bytes(lmask, gmask, H: int, d: int, elt: int) -> int:
     return total
 
 
+def local_global_key_pairs(lmask, gmask, H: int) -> int:
+    """Pairs of local rows with global keys (every local row sees every global key)."""
+    v, g = _flags(lmask, gmask)
+    return int(H * (((v & ~g).sum(axis=1)) * g.sum(axis=1)).sum())
+
+
+def backward_kernel_flops(lmask, gmask, window: int, dilation: Sequence[int], d: int) -> dict:
+    """Matrix FLOPs each bf16 backward kernel needs for what it writes, 2 d per
+    product and pair: dq_kernel S, dP, dQ over the local rows' pairs;
+    global_chunk_kernel S, dP, dQg over the global rows' pairs and S, dP, dK, dV
+    over the local rows' pairs with global keys; dkv_kernel S, dP, dK, dV over
+    the window pairs and S, dP, dKg, dVg over the global rows' pairs."""
+    H = len(dilation)
+    allp = pairs(lmask, gmask, window, dilation)
+    gp = global_pairs(lmask, gmask, H)
+    lg = local_global_key_pairs(lmask, gmask, H)
+    win = allp - gp - lg
+    return {"dq_kernel": 6 * d * (win + lg), "global_chunk_kernel": 6 * d * gp + 8 * d * lg,
+            "global_merge_kernel": 0, "compact_kernel": 0, "dkv_kernel": 8 * d * (win + gp)}
+
+
 def backward_flops(lmask, gmask, window: int, dilation: Sequence[int], d: int) -> int:
     """Algorithmic FLOPs of the backward: per allowed pair, the five d-long
     products of the chain rule (the score q.k, dP = dO.v, and the dq, dk, dv

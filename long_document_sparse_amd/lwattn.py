@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(PKG, "liblwattn.so")
 LWATTN_F32, LWATTN_BF16 = 0, 1
 OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_DEVICE, E_TOO_MANY_GLOBALS = range(6)
 KERNELS = ("attention",)
+# kernel slots of lwattn_timing_read_backward
+BW_KERNELS = ("compact_kernel", "dq_kernel", "global_chunk_kernel", "global_merge_kernel", "dkv_kernel")
 
 # (name, restype, argtypes) of every exported function, in header order
 _c_p = ctypes.c_void_p
@@ -46,6 +48,8 @@ SIGNATURES = [
     ("lwattn_timing_every", ctypes.c_int, [_c_p, _i32]),
     ("lwattn_timing_read", ctypes.c_int, [_c_p, ctypes.POINTER(ctypes.c_float), _i32,
                                           ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    ("lwattn_timing_read_backward", ctypes.c_int, [_c_p, ctypes.POINTER(ctypes.c_float), _i32,
+                                                   ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     ("lwattn_timing_disable", ctypes.c_int, [_c_p]),
     ("lwattn_test_inject_wait_timeout", ctypes.c_int, [_c_p]),
     ("lwattn_strerror", ctypes.c_char_p, [ctypes.c_int]),
@@ -275,6 +279,16 @@ class Plan:
         if st != OK:
             raise LwattnError(st, "lwattn_timing_read")
         return {KERNELS[i]: float(ms[i]) for i in range(nk.value)}, int(nc.value)
+
+    def timing_read_backward(self):
+        """({kernel: total ms}, calls) over the backwards recorded since timing_enable
+        (kernels a call did not launch count zero)."""
+        ms = (ctypes.c_float * 8)()
+        nk, nc = _i32(), _i32()
+        st = self.lib.lwattn_timing_read_backward(self.handle, ms, 8, ctypes.byref(nk), ctypes.byref(nc))
+        if st != OK:
+            raise LwattnError(st, "lwattn_timing_read_backward")
+        return {BW_KERNELS[i]: float(ms[i]) for i in range(nk.value)}, int(nc.value)
 
     def timing_disable(self):
         self.lib.lwattn_timing_disable(self.handle)

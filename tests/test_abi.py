@@ -83,6 +83,7 @@ def test_null_config_and_plan_arguments_are_rejected():
     assert lib.lwattn_timing_disable(None) == lw.E_INVALID
     nk, nc = ctypes.c_int32(), ctypes.c_int32()
     assert lib.lwattn_timing_read(None, None, 0, ctypes.byref(nk), ctypes.byref(nc)) == lw.E_INVALID
+    assert lib.lwattn_timing_read_backward(None, None, 0, ctypes.byref(nk), ctypes.byref(nc)) == lw.E_INVALID
     cfg, keep = lw.make_config(**BASE)
     assert lib.lwattn_plan(ctypes.byref(cfg), 0, None) == lw.E_INVALID
 

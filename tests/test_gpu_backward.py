@@ -2,11 +2,14 @@
 oracle's backward, element by element over all six gradients.
 
 Tolerance, derived from the arithmetic: both sides see the same stored inputs;
-the HIP path computes in fp32 (scores, exp, every sum over up to n rows or keys)
-and rounds the gradients to the storage type, the oracle in fp64.  Per tensor,
-relative to its largest entry: fp32 storage |err| <= 1e-4 * max |g|; bf16
-storage (output rounding alone is 2^-9 relative) |err| <= 2e-2 * max |g|.  A
-tensor that no path reaches must be exactly zero.
+the HIP path accumulates in fp32 (scores, exp, every sum over up to n rows or
+keys) and rounds the gradients to the storage type, the oracle works in fp64.
+With bf16 storage the matrix cores also take P and dS rounded to bf16 (2^-9
+relative per term, of either sign, so a sum of k terms drifts by about
+2^-9 sqrt(k) of its scale) and the gradients are rounded to bf16 (2^-9).  Per
+tensor, relative to its largest entry: fp32 storage |err| <= 1e-4 * max |g|;
+bf16 storage |err| <= 2e-2 * max |g|.  A tensor that no path reaches must be
+exactly zero.
 """
 import numpy as np
 import pytest
@@ -30,6 +33,9 @@ CASES = [
     (2, 2, 130, 400, "bf16", [0, 0], 3, "first", "none", 0),             # window > n
     (1, 2, 257, 16, "f32", [1, 4], 0, "first", "scatter", 40),           # no globals, scattered pads
     (1, 1, 65, 8, "bf16", [0], 65, "first", "none", 0),                  # every token global
+    (1, 3, 300, 128, "bf16", [0, 1, 3], 70, "random", "per_batch", 60),  # matrix cores: two global tiles
+    (1, 2, 257, 16, "bf16", [1, 4], 0, "first", "scatter", 40),          # no globals, scattered pads
+    (2, 2, 1000, 256, "bf16", [0, 1], 3, "random", "per_batch", 200),    # interior and edge tiles, pads
 ]
 
 
@@ -91,3 +97,29 @@ def test_backward_base_size_bf16():
         say(f"base {name}: max abs err {err:.3e}, max |g| {ref:.3e}")
         assert np.all(np.isfinite(got))
         assert err <= TOL["bf16"] * ref, name
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_kernel_timing(dtype):
+    """lwattn_timing_read_backward: every launched kernel slot has time, the
+    slots a storage type does not launch have none."""
+    spec = workloads.custom(1, 2, 512, 64, 128, dtype, [0, 1], seed=5, n_global=3)
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec, max_global=4)
+    o = torch.empty_like(ts[0])
+    plan(*ts, lm, gm, out=o)
+    go = torch.from_numpy(_grad_out(x, 4)).to(ts[0].device).to(ts[0].dtype)
+    grads = tuple(torch.empty_like(ts[0]) for _ in range(6))
+    plan.timing_enable(4)
+    for _ in range(3):
+        plan.backward(*ts, lm, gm, o, go, grads=grads)
+    tot, calls = plan.timing_read_backward()
+    plan.timing_disable()
+    assert calls == 3
+    launched = (lw.BW_KERNELS if dtype == "bf16" else ("compact_kernel", "dq_kernel", "dkv_kernel"))
+    for k in lw.BW_KERNELS:
+        if k in launched:
+            assert tot[k] > 0.0, (k, tot)
+        else:
+            assert tot[k] == 0.0, (k, tot)

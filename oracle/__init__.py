@@ -48,6 +48,7 @@ class _Problem(ctypes.Structure):
         ("Q", ctypes.c_void_p), ("K", ctypes.c_void_p), ("V", ctypes.c_void_p),
         ("Qg", ctypes.c_void_p), ("Kg", ctypes.c_void_p), ("Vg", ctypes.c_void_p),
         ("lmask", ctypes.c_void_p), ("gmask", ctypes.c_void_p),
+        ("causal", ctypes.c_int32),
     ]
 
 
@@ -71,6 +72,10 @@ def _load():
                                  ctypes.c_void_p, ctypes.c_int32]
         lib.lwo_rows.restype = ctypes.c_int
         lib.lwo_forward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int32]
+        lib.lwo_allowed_causal.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        lib.lwo_allowed_causal.restype = ctypes.c_int64
         lib.lwo_forward.restype = ctypes.c_int
         lib.lwo_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p] + \
             [ctypes.c_void_p] * 6 + [ctypes.c_int32]
@@ -114,7 +119,7 @@ def allowed(lmask_row, gmask_row, window, gap, i):
 class _Bound:
     """Keeps the float32 copies alive while the C call runs."""
 
-    def __init__(self, Q, K, V, Qg, Kg, Vg, lmask, gmask, window, dilation, scale):
+    def __init__(self, Q, K, V, Qg, Kg, Vg, lmask, gmask, window, dilation, scale, causal=False):
         self.arrs = [_f32(x) for x in (Q, K, V, Qg, Kg, Vg, lmask, gmask)]
         B, H, n, d = self.arrs[0].shape
         for a in self.arrs[1:6]:
@@ -131,7 +136,7 @@ class _Bound:
         self.shape = (B, H, n, d)
         self.p = _Problem(B, H, n, d, int(window),
                           self.gap.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                          float(scale), *[a.ctypes.data for a in self.arrs])
+                          float(scale), *[a.ctypes.data for a in self.arrs], int(bool(causal)))
 
 
 def forward(Q, K, V, Qg, Kg, Vg, lmask, gmask, window, dilation=None, scale=None,
@@ -183,3 +188,45 @@ def backward(Q, K, V, Qg, Kg, Vg, lmask, gmask, dO, window, dilation=None, scale
     if rc:
         raise RuntimeError(f"oracle backward failed ({rc})")
     return tuple(outs)
+
+
+def allowed_causal(lmask_row, window, gap, i):
+    """(kind, keys) of query row i of one batch row in the causal variant."""
+    lm = _f32(lmask_row)
+    n = lm.shape[0]
+    keys = np.empty((max(n, 1),), np.int32)
+    kind = ctypes.c_int32(-1)
+    cnt = _load().lwo_allowed_causal(lm.ctypes.data, n, int(window), int(gap), int(i),
+                                     keys.ctypes.data, ctypes.byref(kind))
+    return kind.value, keys[:cnt].copy()
+
+
+def forward_causal(Q, K, V, lmask, window, dilation=None, scale=None, threads=None):
+    """Causal variant (the window's taps at or before each row, no global
+    attention): every output row, float64 [B,H,n,d]."""
+    d = np.shape(Q)[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    gm = np.zeros_like(_f32(lmask))
+    bound = _Bound(Q, K, V, Q, K, V, lmask, gm, window, dilation, scale, causal=True)
+    out = np.empty(bound.shape, np.float64)
+    rc = _load().lwo_forward(ctypes.byref(bound.p), out.ctypes.data, threads or default_threads())
+    if rc:
+        raise RuntimeError(f"oracle causal forward failed ({rc})")
+    return out
+
+
+def rows_causal(Q, K, V, lmask, window, row_index, dilation=None, scale=None, threads=None):
+    """Selected rows of the causal variant: row_index holds flat (b*H + h)*n + i."""
+    d = np.shape(Q)[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    gm = np.zeros_like(_f32(lmask))
+    bound = _Bound(Q, K, V, Q, K, V, lmask, gm, window, dilation, scale, causal=True)
+    idx = np.ascontiguousarray(row_index, dtype=np.int64)
+    out = np.empty((idx.shape[0], d), np.float64)
+    rc = _load().lwo_rows(ctypes.byref(bound.p), idx.ctypes.data, idx.shape[0],
+                          out.ctypes.data, threads or default_threads())
+    if rc:
+        raise RuntimeError(f"oracle causal rows failed ({rc})")
+    return out

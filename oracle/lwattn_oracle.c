@@ -35,6 +35,14 @@
  *   softmax : two passes -- the maximum over the allowed set, then
  *             p_j = exp(x_j - max) / sum_k exp(x_k - max).
  *
+ * The causal variant (problem.causal != 0) follows the same notes, section
+ * "Implementation": an autoregressive language model uses the dilated sliding
+ * window, with window sizes that may differ from layer to layer, and no global
+ * attention; and "Longformer模型深度解析与应用指南" (bmjup.com), where a local mask
+ * and a causal mask are combined by intersection.  Reading: row i's keys are
+ * the window's taps at or before i, i - k*s for 0 <= k <= w/2, that are
+ * valid; the global mask is not read.
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC (see oracle/__init__.py).
  */
 #include <math.h>
@@ -54,6 +62,7 @@ typedef struct {
   const float *Q, *K, *V, *Qg, *Kg, *Vg; /* [B,H,n,d] */
   const float* lmask;    /* [B,n] */
   const float* gmask;    /* [B,n] */
+  int32_t causal;        /* nonzero: the causal variant (window taps at or before i, no globals) */
 } lwo_problem;
 
 static int is_valid(const float* lm, int64_t j) { return lm[j] != 0.0f; }
@@ -111,6 +120,28 @@ int64_t lwo_allowed(const float* lm, const float* gm, int32_t n, int32_t window,
   return cnt;
 }
 
+/* Causal variant: the valid taps i - k*s, 0 <= k <= w/2, in ascending position
+ * order; 0 keys for a padded row (kind LWO_PADDED), else kind LWO_LOCAL. */
+int64_t lwo_allowed_causal(const float* lm, int32_t n, int32_t window, int32_t gap, int32_t i,
+                           int32_t* keys, int32_t* kind) {
+  int64_t cnt = 0;
+  (void)n;
+  if (!is_valid(lm, i)) {
+    *kind = LWO_PADDED;
+    return 0;
+  }
+  *kind = LWO_LOCAL;
+  const int64_t s = (int64_t)gap + 1;
+  const int64_t r = window / 2;
+  int64_t kmax = (int64_t)i / s;   /* taps at position >= 0 */
+  if (kmax > r) kmax = r;
+  for (int64_t k = kmax; k >= 0; --k) {
+    const int64_t j = (int64_t)i - k * s;
+    if (is_valid(lm, j)) keys[cnt++] = (int32_t)j;
+  }
+  return cnt;
+}
+
 /* One output row (b, h, i) into out[0..d). keys/p are scratch of size n. */
 static void lwo_row(const lwo_problem* p, int32_t b, int32_t h, int32_t i,
                     int32_t* keys, double* prob, double* out) {
@@ -118,7 +149,8 @@ static void lwo_row(const lwo_problem* p, int32_t b, int32_t h, int32_t i,
   const float* lm = p->lmask + (int64_t)b * n;
   const float* gm = p->gmask + (int64_t)b * n;
   int32_t kind;
-  int64_t cnt = lwo_allowed(lm, gm, n, p->window, p->gap[h], i, keys, &kind);
+  int64_t cnt = p->causal ? lwo_allowed_causal(lm, n, p->window, p->gap[h], i, keys, &kind)
+                          : lwo_allowed(lm, gm, n, p->window, p->gap[h], i, keys, &kind);
   for (int32_t c = 0; c < d; ++c) out[c] = 0.0;
   if (kind == LWO_PADDED) return;
 
@@ -228,6 +260,7 @@ int lwo_forward(const lwo_problem* p, double* out, int32_t threads) {
  * task each); within a pair the rows are summed in order. */
 int lwo_backward(const lwo_problem* p, const float* dO, double* dQ, double* dK, double* dV,
                  double* dQg, double* dKg, double* dVg, int32_t threads) {
+  if (p->causal) return 2;   /* the causal variant has no backward here */
   const int32_t n = p->n, d = p->d;
   const int64_t pairs = (int64_t)p->B * p->H;
   const int64_t per = (int64_t)n * d;

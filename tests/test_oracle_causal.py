@@ -1,0 +1,124 @@
+"""Pins of the oracle's causal variant (the dilated sliding window of an
+autoregressive language model: "LongFormer: The Long-Document Transformer"
+notes, section Implementation; a local mask intersected with a causal mask:
+"Longformer模型深度解析与应用指南", xformers mask composition).  Reading: row i
+sees the valid taps i - k*s, 0 <= k <= w/2; no global attention.
+
+Pinned against hand-derived key sets, a dense masked softmax built here from
+the reading, torch's causal scaled_dot_product_attention in float64 where the
+window covers the whole prefix, the Q = 0 closed form, the residue-class
+decomposition of dilated heads, and causality itself (poisoned future rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def test_hand_derived_causal_key_sets():
+    lm = np.ones(10, np.float32)
+    # w = 4 (reach 2), gap 1 (stride 2): row 7 sees 7, 5, 3
+    assert list(oracle.allowed_causal(lm, 4, 1, 7)[1]) == [3, 5, 7]
+    # row 1 sees only itself (1 - 2 < 0)
+    assert list(oracle.allowed_causal(lm, 4, 1, 1)[1]) == [1]
+    # w = 6 (reach 3), stride 1: row 2 sees 0, 1, 2; row 9 sees 6..9
+    assert list(oracle.allowed_causal(lm, 6, 0, 2)[1]) == [0, 1, 2]
+    assert list(oracle.allowed_causal(lm, 6, 0, 9)[1]) == [6, 7, 8, 9]
+    # w = 0: itself only
+    assert list(oracle.allowed_causal(lm, 0, 0, 5)[1]) == [5]
+    # padding at 5 drops the tap; a padded row has no keys (kind 0)
+    lm2 = lm.copy()
+    lm2[5] = 0.0
+    assert list(oracle.allowed_causal(lm2, 4, 1, 7)[1]) == [3, 7]
+    kind, keys = oracle.allowed_causal(lm2, 4, 1, 5)
+    assert kind == 0 and keys.size == 0
+
+
+def _dense_causal(Q, K, V, lm, window, gaps, scale):
+    """Masked softmax attention over an explicit n x n mask built from the reading."""
+    B, H, n, d = Q.shape
+    out = np.zeros((B, H, n, d))
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    for b in range(B):
+        valid = lm[b] != 0
+        for h in range(H):
+            s = gaps[h] + 1
+            diff = i - j
+            mask = (diff >= 0) & (diff % s == 0) & (diff // s <= window // 2)
+            mask &= valid[None, :] & valid[:, None]
+            x = scale * (Q[b, h].astype(np.float64) @ K[b, h].astype(np.float64).T)
+            x = np.where(mask, x, -np.inf)
+            rows = mask.any(axis=1)
+            x[~rows] = 0.0
+            p = np.exp(x - x.max(axis=1, keepdims=True))
+            p = np.where(mask, p, 0.0)
+            p /= np.where(rows, p.sum(axis=1), 1.0)[:, None]
+            out[b, h] = p @ V[b, h].astype(np.float64)
+    return out
+
+
+def _inputs(seed, B, H, n, d, pad=0):
+    rng = np.random.default_rng(seed)
+    Q, K, V = (rng.standard_normal((B, H, n, d)).astype(np.float32) for _ in range(3))
+    lm = np.ones((B, n), np.float32)
+    if pad:
+        for b in range(B):
+            lm[b, rng.choice(n, pad, replace=False)] = 0.0
+    return Q, K, V, lm
+
+
+@pytest.mark.parametrize("window,gaps,pad", [(8, [0, 1, 3], 0), (5, [0, 2], 7), (40, [1], 3), (0, [0], 0)])
+def test_causal_matches_dense_masked_softmax(window, gaps, pad):
+    Q, K, V, lm = _inputs(11, 2, len(gaps), 37, 6, pad)
+    got = oracle.forward_causal(Q, K, V, lm, window, gaps, 0.4, threads=2)
+    want = _dense_causal(Q, K, V, lm, window, gaps, 0.4)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_wide_causal_window_is_causal_sdpa():
+    Q, K, V, lm = _inputs(12, 1, 2, 29, 8)
+    got = oracle.forward_causal(Q, K, V, lm, 2 * 29, [0, 0], 1 / np.sqrt(8), threads=2)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q).double(), torch.from_numpy(K).double(), torch.from_numpy(V).double(),
+        is_causal=True).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_queries_average_the_allowed_values():
+    Q, K, V, lm = _inputs(13, 1, 1, 23, 4, pad=4)
+    Q[:] = 0.0
+    got = oracle.forward_causal(Q, K, V, lm, 6, [1], 0.5, threads=1)
+    for i in range(23):
+        kind, keys = oracle.allowed_causal(lm[0], 6, 1, i)
+        want = V[0, 0, keys].astype(np.float64).mean(axis=0) if keys.size else np.zeros(4)
+        np.testing.assert_allclose(got[0, 0, i], want, rtol=1e-12, atol=1e-14)
+
+
+def test_dilated_head_is_the_plain_causal_window_on_each_residue_class():
+    Q, K, V, lm = _inputs(14, 1, 1, 41, 5, pad=3)
+    s = 3
+    got = oracle.forward_causal(Q, K, V, lm, 6, [s - 1], 0.3, threads=1)
+    for rho in range(s):
+        sub = oracle.forward_causal(Q[:, :, rho::s], K[:, :, rho::s], V[:, :, rho::s],
+                                    lm[:, rho::s], 6, [0], 0.3, threads=1)
+        np.testing.assert_allclose(got[:, :, rho::s], sub, rtol=1e-13, atol=1e-15)
+
+
+def test_future_rows_never_reach_a_row():
+    Q, K, V, lm = _inputs(15, 1, 2, 30, 4)
+    base = oracle.forward_causal(Q, K, V, lm, 10, [0, 1], 0.5, threads=1)
+    cut = 17
+    K2, V2, Q2 = K.copy(), V.copy(), Q.copy()
+    K2[:, :, cut:] = np.nan
+    V2[:, :, cut:] = np.nan
+    Q2[:, :, cut:] = np.nan
+    got = oracle.forward_causal(Q2, K2, V2, lm, 10, [0, 1], 0.5, threads=1)
+    np.testing.assert_array_equal(got[:, :, :cut], base[:, :, :cut])
+
+
+def test_padded_rows_are_zero():
+    Q, K, V, lm = _inputs(16, 1, 1, 20, 4, pad=5)
+    got = oracle.forward_causal(Q, K, V, lm, 6, [0], 0.5, threads=1)
+    assert not np.any(got[0, 0][lm[0] == 0])

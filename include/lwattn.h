@@ -113,6 +113,25 @@ lwattn_status lwattn_forward(lwattn_plan_t plan,
                              const float* local_attn_mask, const float* global_attn_mask,
                              void* O, hipStream_t stream);
 
+/* Causal variant of the window attention ("LongFormer: The Long-Document
+ * Transformer" notes, section Implementation: an autoregressive language model
+ * uses the dilated sliding window, its size chosen per layer, with no global
+ * attention; "Longformer模型深度解析与应用指南": a local mask intersected with a causal
+ * mask).  Row i of head h (stride s = dilation[h] + 1, reach r = window / 2 of
+ * the plan) attends to the taps i - k*s, 0 <= k <= r, whose lmask is nonzero;
+ * softmax of scale <Q_i, K_j> over them, O_i = sum_j p_j V_j; a row with
+ * lmask 0 gets O_i = 0.  The plan's max_global and any global mask play no
+ * part.  Per-layer window sizes: one plan per window size.
+ * Q, K, V, O: [B][H][n][64] bf16, 16-byte aligned, device memory; lmask float32
+ * [B][n], 4-byte aligned.  Every element of O is written.  Enqueued on
+ * `stream` (one kernel launch, no allocation, no host sync); it uses no plan
+ * workspace, so it may overlap other calls of the same plan.
+ * Errors: LWATTN_E_INVALID for a null plan or pointer or a misaligned one;
+ * LWATTN_E_UNSUPPORTED for fp32 storage or n * 128 >= 2^31 - 256;
+ * LWATTN_E_DEVICE if the launch fails. */
+lwattn_status lwattn_forward_causal(lwattn_plan_t plan, const void* Q, const void* K, const void* V,
+                                    const float* lmask, void* O, hipStream_t stream);
+
 /* Enqueues the backward of one forward on `stream` (asynchronous; no
  * allocation, no host sync): the gradients of a loss with respect to Q, K, V,
  * Qg, Kg, Vg, given dO = dLoss/dO.  It differentiates the operation that

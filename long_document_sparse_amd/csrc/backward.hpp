@@ -701,7 +701,8 @@ __device__ void dkv_global_keys(const BwParams& p, int b, int h, int gt, float* 
 
 // Block id of a 64-row block (all residue classes of all heads of a batch row)
 // into (b, h, rho, block within the class).
-__device__ __forceinline__ void decode_block(const BwParams& p, int lb, int& b, int& h, int& rho, int& blk) {
+template <typename P>
+__device__ __forceinline__ void decode_block(const P& p, int lb, int& b, int& h, int& rho, int& blk) {
   b = lb / p.blocks_per_b;
   int rem = lb - b * p.blocks_per_b;
   h = 0;

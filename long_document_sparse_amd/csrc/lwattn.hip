@@ -17,6 +17,7 @@
 
 #include "kernels.hpp"
 #include "backward.hpp"
+#include "causal.hpp"
 #include "lwattn.h"
 
 namespace {
@@ -381,6 +382,42 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
 
   if (timed) ++p->timing_calls;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_forward_causal(lwattn_plan_t p, const void* Q, const void* K, const void* V,
+                                    const float* lmask, void* O, hipStream_t stream) {
+  if (!p) return LWATTN_E_INVALID;
+  const lwattn_config& c = p->cfg;
+  if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
+  if (c.dtype != LWATTN_BF16) return LWATTN_E_UNSUPPORTED;
+  // tiles are read through 32-bit buffer offsets over a head's n rows
+  if ((int64_t)c.n * 128 >= lwk::OOB_OFF) return LWATTN_E_UNSUPPORTED;
+  const void* ptrs[] = {Q, K, V, O};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return LWATTN_E_INVALID;
+  if (!lmask || ((uintptr_t)lmask & 3u)) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  lwk::cz::CzParams cp;
+  cp.Q = (const uint8_t*)Q;
+  cp.K = (const uint8_t*)K;
+  cp.V = (const uint8_t*)V;
+  cp.O = (uint8_t*)O;
+  cp.lmask = lmask;
+  cp.head_stride = p->head_stride;
+  cp.head_blk = p->head_blk64;
+  cp.B = c.B;
+  cp.H = c.H;
+  cp.n = c.n;
+  cp.r = (int)std::min<int64_t>(c.window / 2, c.n);
+  cp.blocks_per_b = p->blocks64_per_b;
+  cp.scale = c.scale;
+  const int64_t grid = (int64_t)c.B * p->blocks64_per_b;
+  if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
+  (void)hipFuncSetAttribute((const void*)lwk::cz::causal_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            lwk::cz::SMEM);
+  hipLaunchKernelGGL(lwk::cz::causal_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::SMEM, stream, cp);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   return LWATTN_OK;
 }
 

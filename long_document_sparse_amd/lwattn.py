@@ -41,6 +41,7 @@ SIGNATURES = [
     ("lwattn_plan", ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_int, ctypes.POINTER(_c_p)]),
     ("lwattn_forward", ctypes.c_int, [_c_p] * 9 + [_c_p, _c_p]),
     ("lwattn_backward", ctypes.c_int, [_c_p] * 17 + [_c_p]),
+    ("lwattn_forward_causal", ctypes.c_int, [_c_p] * 6 + [_c_p]),
     ("lwattn_destroy", ctypes.c_int, [_c_p]),
     ("lwattn_global_index", ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
     ("lwattn_sync_status", ctypes.c_int, [_c_p, _c_p]),
@@ -182,6 +183,31 @@ class Plan:
                                      _stream_handle(stream))
         if st != OK:
             raise LwattnError(st, "lwattn_forward")
+        return out
+
+    def forward_causal(self, q, k, v, lmask, out=None, stream=None):
+        """Enqueue the causal variant (window taps at or before each row, no
+        global attention; bf16 plans); returns O (allocated if `out` is None)."""
+        import torch
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        for t, name in ((q, "q"), (k, "k"), (v, "v")):
+            self._check(t, name, tdt)
+            if tuple(t.shape) != self.shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {self.shape}")
+        B, H, n, d = self.shape
+        self._check(lmask, "local_attn_mask", torch.float32)
+        if tuple(lmask.shape) != (B, n):
+            raise ValueError("local_attn_mask must be [B,n]")
+        if out is None:
+            out = torch.empty(self.shape, dtype=tdt, device=q.device)
+        else:
+            self._check(out, "out", tdt)
+            if tuple(out.shape) != self.shape:
+                raise ValueError("out has the wrong shape")
+        st = self.lib.lwattn_forward_causal(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            lmask.data_ptr(), out.data_ptr(), _stream_handle(stream))
+        if st != OK:
+            raise LwattnError(st, "lwattn_forward_causal")
         return out
 
     def backward(self, q, k, v, qg, kg, vg, lmask, gmask, o, do, grads=None, stream=None):

@@ -80,10 +80,16 @@ def named(name: str) -> Spec:
         return Spec("long", 8, 16, 16384, 64, 1024, "bf16", [0] * 16, seed=5, max_global=128,
                     global_mode="random", n_global=128, pad_mode="one_seq", pad_lo=1, pad_hi=4096,
                     k_boost_frac=0.01)
+    if name == "charlm":
+        # causal variant (an autoregressive character model's attention): no
+        # global tokens, no padding, two dilated heads
+        return Spec("charlm", 2, 12, 8192, 64, 512, "bf16", [0] * 10 + [1] * 2, seed=6, max_global=0,
+                    global_mode="first", n_global=0)
     raise KeyError(name)
 
 
 NAMES = ("tiny", "base", "qa", "dilated", "long")
+CAUSAL_NAMES = ("charlm",)
 
 
 @dataclasses.dataclass

@@ -155,6 +155,91 @@ def cpu_baseline_backward(x, go, budget_s=12.0):
             "sample": f"the whole backward, repeated {reps} times ({t:.2f} s)"}
 
 
+def cpu_baseline_causal(x, budget_s=12.0):
+    """The oracle's causal forward, as it is, on the host cores, repeated over
+    the whole problem for about budget_s seconds."""
+    import oracle
+    spec = x.spec
+    threads = oracle.default_threads()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    reps, t = 0, 0.0
+    while t < budget_s:
+        t0 = time.perf_counter()
+        oracle.forward_causal(x.Q, x.K, x.V, x.lmask, spec.window, spec.dilation, spec.scale,
+                              threads=threads)
+        t += time.perf_counter() - t0
+        reps += 1
+    value = spec.B * spec.n * reps / t
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole causal forward, repeated {reps} times ({t:.2f} s)"}
+
+
+def run_causal(args, spec, x, ts, lm, plan):
+    """--pass causal: one JSON line for lwattn_forward_causal (one kernel a call)."""
+    import ctypes
+    import torch
+    from long_document_sparse_amd import flops as fl
+    from long_document_sparse_amd import lwattn
+    if spec.dtype != "bf16":
+        raise SystemExit("the causal variant runs on bf16 storage")
+    q, k, v = ts[0], ts[1], ts[2]
+    o = torch.empty_like(q)
+    plan.forward_causal(q, k, v, lm, out=o)
+    fn = plan.lib.lwattn_forward_causal
+    cargs = (plan.handle,) + tuple(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, lm, o)) + (None,)
+
+    def step():
+        st = fn(*cargs)
+        if st != lwattn.OK:
+            raise SystemExit(f"causal forward failed: {lwattn.strerror(st)}")
+
+    for _ in range(args.warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_call = e0.elapsed_time(e1) * 1e-3 / args.steps        # s per launch, on the stream
+    pairs = fl.causal_pairs(x.lmask, spec.window, spec.dilation)
+    flop = 4 * spec.d * pairs                                 # S and P V, 2 d per product and pair
+    achieved = flop / t_call / 1e12
+    tokens = spec.B * spec.n
+    res = {
+        "metric": "causal dilated window attn fwd tokens/s, n=8192 w=512",
+        "value": round(tokens / (elapsed / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded, N(0,1)/sqrt(d) inputs; no dataset)",
+        "config": {"workload": describe(spec) + "; causal", "global_batch": spec.B, "seq_len": spec.n,
+                   "heads": spec.H, "head_dim": spec.d, "window": spec.window,
+                   "parallelism": "single GPU", "timing": "warm (back to back)"},
+        "us_per_launch_on_stream": round(t_call * 1e6, 2),
+        "algorithmic_pairs": pairs,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_MFMA,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_MFMA, 4), "traffic": None,
+                     "kernel": "causal_kernel", "algorithmic_flop": flop,
+                     "source_sha256": source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_causal(x)
+    plan.close()
+    print(json.dumps(res), flush=True)
+
+
 def run_backward(args, spec, x, ts, lm, gm, plan):
     """--pass backward: one JSON line for lwattn_backward."""
     import numpy as np
@@ -248,11 +333,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="base")
+    ap.add_argument("--workload", default=None,
+                    help="named workload (default: base; charlm for --pass causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel HIP events (roofline fields become null)")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal"), default="forward",
                     help="time the forward (default) or the backward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device to device 5 times (counter calibration)")
@@ -267,6 +353,8 @@ def main():
     from long_document_sparse_amd import flops as fl
     from long_document_sparse_amd import lwattn, workloads
 
+    if args.workload is None:
+        args.workload = "charlm" if args.which == "causal" else "base"
     spec = workloads.named(args.workload)
     x = workloads.generate(spec)
     dev = torch.device("cuda", 0)
@@ -279,6 +367,9 @@ def main():
                        spec.max_global, spec.scale, spec.dtype)
     if args.which == "backward":
         run_backward(args, spec, x, ts, lm, gm, plan)
+        return
+    if args.which == "causal":
+        run_causal(args, spec, x, ts, lm, plan)
         return
 
     # the buffers are validated and the call marshalled once; every step

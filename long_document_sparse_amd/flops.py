@@ -80,6 +80,25 @@ def hbm_bytes(lmask, gmask, H: int, d: int, elt: int) -> int:
     return total
 
 
+def causal_pairs(lmask, window: int, dilation: Sequence[int]) -> int:
+    """Allowed pairs of the causal variant: each valid row with its valid taps
+    i - k s, 0 <= k <= window // 2."""
+    lm = np.asarray(lmask) != 0
+    B, n = lm.shape
+    r = window // 2
+    total = 0
+    for b in range(B):
+        for gap in dilation:
+            s = int(gap) + 1
+            for rho in range(min(s, n)):
+                sub = lm[b, rho::s].astype(np.int64)
+                pre = np.concatenate([[0], np.cumsum(sub)])
+                t = np.arange(sub.shape[0])
+                cnt = pre[t + 1] - pre[np.maximum(t - r, 0)]
+                total += int((cnt * sub).sum())
+    return total
+
+
 def local_global_key_pairs(lmask, gmask, H: int) -> int:
     """Pairs of local rows with global keys (every local row sees every global key)."""
     v, g = _flags(lmask, gmask)

@@ -122,3 +122,12 @@ def test_padded_rows_are_zero():
     Q, K, V, lm = _inputs(16, 1, 1, 20, 4, pad=5)
     got = oracle.forward_causal(Q, K, V, lm, 6, [0], 0.5, threads=1)
     assert not np.any(got[0, 0][lm[0] == 0])
+
+
+def test_causal_pair_counter_matches_the_oracle_key_sets():
+    from long_document_sparse_amd import flops
+    rng = np.random.default_rng(17)
+    lm = (rng.random((2, 50)) > 0.2).astype(np.float32)
+    total = sum(oracle.allowed_causal(lm[b], 10, gap, i)[1].size
+                for b in range(2) for gap in (0, 2) for i in range(50))
+    assert flops.causal_pairs(lm, 10, [0, 2]) == total

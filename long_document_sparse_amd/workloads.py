@@ -180,3 +180,42 @@ def custom(B: int, H: int, n: int, d: int = 64, window: int = 128, dtype: str = 
                 max_global=max_global if max_global is not None else max(n_global, 1),
                 global_mode=global_mode, n_global=n_global, pad_mode=pad_mode,
                 pad_lo=pad_lo, pad_hi=pad_hi, k_boost_frac=k_boost_frac)
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse layouts over 64 x 64 blocks of the score matrix (xFormers'
+# attention-mask notes build such layouts per head with block_size 64).  A
+# synthetic stand-in for a "fixed" layout: every query block sees its own
+# block and the `local` - 1 blocks before it, plus `extra` other key blocks
+# drawn per head and query block (at or before it when causal).
+
+BS_BLOCK = 64
+
+
+def blocksparse_layout(H: int, n: int, seed: int, local: int = 4, extra: int = 4,
+                       causal: bool = False) -> np.ndarray:
+    """uint8 [H, nb, nb] layout, nb = ceil(n / 64)."""
+    rng = np.random.default_rng(seed)
+    nb = (n + BS_BLOCK - 1) // BS_BLOCK
+    lay = np.zeros((H, nb, nb), np.uint8)
+    for h in range(H):
+        for qb in range(nb):
+            lay[h, qb, max(0, qb - local + 1):qb + 1] = 1
+            hi = qb + 1 if causal else nb
+            if extra > 0 and hi > 0:
+                lay[h, qb, rng.choice(hi, min(extra, hi), replace=False)] = 1
+    return lay
+
+
+def layout_csr(layout) -> tuple:
+    """(rowptr int32 [H*nb + 1], cols int32 [nnz]) of a [H, nb, nb] layout:
+    the key blocks of query block qb of head h are cols[rowptr[h*nb + qb] ..
+    rowptr[h*nb + qb + 1]), ascending."""
+    lay = np.asarray(layout) != 0
+    H, nb, _ = lay.shape
+    flat = lay.reshape(H * nb, nb)
+    counts = flat.sum(axis=1)
+    rowptr = np.zeros(H * nb + 1, np.int32)
+    np.cumsum(counts, out=rowptr[1:])
+    cols = np.nonzero(flat)[1].astype(np.int32)
+    return rowptr, cols

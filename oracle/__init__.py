@@ -77,6 +77,10 @@ def _load():
                                            ctypes.c_void_p]
         lib.lwo_allowed_causal.restype = ctypes.c_int64
         lib.lwo_forward.restype = ctypes.c_int
+        lib.lwo_rows_blocksparse.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_double] + \
+            [ctypes.c_void_p] * 5 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int32]
+        lib.lwo_rows_blocksparse.restype = ctypes.c_int
         lib.lwo_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p] + \
             [ctypes.c_void_p] * 6 + [ctypes.c_int32]
         lib.lwo_backward.restype = ctypes.c_int
@@ -230,3 +234,36 @@ def rows_causal(Q, K, V, lmask, window, row_index, dilation=None, scale=None, th
     if rc:
         raise RuntimeError(f"oracle causal rows failed ({rc})")
     return out
+
+
+def rows_blocksparse(Q, K, V, lmask, layout, row_index, causal=False, scale=None, threads=None):
+    """Selected rows of block-sparse attention (layout: uint8/bool [H, nb, nb]
+    over 64-blocks, nb = ceil(n/64); row_index holds flat (b*H + h)*n + i),
+    float64 [len, d]."""
+    Qf, Kf, Vf = (_f32(x) for x in (Q, K, V))
+    B, H, n, d = Qf.shape
+    if Kf.shape != Qf.shape or Vf.shape != Qf.shape:
+        raise ValueError("Q, K, V must share the shape [B,H,n,d]")
+    lm = _f32(lmask)
+    nb = (n + 63) // 64
+    lay = np.ascontiguousarray(np.asarray(layout) != 0, dtype=np.uint8)
+    if lay.shape != (H, nb, nb):
+        raise ValueError(f"layout must be [H, {nb}, {nb}]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    idx = np.ascontiguousarray(row_index, dtype=np.int64)
+    out = np.empty((idx.shape[0], d), np.float64)
+    rc = _load().lwo_rows_blocksparse(B, H, n, d, float(scale), Qf.ctypes.data, Kf.ctypes.data,
+                                      Vf.ctypes.data, lm.ctypes.data, lay.ctypes.data, int(bool(causal)),
+                                      idx.ctypes.data, idx.shape[0], out.ctypes.data,
+                                      threads or default_threads())
+    if rc:
+        raise RuntimeError(f"oracle block-sparse rows failed ({rc})")
+    return out
+
+
+def forward_blocksparse(Q, K, V, lmask, layout, causal=False, scale=None, threads=None):
+    """Every output row of block-sparse attention, float64 [B,H,n,d]."""
+    B, H, n, d = np.shape(Q)
+    out = rows_blocksparse(Q, K, V, lmask, layout, np.arange(B * H * n), causal, scale, threads)
+    return out.reshape(B, H, n, d)

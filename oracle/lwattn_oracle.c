@@ -43,6 +43,13 @@
  * the window's taps at or before i, i - k*s for 0 <= k <= w/2, that are
  * valid; the global mask is not read.
  *
+ * Block-sparse layouts (lwo_rows_blocksparse) follow xFormers' attention-mask
+ * notes (gitcode xformers page): a per-head layout over 64 x 64 blocks of the
+ * score matrix says which query block sees which key block, and masks compose
+ * by intersection (a layout and a causal mask).  Reading: row i of head h sees
+ * key j when layout[h][i/64][j/64] is set, j is valid, and (causal) j <= i; a
+ * padded row, or a row that sees no key, has output zero.
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC (see oracle/__init__.py).
  */
 #include <math.h>
@@ -337,6 +344,67 @@ int lwo_backward(const lwo_problem* p, const float* dO, double* dQ, double* dK, 
     free(keys);
     free(prob);
     free(dx);
+  }
+  return err;
+}
+
+/* Block-sparse layout: rows[t] is the flat index (b*H + h)*n + i; out is
+ * [nrows, d].  layout is uint8 [H][nb][nb], nb = ceil(n / 64). */
+int lwo_rows_blocksparse(int32_t B, int32_t H, int32_t n, int32_t d, double scale, const float* Q,
+                         const float* K, const float* V, const float* lmask, const uint8_t* layout,
+                         int32_t causal, const int64_t* rows, int64_t nrows, double* out,
+                         int32_t threads) {
+  const int64_t nb = ((int64_t)n + 63) / 64;
+  if (threads < 1) threads = 1;
+  int err = 0;
+#pragma omp parallel num_threads(threads)
+  {
+    int32_t* keys = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+    double* prob = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    if (!keys || !prob) {
+#pragma omp atomic write
+      err = 1;
+    } else {
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t f = rows[t];
+        const int32_t i = (int32_t)(f % n);
+        const int64_t bh = f / n;
+        const int32_t b = (int32_t)(bh / H), h = (int32_t)(bh % H);
+        const float* lm = lmask + (int64_t)b * n;
+        double* o = out + t * d;
+        for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+        if (!is_valid(lm, i)) continue;
+        /* the allowed keys */
+        int64_t cnt = 0;
+        const uint8_t* lrow = layout + ((int64_t)h * nb + i / 64) * nb;
+        for (int32_t j = 0; j < n; ++j)
+          if (lrow[j / 64] && is_valid(lm, j) && (!causal || j <= i)) keys[cnt++] = j;
+        if (cnt == 0) continue;
+        const int64_t head = bh * (int64_t)n * d;
+        const float* q = Q + head + (int64_t)i * d;
+        double mx = -INFINITY;
+        for (int64_t u = 0; u < cnt; ++u) {
+          const float* kr = K + head + (int64_t)keys[u] * d;
+          double dot = 0.0;
+          for (int32_t c = 0; c < d; ++c) dot += (double)q[c] * (double)kr[c];
+          prob[u] = scale * dot;
+          if (prob[u] > mx) mx = prob[u];
+        }
+        double sum = 0.0;
+        for (int64_t u = 0; u < cnt; ++u) {
+          prob[u] = exp(prob[u] - mx);
+          sum += prob[u];
+        }
+        for (int64_t u = 0; u < cnt; ++u) {
+          const float* vr = V + head + (int64_t)keys[u] * d;
+          const double pu = prob[u] / sum;
+          for (int32_t c = 0; c < d; ++c) o[c] += pu * (double)vr[c];
+        }
+      }
+    }
+    free(keys);
+    free(prob);
   }
   return err;
 }

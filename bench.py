@@ -240,6 +240,104 @@ def run_causal(args, spec, x, ts, lm, plan):
     print(json.dumps(res), flush=True)
 
 
+def cpu_baseline_blocksparse(x, layout, causal, budget_s=12.0):
+    """The oracle's block-sparse rows, as they are, on the host cores: a
+    random sample of rows, grown until about budget_s seconds, scaled to
+    tokens/s (a token is all H heads' rows)."""
+    import numpy as np
+    import oracle
+    spec = x.spec
+    threads = oracle.default_threads()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    rng = np.random.default_rng(0)
+    total = spec.B * spec.H * spec.n
+    count, t, rows = 2048, 0.0, 0
+    while t < budget_s:
+        idx = rng.choice(total, min(count, total), replace=False)
+        t0 = time.perf_counter()
+        oracle.rows_blocksparse(x.Q, x.K, x.V, x.lmask, layout, idx, causal, spec.scale, threads=threads)
+        t += time.perf_counter() - t0
+        rows += idx.size
+        count *= 2
+    value = rows / spec.H / t
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} random rows of all heads ({t:.2f} s), scaled by 1/H to tokens"}
+
+
+def run_blocksparse(args, spec, x, ts, lm, plan):
+    """--pass blocksparse: one JSON line for lwattn_forward_blocksparse."""
+    import ctypes
+    import torch
+    from long_document_sparse_amd import flops as fl
+    from long_document_sparse_amd import lwattn, workloads
+    if spec.dtype != "bf16":
+        raise SystemExit("block-sparse attention runs on bf16 storage")
+    kw = workloads.BSPARSE_LAYOUT
+    layout = workloads.blocksparse_layout(spec.H, spec.n, seed=spec.seed, **kw)
+    rowptr, cols = workloads.layout_csr(layout)
+    rp = torch.from_numpy(rowptr).to(ts[0].device)
+    cl = torch.from_numpy(cols).to(ts[0].device)
+    q, k, v = ts[0], ts[1], ts[2]
+    o = torch.empty_like(q)
+    plan.forward_blocksparse(q, k, v, lm, rp, cl, causal=kw["causal"], out=o)
+    fn = plan.lib.lwattn_forward_blocksparse
+    cargs = (plan.handle,) + tuple(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, lm, rp, cl)) + \
+        (int(kw["causal"]), ctypes.c_void_p(o.data_ptr()), None)
+
+    def step():
+        st = fn(*cargs)
+        if st != lwattn.OK:
+            raise SystemExit(f"block-sparse forward failed: {lwattn.strerror(st)}")
+
+    for _ in range(args.warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_call = e0.elapsed_time(e1) * 1e-3 / args.steps
+    pairs = fl.blocksparse_pairs(x.lmask, layout, kw["causal"])
+    flop = 4 * spec.d * pairs
+    achieved = flop / t_call / 1e12
+    tokens = spec.B * spec.n
+    res = {
+        "metric": "block-sparse (64-block layout) attn fwd tokens/s, n=16384",
+        "value": round(tokens / (elapsed / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded, N(0,1)/sqrt(d) inputs, seeded layout; no dataset)",
+        "config": {"workload": (f"{spec.name}: B={spec.B} H={spec.H} n={spec.n} d={spec.d} bf16; layout "
+                                f"own + {kw['local'] - 1} previous + {kw['extra']} drawn key blocks per query "
+                                f"block{' (causal)' if kw['causal'] else ''}; {cols.size} blocks listed"),
+                   "global_batch": spec.B, "seq_len": spec.n, "heads": spec.H, "head_dim": spec.d,
+                   "parallelism": "single GPU", "timing": "warm (back to back)"},
+        "us_per_launch_on_stream": round(t_call * 1e6, 2),
+        "algorithmic_pairs": pairs,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_MFMA,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_MFMA, 4), "traffic": None,
+                     "kernel": "blocksparse_kernel", "algorithmic_flop": flop,
+                     "source_sha256": source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_blocksparse(x, layout, kw["causal"])
+    plan.close()
+    print(json.dumps(res), flush=True)
+
+
 def run_backward(args, spec, x, ts, lm, gm, plan):
     """--pass backward: one JSON line for lwattn_backward."""
     import numpy as np
@@ -338,7 +436,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel HIP events (roofline fields become null)")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal"), default="forward",
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal", "blocksparse"), default="forward",
                     help="time the forward (default) or the backward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device to device 5 times (counter calibration)")
@@ -354,7 +452,7 @@ def main():
     from long_document_sparse_amd import lwattn, workloads
 
     if args.workload is None:
-        args.workload = "charlm" if args.which == "causal" else "base"
+        args.workload = {"causal": "charlm", "blocksparse": "bsparse"}.get(args.which, "base")
     spec = workloads.named(args.workload)
     x = workloads.generate(spec)
     dev = torch.device("cuda", 0)
@@ -370,6 +468,9 @@ def main():
         return
     if args.which == "causal":
         run_causal(args, spec, x, ts, lm, plan)
+        return
+    if args.which == "blocksparse":
+        run_blocksparse(args, spec, x, ts, lm, plan)
         return
 
     # the buffers are validated and the call marshalled once; every step

@@ -132,6 +132,30 @@ lwattn_status lwattn_forward(lwattn_plan_t plan,
 lwattn_status lwattn_forward_causal(lwattn_plan_t plan, const void* Q, const void* K, const void* V,
                                     const float* lmask, void* O, hipStream_t stream);
 
+/* Block-sparse attention over 64 x 64 blocks (xFormers' attention-mask notes:
+ * a per-head layout over 64 x 64 blocks of the score matrix with block size
+ * 64, and masks that compose by intersection, as a layout with a causal mask).
+ * Row i of head h attends to key j when the layout holds block (i / 64,
+ * j / 64) for h, lmask[b][j] != 0 and, if `causal` is nonzero, j <= i;
+ * softmax of scale <Q_i, K_j> over those keys, O_i = sum_j p_j V_j.  A row with
+ * lmask 0, or one that sees no key, gets O_i = 0.  The plan gives B, H, n,
+ * scale and the storage type; its window, dilation and max_global play no part.
+ * Layout, CSR over (head, query block), device memory, int32, 4-byte aligned:
+ * the key blocks of query block qb of head h are cols[rowptr[h*nb + qb] ..
+ * rowptr[h*nb + qb + 1]) with nb = ceil(n / 64); rowptr has H*nb + 1 entries.
+ * Each listed key block is visited once per listing (list a block once); a
+ * block index outside [0, nb) contributes no key; a list longer than nb is cut
+ * to its first nb entries.  Q, K, V, O: [B][H][n][64] bf16, 16-byte aligned;
+ * lmask float32 [B][n].  Every element of O is written.  One kernel launch on
+ * `stream`, no allocation, no host sync, no plan workspace.
+ * Errors: LWATTN_E_INVALID for a null plan or pointer or a misaligned one;
+ * LWATTN_E_UNSUPPORTED for fp32 storage, n * 128 >= 2^31 - 256 or
+ * nb > 4096; LWATTN_E_DEVICE if the launch fails. */
+lwattn_status lwattn_forward_blocksparse(lwattn_plan_t plan, const void* Q, const void* K,
+                                         const void* V, const float* lmask, const int32_t* rowptr,
+                                         const int32_t* cols, int32_t causal, void* O,
+                                         hipStream_t stream);
+
 /* Enqueues the backward of one forward on `stream` (asynchronous; no
  * allocation, no host sync): the gradients of a loss with respect to Q, K, V,
  * Qg, Kg, Vg, given dO = dLoss/dO.  It differentiates the operation that

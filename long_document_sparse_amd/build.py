@@ -10,6 +10,7 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "lwattn.hip")
 DEPS = [SRC, os.path.join(PKG, "csrc", "kernels.hpp"), os.path.join(PKG, "csrc", "backward.hpp"),
         os.path.join(PKG, "csrc", "causal.hpp"),
+        os.path.join(PKG, "csrc", "blocksparse.hpp"),
         os.path.join(ROOT, "include", "lwattn.h")]
 LIB = os.path.join(PKG, "liblwattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

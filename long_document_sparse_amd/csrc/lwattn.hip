@@ -18,6 +18,7 @@
 #include "kernels.hpp"
 #include "backward.hpp"
 #include "causal.hpp"
+#include "blocksparse.hpp"
 #include "lwattn.h"
 
 namespace {
@@ -417,6 +418,48 @@ lwattn_status lwattn_forward_causal(lwattn_plan_t p, const void* Q, const void* 
   (void)hipFuncSetAttribute((const void*)lwk::cz::causal_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             lwk::cz::SMEM);
   hipLaunchKernelGGL(lwk::cz::causal_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::SMEM, stream, cp);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_forward_blocksparse(lwattn_plan_t p, const void* Q, const void* K, const void* V,
+                                         const float* lmask, const int32_t* rowptr, const int32_t* cols,
+                                         int32_t causal, void* O, hipStream_t stream) {
+  if (!p) return LWATTN_E_INVALID;
+  const lwattn_config& c = p->cfg;
+  if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
+  if (c.dtype != LWATTN_BF16) return LWATTN_E_UNSUPPORTED;
+  // tiles are read through 32-bit buffer offsets over a head's n rows; the
+  // column list of a query block lives in LDS
+  const int64_t nb = ((int64_t)c.n + 63) / 64;
+  if ((int64_t)c.n * 128 >= lwk::OOB_OFF || nb > 4096) return LWATTN_E_UNSUPPORTED;
+  const void* ptrs[] = {Q, K, V, O};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return LWATTN_E_INVALID;
+  if (!lmask || ((uintptr_t)lmask & 3u) || !rowptr || ((uintptr_t)rowptr & 3u) || !cols ||
+      ((uintptr_t)cols & 3u))
+    return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  lwk::bsp::BsParams bp;
+  bp.Q = (const uint8_t*)Q;
+  bp.K = (const uint8_t*)K;
+  bp.V = (const uint8_t*)V;
+  bp.O = (uint8_t*)O;
+  bp.lmask = lmask;
+  bp.rowptr = rowptr;
+  bp.cols = cols;
+  bp.B = c.B;
+  bp.H = c.H;
+  bp.n = c.n;
+  bp.nb = (int)nb;
+  bp.causal = causal ? 1 : 0;
+  bp.scale = c.scale;
+  const int64_t grid = (int64_t)c.B * c.H * nb;
+  if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
+  const uint32_t smem = (uint32_t)(lwk::bsp::SMEM_BASE + 4 * nb);
+  (void)hipFuncSetAttribute((const void*)lwk::bsp::blocksparse_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipLaunchKernelGGL(lwk::bsp::blocksparse_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), smem, stream, bp);
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   return LWATTN_OK;
 }

@@ -99,6 +99,31 @@ def causal_pairs(lmask, window: int, dilation: Sequence[int]) -> int:
     return total
 
 
+def blocksparse_pairs(lmask, layout, causal: bool = False) -> int:
+    """Allowed pairs of block-sparse attention: valid rows with the valid keys
+    of their listed 64-blocks (with `causal`, keys at or before the row)."""
+    lm = np.asarray(lmask) != 0
+    lay = np.asarray(layout) != 0
+    B, n = lm.shape
+    H, nb, _ = lay.shape
+    total = 0
+    for b in range(B):
+        v = np.zeros(nb * 64, bool)
+        v[:n] = lm[b]
+        vb = v.reshape(nb, 64)
+        cnt = vb.sum(axis=1).astype(np.int64)           # valid keys (= valid rows) per block
+        # within one block: valid rows times valid keys at or before them
+        tri = (vb * np.cumsum(vb, axis=1)).sum(axis=1).astype(np.int64)
+        for h in range(H):
+            L = lay[h]
+            if not causal:
+                total += int(cnt @ L.astype(np.int64) @ cnt)
+            else:
+                below = np.tril(L, -1).astype(np.int64)
+                total += int(cnt @ below @ cnt) + int((np.diag(L).astype(np.int64) * tri).sum())
+    return total
+
+
 def local_global_key_pairs(lmask, gmask, H: int) -> int:
     """Pairs of local rows with global keys (every local row sees every global key)."""
     v, g = _flags(lmask, gmask)

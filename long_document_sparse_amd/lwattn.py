@@ -42,6 +42,7 @@ SIGNATURES = [
     ("lwattn_forward", ctypes.c_int, [_c_p] * 9 + [_c_p, _c_p]),
     ("lwattn_backward", ctypes.c_int, [_c_p] * 17 + [_c_p]),
     ("lwattn_forward_causal", ctypes.c_int, [_c_p] * 6 + [_c_p]),
+    ("lwattn_forward_blocksparse", ctypes.c_int, [_c_p] * 7 + [_i32, _c_p, _c_p]),
     ("lwattn_destroy", ctypes.c_int, [_c_p]),
     ("lwattn_global_index", ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
     ("lwattn_sync_status", ctypes.c_int, [_c_p, _c_p]),
@@ -208,6 +209,40 @@ class Plan:
                                             lmask.data_ptr(), out.data_ptr(), _stream_handle(stream))
         if st != OK:
             raise LwattnError(st, "lwattn_forward_causal")
+        return out
+
+    def forward_blocksparse(self, q, k, v, lmask, rowptr, cols, causal=False, out=None, stream=None):
+        """Enqueue block-sparse attention over 64-blocks (bf16 plans): the
+        layout as CSR over (head, query block), int32 device tensors rowptr
+        [H*nb + 1] and cols [nnz]; returns O (allocated if `out` is None)."""
+        import torch
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        for t, name in ((q, "q"), (k, "k"), (v, "v")):
+            self._check(t, name, tdt)
+            if tuple(t.shape) != self.shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {self.shape}")
+        B, H, n, d = self.shape
+        nb = (n + 63) // 64
+        self._check(lmask, "local_attn_mask", torch.float32)
+        if tuple(lmask.shape) != (B, n):
+            raise ValueError("local_attn_mask must be [B,n]")
+        self._check(rowptr, "rowptr", torch.int32)
+        self._check(cols, "cols", torch.int32)
+        if tuple(rowptr.shape) != (H * nb + 1,):
+            raise ValueError(f"rowptr must have H*nb + 1 = {H * nb + 1} entries")
+        if out is None:
+            out = torch.empty(self.shape, dtype=tdt, device=q.device)
+        else:
+            self._check(out, "out", tdt)
+            if tuple(out.shape) != self.shape:
+                raise ValueError("out has the wrong shape")
+        # an empty column list still needs a valid pointer
+        cptr = cols.data_ptr() if cols.numel() > 0 else rowptr.data_ptr()
+        st = self.lib.lwattn_forward_blocksparse(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 lmask.data_ptr(), rowptr.data_ptr(), cptr,
+                                                 int(bool(causal)), out.data_ptr(), _stream_handle(stream))
+        if st != OK:
+            raise LwattnError(st, "lwattn_forward_blocksparse")
         return out
 
     def backward(self, q, k, v, qg, kg, vg, lmask, gmask, o, do, grads=None, stream=None):

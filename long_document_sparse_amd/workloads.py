@@ -80,6 +80,11 @@ def named(name: str) -> Spec:
         return Spec("long", 8, 16, 16384, 64, 1024, "bf16", [0] * 16, seed=5, max_global=128,
                     global_mode="random", n_global=128, pad_mode="one_seq", pad_lo=1, pad_hi=4096,
                     k_boost_frac=0.01)
+    if name == "bsparse":
+        # block-sparse layout over 64-blocks (8 heads, n = 16384): each query
+        # block sees its own and 3 previous key blocks and 4 drawn ones
+        return Spec("bsparse", 1, 8, 16384, 64, 0, "bf16", [0] * 8, seed=7, max_global=0,
+                    global_mode="first", n_global=0)
     if name == "charlm":
         # causal variant (an autoregressive character model's attention): no
         # global tokens, no padding, two dilated heads
@@ -90,6 +95,8 @@ def named(name: str) -> Spec:
 
 NAMES = ("tiny", "base", "qa", "dilated", "long")
 CAUSAL_NAMES = ("charlm",)
+# layout of the "bsparse" workload (blocksparse_layout arguments)
+BSPARSE_LAYOUT = dict(local=4, extra=4, causal=False)
 
 
 @dataclasses.dataclass

@@ -1,0 +1,111 @@
+"""GPU parity of block-sparse attention (lwattn_forward_blocksparse through the
+C ABI) against the oracle's block-sparse rows.
+
+Tolerance, from the arithmetic: scores, the running softmax and the sums of
+P V accumulate in fp32; P is rounded to bf16 as the matrix-core operand and O
+to bf16 (2^-9 relative each).  Every case runs with the workloads' scaled
+inputs and with unscaled N(0,1) inputs; |err| <= 2e-2 * max |O| of the case.
+Padded rows, and rows whose query block lists no key block, must be exactly
+zero.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import make_plan, say, to_np64
+from long_document_sparse_amd import lwattn as lw
+from long_document_sparse_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # (B, H, n, local, extra, causal, pad_mode, pad_hi)
+    (1, 2, 200, 2, 1, False, "none", 0),
+    (2, 3, 333, 2, 2, True, "per_batch", 80),
+    (1, 2, 257, 1, 3, False, "scatter", 40),
+    (1, 1, 64, 1, 0, True, "none", 0),
+    (2, 2, 1000, 4, 4, False, "per_batch", 200),
+    (1, 2, 130, 3, 0, True, "none", 0),
+]
+
+
+def _run(spec, layout, causal, strong):
+    x = workloads.generate(spec, strong=strong)
+    dev = "cuda:0"
+    q, k, v = (torch.from_numpy(a).to(dev).to(torch.bfloat16) for a in (x.Q, x.K, x.V))
+    lm = torch.from_numpy(x.lmask).to(dev)
+    rowptr, cols = workloads.layout_csr(layout)
+    rp = torch.from_numpy(rowptr).to(dev)
+    cl = torch.from_numpy(cols).to(dev)
+    plan = make_plan(spec, max_global=0)
+    out = torch.full_like(q, float("nan"))
+    plan.forward_blocksparse(q, k, v, lm, rp, cl, causal=causal, out=out)
+    torch.cuda.synchronize()
+    return x, (q, k, v), out
+
+
+@pytest.mark.parametrize("strong", [False, True], ids=["scaled", "strong"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}n{c[2]}l{c[3]}e{c[4]}{'c' if c[5] else ''}{c[6]}")
+def test_blocksparse_matches_oracle(case, strong):
+    B, H, n, local, extra, causal, pmode, phi = case
+    spec = workloads.custom(B, H, n, 64, 0, "bf16", [0] * H, seed=41, n_global=0,
+                            pad_mode=pmode, pad_hi=phi, max_global=0)
+    layout = workloads.blocksparse_layout(H, n, seed=9, local=local, extra=extra, causal=causal)
+    say(f"block-sparse case {case} strong={strong}")
+    x, (q, k, v), out = _run(spec, layout, causal, strong)
+    want = oracle.forward_blocksparse(to_np64(q), to_np64(k), to_np64(v), x.lmask, layout, causal,
+                                      spec.scale)
+    got = to_np64(out)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - want).max()
+    bound = 2e-2 * max(np.abs(want).max(), 1e-30)
+    assert err <= bound, (err, bound)
+    pad = x.lmask == 0
+    for b in range(B):
+        assert not np.any(got[b][:, pad[b]])
+
+
+def test_query_blocks_without_key_blocks_output_zero():
+    spec = workloads.custom(1, 2, 300, 64, 0, "bf16", [0, 0], seed=42, n_global=0, max_global=0)
+    layout = workloads.blocksparse_layout(2, 300, seed=3, local=2, extra=1)
+    layout[0, 2] = 0      # head 0, query block 2 lists nothing
+    layout[1, :, 0] = 0   # head 1 never sees key block 0
+    x, (q, k, v), out = _run(spec, layout, False, True)
+    got = to_np64(out)
+    assert not np.any(got[0, 0, 128:192])
+    want = oracle.forward_blocksparse(to_np64(q), to_np64(k), to_np64(v), x.lmask, layout, False,
+                                      spec.scale)
+    assert np.abs(got - want).max() <= 2e-2 * np.abs(want).max()
+
+
+def test_blocksparse_full_size_sampled_rows():
+    spec = workloads.named("bsparse")
+    lay_kw = workloads.BSPARSE_LAYOUT
+    layout = workloads.blocksparse_layout(spec.H, spec.n, seed=spec.seed, **lay_kw)
+    x, (q, k, v), out = _run(spec, layout, lay_kw["causal"], False)
+    rng = np.random.default_rng(8)
+    B, H, n = spec.B, spec.H, spec.n
+    idx = rng.choice(B * H * n, 1500, replace=False)
+    extra = [(h * n) + i for h in range(H) for i in (0, 63, 64, 127, n - 64, n - 1)]
+    idx = np.unique(np.concatenate([idx, np.array(extra)]))
+    want = oracle.rows_blocksparse(to_np64(q), to_np64(k), to_np64(v), x.lmask, layout, idx,
+                                   lay_kw["causal"], spec.scale)
+    got = to_np64(out).reshape(-1, spec.d)[idx]
+    assert np.abs(got - want).max() <= 2e-2 * np.abs(want).max()
+
+
+def test_blocksparse_rejects_fp32_and_bad_pointers():
+    spec = workloads.custom(1, 1, 64, 64, 0, "f32", [0], n_global=0, max_global=0)
+    plan = make_plan(spec, max_global=0)
+    t = torch.zeros((1, 1, 64, 64), device="cuda:0")
+    lm = torch.ones((1, 64), device="cuda:0")
+    rp = torch.tensor([0, 1], dtype=torch.int32, device="cuda:0")
+    cl = torch.tensor([0], dtype=torch.int32, device="cuda:0")
+    with pytest.raises(lw.LwattnError):
+        plan.forward_blocksparse(t, t, t, lm, rp, cl, out=t)
+    spec = workloads.custom(1, 1, 64, 64, 0, "bf16", [0], n_global=0, max_global=0)
+    plan = make_plan(spec, max_global=0)
+    lib = lw.load_library()
+    assert lib.lwattn_forward_blocksparse(plan.handle, None, None, None, None, None, None, 0, None,
+                                          None) == lw.E_INVALID

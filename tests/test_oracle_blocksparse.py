@@ -111,3 +111,21 @@ def test_layout_csr_lists_every_set_block_in_order():
             r = h * nb + qb
             assert list(cols[rowptr[r]:rowptr[r + 1]]) == list(np.flatnonzero(lay[h, qb]))
             assert all(c <= qb for c in cols[rowptr[r]:rowptr[r + 1]])   # causal layout
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_pair_counter_matches_the_reading(causal):
+    from long_document_sparse_amd import flops
+    rng = np.random.default_rng(26)
+    n, H = 200, 2
+    lm = (rng.random((2, n)) > 0.15).astype(np.float32)
+    lay = workloads.blocksparse_layout(H, n, seed=7, local=2, extra=2, causal=causal)
+    total = 0
+    for b in range(2):
+        for h in range(H):
+            for i in range(n):
+                if lm[b, i] == 0:
+                    continue
+                total += sum(1 for j in range(n) if lay[h, i // 64, j // 64] and lm[b, j] != 0
+                             and (not causal or j <= i))
+    assert flops.blocksparse_pairs(lm, lay, causal) == total

@@ -267,3 +267,6 @@ def forward_blocksparse(Q, K, V, lmask, layout, causal=False, scale=None, thread
     B, H, n, d = np.shape(Q)
     out = rows_blocksparse(Q, K, V, lmask, layout, np.arange(B * H * n), causal, scale, threads)
     return out.reshape(B, H, n, d)
+
+
+from .layer import layer_forward, gelu, layernorm  # noqa: E402  (encoder layer oracle)

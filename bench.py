@@ -338,6 +338,101 @@ def run_blocksparse(args, spec, x, ts, lm, plan):
     print(json.dumps(res), flush=True)
 
 
+def cpu_baseline_layer(x, X, w, inter, budget_s=12.0):
+    """The oracle's layer, as it is, on the host cores, over a prefix of the
+    rows' batch row grown until about budget_s seconds; scaled to tokens/s."""
+    import oracle
+    spec = x.spec
+    threads = oracle.default_threads()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    t0 = time.perf_counter()
+    oracle.layer_forward(X.reshape(spec.B, spec.n, -1), w, x.lmask, x.gmask, spec.window, spec.dilation,
+                         spec.H, 1e-5, threads=threads)
+    t = time.perf_counter() - t0
+    return {"value": round(spec.B * spec.n / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole layer once ({t:.2f} s; float64 numpy GEMMs, the attention oracle in C)"}
+
+
+def run_layer(args, spec, x, lm, gm, plan):
+    """--pass layer: one JSON line for lwattn_layer_forward (one encoder layer)."""
+    import math
+    import numpy as np
+    import torch
+    from long_document_sparse_amd import flops as fl
+    from long_document_sparse_amd import lwattn, workloads
+    inter = workloads.FTLAYER_INTER
+    layer = lwattn.Layer(plan, inter, 1e-5)
+    dev = lm.device
+    rng = np.random.default_rng(spec.seed + 7)
+    w_np = {}
+    for name, shape in layer.shapes().items():
+        if name.startswith("ln") and name.endswith("_g"):
+            a = 1.0 + 0.1 * rng.standard_normal(shape)
+        elif len(shape) == 2:
+            a = rng.standard_normal(shape) / math.sqrt(shape[0])
+        else:
+            a = 0.1 * rng.standard_normal(shape)
+        w_np[name] = a.astype(np.float32)
+    w = {k: torch.from_numpy(a).to(dev).to(torch.bfloat16) for k, a in w_np.items()}
+    hid = spec.H * spec.d
+    X_np = rng.standard_normal((spec.B * spec.n, hid)).astype(np.float32)
+    X = torch.from_numpy(X_np).to(dev).to(torch.bfloat16)
+    Y = torch.empty_like(X)
+    layer.forward(X, w, lm, gm, out=Y)
+    for _ in range(args.warmup):
+        layer.forward(X, w, lm, gm, out=Y)
+    st = plan.sync_status()
+    if st != lwattn.OK:
+        raise SystemExit(f"layer failed: {lwattn.strerror(st)}")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        layer.forward(X, w, lm, gm, out=Y)
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_call = e0.elapsed_time(e1) * 1e-3 / args.steps
+    M = spec.B * spec.n
+    gemm = 2 * M * hid * (3 * hid) * 2 + 2 * M * hid * hid + 2 * 2 * M * hid * inter
+    attn = fl.flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
+    flop = gemm + attn
+    achieved = flop / t_call / 1e12
+    res = {
+        "metric": "Longformer encoder layer tokens/s (one layer), n=4096 H=16 inter=4096 w=512",
+        "value": round(M / (elapsed / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded inputs and weights; no dataset, no trained weights)",
+        "config": {"workload": describe(spec) + f"; encoder layer, hidden {hid}, intermediate {inter}",
+                   "global_batch": spec.B, "seq_len": spec.n, "heads": spec.H, "head_dim": spec.d,
+                   "window": spec.window, "parallelism": "single GPU", "timing": "warm (back to back)"},
+        "us_per_layer_on_stream": round(t_call * 1e6, 2),
+        "ms_for_24_layers": round(t_call * 24 * 1e3, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_MFMA, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_MFMA, 4), "traffic": None,
+                     "kernel": "whole layer (rocBLAS GEMMs and the library's kernels)",
+                     "algorithmic_flop": flop, "gemm_flop": gemm, "attention_flop": attn,
+                     "source_sha256": source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_layer(x, X.float().cpu().numpy(),
+                                                 {k: t.float().cpu().numpy() for k, t in w.items()}, inter)
+    layer.close()
+    plan.close()
+    print(json.dumps(res), flush=True)
+
+
 def run_backward(args, spec, x, ts, lm, gm, plan):
     """--pass backward: one JSON line for lwattn_backward."""
     import numpy as np
@@ -436,7 +531,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel HIP events (roofline fields become null)")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal", "blocksparse"), default="forward",
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal", "blocksparse", "layer"), default="forward",
                     help="time the forward (default) or the backward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device to device 5 times (counter calibration)")
@@ -452,7 +547,7 @@ def main():
     from long_document_sparse_amd import lwattn, workloads
 
     if args.workload is None:
-        args.workload = {"causal": "charlm", "blocksparse": "bsparse"}.get(args.which, "base")
+        args.workload = {"causal": "charlm", "blocksparse": "bsparse", "layer": "ftlayer"}.get(args.which, "base")
     spec = workloads.named(args.workload)
     x = workloads.generate(spec)
     dev = torch.device("cuda", 0)
@@ -471,6 +566,9 @@ def main():
         return
     if args.which == "blocksparse":
         run_blocksparse(args, spec, x, ts, lm, plan)
+        return
+    if args.which == "layer":
+        run_layer(args, spec, x, lm, gm, plan)
         return
 
     # the buffers are validated and the call marshalled once; every step

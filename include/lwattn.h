@@ -156,6 +156,46 @@ lwattn_status lwattn_forward_blocksparse(lwattn_plan_t plan, const void* Q, cons
                                          const int32_t* cols, int32_t causal, void* O,
                                          hipStream_t stream);
 
+/* Encoder layer around the attention (FasterTransformer Longformer encoder
+ * guide, compute flow; bf16 storage, fp32 accumulation).  With M = B*n rows
+ * of hid = H*64 columns, X [M][hid] the layer input:
+ *   [Q | K | V]    = X w_qkv + b_qkv      (w_qkv [hid][3 hid], b_qkv [3 hid])
+ *   [Qg | Kg | Vg] = X w_g + b_g          (same shapes), each split into heads
+ *                    [B][H][n][64] (column h*64 + j of a part: head h, element j)
+ *   A  = the attention of the plan (lwattn_forward) on those six tensors and
+ *        the masks, heads merged back to [M][hid]
+ *   H1 = LayerNorm(A w_o + b_o + X) * ln1_g + ln1_b
+ *   F  = gelu(H1 w_1 + b_1), gelu(x) = x (1 + erf(x / sqrt 2)) / 2
+ *   Y  = LayerNorm(F w_2 + b_2 + H1) * ln2_g + ln2_b
+ * LayerNorm over each row: (x - mean) / sqrt(biased variance + eps).  All
+ * weights row-major [in][out], bf16, 16-byte aligned device memory; X and Y
+ * [M][hid] bf16.  The GEMMs run in rocBLAS (fp32 results), the bias, split,
+ * merge, LayerNorm and GELU steps in the library's kernels; each intermediate
+ * is rounded to bf16 once.  lwattn_layer_create(plan, inter, eps, &layer):
+ * plan with bf16 storage and H in {8, 16, 24, 32, 48, 64}, inter a positive
+ * multiple of 8, eps > 0; the layer keeps the plan (which must outlive it) and
+ * allocates its intermediates and a rocBLAS handle.  lwattn_layer_forward
+ * enqueues the layer on `stream` (no allocation, no host sync; it uses the
+ * plan's workspace, so it must not overlap other calls of the plan).
+ * Errors: LWATTN_E_INVALID for null or misaligned arguments or a bad inter /
+ * eps; LWATTN_E_UNSUPPORTED for fp32 storage, another H, or M * 3 hid or
+ * M * inter >= 2^31; LWATTN_E_NOMEM; LWATTN_E_DEVICE if a launch or GEMM fails;
+ * the attention's own errors as lwattn_forward reports them. */
+typedef struct lwattn_layer_s* lwattn_layer_t;
+typedef struct {
+  const void *w_qkv, *b_qkv;   /* [hid][3 hid], [3 hid]: Q, K, V */
+  const void *w_g, *b_g;       /* [hid][3 hid], [3 hid]: Qg, Kg, Vg */
+  const void *w_o, *b_o;       /* [hid][hid], [hid] */
+  const void *ln1_g, *ln1_b;   /* [hid] */
+  const void *w_1, *b_1;       /* [hid][inter], [inter] */
+  const void *w_2, *b_2;       /* [inter][hid], [hid] */
+  const void *ln2_g, *ln2_b;   /* [hid] */
+} lwattn_layer_weights;
+lwattn_status lwattn_layer_create(lwattn_plan_t plan, int32_t inter, float eps, lwattn_layer_t* out);
+lwattn_status lwattn_layer_forward(lwattn_layer_t layer, const void* X, const lwattn_layer_weights* w,
+                                   const float* lmask, const float* gmask, void* Y, hipStream_t stream);
+lwattn_status lwattn_layer_destroy(lwattn_layer_t layer);
+
 /* Enqueues the backward of one forward on `stream` (asynchronous; no
  * allocation, no host sync): the gradients of a loss with respect to Q, K, V,
  * Qg, Kg, Vg, given dO = dLoss/dO.  It differentiates the operation that

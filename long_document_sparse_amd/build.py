@@ -11,6 +11,7 @@ SRC = os.path.join(PKG, "csrc", "lwattn.hip")
 DEPS = [SRC, os.path.join(PKG, "csrc", "kernels.hpp"), os.path.join(PKG, "csrc", "backward.hpp"),
         os.path.join(PKG, "csrc", "causal.hpp"),
         os.path.join(PKG, "csrc", "blocksparse.hpp"),
+        os.path.join(PKG, "csrc", "layer.hpp"),
         os.path.join(ROOT, "include", "lwattn.h")]
 LIB = os.path.join(PKG, "liblwattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,7 +29,8 @@ FLAGS = [
 
 def build(verbose: bool = False, extra=None) -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    # rocBLAS runs the encoder layer's plain GEMMs
+    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC, "-lrocblas"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

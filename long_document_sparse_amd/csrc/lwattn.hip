@@ -19,6 +19,9 @@
 #include "backward.hpp"
 #include "causal.hpp"
 #include "blocksparse.hpp"
+#include "layer.hpp"
+
+#include <rocblas/rocblas.h>
 #include "lwattn.h"
 
 namespace {
@@ -108,6 +111,74 @@ static void free_plan(lwattn_plan_s* p) {
 }
 
 static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+
+// ---------------------------------------------------------------------------
+// Encoder layer around the attention (bf16 storage): the plan gives B, H, n,
+// the window, dilation and globals; the layer object owns the intermediate
+// buffers and a rocBLAS handle.
+struct lwattn_layer_s {
+  lwattn_plan_t attn = nullptr;   // not owned
+  int32_t inter = 0;
+  float eps = 0.f;
+  rocblas_handle blas = nullptr;
+  float* P = nullptr;                  // [M, max(3 hid, inter)] fp32 GEMM results
+  __bf16* qkv[6] = {};                 // Q, K, V, Qg, Kg, Vg [B, H, n, 64]
+  __bf16* A = nullptr;                 // attention output [B, H, n, 64]
+  __bf16* Am = nullptr;                // [M, hid]
+  __bf16* H1 = nullptr;                // [M, hid]
+  __bf16* F = nullptr;                 // [M, inter]
+};
+
+static void free_layer(lwattn_layer_t L) {
+  if (!L) return;
+  if (L->attn) (void)hipSetDevice(L->attn->device);
+  (void)hipFree(L->P);
+  for (auto* q : L->qkv) (void)hipFree(q);
+  (void)hipFree(L->A);
+  (void)hipFree(L->Am);
+  (void)hipFree(L->H1);
+  (void)hipFree(L->F);
+  if (L->blas) (void)rocblas_destroy_handle(L->blas);
+  delete L;
+}
+
+// Row-major Y[M, N] (fp32) = X[M, K] W[K, N] (bf16), as the column-major
+// product Y^T = W^T X^T.
+static bool gemm_rm(rocblas_handle h, int64_t M, int64_t N, int64_t K, const void* X, const void* W, float* Y) {
+  const float one = 1.0f, zero = 0.0f;
+  const rocblas_status st = rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)N,
+                                            (rocblas_int)M, (rocblas_int)K, &one, W, rocblas_datatype_bf16_r,
+                                            (rocblas_int)N, X, rocblas_datatype_bf16_r, (rocblas_int)K, &zero, Y,
+                                            rocblas_datatype_f32_r, (rocblas_int)N, Y, rocblas_datatype_f32_r,
+                                            (rocblas_int)N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  if (st != rocblas_status_success) {
+    std::fprintf(stderr, "lwattn: rocblas_gemm_ex failed (%d)\n", (int)st);
+    return false;
+  }
+  return true;
+}
+
+template <int PER>
+static void launch_ln(const float* G, const void* b, const __bf16* R, const void* g, const void* be, float eps,
+                      __bf16* Y, int64_t M, hipStream_t stream) {
+  hipLaunchKernelGGL(lwk::layer::bias_residual_layernorm<PER>, dim3((uint32_t)((M + 3) / 4)),
+                     dim3(lwk::layer::LNT), 0, stream, G, (const __bf16*)b, R, (const __bf16*)g,
+                     (const __bf16*)be, eps, Y, M);
+}
+
+static bool layernorm(int H, const float* G, const void* b, const __bf16* R, const void* g, const void* be,
+                      float eps, __bf16* Y, int64_t M, hipStream_t stream) {
+  switch (H) {
+    case 8: launch_ln<8>(G, b, R, g, be, eps, Y, M, stream); return true;
+    case 16: launch_ln<16>(G, b, R, g, be, eps, Y, M, stream); return true;
+    case 24: launch_ln<24>(G, b, R, g, be, eps, Y, M, stream); return true;
+    case 32: launch_ln<32>(G, b, R, g, be, eps, Y, M, stream); return true;
+    case 48: launch_ln<48>(G, b, R, g, be, eps, Y, M, stream); return true;
+    case 64: launch_ln<64>(G, b, R, g, be, eps, Y, M, stream); return true;
+    default: return false;
+  }
+}
 
 extern "C" {
 
@@ -688,6 +759,93 @@ lwattn_status lwattn_timing_disable(lwattn_plan_t p) {
   p->timing_cap = 0;
   p->timing_calls = 0;
   p->bw_calls = 0;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwattn_layer_t* out) {
+  if (!out) return LWATTN_E_INVALID;
+  *out = nullptr;
+  if (!p || inter <= 0 || (inter % 8) != 0 || !(eps > 0.0f)) return LWATTN_E_INVALID;
+  const lwattn_config& c = p->cfg;
+  const int H = c.H;
+  if (c.dtype != LWATTN_BF16 || !(H == 8 || H == 16 || H == 24 || H == 32 || H == 48 || H == 64))
+    return LWATTN_E_UNSUPPORTED;
+  const int64_t M = (int64_t)c.B * c.n, hid = (int64_t)H * 64;
+  if (M * std::max<int64_t>(3 * hid, inter) >= ((int64_t)1 << 31)) return LWATTN_E_UNSUPPORTED;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  lwattn_layer_t L = new (std::nothrow) lwattn_layer_s;
+  if (!L) return LWATTN_E_NOMEM;
+  L->attn = p;
+  L->inter = inter;
+  L->eps = eps;
+  bool ok = true;
+  auto alloc = [&](void** ptr, size_t bytes) {
+    if (!ok) return;
+    if (bytes == 0) bytes = 16;
+    if (!hip_ok(hipMalloc(ptr, bytes), "hipMalloc")) { ok = false; *ptr = nullptr; }
+  };
+  alloc((void**)&L->P, (size_t)M * std::max<int64_t>(3 * hid, inter) * 4);
+  for (auto*& q : L->qkv) alloc((void**)&q, (size_t)M * hid * 2);
+  alloc((void**)&L->A, (size_t)M * hid * 2);
+  alloc((void**)&L->Am, (size_t)M * hid * 2);
+  alloc((void**)&L->H1, (size_t)M * hid * 2);
+  alloc((void**)&L->F, (size_t)M * inter * 2);
+  if (ok && rocblas_create_handle(&L->blas) != rocblas_status_success) ok = false;
+  if (!ok) {
+    free_layer(L);
+    return LWATTN_E_NOMEM;
+  }
+  *out = L;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_layer_forward(lwattn_layer_t L, const void* X, const lwattn_layer_weights* w,
+                                   const float* lmask, const float* gmask, void* Y, hipStream_t stream) {
+  if (!L || !w) return LWATTN_E_INVALID;
+  lwattn_plan_t p = L->attn;
+  const lwattn_config& c = p->cfg;
+  const int H = c.H;
+  const int64_t M = (int64_t)c.B * c.n, hid = (int64_t)H * 64, inter = L->inter;
+  if (M == 0) return LWATTN_OK;
+  const void* ptrs[] = {X, Y, w->w_qkv, w->b_qkv, w->w_g, w->b_g, w->w_o, w->b_o, w->ln1_g, w->ln1_b,
+                        w->w_1, w->b_1, w->w_2, w->b_2, w->ln2_g, w->ln2_b};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return LWATTN_E_INVALID;
+  if (!lmask || !gmask || ((uintptr_t)lmask & 3u) || ((uintptr_t)gmask & 3u)) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  if (rocblas_set_stream(L->blas, stream) != rocblas_status_success) return LWATTN_E_DEVICE;
+  namespace ly = lwk::layer;
+  auto blocks = [](int64_t threads) { return dim3((uint32_t)((threads + ly::LNT - 1) / ly::LNT)); };
+  // 1. projections: Q, K, V then Qg, Kg, Vg, bias added while splitting heads
+  if (!gemm_rm(L->blas, M, 3 * hid, hid, X, w->w_qkv, L->P)) return LWATTN_E_DEVICE;
+  hipLaunchKernelGGL(ly::split_heads, blocks(M * 3 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
+                     (const __bf16*)w->b_qkv, L->qkv[0], L->qkv[1], L->qkv[2], c.B, c.n, H);
+  if (!gemm_rm(L->blas, M, 3 * hid, hid, X, w->w_g, L->P)) return LWATTN_E_DEVICE;
+  hipLaunchKernelGGL(ly::split_heads, blocks(M * 3 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
+                     (const __bf16*)w->b_g, L->qkv[3], L->qkv[4], L->qkv[5], c.B, c.n, H);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  // 2. the attention
+  lwattn_status st = lwattn_forward(p, L->qkv[0], L->qkv[1], L->qkv[2], L->qkv[3], L->qkv[4], L->qkv[5],
+                                    lmask, gmask, L->A, stream);
+  if (st != LWATTN_OK) return st;
+  // 3. output projection, bias, residual, LayerNorm
+  hipLaunchKernelGGL(ly::merge_heads, blocks(M * hid / 8), dim3(ly::LNT), 0, stream, L->A, L->Am, c.B, c.n, H);
+  if (!gemm_rm(L->blas, M, hid, hid, L->Am, w->w_o, L->P)) return LWATTN_E_DEVICE;
+  if (!layernorm(H, L->P, w->b_o, (const __bf16*)X, w->ln1_g, w->ln1_b, L->eps, L->H1, M, stream))
+    return LWATTN_E_UNSUPPORTED;
+  // 4. FFN: intermediate GEMM, bias, GELU; output GEMM, bias, residual, LayerNorm
+  if (!gemm_rm(L->blas, M, inter, hid, L->H1, w->w_1, L->P)) return LWATTN_E_DEVICE;
+  hipLaunchKernelGGL(ly::bias_gelu, blocks(M * inter / 8), dim3(ly::LNT), 0, stream, L->P,
+                     (const __bf16*)w->b_1, L->F, M, (int)inter);
+  if (!gemm_rm(L->blas, M, hid, inter, L->F, w->w_2, L->P)) return LWATTN_E_DEVICE;
+  if (!layernorm(H, L->P, w->b_2, L->H1, w->ln2_g, w->ln2_b, L->eps, (__bf16*)Y, M, stream))
+    return LWATTN_E_UNSUPPORTED;
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_layer_destroy(lwattn_layer_t L) {
+  free_layer(L);
   return LWATTN_OK;
 }
 

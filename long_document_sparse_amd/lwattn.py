@@ -43,6 +43,9 @@ SIGNATURES = [
     ("lwattn_backward", ctypes.c_int, [_c_p] * 17 + [_c_p]),
     ("lwattn_forward_causal", ctypes.c_int, [_c_p] * 6 + [_c_p]),
     ("lwattn_forward_blocksparse", ctypes.c_int, [_c_p] * 7 + [_i32, _c_p, _c_p]),
+    ("lwattn_layer_create", ctypes.c_int, [_c_p, _i32, ctypes.c_float, ctypes.POINTER(_c_p)]),
+    ("lwattn_layer_forward", ctypes.c_int, [_c_p] * 7),
+    ("lwattn_layer_destroy", ctypes.c_int, [_c_p]),
     ("lwattn_destroy", ctypes.c_int, [_c_p]),
     ("lwattn_global_index", ctypes.c_int, [_c_p, _c_p, _c_p, _c_p]),
     ("lwattn_sync_status", ctypes.c_int, [_c_p, _c_p]),
@@ -353,3 +356,75 @@ class Plan:
 
     def timing_disable(self):
         self.lib.lwattn_timing_disable(self.handle)
+
+
+LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_g", "b_g", "w_o", "b_o", "ln1_g", "ln1_b",
+                 "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
+
+
+class _LayerWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in LAYER_WEIGHTS]
+
+
+class Layer:
+    """Encoder layer around the attention of `plan` (lwattn_layer_*): bf16
+    weights as a dict of device tensors (row-major [in, out]), X and Y [B*n, hid]."""
+
+    def __init__(self, plan: "Plan", inter: int, eps: float = 1e-5):
+        self.plan = plan
+        self.lib = plan.lib
+        self.inter = int(inter)
+        h = ctypes.c_void_p()
+        st = self.lib.lwattn_layer_create(plan.handle, self.inter, float(eps), ctypes.byref(h))
+        if st != OK:
+            raise LwattnError(st, "lwattn_layer_create")
+        self.handle = h
+
+    def shapes(self):
+        B, H, n, d = self.plan.shape
+        hid, inter = H * d, self.inter
+        return {"w_qkv": (hid, 3 * hid), "b_qkv": (3 * hid,), "w_g": (hid, 3 * hid), "b_g": (3 * hid,),
+                "w_o": (hid, hid), "b_o": (hid,), "ln1_g": (hid,), "ln1_b": (hid,),
+                "w_1": (hid, inter), "b_1": (inter,), "w_2": (inter, hid), "b_2": (hid,),
+                "ln2_g": (hid,), "ln2_b": (hid,)}
+
+    def forward(self, x, weights, lmask, gmask, out=None, stream=None):
+        import torch
+        B, H, n, d = self.plan.shape
+        hid = H * d
+        self.plan._check(x, "x", torch.bfloat16)
+        if tuple(x.shape) != (B * n, hid):
+            raise ValueError(f"x must be [{B * n}, {hid}]")
+        for name, shape in self.shapes().items():
+            t = weights[name]
+            self.plan._check(t, name, torch.bfloat16)
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        for t, name in ((lmask, "local_attn_mask"), (gmask, "global_attn_mask")):
+            self.plan._check(t, name, torch.float32)
+            if tuple(t.shape) != (B, n):
+                raise ValueError(f"{name} must be [B,n]")
+        if out is None:
+            out = torch.empty_like(x)
+        else:
+            self.plan._check(out, "out", torch.bfloat16)
+            if tuple(out.shape) != tuple(x.shape):
+                raise ValueError("out has the wrong shape")
+        self._w = _LayerWeights(*[weights[name].data_ptr() for name in LAYER_WEIGHTS])
+        st = self.lib.lwattn_layer_forward(self.handle, x.data_ptr(), ctypes.byref(self._w),
+                                           lmask.data_ptr(), gmask.data_ptr(), out.data_ptr(),
+                                           _stream_handle(stream))
+        if st != OK:
+            raise LwattnError(st, "lwattn_layer_forward")
+        return out
+
+    def close(self):
+        if self.handle:
+            self.lib.lwattn_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

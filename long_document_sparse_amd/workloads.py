@@ -85,6 +85,12 @@ def named(name: str) -> Spec:
         # block sees its own and 3 previous key blocks and 4 drawn ones
         return Spec("bsparse", 1, 8, 16384, 64, 0, "bf16", [0] * 8, seed=7, max_global=0,
                     global_mode="first", n_global=0)
+    if name == "ftlayer":
+        # one encoder layer of the QA model the FasterTransformer guide measures:
+        # 16 heads of 64, intermediate 4096, window 512; the question's 64
+        # tokens global at the start
+        return Spec("ftlayer", 1, 16, 4096, 64, 512, "bf16", [0] * 16, seed=8, max_global=64,
+                    global_mode="first", n_global=64)
     if name == "charlm":
         # causal variant (an autoregressive character model's attention): no
         # global tokens, no padding, two dilated heads
@@ -97,6 +103,8 @@ NAMES = ("tiny", "base", "qa", "dilated", "long")
 CAUSAL_NAMES = ("charlm",)
 # layout of the "bsparse" workload (blocksparse_layout arguments)
 BSPARSE_LAYOUT = dict(local=4, extra=4, causal=False)
+# intermediate size of the "ftlayer" workload's FFN
+FTLAYER_INTER = 4096
 
 
 @dataclasses.dataclass

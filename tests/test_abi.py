@@ -77,6 +77,9 @@ def test_null_config_and_plan_arguments_are_rejected():
     assert lib.lwattn_backward(*([None] * 18)) == lw.E_INVALID
     assert lib.lwattn_forward_causal(*([None] * 7)) == lw.E_INVALID
     assert lib.lwattn_forward_blocksparse(None, None, None, None, None, None, None, 0, None, None) == lw.E_INVALID
+    assert lib.lwattn_layer_create(None, 4096, 1e-5, None) == lw.E_INVALID
+    assert lib.lwattn_layer_forward(*([None] * 7)) == lw.E_INVALID
+    assert lib.lwattn_layer_destroy(None) == lw.OK
     assert lib.lwattn_global_index(None, None, None, None) == lw.E_INVALID
     assert lib.lwattn_sync_status(None, None) == lw.E_INVALID
     assert lib.lwattn_timing_enable(None, 4) == lw.E_INVALID

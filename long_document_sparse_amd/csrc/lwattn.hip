@@ -86,6 +86,7 @@ struct lwattn_plan_s {
   int bw_calls = 0;                 // backwards recorded
   int64_t bw_seen = 0;              // backwards since timing was enabled
   std::vector<hipEvent_t> bw_events;   // 2 kNumBwKernels per recorded backward
+  std::vector<uint8_t> bw_launched;    // per recorded backward: bit k = slot k's kernel ran
 };
 
 static void free_plan(lwattn_plan_s* p) {
@@ -324,7 +325,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->head_blk, (size_t)(H + 1) * 4);
   alloc((void**)&p->head_blk64, (size_t)(H + 1) * 4);
   alloc((void**)&p->stats, (size_t)B * H * n * sizeof(float2));
-  if (cfg->dtype == LWATTN_BF16 && cfg->max_global > 0 && n > 0) {
+  if (cfg->dtype == LWATTN_BF16 && cfg->max_global > 0 && n > 0 && B > 0 && H > 0) {
     // the positions of a head are cut into chunks of whole 64-row tiles, as
     // many as bring the workgroups of the chunk sums (one per batch row, head,
     // 64 global rows and chunk) to about 1024
@@ -576,8 +577,11 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   }
   // a timed backward launches each kernel with the pair of events its
   // dispatch records (slot k: events 2k, 2k + 1 of the call's record)
+  uint8_t launched = 0;   // slots whose kernel this call launches
   auto ev = [&](int k, int e) -> hipEvent_t {
-    return timed ? p->bw_events[(size_t)p->bw_calls * 2 * kNumBwKernels + 2 * k + e] : nullptr;
+    if (!timed) return nullptr;
+    launched |= (uint8_t)(1u << k);
+    return p->bw_events[(size_t)p->bw_calls * 2 * kNumBwKernels + 2 * k + e];
   };
   hipExtLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream,
                         ev(0, 0), ev(0, 1), 0u, cp);
@@ -654,7 +658,10 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
                           stream, ev(4, 0), ev(4, 1), 0u, bp);
   }
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-  if (timed) ++p->bw_calls;
+  if (timed) {
+    p->bw_launched[(size_t)p->bw_calls] = launched;
+    ++p->bw_calls;
+  }
   return LWATTN_OK;
 }
 
@@ -711,6 +718,7 @@ lwattn_status lwattn_timing_enable(lwattn_plan_t p, int32_t max_calls) {
   if (!make(p->events, (size_t)max_calls * (kNumKernels + 1)) ||
       !make(p->bw_events, (size_t)max_calls * 2 * kNumBwKernels))
     return LWATTN_E_DEVICE;
+  p->bw_launched.assign((size_t)max_calls, 0);
   p->timing_cap = max_calls;
   return LWATTN_OK;
 }
@@ -859,11 +867,11 @@ lwattn_status lwattn_timing_read_backward(lwattn_plan_t p, float* ms, int32_t ca
     // the dK/dV kernel ends every backward
     if (!hip_ok(hipEventSynchronize(ev[2 * kNumBwKernels - 1]), "hipEventSynchronize")) return LWATTN_E_DEVICE;
     for (int k = 0; k < kNumBwKernels; ++k) {
+      // only the pairs of kernels this call launched were recorded
+      if (!((p->bw_launched[(size_t)call] >> k) & 1u)) continue;
       float t = 0.f;
-      // a kernel the call did not launch left its pair unrecorded: both are
-      // then the pair's last recording or never recorded, and count as zero
-      hipError_t e = hipEventElapsedTime(&t, ev[2 * k], ev[2 * k + 1]);
-      if (e != hipSuccess) t = 0.f;
+      if (!hip_ok(hipEventElapsedTime(&t, ev[2 * k], ev[2 * k + 1]), "hipEventElapsedTime"))
+        return LWATTN_E_DEVICE;
       tot[k] += t;
     }
   }

@@ -274,7 +274,8 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   // When that round is nearly empty (under a quarter used), a full round of
   // global-row workgroups would run behind the band ones with long merges of
   // many slices: a quarter of the slots serves them better (measured at
-  // B=1, H=16, n=4096, 64 globals: 47 instead of 103 us)
+  // B=1, H=16, n=4096, 64 globals: 47 instead of 105 us; B=4: 114 instead of
+  // 134 us)
   int ncu = 256;
   {
     hipDeviceProp_t prop;
@@ -294,6 +295,9 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
     const int64_t maxs = (n + 127) / 128;
     if (want > maxs) want = maxs;
     if (want < 1) want = 1;
+    // but no slice longer than 4096 keys, so that no global-row workgroup
+    // outlasts the band ones on long sequences
+    if (want < (n + 4095) / 4096) want = (n + 4095) / 4096;
     p->ksplit = ceil_div(ceil_div(n, want), 64) * 64;   // whole 64-key steps
     p->nsplit = ceil_div(n, p->ksplit);
     nglob = units * p->nsplit;

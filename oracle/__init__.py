@@ -220,6 +220,25 @@ def forward_causal(Q, K, V, lmask, window, dilation=None, scale=None, threads=No
     return out
 
 
+def backward_causal(Q, K, V, lmask, dO, window, dilation=None, scale=None, threads=None):
+    """Gradients (dQ, dK, dV), float64 [B,H,n,d] each, of the causal variant
+    (the same chain rule over the causal key sets; every row is local)."""
+    d = np.shape(Q)[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    gm = np.zeros_like(_f32(lmask))
+    bound = _Bound(Q, K, V, Q, K, V, lmask, gm, window, dilation, scale, causal=True)
+    go = _f32(dO)
+    if go.shape != bound.shape:
+        raise ValueError("dO must have the shape of the output [B,H,n,d]")
+    outs = [np.empty(bound.shape, np.float64) for _ in range(6)]
+    rc = _load().lwo_backward(ctypes.byref(bound.p), go.ctypes.data,
+                              *[o.ctypes.data for o in outs], threads or default_threads())
+    if rc:
+        raise RuntimeError(f"oracle causal backward failed ({rc})")
+    return outs[0], outs[1], outs[2]
+
+
 def rows_causal(Q, K, V, lmask, window, row_index, dilation=None, scale=None, threads=None):
     """Selected rows of the causal variant: row_index holds flat (b*H + h)*n + i."""
     d = np.shape(Q)[-1]

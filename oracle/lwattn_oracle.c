@@ -267,7 +267,6 @@ int lwo_forward(const lwo_problem* p, double* out, int32_t threads) {
  * task each); within a pair the rows are summed in order. */
 int lwo_backward(const lwo_problem* p, const float* dO, double* dQ, double* dK, double* dV,
                  double* dQg, double* dKg, double* dVg, int32_t threads) {
-  if (p->causal) return 2;   /* the causal variant has no backward here */
   const int32_t n = p->n, d = p->d;
   const int64_t pairs = (int64_t)p->B * p->H;
   const int64_t per = (int64_t)n * d;
@@ -294,7 +293,8 @@ int lwo_backward(const lwo_problem* p, const float* dO, double* dQ, double* dK, 
         const float* gm = p->gmask + (int64_t)b * n;
         for (int32_t i = 0; i < n; ++i) {
           int32_t kind;
-          const int64_t cnt = lwo_allowed(lm, gm, n, p->window, p->gap[h], i, keys, &kind);
+          const int64_t cnt = p->causal ? lwo_allowed_causal(lm, n, p->window, p->gap[h], i, keys, &kind)
+                                        : lwo_allowed(lm, gm, n, p->window, p->gap[h], i, keys, &kind);
           if (kind == LWO_PADDED || cnt == 0) continue;
           const int glob = kind == LWO_GLOBAL;
           const float* q = (glob ? p->Qg : p->Q) + head + (int64_t)i * d;

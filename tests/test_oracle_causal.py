@@ -131,3 +131,44 @@ def test_causal_pair_counter_matches_the_oracle_key_sets():
     total = sum(oracle.allowed_causal(lm[b], 10, gap, i)[1].size
                 for b in range(2) for gap in (0, 2) for i in range(50))
     assert flops.causal_pairs(lm, 10, [0, 2]) == total
+
+
+def _loss(Q, K, V, lm, dO, window, gaps, scale):
+    return float((oracle.forward_causal(Q, K, V, lm, window, gaps, scale, threads=1) * dO).sum())
+
+
+@pytest.mark.parametrize("window,gaps,pad", [(4, [0, 1], 2), (6, [2], 0)])
+def test_causal_backward_matches_central_differences(window, gaps, pad):
+    """dL/dX of L = sum(O * dO) for X in Q, K, V against central differences
+    of the forward oracle (step 2^-10, exact in float32 for these inputs)."""
+    Q, K, V, lm = _inputs(41, 1, len(gaps), 11, 3, pad)
+    rng = np.random.default_rng(42)
+    dO = rng.standard_normal(Q.shape).astype(np.float32)
+    dQ, dK, dV = oracle.backward_causal(Q, K, V, lm, dO, window, gaps, 0.7, threads=1)
+    eps = 2.0 ** -10
+    for X, G in ((Q, dQ), (K, dK), (V, dV)):
+        num = np.zeros_like(G)
+        for idx in np.ndindex(X.shape):
+            old = X[idx]
+            X[idx] = old + eps
+            lp = _loss(Q, K, V, lm, dO, window, gaps, 0.7)
+            X[idx] = old - eps
+            lm_ = _loss(Q, K, V, lm, dO, window, gaps, 0.7)
+            X[idx] = old
+            num[idx] = (lp - lm_) / (2 * eps)
+        np.testing.assert_allclose(G, num, rtol=1e-5, atol=1e-6)
+
+
+def test_causal_backward_identities():
+    Q, K, V, lm = _inputs(43, 2, 2, 40, 4, pad=6)
+    rng = np.random.default_rng(44)
+    dO = rng.standard_normal(Q.shape).astype(np.float32)
+    dQ, dK, dV = oracle.backward_causal(Q, K, V, lm, dO, 10, [0, 2], 0.5, threads=2)
+    valid = lm != 0
+    for b in range(2):
+        for h in range(2):
+            np.testing.assert_allclose(dK[b, h].sum(0), 0.0, atol=1e-10)
+            np.testing.assert_allclose(dV[b, h].sum(0), dO[b, h][valid[b]].astype(np.float64).sum(0),
+                                       atol=1e-10)
+            for t in (dQ, dK, dV):
+                assert not np.any(t[b, h][~valid[b]])

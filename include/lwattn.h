@@ -132,6 +132,21 @@ lwattn_status lwattn_forward(lwattn_plan_t plan,
 lwattn_status lwattn_forward_causal(lwattn_plan_t plan, const void* Q, const void* K, const void* V,
                                     const float* lmask, void* O, hipStream_t stream);
 
+/* Backward of lwattn_forward_causal: the chain rule through its softmax,
+ * the same derivation as lwattn_backward over the causal tap sets (dS_ij =
+ * P_ij (dP_ij - D_i) with dP_ij = <dO_i, V_j> and D_i = <dO_i, O_i>;
+ * dQ_i = scale sum_j dS_ij K_j, dK_j = scale sum_i dS_ij Q_i,
+ * dV_j = sum_i P_ij dO_i).  O is the output of lwattn_forward_causal on the
+ * same inputs.  Q, K, V, O, dO, dQ, dK, dV: [B][H][n][64] bf16, 16-byte
+ * aligned, device memory; lmask float32 [B][n].  Every element of dQ, dK, dV
+ * is written (zero at rows and keys whose lmask is 0).  Enqueued on `stream`
+ * (two kernel launches, no allocation, no host sync); it uses the plan's
+ * per-row statistics buffer, so it must not overlap a backward of the same
+ * plan.  Errors as lwattn_forward_causal. */
+lwattn_status lwattn_backward_causal(lwattn_plan_t plan, const void* Q, const void* K, const void* V,
+                                     const float* lmask, const void* O, const void* dO,
+                                     void* dQ, void* dK, void* dV, hipStream_t stream);
+
 /* Block-sparse attention over 64 x 64 blocks (xFormers' attention-mask notes:
  * a per-head layout over 64 x 64 blocks of the score matrix with block size
  * 64, and masks that compose by intersection, as a layout with a causal mask).

@@ -1207,9 +1207,10 @@ __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint
 // order; P = exp2(c S - lse2(row)) (c = scale log2(e), lse2 the row's
 // log-sum-exp in log2 units, from mt.lse), dS = P (dP - D).  Bit k of M: row
 // 32 rq + k counts for the lane's key (ignored when `full`: every row counts).
+template <typename MT>
 __device__ __forceinline__ void kv_tile(f32x16 (&dk)[2], f32x16 (&dv)[2], const uint8_t* tQ,
                                         const uint8_t* tdO, const bf16x8 (&kf)[4], const bf16x8 (&vf)[4],
-                                        const Meta& mt, float c, int rq, int lane, uint32_t M, bool full) {
+                                        const MT& mt, float c, int rq, int lane, uint32_t M, bool full) {
   const int h32 = lane >> 5, qi = lane & 31;
   f32x16 x = {}, e = {};
 #pragma unroll

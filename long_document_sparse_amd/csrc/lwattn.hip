@@ -503,6 +503,53 @@ lwattn_status lwattn_forward_causal(lwattn_plan_t p, const void* Q, const void* 
   return LWATTN_OK;
 }
 
+lwattn_status lwattn_backward_causal(lwattn_plan_t p, const void* Q, const void* K, const void* V,
+                                     const float* lmask, const void* O, const void* dO, void* dQ, void* dK,
+                                     void* dV, hipStream_t stream) {
+  if (!p) return LWATTN_E_INVALID;
+  const lwattn_config& c = p->cfg;
+  if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
+  if (c.dtype != LWATTN_BF16) return LWATTN_E_UNSUPPORTED;
+  if ((int64_t)c.n * 128 >= lwk::OOB_OFF) return LWATTN_E_UNSUPPORTED;
+  const void* ptrs[] = {Q, K, V, O, dO, dQ, dK, dV};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return LWATTN_E_INVALID;
+  if (!lmask || ((uintptr_t)lmask & 3u)) return LWATTN_E_INVALID;
+  if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  lwk::cz::CzBwParams bp;
+  bp.Q = (const uint8_t*)Q;
+  bp.K = (const uint8_t*)K;
+  bp.V = (const uint8_t*)V;
+  bp.O = (const uint8_t*)O;
+  bp.dO = (const uint8_t*)dO;
+  bp.dQ = (uint8_t*)dQ;
+  bp.dK = (uint8_t*)dK;
+  bp.dV = (uint8_t*)dV;
+  bp.lmask = lmask;
+  bp.stats = p->stats;
+  bp.head_stride = p->head_stride;
+  bp.head_blk = p->head_blk64;
+  bp.B = c.B;
+  bp.H = c.H;
+  bp.n = c.n;
+  bp.r = (int)std::min<int64_t>(c.window / 2, c.n);
+  bp.blocks_per_b = p->blocks64_per_b;
+  bp.scale = c.scale;
+  const int64_t grid = (int64_t)c.B * p->blocks64_per_b;
+  if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
+  (void)hipFuncSetAttribute((const void*)lwk::cz::causal_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            lwk::cz::BW_DQ_SMEM);
+  (void)hipFuncSetAttribute((const void*)lwk::cz::causal_dkv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            lwk::cz::BW_DKV_SMEM);
+  // dQ and the rows' statistics first; dK, dV read those statistics
+  hipLaunchKernelGGL(lwk::cz::causal_dq_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::BW_DQ_SMEM,
+                     stream, bp);
+  hipLaunchKernelGGL(lwk::cz::causal_dkv_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::BW_DKV_SMEM,
+                     stream, bp);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  return LWATTN_OK;
+}
+
 lwattn_status lwattn_forward_blocksparse(lwattn_plan_t p, const void* Q, const void* K, const void* V,
                                          const float* lmask, const int32_t* rowptr, const int32_t* cols,
                                          int32_t causal, void* O, hipStream_t stream) {

@@ -42,6 +42,7 @@ SIGNATURES = [
     ("lwattn_forward", ctypes.c_int, [_c_p] * 9 + [_c_p, _c_p]),
     ("lwattn_backward", ctypes.c_int, [_c_p] * 17 + [_c_p]),
     ("lwattn_forward_causal", ctypes.c_int, [_c_p] * 6 + [_c_p]),
+    ("lwattn_backward_causal", ctypes.c_int, [_c_p] * 10 + [_c_p]),
     ("lwattn_forward_blocksparse", ctypes.c_int, [_c_p] * 7 + [_i32, _c_p, _c_p]),
     ("lwattn_layer_create", ctypes.c_int, [_c_p, _i32, ctypes.c_float, ctypes.POINTER(_c_p)]),
     ("lwattn_layer_forward", ctypes.c_int, [_c_p] * 7),
@@ -213,6 +214,28 @@ class Plan:
         if st != OK:
             raise LwattnError(st, "lwattn_forward_causal")
         return out
+
+    def backward_causal(self, q, k, v, lmask, o, do, stream=None):
+        """Enqueue the backward of the causal variant (bf16 plans); `o` is
+        forward_causal's output on the same inputs.  Returns (dQ, dK, dV)."""
+        import torch
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+            self._check(t, name, tdt)
+            if tuple(t.shape) != self.shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {self.shape}")
+        B, H, n, d = self.shape
+        self._check(lmask, "local_attn_mask", torch.float32)
+        if tuple(lmask.shape) != (B, n):
+            raise ValueError("local_attn_mask must be [B,n]")
+        dq, dk, dv = (torch.empty(self.shape, dtype=tdt, device=q.device) for _ in range(3))
+        st = self.lib.lwattn_backward_causal(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                             lmask.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                             _stream_handle(stream))
+        if st != OK:
+            raise LwattnError(st, "lwattn_backward_causal")
+        return dq, dk, dv
 
     def forward_blocksparse(self, q, k, v, lmask, rowptr, cols, causal=False, out=None, stream=None):
         """Enqueue block-sparse attention over 64-blocks (bf16 plans): the

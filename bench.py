@@ -176,6 +176,103 @@ def cpu_baseline_causal(x, budget_s=12.0):
             "sample": f"the whole causal forward, repeated {reps} times ({t:.2f} s)"}
 
 
+def cpu_baseline_causal_backward(x, budget_s=12.0):
+    """The oracle's causal backward, as it is, on the host cores, over whole
+    (batch row, head) slices in turn for about budget_s seconds (heads are
+    independent, so a slice is a fair sample of the work)."""
+    import numpy as np
+    import oracle
+    spec = x.spec
+    threads = oracle.default_threads()
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    rng = np.random.default_rng(5)
+    do = (rng.standard_normal(x.Q.shape[2:]) / 8).astype(np.float32)
+    dil = list(spec.dilation)
+    heads, t = 0, 0.0
+    while t < budget_s:
+        b, h = divmod(heads % (spec.B * spec.H), spec.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        t0 = time.perf_counter()
+        oracle.backward_causal(x.Q[sl], x.K[sl], x.V[sl], x.lmask[b:b + 1], do[None, None], spec.window,
+                               [dil[h]], spec.scale, threads=threads)
+        t += time.perf_counter() - t0
+        heads += 1
+    value = spec.n * heads / spec.H / t          # a token is one row of every head
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} whole (batch row, head) slices of the causal backward ({t:.2f} s), "
+                      f"scaled by the {spec.H} heads of a token"}
+
+
+def run_causal_backward(args, spec, x, ts, lm, plan):
+    """--pass causal_backward: one JSON line for lwattn_backward_causal (two
+    kernels a call: dQ with the rows' statistics, then dK/dV)."""
+    import ctypes
+    import torch
+    from long_document_sparse_amd import flops as fl
+    from long_document_sparse_amd import lwattn
+    if spec.dtype != "bf16":
+        raise SystemExit("the causal variant runs on bf16 storage")
+    q, k, v = ts[0], ts[1], ts[2]
+    g = torch.Generator().manual_seed(5)
+    do = (torch.randn(q.shape, generator=g) / 8).to(q.device).to(torch.bfloat16)
+    o = plan.forward_causal(q, k, v, lm)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    fn = plan.lib.lwattn_backward_causal
+    cargs = (plan.handle,) + tuple(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, lm, o, do, dq, dk, dv)) + (None,)
+
+    def step():
+        st = fn(*cargs)
+        if st != lwattn.OK:
+            raise SystemExit(f"causal backward failed: {lwattn.strerror(st)}")
+
+    for _ in range(args.warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_call = e0.elapsed_time(e1) * 1e-3 / args.steps        # s per call (both kernels), on the stream
+    pairs = fl.causal_pairs(x.lmask, spec.window, spec.dilation)
+    # S, dP, dQ, dK, dV: five products of 2 d flops per pair (recomputation not counted)
+    flop = 10 * spec.d * pairs
+    achieved = flop / t_call / 1e12
+    tokens = spec.B * spec.n
+    res = {
+        "metric": "causal dilated window attn bwd tokens/s, n=8192 w=512",
+        "value": round(tokens / (elapsed / args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded, N(0,1)/sqrt(d) inputs; no dataset)",
+        "config": {"workload": describe(spec) + "; causal backward", "global_batch": spec.B, "seq_len": spec.n,
+                   "heads": spec.H, "head_dim": spec.d, "window": spec.window,
+                   "parallelism": "single GPU", "timing": "warm (back to back)"},
+        "us_per_call_on_stream": round(t_call * 1e6, 2),
+        "algorithmic_pairs": pairs,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_MFMA,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_MFMA, 4), "traffic": None,
+                     "kernel": "causal_dq_kernel + causal_dkv_kernel (one call)", "algorithmic_flop": flop,
+                     "source_sha256": source_hash()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_causal_backward(x)
+    plan.close()
+    print(json.dumps(res), flush=True)
+
+
 def run_causal(args, spec, x, ts, lm, plan):
     """--pass causal: one JSON line for lwattn_forward_causal (one kernel a call)."""
     import ctypes
@@ -531,7 +628,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel HIP events (roofline fields become null)")
-    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal", "blocksparse", "layer"), default="forward",
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal", "causal_backward", "blocksparse", "layer"), default="forward",
                     help="time the forward (default) or the backward")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device to device 5 times (counter calibration)")
@@ -547,7 +644,7 @@ def main():
     from long_document_sparse_amd import lwattn, workloads
 
     if args.workload is None:
-        args.workload = {"causal": "charlm", "blocksparse": "bsparse", "layer": "ftlayer"}.get(args.which, "base")
+        args.workload = {"causal": "charlm", "causal_backward": "charlm", "blocksparse": "bsparse", "layer": "ftlayer"}.get(args.which, "base")
     spec = workloads.named(args.workload)
     x = workloads.generate(spec)
     dev = torch.device("cuda", 0)
@@ -563,6 +660,9 @@ def main():
         return
     if args.which == "causal":
         run_causal(args, spec, x, ts, lm, plan)
+        return
+    if args.which == "causal_backward":
+        run_causal_backward(args, spec, x, ts, lm, plan)
         return
     if args.which == "blocksparse":
         run_blocksparse(args, spec, x, ts, lm, plan)

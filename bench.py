@@ -381,7 +381,7 @@ def run_blocksparse(args, spec, x, ts, lm, plan):
     plan.forward_blocksparse(q, k, v, lm, rp, cl, causal=kw["causal"], out=o)
     fn = plan.lib.lwattn_forward_blocksparse
     cargs = (plan.handle,) + tuple(ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, lm, rp, cl)) + \
-        (int(kw["causal"]), ctypes.c_void_p(o.data_ptr()), None)
+        (int(cl.numel()), int(kw["causal"]), ctypes.c_void_p(o.data_ptr()), None)
 
     def step():
         st = fn(*cargs)

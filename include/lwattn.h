@@ -157,18 +157,20 @@ lwattn_status lwattn_backward_causal(lwattn_plan_t plan, const void* Q, const vo
  * scale and the storage type; its window, dilation and max_global play no part.
  * Layout, CSR over (head, query block), device memory, int32, 4-byte aligned:
  * the key blocks of query block qb of head h are cols[rowptr[h*nb + qb] ..
- * rowptr[h*nb + qb + 1]) with nb = ceil(n / 64); rowptr has H*nb + 1 entries.
- * Each listed key block is visited once per listing (list a block once); a
- * block index outside [0, nb) contributes no key; a list longer than nb is cut
- * to its first nb entries.  Q, K, V, O: [B][H][n][64] bf16, 16-byte aligned;
+ * rowptr[h*nb + qb + 1]) with nb = ceil(n / 64); rowptr has H*nb + 1 entries
+ * and cols holds nnz >= 0 entries.  Each listed key block is visited once per
+ * listing (list a block once); a block index outside [0, nb) contributes no
+ * key; a list longer than nb is cut to its first nb entries; offsets are
+ * clamped into [0, nnz], so a malformed rowptr (negative, decreasing or past
+ * nnz) never reads outside cols (its lists come out empty or cut).  Q, K, V, O: [B][H][n][64] bf16, 16-byte aligned;
  * lmask float32 [B][n].  Every element of O is written.  One kernel launch on
  * `stream`, no allocation, no host sync, no plan workspace.
- * Errors: LWATTN_E_INVALID for a null plan or pointer or a misaligned one;
- * LWATTN_E_UNSUPPORTED for fp32 storage, n * 128 >= 2^31 - 256 or
+ * Errors: LWATTN_E_INVALID for a null plan or pointer, a misaligned one or
+ * nnz < 0; LWATTN_E_UNSUPPORTED for fp32 storage, n * 128 >= 2^31 - 256 or
  * nb > 4096; LWATTN_E_DEVICE if the launch fails. */
 lwattn_status lwattn_forward_blocksparse(lwattn_plan_t plan, const void* Q, const void* K,
                                          const void* V, const float* lmask, const int32_t* rowptr,
-                                         const int32_t* cols, int32_t causal, void* O,
+                                         const int32_t* cols, int32_t nnz, int32_t causal, void* O,
                                          hipStream_t stream);
 
 /* Encoder layer around the attention (FasterTransformer Longformer encoder

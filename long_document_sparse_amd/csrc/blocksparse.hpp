@@ -31,6 +31,7 @@ struct BsParams {
   const int32_t* rowptr;    // [H*nb + 1]
   const int32_t* cols;      // [nnz]
   int B, H, n, nb, causal;
+  int nnz;                  // entries of cols: every list is clamped into [0, nnz)
   float scale;
 };
 
@@ -46,8 +47,11 @@ __device__ void bs_block(const BsParams& p, int b, int h, int qb, uint8_t* sm, T
   const int n = p.n, nb = p.nb;
   const int64_t bh = (int64_t)b * p.H + h;
   const int64_t hoff = bh * n * 128;
-  const int rbeg = p.rowptr[h * nb + qb];
-  int nt = p.rowptr[h * nb + qb + 1] - rbeg;
+  // a malformed CSR (negative, decreasing or out-of-range offsets) reads no
+  // column entry outside cols[0, nnz)
+  const int rbeg = min(max(p.rowptr[h * nb + qb], 0), p.nnz);
+  const int rend = min(max(p.rowptr[h * nb + qb + 1], 0), p.nnz);
+  int nt = rend - rbeg;
   nt = nt < 0 ? 0 : (nt > nb ? nb : nt);
   for (int j = t; j < nt; j += NTH) colsl[j] = p.cols[rbeg + j];
   const int P0 = T * qb;

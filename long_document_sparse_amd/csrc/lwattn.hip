@@ -552,7 +552,7 @@ lwattn_status lwattn_backward_causal(lwattn_plan_t p, const void* Q, const void*
 
 lwattn_status lwattn_forward_blocksparse(lwattn_plan_t p, const void* Q, const void* K, const void* V,
                                          const float* lmask, const int32_t* rowptr, const int32_t* cols,
-                                         int32_t causal, void* O, hipStream_t stream) {
+                                         int32_t nnz, int32_t causal, void* O, hipStream_t stream) {
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
@@ -565,7 +565,7 @@ lwattn_status lwattn_forward_blocksparse(lwattn_plan_t p, const void* Q, const v
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return LWATTN_E_INVALID;
   if (!lmask || ((uintptr_t)lmask & 3u) || !rowptr || ((uintptr_t)rowptr & 3u) || !cols ||
-      ((uintptr_t)cols & 3u))
+      ((uintptr_t)cols & 3u) || nnz < 0)
     return LWATTN_E_INVALID;
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
   lwk::bsp::BsParams bp;
@@ -581,6 +581,7 @@ lwattn_status lwattn_forward_blocksparse(lwattn_plan_t p, const void* Q, const v
   bp.n = c.n;
   bp.nb = (int)nb;
   bp.causal = causal ? 1 : 0;
+  bp.nnz = nnz;
   bp.scale = c.scale;
   const int64_t grid = (int64_t)c.B * c.H * nb;
   if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;

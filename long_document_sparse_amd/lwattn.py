@@ -43,7 +43,7 @@ SIGNATURES = [
     ("lwattn_backward", ctypes.c_int, [_c_p] * 17 + [_c_p]),
     ("lwattn_forward_causal", ctypes.c_int, [_c_p] * 6 + [_c_p]),
     ("lwattn_backward_causal", ctypes.c_int, [_c_p] * 10 + [_c_p]),
-    ("lwattn_forward_blocksparse", ctypes.c_int, [_c_p] * 7 + [_i32, _c_p, _c_p]),
+    ("lwattn_forward_blocksparse", ctypes.c_int, [_c_p] * 7 + [_i32, _i32, _c_p, _c_p]),
     ("lwattn_layer_create", ctypes.c_int, [_c_p, _i32, ctypes.c_float, ctypes.POINTER(_c_p)]),
     ("lwattn_layer_forward", ctypes.c_int, [_c_p] * 7),
     ("lwattn_layer_destroy", ctypes.c_int, [_c_p]),
@@ -265,7 +265,7 @@ class Plan:
         # an empty column list still needs a valid pointer
         cptr = cols.data_ptr() if cols.numel() > 0 else rowptr.data_ptr()
         st = self.lib.lwattn_forward_blocksparse(self.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                                 lmask.data_ptr(), rowptr.data_ptr(), cptr,
+                                                 lmask.data_ptr(), rowptr.data_ptr(), cptr, int(cols.numel()),
                                                  int(bool(causal)), out.data_ptr(), _stream_handle(stream))
         if st != OK:
             raise LwattnError(st, "lwattn_forward_blocksparse")

@@ -31,7 +31,9 @@ PADDED, GLOBAL, LOCAL = 0, 1, 2
 def build() -> str:
     """Compile the oracle with gcc (always rebuilds). Returns the .so path."""
     tmp = _LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC",
+    # x86-64-v3 (AVX2, FMA): the library built here also runs on the GPU box's
+    # host, whose CPU model may differ from this one, so no -march=native
+    cmd = ["gcc", "-O3", "-march=x86-64-v3", "-std=c11", "-fopenmp", "-shared", "-fPIC",
            "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)

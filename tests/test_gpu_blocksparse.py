@@ -107,5 +107,39 @@ def test_blocksparse_rejects_fp32_and_bad_pointers():
     spec = workloads.custom(1, 1, 64, 64, 0, "bf16", [0], n_global=0, max_global=0)
     plan = make_plan(spec, max_global=0)
     lib = lw.load_library()
-    assert lib.lwattn_forward_blocksparse(plan.handle, None, None, None, None, None, None, 0, None,
+    assert lib.lwattn_forward_blocksparse(plan.handle, None, None, None, None, None, None, 0, 0, None,
                                           None) == lw.E_INVALID
+
+
+def test_malformed_csr_offsets_are_clamped_into_the_column_list():
+    """Offsets below 0, decreasing or past nnz are clamped into [0, nnz] by the
+    kernel: no read outside cols, and the lists that remain are the clamped
+    slices (the layout the oracle then sees)."""
+    B, H, n = 1, 2, 320
+    nb = (n + 63) // 64
+    spec = workloads.custom(B, H, n, 64, 0, "bf16", [0] * H, seed=43, n_global=0, max_global=0)
+    cols = np.array([0, 1, 2, 3, 4, 1, 3, 0, 2, 4], np.int32)
+    nnz = cols.size
+    rowptr = np.array([-5, 2, 1, 4, 7, 9, 30, 40, 3, 6, 10], np.int32)
+    assert rowptr.size == H * nb + 1
+    layout = np.zeros((H, nb, nb), np.uint8)
+    for r in range(H * nb):
+        rb = min(max(int(rowptr[r]), 0), nnz)
+        re = min(max(int(rowptr[r + 1]), 0), nnz)
+        nt = min(max(re - rb, 0), nb)
+        for c in cols[rb:rb + nt]:
+            layout[r // nb, r % nb, c] = 1
+    x = workloads.generate(spec, strong=True)
+    dev = "cuda:0"
+    q, k, v = (torch.from_numpy(a).to(dev).to(torch.bfloat16) for a in (x.Q, x.K, x.V))
+    lm = torch.from_numpy(x.lmask).to(dev)
+    plan = make_plan(spec, max_global=0)
+    out = torch.full_like(q, float("nan"))
+    say("block-sparse malformed CSR (clamped)")
+    plan.forward_blocksparse(q, k, v, lm, torch.from_numpy(rowptr).to(dev), torch.from_numpy(cols).to(dev),
+                             out=out)
+    torch.cuda.synchronize()
+    want = oracle.forward_blocksparse(to_np64(q), to_np64(k), to_np64(v), x.lmask, layout, False, spec.scale)
+    got = to_np64(out)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - want).max() <= 2e-2 * np.abs(want).max()

@@ -14,7 +14,12 @@ The default workload is "base": B=1, H=12, n=4096, d=64, w=512 (+-256), no
 dilation, one global token at position 0, bf16 storage, fp32 accumulation.
 
 Timing is "warm": forwards run back to back, so inputs that fit the 256 MB
-last-level cache stay there between steps.  Kernel durations come from HIP
+last-level cache stay there between steps.  After the timed loop, a "cold"
+pass (--cold-steps) writes 1 GiB between forwards, so every forward starts
+with its inputs in HBM only, and reports that kernel time beside the warm one.
+The line also carries on-device peaks measured by the library's probes (a
+matrix-core loop, an HBM read stream) and a plain copy, and the roofline
+fraction against them beside the published peak.  Kernel durations come from HIP
 events that the dispatch of the attention kernel itself records at the start
 and the end of its execution, on every fourth forward of the timed loop
 (recording them on every forward would make the host, not the GPU, set the
@@ -94,6 +99,78 @@ def measured_traffic(workload: str):
     return None
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measure_peaks(lib, dev):
+    """What this GPU delivers, measured with the library's probes and a plain
+    copy (each timed with events over 3 launches after one warm-up):
+    bf16 matrix-core rate, HBM read rate over 2 GiB, device-to-device copy
+    rate over 1 GiB (read + write bytes)."""
+    import ctypes
+    import torch
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = torch.empty(4096, dtype=torch.float32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    iters = 2048
+    t = timed(lambda: lib.lwattn_probe_mfma(iters, ctypes.c_void_p(out.data_ptr()), stream))
+    mfma = 512 * 4 * iters * 8 * 32768 / t / 1e12
+    nread = 2 << 30
+    buf = torch.empty(nread, dtype=torch.uint8, device=dev)
+    buf.fill_(3)
+    t = timed(lambda: lib.lwattn_probe_read(ctypes.c_void_p(buf.data_ptr()), nread,
+                                            ctypes.c_void_p(out.data_ptr()), stream))
+    read = nread / t / 1e9
+    del buf
+    ncopy = 1 << 30
+    a = torch.empty(ncopy, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    t = timed(lambda: b.copy_(a))
+    copy = 2 * ncopy / t / 1e9
+    del a, b
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbs": round(read, 1),
+            "hbm_copy_gbs": round(copy, 1),
+            "how": "lwattn_probe_mfma (8 chains of v_mfma_f32_32x32x16_bf16 per wave, 2 waves/SIMD), "
+                   "lwattn_probe_read over 2 GiB, torch copy of 1 GiB (read + write bytes)"}
+
+
+def time_cold(step, plan, steps, dev):
+    """Kernel time with the last-level cache emptied before every forward: a
+    1 GiB scratch buffer is written between calls (outside the timed kernel);
+    the duration comes from the events the dispatch records."""
+    import torch
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    plan.timing_enable(steps, every=1)
+    for i in range(steps):
+        scratch.fill_(i & 255)
+        step()
+    torch.cuda.synchronize()
+    tot, calls = plan.timing_read()
+    plan.timing_disable()
+    del scratch
+    return tot["attention"] / calls * 1e-3
+
+
 def cpu_baseline(x, budget_s=12.0):
     """The oracle, as it is, on the host cores over a bounded sample of the workload."""
     import numpy as np
@@ -130,7 +207,7 @@ def cpu_baseline(x, budget_s=12.0):
         value = B * n / (t * total_heads / k)
         sample = (f"every query row of {k} of the {total_heads} (batch, head) pairs "
                   f"({k * n} rows, {t:.2f} s), scaled to the full workload")
-    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": sample}
 
 
@@ -151,7 +228,7 @@ def cpu_baseline_backward(x, go, budget_s=12.0):
         t += time.perf_counter() - t0
         reps += 1
     value = spec.B * spec.n * reps / t
-    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"the whole backward, repeated {reps} times ({t:.2f} s)"}
 
 
@@ -172,7 +249,7 @@ def cpu_baseline_causal(x, budget_s=12.0):
         t += time.perf_counter() - t0
         reps += 1
     value = spec.B * spec.n * reps / t
-    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"the whole causal forward, repeated {reps} times ({t:.2f} s)"}
 
 
@@ -200,7 +277,7 @@ def cpu_baseline_causal_backward(x, budget_s=12.0):
         t += time.perf_counter() - t0
         heads += 1
     value = spec.n * heads / spec.H / t          # a token is one row of every head
-    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"{heads} whole (batch row, head) slices of the causal backward ({t:.2f} s), "
                       f"scaled by the {spec.H} heads of a token"}
 
@@ -359,7 +436,7 @@ def cpu_baseline_blocksparse(x, layout, causal, budget_s=12.0):
         rows += idx.size
         count *= 2
     value = rows / spec.H / t
-    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": threads, "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"{rows} random rows of all heads ({t:.2f} s), scaled by 1/H to tokens"}
 
 
@@ -448,7 +525,7 @@ def cpu_baseline_layer(x, X, w, inter, budget_s=12.0):
     oracle.layer_forward(X.reshape(spec.B, spec.n, -1), w, x.lmask, x.gmask, spec.window, spec.dilation,
                          spec.H, 1e-5, threads=threads)
     t = time.perf_counter() - t0
-    return {"value": round(spec.B * spec.n / t, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(spec.B * spec.n / t, 3), "unit": "tokens/s", "cores": threads, "cpu_model": host_cpu_model(), "kind": "oracle",
             "sample": f"the whole layer once ({t:.2f} s; float64 numpy GEMMs, the attention oracle in C)"}
 
 
@@ -630,6 +707,10 @@ def main():
                     help="do not record per-kernel HIP events (roofline fields become null)")
     ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal", "causal_backward", "blocksparse", "layer"), default="forward",
                     help="time the forward (default) or the backward")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="forwards timed cold (1 GiB written between calls); 0 skips the cold mode")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the on-device peak probes (matrix-core loop, HBM read, copy)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device to device 5 times (counter calibration)")
     args = ap.parse_args()
@@ -710,8 +791,17 @@ def main():
 
     roofline = None
     kernels = None
+    tot, calls = plan.timing_read() if not args.no_timing else ({}, 0)
+    plan.timing_disable()
+    # cold mode and the on-device peaks, after the warm events are read
+    cold = None
+    if args.cold_steps > 0:
+        t_cold = time_cold(step, plan, args.cold_steps, dev)
+        st = plan.sync_status()
+        if st != lwattn.OK:
+            raise SystemExit(f"forward failed: {lwattn.strerror(st)}")
+    peaks = None if args.no_peaks else measure_peaks(plan.lib, dev)
     if not args.no_timing:
-        tot, calls = plan.timing_read()
         kernels = {k: round(v * 1e3 / calls, 3) for k, v in tot.items()}   # us per launch
         t_attn = tot["attention"] / calls * 1e-3                            # s per launch
         tflops = flop / t_attn / 1e12
@@ -726,6 +816,12 @@ def main():
         else:
             roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic}
+        if peaks:
+            # the same achieved figure against what the probes measured on this GPU
+            meas = peaks["hbm_read_gbs"] if hbm_bound else peaks["mfma_bf16_tflops"]
+            if hbm_bound or spec.dtype == "bf16":
+                roofline["frac_of_measured_peak"] = round(roofline["achieved"] / meas, 4)
+                roofline["measured_peak"] = meas
         roofline.update({
             "kernel": "attn_kernel",
             "algorithmic_flop": flop, "algorithmic_bytes": nbytes,
@@ -736,6 +832,14 @@ def main():
             "source_sha256": source_hash(),
         })
 
+    if args.cold_steps > 0:
+        cold = {"steps": args.cold_steps, "us_per_launch": round(t_cold * 1e6, 2),
+                "tokens_per_s": round(tokens / t_cold, 1),
+                "tflops": round(flop / t_cold / 1e12, 2), "mfma_frac": round(flop / t_cold / 1e12 / peak, 4),
+                "hbm_gbs": round(nbytes / t_cold / 1e9, 1),
+                "hbm_frac": round(nbytes / t_cold / 1e9 / PEAK_HBM_GBS, 4),
+                "how": "1 GiB written between forwards (outside the timed kernel); kernel time from the "
+                       "events its dispatch records, every forward"}
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -756,6 +860,8 @@ def main():
         "pct_mfma_peak": round(100 * flop / (elapsed / args.steps) / 1e12 / peak, 2),
         "kernel_us": kernels,
         "roofline": roofline,
+        "cold": cold,
+        "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x)

@@ -300,6 +300,21 @@ lwattn_status lwattn_timing_disable(lwattn_plan_t plan);
  * to be destroyed).  LWATTN_E_INVALID for a null plan. */
 lwattn_status lwattn_test_inject_wait_timeout(lwattn_plan_t plan);
 
+/* Measurement aids (bench and tests only): what the chip delivers, so that
+ * roofline fractions can be stated against measured peaks as well as the
+ * published ones.  Each enqueues one kernel on `stream` and returns at once.
+ * lwattn_probe_mfma: 512 workgroups of 4 waves; every wave runs `iters`
+ *   rounds of 8 independent v_mfma_f32_32x32x16_bf16 (32768 flops each), so a
+ *   launch performs 512 * 4 * iters * 8 * 32768 flops; out: device float
+ *   [2048], one value per wave (written so that nothing is optimised away).
+ * lwattn_probe_read: reads `bytes` (rounded down to 16) of device memory at
+ *   `buf` (16-byte aligned) once, 16-byte loads in a grid-stride stream;
+ *   out: device float [4096], one value per workgroup.
+ * Errors: LWATTN_E_INVALID for null or misaligned pointers or negative
+ * sizes; LWATTN_E_DEVICE if the launch fails. */
+lwattn_status lwattn_probe_mfma(int32_t iters, float* out, hipStream_t stream);
+lwattn_status lwattn_probe_read(const void* buf, int64_t bytes, float* out, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* lwattn_strerror(lwattn_status s);
 

@@ -12,6 +12,7 @@ DEPS = [SRC, os.path.join(PKG, "csrc", "kernels.hpp"), os.path.join(PKG, "csrc",
         os.path.join(PKG, "csrc", "causal.hpp"),
         os.path.join(PKG, "csrc", "blocksparse.hpp"),
         os.path.join(PKG, "csrc", "layer.hpp"),
+        os.path.join(PKG, "csrc", "probe.hpp"),
         os.path.join(ROOT, "include", "lwattn.h")]
 LIB = os.path.join(PKG, "liblwattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

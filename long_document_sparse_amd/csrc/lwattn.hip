@@ -20,6 +20,7 @@
 #include "causal.hpp"
 #include "blocksparse.hpp"
 #include "layer.hpp"
+#include "probe.hpp"
 
 #include <rocblas/rocblas.h>
 #include "lwattn.h"
@@ -44,6 +45,15 @@ bool hip_ok(hipError_t e, const char* what) {
 
 }  // namespace
 
+// Launch geometry of the forward (attn_kernel), shared by the plan and the
+// allocation-free entry point.
+struct FwdGeom {
+  int nqt = 0, nqg = 0, nsplit = 0, ksplit = 0;
+  int n_comp_wg = 0, n_glob_wg = 0, n_band_wg = 0, blocks_per_b = 0;
+  int uni_stride = 0, blocks_per_head = 0, band_fast = 0;
+  size_t smem = 0;
+};
+
 struct lwattn_plan_s {
   lwattn_config cfg;
   std::vector<int32_t> gap;
@@ -55,6 +65,7 @@ struct lwattn_plan_s {
   int band_fast = 0;
   std::vector<int32_t> stride_host, blk_host;
   size_t smem = 0;
+  FwdGeom geom;
   // workspace
   uint8_t* flags = nullptr;
   int32_t* gidx = nullptr;
@@ -181,6 +192,170 @@ static bool layernorm(int H, const float* G, const void* b, const __bf16* R, con
   }
 }
 
+
+// Launch geometry of the forward (attn_kernel), computed by forward_geometry
+// below.  stride [H] and blk [H + 1] receive each head's stride and the prefix
+// of band workgroups per batch row.
+
+static bool forward_geometry(const lwattn_config& c, const int32_t* gap, int ncu, FwdGeom& g, int32_t* stride,
+                             int32_t* blk) {
+  const int B = c.B, H = c.H, n = c.n;
+  blk[0] = 0;
+  for (int h = 0; h < H; ++h) {
+    const int s = gap[h] + 1;
+    stride[h] = s;
+    int64_t nb = 0;
+    for (int rho = 0; rho < s && rho < n; ++rho) {
+      const int64_t nr = ((int64_t)n - rho + s - 1) / s;
+      nb += (nr + lwk::ROWS_WG - 1) / lwk::ROWS_WG;
+    }
+    if ((int64_t)blk[h] + nb > INT32_MAX) return false;
+    blk[h + 1] = blk[h] + (int32_t)nb;
+  }
+  g.blocks_per_b = blk[H];
+  bool uni = H > 0;
+  for (int h = 1; h < H; ++h) uni = uni && stride[h] == stride[0];
+  g.uni_stride = uni ? stride[0] : 0;
+  g.blocks_per_head = uni ? blk[1] : 0;
+  const int64_t nband = (int64_t)B * blk[H];
+  // band workgroups may take the bf16 fast path when every subsequence key
+  // they stage has a byte offset that fits in 32 bits
+  int smax = 1;
+  for (int h = 0; h < H; ++h) smax = std::max(smax, stride[h]);
+  g.band_fast = (c.dtype == LWATTN_BF16 && (int64_t)n + 128 * (int64_t)smax < ((int64_t)1 << 24)) ? 1 : 0;
+  // compaction workgroups lead the grid, padded to a multiple of 8 so that the
+  // band workgroups behind them keep their XCD placement
+  const int64_t ncomp = ((int64_t)B + 7) / 8 * 8;
+  // global-row geometry: the key slices are sized so that the global-row
+  // workgroups fill what the compaction and band workgroups leave of the last
+  // round of workgroup slots (two per compute unit), with at least 64 of them.
+  // When that round is nearly empty (under a quarter used), a full round of
+  // global-row workgroups would run behind the band ones with long merges of
+  // many slices: a quarter of the slots serves them better (measured at
+  // B=1, H=16, n=4096, 64 globals: 47 instead of 105 us; B=4: 114 instead of
+  // 134 us)
+  const int64_t slots = 2 * (int64_t)ncu;
+  g.nqt = ceil_div(c.max_global, 32);
+  g.nqg = ceil_div(g.nqt, lwk::NW);
+  int64_t nglob = 0;
+  g.ksplit = g.nsplit = 0;
+  if (g.nqt > 0 && n > 0 && B > 0 && H > 0) {
+    const int64_t units = (int64_t)B * H * g.nqg;
+    const int64_t used = (ncomp + nband) % slots;
+    int64_t target = used < slots / 4 ? slots / 4 : slots - used;
+    if (target < 64) target = 64;
+    int64_t want = (target + units - 1) / units;
+    const int64_t maxs = (n + 127) / 128;
+    if (want > maxs) want = maxs;
+    if (want < 1) want = 1;
+    // but no slice longer than 4096 keys, so that no global-row workgroup
+    // outlasts the band ones on long sequences
+    if (want < (n + 4095) / 4096) want = (n + 4095) / 4096;
+    g.ksplit = ceil_div(ceil_div(n, want), 64) * 64;   // whole 64-key steps
+    g.nsplit = ceil_div(n, g.ksplit);
+    nglob = units * g.nsplit;
+  }
+  const int64_t nglob_pad = (nglob + 7) / 8 * 8;
+  if (ncomp + nband + nglob_pad > INT32_MAX) return false;
+  g.n_comp_wg = (int)ncomp;
+  g.n_band_wg = (int)nband;
+  g.n_glob_wg = (int)nglob_pad;
+  g.smem = c.dtype == LWATTN_BF16 ? lwk::smem_bytes<true>() : lwk::smem_bytes<false>();
+  return true;
+}
+
+// Device workspace of one forward: where attn_kernel keeps the flags, the
+// global index, the per-row status and readiness words, the fault word, the
+// global rows' partials and the merge counters.
+struct FwdWork {
+  uint8_t* flags;
+  int32_t *gidx, *gcnt, *status, *tile_cnt, *ready, *fault;
+  float *part_o, *part_ml;
+  const int32_t *head_stride, *head_blk;   // device copies (read only when H > MAXH_ARG)
+};
+
+static size_t fwd_parts(const lwattn_config& c, const FwdGeom& g) {
+  return (size_t)c.B * c.H * g.nqt * (g.nsplit > 0 ? g.nsplit : 0) * 32;
+}
+
+static void forward_params(lwk::Params& prm, const lwattn_config& c, const FwdGeom& g, const FwdWork& w,
+                           const int32_t* stride, const int32_t* blk, const void* Q, const void* K, const void* V,
+                           const void* Qg, const void* Kg, const void* Vg, const float* lmask, const float* gmask,
+                           void* O, int32_t epoch) {
+  prm.Q = (const uint8_t*)Q;
+  prm.K = (const uint8_t*)K;
+  prm.V = (const uint8_t*)V;
+  prm.Qg = (const uint8_t*)Qg;
+  prm.Kg = (const uint8_t*)Kg;
+  prm.Vg = (const uint8_t*)Vg;
+  prm.O = (uint8_t*)O;
+  prm.lmask = lmask;
+  prm.gmask = gmask;
+  prm.flags = w.flags;
+  prm.gidx = w.gidx;
+  prm.gcnt = w.gcnt;
+  prm.status = w.status;
+  prm.part_o = w.part_o;
+  prm.part_ml = w.part_ml;
+  prm.tile_cnt = w.tile_cnt;
+  prm.ready = w.ready;
+  prm.fault = w.fault;
+  prm.epoch = epoch;
+  prm.publish = epoch;
+  prm.spin_limit = (1 << 18) + (int32_t)(c.n >> 2);
+  prm.n_comp_wg = g.n_comp_wg;
+  prm.head_stride = w.head_stride;
+  prm.head_blk = w.head_blk;
+  prm.B = c.B;
+  prm.H = c.H;
+  prm.n = c.n;
+  prm.r = (int)std::min<int64_t>(c.window / 2, c.n);
+  prm.max_global = c.max_global;
+  prm.nqt = g.nqt;
+  prm.nqg = g.nqg;
+  prm.nsplit = g.nsplit;
+  prm.ksplit = g.ksplit;
+  prm.n_glob_wg = g.n_glob_wg;
+  prm.n_band_wg = g.n_band_wg;
+  prm.blocks_per_b = g.blocks_per_b;
+  prm.c = c.scale * 1.4426950408889634f;
+  prm.mask_vec = ((((uintptr_t)lmask | (uintptr_t)gmask) & 15u) == 0 && (c.n % 4) == 0) ? 1 : 0;
+  prm.uni_stride = g.uni_stride;
+  prm.blocks_per_head = g.blocks_per_head;
+  prm.band_fast = g.band_fast;
+  for (int h = 0; h < lwk::MAXH_ARG; ++h) prm.hs[h] = h < c.H ? stride[h] : 0;
+  for (int h = 0; h <= lwk::MAXH_ARG; ++h) prm.hb[h] = h <= c.H ? blk[h] : 0;
+}
+
+static bool launch_forward(const lwattn_config& c, const FwdGeom& g, const lwk::Params& prm, hipStream_t stream,
+                           hipEvent_t ev0, hipEvent_t ev1) {
+  const int grid = g.n_comp_wg + g.n_band_wg + g.n_glob_wg;
+  if (c.dtype == LWATTN_BF16)
+    hipExtLaunchKernelGGL(lwk::attn_kernel<true>, dim3(grid), dim3(lwk::NT), (uint32_t)g.smem, stream, ev0, ev1, 0u,
+                          prm);
+  else
+    hipExtLaunchKernelGGL(lwk::attn_kernel<false>, dim3(grid), dim3(lwk::NT), (uint32_t)g.smem, stream, ev0, ev1,
+                          0u, prm);
+  return hip_ok(hipGetLastError(), "hipGetLastError");
+}
+
+static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+// Checks shared by the forward entry points: LWATTN_OK when the call may
+// launch (or is empty, *empty set).
+static lwattn_status forward_args(const lwattn_config& c, const void* Q, const void* K, const void* V, const void* Qg,
+                                  const void* Kg, const void* Vg, const float* lmask, const float* gmask, void* O,
+                                  bool* empty) {
+  *empty = (int64_t)c.B * c.H * c.n == 0;
+  if (*empty) return LWATTN_OK;
+  const void* ptrs[] = {Q, K, V, Qg, Kg, Vg, O};
+  for (const void* q : ptrs)
+    if (!q || !aligned16(q)) return LWATTN_E_INVALID;
+  if (!lmask || !gmask || ((uintptr_t)lmask & 3u) || ((uintptr_t)gmask & 3u)) return LWATTN_E_INVALID;
+  return LWATTN_OK;
+}
+
+
 extern "C" {
 
 const char* lwattn_strerror(lwattn_status s) {
@@ -236,81 +411,45 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
     for (int h = 0; h < H; ++h) p->gap[h] = cfg->dilation[h];
   p->cfg.dilation = nullptr;   // the plan keeps its own copy
 
-  // band geometry: per head, sum over residue classes of ceil(n_rho / 128)
-  // (forward) and of ceil(n_rho / 64) (backward)
-  std::vector<int32_t> stride(H), blk(H + 1, 0), blk64(H + 1, 0);
-  for (int h = 0; h < H; ++h) {
-    const int s = p->gap[h] + 1;
-    stride[h] = s;
-    int64_t nb = 0, nb64 = 0;
-    for (int rho = 0; rho < s && rho < n; ++rho) {
-      const int64_t nr = ((int64_t)n - rho + s - 1) / s;
-      nb += (nr + lwk::ROWS_WG - 1) / lwk::ROWS_WG;
-      nb64 += (nr + lwk::bw::T - 1) / lwk::bw::T;
-    }
-    blk[h + 1] = blk[h] + (int32_t)nb;
-    blk64[h + 1] = blk64[h] + (int32_t)nb64;
-  }
-  p->blocks64_per_b = blk64[H];
-  p->blocks_per_b = blk[H];
-  p->stride_host = stride;
-  p->blk_host = blk;
-  bool uni = H > 0;
-  for (int h = 1; h < H; ++h) uni = uni && stride[h] == stride[0];
-  p->uni_stride = uni ? stride[0] : 0;
-  p->blocks_per_head = uni ? blk[1] : 0;
-  const int64_t nband = (int64_t)B * blk[H];
-  // band workgroups may take the bf16 fast path when every subsequence key
-  // they stage has a byte offset that fits in 32 bits
-  int smax = 1;
-  for (int h = 0; h < H; ++h) smax = std::max(smax, stride[h]);
-  p->band_fast = (cfg->dtype == LWATTN_BF16 && (int64_t)n + 128 * (int64_t)smax < ((int64_t)1 << 24)) ? 1 : 0;
-  // compaction workgroups lead the grid, padded to a multiple of 8 so that the
-  // band workgroups behind them keep their XCD placement
-  const int64_t ncomp = ((int64_t)B + 7) / 8 * 8;
-  // global-row geometry: the key slices are sized so that the global-row
-  // workgroups fill what the compaction and band workgroups leave of the last
-  // round of workgroup slots (two per compute unit), with at least 64 of them.
-  // When that round is nearly empty (under a quarter used), a full round of
-  // global-row workgroups would run behind the band ones with long merges of
-  // many slices: a quarter of the slots serves them better (measured at
-  // B=1, H=16, n=4096, 64 globals: 47 instead of 105 us; B=4: 114 instead of
-  // 134 us)
+  // band geometry of the forward (per head, sum over residue classes of
+  // ceil(n_rho / 128)) and of the backward (of ceil(n_rho / 64))
   int ncu = 256;
   {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, hip_device) == hipSuccess && prop.multiProcessorCount > 0)
-      ncu = prop.multiProcessorCount;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, hip_device) == hipSuccess && v > 0)
+      ncu = v;
   }
-  const int64_t slots = 2 * (int64_t)ncu;
-  p->nqt = ceil_div(cfg->max_global, 32);
-  p->nqg = ceil_div(p->nqt, lwk::NW);
-  int64_t nglob = 0;
-  if (p->nqt > 0 && n > 0 && B > 0 && H > 0) {
-    const int64_t units = (int64_t)B * H * p->nqg;
-    const int64_t used = (ncomp + nband) % slots;
-    int64_t target = used < slots / 4 ? slots / 4 : slots - used;
-    if (target < 64) target = 64;
-    int64_t want = (target + units - 1) / units;
-    const int64_t maxs = (n + 127) / 128;
-    if (want > maxs) want = maxs;
-    if (want < 1) want = 1;
-    // but no slice longer than 4096 keys, so that no global-row workgroup
-    // outlasts the band ones on long sequences
-    if (want < (n + 4095) / 4096) want = (n + 4095) / 4096;
-    p->ksplit = ceil_div(ceil_div(n, want), 64) * 64;   // whole 64-key steps
-    p->nsplit = ceil_div(n, p->ksplit);
-    nglob = units * p->nsplit;
-  }
-  const int64_t nglob_pad = (nglob + 7) / 8 * 8;
-  if (ncomp + nband + nglob_pad > INT32_MAX) {
+  std::vector<int32_t> stride(H), blk(H + 1, 0), blk64(H + 1, 0);
+  FwdGeom g;
+  if (!forward_geometry(p->cfg, p->gap.data(), ncu, g, stride.data(), blk.data())) {
     free_plan(p);
     return LWATTN_E_INVALID;
   }
-  p->n_comp_wg = (int)ncomp;
-  p->n_band_wg = (int)nband;
-  p->n_glob_wg = (int)nglob_pad;
-  p->smem = cfg->dtype == LWATTN_BF16 ? lwk::smem_bytes<true>() : lwk::smem_bytes<false>();
+  for (int h = 0; h < H; ++h) {
+    const int s = stride[h];
+    int64_t nb64 = 0;
+    for (int rho = 0; rho < s && rho < n; ++rho) {
+      const int64_t nr = ((int64_t)n - rho + s - 1) / s;
+      nb64 += (nr + lwk::bw::T - 1) / lwk::bw::T;
+    }
+    blk64[h + 1] = blk64[h] + (int32_t)nb64;
+  }
+  p->geom = g;
+  p->blocks64_per_b = blk64[H];
+  p->blocks_per_b = g.blocks_per_b;
+  p->stride_host = stride;
+  p->blk_host = blk;
+  p->uni_stride = g.uni_stride;
+  p->blocks_per_head = g.blocks_per_head;
+  p->band_fast = g.band_fast;
+  p->nqt = g.nqt;
+  p->nqg = g.nqg;
+  p->ksplit = g.ksplit;
+  p->nsplit = g.nsplit;
+  p->n_comp_wg = g.n_comp_wg;
+  p->n_band_wg = g.n_band_wg;
+  p->n_glob_wg = g.n_glob_wg;
+  p->smem = g.smem;
 
   // workspace
   const size_t bn = (size_t)B * n;
@@ -324,7 +463,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->gidx, bn * 4);
   alloc((void**)&p->gcnt, (size_t)B * 4);
   alloc((void**)&p->status, (size_t)B * 4);
-  const size_t nparts = (size_t)B * H * p->nqt * (p->nsplit > 0 ? p->nsplit : 0) * 32;
+  const size_t nparts = fwd_parts(p->cfg, g);
   alloc((void**)&p->part_o, nparts * lwk::D * 4);
   alloc((void**)&p->part_ml, nparts * 2 * 4);
   alloc((void**)&p->tile_cnt, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4);
@@ -375,43 +514,32 @@ lwattn_status lwattn_destroy(lwattn_plan_t p) {
   return LWATTN_OK;
 }
 
-static bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
-
 lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, const void* V,
                              const void* Qg, const void* Kg, const void* Vg,
                              const float* lmask, const float* gmask, void* O, hipStream_t stream) {
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
-  if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
-  const void* ptrs[] = {Q, K, V, Qg, Kg, Vg, O};
-  for (const void* q : ptrs)
-    if (!q || !aligned16(q)) return LWATTN_E_INVALID;
-  if (!lmask || !gmask || ((uintptr_t)lmask & 3u) || ((uintptr_t)gmask & 3u)) return LWATTN_E_INVALID;
+  bool empty = false;
+  const lwattn_status ast = forward_args(c, Q, K, V, Qg, Kg, Vg, lmask, gmask, O, &empty);
+  if (ast != LWATTN_OK || empty) return ast;
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
 
-  lwk::Params prm;
-  prm.Q = (const uint8_t*)Q;
-  prm.K = (const uint8_t*)K;
-  prm.V = (const uint8_t*)V;
-  prm.Qg = (const uint8_t*)Qg;
-  prm.Kg = (const uint8_t*)Kg;
-  prm.Vg = (const uint8_t*)Vg;
-  prm.O = (uint8_t*)O;
-  prm.lmask = lmask;
-  prm.gmask = gmask;
-  prm.flags = p->flags;
-  prm.gidx = p->gidx;
-  prm.gcnt = p->gcnt;
-  prm.status = p->status;
-  prm.part_o = p->part_o;
-  prm.part_ml = p->part_ml;
-  prm.tile_cnt = p->tile_cnt;
-  prm.ready = p->ready;
-  prm.fault = p->fault;
+  FwdWork w;
+  w.flags = p->flags;
+  w.gidx = p->gidx;
+  w.gcnt = p->gcnt;
+  w.status = p->status;
+  w.tile_cnt = p->tile_cnt;
+  w.ready = p->ready;
+  w.fault = p->fault;
+  w.part_o = p->part_o;
+  w.part_ml = p->part_ml;
+  w.head_stride = p->head_stride;
+  w.head_blk = p->head_blk;
   p->epoch = p->epoch >= INT32_MAX - 1 ? 1 : p->epoch + 1;
-  prm.epoch = p->epoch;
-  prm.publish = p->epoch;
-  prm.spin_limit = (1 << 18) + (int32_t)(c.n >> 2);
+  lwk::Params prm;
+  forward_params(prm, c, p->geom, w, p->stride_host.data(), p->blk_host.data(), Q, K, V, Qg, Kg, Vg, lmask, gmask, O,
+                 p->epoch);
   if (p->inject_timeout) {
     // the rows are published under another number and nobody waits long:
     // every waiting workgroup gives up, sets the fault word and skips its work
@@ -419,28 +547,6 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
     prm.publish = -1;
     prm.spin_limit = 64;
   }
-  prm.n_comp_wg = p->n_comp_wg;
-  prm.head_stride = p->head_stride;
-  prm.head_blk = p->head_blk;
-  prm.B = c.B;
-  prm.H = c.H;
-  prm.n = c.n;
-  prm.r = (int)std::min<int64_t>(c.window / 2, c.n);
-  prm.max_global = c.max_global;
-  prm.nqt = p->nqt;
-  prm.nqg = p->nqg;
-  prm.nsplit = p->nsplit;
-  prm.ksplit = p->ksplit;
-  prm.n_glob_wg = p->n_glob_wg;
-  prm.n_band_wg = p->n_band_wg;
-  prm.blocks_per_b = p->blocks_per_b;
-  prm.c = c.scale * 1.4426950408889634f;
-  prm.mask_vec = ((((uintptr_t)lmask | (uintptr_t)gmask) & 15u) == 0 && (c.n % 4) == 0) ? 1 : 0;
-  prm.uni_stride = p->uni_stride;
-  prm.blocks_per_head = p->blocks_per_head;
-  prm.band_fast = p->band_fast;
-  for (int h = 0; h < lwk::MAXH_ARG; ++h) prm.hs[h] = h < c.H ? p->stride_host[h] : 0;
-  for (int h = 0; h <= lwk::MAXH_ARG; ++h) prm.hb[h] = h <= c.H ? p->blk_host[h] : 0;
 
   bool timed = false;
   if (p->timing_cap > 0 && p->timing_calls < p->timing_cap) {
@@ -454,15 +560,7 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
     ev0 = p->events[(size_t)p->timing_calls * (kNumKernels + 1)];
     ev1 = p->events[(size_t)p->timing_calls * (kNumKernels + 1) + 1];
   }
-  const int grid = p->n_comp_wg + p->n_band_wg + p->n_glob_wg;
-  if (c.dtype == LWATTN_BF16)
-    hipExtLaunchKernelGGL(lwk::attn_kernel<true>, dim3(grid), dim3(lwk::NT), (uint32_t)p->smem, stream,
-                          ev0, ev1, 0u, prm);
-  else
-    hipExtLaunchKernelGGL(lwk::attn_kernel<false>, dim3(grid), dim3(lwk::NT), (uint32_t)p->smem, stream,
-                          ev0, ev1, 0u, prm);
-  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-
+  if (!launch_forward(c, p->geom, prm, stream, ev0, ev1)) return LWATTN_E_DEVICE;
   if (timed) ++p->timing_calls;
   return LWATTN_OK;
 }
@@ -937,5 +1035,23 @@ lwattn_status lwattn_timing_read_backward(lwattn_plan_t p, float* ms, int32_t ca
   *ncalls = p->bw_calls;
   return LWATTN_OK;
 }
+
+
+lwattn_status lwattn_probe_mfma(int32_t iters, float* out, hipStream_t stream) {
+  if (iters < 0 || !out || ((uintptr_t)out & 3u)) return LWATTN_E_INVALID;
+  hipLaunchKernelGGL(lwk::probe::mfma_probe_kernel, dim3(lwk::probe::MFMA_BLOCKS), dim3(lwk::probe::MFMA_THREADS), 0,
+                     stream, (int)iters, 1.0f / 1024.0f, out);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  return LWATTN_OK;
+}
+
+lwattn_status lwattn_probe_read(const void* buf, int64_t bytes, float* out, hipStream_t stream) {
+  if (!buf || !out || bytes < 0 || ((uintptr_t)buf & 15u) || ((uintptr_t)out & 3u)) return LWATTN_E_INVALID;
+  hipLaunchKernelGGL(lwk::probe::read_probe_kernel, dim3(lwk::probe::READ_BLOCKS), dim3(lwk::probe::READ_THREADS), 0,
+                     stream, (const uint4*)buf, bytes / 16, out);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  return LWATTN_OK;
+}
+
 
 }  // extern "C"

@@ -58,6 +58,8 @@ SIGNATURES = [
                                                    ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     ("lwattn_timing_disable", ctypes.c_int, [_c_p]),
     ("lwattn_test_inject_wait_timeout", ctypes.c_int, [_c_p]),
+    ("lwattn_probe_mfma", ctypes.c_int, [_i32, _c_p, _c_p]),
+    ("lwattn_probe_read", ctypes.c_int, [_c_p, ctypes.c_int64, _c_p, _c_p]),
     ("lwattn_strerror", ctypes.c_char_p, [ctypes.c_int]),
 ]
 

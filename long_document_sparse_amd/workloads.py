@@ -125,9 +125,9 @@ class Inputs:
         return (self.Q, self.K, self.V, self.Qg, self.Kg, self.Vg)
 
 
-def generate(spec: Spec, strong: bool = False, seed: Optional[int] = None) -> Inputs:
-    rng = np.random.default_rng(spec.seed if seed is None else seed)
-    B, H, n, d = spec.B, spec.H, spec.n, spec.d
+def _structure(spec: Spec, rng) -> tuple:
+    """Draws 1-3 of the recipe: (lmask, gmask, pad_len, global_pos)."""
+    B, n = spec.B, spec.n
 
     # 1. pad lengths (and 2. which sequence is padded)
     pad_len = np.zeros(B, np.int64)
@@ -161,6 +161,19 @@ def generate(spec: Spec, strong: bool = False, seed: Optional[int] = None) -> In
             pos = np.sort(valid[rng.choice(valid.size, size=g, replace=False)])
         gmask[b, pos] = 1.0
         global_pos.append(pos.astype(np.int64))
+    return lmask, gmask, pad_len, global_pos
+
+
+def structure(spec: Spec, seed: Optional[int] = None) -> tuple:
+    """The masks of a workload alone, (lmask, gmask, pad_len, global_pos): the
+    same draws as generate() makes before the tensors."""
+    return _structure(spec, np.random.default_rng(spec.seed if seed is None else seed))
+
+
+def generate(spec: Spec, strong: bool = False, seed: Optional[int] = None) -> Inputs:
+    rng = np.random.default_rng(spec.seed if seed is None else seed)
+    B, H, n, d = spec.B, spec.H, spec.n, spec.d
+    lmask, gmask, pad_len, global_pos = _structure(spec, rng)
 
     # 4. the six projected tensors
     div = np.float32(1.0) if strong else np.float32(math.sqrt(d))

@@ -298,3 +298,28 @@ def test_rows_equal_forward_rows():
     idx = np.random.default_rng(0).choice(2 * 3 * 300, size=200, replace=False)
     part = oracle.rows(*x.tensors(), x.lmask, x.gmask, spec.window, idx, spec.dilation, spec.scale)
     assert np.array_equal(part, full.reshape(-1, 64)[idx])
+
+
+def test_closed_form_helper_matches_the_oracle_forward():
+    """The helper behind the full-size GPU closed-form test reproduces the
+    oracle's forward with Q = Qg = 0 and one-hot V, Vg (distinct shifts), over
+    dilation, padding and globals inside windows."""
+    import closed_form as cf
+    B, H, n, d, w = 2, 3, 90, 64, 10
+    dil = [0, 1, 2]
+    rng = np.random.default_rng(5)
+    lm = np.ones((B, n), np.float32)
+    lm[1, 70:] = 0.0
+    lm[0, [13, 40]] = 0.0
+    gm = np.zeros((B, n), np.float32)
+    gm[0, [0, 20, 44]] = 1.0
+    gm[1, [5, 71]] = 1.0            # 71 is padded
+    Z = np.zeros((B, H, n, d), np.float32)
+    K = rng.standard_normal((B, H, n, d)).astype(np.float32)
+    V = np.broadcast_to(cf.one_hot_rows(n, d, cf.SHIFT_LOCAL), (B, H, n, d)).astype(np.float32)
+    Vg = np.broadcast_to(cf.one_hot_rows(n, d, cf.SHIFT_GLOBAL), (B, H, n, d)).astype(np.float32)
+    got = oracle.forward(Z, K, V, Z, K, Vg, lm, gm, w, dil, 0.125, threads=2)
+    for b in range(B):
+        for h in range(H):
+            want = cf.expected_rows(lm[b], gm[b], w, dil[h], d)
+            np.testing.assert_allclose(got[b, h], want, rtol=1e-14, atol=1e-15)

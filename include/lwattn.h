@@ -56,7 +56,9 @@ typedef enum {
   LWATTN_E_UNSUPPORTED = 2,       /* valid but not implemented (d != 64) */
   LWATTN_E_NOMEM = 3,             /* workspace allocation failed */
   LWATTN_E_DEVICE = 4,            /* a HIP call failed */
-  LWATTN_E_TOO_MANY_GLOBALS = 5   /* a batch row had more than max_global global tokens */
+  LWATTN_E_TOO_MANY_GLOBALS = 5,  /* a batch row had more than max_global global tokens */
+  LWATTN_E_SCRATCH = 6            /* lwattn_forward_noalloc: the problem needs more workspace
+                                     than its static buffer holds */
 } lwattn_status;
 
 typedef struct {
@@ -299,6 +301,35 @@ lwattn_status lwattn_timing_disable(lwattn_plan_t plan);
  * lwattn_sync_status reports LWATTN_E_DEVICE from then on (the plan is then
  * to be destroyed).  LWATTN_E_INVALID for a null plan. */
 lwattn_status lwattn_test_inject_wait_timeout(lwattn_plan_t plan);
+
+/* Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It computes exactly what lwattn_forward computes for a plan
+ * made from *cfg (same kernel, same launch geometry), without a plan: the
+ * workspace is a static device buffer of 32 MiB per GPU, held from the first
+ * call on that GPU until the process ends, and the call makes no hipMalloc,
+ * hipFree or other allocating call, on the device or the host.
+ * cfg: as for lwattn_plan, with H <= 32 (the head tables travel in the kernel
+ * arguments).  hip_device: the GPU the tensors live on (< 64); it becomes the
+ * current device.  Q .. O, lmask, gmask: as lwattn_forward.  status: NULL, or
+ * device int32 [B + 1], written on `stream` after the forward: [0] nonzero if
+ * a workgroup gave up waiting for its row's global index (O undefined), [1 + b]
+ * = 1 if batch row b had more than max_global global tokens (its O undefined),
+ * else 0.  Asynchronous on `stream`, no host sync.  Every call on one GPU
+ * shares that GPU's buffer (the words that must start at zero are cleared by
+ * a kernel at the start of each call): calls that may overlap on one GPU, on
+ * different streams or from different threads, race and must be serialised
+ * by the caller.  The workspace needed is about B n 5 bytes plus, for the
+ * global rows, B H ceil(max_global / 32) nsplit 8448 bytes (nsplit <= 32
+ * key slices); a problem that needs more than the buffer returns
+ * LWATTN_E_SCRATCH before anything is launched.
+ * Errors: as lwattn_check_config; LWATTN_E_INVALID for a null or misaligned
+ * pointer or a bad hip_device; LWATTN_E_UNSUPPORTED for H > 32;
+ * LWATTN_E_SCRATCH; LWATTN_E_DEVICE if a HIP call fails. */
+lwattn_status lwattn_forward_noalloc(const lwattn_config* cfg, int hip_device, const void* Q, const void* K,
+                                     const void* V, const void* Qg, const void* Kg, const void* Vg,
+                                     const float* lmask, const float* gmask, void* O, int32_t* status,
+                                     hipStream_t stream);
 
 /* Measurement aids (bench and tests only): what the chip delivers, so that
  * roofline fractions can be stated against measured peaks as well as the

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -356,6 +357,45 @@ static lwattn_status forward_args(const lwattn_config& c, const void* Q, const v
 }
 
 
+// ---------------------------------------------------------------------------
+// Allocation-free forward.  Its workspace is one file-scope device array per
+// GPU, `scratch`, of kScratchBytes; the host never passes the array's name to
+// a kernel (in host code that name is a stand-in, not a device address) but
+// the address hipGetSymbolAddress returned for that device, looked up once per
+// device with the device current.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+int g_scratch_ncu[kMaxDevices];
+
+// The per-device address of `scratch` and the device's compute-unit count;
+// nullptr if the lookup failed.  The device must be current.
+void* scratch_of(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (!hip_ok(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress") || !ptr) return nullptr;
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+    g_scratch_ncu[dev] = ncu;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+}  // namespace
+
+// Zeroes `count` 32-bit words (a kernel rather than a memset, so that the
+// call can sit in a captured graph).
+__global__ void zero_words_kernel(int32_t* p, int count) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
 extern "C" {
 
 const char* lwattn_strerror(lwattn_status s) {
@@ -366,6 +406,7 @@ const char* lwattn_strerror(lwattn_status s) {
     case LWATTN_E_NOMEM: return "device workspace allocation failed";
     case LWATTN_E_DEVICE: return "HIP runtime error";
     case LWATTN_E_TOO_MANY_GLOBALS: return "a batch row has more global tokens than max_global";
+    case LWATTN_E_SCRATCH: return "the problem needs more workspace than the static no-allocation buffer holds";
   }
   return "unknown status";
 }
@@ -1053,5 +1094,69 @@ lwattn_status lwattn_probe_read(const void* buf, int64_t bytes, float* out, hipS
   return LWATTN_OK;
 }
 
+
+lwattn_status lwattn_forward_noalloc(const lwattn_config* cfg, int hip_device, const void* Q, const void* K,
+                                     const void* V, const void* Qg, const void* Kg, const void* Vg,
+                                     const float* lmask, const float* gmask, void* O, int32_t* status,
+                                     hipStream_t stream) {
+  lwattn_status st = lwattn_check_config(cfg);
+  if (st != LWATTN_OK) return st;
+  const lwattn_config& c = *cfg;
+  if (hip_device < 0 || hip_device >= kMaxDevices) return LWATTN_E_INVALID;
+  if (status && ((uintptr_t)status & 3u)) return LWATTN_E_INVALID;
+  bool empty = false;
+  st = forward_args(c, Q, K, V, Qg, Kg, Vg, lmask, gmask, O, &empty);
+  if (st != LWATTN_OK || empty) return st;
+  // the head tables travel by value in the kernel arguments
+  if (c.H > lwk::MAXH_ARG) return LWATTN_E_UNSUPPORTED;
+  int32_t gap[lwk::MAXH_ARG], stride[lwk::MAXH_ARG], blk[lwk::MAXH_ARG + 1];
+  for (int h = 0; h < c.H; ++h) gap[h] = c.dilation ? c.dilation[h] : 0;
+  if (!hip_ok(hipSetDevice(hip_device), "hipSetDevice")) return LWATTN_E_DEVICE;
+  uint8_t* base = (uint8_t*)scratch_of(hip_device);
+  if (!base) return LWATTN_E_DEVICE;
+  FwdGeom g;
+  if (!forward_geometry(c, gap, g_scratch_ncu[hip_device], g, stride, blk)) return LWATTN_E_INVALID;
+
+  // layout: the words that must start at zero (ready [B], fault, status [B],
+  // gcnt [B], merge counters [B H nqt]), then the flags, the global index and
+  // the global rows' partials, each 256-byte aligned
+  const size_t B = (size_t)c.B, n = (size_t)c.n;
+  const size_t ntile = B * c.H * (size_t)(g.nqt > 0 ? g.nqt : 1);
+  const size_t nzero = 3 * B + 1 + ntile;
+  const size_t nparts = fwd_parts(c, g);
+  const size_t off_flags = align256(nzero * 4);
+  const size_t off_gidx = off_flags + align256(B * n);
+  const size_t off_po = off_gidx + align256(B * n * 4);
+  const size_t off_pml = off_po + align256(nparts * lwk::D * 4);
+  const size_t total = off_pml + align256(nparts * 2 * 4);
+  if (total > kScratchBytes || nzero > (size_t)INT32_MAX) return LWATTN_E_SCRATCH;
+
+  FwdWork w;
+  int32_t* ctrl = (int32_t*)base;
+  w.ready = ctrl;
+  w.fault = ctrl + B;
+  w.status = ctrl + B + 1;
+  w.gcnt = ctrl + 2 * B + 1;
+  w.tile_cnt = ctrl + 3 * B + 1;
+  w.flags = base + off_flags;
+  w.gidx = (int32_t*)(base + off_gidx);
+  w.part_o = (float*)(base + off_po);
+  w.part_ml = (float*)(base + off_pml);
+  w.head_stride = nullptr;
+  w.head_blk = nullptr;
+  lwk::Params prm;
+  // the readiness words start at zero on every call, so every call is forward 1
+  forward_params(prm, c, g, w, stride, blk, Q, K, V, Qg, Kg, Vg, lmask, gmask, O, 1);
+  const int zblocks = (int)std::min<size_t>((nzero + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_words_kernel, dim3(zblocks), dim3(256), 0, stream, ctrl, (int)nzero);
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  if (!launch_forward(c, g, prm, stream, nullptr, nullptr)) return LWATTN_E_DEVICE;
+  if (status) {
+    // [0]: the fault word, [1 + b]: batch row b had more than max_global globals
+    if (!hip_ok(hipMemcpyAsync(status, w.fault, (B + 1) * 4, hipMemcpyDeviceToDevice, stream), "hipMemcpyAsync"))
+      return LWATTN_E_DEVICE;
+  }
+  return LWATTN_OK;
+}
 
 }  // extern "C"

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblwattn.so")
 
 LWATTN_F32, LWATTN_BF16 = 0, 1
-OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_DEVICE, E_TOO_MANY_GLOBALS = range(6)
+OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_DEVICE, E_TOO_MANY_GLOBALS, E_SCRATCH = range(7)
 KERNELS = ("attention",)
 # kernel slots of lwattn_timing_read_backward
 BW_KERNELS = ("compact_kernel", "dq_kernel", "global_chunk_kernel", "global_merge_kernel", "dkv_kernel")
@@ -58,6 +58,7 @@ SIGNATURES = [
                                                    ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     ("lwattn_timing_disable", ctypes.c_int, [_c_p]),
     ("lwattn_test_inject_wait_timeout", ctypes.c_int, [_c_p]),
+    ("lwattn_forward_noalloc", ctypes.c_int, [ctypes.POINTER(Config), ctypes.c_int] + [_c_p] * 11),
     ("lwattn_probe_mfma", ctypes.c_int, [_i32, _c_p, _c_p]),
     ("lwattn_probe_read", ctypes.c_int, [_c_p, ctypes.c_int64, _c_p, _c_p]),
     ("lwattn_strerror", ctypes.c_char_p, [ctypes.c_int]),
@@ -381,6 +382,41 @@ class Plan:
 
     def timing_disable(self):
         self.lib.lwattn_timing_disable(self.handle)
+
+
+def forward_noalloc(q, k, v, qg, kg, vg, lmask, gmask, out, window: int,
+                    dilation: Optional[Sequence[int]] = None, max_global: int = 64,
+                    scale: Optional[float] = None, status=None, stream=None, device: Optional[int] = None):
+    """lwattn_forward_noalloc: the forward without a plan or any allocation
+    (the library's static per-GPU workspace).  All tensors are caller-owned
+    device tensors of the plan-based forward's shapes; `status`, if given, is a
+    device int32 tensor [B + 1] (fault word, then the per-row too-many-globals
+    flags).  Returns `out`."""
+    import torch
+    B, H, n, d = tuple(q.shape)
+    tdt = q.dtype
+    dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(tdt)
+    if dtype is None:
+        raise TypeError(f"unsupported dtype {tdt}")
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (qg, "qg"), (kg, "kg"), (vg, "vg"), (out, "out")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != tdt or not t.is_contiguous() \
+                or tuple(t.shape) != (B, H, n, d):
+            raise ValueError(f"{name} must be a contiguous device tensor [B,H,n,d] of {tdt}")
+    for t, name in ((lmask, "local_attn_mask"), (gmask, "global_attn_mask")):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (B, n):
+            raise ValueError(f"{name} must be a contiguous float32 device tensor [B,n]")
+    if status is not None and (status.dtype != torch.int32 or not status.is_cuda or status.numel() < B + 1):
+        raise ValueError("status must be an int32 device tensor of B + 1 entries")
+    cfg, keep = make_config(B, H, n, d, window, dilation, max_global, scale, dtype)
+    dev = q.device.index if device is None else device
+    st = load_library().lwattn_forward_noalloc(
+        ctypes.byref(cfg), int(dev if dev is not None else 0), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        qg.data_ptr(), kg.data_ptr(), vg.data_ptr(), lmask.data_ptr(), gmask.data_ptr(), out.data_ptr(),
+        status.data_ptr() if status is not None else None, _stream_handle(stream))
+    del keep
+    if st != OK:
+        raise LwattnError(st, "lwattn_forward_noalloc")
+    return out
 
 
 LAYER_WEIGHTS = ("w_qkv", "b_qkv", "w_g", "b_g", "w_o", "b_o", "ln1_g", "ln1_b",

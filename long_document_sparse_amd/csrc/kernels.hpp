@@ -83,6 +83,7 @@ struct Params {
   int32_t max_global, nqt, nqg, nsplit, ksplit;
   int32_t n_glob_wg;       // padded to a multiple of 8
   int32_t n_band_wg;
+  int32_t band_pre;        // band workgroups dispatched before the global-row ones (a multiple of 8)
   int32_t blocks_per_b;    // head_blk[H]
   int32_t mask_vec;        // masks 16-byte aligned and n % 4 == 0
   int32_t uni_stride;      // > 0: every head has this stride
@@ -957,6 +958,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// A 16-byte store that writes through to the device-coherent level (cache
+// policy sc1), so that no dirty line is left in L2 for a later release or the
+// kernel's end to write back.  It goes through the compiler's buffer-store
+// builtin, never inline asm: a store of more than 8 bytes reads its data
+// registers after issue, and only a store the compiler can see gets the wait
+// states that keep the next instruction from overwriting them.
+constexpr int CPOL_SC1 = 16;
+typedef unsigned u32x4s __attribute__((__vector_size__(16)));
+template <typename V16>
+__device__ __forceinline__ void store_wt(__amdgpu_buffer_rsrc_t r, int off, V16 v) {
+  static_assert(sizeof(V16) == 16, "16-byte store");
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, v), r, off, 0, CPOL_SC1);
+}
 
 // Per-lane LDS byte offsets used by the compute of every tile.
 struct FLane {
@@ -1677,8 +1691,6 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   }
   // the output row, kept in registers: reloading the pointer at the end
   // would be a scalar load that misses by then
-  uint64_t orow_bits = (uint64_t)(uintptr_t)(p.O + (head + my_pos) * RB);
-  asm volatile("" : "+v"(orow_bits));
   const int sc_lo = kb0 > 0 ? kb0 : 0;
   const int sc_hi = kb + 64 * T < nr ? kb + 64 * T : nr;
   int first, ninv;
@@ -1965,16 +1977,13 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
       *reinterpret_cast<bf16x4*>(stg + qi * 128 + chunk * 16 + h32 * 8) = t;
     }
   }
-  const uint32_t or_lo = (uint32_t)orow_bits, or_hi = (uint32_t)(orow_bits >> 32);
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.O + head * RB, n * RB);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 8 * i + (lane >> 3), c = lane & 7;
     const i32x4 v = *reinterpret_cast<const i32x4*>(stg + row * 128 + ((c ^ (row & 7)) * 16));
-    const uint64_t rt = ((uint64_t)(uint32_t)__shfl((int)or_hi, row) << 32) | (uint32_t)__shfl((int)or_lo, row);
-    if (__shfl(keep ? 1 : 0, row)) {
-      uint8_t* dst = reinterpret_cast<uint8_t*>((uintptr_t)rt) + c * 16;
-      asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(v) : "memory");
-    }
+    const int off = __shfl(my_pos, row) * RB + c * 16;
+    if (__shfl(keep ? 1 : 0, row)) store_wt(rout, off, v);
   }
   return true;
 }
@@ -2103,8 +2112,15 @@ __device__ __forceinline__ int xcd_remap(int pid, int count) {
 
 // Dispatch order: the compaction workgroups (one per batch row, padded to a
 // multiple of 8 so that the band workgroups behind them keep their XCD
-// placement), then the band workgroups (the long ones), then the global-row
-// workgroups that fill the gaps behind them.
+// placement), then the first band_pre band workgroups, then the global-row
+// workgroups, then the rest of the band workgroups.  When the grid fits one
+// round of workgroup slots, band_pre is every band workgroup and the
+// global-row ones fill the gaps behind them.  On longer grids they follow the
+// first round: they start as slots free up (the compaction is done by then)
+// and finish under the later rounds, where at the end of the grid they would
+// run on as a tail (each takes several band workgroups' time).  band_pre and
+// the global-row count are multiples of 8, so every band workgroup keeps the
+// XCD its band index names.
 template <bool BF>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -2114,8 +2130,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     return;
   }
   bid -= p.n_comp_wg;
-  if (bid >= p.n_band_wg) {
-    const int lg = bid - p.n_band_wg;
+  if (bid >= p.band_pre && bid < p.band_pre + p.n_glob_wg) {
+    const int lg = bid - p.band_pre;
     if (lg >= p.B * p.H * p.nqg * p.nsplit) return;
     const int sp = lg % p.nsplit;
     int t = lg / p.nsplit;
@@ -2129,6 +2145,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     if (!wait_ready(p, b, true)) return;
     global_wg<BF>(p, b, h, qg, sp, smem);
   } else {
+    if (bid >= p.band_pre) bid -= p.n_glob_wg;
     const int lb = xcd_remap(bid, p.n_band_wg);
     const int b = lb / p.blocks_per_b;
     const int rem = lb - b * p.blocks_per_b;

@@ -571,7 +571,11 @@ def run_layer(args, spec, x, lm, gm, plan):
     elapsed = time.perf_counter() - t0
     t_call = e0.elapsed_time(e1) * 1e-3 / args.steps
     M = spec.B * spec.n
-    gemm = 2 * M * hid * (3 * hid) * 2 + 2 * M * hid * hid + 2 * 2 * M * hid * inter
+    # Q, K, V and Kg, Vg for every row, Qg for the global tokens' rows only
+    # (the layer projects no other row of it), output projection, FFN
+    n_glob = int(((x.lmask != 0) & (x.gmask != 0)).sum())
+    gemm = (2 * M * hid * (3 * hid) + 2 * M * hid * (2 * hid) + 2 * n_glob * hid * hid
+            + 2 * M * hid * hid + 2 * 2 * M * hid * inter)
     attn = fl.flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
     flop = gemm + attn
     achieved = flop / t_call / 1e12

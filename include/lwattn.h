@@ -180,7 +180,10 @@ lwattn_status lwattn_forward_blocksparse(lwattn_plan_t plan, const void* Q, cons
  * of hid = H*64 columns, X [M][hid] the layer input:
  *   [Q | K | V]    = X w_qkv + b_qkv      (w_qkv [hid][3 hid], b_qkv [3 hid])
  *   [Qg | Kg | Vg] = X w_g + b_g          (same shapes), each split into heads
- *                    [B][H][n][64] (column h*64 + j of a part: head h, element j)
+ *                    [B][H][n][64] (column h*64 + j of a part: head h, element j);
+ *                    Qg is formed for the global tokens' rows only (gathered,
+ *                    projected, scattered back), the only rows the attention
+ *                    reads of it
  *   A  = the attention of the plan (lwattn_forward) on those six tensors and
  *        the masks, heads merged back to [M][hid]
  *   H1 = LayerNorm(A w_o + b_o + X) * ln1_g + ln1_b
@@ -191,7 +194,7 @@ lwattn_status lwattn_forward_blocksparse(lwattn_plan_t plan, const void* Q, cons
  * [M][hid] bf16.  The GEMMs run in rocBLAS (fp32 results), the bias, split,
  * merge, LayerNorm and GELU steps in the library's kernels; each intermediate
  * is rounded to bf16 once.  lwattn_layer_create(plan, inter, eps, &layer):
- * plan with bf16 storage and H in {8, 16, 24, 32, 48, 64}, inter a positive
+ * plan with bf16 storage and H a multiple of 4 up to 64, inter a positive
  * multiple of 8, eps > 0; the layer keeps the plan (which must outlive it) and
  * allocates its intermediates and a rocBLAS handle.  lwattn_layer_forward
  * enqueues the layer on `stream` (no allocation, no host sync; it uses the

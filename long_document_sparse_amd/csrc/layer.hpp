@@ -1,11 +1,13 @@
 // The rest of a Longformer encoder layer around the attention, after the
-// FasterTransformer Longformer encoder guide (hnwysp.cn), compute flow: five
-// projection GEMMs (Q, K, V and the global path's Qg, Kg, Vg), bias add and
-// transpose to [B, H, n, d], the attention, the output projection,
+// FasterTransformer Longformer encoder guide (hnwysp.cn), compute flow: the
+// projection GEMMs (Q, K, V for every token; the global path's Kg, Vg for every
+// token and Qg for the global tokens only), bias add and transpose to
+// [B, H, n, d], the attention, the output projection,
 // AddBiasResidualLayerNorm, the FFN (intermediate GEMM, bias, GELU, output
 // GEMM) and AddBiasResidualLayerNorm again.  The GEMMs are plain library
-// GEMMs (rocBLAS, bf16 inputs, fp32 results); the element-wise and row
-// reductions here each read the fp32 GEMM result once and write bf16 once.
+// GEMMs (16-bit inputs, fp32 results); the element-wise and row reductions
+// here each read the fp32 GEMM result once and write the 16-bit storage type
+// (bf16 or fp16, the template argument T) once.
 #pragma once
 
 namespace lwk {
@@ -13,31 +15,39 @@ namespace layer {
 
 constexpr int LNT = 256;   // threads per block of the element-wise kernels
 
-__device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-__device__ __forceinline__ void load8b(const __bf16* p, float (&v)[8]) {
-  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+template <typename T, int N>
+using vec_t = T __attribute__((ext_vector_type(N)));
+
+template <int N>
+__device__ __forceinline__ void loadf(const float* p, float (&v)[N]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
+  for (int q = 0; q < N / 4; ++q) {
+    const float4 a = *reinterpret_cast<const float4*>(p + 4 * q);
+    v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
+  }
 }
-__device__ __forceinline__ void store8b(__bf16* p, const float (&v)[8]) {
-  bf16x8 a;
+template <int N, typename T>
+__device__ __forceinline__ void loadh(const T* p, float (&v)[N]) {
+  const vec_t<T, N> a = *reinterpret_cast<const vec_t<T, N>*>(p);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) a[e] = (__bf16)v[e];
-  *reinterpret_cast<bf16x8*>(p) = a;
+  for (int e = 0; e < N; ++e) v[e] = (float)a[e];
+}
+template <int N, typename T>
+__device__ __forceinline__ void storeh(T* p, const float (&v)[N]) {
+  vec_t<T, N> a;
+#pragma unroll
+  for (int e = 0; e < N; ++e) a[e] = (T)v[e];
+  *reinterpret_cast<vec_t<T, N>*>(p) = a;
 }
 
-// P [M, 3 hid] (fp32, M = B n) + bias [3 hid] -> three [B, H, n, 64] bf16
-// tensors (columns 0 .. hid: the first, hid .. 2 hid: the second, 2 hid ..:
-// the third; column h 64 + j of a third is head h, element j).  One thread per
-// 8 consecutive columns of a row.
-__global__ __launch_bounds__(LNT) void split_heads(const float* P, const __bf16* bias, __bf16* o0, __bf16* o1,
-                                                   __bf16* o2, int B, int n, int H) {
-  const int hid = H * 64, per_row = 3 * hid / 8;
+// P [M, parts hid] (fp32, M = B n) + bias [parts hid] -> `parts` tensors
+// [B, H, n, 64] (columns 0 .. hid: the first, hid .. 2 hid: the second, ...;
+// column h 64 + j of a part is head h, element j).  One thread per 8
+// consecutive columns of a row.
+template <typename T>
+__global__ __launch_bounds__(LNT) void split_heads(const float* P, const T* bias, T* o0, T* o1, T* o2, int parts,
+                                                   int B, int n, int H) {
+  const int hid = H * 64, per_row = parts * hid / 8;
   const int64_t g = (int64_t)blockIdx.x * LNT + threadIdx.x;
   if (g >= (int64_t)B * n * per_row) return;
   const int64_t m = g / per_row;
@@ -45,16 +55,84 @@ __global__ __launch_bounds__(LNT) void split_heads(const float* P, const __bf16*
   const int which = c / hid, ch = c % hid, h = ch / 64, j = ch % 64;
   const int b = (int)(m / n), i = (int)(m % n);
   float v[8], bb[8];
-  load8f(P + m * 3 * hid + c, v);
-  load8b(bias + c, bb);
+  loadf<8>(P + m * parts * hid + c, v);
+  loadh<8>(bias + c, bb);
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] += bb[e];
-  __bf16* o = which == 0 ? o0 : (which == 1 ? o1 : o2);
-  store8b(o + (((int64_t)b * H + h) * n + i) * 64 + j, v);
+  T* o = which == 0 ? o0 : (which == 1 ? o1 : o2);
+  storeh<8>(o + (((int64_t)b * H + h) * n + i) * 64 + j, v);
 }
 
-// [B, H, n, 64] -> [M, hid] (bf16 both), 8 elements a thread.
-__global__ __launch_bounds__(LNT) void merge_heads(const __bf16* A, __bf16* out, int B, int n, int H) {
+// The global tokens of each batch row (valid and global in the masks, in
+// position order), at most mg of them: gpos [B][mg] receives their positions
+// (-1 past the row's count) and Xg [B mg, hid] their rows of X (zero past the
+// count).  One workgroup per batch row.
+template <typename T>
+__global__ __launch_bounds__(LNT) void gather_global_rows(const T* X, const float* lmask, const float* gmask, int n,
+                                                          int hid, int mg, T* Xg, int32_t* gpos) {
+  __shared__ int wsum[LNT / 64];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* lm = lmask + (int64_t)b * n;
+  const float* gm = gmask + (int64_t)b * n;
+  int32_t* gp = gpos + (int64_t)b * mg;
+  int carry = 0;
+  for (int base = 0; base < n && carry < mg; base += LNT) {
+    const int j = base + tid;
+    const bool is_g = j < n && lm[j] != 0.0f && gm[j] != 0.0f;
+    const uint64_t bal = __ballot(is_g);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < LNT / 64; ++w) {
+      pre += w < wave ? wsum[w] : 0;
+      tot += wsum[w];
+    }
+    const int k = carry + pre + before;
+    if (is_g && k < mg) gp[k] = j;
+    carry += tot;
+    __syncthreads();
+  }
+  const int cnt = carry < mg ? carry : mg;
+  for (int k = cnt + tid; k < mg; k += LNT) gp[k] = -1;
+  __syncthreads();
+  // rows of X, 8 elements a thread
+  const int per_row = hid / 8;
+  for (int q = tid; q < mg * per_row; q += LNT) {
+    const int k = q / per_row, c = (q % per_row) * 8;
+    vec_t<T, 8> v = {};
+    if (k < cnt) v = *reinterpret_cast<const vec_t<T, 8>*>(X + ((int64_t)b * n + gp[k]) * hid + c);
+    *reinterpret_cast<vec_t<T, 8>*>(Xg + ((int64_t)b * mg + k) * hid + c) = v;
+  }
+}
+
+// Qg at the global tokens: Pg [B mg, hid] (fp32, the projection of the
+// gathered rows) + bias [hid] -> Qg [B, H, n, 64] at row gpos[b][k]; rows of
+// Qg at other positions are not written (the attention reads Qg at the global
+// tokens only).  One thread per 8 columns of a gathered row.
+template <typename T>
+__global__ __launch_bounds__(LNT) void scatter_global_rows(const float* Pg, const T* bias, const int32_t* gpos, T* Qg,
+                                                           int B, int n, int H, int mg) {
+  const int hid = H * 64, per_row = hid / 8;
+  const int64_t g = (int64_t)blockIdx.x * LNT + threadIdx.x;
+  if (g >= (int64_t)B * mg * per_row) return;
+  const int64_t r = g / per_row;
+  const int pos = gpos[r];
+  if (pos < 0) return;
+  const int c = (int)(g % per_row) * 8, h = c / 64, j = c % 64;
+  const int b = (int)(r / mg);
+  float v[8], bb[8];
+  loadf<8>(Pg + r * hid + c, v);
+  loadh<8>(bias + c, bb);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] += bb[e];
+  storeh<8>(Qg + (((int64_t)b * H + h) * n + pos) * 64 + j, v);
+}
+
+// [B, H, n, 64] -> [M, hid], 8 elements a thread.
+template <typename T>
+__global__ __launch_bounds__(LNT) void merge_heads(const T* A, T* out, int B, int n, int H) {
   const int hid = H * 64, per_row = hid / 8;
   const int64_t g = (int64_t)blockIdx.x * LNT + threadIdx.x;
   if (g >= (int64_t)B * n * per_row) return;
@@ -62,34 +140,35 @@ __global__ __launch_bounds__(LNT) void merge_heads(const __bf16* A, __bf16* out,
   const int c = (int)(g % per_row) * 8;
   const int h = c / 64, j = c % 64;
   const int b = (int)(m / n), i = (int)(m % n);
-  *reinterpret_cast<bf16x8*>(out + m * hid + c) =
-      *reinterpret_cast<const bf16x8*>(A + (((int64_t)b * H + h) * n + i) * 64 + j);
+  *reinterpret_cast<vec_t<T, 8>*>(out + m * hid + c) =
+      *reinterpret_cast<const vec_t<T, 8>*>(A + (((int64_t)b * H + h) * n + i) * 64 + j);
 }
 
-// Y = LayerNorm(G + bias + R) * gamma + beta over each row of hid columns
-// (G fp32 from the GEMM, the rest bf16); mean and variance in fp32 (two
-// passes over the row held in registers), biased variance, eps inside the
-// square root.  One wave per row, hid / 64 columns a lane (hid a multiple of
-// 512, at most 4096).
-template <int PER>
-__global__ __launch_bounds__(LNT) void bias_residual_layernorm(const float* G, const __bf16* bias,
-                                                               const __bf16* R, const __bf16* gamma,
-                                                               const __bf16* beta, float eps, __bf16* Y,
+// Y = LayerNorm(G + bias + R) * gamma + beta over each row of hid = 64 PER
+// columns (G fp32 from the GEMM, the rest 16-bit); mean and variance in fp32
+// (two passes over the row held in registers), biased variance, eps inside the
+// square root.  One wave per row: PER columns a lane, as PER / VW groups of VW
+// consecutive columns (VW = 8, or 4 when PER is not a multiple of 8).
+template <typename T, int PER>
+__global__ __launch_bounds__(LNT) void bias_residual_layernorm(const float* G, const T* bias, const T* R,
+                                                               const T* gamma, const T* beta, float eps, T* Y,
                                                                int64_t M) {
   constexpr int hid = PER * 64;
+  constexpr int VW = PER % 8 == 0 ? 8 : 4;
+  static_assert(PER % VW == 0, "columns per lane");
   const int lane = threadIdx.x & 63;
   const int64_t m = (int64_t)blockIdx.x * (LNT / 64) + (threadIdx.x >> 6);
   if (m >= M) return;
   float x[PER];
 #pragma unroll
-  for (int q = 0; q < PER / 8; ++q) {
-    const int c = (q * 64 + lane) * 8;
-    float g[8], b[8], r[8];
-    load8f(G + m * hid + c, g);
-    load8b(bias + c, b);
-    load8b(R + m * hid + c, r);
+  for (int q = 0; q < PER / VW; ++q) {
+    const int c = (q * 64 + lane) * VW;
+    float g[VW], b[VW], r[VW];
+    loadf<VW>(G + m * hid + c, g);
+    loadh<VW>(bias + c, b);
+    loadh<VW>(R + m * hid + c, r);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[q * 8 + e] = g[e] + b[e] + r[e];
+    for (int e = 0; e < VW; ++e) x[q * VW + e] = g[e] + b[e] + r[e];
   }
   float s = 0.0f;
 #pragma unroll
@@ -104,35 +183,35 @@ __global__ __launch_bounds__(LNT) void bias_residual_layernorm(const float* G, c
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   const float rstd = 1.0f / sqrtf(v / hid + eps);
 #pragma unroll
-  for (int q = 0; q < PER / 8; ++q) {
-    const int c = (q * 64 + lane) * 8;
-    float ga[8], be[8], y[8];
-    load8b(gamma + c, ga);
-    load8b(beta + c, be);
+  for (int q = 0; q < PER / VW; ++q) {
+    const int c = (q * 64 + lane) * VW;
+    float ga[VW], be[VW], y[VW];
+    loadh<VW>(gamma + c, ga);
+    loadh<VW>(beta + c, be);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (x[q * 8 + e] - mean) * rstd * ga[e] + be[e];
-    store8b(Y + m * hid + c, y);
+    for (int e = 0; e < VW; ++e) y[e] = (x[q * VW + e] - mean) * rstd * ga[e] + be[e];
+    storeh<VW>(Y + m * hid + c, y);
   }
 }
 
 // Y = gelu(G + bias), gelu(x) = x Phi(x) = x (1 + erf(x / sqrt 2)) / 2, G fp32
-// [M, cols], Y bf16; 8 columns a thread.
-__global__ __launch_bounds__(LNT) void bias_gelu(const float* G, const __bf16* bias, __bf16* Y, int64_t M,
-                                                 int cols) {
+// [M, cols], Y 16-bit; 8 columns a thread.
+template <typename T>
+__global__ __launch_bounds__(LNT) void bias_gelu(const float* G, const T* bias, T* Y, int64_t M, int cols) {
   const int per_row = cols / 8;
   const int64_t g = (int64_t)blockIdx.x * LNT + threadIdx.x;
   if (g >= M * per_row) return;
   const int64_t m = g / per_row;
   const int c = (int)(g % per_row) * 8;
   float v[8], b[8];
-  load8f(G + m * cols + c, v);
-  load8b(bias + c, b);
+  loadf<8>(G + m * cols + c, v);
+  loadh<8>(bias + c, b);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = v[e] + b[e];
     v[e] = 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
   }
-  store8b(Y + m * cols + c, v);
+  storeh<8>(Y + m * cols + c, v);
 }
 
 }  // namespace layer

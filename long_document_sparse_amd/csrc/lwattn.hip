@@ -128,44 +128,53 @@ static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 
 // ---------------------------------------------------------------------------
-// Encoder layer around the attention (bf16 storage): the plan gives B, H, n,
-// the window, dilation and globals; the layer object owns the intermediate
-// buffers and a rocBLAS handle.
+// Encoder layer around the attention (16-bit storage, the plan's): the plan
+// gives B, H, n, the window, dilation and globals; the layer object owns the
+// intermediate buffers and a rocBLAS handle.
 struct lwattn_layer_s {
   lwattn_plan_t attn = nullptr;   // not owned
   int32_t inter = 0;
   float eps = 0.f;
+  int mg = 0;                          // gathered global rows per batch row: min(max_global, n)
   rocblas_handle blas = nullptr;
   float* P = nullptr;                  // [M, max(3 hid, inter)] fp32 GEMM results
-  __bf16* qkv[6] = {};                 // Q, K, V, Qg, Kg, Vg [B, H, n, 64]
-  __bf16* A = nullptr;                 // attention output [B, H, n, 64]
-  __bf16* Am = nullptr;                // [M, hid]
-  __bf16* H1 = nullptr;                // [M, hid]
-  __bf16* F = nullptr;                 // [M, inter]
+  float* Pg = nullptr;                 // [B mg, hid] fp32: Qg of the gathered rows
+  void* qkv[6] = {};                   // Q, K, V, Qg, Kg, Vg [B, H, n, 64]
+  void* A = nullptr;                   // attention output [B, H, n, 64]
+  void* Am = nullptr;                  // [M, hid]
+  void* H1 = nullptr;                  // [M, hid]
+  void* F = nullptr;                   // [M, inter]
+  void* Xg = nullptr;                  // [B mg, hid] rows of X at the global tokens
+  int32_t* gpos = nullptr;             // [B, mg] their positions (-1 past the count)
 };
 
 static void free_layer(lwattn_layer_t L) {
   if (!L) return;
   if (L->attn) (void)hipSetDevice(L->attn->device);
   (void)hipFree(L->P);
+  (void)hipFree(L->Pg);
   for (auto* q : L->qkv) (void)hipFree(q);
   (void)hipFree(L->A);
   (void)hipFree(L->Am);
   (void)hipFree(L->H1);
   (void)hipFree(L->F);
+  (void)hipFree(L->Xg);
+  (void)hipFree(L->gpos);
   if (L->blas) (void)rocblas_destroy_handle(L->blas);
   delete L;
 }
 
-// Row-major Y[M, N] (fp32) = X[M, K] W[K, N] (bf16), as the column-major
+// Row-major Y[M, N] (fp32, row stride N) = X[M, K] W[K, N] (16-bit of type
+// dt, X rows of stride K, W rows of stride ldw >= N), as the column-major
 // product Y^T = W^T X^T.
-static bool gemm_rm(rocblas_handle h, int64_t M, int64_t N, int64_t K, const void* X, const void* W, float* Y) {
+static bool gemm_rm(rocblas_handle h, rocblas_datatype dt, int64_t M, int64_t N, int64_t K, const void* X,
+                    const void* W, int64_t ldw, float* Y) {
   const float one = 1.0f, zero = 0.0f;
   const rocblas_status st = rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, (rocblas_int)N,
-                                            (rocblas_int)M, (rocblas_int)K, &one, W, rocblas_datatype_bf16_r,
-                                            (rocblas_int)N, X, rocblas_datatype_bf16_r, (rocblas_int)K, &zero, Y,
-                                            rocblas_datatype_f32_r, (rocblas_int)N, Y, rocblas_datatype_f32_r,
-                                            (rocblas_int)N, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+                                            (rocblas_int)M, (rocblas_int)K, &one, W, dt, (rocblas_int)ldw, X, dt,
+                                            (rocblas_int)K, &zero, Y, rocblas_datatype_f32_r, (rocblas_int)N, Y,
+                                            rocblas_datatype_f32_r, (rocblas_int)N, rocblas_datatype_f32_r,
+                                            rocblas_gemm_algo_standard, 0, 0);
   if (st != rocblas_status_success) {
     std::fprintf(stderr, "lwattn: rocblas_gemm_ex failed (%d)\n", (int)st);
     return false;
@@ -173,23 +182,29 @@ static bool gemm_rm(rocblas_handle h, int64_t M, int64_t N, int64_t K, const voi
   return true;
 }
 
-template <int PER>
-static void launch_ln(const float* G, const void* b, const __bf16* R, const void* g, const void* be, float eps,
-                      __bf16* Y, int64_t M, hipStream_t stream) {
-  hipLaunchKernelGGL(lwk::layer::bias_residual_layernorm<PER>, dim3((uint32_t)((M + 3) / 4)),
-                     dim3(lwk::layer::LNT), 0, stream, G, (const __bf16*)b, R, (const __bf16*)g,
-                     (const __bf16*)be, eps, Y, M);
+template <typename T, int PER>
+static void launch_ln(const float* G, const void* b, const void* R, const void* g, const void* be, float eps,
+                      void* Y, int64_t M, hipStream_t stream) {
+  hipLaunchKernelGGL((lwk::layer::bias_residual_layernorm<T, PER>), dim3((uint32_t)((M + 3) / 4)),
+                     dim3(lwk::layer::LNT), 0, stream, G, (const T*)b, (const T*)R, (const T*)g, (const T*)be, eps,
+                     (T*)Y, M);
 }
 
-static bool layernorm(int H, const float* G, const void* b, const __bf16* R, const void* g, const void* be,
-                      float eps, __bf16* Y, int64_t M, hipStream_t stream) {
+// Heads the layer takes: H a multiple of 4 up to 64 (hid = 64 H columns, held
+// H to a lane by the LayerNorm).
+static bool layer_heads_ok(int H) { return H >= 4 && H <= 64 && H % 4 == 0; }
+
+template <typename T>
+static bool layernorm(int H, const float* G, const void* b, const void* R, const void* g, const void* be, float eps,
+                      void* Y, int64_t M, hipStream_t stream) {
   switch (H) {
-    case 8: launch_ln<8>(G, b, R, g, be, eps, Y, M, stream); return true;
-    case 16: launch_ln<16>(G, b, R, g, be, eps, Y, M, stream); return true;
-    case 24: launch_ln<24>(G, b, R, g, be, eps, Y, M, stream); return true;
-    case 32: launch_ln<32>(G, b, R, g, be, eps, Y, M, stream); return true;
-    case 48: launch_ln<48>(G, b, R, g, be, eps, Y, M, stream); return true;
-    case 64: launch_ln<64>(G, b, R, g, be, eps, Y, M, stream); return true;
+#define LWATTN_LN_CASE(h) \
+  case h: launch_ln<T, h>(G, b, R, g, be, eps, Y, M, stream); return true;
+    LWATTN_LN_CASE(4) LWATTN_LN_CASE(8) LWATTN_LN_CASE(12) LWATTN_LN_CASE(16)
+    LWATTN_LN_CASE(20) LWATTN_LN_CASE(24) LWATTN_LN_CASE(28) LWATTN_LN_CASE(32)
+    LWATTN_LN_CASE(36) LWATTN_LN_CASE(40) LWATTN_LN_CASE(44) LWATTN_LN_CASE(48)
+    LWATTN_LN_CASE(52) LWATTN_LN_CASE(56) LWATTN_LN_CASE(60) LWATTN_LN_CASE(64)
+#undef LWATTN_LN_CASE
     default: return false;
   }
 }
@@ -981,16 +996,18 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
   if (!p || inter <= 0 || (inter % 8) != 0 || !(eps > 0.0f)) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   const int H = c.H;
-  if (c.dtype != LWATTN_BF16 || !(H == 8 || H == 16 || H == 24 || H == 32 || H == 48 || H == 64))
-    return LWATTN_E_UNSUPPORTED;
+  if (c.dtype != LWATTN_BF16 || !layer_heads_ok(H)) return LWATTN_E_UNSUPPORTED;
   const int64_t M = (int64_t)c.B * c.n, hid = (int64_t)H * 64;
-  if (M * std::max<int64_t>(3 * hid, inter) >= ((int64_t)1 << 31)) return LWATTN_E_UNSUPPORTED;
+  const int mg = std::min(c.max_global, c.n);
+  if (M * std::max<int64_t>(3 * hid, inter) >= ((int64_t)1 << 31) || (int64_t)c.B * mg * hid >= ((int64_t)1 << 31))
+    return LWATTN_E_UNSUPPORTED;
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
   lwattn_layer_t L = new (std::nothrow) lwattn_layer_s;
   if (!L) return LWATTN_E_NOMEM;
   L->attn = p;
   L->inter = inter;
   L->eps = eps;
+  L->mg = mg;
   bool ok = true;
   auto alloc = [&](void** ptr, size_t bytes) {
     if (!ok) return;
@@ -998,11 +1015,14 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
     if (!hip_ok(hipMalloc(ptr, bytes), "hipMalloc")) { ok = false; *ptr = nullptr; }
   };
   alloc((void**)&L->P, (size_t)M * std::max<int64_t>(3 * hid, inter) * 4);
-  for (auto*& q : L->qkv) alloc((void**)&q, (size_t)M * hid * 2);
-  alloc((void**)&L->A, (size_t)M * hid * 2);
-  alloc((void**)&L->Am, (size_t)M * hid * 2);
-  alloc((void**)&L->H1, (size_t)M * hid * 2);
-  alloc((void**)&L->F, (size_t)M * inter * 2);
+  alloc((void**)&L->Pg, (size_t)c.B * mg * hid * 4);
+  for (auto*& q : L->qkv) alloc(&q, (size_t)M * hid * 2);
+  alloc(&L->A, (size_t)M * hid * 2);
+  alloc(&L->Am, (size_t)M * hid * 2);
+  alloc(&L->H1, (size_t)M * hid * 2);
+  alloc(&L->F, (size_t)M * inter * 2);
+  alloc(&L->Xg, (size_t)c.B * mg * hid * 2);
+  alloc((void**)&L->gpos, (size_t)c.B * mg * 4);
   if (ok && rocblas_create_handle(&L->blas) != rocblas_status_success) ok = false;
   if (!ok) {
     free_layer(L);
@@ -1012,14 +1032,64 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
   return LWATTN_OK;
 }
 
+// (a template inside the extern "C" block: C++ linkage of its own)
+extern "C++" {
+template <typename T>
+static lwattn_status layer_forward(lwattn_layer_t L, rocblas_datatype dt, const void* X, const lwattn_layer_weights* w,
+                                   const float* lmask, const float* gmask, void* Y, hipStream_t stream) {
+  lwattn_plan_t p = L->attn;
+  const lwattn_config& c = p->cfg;
+  const int H = c.H, mg = L->mg;
+  const int64_t M = (int64_t)c.B * c.n, hid = (int64_t)H * 64, inter = L->inter;
+  namespace ly = lwk::layer;
+  auto blocks = [](int64_t threads) { return dim3((uint32_t)((threads + ly::LNT - 1) / ly::LNT)); };
+  T* const* t = reinterpret_cast<T* const*>(L->qkv);
+  // 1. projections.  Q, K, V: every row, bias added while splitting heads.
+  if (!gemm_rm(L->blas, dt, M, 3 * hid, hid, X, w->w_qkv, 3 * hid, L->P)) return LWATTN_E_DEVICE;
+  hipLaunchKernelGGL(ly::split_heads<T>, blocks(M * 3 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
+                     (const T*)w->b_qkv, t[0], t[1], t[2], 3, c.B, c.n, H);
+  // Kg, Vg: every row (the global rows attend to all keys), from the last two
+  // column blocks of w_g
+  const T* wg = (const T*)w->w_g;
+  if (!gemm_rm(L->blas, dt, M, 2 * hid, hid, X, wg + hid, 3 * hid, L->P)) return LWATTN_E_DEVICE;
+  hipLaunchKernelGGL(ly::split_heads<T>, blocks(M * 2 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
+                     (const T*)w->b_g + hid, t[4], t[5], t[5], 2, c.B, c.n, H);
+  // Qg: only the global tokens' rows (the attention reads Qg nowhere else),
+  // gathered, projected by the first column block of w_g and scattered back
+  if (mg > 0) {
+    hipLaunchKernelGGL(ly::gather_global_rows<T>, dim3((uint32_t)c.B), dim3(ly::LNT), 0, stream, (const T*)X, lmask,
+                       gmask, c.n, (int)hid, mg, (T*)L->Xg, L->gpos);
+    if (!gemm_rm(L->blas, dt, (int64_t)c.B * mg, hid, hid, L->Xg, wg, 3 * hid, L->Pg)) return LWATTN_E_DEVICE;
+    hipLaunchKernelGGL(ly::scatter_global_rows<T>, blocks((int64_t)c.B * mg * hid / 8), dim3(ly::LNT), 0, stream,
+                       L->Pg, (const T*)w->b_g, L->gpos, t[3], c.B, c.n, H, mg);
+  }
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  // 2. the attention
+  lwattn_status st = lwattn_forward(p, L->qkv[0], L->qkv[1], L->qkv[2], L->qkv[3], L->qkv[4], L->qkv[5], lmask,
+                                    gmask, L->A, stream);
+  if (st != LWATTN_OK) return st;
+  // 3. output projection, bias, residual, LayerNorm
+  hipLaunchKernelGGL(ly::merge_heads<T>, blocks(M * hid / 8), dim3(ly::LNT), 0, stream, (const T*)L->A, (T*)L->Am,
+                     c.B, c.n, H);
+  if (!gemm_rm(L->blas, dt, M, hid, hid, L->Am, w->w_o, hid, L->P)) return LWATTN_E_DEVICE;
+  if (!layernorm<T>(H, L->P, w->b_o, X, w->ln1_g, w->ln1_b, L->eps, L->H1, M, stream)) return LWATTN_E_UNSUPPORTED;
+  // 4. FFN: intermediate GEMM, bias, GELU; output GEMM, bias, residual, LayerNorm
+  if (!gemm_rm(L->blas, dt, M, inter, hid, L->H1, w->w_1, inter, L->P)) return LWATTN_E_DEVICE;
+  hipLaunchKernelGGL(ly::bias_gelu<T>, blocks(M * inter / 8), dim3(ly::LNT), 0, stream, L->P, (const T*)w->b_1,
+                     (T*)L->F, M, (int)inter);
+  if (!gemm_rm(L->blas, dt, M, hid, inter, L->F, w->w_2, hid, L->P)) return LWATTN_E_DEVICE;
+  if (!layernorm<T>(H, L->P, w->b_2, L->H1, w->ln2_g, w->ln2_b, L->eps, Y, M, stream)) return LWATTN_E_UNSUPPORTED;
+  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  return LWATTN_OK;
+}
+}  // extern "C++"
+
 lwattn_status lwattn_layer_forward(lwattn_layer_t L, const void* X, const lwattn_layer_weights* w,
                                    const float* lmask, const float* gmask, void* Y, hipStream_t stream) {
   if (!L || !w) return LWATTN_E_INVALID;
   lwattn_plan_t p = L->attn;
   const lwattn_config& c = p->cfg;
-  const int H = c.H;
-  const int64_t M = (int64_t)c.B * c.n, hid = (int64_t)H * 64, inter = L->inter;
-  if (M == 0) return LWATTN_OK;
+  if ((int64_t)c.B * c.n == 0) return LWATTN_OK;
   const void* ptrs[] = {X, Y, w->w_qkv, w->b_qkv, w->w_g, w->b_g, w->w_o, w->b_o, w->ln1_g, w->ln1_b,
                         w->w_1, w->b_1, w->w_2, w->b_2, w->ln2_g, w->ln2_b};
   for (const void* q : ptrs)
@@ -1027,34 +1097,7 @@ lwattn_status lwattn_layer_forward(lwattn_layer_t L, const void* X, const lwattn
   if (!lmask || !gmask || ((uintptr_t)lmask & 3u) || ((uintptr_t)gmask & 3u)) return LWATTN_E_INVALID;
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
   if (rocblas_set_stream(L->blas, stream) != rocblas_status_success) return LWATTN_E_DEVICE;
-  namespace ly = lwk::layer;
-  auto blocks = [](int64_t threads) { return dim3((uint32_t)((threads + ly::LNT - 1) / ly::LNT)); };
-  // 1. projections: Q, K, V then Qg, Kg, Vg, bias added while splitting heads
-  if (!gemm_rm(L->blas, M, 3 * hid, hid, X, w->w_qkv, L->P)) return LWATTN_E_DEVICE;
-  hipLaunchKernelGGL(ly::split_heads, blocks(M * 3 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
-                     (const __bf16*)w->b_qkv, L->qkv[0], L->qkv[1], L->qkv[2], c.B, c.n, H);
-  if (!gemm_rm(L->blas, M, 3 * hid, hid, X, w->w_g, L->P)) return LWATTN_E_DEVICE;
-  hipLaunchKernelGGL(ly::split_heads, blocks(M * 3 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
-                     (const __bf16*)w->b_g, L->qkv[3], L->qkv[4], L->qkv[5], c.B, c.n, H);
-  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-  // 2. the attention
-  lwattn_status st = lwattn_forward(p, L->qkv[0], L->qkv[1], L->qkv[2], L->qkv[3], L->qkv[4], L->qkv[5],
-                                    lmask, gmask, L->A, stream);
-  if (st != LWATTN_OK) return st;
-  // 3. output projection, bias, residual, LayerNorm
-  hipLaunchKernelGGL(ly::merge_heads, blocks(M * hid / 8), dim3(ly::LNT), 0, stream, L->A, L->Am, c.B, c.n, H);
-  if (!gemm_rm(L->blas, M, hid, hid, L->Am, w->w_o, L->P)) return LWATTN_E_DEVICE;
-  if (!layernorm(H, L->P, w->b_o, (const __bf16*)X, w->ln1_g, w->ln1_b, L->eps, L->H1, M, stream))
-    return LWATTN_E_UNSUPPORTED;
-  // 4. FFN: intermediate GEMM, bias, GELU; output GEMM, bias, residual, LayerNorm
-  if (!gemm_rm(L->blas, M, inter, hid, L->H1, w->w_1, L->P)) return LWATTN_E_DEVICE;
-  hipLaunchKernelGGL(ly::bias_gelu, blocks(M * inter / 8), dim3(ly::LNT), 0, stream, L->P,
-                     (const __bf16*)w->b_1, L->F, M, (int)inter);
-  if (!gemm_rm(L->blas, M, hid, inter, L->F, w->w_2, L->P)) return LWATTN_E_DEVICE;
-  if (!layernorm(H, L->P, w->b_2, L->H1, w->ln2_g, w->ln2_b, L->eps, (__bf16*)Y, M, stream))
-    return LWATTN_E_UNSUPPORTED;
-  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-  return LWATTN_OK;
+  return layer_forward<__bf16>(L, rocblas_datatype_bf16_r, X, w, lmask, gmask, Y, stream);
 }
 
 lwattn_status lwattn_layer_destroy(lwattn_layer_t L) {

@@ -43,6 +43,8 @@ CASES = [
     # (B, H, n, window, dilation, n_global, pad_mode, pad_hi, inter)
     (2, 8, 300, 64, [0] * 6 + [1, 2], 3, "per_batch", 60, 1024),
     (1, 16, 512, 128, [0] * 16, 8, "none", 0, 4096),
+    (1, 12, 1024, 256, [0] * 12, 40, "per_batch", 100, 3072),   # base-model heads (hid 768)
+    (2, 4, 200, 32, [0, 1, 2, 3], 0, "none", 0, 512),           # no global token at all
 ]
 
 
@@ -50,7 +52,7 @@ CASES = [
 def test_layer_matches_oracle(case):
     B, H, n, window, dil, ng, pmode, phi, inter = case
     spec = workloads.custom(B, H, n, 64, window, "bf16", dil, seed=51, n_global=ng,
-                            pad_mode=pmode, pad_hi=phi)
+                            global_mode="random", pad_mode=pmode, pad_hi=phi)
     say(f"layer case {case}")
     x = workloads.generate(spec)
     dev = "cuda:0"
@@ -77,7 +79,7 @@ def test_layer_matches_oracle(case):
 
 
 def test_layer_rejects_unsupported_heads_and_bad_arguments():
-    spec = workloads.custom(1, 12, 128, 64, 32, "bf16", [0] * 12, n_global=1)
+    spec = workloads.custom(1, 6, 128, 64, 32, "bf16", [0] * 6, n_global=1)
     plan = make_plan(spec, max_global=1)
     with pytest.raises(lw.LwattnError):
         lw.Layer(plan, 1024)

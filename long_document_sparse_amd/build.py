@@ -31,7 +31,7 @@ FLAGS = [
 def build(verbose: bool = False, extra=None) -> str:
     tmp = LIB + ".tmp"
     # rocBLAS runs the encoder layer's plain GEMMs
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC, "-lrocblas"]
+    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC, "-lrocblas", "-lhipblaslt"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

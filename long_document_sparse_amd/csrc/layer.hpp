@@ -63,25 +63,37 @@ __global__ __launch_bounds__(LNT) void split_heads(const float* P, const T* bias
   storeh<8>(o + (((int64_t)b * H + h) * n + i) * 64 + j, v);
 }
 
-// The global tokens of each batch row (valid and global in the masks, in
-// position order), at most mg of them: gpos [B][mg] receives their positions
-// (-1 past the row's count) and Xg [B mg, hid] their rows of X (zero past the
-// count).  One workgroup per batch row.
-template <typename T>
-__global__ __launch_bounds__(LNT) void gather_global_rows(const T* X, const float* lmask, const float* gmask, int n,
-                                                          int hid, int mg, T* Xg, int32_t* gpos) {
+// The global tokens of each batch row (valid and global in the masks), in
+// position order, at most mg of them: gpos [B][mg] receives their positions
+// and -1 past the row's count.  One workgroup per batch row, 16 positions a
+// thread per pass (4096 a pass), stopping once mg are found.
+constexpr int GPT = 16;
+__global__ __launch_bounds__(LNT) void find_global_rows(const float* lmask, const float* gmask, int n, int mg,
+                                                        int32_t* gpos) {
   __shared__ int wsum[LNT / 64];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* lm = lmask + (int64_t)b * n;
   const float* gm = gmask + (int64_t)b * n;
   int32_t* gp = gpos + (int64_t)b * mg;
   int carry = 0;
-  for (int base = 0; base < n && carry < mg; base += LNT) {
-    const int j = base + tid;
-    const bool is_g = j < n && lm[j] != 0.0f && gm[j] != 0.0f;
-    const uint64_t bal = __ballot(is_g);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(bal);
+  for (int base = 0; base < n && carry < mg; base += LNT * GPT) {
+    const int j0 = base + tid * GPT;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < GPT; ++e) {
+      const int j = j0 + e;
+      const bool is_g = j < n && lm[j] != 0.0f && gm[j] != 0.0f;
+      bits |= (is_g ? 1u : 0u) << e;
+    }
+    // exclusive prefix of the per-thread counts over the workgroup
+    const int mine = __popc(bits);
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     int pre = 0, tot = 0;
 #pragma unroll
@@ -89,21 +101,35 @@ __global__ __launch_bounds__(LNT) void gather_global_rows(const T* X, const floa
       pre += w < wave ? wsum[w] : 0;
       tot += wsum[w];
     }
-    const int k = carry + pre + before;
-    if (is_g && k < mg) gp[k] = j;
+    int k = carry + pre + incl - mine;
+    while (bits) {
+      const int e = __builtin_ctz(bits);
+      bits &= bits - 1;
+      if (k < mg) gp[k] = j0 + e;
+      ++k;
+    }
     carry += tot;
     __syncthreads();
   }
-  const int cnt = carry < mg ? carry : mg;
-  for (int k = cnt + tid; k < mg; k += LNT) gp[k] = -1;
-  __syncthreads();
-  // rows of X, 8 elements a thread
-  const int per_row = hid / 8;
-  for (int q = tid; q < mg * per_row; q += LNT) {
-    const int k = q / per_row, c = (q % per_row) * 8;
+  for (int k = (carry < mg ? carry : mg) + tid; k < mg; k += LNT) gp[k] = -1;
+}
+
+// Xg [B mg, hid] = the rows of X at gpos (zero rows where gpos is -1): one
+// wave per gathered row, 8 elements a lane at a time.
+template <typename T>
+__global__ __launch_bounds__(LNT) void gather_global_rows(const T* X, const int32_t* gpos, int n, int hid, int mg,
+                                                          int64_t rows, T* Xg) {
+  const int64_t r = (int64_t)blockIdx.x * (LNT / 64) + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int pos = gpos[r];
+  const int64_t b = r / mg;
+  const T* src = X + (b * n + (pos < 0 ? 0 : pos)) * hid;
+  T* dst = Xg + r * hid;
+  for (int c = lane * 8; c < hid; c += 64 * 8) {
     vec_t<T, 8> v = {};
-    if (k < cnt) v = *reinterpret_cast<const vec_t<T, 8>*>(X + ((int64_t)b * n + gp[k]) * hid + c);
-    *reinterpret_cast<vec_t<T, 8>*>(Xg + ((int64_t)b * mg + k) * hid + c) = v;
+    if (pos >= 0) v = *reinterpret_cast<const vec_t<T, 8>*>(src + c);
+    *reinterpret_cast<vec_t<T, 8>*>(dst + c) = v;
   }
 }
 

@@ -6,6 +6,7 @@
 // caller's stream (see kernels.hpp) and never allocates or synchronizes.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
 
 #include <cmath>
 #include <cstdint>
@@ -131,6 +132,92 @@ static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // Encoder layer around the attention (16-bit storage, the plan's): the plan
 // gives B, H, n, the window, dilation and globals; the layer object owns the
 // intermediate buffers and a rocBLAS handle.
+// One GEMM shape of the layer in hipBLASLt: row-major Y[M, N] (fp32) =
+// X[M, K] W[K, N] (16-bit), set up as the column-major product
+// Y^T = W^T X^T.  At set-up the (up to 8) algorithms its heuristic ranks
+// first are timed on scratch operands and the fastest is kept; when hipBLASLt
+// has none for a shape, the layer runs it in rocBLAS.
+struct LtGemm {
+  bool ok = false;
+  int64_t M = 0, N = 0, K = 0, ldw = 0;
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t lw = nullptr, lx = nullptr, ly = nullptr;
+  hipblasLtMatmulAlgo_t algo;
+  size_t ws = 0;
+};
+
+static void lt_free(LtGemm& g) {
+  if (g.desc) (void)hipblasLtMatmulDescDestroy(g.desc);
+  if (g.lw) (void)hipblasLtMatrixLayoutDestroy(g.lw);
+  if (g.lx) (void)hipblasLtMatrixLayoutDestroy(g.lx);
+  if (g.ly) (void)hipblasLtMatrixLayoutDestroy(g.ly);
+  g = LtGemm();
+}
+
+// Scratch operands for timing the candidates: W, X (16-bit), Y (fp32) and
+// the workspace, zero-filled, on a stream of their own.
+struct LtTune {
+  void *w = nullptr, *x = nullptr, *ws = nullptr;
+  float* y = nullptr;
+  size_t ws_cap = 0;
+  hipStream_t stream = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+};
+
+static void lt_setup(hipblasLtHandle_t h, LtGemm& g, hipDataType dt, int64_t M, int64_t N, int64_t K, int64_t ldw,
+                     const LtTune& tu) {
+  g.M = M; g.N = N; g.K = K; g.ldw = ldw;
+  if (!h || !tu.stream || M == 0 || N == 0 || K == 0) return;
+  const hipblasOperation_t op = HIPBLAS_OP_N;
+  bool ok = hipblasLtMatmulDescCreate(&g.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &op, sizeof(op)) ==
+                HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &op, sizeof(op)) ==
+                HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatrixLayoutCreate(&g.lw, dt, (uint64_t)N, (uint64_t)K, ldw) == HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatrixLayoutCreate(&g.lx, dt, (uint64_t)K, (uint64_t)M, K) == HIPBLAS_STATUS_SUCCESS &&
+            hipblasLtMatrixLayoutCreate(&g.ly, HIP_R_32F, (uint64_t)N, (uint64_t)M, N) == HIPBLAS_STATUS_SUCCESS;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
+  const uint64_t cap = tu.ws_cap;
+  ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap,
+                                                   sizeof(cap)) == HIPBLAS_STATUS_SUCCESS;
+  hipblasLtMatmulHeuristicResult_t res[8];
+  int nret = 0;
+  ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, g.desc, g.lw, g.lx, g.ly, g.ly, pref, 8, res, &nret) ==
+                 HIPBLAS_STATUS_SUCCESS;
+  if (pref) (void)hipblasLtMatmulPreferenceDestroy(pref);
+  float best = 0.f;
+  int pick = -1;
+  const float one = 1.0f, zero = 0.0f;
+  for (int a = 0; ok && a < nret; ++a) {
+    if (res[a].state != HIPBLAS_STATUS_SUCCESS || res[a].workspaceSize > tu.ws_cap) continue;
+    auto run = [&]() {
+      return hipblasLtMatmul(h, g.desc, &one, tu.w, g.lw, tu.x, g.lx, &zero, tu.y, g.ly, tu.y, g.ly, &res[a].algo,
+                             tu.ws, res[a].workspaceSize, tu.stream) == HIPBLAS_STATUS_SUCCESS;
+    };
+    if (!run()) continue;   // warm-up (and a check that it runs)
+    bool good = hipEventRecord(tu.e0, tu.stream) == hipSuccess;
+    for (int r = 0; good && r < 3; ++r) good = run();
+    good = good && hipEventRecord(tu.e1, tu.stream) == hipSuccess && hipEventSynchronize(tu.e1) == hipSuccess;
+    float ms = 0.f;
+    if (!good || hipEventElapsedTime(&ms, tu.e0, tu.e1) != hipSuccess) continue;
+    if (pick < 0 || ms < best) {
+      best = ms;
+      pick = a;
+    }
+  }
+  (void)hipGetLastError();
+  if (!ok || pick < 0) {
+    lt_free(g);
+    g.M = M; g.N = N; g.K = K; g.ldw = ldw;
+    return;
+  }
+  g.algo = res[pick].algo;
+  g.ws = res[pick].workspaceSize;
+  g.ok = true;
+}
+
 struct lwattn_layer_s {
   lwattn_plan_t attn = nullptr;   // not owned
   int32_t inter = 0;
@@ -146,6 +233,10 @@ struct lwattn_layer_s {
   void* F = nullptr;                   // [M, inter]
   void* Xg = nullptr;                  // [B mg, hid] rows of X at the global tokens
   int32_t* gpos = nullptr;             // [B, mg] their positions (-1 past the count)
+  hipblasLtHandle_t lt = nullptr;
+  void* lt_ws = nullptr;               // hipBLASLt workspace
+  size_t lt_ws_bytes = 0;
+  LtGemm g_qkv, g_kv, g_qg, g_o, g_f1, g_f2;
 };
 
 static void free_layer(lwattn_layer_t L) {
@@ -160,6 +251,9 @@ static void free_layer(lwattn_layer_t L) {
   (void)hipFree(L->F);
   (void)hipFree(L->Xg);
   (void)hipFree(L->gpos);
+  for (LtGemm* g : {&L->g_qkv, &L->g_kv, &L->g_qg, &L->g_o, &L->g_f1, &L->g_f2}) lt_free(*g);
+  (void)hipFree(L->lt_ws);
+  if (L->lt) (void)hipblasLtDestroy(L->lt);
   if (L->blas) (void)rocblas_destroy_handle(L->blas);
   delete L;
 }
@@ -180,6 +274,23 @@ static bool gemm_rm(rocblas_handle h, rocblas_datatype dt, int64_t M, int64_t N,
     return false;
   }
   return true;
+}
+
+// One of the layer's GEMMs: hipBLASLt with the algorithm chosen at set-up,
+// else rocBLAS.
+static bool layer_gemm(lwattn_layer_t L, const LtGemm& g, rocblas_datatype dt, const void* X, const void* W, float* Y,
+                       hipStream_t stream) {
+  if (g.ok) {
+    const float one = 1.0f, zero = 0.0f;
+    const hipblasStatus_t st = hipblasLtMatmul(L->lt, g.desc, &one, W, g.lw, X, g.lx, &zero, Y, g.ly, Y, g.ly, &g.algo,
+                                               L->lt_ws, g.ws, stream);
+    if (st != HIPBLAS_STATUS_SUCCESS) {
+      std::fprintf(stderr, "lwattn: hipblasLtMatmul failed (%d)\n", (int)st);
+      return false;
+    }
+    return true;
+  }
+  return gemm_rm(L->blas, dt, g.M, g.N, g.K, X, W, g.ldw, Y);
 }
 
 template <typename T, int PER>
@@ -1024,6 +1135,40 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
   alloc(&L->Xg, (size_t)c.B * mg * hid * 2);
   alloc((void**)&L->gpos, (size_t)c.B * mg * 4);
   if (ok && rocblas_create_handle(&L->blas) != rocblas_status_success) ok = false;
+  // hipBLASLt for the GEMMs (rocBLAS takes a shape it has no algorithm for),
+  // each shape's algorithm timed here on scratch operands
+  if (ok && hipblasLtCreate(&L->lt) != HIPBLAS_STATUS_SUCCESS) L->lt = nullptr;
+  if (ok && L->lt) {
+    const hipDataType dt = HIP_R_16BF;
+    const int64_t Mg = (int64_t)c.B * mg, big = std::max<int64_t>(3 * hid, inter);
+    LtTune tu;
+    tu.ws_cap = (size_t)32 << 20;
+    const size_t wb = (size_t)std::max(hid, (int64_t)inter) * big * 2, xb = (size_t)M * big * 2,
+                 yb = (size_t)M * big * 4;
+    bool tok = hipMalloc(&tu.w, wb) == hipSuccess && hipMalloc(&tu.x, xb) == hipSuccess &&
+               hipMalloc((void**)&tu.y, yb) == hipSuccess && hipMalloc(&tu.ws, tu.ws_cap) == hipSuccess &&
+               hipStreamCreate(&tu.stream) == hipSuccess && hipEventCreate(&tu.e0) == hipSuccess &&
+               hipEventCreate(&tu.e1) == hipSuccess && hipMemset(tu.w, 0, wb) == hipSuccess &&
+               hipMemset(tu.x, 0, xb) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+    if (!tok) tu.stream = nullptr;   // no tuning: every shape goes to rocBLAS
+    lt_setup(L->lt, L->g_qkv, dt, M, 3 * hid, hid, 3 * hid, tu);
+    lt_setup(L->lt, L->g_kv, dt, M, 2 * hid, hid, 3 * hid, tu);
+    lt_setup(L->lt, L->g_qg, dt, Mg, hid, hid, 3 * hid, tu);
+    lt_setup(L->lt, L->g_o, dt, M, hid, hid, hid, tu);
+    lt_setup(L->lt, L->g_f1, dt, M, inter, hid, inter, tu);
+    lt_setup(L->lt, L->g_f2, dt, M, hid, inter, hid, tu);
+    if (tu.e0) (void)hipEventDestroy(tu.e0);
+    if (tu.e1) (void)hipEventDestroy(tu.e1);
+    if (tu.stream) (void)hipStreamDestroy(tu.stream);
+    (void)hipFree(tu.w);
+    (void)hipFree(tu.x);
+    (void)hipFree(tu.y);
+    (void)hipFree(tu.ws);
+    (void)hipGetLastError();
+    for (const LtGemm* g : {&L->g_qkv, &L->g_kv, &L->g_qg, &L->g_o, &L->g_f1, &L->g_f2})
+      if (g->ok) L->lt_ws_bytes = std::max(L->lt_ws_bytes, g->ws);
+    if (L->lt_ws_bytes) alloc(&L->lt_ws, L->lt_ws_bytes);
+  }
   if (!ok) {
     free_layer(L);
     return LWATTN_E_NOMEM;
@@ -1045,21 +1190,24 @@ static lwattn_status layer_forward(lwattn_layer_t L, rocblas_datatype dt, const 
   auto blocks = [](int64_t threads) { return dim3((uint32_t)((threads + ly::LNT - 1) / ly::LNT)); };
   T* const* t = reinterpret_cast<T* const*>(L->qkv);
   // 1. projections.  Q, K, V: every row, bias added while splitting heads.
-  if (!gemm_rm(L->blas, dt, M, 3 * hid, hid, X, w->w_qkv, 3 * hid, L->P)) return LWATTN_E_DEVICE;
+  if (!layer_gemm(L, L->g_qkv, dt, X, w->w_qkv, L->P, stream)) return LWATTN_E_DEVICE;
   hipLaunchKernelGGL(ly::split_heads<T>, blocks(M * 3 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
                      (const T*)w->b_qkv, t[0], t[1], t[2], 3, c.B, c.n, H);
   // Kg, Vg: every row (the global rows attend to all keys), from the last two
   // column blocks of w_g
   const T* wg = (const T*)w->w_g;
-  if (!gemm_rm(L->blas, dt, M, 2 * hid, hid, X, wg + hid, 3 * hid, L->P)) return LWATTN_E_DEVICE;
+  if (!layer_gemm(L, L->g_kv, dt, X, wg + hid, L->P, stream)) return LWATTN_E_DEVICE;
   hipLaunchKernelGGL(ly::split_heads<T>, blocks(M * 2 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
                      (const T*)w->b_g + hid, t[4], t[5], t[5], 2, c.B, c.n, H);
   // Qg: only the global tokens' rows (the attention reads Qg nowhere else),
   // gathered, projected by the first column block of w_g and scattered back
   if (mg > 0) {
-    hipLaunchKernelGGL(ly::gather_global_rows<T>, dim3((uint32_t)c.B), dim3(ly::LNT), 0, stream, (const T*)X, lmask,
-                       gmask, c.n, (int)hid, mg, (T*)L->Xg, L->gpos);
-    if (!gemm_rm(L->blas, dt, (int64_t)c.B * mg, hid, hid, L->Xg, wg, 3 * hid, L->Pg)) return LWATTN_E_DEVICE;
+    const int64_t rows = (int64_t)c.B * mg;
+    hipLaunchKernelGGL(ly::find_global_rows, dim3((uint32_t)c.B), dim3(ly::LNT), 0, stream, lmask, gmask, c.n, mg,
+                       L->gpos);
+    hipLaunchKernelGGL(ly::gather_global_rows<T>, dim3((uint32_t)((rows + 3) / 4)), dim3(ly::LNT), 0, stream,
+                       (const T*)X, L->gpos, c.n, (int)hid, mg, rows, (T*)L->Xg);
+    if (!layer_gemm(L, L->g_qg, dt, L->Xg, wg, L->Pg, stream)) return LWATTN_E_DEVICE;
     hipLaunchKernelGGL(ly::scatter_global_rows<T>, blocks((int64_t)c.B * mg * hid / 8), dim3(ly::LNT), 0, stream,
                        L->Pg, (const T*)w->b_g, L->gpos, t[3], c.B, c.n, H, mg);
   }
@@ -1071,13 +1219,13 @@ static lwattn_status layer_forward(lwattn_layer_t L, rocblas_datatype dt, const 
   // 3. output projection, bias, residual, LayerNorm
   hipLaunchKernelGGL(ly::merge_heads<T>, blocks(M * hid / 8), dim3(ly::LNT), 0, stream, (const T*)L->A, (T*)L->Am,
                      c.B, c.n, H);
-  if (!gemm_rm(L->blas, dt, M, hid, hid, L->Am, w->w_o, hid, L->P)) return LWATTN_E_DEVICE;
+  if (!layer_gemm(L, L->g_o, dt, L->Am, w->w_o, L->P, stream)) return LWATTN_E_DEVICE;
   if (!layernorm<T>(H, L->P, w->b_o, X, w->ln1_g, w->ln1_b, L->eps, L->H1, M, stream)) return LWATTN_E_UNSUPPORTED;
   // 4. FFN: intermediate GEMM, bias, GELU; output GEMM, bias, residual, LayerNorm
-  if (!gemm_rm(L->blas, dt, M, inter, hid, L->H1, w->w_1, inter, L->P)) return LWATTN_E_DEVICE;
+  if (!layer_gemm(L, L->g_f1, dt, L->H1, w->w_1, L->P, stream)) return LWATTN_E_DEVICE;
   hipLaunchKernelGGL(ly::bias_gelu<T>, blocks(M * inter / 8), dim3(ly::LNT), 0, stream, L->P, (const T*)w->b_1,
                      (T*)L->F, M, (int)inter);
-  if (!gemm_rm(L->blas, dt, M, hid, inter, L->F, w->w_2, hid, L->P)) return LWATTN_E_DEVICE;
+  if (!layer_gemm(L, L->g_f2, dt, L->F, w->w_2, L->P, stream)) return LWATTN_E_DEVICE;
   if (!layernorm<T>(H, L->P, w->b_2, L->H1, w->ln2_g, w->ln2_b, L->eps, Y, M, stream)) return LWATTN_E_UNSUPPORTED;
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   return LWATTN_OK;

@@ -49,7 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # MI355X dense MFMA
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}     # MI355X dense MFMA
 PEAK_FP32_VECTOR = 157.3                          # MI355X fp32 vector ALU, TFLOP/s
 PEAK_BF16_MFMA = 2500.0                           # MI355X dense bf16 matrix cores, TFLOP/s
 PEAK_HBM_GBS = 8000.0
@@ -81,7 +81,7 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, dtype: str = "bf16"):
     """HBM bytes per attn_kernel launch from the committed counter summary, or
     None when there is none for this workload or the kernels changed since."""
     try:
@@ -94,7 +94,8 @@ def measured_traffic(workload: str):
         if not line.startswith("{"):
             continue
         rec = json.loads(line)
-        if rec.get("workload") == workload and rec.get("source_sha256") == want:
+        if rec.get("workload") == workload and rec.get("source_sha256") == want and \
+                rec.get("dtype", "bf16") == dtype:
             return rec
     return None
 
@@ -549,10 +550,11 @@ def run_layer(args, spec, x, lm, gm, plan):
         else:
             a = 0.1 * rng.standard_normal(shape)
         w_np[name] = a.astype(np.float32)
-    w = {k: torch.from_numpy(a).to(dev).to(torch.bfloat16) for k, a in w_np.items()}
+    tdt = lwattn.torch_dtype(spec.dtype)
+    w = {k: torch.from_numpy(a).to(dev).to(tdt) for k, a in w_np.items()}
     hid = spec.H * spec.d
     X_np = rng.standard_normal((spec.B * spec.n, hid)).astype(np.float32)
-    X = torch.from_numpy(X_np).to(dev).to(torch.bfloat16)
+    X = torch.from_numpy(X_np).to(dev).to(tdt)
     Y = torch.empty_like(X)
     layer.forward(X, w, lm, gm, out=Y)
     for _ in range(args.warmup):
@@ -707,6 +709,8 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="named workload (default: base; charlm for --pass causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", choices=("bf16", "f16", "f32"), default=None,
+                    help="storage type in place of the workload's own (forward and layer passes)")
     ap.add_argument("--no-timing", action="store_true",
                     help="do not record per-kernel HIP events (roofline fields become null)")
     ap.add_argument("--pass", dest="which", choices=("forward", "backward", "causal", "causal_backward", "blocksparse", "layer"), default="forward",
@@ -731,9 +735,14 @@ def main():
     if args.workload is None:
         args.workload = {"causal": "charlm", "causal_backward": "charlm", "blocksparse": "bsparse", "layer": "ftlayer"}.get(args.which, "base")
     spec = workloads.named(args.workload)
+    if args.dtype is not None:
+        if args.which not in ("forward", "layer"):
+            raise SystemExit("--dtype applies to the forward and layer passes")
+        import dataclasses
+        spec = dataclasses.replace(spec, dtype=args.dtype)
     x = workloads.generate(spec)
     dev = torch.device("cuda", 0)
-    tdt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+    tdt = lwattn.torch_dtype(spec.dtype)
     ts = [torch.from_numpy(a).to(dev).to(tdt) for a in x.tensors()]
     lm = torch.from_numpy(x.lmask).to(dev)
     gm = torch.from_numpy(x.gmask).to(dev)
@@ -790,7 +799,7 @@ def main():
     tokens = spec.B * spec.n
     value = tokens / (elapsed / args.steps)
     flop = fl.flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
-    nbytes = fl.hbm_bytes(x.lmask, x.gmask, spec.H, spec.d, 2 if spec.dtype == "bf16" else 4)
+    nbytes = fl.hbm_bytes(x.lmask, x.gmask, spec.H, spec.d, 4 if spec.dtype == "f32" else 2)
     peak = PEAK_TFLOPS[spec.dtype]
 
     roofline = None
@@ -812,7 +821,7 @@ def main():
         gbs = nbytes / t_attn / 1e9
         # the bound is the roof whose ideal time is longer at this arithmetic intensity
         hbm_bound = nbytes / (PEAK_HBM_GBS * 1e9) > flop / (peak * 1e12)
-        tr = measured_traffic(spec.name)
+        tr = measured_traffic(spec.name, spec.dtype)
         traffic = tr["traffic_bytes"] if tr else None
         if hbm_bound:
             roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -823,7 +832,7 @@ def main():
         if peaks:
             # the same achieved figure against what the probes measured on this GPU
             meas = peaks["hbm_read_gbs"] if hbm_bound else peaks["mfma_bf16_tflops"]
-            if hbm_bound or spec.dtype == "bf16":
+            if hbm_bound or spec.dtype != "f32":
                 roofline["frac_of_measured_peak"] = round(roofline["achieved"] / meas, 4)
                 roofline["measured_peak"] = meas
         roofline.update({

@@ -46,9 +46,14 @@ extern "C" {
 
 typedef struct lwattn_plan_s* lwattn_plan_t;
 
-/* Storage type of Q, K, V, Qg, Kg, Vg and O.  Scores, softmax and the output
- * accumulation are always float32. */
-typedef enum { LWATTN_F32 = 0, LWATTN_BF16 = 1 } lwattn_dtype;
+/* Storage type of Q, K, V, Qg, Kg, Vg and O (FasterTransformer Longformer
+ * encoder guide, implementation scope: the float, half and bfloat16
+ * instantiations).  Scores, softmax and the output accumulation are always
+ * float32; with 16-bit storage the matrix cores take the probabilities rounded
+ * to the storage type.  LWATTN_F16 (IEEE half) runs the forward
+ * (lwattn_forward, lwattn_forward_noalloc) and the encoder layer; the backward,
+ * causal and block-sparse calls return LWATTN_E_UNSUPPORTED for it. */
+typedef enum { LWATTN_F32 = 0, LWATTN_BF16 = 1, LWATTN_F16 = 2 } lwattn_dtype;
 
 typedef enum {
   LWATTN_OK = 0,

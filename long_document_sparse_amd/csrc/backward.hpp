@@ -100,12 +100,12 @@ __device__ __forceinline__ void store16(uint8_t* dst, const float (&v)[16]) {
 // tile, row-major ([row][d]) or transposed ([d][row]).
 template <bool BF>
 __device__ __forceinline__ void load_tile(float* dst, const uint8_t* head, const int* pos, bool tr) {
-  constexpr int RB = D * Lay<BF>::ELT;
+  constexpr int RB = D * (BF ? 2 : 4);
   const int t = threadIdx.x, row = t >> 2, q = t & 3;
   const int ps = pos[row];
   float v[16];
   if (ps >= 0) {
-    load16<BF>(head + (int64_t)ps * RB + q * 16 * Lay<BF>::ELT, v);
+    load16<BF>(head + (int64_t)ps * RB + q * 16 * (BF ? 2 : 4), v);
   } else {
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = 0.0f;
@@ -171,14 +171,14 @@ __device__ __forceinline__ void put(float* dst, const float (&c)[4][4]) {
 template <bool BF>
 __device__ __forceinline__ void store_tile(uint8_t* head, const float* src, const int* pos,
                                            const uint8_t* keep) {
-  constexpr int RB = D * Lay<BF>::ELT;
+  constexpr int RB = D * (BF ? 2 : 4);
   const int t = threadIdx.x, row = t >> 2, q = t & 3;
   const int ps = pos[row];
   if (ps < 0 || !keep[row]) return;
   float v[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) v[e] = src[row * LS + 16 * q + e];
-  store16<BF>(head + (int64_t)ps * RB + q * 16 * Lay<BF>::ELT, v);
+  store16<BF>(head + (int64_t)ps * RB + q * 16 * (BF ? 2 : 4), v);
 }
 
 // Shared per-tile bookkeeping in LDS.
@@ -201,7 +201,7 @@ struct KeyTiles {
 // gradient, and the rows' (log-sum-exp, D).
 template <bool BF>
 __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, float* sm, Meta& mt) {
-  constexpr int RB = D * Lay<BF>::ELT;
+  constexpr int RB = D * (BF ? 2 : 4);
   float* tQ = sm;
   float* tdO = sm + TILE;
   float* tK = sm + 2 * TILE;
@@ -355,7 +355,7 @@ __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, floa
 // dQg of global rows T*gt .. T*gt+63 of (b, h): every real key, with Qg, Kg, Vg.
 template <bool BF>
 __device__ void dq_global(const BwParams& p, int b, int h, int gt, float* sm, Meta& mt) {
-  constexpr int RB = D * Lay<BF>::ELT;
+  constexpr int RB = D * (BF ? 2 : 4);
   float* tQ = sm;
   float* tdO = sm + TILE;
   float* tK = sm + 2 * TILE;
@@ -538,7 +538,7 @@ __device__ __forceinline__ void kv_sweep(const BwParams& p, const uint8_t* Qsrc,
 // of residue class rho of (b, h).
 template <bool BF>
 __device__ void dkv_window(const BwParams& p, int b, int h, int rho, int blk, float* sm, Meta& mt) {
-  constexpr int RB = D * Lay<BF>::ELT;
+  constexpr int RB = D * (BF ? 2 : 4);
   float* tK = sm;
   float* tV = sm + TILE;
   float* tQ = sm + 2 * TILE;
@@ -641,7 +641,7 @@ __device__ void dkv_window(const BwParams& p, int b, int h, int rho, int blk, fl
 // them through K and V.
 template <bool BF>
 __device__ void dkv_global_keys(const BwParams& p, int b, int h, int gt, float* sm, Meta& mt) {
-  constexpr int RB = D * Lay<BF>::ELT;
+  constexpr int RB = D * (BF ? 2 : 4);
   float* tK = sm;
   float* tV = sm + TILE;
   float* tQ = sm + 2 * TILE;

@@ -58,6 +58,30 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Storage element types: float, or one of the two 16-bit formats (__bf16,
+// _Float16), which share every layout and differ only in the matrix-core and
+// dot-product instructions and the rounding of conversions.
+template <typename S, int N>
+using svec = S __attribute__((ext_vector_type(N)));
+template <typename S>
+__device__ __host__ constexpr bool is16() { return sizeof(S) == 2; }
+
+// 32x32x16 matrix-core product, fp32 accumulation, for either 16-bit format.
+__device__ __forceinline__ f32x16 mfma16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma16(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// acc + a0 b0 + a1 b1 in fp32, for either 16-bit format.
+__device__ __forceinline__ float dot2(svec<__bf16, 2> a, svec<__bf16, 2> b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(a, b, acc, false);
+}
+__device__ __forceinline__ float dot2(svec<_Float16, 2> a, svec<_Float16, 2> b, float acc) {
+  return __builtin_amdgcn_fdot2(a, b, acc, false);
+}
 
 struct Params {
   const uint8_t *Q, *K, *V, *Qg, *Kg, *Vg;
@@ -96,10 +120,7 @@ struct Params {
 
 // ---------------------------------------------------------------------------
 // Layout of one LDS tile slot.
-template <bool BF>
-struct Lay;
-template <>
-struct Lay<true> {             // bf16 storage
+struct Lay16 {                 // 16-bit storage
   static constexpr int ELT = 2;
   static constexpr int CH = 8;           // 16-byte chunks per 64-element row
   static constexpr int KROW = 144;       // K row stride (128 + 16 pad: conflict-free b128 reads)
@@ -107,8 +128,7 @@ struct Lay<true> {             // bf16 storage
   static constexpr int KBYTES = KT * KROW;
   static constexpr int VBYTES = D * VROW;
 };
-template <>
-struct Lay<false> {            // float32 storage
+struct Lay32 {                 // float32 storage
   static constexpr int ELT = 4;
   static constexpr int CH = 16;
   static constexpr int KROW = 272;
@@ -116,14 +136,16 @@ struct Lay<false> {            // float32 storage
   static constexpr int KBYTES = KT * KROW;
   static constexpr int VBYTES = KT * VROW;
 };
-template <bool BF>
+template <typename S>
+struct Lay : std::conditional_t<sizeof(S) == 2, Lay16, Lay32> {};
+template <typename S>
 struct SlotLay {
   static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = Lay<BF>::KBYTES;
-  static constexpr int POS_OFF = V_OFF + Lay<BF>::VBYTES;
+  static constexpr int V_OFF = Lay<S>::KBYTES;
+  static constexpr int POS_OFF = V_OFF + Lay<S>::VBYTES;
   static constexpr int OK_OFF = POS_OFF + KT * 4;      // uint32: bit k = key k usable
   static constexpr int BYTES = (OK_OFF + 4 + 15) / 16 * 16;
-  static constexpr int NCH = KT * Lay<BF>::CH / NT;    // chunks per thread per array
+  static constexpr int NCH = KT * Lay<S>::CH / NT;    // chunks per thread per array
 };
 
 // Which keys a tile holds.  Positions are computed for every key, clamped to
@@ -153,9 +175,9 @@ __device__ __forceinline__ void key_pos(const TileDesc& td, const Ctx& cx, int k
     pos = td.base + jc * td.stride;
 }
 
-template <bool BF>
+template <typename S>
 struct Stage {
-  static constexpr int NCH = SlotLay<BF>::NCH;
+  static constexpr int NCH = SlotLay<S>::NCH;
   uint4 kr[NCH], vr[NCH];
   bool in[NCH];     // the chunk's key exists
   uint8_t fl[NCH];  // raw flag byte of that key (bit0: real token), inspected at store time
@@ -168,15 +190,15 @@ struct Stage {
 // Issue the global loads of one tile into registers.  Nothing here consumes a
 // loaded value, and no load sits under a divergent branch, so the compiler
 // need not wait for them before the next tile's compute.
-template <bool BF>
-__device__ __forceinline__ void stage_load(Stage<BF>& st, const TileDesc& td, const Ctx& cx,
+template <typename S>
+__device__ __forceinline__ void stage_load(Stage<S>& st, const TileDesc& td, const Ctx& cx,
                                            const uint8_t* kbase, const uint8_t* vbase) {
-  constexpr int CH = Lay<BF>::CH;
-  constexpr int RB = D * Lay<BF>::ELT;
+  constexpr int CH = Lay<S>::CH;
+  constexpr int RB = D * Lay<S>::ELT;
   const int tid = threadIdx.x;
   st.list = td.list != 0;
 #pragma unroll
-  for (int e = 0; e < Stage<BF>::NCH; ++e) {
+  for (int e = 0; e < Stage<S>::NCH; ++e) {
     const int q = tid + NT * e;
     const int kt = q / CH, ch = q % CH;
     int pos;
@@ -201,30 +223,30 @@ constexpr int JREL_NONE = -(1 << 30);
 // Write the staged registers into an LDS slot (V transposed for bf16).  For a
 // global-column tile the slot also gets, per key, its index in the band's
 // residue subsequence (or JREL_NONE), used to drop keys already in the window.
-template <bool BF>
-__device__ __forceinline__ void stage_store(const Stage<BF>& st, uint8_t* slot, const TileDesc& td,
+template <typename S>
+__device__ __forceinline__ void stage_store(const Stage<S>& st, uint8_t* slot, const TileDesc& td,
                                             const Ctx& cx) {
-  using SL = SlotLay<BF>;
-  constexpr int CH = Lay<BF>::CH;
+  using SL = SlotLay<S>;
+  constexpr int CH = Lay<S>::CH;
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int e = 0; e < Stage<BF>::NCH; ++e) {
+  for (int e = 0; e < Stage<S>::NCH; ++e) {
     const int q = tid + NT * e;
     const int kt = q / CH, ch = q % CH;
     const uint4 z = make_uint4(0, 0, 0, 0);
     const bool use = st.in[e] && (st.list || (st.fl[e] & 1));
     const uint4 kv = use ? st.kr[e] : z;
     const uint4 vv = use ? st.vr[e] : z;
-    *reinterpret_cast<uint4*>(slot + SL::K_OFF + kt * Lay<BF>::KROW + ch * 16) = kv;
-    if constexpr (BF) {
+    *reinterpret_cast<uint4*>(slot + SL::K_OFF + kt * Lay<S>::KROW + ch * 16) = kv;
+    if constexpr (is16<S>()) {
       const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const uint16_t hv = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
-        *reinterpret_cast<uint16_t*>(slot + SL::V_OFF + (ch * 8 + t) * Lay<BF>::VROW + kt * 2) = hv;
+        *reinterpret_cast<uint16_t*>(slot + SL::V_OFF + (ch * 8 + t) * Lay<S>::VROW + kt * 2) = hv;
       }
     } else {
-      *reinterpret_cast<uint4*>(slot + SL::V_OFF + kt * Lay<BF>::VROW + ch * 16) = vv;
+      *reinterpret_cast<uint4*>(slot + SL::V_OFF + kt * Lay<S>::VROW + ch * 16) = vv;
     }
   }
   if (tid < 64) {
@@ -243,64 +265,62 @@ __device__ __forceinline__ void stage_store(const Stage<BF>& st, uint8_t* slot, 
 // MFMA work per tile is 8x longer, keeps one register set.  `pre()` runs once
 // after the first loads are issued and before the first barrier.  Every thread
 // of the workgroup must call it with the same U >= 1.
-template <bool BF, class DescFn, class CompFn, class PreFn>
+template <typename S, class DescFn, class CompFn, class PreFn>
 __device__ __forceinline__ void tile_pipeline(int U, DescFn desc, CompFn comp, PreFn pre,
                                               const Ctx& cx, const uint8_t* kbase,
                                               const uint8_t* vbase, uint8_t* smem) {
-  using SL = SlotLay<BF>;
+  using SL = SlotLay<S>;
   uint8_t* slot0 = smem;
   uint8_t* slot1 = smem + SL::BYTES;
-  if constexpr (BF) {
-    Stage<BF> s0, s1;
-    stage_load<BF>(s0, desc(0), cx, kbase, vbase);
-    if (U > 1) stage_load<BF>(s1, desc(1), cx, kbase, vbase);
+  if constexpr (is16<S>()) {
+    Stage<S> s0, s1;
+    stage_load<S>(s0, desc(0), cx, kbase, vbase);
+    if (U > 1) stage_load<S>(s1, desc(1), cx, kbase, vbase);
     pre();
-    stage_store<BF>(s0, slot0, desc(0), cx);
+    stage_store<S>(s0, slot0, desc(0), cx);
     __syncthreads();
     for (int u = 0; u < U; u += 2) {
-      if (u + 2 < U) stage_load<BF>(s0, desc(u + 2), cx, kbase, vbase);
+      if (u + 2 < U) stage_load<S>(s0, desc(u + 2), cx, kbase, vbase);
       comp(u, slot0);
-      if (u + 1 < U) stage_store<BF>(s1, slot1, desc(u + 1), cx);
+      if (u + 1 < U) stage_store<S>(s1, slot1, desc(u + 1), cx);
       __syncthreads();
       if (u + 1 >= U) break;
-      if (u + 3 < U) stage_load<BF>(s1, desc(u + 3), cx, kbase, vbase);
+      if (u + 3 < U) stage_load<S>(s1, desc(u + 3), cx, kbase, vbase);
       comp(u + 1, slot1);
-      if (u + 2 < U) stage_store<BF>(s0, slot0, desc(u + 2), cx);
+      if (u + 2 < U) stage_store<S>(s0, slot0, desc(u + 2), cx);
       __syncthreads();
     }
   } else {
-    Stage<BF> st;
-    stage_load<BF>(st, desc(0), cx, kbase, vbase);
+    Stage<S> st;
+    stage_load<S>(st, desc(0), cx, kbase, vbase);
     pre();
-    stage_store<BF>(st, slot0, desc(0), cx);
+    stage_store<S>(st, slot0, desc(0), cx);
     __syncthreads();
     for (int u = 0; u < U; ++u) {
       const bool more = u + 1 < U;
-      if (more) stage_load<BF>(st, desc(u + 1), cx, kbase, vbase);
+      if (more) stage_load<S>(st, desc(u + 1), cx, kbase, vbase);
       comp(u, (u & 1) ? slot1 : slot0);
-      if (more) stage_store<BF>(st, (u & 1) ? slot0 : slot1, desc(u + 1), cx);
+      if (more) stage_store<S>(st, (u & 1) ? slot0 : slot1, desc(u + 1), cx);
       __syncthreads();
     }
   }
 }
 
 // Query operand held in registers for the whole key loop.
-template <bool BF>
-struct QOp;
-template <>
-struct QOp<true> {
-  bf16x8 q[4];   // Q[row][32*h + 8*c .. +8], c = 0..3
+template <typename S>
+struct QOp {                   // 16-bit storage
+  svec<S, 8> q[4];   // Q[row][32*h + 8*c .. +8], c = 0..3
   __device__ void load(const uint8_t* row, bool ok, int h) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (ok) v = *reinterpret_cast<const uint4*>(row + (32 * h + 8 * c) * 2);
-      q[c] = __builtin_bit_cast(bf16x8, v);
+      q[c] = __builtin_bit_cast(svec<S, 8>, v);
     }
   }
 };
 template <>
-struct QOp<false> {
+struct QOp<float> {
   float q[32];   // Q[row][32*h + c], c = 0..31
   __device__ void load(const uint8_t* row, bool ok, int h) {
 #pragma unroll
@@ -316,24 +336,25 @@ struct QOp<false> {
 };
 
 // S^T tile: 16 scores of this lane's query.
-__device__ __forceinline__ f32x16 qk_tile(const QOp<true>& qo, const uint8_t* slot, int lane) {
+template <typename S>
+__device__ __forceinline__ f32x16 qk_tile(const QOp<S>& qo, const uint8_t* slot, int lane) {
   const int key = lane & 31, h = lane >> 5;
   f32x16 s = {};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(slot + SlotLay<true>::K_OFF +
-                                                      key * Lay<true>::KROW + (4 * h + c) * 16);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qo.q[c], s, 0, 0, 0);
+    const svec<S, 8> a = *reinterpret_cast<const svec<S, 8>*>(slot + SlotLay<S>::K_OFF +
+                                                              key * Lay<S>::KROW + (4 * h + c) * 16);
+    s = mfma16(a, qo.q[c], s);
   }
   return s;
 }
-__device__ __forceinline__ f32x16 qk_tile(const QOp<false>& qo, const uint8_t* slot, int lane) {
+__device__ __forceinline__ f32x16 qk_tile(const QOp<float>& qo, const uint8_t* slot, int lane) {
   const int key = lane & 31, h = lane >> 5;
   f32x16 s = {};
 #pragma unroll
   for (int c4 = 0; c4 < 8; ++c4) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(slot + SlotLay<false>::K_OFF +
-                                                    key * Lay<false>::KROW + (8 * h + c4) * 16);
+    const f32x4 a = *reinterpret_cast<const f32x4*>(slot + SlotLay<float>::K_OFF +
+                                                    key * Lay<float>::KROW + (8 * h + c4) * 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qo.q[4 * c4 + e], s, 0, 0, 0);
@@ -342,37 +363,39 @@ __device__ __forceinline__ f32x16 qk_tile(const QOp<false>& qo, const uint8_t* s
 }
 
 // O^T += V^T * P^T for one tile.
+template <typename S>
 __device__ __forceinline__ void pv_tile(f32x16 (&o)[2], const float (&p)[16], const uint8_t* slot,
-                                        int lane, std::true_type) {
+                                        int lane) {
   const int h = lane >> 5, dl = lane & 31;
-  const uint8_t* vt = slot + SlotLay<true>::V_OFF;
+  const uint8_t* vt = slot + SlotLay<S>::V_OFF;
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    bf16x8 bp;
+    svec<S, 8> bp;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bp[e] = (__bf16)p[8 * c2 + e];
+    for (int e = 0; e < 8; ++e) bp[e] = (S)p[8 * c2 + e];
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      const uint8_t* row = vt + (32 * db + dl) * Lay<true>::VROW;
-      const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + (16 * c2 + 4 * h) * 2);
-      const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + (16 * c2 + 8 + 4 * h) * 2);
-      bf16x8 a;
+      const uint8_t* row = vt + (32 * db + dl) * Lay<S>::VROW;
+      const svec<S, 4> lo = *reinterpret_cast<const svec<S, 4>*>(row + (16 * c2 + 4 * h) * 2);
+      const svec<S, 4> hi = *reinterpret_cast<const svec<S, 4>*>(row + (16 * c2 + 8 + 4 * h) * 2);
+      svec<S, 8> a;
       a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
       a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[db], 0, 0, 0);
+      o[db] = mfma16(a, bp, o[db]);
     }
   }
 }
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[2], const float (&p)[16], const uint8_t* slot,
-                                        int lane, std::false_type) {
+template <>
+__device__ __forceinline__ void pv_tile<float>(f32x16 (&o)[2], const float (&p)[16], const uint8_t* slot,
+                                               int lane) {
   const int h = lane >> 5, dl = lane & 31;
-  const uint8_t* vb = slot + SlotLay<false>::V_OFF;
+  const uint8_t* vb = slot + SlotLay<float>::V_OFF;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = 8 * (r >> 2) + 4 * h + (r & 3);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      const float a = *reinterpret_cast<const float*>(vb + key * Lay<false>::VROW + (32 * db + dl) * 4);
+      const float a = *reinterpret_cast<const float*>(vb + key * Lay<float>::VROW + (32 * db + dl) * 4);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p[r], o[db], 0, 0, 0);
     }
   }
@@ -581,11 +604,11 @@ __device__ __forceinline__ bool wait_ready(const Params& p, int b, bool acquire)
 // mask_kind: 0 none, 1 window tile (key usable and |i - j| <= r),
 //            2 global columns (usable and not already in the row's window),
 //            3 key usable only.  Every mask is a select, never a branch.
-template <bool BF>
-__device__ __forceinline__ void process_tile(const QOp<BF>& qo, Softmax& sm, const uint8_t* slot,
+template <typename S>
+__device__ __forceinline__ void process_tile(const QOp<S>& qo, Softmax& sm, const uint8_t* slot,
                                              int lane, float c, int mask_kind, int my_i, int band_j0,
                                              int r) {
-  using SL = SlotLay<BF>;
+  using SL = SlotLay<S>;
   f32x16 sc = qk_tile(qo, slot, lane);
   if (mask_kind != 0) {
     const uint32_t okb = *reinterpret_cast<const uint32_t*>(slot + SL::OK_OFF);
@@ -619,15 +642,15 @@ __device__ __forceinline__ void process_tile(const QOp<BF>& qo, Softmax& sm, con
   }
   float pr[16];
   sm.update(sc, c, pr);
-  pv_tile(sm.o, pr, slot, lane, std::integral_constant<bool, BF>());
+  pv_tile<S>(sm.o, pr, slot, lane);
 }
 
-template <bool BF>
+template <typename S>
 __device__ __forceinline__ void store_row4(uint8_t* dst, const float* v) {
-  if constexpr (BF) {
-    bf16x4 t;
-    t[0] = (__bf16)v[0]; t[1] = (__bf16)v[1]; t[2] = (__bf16)v[2]; t[3] = (__bf16)v[3];
-    *reinterpret_cast<bf16x4*>(dst) = t;
+  if constexpr (is16<S>()) {
+    svec<S, 4> t;
+    t[0] = (S)v[0]; t[1] = (S)v[1]; t[2] = (S)v[2]; t[3] = (S)v[3];
+    *reinterpret_cast<svec<S, 4>*>(dst) = t;
   } else {
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
   }
@@ -637,13 +660,13 @@ __device__ __forceinline__ void store_row4(uint8_t* dst, const float* v) {
 // beyond it are read from the global-index list directly (second pass).
 constexpr int GL_MAX = 512;
 
-template <bool BF>
-constexpr int smem_bytes_general() { return 2 * SlotLay<BF>::BYTES + GL_MAX * 4; }
+template <typename S>
+constexpr int smem_bytes_general() { return 2 * SlotLay<S>::BYTES + GL_MAX * 4; }
 
-template <bool BF>
+template <typename S>
 __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t* smem) {
-  using SL = SlotLay<BF>;
-  constexpr int RB = D * Lay<BF>::ELT;
+  using SL = SlotLay<S>;
+  constexpr int RB = D * Lay<S>::ELT;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = p.n;
@@ -681,7 +704,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
   const bool row_in = my_i < nr;
   const int my_pos = rho + (row_in ? my_i : 0) * s;
   const uint8_t my_fl = cx.fl[my_pos];
-  QOp<BF> qo;
+  QOp<S> qo;
   qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
   Softmax sm;
   sm.init();
@@ -712,11 +735,11 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
       if (up >= 0 && up < T) {
         const uint32_t okb = *reinterpret_cast<const uint32_t*>(slot + SL::OK_OFF);
         const bool diag = (up == 0) || (32 * up + 31 > 2 * r);
-        process_tile<BF>(qo, sm, slot, lane, p.c, (diag || okb != 0xFFFFFFFFu) ? 1 : 0, my_i,
+        process_tile<S>(qo, sm, slot, lane, p.c, (diag || okb != 0xFFFFFFFFu) ? 1 : 0, my_i,
                          kb + t * KT, r);
       }
     } else {
-      process_tile<BF>(qo, sm, slot, lane, p.c, 2, my_i, 0, r);
+      process_tile<S>(qo, sm, slot, lane, p.c, 2, my_i, 0, r);
     }
   };
   auto fill_gl = [&]() {
@@ -726,11 +749,11 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
   const uint8_t* kbase = p.K + head * RB;
   const uint8_t* vbase = p.V + head * RB;
   if (nband >= 2 || ngt == 0) {
-    tile_pipeline<BF>(U, desc, comp, fill_gl, cx, kbase, vbase, smem);
+    tile_pipeline<S>(U, desc, comp, fill_gl, cx, kbase, vbase, smem);
   } else {
     fill_gl();
     __syncthreads();
-    tile_pipeline<BF>(U, desc, comp, nothing, cx, kbase, vbase, smem);
+    tile_pipeline<S>(U, desc, comp, nothing, cx, kbase, vbase, smem);
   }
   if (g > GL_MAX) {
     // global columns past the LDS copy: positions straight from the list
@@ -747,9 +770,9 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
       return td;
     };
     auto comp2 = [&](int u, const uint8_t* slot) {
-      if (wave_work) process_tile<BF>(qo, sm, slot, lane, p.c, 2, my_i, 0, r);
+      if (wave_work) process_tile<S>(qo, sm, slot, lane, p.c, 2, my_i, 0, r);
     };
-    tile_pipeline<BF>(U2, desc2, comp2, nothing, cx2, kbase, vbase, smem);
+    tile_pipeline<S>(U2, desc2, comp2, nothing, cx2, kbase, vbase, smem);
   }
 
   // normalise and store this lane's half of its query row (global rows are
@@ -766,7 +789,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = valid ? sm.o[db][4 * a + e] * inv : 0.0f;
-        store_row4<BF>(orow + (32 * db + 8 * a + 4 * h32) * Lay<BF>::ELT, v);
+        store_row4<S>(orow + (32 * db + 8 * a + 4 * h32) * Lay<S>::ELT, v);
       }
     }
   }
@@ -781,7 +804,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
 // channels 32 (l / 32) .. +31; pos is that row's sequence position.  The
 // partials are streamed two chunks deep, so the merge waits for about one
 // memory round trip instead of one per chunk.
-template <bool BF>
+template <typename S>
 __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g, int lane, int pos) {
   // this slice's partial rows are written back before it is counted; the
   // wave that counts the last slice reads all of them with coherent loads
@@ -853,17 +876,17 @@ __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g,
     const float inv = 1.0f / L;
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] *= inv;
-    constexpr int RB = D * Lay<BF>::ELT;
-    uint8_t* orow = p.O + (((int64_t)b * p.H + h) * p.n + pos) * RB + 32 * ch * Lay<BF>::ELT;
+    constexpr int RB = D * Lay<S>::ELT;
+    uint8_t* orow = p.O + (((int64_t)b * p.H + h) * p.n + pos) * RB + 32 * ch * Lay<S>::ELT;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) store_row4<BF>(orow + 4 * k * Lay<BF>::ELT, acc + 4 * k);
+    for (int k = 0; k < 8; ++k) store_row4<S>(orow + 4 * k * Lay<S>::ELT, acc + 4 * k);
   }
   if (lane == 0) *cnt = 0;
 }
 
-template <bool BF>
+template <typename S>
 __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t* smem) {
-  constexpr int RB = D * Lay<BF>::ELT;
+  constexpr int RB = D * Lay<S>::ELT;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   int g = p.gcnt[b];
@@ -884,7 +907,7 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
   const int qidx = qt * 32 + qi;
   const bool qok = wave_work && qidx < g;
   const int qpos = gidx_b[qok ? qidx : 0];
-  QOp<BF> qo;
+  QOp<S> qo;
   qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
   Softmax sm;
   sm.init();
@@ -904,11 +927,11 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
   };
   auto comp = [&](int u, const uint8_t* slot) {
     if (!wave_work) return;
-    const uint32_t okb = *reinterpret_cast<const uint32_t*>(slot + SlotLay<BF>::OK_OFF);
-    process_tile<BF>(qo, sm, slot, lane, p.c, okb == 0xFFFFFFFFu ? 0 : 3, 0, 0, 0);
+    const uint32_t okb = *reinterpret_cast<const uint32_t*>(slot + SlotLay<S>::OK_OFF);
+    process_tile<S>(qo, sm, slot, lane, p.c, okb == 0xFFFFFFFFu ? 0 : 3, 0, 0, 0);
   };
   auto nothing = []() {};
-  tile_pipeline<BF>(U, desc, comp, nothing, cx, p.Kg + head * RB, p.Vg + head * RB, smem);
+  tile_pipeline<S>(U, desc, comp, nothing, cx, p.Kg + head * RB, p.Vg + head * RB, smem);
 
   const float lt = sm.l + __shfl_xor(sm.l, 32);
   if (qok) {
@@ -925,7 +948,7 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
       p.part_ml[pidx * 2 + 1] = lt;
     }
   }
-  if (wave_work) finish_global_tile<BF>(p, b, h, qt, g, lane, qpos);
+  if (wave_work) finish_global_tile<S>(p, b, h, qt, g, lane, qpos);
 }
 
 // ---------------------------------------------------------------------------
@@ -989,12 +1012,13 @@ struct FLane {
   }
 };
 
-__device__ __forceinline__ f32x16 fqk(const QOp<true>& qo, const uint8_t* kt, const FLane& fl) {
+template <typename S>
+__device__ __forceinline__ f32x16 fqk(const QOp<S>& qo, const uint8_t* kt, const FLane& fl) {
   f32x16 s = {};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + fl.k[c]);
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qo.q[c], s, 0, 0, 0);
+    const svec<S, 8> a = *reinterpret_cast<const svec<S, 8>*>(kt + fl.k[c]);
+    s = mfma16(a, qo.q[c], s);
   }
   return s;
 }
@@ -1004,7 +1028,8 @@ __device__ __forceinline__ s16x4 tr_read(const uint8_t* addr) {
       (__attribute__((address_space(3))) s16x4*)(addr));
 }
 
-__device__ __forceinline__ void fpv(f32x16 (&o)[2], const bf16x8 (&pb)[2], const uint8_t* vt,
+template <typename S>
+__device__ __forceinline__ void fpv(f32x16 (&o)[2], const svec<S, 8> (&pb)[2], const uint8_t* vt,
                                     const FLane& fl) {
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
@@ -1014,8 +1039,7 @@ __device__ __forceinline__ void fpv(f32x16 (&o)[2], const bf16x8 (&pb)[2], const
       const s16x4 hi = tr_read(vt + fl.v[db] + c2 * 2048 + 1024);     // keys 16c2 + 8 + 4h + e
       typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[c2], o[db],
-                                                      0, 0, 0);
+      o[db] = mfma16(__builtin_bit_cast(svec<S, 8>, a8), pb[c2], o[db]);
     }
   }
 }
@@ -1096,9 +1120,11 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return d;
 }
 
-// Online-softmax update of one tile; the probabilities come out as bf16 and
-// the row sum is taken over those rounded values (the ones PV multiplies).
-__device__ __forceinline__ void softmax_bf16(Softmax& sm, const f32x16& s, float c, bf16x8 (&pb)[2]) {
+// Online-softmax update of one tile; the probabilities come out in the 16-bit
+// storage format and the row sum is taken over those rounded values (the ones
+// PV multiplies).
+template <typename S>
+__device__ __forceinline__ void softmax16(Softmax& sm, const f32x16& s, float c, svec<S, 8> (&pb)[2]) {
   float mx = max3f(s[0], s[1], s[2]);
 #pragma unroll
   for (int r = 3; r < 15; r += 2) mx = max3f(mx, s[r], s[r + 1]);
@@ -1112,19 +1138,18 @@ __device__ __forceinline__ void softmax_bf16(Softmax& sm, const f32x16& s, float
     for (int r = 0; r < 16; ++r) { sm.o[0][r] *= alpha; sm.o[1][r] *= alpha; }
     sm.m = mnew;
   }
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const svec<S, 2> ones = {(S)1.0f, (S)1.0f};
   float acc = sm.l;
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      bf16x2 pp;
-      pp[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e], c, -sm.m));
-      pp[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e + 1], c, -sm.m));
+      svec<S, 2> pp;
+      pp[0] = (S)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e], c, -sm.m));
+      pp[1] = (S)__builtin_amdgcn_exp2f(fmaf(s[8 * c2 + e + 1], c, -sm.m));
       pb[c2][e] = pp[0];
       pb[c2][e + 1] = pp[1];
-      acc = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, acc, false);
+      acc = dot2(pp, ones, acc);
     }
   }
   sm.l = acc;
@@ -1224,26 +1249,25 @@ struct BandRow {
   bool first;    // the offset is still to be set from the first half with a live key
 };
 
-// Probabilities of one 32-key half (bf16, as PV multiplies them) and this
+// Probabilities of one 32-key half (16-bit, as PV multiplies them) and this
 // lane's share of their sum.  The scores arrive already scaled and offset
 // (c s - m0: Q is pre-scaled by c and the QK^T accumulator starts at -m0), so
 // p = 2^(s - x) with x the part of the row's offset beyond m0 -- zero until a
 // rebase, and then the subtraction is only paid off the fast loop.
-template <bool OFF>
-__device__ __forceinline__ float band_exp_half(const f32x16& s, float x, bf16x8 (&pb)[2]) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+template <bool OFF, typename S>
+__device__ __forceinline__ float band_exp_half(const f32x16& s, float x, svec<S, 8> (&pb)[2]) {
+  const svec<S, 2> ones = {(S)1.0f, (S)1.0f};
   float acc = 0.f;
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      bf16x2 q;
-      q[0] = (__bf16)__builtin_amdgcn_exp2f(OFF ? s[8 * c2 + e] - x : s[8 * c2 + e]);
-      q[1] = (__bf16)__builtin_amdgcn_exp2f(OFF ? s[8 * c2 + e + 1] - x : s[8 * c2 + e + 1]);
+      svec<S, 2> q;
+      q[0] = (S)__builtin_amdgcn_exp2f(OFF ? s[8 * c2 + e] - x : s[8 * c2 + e]);
+      q[1] = (S)__builtin_amdgcn_exp2f(OFF ? s[8 * c2 + e + 1] - x : s[8 * c2 + e + 1]);
       pb[c2][e] = q[0];
       pb[c2][e + 1] = q[1];
-      acc = __builtin_amdgcn_fdot2_f32_bf16(q, ones, acc, false);
+      acc = dot2(q, ones, acc);
     }
   }
   return acc;
@@ -1253,8 +1277,9 @@ __device__ __forceinline__ float band_exp_half(const f32x16& s, float x, bf16x8 
 // offset is still unset.  Such rows move their offset to the half's maximum,
 // rescale what they have accumulated and recompute the half.  s is relative
 // to the row's m0.
+template <typename S>
 __device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float m0,
-                                            bf16x8 (&pb)[2], float& ts) {
+                                            svec<S, 8> (&pb)[2], float& ts) {
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -1270,23 +1295,25 @@ __device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float 
 #pragma unroll
   for (int r = 0; r < 16; ++r) { st.o[0][r] *= alpha; st.o[1][r] *= alpha; }
   st.m += delta;
-  ts = band_exp_half<true>(s, st.m - m0, pb);
+  ts = band_exp_half<true, S>(s, st.m - m0, pb);
 }
 
 // Q scaled by c = scale log2(e) once, so that QK^T yields the exponent's
-// argument directly (the scaled value is rounded to bf16, a relative change of
-// at most 2^-9 per element).
-__device__ __forceinline__ void scale_q(QOp<true>& qo, float c) {
+// argument directly (the scaled value is rounded to the storage format: a
+// relative change of at most 2^-9 per element in bf16, 2^-12 in fp16).
+template <typename S>
+__device__ __forceinline__ void scale_q(QOp<S>& qo, float c) {
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qo.q[cc][e] = (__bf16)((float)qo.q[cc][e] * c);
+    for (int e = 0; e < 8; ++e) qo.q[cc][e] = (S)((float)qo.q[cc][e] * c);
 }
 
-__device__ __forceinline__ bf16x8 vfrag(const uint8_t* vt, int off) {
+template <typename S>
+__device__ __forceinline__ svec<S, 8> vfrag(const uint8_t* vt, int off) {
   const s16x4 lo = tr_read(vt + off);
   const s16x4 hi = tr_read(vt + off + 1024);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_bit_cast(svec<S, 8>, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Scheduling template for one phase: each of the 8 MFMAs followed by the LDS
@@ -1308,9 +1335,10 @@ __device__ __forceinline__ void interleave_hint() {
 
 // MFMA operands of one phase: K of one half (A of QK^T) and V^T of one half
 // (A of PV), read from LDS one phase ahead.
+template <typename S>
 struct PhaseOps {
-  bf16x8 kf[4];
-  bf16x8 vf[2][2];
+  svec<S, 8> kf[4];
+  svec<S, 8> vf[2][2];
 };
 
 // Where thread (wave w, lane l) stages its two 16-byte chunks q = (2 w + e) 64
@@ -1344,14 +1372,14 @@ __device__ __forceinline__ void stage_chunk(int wave, int lane, int e, int& srow
 // With extra_half, after the last step the wave takes one more 32-key half
 // whose K and V sit at smem + B_GH_OFF (K half, then V half) under the lane
 // mask extra_mask() -- the few global columns of band rows.
-template <class Idle, class Issue, class IssueBand, class Active, class Masked, class MaskOf,
+template <typename S, class Idle, class Issue, class IssueBand, class Active, class Masked, class MaskOf,
           class Pre, class ExtraMask>
 __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_hi, const Idle& idle,
                                           const Issue& issue, const IssueBand& issue_band,
                                           const Active& active, const Masked& masked,
                                           const MaskOf& mask_of, const Pre& pre,
                                           const bool& extra_half, const ExtraMask& extra_mask,
-                                          const QOp<true>& qo, const FLane& fl, BandRow& st,
+                                          const QOp<S>& qo, const FLane& fl, BandRow& st,
                                           int h32, uint8_t* smem) {
   // the batch of step t: K of step t+3 and V of step t+2 (those that exist);
   // two loads per thread for each
@@ -1373,23 +1401,23 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     f32x16 a = mvec;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
-      a = mfma_bf16(*reinterpret_cast<const bf16x8*>(ks + fl.k[cc]), qo.q[cc], a);
+      a = mfma16(*reinterpret_cast<const svec<S, 8>*>(ks + fl.k[cc]), qo.q[cc], a);
     sx = a;
   };
-  auto pv_half = [&](const bf16x8 (&pb)[2], const uint8_t* vs) {
+  auto pv_half = [&](const svec<S, 8> (&pb)[2], const uint8_t* vs) {
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int db = 0; db < 2; ++db)
-        st.o[db] = mfma_bf16(vfrag(vs, fl.v[db] + c2 * 2048), pb[c2], st.o[db]);
+        st.o[db] = mfma16(vfrag<S>(vs, fl.v[db] + c2 * 2048), pb[c2], st.o[db]);
   };
-  auto load_ops = [&](PhaseOps& ops, const uint8_t* ks, const uint8_t* vs) {
+  auto load_ops = [&](PhaseOps<S>& ops, const uint8_t* ks, const uint8_t* vs) {
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) ops.kf[cc] = *reinterpret_cast<const bf16x8*>(ks + fl.k[cc]);
+    for (int cc = 0; cc < 4; ++cc) ops.kf[cc] = *reinterpret_cast<const svec<S, 8>*>(ks + fl.k[cc]);
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int db = 0; db < 2; ++db) ops.vf[c2][db] = vfrag(vs, fl.v[db] + c2 * 2048);
+      for (int db = 0; db < 2; ++db) ops.vf[c2][db] = vfrag<S>(vs, fl.v[db] + c2 * 2048);
   };
   // the MFMAs of a phase: QK^T of one half into sq and PV of one half, the
   // two chains alternating so that no MFMA waits on the one just before it,
@@ -1397,30 +1425,30 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
   // next phase (K rows at ks, V^T at vs): the reads
   // leave in a stream across the phase instead of in one burst, and the
   // registers of an operand are reused as soon as its MFMA has taken it
-  auto phase_mfma_next = [&](f32x16& sq, PhaseOps& ops, const bf16x8 (&pp)[2], const uint8_t* ks,
+  auto phase_mfma_next = [&](f32x16& sq, PhaseOps<S>& ops, const svec<S, 8> (&pp)[2], const uint8_t* ks,
                              const uint8_t* vs) {
     f32x16 a = mvec;
-    st.o[0] = mfma_bf16(ops.vf[0][0], pp[0], st.o[0]);
-    ops.vf[0][0] = vfrag(vs, fl.v[0]);
-    a = mfma_bf16(ops.kf[0], qo.q[0], a);
-    ops.kf[0] = *reinterpret_cast<const bf16x8*>(ks + fl.k[0]);
-    st.o[1] = mfma_bf16(ops.vf[0][1], pp[0], st.o[1]);
-    ops.vf[0][1] = vfrag(vs, fl.v[1]);
-    a = mfma_bf16(ops.kf[1], qo.q[1], a);
-    ops.kf[1] = *reinterpret_cast<const bf16x8*>(ks + fl.k[1]);
-    st.o[0] = mfma_bf16(ops.vf[1][0], pp[1], st.o[0]);
-    ops.vf[1][0] = vfrag(vs, fl.v[0] + 2048);
-    a = mfma_bf16(ops.kf[2], qo.q[2], a);
-    ops.kf[2] = *reinterpret_cast<const bf16x8*>(ks + fl.k[2]);
-    st.o[1] = mfma_bf16(ops.vf[1][1], pp[1], st.o[1]);
-    ops.vf[1][1] = vfrag(vs, fl.v[1] + 2048);
-    a = mfma_bf16(ops.kf[3], qo.q[3], a);
-    ops.kf[3] = *reinterpret_cast<const bf16x8*>(ks + fl.k[3]);
+    st.o[0] = mfma16(ops.vf[0][0], pp[0], st.o[0]);
+    ops.vf[0][0] = vfrag<S>(vs, fl.v[0]);
+    a = mfma16(ops.kf[0], qo.q[0], a);
+    ops.kf[0] = *reinterpret_cast<const svec<S, 8>*>(ks + fl.k[0]);
+    st.o[1] = mfma16(ops.vf[0][1], pp[0], st.o[1]);
+    ops.vf[0][1] = vfrag<S>(vs, fl.v[1]);
+    a = mfma16(ops.kf[1], qo.q[1], a);
+    ops.kf[1] = *reinterpret_cast<const svec<S, 8>*>(ks + fl.k[1]);
+    st.o[0] = mfma16(ops.vf[1][0], pp[1], st.o[0]);
+    ops.vf[1][0] = vfrag<S>(vs, fl.v[0] + 2048);
+    a = mfma16(ops.kf[2], qo.q[2], a);
+    ops.kf[2] = *reinterpret_cast<const svec<S, 8>*>(ks + fl.k[2]);
+    st.o[1] = mfma16(ops.vf[1][1], pp[1], st.o[1]);
+    ops.vf[1][1] = vfrag<S>(vs, fl.v[1] + 2048);
+    a = mfma16(ops.kf[3], qo.q[3], a);
+    ops.kf[3] = *reinterpret_cast<const svec<S, 8>*>(ks + fl.k[3]);
     sq = a;
   };
-  auto soft_half = [&](f32x16& sx, bf16x8 (&pb)[2]) {
-    float ts = band_exp_half<true>(sx, st.m - m0, pb);
-    if (__builtin_expect(__any(ts > SUM_HI || st.first), 0)) band_rebase(st, sx, m0, pb, ts);
+  auto soft_half = [&](f32x16& sx, svec<S, 8> (&pb)[2]) {
+    float ts = band_exp_half<true, S>(sx, st.m - m0, pb);
+    if (__builtin_expect(__any(ts > SUM_HI || st.first), 0)) band_rebase<S>(st, sx, m0, pb, ts);
     st.l += ts;
   };
 
@@ -1448,11 +1476,11 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
   __syncthreads();
 
   f32x16 sx, sy;           // the two halves of the step being softmaxed
-  bf16x8 pa[2], pb[2];     // probabilities of half 0 / half 1
+  svec<S, 8> pa[2], pb[2];     // probabilities of half 0 / half 1
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { pa[c2][e] = (__bf16)0.0f; pb[c2][e] = (__bf16)0.0f; }
+    for (int e = 0; e < 8; ++e) { pa[c2][e] = (S)0.0f; pb[c2][e] = (S)0.0f; }
   }
   if (U > 0) qk_half(sx, kslot(0));
   if (st.first && U > 0) {
@@ -1523,7 +1551,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     for (int u = 0; u < U; ++u) head_of_step(u);
     return;
   }
-  PhaseOps ops;
+  PhaseOps<S> ops;
   if (U > 0) load_ops(ops, kslot(0) + 4096, vslot(B_NSLOT - 1) + 4096);
   int rare_at = 0;
   float ts_rare = 0.f;
@@ -1543,7 +1571,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     if (msk) mask_half(sx, mask_of(u, 0), h32);
     // phase A
     phase_mfma_next(sy, ops, pb, kslot(u + 1), vslot(u));
-    float ts = band_exp_half<false>(sx, 0.f, pa);   // st.m == m0 in this loop
+    float ts = band_exp_half<false, S>(sx, 0.f, pa);   // st.m == m0 in this loop
     interleave_hint();
     if (__builtin_expect(__any(ts > SUM_HI), 0)) {
       rare_at = 1;
@@ -1555,7 +1583,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     // phase B (the operands read for step u+1 = U are never used; the reads
     // stay inside the ring)
     phase_mfma_next(sx, ops, pa, kslot(u + 1) + 4096, vslot(u) + 4096);
-    ts = band_exp_half<false>(sy, 0.f, pb);
+    ts = band_exp_half<false, S>(sy, 0.f, pb);
     interleave_hint();
     if (__builtin_expect(__any(ts > SUM_HI), 0)) {
       rare_at = 2;
@@ -1566,7 +1594,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
   }
   if (rare_at == 1) {
     // half 0 of step u overflowed: rescale, then phase B of step u
-    band_rebase(st, sx, m0, pa, ts_rare);
+    band_rebase<S>(st, sx, m0, pa, ts_rare);
     st.l += ts_rare;
     if (masked(u)) mask_half(sy, mask_of(u, 1), h32);
     if (u + 1 < U) qk_half(sx, kslot(u + 1));
@@ -1575,7 +1603,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     ++u;
   } else if (rare_at == 2) {
     // half 1 of step u overflowed
-    band_rebase(st, sy, m0, pb, ts_rare);
+    band_rebase<S>(st, sy, m0, pb, ts_rare);
     st.l += ts_rare;
     ++u;
   }
@@ -1588,7 +1616,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     f32x16 sg;
     qk_half(sg, gk);
     mask_half(sg, extra_mask(), h32);
-    bf16x8 pg[2];
+    svec<S, 8> pg[2];
     soft_half(sg, pg);
     pv_half(pg, gk + B_STEP / 2);
   }
@@ -1646,6 +1674,7 @@ __device__ __forceinline__ void pad_scan(const float* lmb, int rho, int s, int l
 // issued.  Returns false, having written nothing, when the real tokens among
 // those keys are not a prefix of them; the general path then takes the
 // workgroup.
+template <typename S>
 __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, uint8_t* smem) {
   constexpr int RB = 128;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
@@ -1681,7 +1710,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   const float g_row = row_in ? gmb[my_pos] : 0.0f;
   // this lane's query row and its own key row (the initial offset), in the
   // same round trip as the masks
-  QOp<true> qo;
+  QOp<S> qo;
   qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
   uint4 kdiag[4];
   {
@@ -1735,16 +1764,16 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   {
     // the row's own score sets the initial offset (this lane's 32 channels,
     // then both half-lanes)
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
     float sd = 0.f;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      const bf16x8 k8 = __builtin_bit_cast(bf16x8, kdiag[cc]);
+      const svec<S, 8> k8 = __builtin_bit_cast(svec<S, 8>, kdiag[cc]);
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const bf16x2 a = {qo.q[cc][e], qo.q[cc][e + 1]};
-        const bf16x2 bb = {k8[e], k8[e + 1]};
-        sd = __builtin_amdgcn_fdot2_f32_bf16(a, bb, sd, false);
+        const svec<S, 2> a = {qo.q[cc][e], qo.q[cc][e + 1]};
+        const svec<S, 2> bb = {k8[e], k8[e + 1]};
+        sd = dot2(a, bb, sd);
       }
     }
     st.m = half_sum(sd);   // Q carries the factor c
@@ -1943,9 +1972,9 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
         ti.j0 = 0;
         f32x16 sc = fqk(qo, smem, fl);   // Q carries the factor c
         apply_mask(sc, lane_mask(ti, my_i, r, jr, lane), lane);
-        bf16x8 pq[2];
-        softmax_bf16(sm, sc, 1.0f, pq);
-        fpv(sm.o, pq, smem + B_V_OFF, fl);
+        svec<S, 8> pq[2];
+        softmax16<S>(sm, sc, 1.0f, pq);
+        fpv<S>(sm.o, pq, smem + B_V_OFF, fl);
       }
     }
     st.m = sm.m;
@@ -1970,11 +1999,11 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   for (int db = 0; db < 2; ++db) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      bf16x4 t;
+      svec<S, 4> t;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = (__bf16)(valid ? st.o[db][4 * a + e] * inv : 0.0f);
+      for (int e = 0; e < 4; ++e) t[e] = (S)(valid ? st.o[db][4 * a + e] * inv : 0.0f);
       const int chunk = (4 * db + a) ^ (qi & 7);
-      *reinterpret_cast<bf16x4*>(stg + qi * 128 + chunk * 16 + h32 * 8) = t;
+      *reinterpret_cast<svec<S, 4>*>(stg + qi * 128 + chunk * 16 + h32 * 8) = t;
     }
   }
   const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.O + head * RB, n * RB);
@@ -1997,6 +2026,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
 // of its slice from the mask and issues its first key batches before it waits
 // for the row's compaction (which names its query rows).  Returns false,
 // having written nothing, when the slice's real tokens are not a prefix of it.
+template <typename S>
 __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, uint8_t* smem) {
   constexpr int RB = 128;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
@@ -2016,7 +2046,7 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
   // the query tiles, known once the row's compaction is visible
   int g = 0, qt = 0, qpos_row = 0;
   bool wave_work = false, qok = false;
-  QOp<true> qo;
+  QOp<S> qo;
   auto load_rows = [&]() {   // while the first keys are in flight
     if (wait_ready(p, b, false)) {
       g = coherent_load(p.gcnt + b);
@@ -2092,13 +2122,13 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
       p.part_ml[pidx * 2 + 1] = lt;
     }
   }
-  if (wave_work) finish_global_tile<true>(p, b, h, qt, g, lane, qpos_row);
+  if (wave_work) finish_global_tile<S>(p, b, h, qt, g, lane, qpos_row);
   return true;
 }
 
-template <bool BF>
+template <typename S>
 constexpr int smem_bytes() {
-  return (BF && B_SMEM > smem_bytes_general<BF>()) ? B_SMEM : smem_bytes_general<BF>();
+  return (is16<S>() && B_SMEM > smem_bytes_general<S>()) ? B_SMEM : smem_bytes_general<S>();
 }
 
 // The logical workgroup order keeps neighbouring query blocks of one head on
@@ -2121,7 +2151,7 @@ __device__ __forceinline__ int xcd_remap(int pid, int count) {
 // run on as a tail (each takes several band workgroups' time).  band_pre and
 // the global-row count are multiples of 8, so every band workgroup keeps the
 // XCD its band index names.
-template <bool BF>
+template <typename S>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int bid = blockIdx.x;
@@ -2139,11 +2169,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     t /= p.nqg;
     const int h = t % p.H;
     const int b = t / p.H;
-    if constexpr (BF) {
-      if (global_wg_fast(p, b, h, qg, sp, smem)) return;
+    if constexpr (is16<S>()) {
+      if (global_wg_fast<S>(p, b, h, qg, sp, smem)) return;
     }
     if (!wait_ready(p, b, true)) return;
-    global_wg<BF>(p, b, h, qg, sp, smem);
+    global_wg<S>(p, b, h, qg, sp, smem);
   } else {
     if (bid >= p.band_pre) bid -= p.n_glob_wg;
     const int lb = xcd_remap(bid, p.n_band_wg);
@@ -2165,11 +2195,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
       local = rem - p.head_blk[h];
       s = p.head_stride[h];
     }
-    if constexpr (BF) {
-      if (p.band_fast && band_wg_fast(p, b, h, local, s, smem)) return;
+    if constexpr (is16<S>()) {
+      if (p.band_fast && band_wg_fast<S>(p, b, h, local, s, smem)) return;
     }
     if (!wait_ready(p, b, true)) return;
-    band_wg<BF>(p, b, h, local, s, smem);
+    band_wg<S>(p, b, h, local, s, smem);
   }
 }
 

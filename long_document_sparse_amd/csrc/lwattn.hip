@@ -350,7 +350,7 @@ static bool forward_geometry(const lwattn_config& c, const int32_t* gap, int ncu
   // they stage has a byte offset that fits in 32 bits
   int smax = 1;
   for (int h = 0; h < H; ++h) smax = std::max(smax, stride[h]);
-  g.band_fast = (c.dtype == LWATTN_BF16 && (int64_t)n + 128 * (int64_t)smax < ((int64_t)1 << 24)) ? 1 : 0;
+  g.band_fast = (c.dtype != LWATTN_F32 && (int64_t)n + 128 * (int64_t)smax < ((int64_t)1 << 24)) ? 1 : 0;
   // compaction workgroups lead the grid, padded to a multiple of 8 so that the
   // band workgroups behind them keep their XCD placement
   const int64_t ncomp = ((int64_t)B + 7) / 8 * 8;
@@ -395,7 +395,7 @@ static bool forward_geometry(const lwattn_config& c, const int32_t* gap, int ncu
   g.band_pre = (int)(ncomp + nband <= slots
                          ? nband
                          : std::min<int64_t>(nband, std::max<int64_t>(0, (slots - ncomp) / 8 * 8)));
-  g.smem = c.dtype == LWATTN_BF16 ? lwk::smem_bytes<true>() : lwk::smem_bytes<false>();
+  g.smem = c.dtype == LWATTN_F32 ? lwk::smem_bytes<float>() : lwk::smem_bytes<__bf16>();   // fp16 as bf16
   return true;
 }
 
@@ -467,10 +467,13 @@ static bool launch_forward(const lwattn_config& c, const FwdGeom& g, const lwk::
                            hipEvent_t ev0, hipEvent_t ev1) {
   const int grid = g.n_comp_wg + g.n_band_wg + g.n_glob_wg;
   if (c.dtype == LWATTN_BF16)
-    hipExtLaunchKernelGGL(lwk::attn_kernel<true>, dim3(grid), dim3(lwk::NT), (uint32_t)g.smem, stream, ev0, ev1, 0u,
-                          prm);
+    hipExtLaunchKernelGGL(lwk::attn_kernel<__bf16>, dim3(grid), dim3(lwk::NT), (uint32_t)g.smem, stream, ev0, ev1,
+                          0u, prm);
+  else if (c.dtype == LWATTN_F16)
+    hipExtLaunchKernelGGL(lwk::attn_kernel<_Float16>, dim3(grid), dim3(lwk::NT), (uint32_t)g.smem, stream, ev0,
+                          ev1, 0u, prm);
   else
-    hipExtLaunchKernelGGL(lwk::attn_kernel<false>, dim3(grid), dim3(lwk::NT), (uint32_t)g.smem, stream, ev0, ev1,
+    hipExtLaunchKernelGGL(lwk::attn_kernel<float>, dim3(grid), dim3(lwk::NT), (uint32_t)g.smem, stream, ev0, ev1,
                           0u, prm);
   return hip_ok(hipGetLastError(), "hipGetLastError");
 }
@@ -552,7 +555,7 @@ lwattn_status lwattn_check_config(const lwattn_config* c) {
   if (c->window < 0 || (c->window & 1)) return LWATTN_E_INVALID;
   if (c->max_global < 0) return LWATTN_E_INVALID;
   if (!(c->scale > 0.0f) || !std::isfinite(c->scale)) return LWATTN_E_INVALID;
-  if (c->dtype != LWATTN_F32 && c->dtype != LWATTN_BF16) return LWATTN_E_INVALID;
+  if (c->dtype != LWATTN_F32 && c->dtype != LWATTN_BF16 && c->dtype != LWATTN_F16) return LWATTN_E_INVALID;
   if (c->dilation) {
     for (int h = 0; h < c->H; ++h) {
       if (c->dilation[h] < 0) return LWATTN_E_INVALID;
@@ -875,6 +878,7 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
+  if (c.dtype == LWATTN_F16) return LWATTN_E_UNSUPPORTED;
   const void* ptrs[] = {Q, K, V, Qg, Kg, Vg, O, dO, dQ, dK, dV, dQg, dKg, dVg};
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return LWATTN_E_INVALID;
@@ -1107,7 +1111,7 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
   if (!p || inter <= 0 || (inter % 8) != 0 || !(eps > 0.0f)) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   const int H = c.H;
-  if (c.dtype != LWATTN_BF16 || !layer_heads_ok(H)) return LWATTN_E_UNSUPPORTED;
+  if (c.dtype == LWATTN_F32 || !layer_heads_ok(H)) return LWATTN_E_UNSUPPORTED;
   const int64_t M = (int64_t)c.B * c.n, hid = (int64_t)H * 64;
   const int mg = std::min(c.max_global, c.n);
   if (M * std::max<int64_t>(3 * hid, inter) >= ((int64_t)1 << 31) || (int64_t)c.B * mg * hid >= ((int64_t)1 << 31))
@@ -1139,7 +1143,7 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
   // each shape's algorithm timed here on scratch operands
   if (ok && hipblasLtCreate(&L->lt) != HIPBLAS_STATUS_SUCCESS) L->lt = nullptr;
   if (ok && L->lt) {
-    const hipDataType dt = HIP_R_16BF;
+    const hipDataType dt = c.dtype == LWATTN_F16 ? HIP_R_16F : HIP_R_16BF;
     const int64_t Mg = (int64_t)c.B * mg, big = std::max<int64_t>(3 * hid, inter);
     LtTune tu;
     tu.ws_cap = (size_t)32 << 20;
@@ -1245,6 +1249,7 @@ lwattn_status lwattn_layer_forward(lwattn_layer_t L, const void* X, const lwattn
   if (!lmask || !gmask || ((uintptr_t)lmask & 3u) || ((uintptr_t)gmask & 3u)) return LWATTN_E_INVALID;
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
   if (rocblas_set_stream(L->blas, stream) != rocblas_status_success) return LWATTN_E_DEVICE;
+  if (c.dtype == LWATTN_F16) return layer_forward<_Float16>(L, rocblas_datatype_f16_r, X, w, lmask, gmask, Y, stream);
   return layer_forward<__bf16>(L, rocblas_datatype_bf16_r, X, w, lmask, gmask, Y, stream);
 }
 

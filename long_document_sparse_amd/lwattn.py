@@ -14,7 +14,14 @@ from typing import Optional, Sequence
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblwattn.so")
 
-LWATTN_F32, LWATTN_BF16 = 0, 1
+LWATTN_F32, LWATTN_BF16, LWATTN_F16 = 0, 1, 2
+DTYPE_CODES = {"f32": LWATTN_F32, "bf16": LWATTN_BF16, "f16": LWATTN_F16}
+
+
+def torch_dtype(dtype: str):
+    """The torch dtype of a storage type name ("f32", "bf16", "f16")."""
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
 OK, E_INVALID, E_UNSUPPORTED, E_NOMEM, E_DEVICE, E_TOO_MANY_GLOBALS, E_SCRATCH = range(7)
 KERNELS = ("attention",)
 # kernel slots of lwattn_timing_read_backward
@@ -108,7 +115,7 @@ def make_config(B: int, H: int, n: int, d: int = 64, window: int = 512,
         ptr = ctypes.cast(dil, ctypes.POINTER(_i32))
     if scale is None:
         scale = 1.0 / math.sqrt(d) if d > 0 else 1.0
-    code = {"bf16": LWATTN_BF16, "f32": LWATTN_F32}.get(dtype, 99) if isinstance(dtype, str) else int(dtype)
+    code = DTYPE_CODES.get(dtype, 99) if isinstance(dtype, str) else int(dtype)
     return Config(B, H, n, d, window, ptr, max_global, scale, code), dil
 
 
@@ -164,7 +171,7 @@ class Plan:
 
     def _validate(self, q, k, v, qg, kg, vg, lmask, gmask, out):
         import torch
-        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        tdt = torch_dtype(self.dtype)
         for t, name in ((q, "q"), (k, "k"), (v, "v"), (qg, "qg"), (kg, "kg"), (vg, "vg")):
             self._check(t, name, tdt)
             if tuple(t.shape) != self.shape:
@@ -197,7 +204,7 @@ class Plan:
         """Enqueue the causal variant (window taps at or before each row, no
         global attention; bf16 plans); returns O (allocated if `out` is None)."""
         import torch
-        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        tdt = torch_dtype(self.dtype)
         for t, name in ((q, "q"), (k, "k"), (v, "v")):
             self._check(t, name, tdt)
             if tuple(t.shape) != self.shape:
@@ -222,7 +229,7 @@ class Plan:
         """Enqueue the backward of the causal variant (bf16 plans); `o` is
         forward_causal's output on the same inputs.  Returns (dQ, dK, dV)."""
         import torch
-        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        tdt = torch_dtype(self.dtype)
         for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
             self._check(t, name, tdt)
             if tuple(t.shape) != self.shape:
@@ -245,7 +252,7 @@ class Plan:
         layout as CSR over (head, query block), int32 device tensors rowptr
         [H*nb + 1] and cols [nnz]; returns O (allocated if `out` is None)."""
         import torch
-        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        tdt = torch_dtype(self.dtype)
         for t, name in ((q, "q"), (k, "k"), (v, "v")):
             self._check(t, name, tdt)
             if tuple(t.shape) != self.shape:
@@ -279,7 +286,7 @@ class Plan:
         (dQ, dK, dV, dQg, dKg, dVg), allocated if `grads` is None."""
         import torch
         self._validate(q, k, v, qg, kg, vg, lmask, gmask, o)
-        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        tdt = torch_dtype(self.dtype)
         self._check(do, "do", tdt)
         if tuple(do.shape) != self.shape:
             raise ValueError("do has the wrong shape")
@@ -395,7 +402,7 @@ def forward_noalloc(q, k, v, qg, kg, vg, lmask, gmask, out, window: int,
     import torch
     B, H, n, d = tuple(q.shape)
     tdt = q.dtype
-    dtype = {torch.bfloat16: "bf16", torch.float32: "f32"}.get(tdt)
+    dtype = {torch.bfloat16: "bf16", torch.float32: "f32", torch.float16: "f16"}.get(tdt)
     if dtype is None:
         raise TypeError(f"unsupported dtype {tdt}")
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (qg, "qg"), (kg, "kg"), (vg, "vg"), (out, "out")):
@@ -453,12 +460,13 @@ class Layer:
         import torch
         B, H, n, d = self.plan.shape
         hid = H * d
-        self.plan._check(x, "x", torch.bfloat16)
+        tdt = torch_dtype(self.plan.dtype)
+        self.plan._check(x, "x", tdt)
         if tuple(x.shape) != (B * n, hid):
             raise ValueError(f"x must be [{B * n}, {hid}]")
         for name, shape in self.shapes().items():
             t = weights[name]
-            self.plan._check(t, name, torch.bfloat16)
+            self.plan._check(t, name, tdt)
             if tuple(t.shape) != shape:
                 raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
         for t, name in ((lmask, "local_attn_mask"), (gmask, "global_attn_mask")):
@@ -468,7 +476,7 @@ class Layer:
         if out is None:
             out = torch.empty_like(x)
         else:
-            self.plan._check(out, "out", torch.bfloat16)
+            self.plan._check(out, "out", tdt)
             if tuple(out.shape) != tuple(x.shape):
                 raise ValueError("out has the wrong shape")
         self._w = _LayerWeights(*[weights[name].data_ptr() for name in LAYER_WEIGHTS])

@@ -26,6 +26,11 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 
+def round_to_f16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest IEEE half (ties to even), kept as float32."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even), kept as float32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
@@ -42,7 +47,7 @@ class Spec:
     n: int
     d: int
     window: int
-    dtype: str                      # "f32" or "bf16"
+    dtype: str                      # "f32", "bf16" or "f16"
     dilation: List[int]             # gap per head
     seed: int
     max_global: int
@@ -195,6 +200,8 @@ def generate(spec: Spec, strong: bool = False, seed: Optional[int] = None) -> In
     # 6. storage rounding
     if spec.dtype == "bf16":
         Q, K, V, Qg, Kg, Vg = (round_to_bf16(a) for a in (Q, K, V, Qg, Kg, Vg))
+    elif spec.dtype == "f16":
+        Q, K, V, Qg, Kg, Vg = (round_to_f16(a) for a in (Q, K, V, Qg, Kg, Vg))
     return Inputs(spec, Q, K, V, Qg, Kg, Vg, lmask, gmask, pad_len, global_pos)
 
 

@@ -1251,7 +1251,8 @@ struct BandRow {
 
 // Probabilities of one 32-key half (16-bit, as PV multiplies them) and this
 // lane's share of their sum.  The scores arrive already scaled and offset
-// (c s - m0: Q is pre-scaled by c and the QK^T accumulator starts at -m0), so
+// (c s - m0: the QK^T accumulator starts at -m0 / c and is multiplied by c in
+// fp32, so Q enters the matrix cores exactly as stored), so
 // p = 2^(s - x) with x the part of the row's offset beyond m0 -- zero until a
 // rebase, and then the subtraction is only paid off the fast loop.
 template <bool OFF, typename S>
@@ -1296,17 +1297,6 @@ __device__ __forceinline__ void band_rebase(BandRow& st, const f32x16& s, float 
   for (int r = 0; r < 16; ++r) { st.o[0][r] *= alpha; st.o[1][r] *= alpha; }
   st.m += delta;
   ts = band_exp_half<true, S>(s, st.m - m0, pb);
-}
-
-// Q scaled by c = scale log2(e) once, so that QK^T yields the exponent's
-// argument directly (the scaled value is rounded to the storage format: a
-// relative change of at most 2^-9 per element in bf16, 2^-12 in fp16).
-template <typename S>
-__device__ __forceinline__ void scale_q(QOp<S>& qo, float c) {
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qo.q[cc][e] = (S)((float)qo.q[cc][e] * c);
 }
 
 template <typename S>
@@ -1379,7 +1369,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
                                           const Active& active, const Masked& masked,
                                           const MaskOf& mask_of, const Pre& pre,
                                           const bool& extra_half, const ExtraMask& extra_mask,
-                                          const QOp<S>& qo, const FLane& fl, BandRow& st,
+                                          const QOp<S>& qo, float c, const FLane& fl, BandRow& st,
                                           int h32, uint8_t* smem) {
   // the batch of step t: K of step t+3 and V of step t+2 (those that exist);
   // two loads per thread for each
@@ -1390,19 +1380,21 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
   auto kslot = [&](int t) { return smem + (t % B_NSLOT) * B_STEP; };
   auto vslot = [&](int t) { return smem + B_V_OFF + (t % B_NSLOT) * B_STEP; };
   // QK^T of one half of a step; PV of one half of a step
-  // the row's fixed exponent offset, folded into every QK^T accumulator (so
-  // that the scores come out as c s - m0); set again after the first-half
-  // maximum of rows without an anchor
+  // the row's fixed exponent offset, folded into every QK^T accumulator as
+  // -m0 / c, the accumulator then multiplied by c = scale log2(e) in fp32: the
+  // scores come out as c s - m0 (and Q is never rounded again after scaling);
+  // set again after the first-half maximum of rows without an anchor
+  const float inv_c = 1.0f / c;
   float m0 = st.m;
   f32x16 mvec;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) mvec[i] = -m0;
+  for (int i = 0; i < 16; ++i) mvec[i] = -m0 * inv_c;
   auto qk_half = [&](f32x16& sx, const uint8_t* ks) {
     f32x16 a = mvec;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
       a = mfma16(*reinterpret_cast<const svec<S, 8>*>(ks + fl.k[cc]), qo.q[cc], a);
-    sx = a;
+    sx = a * c;
   };
   auto pv_half = [&](const svec<S, 8> (&pb)[2], const uint8_t* vs) {
 #pragma unroll
@@ -1444,7 +1436,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     ops.vf[1][1] = vfrag<S>(vs, fl.v[1] + 2048);
     a = mfma16(ops.kf[3], qo.q[3], a);
     ops.kf[3] = *reinterpret_cast<const svec<S, 8>*>(ks + fl.k[3]);
-    sq = a;
+    sq = a * c;
   };
   auto soft_half = [&](f32x16& sx, svec<S, 8> (&pb)[2]) {
     float ts = band_exp_half<true, S>(sx, st.m - m0, pb);
@@ -1500,7 +1492,7 @@ __device__ __forceinline__ void half_pipe(const int& U, int plain_lo, int plain_
     for (int r = 0; r < 16; ++r) sx[r] -= st.m - m0;
     m0 = st.m;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mvec[i] = -m0;
+    for (int i = 0; i < 16; ++i) mvec[i] = -m0 * inv_c;
   }
 
   auto head_of_step = [&](int u) {
@@ -1757,7 +1749,6 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   // compiler's view of outstanding loads, since the loop below issues
   // buffer-to-LDS loads the compiler does not count, and a wait it placed for
   // Q inside the loop would also wait for those.
-  scale_q(qo, p.c);
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
   BandRow st;
@@ -1776,7 +1767,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
         sd = dot2(a, bb, sd);
       }
     }
-    st.m = half_sum(sd);   // Q carries the factor c
+    st.m = p.c * half_sum(sd);   // c s_ii, the offset in the exponent's units
     asm volatile("" : "+v"(st.m));
   }
   st.l = 0.f;
@@ -1931,7 +1922,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   const int plain_lo = fa > 0 ? fa : 0;
   const int plain_hi = fb < nband - 4 ? fb : nband - 4;
   half_pipe(U, plain_lo, plain_hi, idle, issue, issue_band, active, masked, mask_of, pre, gh, gh_mask,
-            qo, fl, st, h32, smem);
+            qo, p.c, fl, st, h32, smem);
 
   if (g > GL_MAX && R0 < nrv) {
     // global columns past the LDS copy, 32 at a time through the first K and
@@ -1970,10 +1961,10 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
         ti.kind = 2;
         ti.okb = bit_range(0, g - jb);
         ti.j0 = 0;
-        f32x16 sc = fqk(qo, smem, fl);   // Q carries the factor c
+        f32x16 sc = fqk(qo, smem, fl);
         apply_mask(sc, lane_mask(ti, my_i, r, jr, lane), lane);
         svec<S, 8> pq[2];
-        softmax16<S>(sm, sc, 1.0f, pq);
+        softmax16<S>(sm, sc, p.c, pq);
         fpv<S>(sm.o, pq, smem + B_V_OFF, fl);
       }
     }
@@ -2066,7 +2057,6 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
     qo.load(p.Qg + (head + qpos) * RB, qok, h32);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
-    scale_q(qo, p.c);
   };
   BandRow st;
   st.m = 0.f;
@@ -2104,7 +2094,7 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
   auto idle = [&]() { return !wave_work; };
   const bool no_extra = false;
   half_pipe(U, 1, 0, idle, issue, issue, active, masked, mask_of, load_rows, no_extra,
-            [] { return 0u; }, qo, fl, st, h32, smem);
+            [] { return 0u; }, qo, p.c, fl, st, h32, smem);
 
   const float lt = half_sum(st.l);
   if (qok) {

@@ -9,10 +9,25 @@ import oracle
 from long_document_sparse_amd import lwattn as lw
 from long_document_sparse_amd import workloads
 
-# Tolerances: max |O_gpu - O_oracle| over every compared element.
-TOL_ABS = {"f32": 1e-4, "bf16": 2e-2, "f16": 3e-3}
-# Strong variant (unscaled N(0,1) inputs, O(1) outputs): error relative to max |O|.
-TOL_REL = {"f32": 1e-5, "bf16": 2e-2, "f16": 3e-3}
+# Tolerance of the forward: max |O_gpu - O_oracle| over every compared element,
+# relative to max |O_oracle| over them.  Both sides see the same stored
+# inputs; scores, exponentials and every sum are fp32 on the GPU (the factor
+# scale log2 e applied in fp32), so fp32 storage leaves fp32 rounding over
+# sums of up to a few thousand terms: 1e-5.  16-bit storage adds the rounding
+# of each probability for the matrix cores and of the output, one unit
+# roundoff u each (bf16 2^-9, fp16 2^-12 relative), and the drift of the row's
+# O and l sums over those rounded probabilities (terms of one sign, so at most
+# u of the sum): a few u in all -- 1e-2 for bf16 (5 u), 3e-3 for fp16 (12 u).
+# Measured maxima over the named workloads, plain and strong inputs: bf16
+# 3.5e-3, fp16 4.8e-4, fp32 7.6e-7.
+TOL_REL = {"f32": 1e-5, "bf16": 1e-2, "f16": 3e-3}
+
+
+def rel_err(got, want):
+    """max |got - want| / max |want| (0 when both are empty or zero)."""
+    if want.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - want))) / max(float(np.max(np.abs(want))), 1e-30)
 
 
 def say(msg):
@@ -73,10 +88,6 @@ def oracle_rows(x: workloads.Inputs, rows):
     return oracle.rows(*x.tensors(), x.lmask, x.gmask, s.window, rows, s.dilation, s.scale)
 
 
-def check_rows(x, got_np64_flat_rows, want, rel=False):
-    s = x.spec
-    err = np.max(np.abs(got_np64_flat_rows - want)) if want.size else 0.0
-    if rel:
-        ref = max(np.max(np.abs(want)), 1e-30)
-        return err / ref, TOL_REL[s.dtype]
-    return err, TOL_ABS[s.dtype]
+def check_rows(x, got_np64_flat_rows, want):
+    """(error relative to max |want|, the storage type's bound)."""
+    return rel_err(got_np64_flat_rows, want), TOL_REL[x.spec.dtype]

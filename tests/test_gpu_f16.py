@@ -4,12 +4,12 @@ the oracle's layer.
 
 Tolerance, from the arithmetic (as for bf16, with fp16's unit roundoff 2^-11
 in place of bf16's 2^-8): the oracle sees exactly the stored fp16 values; the
-HIP path rounds Q c once to fp16 (2^-11 relative per element, so a score s
-moves by about 2^-11 |s| in log2 units), rounds each probability to fp16 for
-the matrix cores (2^-11 relative, the row sum taken over the same rounded
-values) and the output once (2^-11).  Per compared tensor, relative to its
-largest entry: |err| <= 3e-3 * max |O| (about 6 units of 2^-11, for the few
-roundings that reach each output and the score shift of the strong inputs).
+HIP path takes Q and K as stored into the matrix cores (fp32 accumulation, the
+factor scale log2 e applied in fp32), rounds each probability to fp16 for the
+matrix cores (2^-11 relative, the row sum taken over the same rounded values)
+and the output once (2^-11).  Per compared tensor, relative to its largest
+entry: |err| <= 3e-3 * max |O| (about 6 units of 2^-11, for the few
+roundings that reach each output).
 The closed form (Q = 0, one-hot V) has exact fp32 quotients rounded once:
 |err| <= 2^-10 * expected there, and channels without keys exactly zero.
 """

@@ -83,6 +83,30 @@ __device__ __forceinline__ float dot2(svec<_Float16, 2> a, svec<_Float16, 2> b, 
   return __builtin_amdgcn_fdot2(a, b, acc, false);
 }
 
+// Raw buffer resources over device memory, and their 16-byte loads and stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+// A 16-byte store that writes through to the device-coherent level (cache
+// policy sc1), so that no dirty line is left in L2 for a later release or the
+// kernel's end to write back.  It goes through the compiler's buffer-store
+// builtin, never inline asm: a store of more than 8 bytes reads its data
+// registers after issue, and only a store the compiler can see gets the wait
+// states that keep the next instruction from overwriting them.
+constexpr int CPOL_SC1 = 16;
+typedef unsigned u32x4s __attribute__((__vector_size__(16)));
+typedef unsigned u32x2 __attribute__((__vector_size__(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <typename V16>
+__device__ __forceinline__ void store_wt(__amdgpu_buffer_rsrc_t r, int off, V16 v) {
+  static_assert(sizeof(V16) == 16, "16-byte store");
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, v), r, off, 0, CPOL_SC1);
+}
+
+
 struct Params {
   const uint8_t *Q, *K, *V, *Qg, *Kg, *Vg;
   uint8_t* O;
@@ -108,6 +132,13 @@ struct Params {
   int32_t n_glob_wg;       // padded to a multiple of 8
   int32_t n_band_wg;
   int32_t band_pre;        // band workgroups dispatched before the global-row ones (a multiple of 8)
+  // key parts per band block on the register-staged path (1: none).  With
+  // more, each wave leaves its rows' partial (offset, sum, O) in the block's
+  // slots and the last part to finish merges them.
+  int32_t bparts;
+  float* bpart_o;          // [blocks][NW][bparts][64 lanes][32]
+  float* bpart_ml;         // [blocks][NW][bparts][32 rows][2]: offset, row sum
+  int32_t* bcnt;           // [blocks][NW] parts finished (re-armed by the merge)
   int32_t blocks_per_b;    // head_blk[H]
   int32_t mask_vec;        // masks 16-byte aligned and n % 4 == 0
   int32_t uni_stride;      // > 0: every head has this stride
@@ -350,16 +381,20 @@ __device__ __forceinline__ f32x16 qk_tile(const QOp<S>& qo, const uint8_t* slot,
 }
 __device__ __forceinline__ f32x16 qk_tile(const QOp<float>& qo, const uint8_t* slot, int lane) {
   const int key = lane & 31, h = lane >> 5;
-  f32x16 s = {};
+  // two independent accumulation chains (even and odd channel groups), so
+  // each MFMA waits on the one two back instead of the one just before it
+  f32x16 s0 = {}, s1 = {};
 #pragma unroll
   for (int c4 = 0; c4 < 8; ++c4) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(slot + SlotLay<float>::K_OFF +
                                                     key * Lay<float>::KROW + (8 * h + c4) * 16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qo.q[4 * c4 + e], s, 0, 0, 0);
+    for (int e = 0; e < 4; e += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qo.q[4 * c4 + e], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e + 1], qo.q[4 * c4 + e + 1], s1, 0, 0, 0);
+    }
   }
-  return s;
+  return s0 + s1;
 }
 
 // O^T += V^T * P^T for one tile.
@@ -663,8 +698,81 @@ constexpr int GL_MAX = 512;
 template <typename S>
 constexpr int smem_bytes_general() { return 2 * SlotLay<S>::BYTES + GL_MAX * 4; }
 
+// Key parts of a band block (register-staged path): each wave leaves its 32
+// rows' partial result -- offset m, row sum l, unnormalised O^T accumulators
+// in register order -- in the block's slot of this part and counts itself
+// on the (block, wave) counter; the wave that counts the last part merges the
+// parts by log-sum-exp into sm and lt (offsets are in the exponent's log2
+// units, so the weights are 2^(m_k - max m)) and returns true, the others
+// false.  The merging wave re-arms the counter for the next forward.  Parts
+// with no key of a row carry (M_INIT, 0, 0) and weigh nothing.
+__device__ bool merge_band_parts(const Params& p, int blk, int part, int wave, int lane, Softmax& sm, float& lt) {
+  const int P = p.bparts, qi = lane & 31;
+  const int64_t wslot = ((int64_t)blk * NW + wave) * P;
+  float* po = p.bpart_o + ((wslot + part) * 64 + lane) * 32;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<float4*>(po + 16 * db + 4 * k) =
+          make_float4(sm.o[db][4 * k], sm.o[db][4 * k + 1], sm.o[db][4 * k + 2], sm.o[db][4 * k + 3]);
+  if (lane < 32) *reinterpret_cast<float2*>(p.bpart_ml + ((wslot + part) * 32 + qi) * 2) = make_float2(sm.m, lt);
+  // this part is written back before it is counted; the wave that counts the
+  // last part reads all of them with agent-coherent loads
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  int32_t* cnt = p.bcnt + (int64_t)blk * NW + wave;
+  int old = 0;
+  if (lane == 0) old = atomicAdd(cnt, 1);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old != P - 1) return false;
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(p.bpart_o + wslot * 64 * 32, (short)0, P * 64 * 32 * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rml =
+      __builtin_amdgcn_make_buffer_rsrc(p.bpart_ml + wslot * 32 * 2, (short)0, P * 32 * 2 * 4, 0x00020000);
+  float mrun = M_INIT, L = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { sm.o[0][r] = 0.f; sm.o[1][r] = 0.f; }
+  // the parts' loads leave four at a time (coherent loads take a round trip
+  // to memory each: two round trips for up to eight parts, not eight); parts
+  // past P read as zeros through the ranges and weigh nothing
+  constexpr int G = 4;
+  for (int k0 = 0; k0 < P; k0 += G) {
+    float2 ml[G];
+    float4 o[G][8];
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const int k = k0 + e;
+      ml[e] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rml, (k * 32 + qi) * 8, 0, 16));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        o[e][j] = __builtin_bit_cast(float4,
+                                     __builtin_amdgcn_raw_buffer_load_b128(ro, ((k * 64 + lane) * 32 + 4 * j) * 4, 0, 16));
+    }
+#pragma unroll
+    for (int e = 0; e < G; ++e) {
+      const bool live = k0 + e < P;
+      const float mn = live ? fmaxf(mrun, ml[e].x) : mrun;
+      const float wa = __builtin_amdgcn_exp2f(mrun - mn), wb = live ? __builtin_amdgcn_exp2f(ml[e].x - mn) : 0.f;
+      L = wa * L + wb * ml[e].y;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int db = j >> 2, r = 4 * (j & 3);
+        sm.o[db][r] = wa * sm.o[db][r] + wb * o[e][j].x;
+        sm.o[db][r + 1] = wa * sm.o[db][r + 1] + wb * o[e][j].y;
+        sm.o[db][r + 2] = wa * sm.o[db][r + 2] + wb * o[e][j].z;
+        sm.o[db][r + 3] = wa * sm.o[db][r + 3] + wb * o[e][j].w;
+      }
+      mrun = mn;
+    }
+  }
+  sm.m = mrun;
+  lt = L;
+  if (lane == 0) *cnt = 0;
+  return true;
+}
+
 template <typename S>
-__device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t* smem) {
+__device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk, int part, uint8_t* smem) {
   using SL = SlotLay<S>;
   constexpr int RB = D * Lay<S>::ELT;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
@@ -748,14 +856,26 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
   auto nothing = []() {};
   const uint8_t* kbase = p.K + head * RB;
   const uint8_t* vbase = p.V + head * RB;
-  if (nband >= 2 || ngt == 0) {
-    tile_pipeline<S>(U, desc, comp, fill_gl, cx, kbase, vbase, smem);
-  } else {
-    fill_gl();
-    __syncthreads();
-    tile_pipeline<S>(U, desc, comp, nothing, cx, kbase, vbase, smem);
+  // this workgroup's tiles [u0, u1) of the U (all of them unless the block's
+  // keys are cut into parts; the last part also takes the columns past the
+  // LDS list)
+  const int P = p.bparts;
+  const int u0 = (int)((int64_t)U * part / P), u1 = (int)((int64_t)U * (part + 1) / P);
+  auto desc_p = [&](int u) { return desc(u0 + u); };
+  auto comp_p = [&](int u, const uint8_t* slot) { comp(u0 + u, slot); };
+  if (u1 > u0) {
+    if (u1 <= nband) {
+      tile_pipeline<S>(u1 - u0, desc_p, comp_p, nothing, cx, kbase, vbase, smem);
+    } else if (nband - u0 >= 2) {
+      // the list is filled while the first (band) tiles load
+      tile_pipeline<S>(u1 - u0, desc_p, comp_p, fill_gl, cx, kbase, vbase, smem);
+    } else {
+      fill_gl();
+      __syncthreads();
+      tile_pipeline<S>(u1 - u0, desc_p, comp_p, nothing, cx, kbase, vbase, smem);
+    }
   }
-  if (g > GL_MAX) {
+  if (g > GL_MAX && part == P - 1) {
     // global columns past the LDS copy: positions straight from the list
     Ctx cx2 = cx;
     cx2.gl = gidx_b + GL_MAX;
@@ -777,7 +897,8 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, uint8_t
 
   // normalise and store this lane's half of its query row (global rows are
   // written by the merge kernel, padded rows get exact zeros)
-  const float lt = sm.l + __shfl_xor(sm.l, 32);
+  float lt = sm.l + __shfl_xor(sm.l, 32);
+  if (P > 1 && !merge_band_parts(p, blk, part, wave, lane, sm, lt)) return;
   if (row_in && (my_fl & 2) == 0) {
     const bool valid = (my_fl & 1) != 0;
     const float inv = valid ? 1.0f / lt : 0.0f;
@@ -975,25 +1096,6 @@ constexpr int OOB_OFF = 0x7FFFFF00;             // a buffer offset past any rang
 __device__ __forceinline__ int swz_k(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int swz_v(int row) { return 2 * (row & 3); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-// A 16-byte store that writes through to the device-coherent level (cache
-// policy sc1), so that no dirty line is left in L2 for a later release or the
-// kernel's end to write back.  It goes through the compiler's buffer-store
-// builtin, never inline asm: a store of more than 8 bytes reads its data
-// registers after issue, and only a store the compiler can see gets the wait
-// states that keep the next instruction from overwriting them.
-constexpr int CPOL_SC1 = 16;
-typedef unsigned u32x4s __attribute__((__vector_size__(16)));
-template <typename V16>
-__device__ __forceinline__ void store_wt(__amdgpu_buffer_rsrc_t r, int off, V16 v) {
-  static_assert(sizeof(V16) == 16, "16-byte store");
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, v), r, off, 0, CPOL_SC1);
-}
 
 // Per-lane LDS byte offsets used by the compute of every tile.
 struct FLane {
@@ -2166,7 +2268,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     global_wg<S>(p, b, h, qg, sp, smem);
   } else {
     if (bid >= p.band_pre) bid -= p.n_glob_wg;
-    const int lb = xcd_remap(bid, p.n_band_wg);
+    int lb = xcd_remap(bid, p.n_band_wg), part = 0;
+    if (p.bparts > 1) {
+      part = lb % p.bparts;
+      lb /= p.bparts;
+    }
     const int b = lb / p.blocks_per_b;
     const int rem = lb - b * p.blocks_per_b;
     int h, local, s;
@@ -2189,7 +2295,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
       if (p.band_fast && band_wg_fast<S>(p, b, h, local, s, smem)) return;
     }
     if (!wait_ready(p, b, true)) return;
-    band_wg<S>(p, b, h, local, s, smem);
+    band_wg<S>(p, b, h, local, s, lb, part, smem);
   }
 }
 

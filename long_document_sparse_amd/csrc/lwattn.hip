@@ -54,6 +54,8 @@ struct FwdGeom {
   int n_comp_wg = 0, n_glob_wg = 0, n_band_wg = 0, blocks_per_b = 0;
   int band_pre = 0;   // band workgroups dispatched before the global-row ones
   int uni_stride = 0, blocks_per_head = 0, band_fast = 0;
+  int n_band_blk = 0;  // band blocks (B * blocks_per_b)
+  int bparts = 1;      // key parts per band block on the register-staged path
   size_t smem = 0;
 };
 
@@ -77,6 +79,9 @@ struct lwattn_plan_s {
   float* part_o = nullptr;
   float* part_ml = nullptr;
   int32_t* tile_cnt = nullptr;
+  float* bpart_o = nullptr;   // band blocks' key parts (bparts > 1)
+  float* bpart_ml = nullptr;
+  int32_t* bcnt = nullptr;
   int32_t* ready = nullptr;   // [B] epoch of the last compaction of each batch row
   int32_t* fault = nullptr;   // sticky: a workgroup gave up waiting for its row
   int32_t epoch = 0;          // forwards launched (kept in 1 .. INT32_MAX - 1)
@@ -112,6 +117,9 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->part_o);
   (void)hipFree(p->part_ml);
   (void)hipFree(p->tile_cnt);
+  (void)hipFree(p->bpart_o);
+  (void)hipFree(p->bpart_ml);
+  (void)hipFree(p->bcnt);
   (void)hipFree(p->ready);
   (void)hipFree(p->fault);
   (void)hipFree(p->head_stride);
@@ -345,12 +353,27 @@ static bool forward_geometry(const lwattn_config& c, const int32_t* gap, int ncu
   for (int h = 1; h < H; ++h) uni = uni && stride[h] == stride[0];
   g.uni_stride = uni ? stride[0] : 0;
   g.blocks_per_head = uni ? blk[1] : 0;
-  const int64_t nband = (int64_t)B * blk[H];
+  const int64_t nblk = (int64_t)B * blk[H];
   // band workgroups may take the bf16 fast path when every subsequence key
   // they stage has a byte offset that fits in 32 bits
   int smax = 1;
   for (int h = 0; h < H; ++h) smax = std::max(smax, stride[h]);
   g.band_fast = (c.dtype != LWATTN_F32 && (int64_t)n + 128 * (int64_t)smax < ((int64_t)1 << 24)) ? 1 : 0;
+  // On the register-staged path (fp32 storage; 16-bit past 32-bit offsets),
+  // whose tiles are long (fp32 MFMA), a grid of band blocks that fills at
+  // most half a round of workgroup slots leaves most SIMDs idle: cut each
+  // block's key tiles into parts (up to 8, and no more than its band tiles),
+  // one workgroup each, merged by log-sum-exp.
+  {
+    const int64_t slots = 2 * (int64_t)ncu;
+    const int r = (int)std::min<int64_t>(c.window / 2, n);
+    const int64_t tiles = (31 + 2 * (int64_t)r) / 32 + 1;
+    g.bparts = 1;
+    if (!g.band_fast && nblk > 0 && 2 * nblk <= slots)
+      g.bparts = (int)std::max<int64_t>(1, std::min<int64_t>({slots / nblk, 8, tiles}));
+  }
+  g.n_band_blk = (int)std::min<int64_t>(nblk, INT32_MAX);
+  const int64_t nband = nblk * g.bparts;
   // compaction workgroups lead the grid, padded to a multiple of 8 so that the
   // band workgroups behind them keep their XCD placement
   const int64_t ncomp = ((int64_t)B + 7) / 8 * 8;
@@ -373,7 +396,7 @@ static bool forward_geometry(const lwattn_config& c, const int32_t* gap, int ncu
     int64_t target = used < slots / 4 ? slots / 4 : slots - used;
     if (target < 64) target = 64;
     int64_t want = (target + units - 1) / units;
-    const int64_t maxs = (n + 127) / 128;
+    const int64_t maxs = (n + 63) / 64;   // slices of at least one 64-key step
     if (want > maxs) want = maxs;
     if (want < 1) want = 1;
     // but no slice longer than 4096 keys, so that no global-row workgroup
@@ -407,7 +430,19 @@ struct FwdWork {
   int32_t *gidx, *gcnt, *status, *tile_cnt, *ready, *fault;
   float *part_o, *part_ml;
   const int32_t *head_stride, *head_blk;   // device copies (read only when H > MAXH_ARG)
+  float *bpart_o, *bpart_ml;               // bparts > 1: the band blocks' key parts
+  int32_t* bcnt;                           // bparts > 1: [blocks][NW] parts finished
 };
+
+// Floats of the band blocks' key parts: O [blocks][NW][bparts][64][32] and
+// (offset, sum) [blocks][NW][bparts][32][2]; words of their counters.
+static size_t bpart_o_floats(const FwdGeom& g) {
+  return g.bparts > 1 ? (size_t)g.n_band_blk * lwk::NW * g.bparts * 64 * 32 : 0;
+}
+static size_t bpart_ml_floats(const FwdGeom& g) {
+  return g.bparts > 1 ? (size_t)g.n_band_blk * lwk::NW * g.bparts * 32 * 2 : 0;
+}
+static size_t bcnt_words(const FwdGeom& g) { return g.bparts > 1 ? (size_t)g.n_band_blk * lwk::NW : 0; }
 
 static size_t fwd_parts(const lwattn_config& c, const FwdGeom& g) {
   return (size_t)c.B * c.H * g.nqt * (g.nsplit > 0 ? g.nsplit : 0) * 32;
@@ -433,6 +468,10 @@ static void forward_params(lwk::Params& prm, const lwattn_config& c, const FwdGe
   prm.part_o = w.part_o;
   prm.part_ml = w.part_ml;
   prm.tile_cnt = w.tile_cnt;
+  prm.bparts = g.bparts;
+  prm.bpart_o = w.bpart_o;
+  prm.bpart_ml = w.bpart_ml;
+  prm.bcnt = w.bcnt;
   prm.ready = w.ready;
   prm.fault = w.fault;
   prm.epoch = epoch;
@@ -646,6 +685,9 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->part_o, nparts * lwk::D * 4);
   alloc((void**)&p->part_ml, nparts * 2 * 4);
   alloc((void**)&p->tile_cnt, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4);
+  alloc((void**)&p->bpart_o, bpart_o_floats(g) * 4);
+  alloc((void**)&p->bpart_ml, bpart_ml_floats(g) * 4);
+  alloc((void**)&p->bcnt, std::max<size_t>(bcnt_words(g), 1) * 4);
   alloc((void**)&p->ready, (size_t)B * 4);
   alloc((void**)&p->fault, 4);
   alloc((void**)&p->head_stride, (size_t)H * 4);
@@ -678,6 +720,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
       !hip_ok(hipMemset(p->tile_cnt, 0, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4), "hipMemset") ||
       (B > 0 && !hip_ok(hipMemset(p->ready, 0, (size_t)B * 4), "hipMemset")) ||
       !hip_ok(hipMemset(p->fault, 0, 4), "hipMemset") ||
+      !hip_ok(hipMemset(p->bcnt, 0, std::max<size_t>(bcnt_words(g), 1) * 4), "hipMemset") ||
       !hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize")) {
     free_plan(p);
     return LWATTN_E_DEVICE;
@@ -715,6 +758,9 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   w.part_ml = p->part_ml;
   w.head_stride = p->head_stride;
   w.head_blk = p->head_blk;
+  w.bpart_o = p->bpart_o;
+  w.bpart_ml = p->bpart_ml;
+  w.bcnt = p->bcnt;
   p->epoch = p->epoch >= INT32_MAX - 1 ? 1 : p->epoch + 1;
   lwk::Params prm;
   forward_params(prm, c, p->geom, w, p->stride_host.data(), p->blk_host.data(), Q, K, V, Qg, Kg, Vg, lmask, gmask, O,
@@ -1323,17 +1369,20 @@ lwattn_status lwattn_forward_noalloc(const lwattn_config* cfg, int hip_device, c
   if (!forward_geometry(c, gap, g_scratch_ncu[hip_device], g, stride, blk)) return LWATTN_E_INVALID;
 
   // layout: the words that must start at zero (ready [B], fault, status [B],
-  // gcnt [B], merge counters [B H nqt]), then the flags, the global index and
-  // the global rows' partials, each 256-byte aligned
+  // gcnt [B], merge counters [B H nqt], band part counters), then the flags,
+  // the global index, the global rows' partials and the band blocks' key
+  // parts, each 256-byte aligned
   const size_t B = (size_t)c.B, n = (size_t)c.n;
   const size_t ntile = B * c.H * (size_t)(g.nqt > 0 ? g.nqt : 1);
-  const size_t nzero = 3 * B + 1 + ntile;
+  const size_t nzero = 3 * B + 1 + ntile + bcnt_words(g);
   const size_t nparts = fwd_parts(c, g);
   const size_t off_flags = align256(nzero * 4);
   const size_t off_gidx = off_flags + align256(B * n);
   const size_t off_po = off_gidx + align256(B * n * 4);
   const size_t off_pml = off_po + align256(nparts * lwk::D * 4);
-  const size_t total = off_pml + align256(nparts * 2 * 4);
+  const size_t off_bpo = off_pml + align256(nparts * 2 * 4);
+  const size_t off_bpml = off_bpo + align256(bpart_o_floats(g) * 4);
+  const size_t total = off_bpml + align256(bpart_ml_floats(g) * 4);
   if (total > kScratchBytes || nzero > (size_t)INT32_MAX) return LWATTN_E_SCRATCH;
 
   FwdWork w;
@@ -1343,6 +1392,9 @@ lwattn_status lwattn_forward_noalloc(const lwattn_config* cfg, int hip_device, c
   w.status = ctrl + B + 1;
   w.gcnt = ctrl + 2 * B + 1;
   w.tile_cnt = ctrl + 3 * B + 1;
+  w.bcnt = ctrl + 3 * B + 1 + ntile;
+  w.bpart_o = (float*)(base + off_bpo);
+  w.bpart_ml = (float*)(base + off_bpml);
   w.flags = base + off_flags;
   w.gidx = (int32_t*)(base + off_gidx);
   w.part_o = (float*)(base + off_po);

@@ -40,6 +40,9 @@ BASE = dict(B=2, H=4, n=1000, d=64, window=128, dilation=[0, 1, 2, 3], max_globa
 @pytest.mark.parametrize("change,want", [
     ({}, lw.OK),
     ({"dtype": "f32"}, lw.OK),
+    ({"dtype": "f16"}, lw.OK),
+    ({"dtype": 2}, lw.OK),             # LWATTN_F16
+    ({"dtype": 3}, lw.E_INVALID),
     ({"window": 0}, lw.OK),
     ({"n": 0}, lw.OK),
     ({"B": 0}, lw.OK),

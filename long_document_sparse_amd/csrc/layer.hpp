@@ -63,6 +63,24 @@ __global__ __launch_bounds__(LNT) void split_heads(const float* P, const T* bias
   storeh<8>(o + (((int64_t)b * H + h) * n + i) * 64 + j, v);
 }
 
+// The same split for a GEMM result that already carries the bias and the
+// storage type (the GEMM's bias epilogue): a 16-bit [M, parts hid] -> `parts`
+// tensors [B, H, n, 64], 8 elements a thread.
+template <typename T>
+__global__ __launch_bounds__(LNT) void split_heads16(const T* P, T* o0, T* o1, T* o2, int parts, int B, int n,
+                                                     int H) {
+  const int hid = H * 64, per_row = parts * hid / 8;
+  const int64_t g = (int64_t)blockIdx.x * LNT + threadIdx.x;
+  if (g >= (int64_t)B * n * per_row) return;
+  const int64_t m = g / per_row;
+  const int c = (int)(g % per_row) * 8;
+  const int which = c / hid, ch = c % hid, h = ch / 64, j = ch % 64;
+  const int b = (int)(m / n), i = (int)(m % n);
+  T* o = which == 0 ? o0 : (which == 1 ? o1 : o2);
+  *reinterpret_cast<vec_t<T, 8>*>(o + (((int64_t)b * H + h) * n + i) * 64 + j) =
+      *reinterpret_cast<const vec_t<T, 8>*>(P + m * parts * hid + c);
+}
+
 // The global tokens of each batch row (valid and global in the masks), in
 // position order, at most mg of them: gpos [B][mg] receives their positions
 // and -1 past the row's count.  One workgroup per batch row, 16 positions a

@@ -142,11 +142,14 @@ static int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 // intermediate buffers and a rocBLAS handle.
 // One GEMM shape of the layer in hipBLASLt: row-major Y[M, N] (fp32) =
 // X[M, K] W[K, N] (16-bit), set up as the column-major product
-// Y^T = W^T X^T.  At set-up the (up to 8) algorithms its heuristic ranks
-// first are timed on scratch operands and the fastest is kept; when hipBLASLt
-// has none for a shape, the layer runs it in rocBLAS.
+// Y^T = W^T X^T; or, with the bias epilogue, Y = X W + bias rounded once to
+// the 16-bit type (bias [N] of that type, added in fp32).  At set-up the (up
+// to 8) algorithms its heuristic ranks first are timed on scratch operands
+// and the fastest is kept; when hipBLASLt has none for a shape, the layer
+// runs it in rocBLAS (fp32 result, the bias added by the split kernel).
 struct LtGemm {
   bool ok = false;
+  bool bias16 = false;   // bias epilogue, 16-bit result
   int64_t M = 0, N = 0, K = 0, ldw = 0;
   hipblasLtMatmulDesc_t desc = nullptr;
   hipblasLtMatrixLayout_t lw = nullptr, lx = nullptr, ly = nullptr;
@@ -173,7 +176,7 @@ struct LtTune {
 };
 
 static void lt_setup(hipblasLtHandle_t h, LtGemm& g, hipDataType dt, int64_t M, int64_t N, int64_t K, int64_t ldw,
-                     const LtTune& tu) {
+                     const LtTune& tu, bool bias16 = false) {
   g.M = M; g.N = N; g.K = K; g.ldw = ldw;
   if (!h || !tu.stream || M == 0 || N == 0 || K == 0) return;
   const hipblasOperation_t op = HIPBLAS_OP_N;
@@ -184,7 +187,21 @@ static void lt_setup(hipblasLtHandle_t h, LtGemm& g, hipDataType dt, int64_t M, 
                 HIPBLAS_STATUS_SUCCESS &&
             hipblasLtMatrixLayoutCreate(&g.lw, dt, (uint64_t)N, (uint64_t)K, ldw) == HIPBLAS_STATUS_SUCCESS &&
             hipblasLtMatrixLayoutCreate(&g.lx, dt, (uint64_t)K, (uint64_t)M, K) == HIPBLAS_STATUS_SUCCESS &&
-            hipblasLtMatrixLayoutCreate(&g.ly, HIP_R_32F, (uint64_t)N, (uint64_t)M, N) == HIPBLAS_STATUS_SUCCESS;
+            hipblasLtMatrixLayoutCreate(&g.ly, bias16 ? dt : HIP_R_32F, (uint64_t)N, (uint64_t)M, N) ==
+                HIPBLAS_STATUS_SUCCESS;
+  if (ok && bias16) {
+    // the bias vector runs along D^T's rows (the output's columns); a dummy
+    // (zero) one while the candidates are timed, the weights' at each call
+    const uint32_t epi = HIPBLASLT_EPILOGUE_BIAS;
+    const int32_t bt = dt;
+    const void* bp = tu.w;
+    ok = hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi, sizeof(epi)) ==
+             HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_BIAS_DATA_TYPE, &bt, sizeof(bt)) ==
+             HIPBLAS_STATUS_SUCCESS &&
+         hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bp, sizeof(bp)) ==
+             HIPBLAS_STATUS_SUCCESS;
+  }
   hipblasLtMatmulPreference_t pref = nullptr;
   ok = ok && hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS;
   const uint64_t cap = tu.ws_cap;
@@ -224,6 +241,7 @@ static void lt_setup(hipblasLtHandle_t h, LtGemm& g, hipDataType dt, int64_t M, 
   g.algo = res[pick].algo;
   g.ws = res[pick].workspaceSize;
   g.ok = true;
+  g.bias16 = bias16;
 }
 
 struct lwattn_layer_s {
@@ -299,6 +317,23 @@ static bool layer_gemm(lwattn_layer_t L, const LtGemm& g, rocblas_datatype dt, c
     return true;
   }
   return gemm_rm(L->blas, dt, g.M, g.N, g.K, X, W, g.ldw, Y);
+}
+
+// A GEMM set up with the bias epilogue: Y16 [M, N] = X W + bias, in the
+// storage type (only when g.bias16).
+static bool layer_gemm_bias(lwattn_layer_t L, const LtGemm& g, const void* X, const void* W, const void* bias,
+                            void* Y16, hipStream_t stream) {
+  if (hipblasLtMatmulDescSetAttribute(g.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias, sizeof(bias)) !=
+      HIPBLAS_STATUS_SUCCESS)
+    return false;
+  const float one = 1.0f, zero = 0.0f;
+  const hipblasStatus_t st = hipblasLtMatmul(L->lt, g.desc, &one, W, g.lw, X, g.lx, &zero, Y16, g.ly, Y16, g.ly,
+                                             &g.algo, L->lt_ws, g.ws, stream);
+  if (st != HIPBLAS_STATUS_SUCCESS) {
+    std::fprintf(stderr, "lwattn: hipblasLtMatmul failed (%d)\n", (int)st);
+    return false;
+  }
+  return true;
 }
 
 template <typename T, int PER>
@@ -1201,8 +1236,10 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
                hipEventCreate(&tu.e1) == hipSuccess && hipMemset(tu.w, 0, wb) == hipSuccess &&
                hipMemset(tu.x, 0, xb) == hipSuccess && hipDeviceSynchronize() == hipSuccess;
     if (!tok) tu.stream = nullptr;   // no tuning: every shape goes to rocBLAS
-    lt_setup(L->lt, L->g_qkv, dt, M, 3 * hid, hid, 3 * hid, tu);
-    lt_setup(L->lt, L->g_kv, dt, M, 2 * hid, hid, 3 * hid, tu);
+    // Q|K|V and Kg|Vg: bias epilogue, 16-bit result (the split kernel then
+    // only moves it)
+    lt_setup(L->lt, L->g_qkv, dt, M, 3 * hid, hid, 3 * hid, tu, true);
+    lt_setup(L->lt, L->g_kv, dt, M, 2 * hid, hid, 3 * hid, tu, true);
     lt_setup(L->lt, L->g_qg, dt, Mg, hid, hid, 3 * hid, tu);
     lt_setup(L->lt, L->g_o, dt, M, hid, hid, hid, tu);
     lt_setup(L->lt, L->g_f1, dt, M, inter, hid, inter, tu);
@@ -1239,16 +1276,25 @@ static lwattn_status layer_forward(lwattn_layer_t L, rocblas_datatype dt, const 
   namespace ly = lwk::layer;
   auto blocks = [](int64_t threads) { return dim3((uint32_t)((threads + ly::LNT - 1) / ly::LNT)); };
   T* const* t = reinterpret_cast<T* const*>(L->qkv);
-  // 1. projections.  Q, K, V: every row, bias added while splitting heads.
-  if (!layer_gemm(L, L->g_qkv, dt, X, w->w_qkv, L->P, stream)) return LWATTN_E_DEVICE;
-  hipLaunchKernelGGL(ly::split_heads<T>, blocks(M * 3 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
-                     (const T*)w->b_qkv, t[0], t[1], t[2], 3, c.B, c.n, H);
+  // 1. projections.  Q, K, V: every row, the bias added by the GEMM's
+  // epilogue (or while splitting heads, on the fallback).
+  const T* wg = (const T*)w->w_g;
+  auto project = [&](const LtGemm& g, const void* W, const T* bias, T* o0, T* o1, T* o2, int parts) {
+    if (g.bias16) {
+      if (!layer_gemm_bias(L, g, X, W, bias, L->P, stream)) return false;
+      hipLaunchKernelGGL(ly::split_heads16<T>, blocks(M * parts * hid / 8), dim3(ly::LNT), 0, stream,
+                         (const T*)L->P, o0, o1, o2, parts, c.B, c.n, H);
+    } else {
+      if (!layer_gemm(L, g, dt, X, W, L->P, stream)) return false;
+      hipLaunchKernelGGL(ly::split_heads<T>, blocks(M * parts * hid / 8), dim3(ly::LNT), 0, stream, L->P, bias,
+                         o0, o1, o2, parts, c.B, c.n, H);
+    }
+    return true;
+  };
+  if (!project(L->g_qkv, w->w_qkv, (const T*)w->b_qkv, t[0], t[1], t[2], 3)) return LWATTN_E_DEVICE;
   // Kg, Vg: every row (the global rows attend to all keys), from the last two
   // column blocks of w_g
-  const T* wg = (const T*)w->w_g;
-  if (!layer_gemm(L, L->g_kv, dt, X, wg + hid, L->P, stream)) return LWATTN_E_DEVICE;
-  hipLaunchKernelGGL(ly::split_heads<T>, blocks(M * 2 * hid / 8), dim3(ly::LNT), 0, stream, L->P,
-                     (const T*)w->b_g + hid, t[4], t[5], t[5], 2, c.B, c.n, H);
+  if (!project(L->g_kv, wg + hid, (const T*)w->b_g + hid, t[4], t[5], t[5], 2)) return LWATTN_E_DEVICE;
   // Qg: only the global tokens' rows (the attention reads Qg nowhere else),
   // gathered, projected by the first column block of w_g and scattered back
   if (mg > 0) {

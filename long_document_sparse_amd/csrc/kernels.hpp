@@ -144,10 +144,19 @@ struct Params {
   int32_t uni_stride;      // > 0: every head has this stride
   int32_t blocks_per_head; // band workgroups of one head when uni_stride > 0
   int32_t band_fast;       // band workgroups may take the bf16 fast path
+  int32_t o_tok;           // 1: O is token-major [B][n][H][64] (the encoder layer's merged heads), 0: [B][H][n][64]
   float c;                 // scale * log2(e)
   int32_t hs[MAXH_ARG];    // head_stride by value when H <= MAXH_ARG
   int32_t hb[MAXH_ARG + 1];
 };
+
+// Output row (b, h, pos) of rb bytes, in either output layout, and the byte
+// distance between consecutive positions of one head.
+__device__ __forceinline__ uint8_t* o_row(const Params& p, int b, int h, int pos, int rb) {
+  const int64_t r = p.o_tok ? ((int64_t)b * p.n + pos) * p.H + h : ((int64_t)b * p.H + h) * p.n + pos;
+  return p.O + r * rb;
+}
+__device__ __forceinline__ int o_stride(const Params& p, int rb) { return p.o_tok ? p.H * rb : rb; }
 
 // ---------------------------------------------------------------------------
 // Layout of one LDS tile slot.
@@ -902,7 +911,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
   if (row_in && (my_fl & 2) == 0) {
     const bool valid = (my_fl & 1) != 0;
     const float inv = valid ? 1.0f / lt : 0.0f;
-    uint8_t* orow = p.O + (head + my_pos) * RB;
+    uint8_t* orow = o_row(p, b, h, my_pos, RB);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -998,7 +1007,7 @@ __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g,
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] *= inv;
     constexpr int RB = D * Lay<S>::ELT;
-    uint8_t* orow = p.O + (((int64_t)b * p.H + h) * p.n + pos) * RB + 32 * ch * Lay<S>::ELT;
+    uint8_t* orow = o_row(p, b, h, pos, RB) + 32 * ch * Lay<S>::ELT;
 #pragma unroll
     for (int k = 0; k < 8; ++k) store_row4<S>(orow + 4 * k * Lay<S>::ELT, acc + 4 * k);
   }
@@ -2099,12 +2108,15 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
       *reinterpret_cast<svec<S, 4>*>(stg + qi * 128 + chunk * 16 + h32 * 8) = t;
     }
   }
-  const __amdgpu_buffer_rsrc_t rout = make_rsrc(p.O + head * RB, n * RB);
+  // the head's rows span (n - 1) ostr + RB bytes (below 2^31: the plan
+  // takes the token-major layout only then)
+  const int ostr = o_stride(p, RB);
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(o_row(p, b, h, 0, RB), (n - 1) * ostr + RB);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 8 * i + (lane >> 3), c = lane & 7;
     const i32x4 v = *reinterpret_cast<const i32x4*>(stg + row * 128 + ((c ^ (row & 7)) * 16));
-    const int off = __shfl(my_pos, row) * RB + c * 16;
+    const int off = __shfl(my_pos, row) * ostr + c * 16;
     if (__shfl(keep ? 1 : 0, row)) store_wt(rout, off, v);
   }
   return true;

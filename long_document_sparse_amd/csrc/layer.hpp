@@ -258,5 +258,18 @@ __global__ __launch_bounds__(LNT) void bias_gelu(const float* G, const T* bias, 
   storeh<8>(Y + m * cols + c, v);
 }
 
+// Y = gelu(Y) in place, Y 16-bit [count8 * 8] (the FFN-in GEMM already added
+// the bias in its epilogue and wrote the storage type); 8 elements a thread.
+template <typename T>
+__global__ __launch_bounds__(LNT) void gelu16(T* Y, int64_t count8) {
+  const int64_t g = (int64_t)blockIdx.x * LNT + threadIdx.x;
+  if (g >= count8) return;
+  float v[8];
+  loadh<8>(Y + g * 8, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0.5f * v[e] * (1.0f + erff(v[e] * 0.70710678118654752f));
+  storeh<8>(Y + g * 8, v);
+}
+
 }  // namespace layer
 }  // namespace lwk

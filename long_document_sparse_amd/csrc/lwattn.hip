@@ -262,7 +262,13 @@ struct lwattn_layer_s {
   hipblasLtHandle_t lt = nullptr;
   void* lt_ws = nullptr;               // hipBLASLt workspace
   size_t lt_ws_bytes = 0;
+  void* lt_ws_side = nullptr;          // the Qg GEMM's own workspace (it runs beside the others)
   LtGemm g_qkv, g_kv, g_qg, g_o, g_f1, g_f2;
+  // the global rows' Qg chain (find, gather, GEMM, scatter) runs on a stream
+  // of its own beside the Q|K|V and Kg|Vg projections: forked from the
+  // caller's stream at the start of a layer, joined before the attention
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 static void free_layer(lwattn_layer_t L) {
@@ -279,6 +285,10 @@ static void free_layer(lwattn_layer_t L) {
   (void)hipFree(L->gpos);
   for (LtGemm* g : {&L->g_qkv, &L->g_kv, &L->g_qg, &L->g_o, &L->g_f1, &L->g_f2}) lt_free(*g);
   (void)hipFree(L->lt_ws);
+  (void)hipFree(L->lt_ws_side);
+  if (L->fork) (void)hipEventDestroy(L->fork);
+  if (L->join) (void)hipEventDestroy(L->join);
+  if (L->side) (void)hipStreamDestroy(L->side);
   if (L->lt) (void)hipblasLtDestroy(L->lt);
   if (L->blas) (void)rocblas_destroy_handle(L->blas);
   delete L;
@@ -305,11 +315,11 @@ static bool gemm_rm(rocblas_handle h, rocblas_datatype dt, int64_t M, int64_t N,
 // One of the layer's GEMMs: hipBLASLt with the algorithm chosen at set-up,
 // else rocBLAS.
 static bool layer_gemm(lwattn_layer_t L, const LtGemm& g, rocblas_datatype dt, const void* X, const void* W, float* Y,
-                       hipStream_t stream) {
+                       hipStream_t stream, void* ws = nullptr) {
   if (g.ok) {
     const float one = 1.0f, zero = 0.0f;
     const hipblasStatus_t st = hipblasLtMatmul(L->lt, g.desc, &one, W, g.lw, X, g.lx, &zero, Y, g.ly, Y, g.ly, &g.algo,
-                                               L->lt_ws, g.ws, stream);
+                                               ws ? ws : L->lt_ws, g.ws, stream);
     if (st != HIPBLAS_STATUS_SUCCESS) {
       std::fprintf(stderr, "lwattn: hipblasLtMatmul failed (%d)\n", (int)st);
       return false;
@@ -529,6 +539,7 @@ static void forward_params(lwk::Params& prm, const lwattn_config& c, const FwdGe
   prm.band_pre = g.band_pre;
   prm.blocks_per_b = g.blocks_per_b;
   prm.c = c.scale * 1.4426950408889634f;
+  prm.o_tok = 0;
   prm.mask_vec = ((((uintptr_t)lmask | (uintptr_t)gmask) & 15u) == 0 && (c.n % 4) == 0) ? 1 : 0;
   prm.uni_stride = g.uni_stride;
   prm.blocks_per_head = g.blocks_per_head;
@@ -771,9 +782,12 @@ lwattn_status lwattn_destroy(lwattn_plan_t p) {
   return LWATTN_OK;
 }
 
-lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, const void* V,
-                             const void* Qg, const void* Kg, const void* Vg,
-                             const float* lmask, const float* gmask, void* O, hipStream_t stream) {
+// The forward; o_tok: O token-major [B][n][H][64] instead of [B][H][n][64]
+// (the encoder layer's merged heads; taken only where a head's rows span less
+// than 2^31 bytes).
+static lwattn_status forward_impl(lwattn_plan_t p, const void* Q, const void* K, const void* V, const void* Qg,
+                                  const void* Kg, const void* Vg, const float* lmask, const float* gmask, void* O,
+                                  bool o_tok, hipStream_t stream) {
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   bool empty = false;
@@ -800,6 +814,7 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   lwk::Params prm;
   forward_params(prm, c, p->geom, w, p->stride_host.data(), p->blk_host.data(), Q, K, V, Qg, Kg, Vg, lmask, gmask, O,
                  p->epoch);
+  prm.o_tok = o_tok ? 1 : 0;
   if (p->inject_timeout) {
     // the rows are published under another number and nobody waits long:
     // every waiting workgroup gives up, sets the fault word and skips its work
@@ -823,6 +838,12 @@ lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, cons
   if (!launch_forward(c, p->geom, prm, stream, ev0, ev1)) return LWATTN_E_DEVICE;
   if (timed) ++p->timing_calls;
   return LWATTN_OK;
+}
+
+lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, const void* V,
+                             const void* Qg, const void* Kg, const void* Vg,
+                             const float* lmask, const float* gmask, void* O, hipStream_t stream) {
+  return forward_impl(p, Q, K, V, Qg, Kg, Vg, lmask, gmask, O, false, stream);
 }
 
 lwattn_status lwattn_forward_causal(lwattn_plan_t p, const void* Q, const void* K, const void* V,
@@ -1242,7 +1263,7 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
     lt_setup(L->lt, L->g_kv, dt, M, 2 * hid, hid, 3 * hid, tu, true);
     lt_setup(L->lt, L->g_qg, dt, Mg, hid, hid, 3 * hid, tu);
     lt_setup(L->lt, L->g_o, dt, M, hid, hid, hid, tu);
-    lt_setup(L->lt, L->g_f1, dt, M, inter, hid, inter, tu);
+    lt_setup(L->lt, L->g_f1, dt, M, inter, hid, inter, tu, true);
     lt_setup(L->lt, L->g_f2, dt, M, hid, inter, hid, tu);
     if (tu.e0) (void)hipEventDestroy(tu.e0);
     if (tu.e1) (void)hipEventDestroy(tu.e1);
@@ -1255,6 +1276,14 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
     for (const LtGemm* g : {&L->g_qkv, &L->g_kv, &L->g_qg, &L->g_o, &L->g_f1, &L->g_f2})
       if (g->ok) L->lt_ws_bytes = std::max(L->lt_ws_bytes, g->ws);
     if (L->lt_ws_bytes) alloc(&L->lt_ws, L->lt_ws_bytes);
+    if (L->g_qg.ok && L->g_qg.ws) alloc(&L->lt_ws_side, L->g_qg.ws);
+  }
+  // the side stream (default priority) only when the Qg GEMM runs on
+  // hipBLASLt (rocBLAS's handle follows the caller's stream)
+  if (ok && mg > 0 && L->g_qg.ok) {
+    ok = hip_ok(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking), "hipStreamCreateWithFlags") &&
+         hip_ok(hipEventCreateWithFlags(&L->fork, hipEventDisableTiming), "hipEventCreateWithFlags") &&
+         hip_ok(hipEventCreateWithFlags(&L->join, hipEventDisableTiming), "hipEventCreateWithFlags");
   }
   if (!ok) {
     free_layer(L);
@@ -1291,36 +1320,57 @@ static lwattn_status layer_forward(lwattn_layer_t L, rocblas_datatype dt, const 
     }
     return true;
   };
+  // Qg: only the global tokens' rows (the attention reads Qg nowhere else),
+  // gathered, projected by the first column block of w_g and scattered back;
+  // a chain of small launches that runs on the side stream beside the big
+  // projections
+  const bool side = mg > 0 && L->side;
+  if (mg > 0) {
+    hipStream_t qs = stream;
+    if (side) {
+      if (!hip_ok(hipEventRecord(L->fork, stream), "hipEventRecord") ||
+          !hip_ok(hipStreamWaitEvent(L->side, L->fork, 0), "hipStreamWaitEvent"))
+        return LWATTN_E_DEVICE;
+      qs = L->side;
+    }
+    const int64_t rows = (int64_t)c.B * mg;
+    hipLaunchKernelGGL(ly::find_global_rows, dim3((uint32_t)c.B), dim3(ly::LNT), 0, qs, lmask, gmask, c.n, mg,
+                       L->gpos);
+    hipLaunchKernelGGL(ly::gather_global_rows<T>, dim3((uint32_t)((rows + 3) / 4)), dim3(ly::LNT), 0, qs,
+                       (const T*)X, L->gpos, c.n, (int)hid, mg, rows, (T*)L->Xg);
+    if (!layer_gemm(L, L->g_qg, dt, L->Xg, wg, L->Pg, qs, side ? L->lt_ws_side : nullptr)) return LWATTN_E_DEVICE;
+    hipLaunchKernelGGL(ly::scatter_global_rows<T>, blocks((int64_t)c.B * mg * hid / 8), dim3(ly::LNT), 0, qs,
+                       L->Pg, (const T*)w->b_g, L->gpos, t[3], c.B, c.n, H, mg);
+    if (side && !hip_ok(hipEventRecord(L->join, L->side), "hipEventRecord")) return LWATTN_E_DEVICE;
+  }
   if (!project(L->g_qkv, w->w_qkv, (const T*)w->b_qkv, t[0], t[1], t[2], 3)) return LWATTN_E_DEVICE;
   // Kg, Vg: every row (the global rows attend to all keys), from the last two
   // column blocks of w_g
   if (!project(L->g_kv, wg + hid, (const T*)w->b_g + hid, t[4], t[5], t[5], 2)) return LWATTN_E_DEVICE;
-  // Qg: only the global tokens' rows (the attention reads Qg nowhere else),
-  // gathered, projected by the first column block of w_g and scattered back
-  if (mg > 0) {
-    const int64_t rows = (int64_t)c.B * mg;
-    hipLaunchKernelGGL(ly::find_global_rows, dim3((uint32_t)c.B), dim3(ly::LNT), 0, stream, lmask, gmask, c.n, mg,
-                       L->gpos);
-    hipLaunchKernelGGL(ly::gather_global_rows<T>, dim3((uint32_t)((rows + 3) / 4)), dim3(ly::LNT), 0, stream,
-                       (const T*)X, L->gpos, c.n, (int)hid, mg, rows, (T*)L->Xg);
-    if (!layer_gemm(L, L->g_qg, dt, L->Xg, wg, L->Pg, stream)) return LWATTN_E_DEVICE;
-    hipLaunchKernelGGL(ly::scatter_global_rows<T>, blocks((int64_t)c.B * mg * hid / 8), dim3(ly::LNT), 0, stream,
-                       L->Pg, (const T*)w->b_g, L->gpos, t[3], c.B, c.n, H, mg);
-  }
+  if (side && !hip_ok(hipStreamWaitEvent(stream, L->join, 0), "hipStreamWaitEvent")) return LWATTN_E_DEVICE;
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
-  // 2. the attention
-  lwattn_status st = lwattn_forward(p, L->qkv[0], L->qkv[1], L->qkv[2], L->qkv[3], L->qkv[4], L->qkv[5], lmask,
-                                    gmask, L->A, stream);
+  // 2. the attention, its output rows written token-major ([M, hid]: the
+  // heads merged) when a head's rows span less than 2^31 bytes
+  const bool tok = (int64_t)c.n * hid * 2 < ((int64_t)1 << 31);
+  lwattn_status st = forward_impl(p, L->qkv[0], L->qkv[1], L->qkv[2], L->qkv[3], L->qkv[4], L->qkv[5], lmask, gmask,
+                                  tok ? L->Am : L->A, tok, stream);
   if (st != LWATTN_OK) return st;
   // 3. output projection, bias, residual, LayerNorm
-  hipLaunchKernelGGL(ly::merge_heads<T>, blocks(M * hid / 8), dim3(ly::LNT), 0, stream, (const T*)L->A, (T*)L->Am,
-                     c.B, c.n, H);
+  if (!tok)
+    hipLaunchKernelGGL(ly::merge_heads<T>, blocks(M * hid / 8), dim3(ly::LNT), 0, stream, (const T*)L->A, (T*)L->Am,
+                       c.B, c.n, H);
   if (!layer_gemm(L, L->g_o, dt, L->Am, w->w_o, L->P, stream)) return LWATTN_E_DEVICE;
   if (!layernorm<T>(H, L->P, w->b_o, X, w->ln1_g, w->ln1_b, L->eps, L->H1, M, stream)) return LWATTN_E_UNSUPPORTED;
   // 4. FFN: intermediate GEMM, bias, GELU; output GEMM, bias, residual, LayerNorm
-  if (!layer_gemm(L, L->g_f1, dt, L->H1, w->w_1, L->P, stream)) return LWATTN_E_DEVICE;
-  hipLaunchKernelGGL(ly::bias_gelu<T>, blocks(M * inter / 8), dim3(ly::LNT), 0, stream, L->P, (const T*)w->b_1,
-                     (T*)L->F, M, (int)inter);
+  if (L->g_f1.bias16) {
+    // the bias in the GEMM's epilogue, the 16-bit result straight into F
+    if (!layer_gemm_bias(L, L->g_f1, L->H1, w->w_1, w->b_1, L->F, stream)) return LWATTN_E_DEVICE;
+    hipLaunchKernelGGL(ly::gelu16<T>, blocks(M * inter / 8), dim3(ly::LNT), 0, stream, (T*)L->F, M * inter / 8);
+  } else {
+    if (!layer_gemm(L, L->g_f1, dt, L->H1, w->w_1, L->P, stream)) return LWATTN_E_DEVICE;
+    hipLaunchKernelGGL(ly::bias_gelu<T>, blocks(M * inter / 8), dim3(ly::LNT), 0, stream, L->P, (const T*)w->b_1,
+                       (T*)L->F, M, (int)inter);
+  }
   if (!layer_gemm(L, L->g_f2, dt, L->F, w->w_2, L->P, stream)) return LWATTN_E_DEVICE;
   if (!layernorm<T>(H, L->P, w->b_2, L->H1, w->ln2_g, w->ln2_b, L->eps, Y, M, stream)) return LWATTN_E_UNSUPPORTED;
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;

@@ -207,9 +207,10 @@ static void lt_setup(hipblasLtHandle_t h, LtGemm& g, hipDataType dt, int64_t M, 
   const uint64_t cap = tu.ws_cap;
   ok = ok && hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &cap,
                                                    sizeof(cap)) == HIPBLAS_STATUS_SUCCESS;
-  hipblasLtMatmulHeuristicResult_t res[8];
+  constexpr int kCand = 8;   // candidates timed per shape (24 measured no better)
+  hipblasLtMatmulHeuristicResult_t res[kCand];
   int nret = 0;
-  ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, g.desc, g.lw, g.lx, g.ly, g.ly, pref, 8, res, &nret) ==
+  ok = ok && hipblasLtMatmulAlgoGetHeuristic(h, g.desc, g.lw, g.lx, g.ly, g.ly, pref, kCand, res, &nret) ==
                  HIPBLAS_STATUS_SUCCESS;
   if (pref) (void)hipblasLtMatmulPreferenceDestroy(pref);
   float best = 0.f;

@@ -106,6 +106,13 @@ __device__ __forceinline__ void store_wt(__amdgpu_buffer_rsrc_t r, int off, V16 
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4s, v), r, off, 0, CPOL_SC1);
 }
 
+// s_waitcnt vmcnt(N): at most N of this wave's loads and stores outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N <= 63, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 
 struct Params {
   const uint8_t *Q, *K, *V, *Qg, *Kg, *Vg;
@@ -934,11 +941,16 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
 // channels 32 (l / 32) .. +31; pos is that row's sequence position.  The
 // partials are streamed two chunks deep, so the merge waits for about one
 // memory round trip instead of one per chunk.
-template <typename S>
+template <typename S, bool WT = false>
 __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g, int lane, int pos) {
-  // this slice's partial rows are written back before it is counted; the
-  // wave that counts the last slice reads all of them with coherent loads
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // this slice's partial rows are visible device-wide before it is counted:
+  // written through (WT: sc1 stores, whose completion is waited for here) or
+  // written back by a release fence; the wave that counts the last slice
+  // reads all of them with coherent loads
+  if constexpr (WT)
+    wait_loads<0>();
+  else
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   int32_t* cnt = p.tile_cnt + ((int64_t)b * p.H + h) * p.nqt + qt;
   int old = 0;
   if (lane == 0) old = atomicAdd(cnt, 1);
@@ -1316,13 +1328,6 @@ constexpr int B_SMEM = B_GH_OFF + 2 * (B_STEP / 2);
 constexpr int B_CH = 512 / NT;          // 16-byte chunks per thread per 8 KB array of a step
 constexpr float SUM_HI = 16384.0f;      // 2^14
 static_assert(B_CH == 2, "each thread stages two chunks of every 8 KB array");
-
-// s_waitcnt vmcnt(N): at most N of this wave's loads outstanding.
-template <int N>
-__device__ __forceinline__ void wait_loads() {
-  static_assert(N >= 0 && N <= 63, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // One 16-byte buffer load per lane into LDS at m0 = lds_base + IMM (lane l
 // writes m0 + 16 l).
@@ -2212,21 +2217,25 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
 
   const float lt = half_sum(st.l);
   if (qok) {
-    const int64_t pidx = ((((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp) * 32 + qi;
-    float* po = p.part_o + pidx * D;
+    // written through (sc1): the count below waits for their completion
+    // instead of a release fence's write-back of the whole L2
+    const int64_t slot = (((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.part_o + slot * 32 * D, 32 * D * 4);
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<float4*>(po + 32 * db + 8 * a + 4 * h32) =
-            make_float4(st.o[db][4 * a], st.o[db][4 * a + 1], st.o[db][4 * a + 2], st.o[db][4 * a + 3]);
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 v = {st.o[db][4 * a], st.o[db][4 * a + 1], st.o[db][4 * a + 2], st.o[db][4 * a + 3]};
+        store_wt(ro, (qi * D + 32 * db + 8 * a + 4 * h32) * 4, v);
+      }
     if (h32 == 0) {
       // a slice with no real key leaves an empty partial
-      p.part_ml[pidx * 2 + 0] = st.first ? -INFINITY : st.m;
-      p.part_ml[pidx * 2 + 1] = lt;
+      const f32x2 ml = {st.first ? -INFINITY : st.m, lt};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), make_rsrc(p.part_ml + slot * 32 * 2, 32 * 2 * 4),
+                                            qi * 8, 0, CPOL_SC1);
     }
   }
-  if (wave_work) finish_global_tile<S>(p, b, h, qt, g, lane, qpos_row);
+  if (wave_work) finish_global_tile<S, true>(p, b, h, qt, g, lane, qpos_row);
   return true;
 }
 

@@ -734,7 +734,8 @@ __device__ bool merge_band_parts(const Params& p, int blk, int part, int wave, i
           make_float4(sm.o[db][4 * k], sm.o[db][4 * k + 1], sm.o[db][4 * k + 2], sm.o[db][4 * k + 3]);
   if (lane < 32) *reinterpret_cast<float2*>(p.bpart_ml + ((wslot + part) * 32 + qi) * 2) = make_float2(sm.m, lt);
   // this part is written back before it is counted; the wave that counts the
-  // last part reads all of them with agent-coherent loads
+  // last part reads all of them with agent-coherent loads (here a fence
+  // measured faster than write-through stores and a wait for them)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   int32_t* cnt = p.bcnt + (int64_t)blk * NW + wave;
   int old = 0;
@@ -941,6 +942,28 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
 // channels 32 (l / 32) .. +31; pos is that row's sequence position.  The
 // partials are streamed two chunks deep, so the merge waits for about one
 // memory round trip instead of one per chunk.
+// One wave's partial result of a global-row query tile over one key slice
+// (32 rows: unnormalised O^T accumulators in register order, offset m, row
+// sum l), written through (sc1) to its slot, so that waiting for the stores'
+// completion publishes it (no release fence, whose write-back of the whole L2
+// serialises over the workgroups of an XCD).
+__device__ __forceinline__ void store_global_partial(const Params& p, int64_t slot, int qi, int h32,
+                                                     const f32x16 (&o)[2], float m, float l) {
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.part_o + slot * 32 * D, 32 * D * 4);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 v = {o[db][4 * a], o[db][4 * a + 1], o[db][4 * a + 2], o[db][4 * a + 3]};
+      store_wt(ro, (qi * D + 32 * db + 8 * a + 4 * h32) * 4, v);
+    }
+  if (h32 == 0) {
+    const f32x2 ml = {m, l};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), make_rsrc(p.part_ml + slot * 32 * 2, 32 * 2 * 4),
+                                          qi * 8, 0, CPOL_SC1);
+  }
+}
+
 template <typename S, bool WT = false>
 __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g, int lane, int pos) {
   // this slice's partial rows are visible device-wide before it is counted:
@@ -1076,21 +1099,8 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
   tile_pipeline<S>(U, desc, comp, nothing, cx, p.Kg + head * RB, p.Vg + head * RB, smem);
 
   const float lt = sm.l + __shfl_xor(sm.l, 32);
-  if (qok) {
-    const int64_t pidx = ((((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp) * 32 + qi;
-    float* po = p.part_o + pidx * D;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<float4*>(po + 32 * db + 8 * a + 4 * h32) =
-            make_float4(sm.o[db][4 * a], sm.o[db][4 * a + 1], sm.o[db][4 * a + 2], sm.o[db][4 * a + 3]);
-    if (h32 == 0) {
-      p.part_ml[pidx * 2 + 0] = sm.m;
-      p.part_ml[pidx * 2 + 1] = lt;
-    }
-  }
-  if (wave_work) finish_global_tile<S>(p, b, h, qt, g, lane, qpos);
+  if (qok) store_global_partial(p, (((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp, qi, h32, sm.o, sm.m, lt);
+  if (wave_work) finish_global_tile<S, true>(p, b, h, qt, g, lane, qpos);
 }
 
 // ---------------------------------------------------------------------------
@@ -2216,25 +2226,10 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
             [] { return 0u; }, qo, p.c, fl, st, h32, smem);
 
   const float lt = half_sum(st.l);
-  if (qok) {
-    // written through (sc1): the count below waits for their completion
-    // instead of a release fence's write-back of the whole L2
-    const int64_t slot = (((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp;
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.part_o + slot * 32 * D, 32 * D * 4);
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 v = {st.o[db][4 * a], st.o[db][4 * a + 1], st.o[db][4 * a + 2], st.o[db][4 * a + 3]};
-        store_wt(ro, (qi * D + 32 * db + 8 * a + 4 * h32) * 4, v);
-      }
-    if (h32 == 0) {
-      // a slice with no real key leaves an empty partial
-      const f32x2 ml = {st.first ? -INFINITY : st.m, lt};
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, ml), make_rsrc(p.part_ml + slot * 32 * 2, 32 * 2 * 4),
-                                            qi * 8, 0, CPOL_SC1);
-    }
-  }
+  // a slice with no real key leaves an empty partial
+  if (qok)
+    store_global_partial(p, (((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp, qi, h32, st.o,
+                         st.first ? -INFINITY : st.m, lt);
   if (wave_work) finish_global_tile<S, true>(p, b, h, qt, g, lane, qpos_row);
   return true;
 }

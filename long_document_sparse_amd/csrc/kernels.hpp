@@ -131,7 +131,8 @@ struct Params {
   int32_t epoch;           // this forward's number (> 0): what every workgroup waits for
   int32_t publish;         // what the compaction publishes (= epoch, except in a fault test)
   int32_t spin_limit;      // polls before a wait for a row gives up
-  int32_t n_comp_wg;       // compaction workgroups at the head of the attention launch (= B)
+  int32_t n_comp_wg;       // compaction workgroups at the head of the attention launch (B padded to 8, or 0)
+  int32_t comp_fold;       // 1: no compaction workgroups; band workgroup bid < B compacts row bid first
   const int32_t* head_stride;  // [H]: dilation gap + 1 (device copy, any H)
   const int32_t* head_blk;     // [H+1]: prefix of band workgroups per batch row
   int32_t B, H, n, r;      // r = min(window/2, n)
@@ -2284,6 +2285,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     global_wg<S>(p, b, h, qg, sp, smem);
   } else {
     if (bid >= p.band_pre) bid -= p.n_glob_wg;
+    if (p.comp_fold && bid < p.B) {
+      // the band grid fits one round of slots here, so the compacting
+      // workgroups are resident beside every workgroup that waits for them
+      compact_row(p, bid, smem);
+      __syncthreads();
+    }
     int lb = xcd_remap(bid, p.n_band_wg), part = 0;
     if (p.bparts > 1) {
       part = lb % p.bparts;

@@ -56,6 +56,7 @@ struct FwdGeom {
   int uni_stride = 0, blocks_per_head = 0, band_fast = 0;
   int n_band_blk = 0;  // band blocks (B * blocks_per_b)
   int bparts = 1;      // key parts per band block on the register-staged path
+  int comp_fold = 0;   // band workgroups 0 .. B-1 compact row bid first (no compaction workgroups)
   size_t smem = 0;
 };
 
@@ -421,8 +422,17 @@ static bool forward_geometry(const lwattn_config& c, const int32_t* gap, int ncu
   g.n_band_blk = (int)std::min<int64_t>(nblk, INT32_MAX);
   const int64_t nband = nblk * g.bparts;
   // compaction workgroups lead the grid, padded to a multiple of 8 so that the
-  // band workgroups behind them keep their XCD placement
-  const int64_t ncomp = ((int64_t)B + 7) / 8 * 8;
+  // band workgroups behind them keep their XCD placement.  When the band
+  // workgroups alone fit one round of slots but not with those ahead of them
+  // (B=1, H=16, n=4096: 512 band workgroups), the last band workgroups would
+  // run as a second round: then band workgroups 0 .. B-1 each compact a row
+  // before their band work instead.
+  int64_t ncomp = ((int64_t)B + 7) / 8 * 8;
+  g.comp_fold = 0;
+  if (ncomp + nband > 2 * (int64_t)ncu && nband <= 2 * (int64_t)ncu && B <= nband) {
+    g.comp_fold = 1;
+    ncomp = 0;
+  }
   // global-row geometry: the key slices are sized so that the global-row
   // workgroups fill what the compaction and band workgroups leave of the last
   // round of workgroup slots (two per compute unit), with at least 64 of them.
@@ -524,6 +534,7 @@ static void forward_params(lwk::Params& prm, const lwattn_config& c, const FwdGe
   prm.publish = epoch;
   prm.spin_limit = (1 << 18) + (int32_t)(c.n >> 2);
   prm.n_comp_wg = g.n_comp_wg;
+  prm.comp_fold = g.comp_fold;
   prm.head_stride = w.head_stride;
   prm.head_blk = w.head_blk;
   prm.B = c.B;

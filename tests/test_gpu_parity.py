@@ -203,6 +203,38 @@ def test_wait_timeout_is_reported_not_hung(dtype):
     assert float(np.max(np.abs(got - want))) <= tol
 
 
+def test_one_round_band_grid_with_compaction_in_band_workgroups():
+    """B=1, H=16, n=4096, window 512 (the FasterTransformer QA encoder's
+    attention, 64 global tokens at the start): 512 band workgroups, one round
+    of slots on a 256-CU device, so the first band workgroup also computes the
+    row's compaction (no compaction workgroup ahead of the band ones).  The
+    compaction is checked bit-exact, sampled rows against the oracle (strong
+    inputs), and the bounded wait under the fault-test hook."""
+    spec = workloads.custom(1, 16, 4096, 64, 512, "bf16", [0] * 16, seed=41, n_global=64,
+                            global_mode="first", max_global=64)
+    x = workloads.generate(spec, strong=True)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec)
+    out, st = run(plan, ts, lm, gm)
+    assert st == lw.OK
+    assert not torch.isnan(out).any().item(), "a row was not written"
+    gidx, gcnt = plan.global_index()
+    og, oc = oracle.compact(x.lmask, x.gmask)
+    assert np.array_equal(gidx.cpu().numpy(), og)
+    assert np.array_equal(gcnt.cpu().numpy(), oc)
+    rows = sample_rows(x, 1000, seed=4)
+    want = oracle_rows(x, rows)
+    got = to_np64(out.reshape(-1, spec.d)[torch.from_numpy(rows).to(out.device)])
+    rel, tol = check_rows(x, got, want)
+    say(f"one-round band grid: rel err {rel:.3e}")
+    assert rel <= tol, rel
+    lib = lw.load_library()
+    assert lib.lwattn_test_inject_wait_timeout(plan.handle) == lw.OK
+    _, st = run(plan, ts, lm, gm)
+    assert st == lw.E_DEVICE
+    plan.close()
+
+
 def test_empty_problem_and_bad_pointers():
     plan = lw.Plan(0, 2, 128, 64, 16, [0, 0], 4, 0.125, "bf16")
     e = torch.empty((0, 2, 128, 64), dtype=torch.bfloat16, device="cuda:0")

@@ -153,6 +153,13 @@ struct Params {
   int32_t blocks_per_head; // band workgroups of one head when uni_stride > 0
   int32_t band_fast;       // band workgroups may take the bf16 fast path
   int32_t o_tok;           // 1: O is token-major [B][n][H][64] (the encoder layer's merged heads), 0: [B][H][n][64]
+  // Input rows: row (b, h, pos) of Q, K, V (k = 0), Qg (k = 1) or Kg, Vg
+  // (k = 2) starts in_bs[k] b + in_hs[k] h + in_rs[k] pos bytes into its
+  // tensor.  [B][H][n][64]: in_bs = H n rb, in_hs = n rb, in_rs = rb; the
+  // encoder layer's projections, [B n][c hid] with the heads side by side:
+  // in_bs = n in_rs, in_hs = rb, in_rs = c hid elt.
+  int64_t in_bs[3], in_hs[3];
+  int32_t in_rs[3];
   float c;                 // scale * log2(e)
   int32_t hs[MAXH_ARG];    // head_stride by value when H <= MAXH_ARG
   int32_t hb[MAXH_ARG + 1];
@@ -165,6 +172,10 @@ __device__ __forceinline__ uint8_t* o_row(const Params& p, int b, int h, int pos
   return p.O + r * rb;
 }
 __device__ __forceinline__ int o_stride(const Params& p, int rb) { return p.o_tok ? p.H * rb : rb; }
+// First row of head (b, h) of an input tensor of class k (see Params).
+__device__ __forceinline__ const uint8_t* in_head(const Params& p, const uint8_t* x, int k, int b, int h) {
+  return x + (int64_t)b * p.in_bs[k] + (int64_t)h * p.in_hs[k];
+}
 
 // ---------------------------------------------------------------------------
 // Layout of one LDS tile slot.
@@ -211,6 +222,7 @@ struct Ctx {
   const uint8_t* fl;       // flags of the batch row (global memory)
   const int32_t* gl;       // global positions of the batch row (LDS copy or global memory)
   int rho, s;              // residue class and stride of the band
+  int64_t rs;              // bytes between consecutive key rows
 };
 
 __device__ __forceinline__ void key_pos(const TileDesc& td, const Ctx& cx, int k, int& pos, bool& in) {
@@ -242,7 +254,6 @@ template <typename S>
 __device__ __forceinline__ void stage_load(Stage<S>& st, const TileDesc& td, const Ctx& cx,
                                            const uint8_t* kbase, const uint8_t* vbase) {
   constexpr int CH = Lay<S>::CH;
-  constexpr int RB = D * Lay<S>::ELT;
   const int tid = threadIdx.x;
   st.list = td.list != 0;
 #pragma unroll
@@ -253,8 +264,8 @@ __device__ __forceinline__ void stage_load(Stage<S>& st, const TileDesc& td, con
     bool in;
     key_pos(td, cx, kt, pos, in);
     st.in[e] = in;
-    st.kr[e] = *reinterpret_cast<const uint4*>(kbase + (int64_t)pos * RB + ch * 16);
-    st.vr[e] = *reinterpret_cast<const uint4*>(vbase + (int64_t)pos * RB + ch * 16);
+    st.kr[e] = *reinterpret_cast<const uint4*>(kbase + (int64_t)pos * cx.rs + ch * 16);
+    st.vr[e] = *reinterpret_cast<const uint4*>(vbase + (int64_t)pos * cx.rs + ch * 16);
     st.fl[e] = cx.fl[pos];
   }
   int pos;
@@ -804,7 +815,6 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
     local -= nb;
   }
   const int R0 = local * ROWS_WG;
-  const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
   int32_t* gl_lds = reinterpret_cast<int32_t*>(smem + 2 * SL::BYTES);
   Ctx cx;
@@ -812,6 +822,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
   cx.gl = gl_lds;
   cx.rho = rho;
   cx.s = s;
+  cx.rs = p.in_rs[0];
 
   const int r = p.r;
   const int kb = R0 - r;
@@ -831,7 +842,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
   const int my_pos = rho + (row_in ? my_i : 0) * s;
   const uint8_t my_fl = cx.fl[my_pos];
   QOp<S> qo;
-  qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
+  qo.load(in_head(p, p.Q, 0, b, h) + (int64_t)my_pos * cx.rs, row_in, h32);
   Softmax sm;
   sm.init();
   const bool wave_work = __any(row_in && (my_fl & 3) == 1);
@@ -872,8 +883,8 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
     for (int j = tid; j < gmain; j += NT) gl_lds[j] = gidx_b[j];
   };
   auto nothing = []() {};
-  const uint8_t* kbase = p.K + head * RB;
-  const uint8_t* vbase = p.V + head * RB;
+  const uint8_t* kbase = in_head(p, p.K, 0, b, h);
+  const uint8_t* vbase = in_head(p, p.V, 0, b, h);
   // this workgroup's tiles [u0, u1) of the U (all of them unless the block's
   // keys are cut into parts; the last part also takes the columns past the
   // LDS list)
@@ -1052,7 +1063,6 @@ __device__ void finish_global_tile(const Params& p, int b, int h, int qt, int g,
 
 template <typename S>
 __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t* smem) {
-  constexpr int RB = D * Lay<S>::ELT;
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   int g = p.gcnt[b];
@@ -1062,19 +1072,19 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
   const int qt = qg * NW + wave;
   const bool wave_work = qt < nqt_b;
   const int n = p.n;
-  const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
   Ctx cx;
   cx.fl = p.flags + (int64_t)b * n;
   cx.gl = gidx_b;
   cx.rho = 0;
   cx.s = 1;
+  cx.rs = p.in_rs[2];
 
   const int qidx = qt * 32 + qi;
   const bool qok = wave_work && qidx < g;
   const int qpos = gidx_b[qok ? qidx : 0];
   QOp<S> qo;
-  qo.load(p.Qg + (head + (qok ? qpos : 0)) * RB, qok, h32);
+  qo.load(in_head(p, p.Qg, 1, b, h) + (int64_t)(qok ? qpos : 0) * p.in_rs[1], qok, h32);
   Softmax sm;
   sm.init();
 
@@ -1097,7 +1107,7 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
     process_tile<S>(qo, sm, slot, lane, p.c, okb == 0xFFFFFFFFu ? 0 : 3, 0, 0, 0);
   };
   auto nothing = []() {};
-  tile_pipeline<S>(U, desc, comp, nothing, cx, p.Kg + head * RB, p.Vg + head * RB, smem);
+  tile_pipeline<S>(U, desc, comp, nothing, cx, in_head(p, p.Kg, 2, b, h), in_head(p, p.Vg, 2, b, h), smem);
 
   const float lt = sm.l + __shfl_xor(sm.l, 32);
   if (qok) store_global_partial(p, (((int64_t)b * p.H + h) * p.nqt + qt) * p.nsplit + sp, qi, h32, sm.o, sm.m, lt);
@@ -1807,8 +1817,13 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
     local -= nb;
   }
   const int R0 = local * ROWS_WG;
-  const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
   const int r = p.r;
+  // this head's K and V rows: rs bytes apart (offsets of every key a step can
+  // name fit in 32 bits: the plan takes this path only then)
+  const uint8_t* kh = in_head(p, p.K, 0, b, h);
+  const uint8_t* vh = in_head(p, p.V, 0, b, h);
+  const int rs = p.in_rs[0];
+  auto span = [&](int rows) { return rows > 0 ? (rows - 1) * rs + RB : 0; };
 
   // band steps: step u holds subsequence keys kb0 + 64 u .. + 63
   const int kb = R0 - r;
@@ -1830,10 +1845,10 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   // this lane's query row and its own key row (the initial offset), in the
   // same round trip as the masks
   QOp<S> qo;
-  qo.load(p.Q + (head + my_pos) * RB, row_in, h32);
+  qo.load(in_head(p, p.Q, 0, b, h) + (int64_t)my_pos * rs, row_in, h32);
   uint4 kdiag[4];
   {
-    const uint8_t* krow = p.K + (head + my_pos) * RB + 64 * h32;
+    const uint8_t* krow = kh + (int64_t)my_pos * rs + 64 * h32;
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) kdiag[cc] = *reinterpret_cast<const uint4*>(krow + 16 * cc);
   }
@@ -1906,15 +1921,15 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
 
   int32_t* gl = reinterpret_cast<int32_t*>(smem + B_GL_OFF);
   int32_t* jr = reinterpret_cast<int32_t*>(smem + B_JR_OFF);
-  const i32x4 dk = make_desc(p.K + head * RB, nv_pos * RB);
-  const i32x4 dv = make_desc(p.V + head * RB, nv_pos * RB);
+  const i32x4 dk = make_desc(kh, span(nv_pos));
+  const i32x4 dv = make_desc(vh, span(nv_pos));
   int kbase[B_CH], vbase[B_CH];
-  const int step_b = 64 * s * RB;
+  const int step_b = 64 * s * rs;
 #pragma unroll
   for (int e = 0; e < B_CH; ++e) {
     int srow, ck16, cv16;
     stage_chunk(wave, lane, e, srow, ck16, cv16);
-    const int rowoff = (rho + (kb0 + srow) * s) * RB;
+    const int rowoff = (rho + (kb0 + srow) * s) * rs;
     kbase[e] = rowoff + ck16;
     vbase[e] = rowoff + cv16;
   }
@@ -1933,14 +1948,14 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
 #pragma unroll
       for (int e = 0; e < B_CH; ++e) off[e] = (is_v ? vbase[e] : kbase[e]) + adv;
     } else {
-      d[2] = n * RB;
+      d[2] = span(n);
 #pragma unroll
       for (int e = 0; e < B_CH; ++e) {
         int srow, ck16, cv16;
         stage_chunk(wave, lane, e, srow, ck16, cv16);
         const int idx = (t - nband) * 64 + srow;
         const bool in = idx < gmain;
-        const int rowoff = gl[in ? idx : 0] * RB;
+        const int rowoff = gl[in ? idx : 0] * rs;
         off[e] = in ? rowoff + (is_v ? cv16 : ck16) : OOB_OFF;
       }
     }
@@ -1996,9 +2011,9 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   auto stage_gh = [&]() {
     if (wave < 2) {
       i32x4 d = dk;
-      d[2] = n * RB;
+      d[2] = span(n);
       i32x4 e = dv;
-      e[2] = n * RB;
+      e[2] = span(n);
       const uint32_t base = lds_w + (uint32_t)B_GH_OFF;   // this wave's 2 KB of the K half
       int offk[B_CH], offv[B_CH];
 #pragma unroll
@@ -2006,7 +2021,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
         int srow, ck16, cv16;
         stage_chunk(wave, lane, c2, srow, ck16, cv16);
         const bool in = srow < gmain;
-        const int rowoff = gl[in ? srow : 0] * RB;
+        const int rowoff = gl[in ? srow : 0] * rs;
         offk[c2] = in ? rowoff + ck16 : OOB_OFF;
         offv[c2] = in ? rowoff + cv16 : OOB_OFF;
       }
@@ -2059,8 +2074,8 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
     sm.l = st.l;
     sm.o[0] = st.o[0];
     sm.o[1] = st.o[1];
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * RB, n * RB);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * RB, n * RB);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kh, span(n));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vh, span(n));
     const int U2 = (g - GL_MAX + KT - 1) / KT;
     for (int u2 = 0; u2 < U2; ++u2) {
       __syncthreads();
@@ -2076,7 +2091,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
       for (int q = tid; q < 256; q += NT) {     // chunk of the 32-key tile
         const int row = q >> 3;
         const bool in = jb + row < g;
-        const int rowoff = gl[row] * RB;
+        const int rowoff = gl[row] * rs;
         const int k16 = ((q & 7) ^ swz_k(row)) * 16, v16 = ((q & 7) ^ swz_v(row)) * 16;
         *reinterpret_cast<uint4*>(smem + q * 16) = bload(rk, in ? rowoff + k16 : OOB_OFF);
         *reinterpret_cast<uint4*>(smem + B_V_OFF + q * 16) = bload(rv, in ? rowoff + v16 : OOB_OFF);
@@ -2153,7 +2168,6 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int n = p.n;
-  const int64_t head = ((int64_t)b * p.H + h) * (int64_t)n;
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
   const int j_start = sp * p.ksplit;
   int j_end = j_start + p.ksplit;
@@ -2184,7 +2198,7 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
     qok = wave_work && qidx < g;
     const int qpos = qok ? coherent_load(gidx_b + qidx) : 0;
     qpos_row = qpos;
-    qo.load(p.Qg + (head + qpos) * RB, qok, h32);
+    qo.load(in_head(p, p.Qg, 1, b, h) + (int64_t)qpos * p.in_rs[1], qok, h32);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) asm volatile("" : "+v"(qo.q[cc]));
   };
@@ -2197,14 +2211,18 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
   FLane fl;
   fl.init(lane);
 
-  const i32x4 dk = make_desc(p.Kg + head * RB, j_use * RB);
-  const i32x4 dv = make_desc(p.Vg + head * RB, j_use * RB);
+  // this head's Kg and Vg rows, rsg bytes apart (offsets in 32 bits: the
+  // plan takes this path only then)
+  const int rsg = p.in_rs[2];
+  const int span_g = j_use > 0 ? (j_use - 1) * rsg + RB : 0;
+  const i32x4 dk = make_desc(in_head(p, p.Kg, 2, b, h), span_g);
+  const i32x4 dv = make_desc(in_head(p, p.Vg, 2, b, h), span_g);
   int kbase[B_CH], vbase[B_CH];
 #pragma unroll
   for (int e = 0; e < B_CH; ++e) {
     int srow, ck16, cv16;
     stage_chunk(wave, lane, e, srow, ck16, cv16);
-    const int rowoff = (j_start + srow) * RB;
+    const int rowoff = (j_start + srow) * rsg;
     kbase[e] = rowoff + ck16;
     vbase[e] = rowoff + cv16;
   }
@@ -2212,7 +2230,7 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
                          wave * (B_CH * 1024);
   auto issue = [&](int t, bool is_v) {
     const uint32_t base = lds_w + (is_v ? B_V_OFF : 0) + (t % B_NSLOT) * B_STEP;
-    const int adv = t * 64 * RB;
+    const int adv = t * 64 * rsg;
     const i32x4 d = is_v ? dv : dk;
     dma16i<0>(d, (is_v ? vbase[0] : kbase[0]) + adv, base);
     dma16i<1024>(d, (is_v ? vbase[1] : kbase[1]) + adv, base);

@@ -252,7 +252,8 @@ struct lwattn_layer_s {
   float eps = 0.f;
   int mg = 0;                          // gathered global rows per batch row: min(max_global, n)
   rocblas_handle blas = nullptr;
-  float* P = nullptr;                  // [M, max(3 hid, inter)] fp32 GEMM results
+  float* P = nullptr;                  // [M, max(3 hid, inter)] fp32 GEMM results (or 16-bit ones)
+  void* P2 = nullptr;                  // [M, 2 hid] 16-bit: the Kg|Vg GEMM's result, read by the attention
   float* Pg = nullptr;                 // [B mg, hid] fp32: Qg of the gathered rows
   void* qkv[6] = {};                   // Q, K, V, Qg, Kg, Vg [B, H, n, 64]
   void* A = nullptr;                   // attention output [B, H, n, 64]
@@ -277,6 +278,7 @@ static void free_layer(lwattn_layer_t L) {
   if (!L) return;
   if (L->attn) (void)hipSetDevice(L->attn->device);
   (void)hipFree(L->P);
+  (void)hipFree(L->P2);
   (void)hipFree(L->Pg);
   for (auto* q : L->qkv) (void)hipFree(q);
   (void)hipFree(L->A);
@@ -552,6 +554,13 @@ static void forward_params(lwk::Params& prm, const lwattn_config& c, const FwdGe
   prm.blocks_per_b = g.blocks_per_b;
   prm.c = c.scale * 1.4426950408889634f;
   prm.o_tok = 0;
+  // inputs [B][H][n][64]
+  const int64_t rb = (int64_t)64 * (c.dtype == LWATTN_F32 ? 4 : 2);
+  for (int k = 0; k < 3; ++k) {
+    prm.in_bs[k] = (int64_t)c.H * c.n * rb;
+    prm.in_hs[k] = (int64_t)c.n * rb;
+    prm.in_rs[k] = (int32_t)rb;
+  }
   prm.mask_vec = ((((uintptr_t)lmask | (uintptr_t)gmask) & 15u) == 0 && (c.n % 4) == 0) ? 1 : 0;
   prm.uni_stride = g.uni_stride;
   prm.blocks_per_head = g.blocks_per_head;
@@ -797,12 +806,21 @@ lwattn_status lwattn_destroy(lwattn_plan_t p) {
   return LWATTN_OK;
 }
 
+// Inputs in the encoder layer's projection layout: Q, K, V rows of
+// `rs_qkv` bytes ([B n][3 hid]: Q, K, V are the column blocks) and Kg, Vg
+// rows of `rs_kv` bytes ([B n][2 hid]); head h at column h 64.  Qg keeps
+// [B][H][n][64].
+struct InRows {
+  int64_t rs_qkv = 0, rs_kv = 0;
+};
+
 // The forward; o_tok: O token-major [B][n][H][64] instead of [B][H][n][64]
 // (the encoder layer's merged heads; taken only where a head's rows span less
-// than 2^31 bytes).
+// than 2^31 bytes); rows: inputs in the projection layout (nullptr:
+// [B][H][n][64]).
 static lwattn_status forward_impl(lwattn_plan_t p, const void* Q, const void* K, const void* V, const void* Qg,
                                   const void* Kg, const void* Vg, const float* lmask, const float* gmask, void* O,
-                                  bool o_tok, hipStream_t stream) {
+                                  bool o_tok, const InRows* rows, hipStream_t stream) {
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   bool empty = false;
@@ -830,6 +848,14 @@ static lwattn_status forward_impl(lwattn_plan_t p, const void* Q, const void* K,
   forward_params(prm, c, p->geom, w, p->stride_host.data(), p->blk_host.data(), Q, K, V, Qg, Kg, Vg, lmask, gmask, O,
                  p->epoch);
   prm.o_tok = o_tok ? 1 : 0;
+  if (rows) {
+    const int64_t rs[3] = {rows->rs_qkv, (int64_t)64 * 2, rows->rs_kv};
+    for (int k : {0, 2}) {
+      prm.in_bs[k] = (int64_t)c.n * rs[k];
+      prm.in_hs[k] = 64 * 2;
+      prm.in_rs[k] = (int32_t)rs[k];
+    }
+  }
   if (p->inject_timeout) {
     // the rows are published under another number and nobody waits long:
     // every waiting workgroup gives up, sets the fault word and skips its work
@@ -858,7 +884,7 @@ static lwattn_status forward_impl(lwattn_plan_t p, const void* Q, const void* K,
 lwattn_status lwattn_forward(lwattn_plan_t p, const void* Q, const void* K, const void* V,
                              const void* Qg, const void* Kg, const void* Vg,
                              const float* lmask, const float* gmask, void* O, hipStream_t stream) {
-  return forward_impl(p, Q, K, V, Qg, Kg, Vg, lmask, gmask, O, false, stream);
+  return forward_impl(p, Q, K, V, Qg, Kg, Vg, lmask, gmask, O, false, nullptr, stream);
 }
 
 lwattn_status lwattn_forward_causal(lwattn_plan_t p, const void* Q, const void* K, const void* V,
@@ -1247,6 +1273,7 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
     if (!hip_ok(hipMalloc(ptr, bytes), "hipMalloc")) { ok = false; *ptr = nullptr; }
   };
   alloc((void**)&L->P, (size_t)M * std::max<int64_t>(3 * hid, inter) * 4);
+  alloc(&L->P2, (size_t)M * 2 * hid * 2);
   alloc((void**)&L->Pg, (size_t)c.B * mg * hid * 4);
   for (auto*& q : L->qkv) alloc(&q, (size_t)M * hid * 2);
   alloc(&L->A, (size_t)M * hid * 2);
@@ -1358,17 +1385,39 @@ static lwattn_status layer_forward(lwattn_layer_t L, rocblas_datatype dt, const 
                        L->Pg, (const T*)w->b_g, L->gpos, t[3], c.B, c.n, H, mg);
     if (side && !hip_ok(hipEventRecord(L->join, L->side), "hipEventRecord")) return LWATTN_E_DEVICE;
   }
-  if (!project(L->g_qkv, w->w_qkv, (const T*)w->b_qkv, t[0], t[1], t[2], 3)) return LWATTN_E_DEVICE;
-  // Kg, Vg: every row (the global rows attend to all keys), from the last two
-  // column blocks of w_g
-  if (!project(L->g_kv, wg + hid, (const T*)w->b_g + hid, t[4], t[5], t[5], 2)) return LWATTN_E_DEVICE;
+  // Q, K, V and Kg, Vg (every row: the global rows attend to all keys, from
+  // the last two column blocks of w_g).  With both GEMMs' 16-bit bias
+  // epilogues, the attention reads the heads straight from the GEMM results
+  // ([M, 3 hid] and [M, 2 hid] row-major) when every key offset its fast path
+  // forms fits in 32 bits; else the heads are split into [B, H, n, 64].
+  int smax = 1;
+  for (int32_t v : p->stride_host) smax = std::max(smax, (int)v);
+  const int64_t rs_qkv = 3 * hid * 2, rs_kv = 2 * hid * 2;
+  const bool in_rows = L->g_qkv.bias16 && L->g_kv.bias16 &&
+                       ((int64_t)c.n + 128 * (int64_t)smax) * rs_qkv < ((int64_t)1 << 31) - (1 << 20);
+  const T* pq = (const T*)L->P;
+  const T* pk = (const T*)L->P2;
+  if (in_rows) {
+    if (!layer_gemm_bias(L, L->g_qkv, X, w->w_qkv, w->b_qkv, L->P, stream) ||
+        !layer_gemm_bias(L, L->g_kv, X, wg + hid, (const T*)w->b_g + hid, L->P2, stream))
+      return LWATTN_E_DEVICE;
+  } else {
+    if (!project(L->g_qkv, w->w_qkv, (const T*)w->b_qkv, t[0], t[1], t[2], 3)) return LWATTN_E_DEVICE;
+    if (!project(L->g_kv, wg + hid, (const T*)w->b_g + hid, t[4], t[5], t[5], 2)) return LWATTN_E_DEVICE;
+  }
   if (side && !hip_ok(hipStreamWaitEvent(stream, L->join, 0), "hipStreamWaitEvent")) return LWATTN_E_DEVICE;
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   // 2. the attention, its output rows written token-major ([M, hid]: the
   // heads merged) when a head's rows span less than 2^31 bytes
   const bool tok = (int64_t)c.n * hid * 2 < ((int64_t)1 << 31);
-  lwattn_status st = forward_impl(p, L->qkv[0], L->qkv[1], L->qkv[2], L->qkv[3], L->qkv[4], L->qkv[5], lmask, gmask,
-                                  tok ? L->Am : L->A, tok, stream);
+  InRows rows;
+  rows.rs_qkv = rs_qkv;
+  rows.rs_kv = rs_kv;
+  lwattn_status st =
+      in_rows ? forward_impl(p, pq, pq + hid, pq + 2 * hid, L->qkv[3], pk, pk + hid, lmask, gmask, tok ? L->Am : L->A,
+                             tok, &rows, stream)
+              : forward_impl(p, L->qkv[0], L->qkv[1], L->qkv[2], L->qkv[3], L->qkv[4], L->qkv[5], lmask, gmask,
+                             tok ? L->Am : L->A, tok, nullptr, stream);
   if (st != LWATTN_OK) return st;
   // 3. output projection, bias, residual, LayerNorm
   if (!tok)

@@ -456,6 +456,11 @@ static bool forward_geometry(const lwattn_config& c, const int32_t* gap, int ncu
     int64_t want = (target + units - 1) / units;
     const int64_t maxs = (n + 63) / 64;   // slices of at least one 64-key step
     if (want > maxs) want = maxs;
+    // at most 8 slices (unless the 4096-key bound below asks for more): the
+    // merge reads every slice's partial (8 KB per query tile) back through
+    // agent-coherent loads, which run at a few hundred GB/s (B=1, H=8,
+    // n=4096, 64 globals: 22 slices 36.4 us, 8 slices 28.8 us)
+    if (want > 8) want = 8;
     if (want < 1) want = 1;
     // but no slice longer than 4096 keys, so that no global-row workgroup
     // outlasts the band ones on long sequences

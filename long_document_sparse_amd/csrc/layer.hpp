@@ -193,8 +193,8 @@ __global__ __launch_bounds__(LNT) void merge_heads(const T* A, T* out, int B, in
 // (two passes over the row held in registers), biased variance, eps inside the
 // square root.  One wave per row: PER columns a lane, as PER / VW groups of VW
 // consecutive columns (VW = 8, or 4 when PER is not a multiple of 8).
-template <typename T, int PER>
-__global__ __launch_bounds__(LNT) void bias_residual_layernorm(const float* G, const T* bias, const T* R,
+template <typename T, int PER, bool G16 = false>
+__global__ __launch_bounds__(LNT) void bias_residual_layernorm(const void* Gv, const T* bias, const T* R,
                                                                const T* gamma, const T* beta, float eps, T* Y,
                                                                int64_t M) {
   constexpr int hid = PER * 64;
@@ -208,8 +208,15 @@ __global__ __launch_bounds__(LNT) void bias_residual_layernorm(const float* G, c
   for (int q = 0; q < PER / VW; ++q) {
     const int c = (q * 64 + lane) * VW;
     float g[VW], b[VW], r[VW];
-    loadf<VW>(G + m * hid + c, g);
-    loadh<VW>(bias + c, b);
+    if constexpr (G16) {
+      // the GEMM's 16-bit result, the bias already added by its epilogue
+      loadh<VW>(static_cast<const T*>(Gv) + m * hid + c, g);
+#pragma unroll
+      for (int e = 0; e < VW; ++e) b[e] = 0.0f;
+    } else {
+      loadf<VW>(static_cast<const float*>(Gv) + m * hid + c, g);
+      loadh<VW>(bias + c, b);
+    }
     loadh<VW>(R + m * hid + c, r);
 #pragma unroll
     for (int e = 0; e < VW; ++e) x[q * VW + e] = g[e] + b[e] + r[e];

@@ -351,11 +351,16 @@ static bool layer_gemm_bias(lwattn_layer_t L, const LtGemm& g, const void* X, co
 }
 
 template <typename T, int PER>
-static void launch_ln(const float* G, const void* b, const void* R, const void* g, const void* be, float eps,
-                      void* Y, int64_t M, hipStream_t stream) {
-  hipLaunchKernelGGL((lwk::layer::bias_residual_layernorm<T, PER>), dim3((uint32_t)((M + 3) / 4)),
-                     dim3(lwk::layer::LNT), 0, stream, G, (const T*)b, (const T*)R, (const T*)g, (const T*)be, eps,
-                     (T*)Y, M);
+static void launch_ln(const void* G, bool g16, const void* b, const void* R, const void* g, const void* be,
+                      float eps, void* Y, int64_t M, hipStream_t stream) {
+  if (g16)
+    hipLaunchKernelGGL((lwk::layer::bias_residual_layernorm<T, PER, true>), dim3((uint32_t)((M + 3) / 4)),
+                       dim3(lwk::layer::LNT), 0, stream, G, (const T*)b, (const T*)R, (const T*)g, (const T*)be, eps,
+                       (T*)Y, M);
+  else
+    hipLaunchKernelGGL((lwk::layer::bias_residual_layernorm<T, PER, false>), dim3((uint32_t)((M + 3) / 4)),
+                       dim3(lwk::layer::LNT), 0, stream, G, (const T*)b, (const T*)R, (const T*)g, (const T*)be, eps,
+                       (T*)Y, M);
 }
 
 // Heads the layer takes: H a multiple of 4 up to 64 (hid = 64 H columns, held
@@ -363,11 +368,11 @@ static void launch_ln(const float* G, const void* b, const void* R, const void* 
 static bool layer_heads_ok(int H) { return H >= 4 && H <= 64 && H % 4 == 0; }
 
 template <typename T>
-static bool layernorm(int H, const float* G, const void* b, const void* R, const void* g, const void* be, float eps,
-                      void* Y, int64_t M, hipStream_t stream) {
+static bool layernorm(int H, const void* G, bool g16, const void* b, const void* R, const void* g, const void* be,
+                      float eps, void* Y, int64_t M, hipStream_t stream) {
   switch (H) {
 #define LWATTN_LN_CASE(h) \
-  case h: launch_ln<T, h>(G, b, R, g, be, eps, Y, M, stream); return true;
+  case h: launch_ln<T, h>(G, g16, b, R, g, be, eps, Y, M, stream); return true;
     LWATTN_LN_CASE(4) LWATTN_LN_CASE(8) LWATTN_LN_CASE(12) LWATTN_LN_CASE(16)
     LWATTN_LN_CASE(20) LWATTN_LN_CASE(24) LWATTN_LN_CASE(28) LWATTN_LN_CASE(32)
     LWATTN_LN_CASE(36) LWATTN_LN_CASE(40) LWATTN_LN_CASE(44) LWATTN_LN_CASE(48)
@@ -1309,9 +1314,9 @@ lwattn_status lwattn_layer_create(lwattn_plan_t p, int32_t inter, float eps, lwa
     lt_setup(L->lt, L->g_qkv, dt, M, 3 * hid, hid, 3 * hid, tu, true);
     lt_setup(L->lt, L->g_kv, dt, M, 2 * hid, hid, 3 * hid, tu, true);
     lt_setup(L->lt, L->g_qg, dt, Mg, hid, hid, 3 * hid, tu);
-    lt_setup(L->lt, L->g_o, dt, M, hid, hid, hid, tu);
+    lt_setup(L->lt, L->g_o, dt, M, hid, hid, hid, tu, true);
     lt_setup(L->lt, L->g_f1, dt, M, inter, hid, inter, tu, true);
-    lt_setup(L->lt, L->g_f2, dt, M, hid, inter, hid, tu);
+    lt_setup(L->lt, L->g_f2, dt, M, hid, inter, hid, tu, true);
     if (tu.e0) (void)hipEventDestroy(tu.e0);
     if (tu.e1) (void)hipEventDestroy(tu.e1);
     if (tu.stream) (void)hipStreamDestroy(tu.stream);
@@ -1428,8 +1433,14 @@ static lwattn_status layer_forward(lwattn_layer_t L, rocblas_datatype dt, const 
   if (!tok)
     hipLaunchKernelGGL(ly::merge_heads<T>, blocks(M * hid / 8), dim3(ly::LNT), 0, stream, (const T*)L->A, (T*)L->Am,
                        c.B, c.n, H);
-  if (!layer_gemm(L, L->g_o, dt, L->Am, w->w_o, L->P, stream)) return LWATTN_E_DEVICE;
-  if (!layernorm<T>(H, L->P, w->b_o, X, w->ln1_g, w->ln1_b, L->eps, L->H1, M, stream)) return LWATTN_E_UNSUPPORTED;
+  // (with the 16-bit bias epilogue the GEMM adds the bias and rounds its
+  // result to the storage type, which the LayerNorm reads)
+  auto project_out = [&](const LtGemm& g, const void* A, const void* W, const void* bias) {
+    return g.bias16 ? layer_gemm_bias(L, g, A, W, bias, L->P, stream) : layer_gemm(L, g, dt, A, W, L->P, stream);
+  };
+  if (!project_out(L->g_o, L->Am, w->w_o, w->b_o)) return LWATTN_E_DEVICE;
+  if (!layernorm<T>(H, L->P, L->g_o.bias16, w->b_o, X, w->ln1_g, w->ln1_b, L->eps, L->H1, M, stream))
+    return LWATTN_E_UNSUPPORTED;
   // 4. FFN: intermediate GEMM, bias, GELU; output GEMM, bias, residual, LayerNorm
   if (L->g_f1.bias16) {
     // the bias in the GEMM's epilogue, the 16-bit result straight into F
@@ -1440,8 +1451,9 @@ static lwattn_status layer_forward(lwattn_layer_t L, rocblas_datatype dt, const 
     hipLaunchKernelGGL(ly::bias_gelu<T>, blocks(M * inter / 8), dim3(ly::LNT), 0, stream, L->P, (const T*)w->b_1,
                        (T*)L->F, M, (int)inter);
   }
-  if (!layer_gemm(L, L->g_f2, dt, L->F, w->w_2, L->P, stream)) return LWATTN_E_DEVICE;
-  if (!layernorm<T>(H, L->P, w->b_2, L->H1, w->ln2_g, w->ln2_b, L->eps, Y, M, stream)) return LWATTN_E_UNSUPPORTED;
+  if (!project_out(L->g_f2, L->F, w->w_2, w->b_2)) return LWATTN_E_DEVICE;
+  if (!layernorm<T>(H, L->P, L->g_f2.bias16, w->b_2, L->H1, w->ln2_g, w->ln2_b, L->eps, Y, M, stream))
+    return LWATTN_E_UNSUPPORTED;
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   return LWATTN_OK;
 }

@@ -3,14 +3,15 @@ the oracle's float64 layer, fed the same stored (bf16) inputs and weights.
 
 Tolerance, from the arithmetic: the GEMMs accumulate in fp32 and every
 intermediate is rounded to bf16 once (Q, K, V, Qg, Kg, Vg; the attention
-output; H1; the FFN-in result before the GELU; the GELU output) and Y itself
-(2^-9 relative each).  LayerNorm
+output; the output projection and FFN-out results before their LayerNorms;
+H1; the FFN-in result before the GELU; the GELU output) and Y itself (2^-9
+relative each).  LayerNorm
 outputs are O(1) (at most a few units); the roundings of H1 and Y alone give
 up to 2^-9 of that, the earlier ones reach Y through the GEMMs' sums over hid
 or inter terms of random sign.  With outputs of magnitude up to about 5 the
 roundings of Y and H1 alone reach 2^-9 * 5 = 0.01.  The bound is |err| <= 4e-2
 elementwise, with the mean error below a tenth of that (measured: at most
-0.030 and 0.0023 over the cases).
+0.030 and 0.0024 over the cases).
 """
 import math
 

@@ -207,6 +207,20 @@ struct SlotLay {
   static constexpr int NCH = KT * Lay<S>::CH / NT;    // chunks per thread per array
 };
 
+// Reads of what other workgroups of the launch wrote (the compaction's
+// outputs, global-row partials) on the fast paths are agent-scope relaxed
+// atomic loads: they compile to loads that are coherent across the XCDs
+// (sc1) and so need no acquire fence, whose cache invalidation costs
+// microseconds when hundreds of workgroups issue it at once.  They are issued
+// only after the epoch (or the slice counter) has been seen, behind a barrier,
+// so they observe what the release published.
+__device__ __forceinline__ int coherent_load(const int32_t* ptr) {
+  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_loadf(const float* ptr) {
+  return __builtin_bit_cast(float, coherent_load(reinterpret_cast<const int32_t*>(ptr)));
+}
+
 // Which keys a tile holds.  Positions are computed for every key, clamped to
 // an existing row, so that every global load of the staging path is issued
 // unconditionally (no divergent branch around a load); keys that do not exist
@@ -219,8 +233,9 @@ struct TileDesc {
 };
 
 struct Ctx {
-  const uint8_t* fl;       // flags of the batch row (global memory)
+  const float* lm;         // the batch row's local mask (an input: plain loads)
   const int32_t* gl;       // global positions of the batch row (LDS copy or global memory)
+  bool gl_global;          // gl is the compaction's list in global memory (read coherently)
   int rho, s;              // residue class and stride of the band
   int64_t rs;              // bytes between consecutive key rows
 };
@@ -230,7 +245,7 @@ __device__ __forceinline__ void key_pos(const TileDesc& td, const Ctx& cx, int k
   in = (jj >= 0) & (jj < td.jend);
   const int jc = min(max(jj, 0), td.jend - 1);
   if (td.list)
-    pos = cx.gl[jc];
+    pos = cx.gl_global ? coherent_load(cx.gl + jc) : cx.gl[jc];
   else
     pos = td.base + jc * td.stride;
 }
@@ -266,14 +281,14 @@ __device__ __forceinline__ void stage_load(Stage<S>& st, const TileDesc& td, con
     st.in[e] = in;
     st.kr[e] = *reinterpret_cast<const uint4*>(kbase + (int64_t)pos * cx.rs + ch * 16);
     st.vr[e] = *reinterpret_cast<const uint4*>(vbase + (int64_t)pos * cx.rs + ch * 16);
-    st.fl[e] = cx.fl[pos];
+    st.fl[e] = cx.lm[pos] != 0.0f ? 1 : 0;
   }
   int pos;
   bool in;
   key_pos(td, cx, tid & (KT - 1), pos, in);
   st.pos = pos;
   st.okin = in;
-  st.okfl = cx.fl[pos];
+  st.okfl = cx.lm[pos] != 0.0f ? 1 : 0;
 }
 
 // Sentinel window index of a global key outside the row's residue class.
@@ -618,32 +633,19 @@ __device__ void compact_row(const Params& p, int b, uint8_t* smem) {
   if (tid == 0) __hip_atomic_store(p.ready + b, p.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Reads of what other workgroups of the launch wrote (the compaction's
-// outputs, global-row partials) on the fast paths are agent-scope relaxed
-// atomic loads: they compile to loads that are coherent across the XCDs
-// (sc1) and so need no acquire fence, whose cache invalidation costs
-// microseconds when hundreds of workgroups issue it at once.  They are issued
-// only after the epoch (or the slice counter) has been seen, behind a barrier,
-// so they observe what the release published.
-__device__ __forceinline__ int coherent_load(const int32_t* ptr) {
-  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_loadf(const float* ptr) {
-  return __builtin_bit_cast(float, coherent_load(reinterpret_cast<const int32_t*>(ptr)));
-}
-
 // Wait until batch row b is compacted for this forward.  The compaction
 // workgroups come first in dispatch order, so they run; the wait is bounded
 // all the same, and a row that never becomes ready is reported in the sticky
 // fault word (the workgroup then skips its work) instead of hanging the
 // launch.  One thread polls with relaxed loads and sleeps between polls; the
-// barrier passes what it saw on to the rest of the workgroup.  Callers that
-// read the compaction's outputs with plain loads (the general paths) ask for
-// an agent-scope acquire fence in every wave as well.
+// barrier passes what it saw on to the rest of the workgroup.  Every caller
+// reads the compaction's outputs with coherent loads (no acquire fence: each
+// one invalidates the XCD's caches, the key tiles other workgroups are
+// reusing included).
 // The limit (p.spin_limit, set by the host) allows at least ~2^18 polls (each
 // sleeps >= 128 clocks) plus n / 4 for the compaction of long rows, far beyond
 // the time it takes.
-__device__ __forceinline__ bool wait_ready(const Params& p, int b, bool acquire) {
+__device__ __forceinline__ bool wait_ready(const Params& p, int b) {
   __shared__ int s_ok;
   if (threadIdx.x == 0) {
     int spins = 0, good = 1;
@@ -658,7 +660,6 @@ __device__ __forceinline__ bool wait_ready(const Params& p, int b, bool acquire)
     s_ok = good;
   }
   __syncthreads();
-  if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return s_ok != 0;
 }
 
@@ -818,8 +819,9 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
   int32_t* gl_lds = reinterpret_cast<int32_t*>(smem + 2 * SL::BYTES);
   Ctx cx;
-  cx.fl = p.flags + (int64_t)b * n;
+  cx.lm = p.lmask + (int64_t)b * n;
   cx.gl = gl_lds;
+  cx.gl_global = false;
   cx.rho = rho;
   cx.s = s;
   cx.rs = p.in_rs[0];
@@ -831,7 +833,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
   int t_hi = (nr - 1 - kb) / 32;
   if (t_hi > NW - 1 + T - 1) t_hi = NW - 1 + T - 1;
   const int nband = t_hi - t_lo + 1;
-  int g = p.gcnt[b];
+  int g = coherent_load(p.gcnt + b);
   if (g > p.max_global) g = p.max_global;
   const int gmain = g < GL_MAX ? g : GL_MAX;
   const int ngt = (gmain + KT - 1) / KT;
@@ -840,7 +842,9 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
   const int my_i = R0 + 32 * wave + qi;
   const bool row_in = my_i < nr;
   const int my_pos = rho + (row_in ? my_i : 0) * s;
-  const uint8_t my_fl = cx.fl[my_pos];
+  // the row's flags (bit 0 real token, bit 1 global) from the masks
+  const bool my_real = cx.lm[my_pos] != 0.0f;
+  const uint8_t my_fl = (my_real ? 1 : 0) | (my_real && p.gmask[(int64_t)b * n + my_pos] != 0.0f ? 2 : 0);
   QOp<S> qo;
   qo.load(in_head(p, p.Q, 0, b, h) + (int64_t)my_pos * cx.rs, row_in, h32);
   Softmax sm;
@@ -880,7 +884,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
     }
   };
   auto fill_gl = [&]() {
-    for (int j = tid; j < gmain; j += NT) gl_lds[j] = gidx_b[j];
+    for (int j = tid; j < gmain; j += NT) gl_lds[j] = coherent_load(gidx_b + j);
   };
   auto nothing = []() {};
   const uint8_t* kbase = in_head(p, p.K, 0, b, h);
@@ -908,6 +912,7 @@ __device__ void band_wg(const Params& p, int b, int h, int local, int s, int blk
     // global columns past the LDS copy: positions straight from the list
     Ctx cx2 = cx;
     cx2.gl = gidx_b + GL_MAX;
+    cx2.gl_global = true;
     const int U2 = (g - GL_MAX + KT - 1) / KT;
     auto desc2 = [&](int u) {
       TileDesc td;
@@ -1065,7 +1070,7 @@ template <typename S>
 __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t* smem) {
   const int tid = threadIdx.x, lane = tid & 63, h32 = lane >> 5, qi = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  int g = p.gcnt[b];
+  int g = coherent_load(p.gcnt + b);
   if (g > p.max_global) g = p.max_global;
   const int nqt_b = (g + 31) / 32;
   if (qg * NW >= nqt_b) return;                     // uniform over the workgroup
@@ -1074,15 +1079,16 @@ __device__ void global_wg(const Params& p, int b, int h, int qg, int sp, uint8_t
   const int n = p.n;
   const int32_t* gidx_b = p.gidx + (int64_t)b * n;
   Ctx cx;
-  cx.fl = p.flags + (int64_t)b * n;
+  cx.lm = p.lmask + (int64_t)b * n;
   cx.gl = gidx_b;
+  cx.gl_global = true;
   cx.rho = 0;
   cx.s = 1;
   cx.rs = p.in_rs[2];
 
   const int qidx = qt * 32 + qi;
   const bool qok = wave_work && qidx < g;
-  const int qpos = gidx_b[qok ? qidx : 0];
+  const int qpos = coherent_load(gidx_b + (qok ? qidx : 0));
   QOp<S> qo;
   qo.load(in_head(p, p.Qg, 1, b, h) + (int64_t)(qok ? qpos : 0) * p.in_rs[1], qok, h32);
   Softmax sm;
@@ -1998,7 +2004,7 @@ __device__ bool band_wg_fast(const Params& p, int b, int h, int local, int s, ui
   // staged once, below), more take whole pipeline steps
   bool gh = false;
   auto learn_globals = [&]() {
-    if (wait_ready(p, b, false)) {
+    if (wait_ready(p, b)) {
       g = coherent_load(p.gcnt + b);
       if (g > p.max_global) g = p.max_global;
     }
@@ -2183,7 +2189,7 @@ __device__ bool global_wg_fast(const Params& p, int b, int h, int qg, int sp, ui
   bool wave_work = false, qok = false;
   QOp<S> qo;
   auto load_rows = [&]() {   // while the first keys are in flight
-    if (wait_ready(p, b, false)) {
+    if (wait_ready(p, b)) {
       g = coherent_load(p.gcnt + b);
       if (g > p.max_global) g = p.max_global;
     }
@@ -2299,7 +2305,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     if constexpr (is16<S>()) {
       if (global_wg_fast<S>(p, b, h, qg, sp, smem)) return;
     }
-    if (!wait_ready(p, b, true)) return;
+    if (!wait_ready(p, b)) return;
     global_wg<S>(p, b, h, qg, sp, smem);
   } else {
     if (bid >= p.band_pre) bid -= p.n_glob_wg;
@@ -2335,7 +2341,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void at
     if constexpr (is16<S>()) {
       if (p.band_fast && band_wg_fast<S>(p, b, h, local, s, smem)) return;
     }
-    if (!wait_ready(p, b, true)) return;
+    if (!wait_ready(p, b)) return;
     band_wg<S>(p, b, h, local, s, lb, part, smem);
   }
 }

@@ -334,11 +334,11 @@ __device__ __forceinline__ void stage_store(const Stage<S>& st, uint8_t* slot, c
   }
 }
 
-// Runs `comp(u, slot)` for tiles u = 0..U-1.  bf16: two-deep register
-// prefetch (loads issued two steps before their LDS store); float32, whose
-// MFMA work per tile is 8x longer, keeps one register set.  `pre()` runs once
-// after the first loads are issued and before the first barrier.  Every thread
-// of the workgroup must call it with the same U >= 1.
+// Runs `comp(u, slot)` for tiles u = 0..U-1 with a two-deep register
+// prefetch: a tile's loads are issued two steps before its LDS store (fp32
+// measured on par with or slightly faster than a one-step prefetch).  `pre()` runs once
+// after the first loads are issued and before the first barrier.  Every
+// thread of the workgroup must call it with the same U >= 1.
 template <typename S, class DescFn, class CompFn, class PreFn>
 __device__ __forceinline__ void tile_pipeline(int U, DescFn desc, CompFn comp, PreFn pre,
                                               const Ctx& cx, const uint8_t* kbase,
@@ -346,37 +346,22 @@ __device__ __forceinline__ void tile_pipeline(int U, DescFn desc, CompFn comp, P
   using SL = SlotLay<S>;
   uint8_t* slot0 = smem;
   uint8_t* slot1 = smem + SL::BYTES;
-  if constexpr (is16<S>()) {
-    Stage<S> s0, s1;
-    stage_load<S>(s0, desc(0), cx, kbase, vbase);
-    if (U > 1) stage_load<S>(s1, desc(1), cx, kbase, vbase);
-    pre();
-    stage_store<S>(s0, slot0, desc(0), cx);
+  Stage<S> s0, s1;
+  stage_load<S>(s0, desc(0), cx, kbase, vbase);
+  if (U > 1) stage_load<S>(s1, desc(1), cx, kbase, vbase);
+  pre();
+  stage_store<S>(s0, slot0, desc(0), cx);
+  __syncthreads();
+  for (int u = 0; u < U; u += 2) {
+    if (u + 2 < U) stage_load<S>(s0, desc(u + 2), cx, kbase, vbase);
+    comp(u, slot0);
+    if (u + 1 < U) stage_store<S>(s1, slot1, desc(u + 1), cx);
     __syncthreads();
-    for (int u = 0; u < U; u += 2) {
-      if (u + 2 < U) stage_load<S>(s0, desc(u + 2), cx, kbase, vbase);
-      comp(u, slot0);
-      if (u + 1 < U) stage_store<S>(s1, slot1, desc(u + 1), cx);
-      __syncthreads();
-      if (u + 1 >= U) break;
-      if (u + 3 < U) stage_load<S>(s1, desc(u + 3), cx, kbase, vbase);
-      comp(u + 1, slot1);
-      if (u + 2 < U) stage_store<S>(s0, slot0, desc(u + 2), cx);
-      __syncthreads();
-    }
-  } else {
-    Stage<S> st;
-    stage_load<S>(st, desc(0), cx, kbase, vbase);
-    pre();
-    stage_store<S>(st, slot0, desc(0), cx);
+    if (u + 1 >= U) break;
+    if (u + 3 < U) stage_load<S>(s1, desc(u + 3), cx, kbase, vbase);
+    comp(u + 1, slot1);
+    if (u + 2 < U) stage_store<S>(s0, slot0, desc(u + 2), cx);
     __syncthreads();
-    for (int u = 0; u < U; ++u) {
-      const bool more = u + 1 < U;
-      if (more) stage_load<S>(st, desc(u + 1), cx, kbase, vbase);
-      comp(u, (u & 1) ? slot1 : slot0);
-      if (more) stage_store<S>(st, (u & 1) ? slot0 : slot1, desc(u + 1), cx);
-      __syncthreads();
-    }
   }
 }
 

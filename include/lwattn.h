@@ -181,29 +181,37 @@ lwattn_status lwattn_forward_blocksparse(lwattn_plan_t plan, const void* Q, cons
                                          hipStream_t stream);
 
 /* Encoder layer around the attention (FasterTransformer Longformer encoder
- * guide, compute flow; bf16 storage, fp32 accumulation).  With M = B*n rows
- * of hid = H*64 columns, X [M][hid] the layer input:
+ * guide, compute flow; the plan's 16-bit storage, bf16 or fp16, with fp32
+ * accumulation).  With M = B*n rows of hid = H*64 columns, X [M][hid] the
+ * layer input:
  *   [Q | K | V]    = X w_qkv + b_qkv      (w_qkv [hid][3 hid], b_qkv [3 hid])
- *   [Qg | Kg | Vg] = X w_g + b_g          (same shapes), each split into heads
- *                    [B][H][n][64] (column h*64 + j of a part: head h, element j);
- *                    Qg is formed for the global tokens' rows only (gathered,
- *                    projected, scattered back), the only rows the attention
- *                    reads of it
- *   A  = the attention of the plan (lwattn_forward) on those six tensors and
+ *   [Qg | Kg | Vg] = X w_g + b_g          (same shapes); column h*64 + j of a
+ *                    part is head h, element j; Qg is formed for the global
+ *                    tokens' rows only (gathered, projected, scattered back),
+ *                    the only rows the attention reads of it
+ *   A  = the attention of the plan (as lwattn_forward) on those six tensors and
  *        the masks, heads merged back to [M][hid]
  *   H1 = LayerNorm(A w_o + b_o + X) * ln1_g + ln1_b
- *   F  = gelu(H1 w_1 + b_1), gelu(x) = x (1 + erf(x / sqrt 2)) / 2
+ *   F  = gelu(H1 w_1 + b_1), gelu(x) = x (1 + erf(x / sqrt 2)) / 2 (erf by
+ *        Abramowitz-Stegun 7.1.26: absolute error of gelu below 2.2e-7)
  *   Y  = LayerNorm(F w_2 + b_2 + H1) * ln2_g + ln2_b
  * LayerNorm over each row: (x - mean) / sqrt(biased variance + eps).  All
- * weights row-major [in][out], bf16, 16-byte aligned device memory; X and Y
- * [M][hid] bf16.  The GEMMs run in rocBLAS (fp32 results), the bias, split,
- * merge, LayerNorm and GELU steps in the library's kernels; each intermediate
- * is rounded to bf16 once.  lwattn_layer_create(plan, inter, eps, &layer):
- * plan with bf16 storage and H a multiple of 4 up to 64, inter a positive
- * multiple of 8, eps > 0; the layer keeps the plan (which must outlive it) and
- * allocates its intermediates and a rocBLAS handle.  lwattn_layer_forward
- * enqueues the layer on `stream` (no allocation, no host sync; it uses the
- * plan's workspace, so it must not overlap other calls of the plan).
+ * weights row-major [in][out] in the storage type, 16-byte aligned device
+ * memory; X and Y [M][hid] in the storage type.  The GEMMs run in hipBLASLt
+ * (rocBLAS for a shape it has no algorithm for), adding the bias in their
+ * epilogue where it has one; each GEMM result and every other intermediate
+ * is rounded to the storage type once.  The attention reads Q, K, V, Kg, Vg
+ * where the GEMMs left them and writes its rows already merged.
+ * lwattn_layer_create(plan, inter, eps, &layer): plan with 16-bit storage and
+ * H a multiple of 4 up to 64, inter a positive multiple of 8, eps > 0; the
+ * layer keeps the plan (which must outlive it) and allocates its
+ * intermediates, its GEMM handles and an internal stream.
+ * lwattn_layer_forward enqueues the layer on `stream` (no allocation, no host
+ * sync): the global rows' Qg chain runs on the layer's internal stream,
+ * forked from `stream` at the start and joined back into it before the
+ * attention, so the call stays ordered with the other work on `stream`.  It
+ * uses the plan's workspace, so it must not overlap other calls of the plan or
+ * of the same layer.
  * Errors: LWATTN_E_INVALID for null or misaligned arguments or a bad inter /
  * eps; LWATTN_E_UNSUPPORTED for fp32 storage, another H, or M * 3 hid or
  * M * inter >= 2^31; LWATTN_E_NOMEM; LWATTN_E_DEVICE if a launch or GEMM fails;

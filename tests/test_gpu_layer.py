@@ -47,6 +47,9 @@ CASES = [
     (1, 16, 512, 128, [0] * 16, 8, "none", 0, 4096),
     (1, 12, 1024, 256, [0] * 12, 40, "per_batch", 100, 3072),   # base-model heads (hid 768)
     (2, 4, 200, 32, [0, 1, 2, 3], 0, "none", 0, 512),           # no global token at all
+    # padding anywhere in the row: the attention's register-staged paths,
+    # reading Q, K, V, Kg, Vg in place from the projections
+    (2, 8, 300, 64, [0] * 4 + [1] * 4, 5, "scatter", 60, 1024),
 ]
 
 

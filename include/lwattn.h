@@ -249,9 +249,13 @@ lwattn_status lwattn_layer_destroy(lwattn_layer_t layer);
  *                         written (zero where no path reaches it).  They must
  *                         not overlap each other or any input.
  * All pointers 16-byte aligned.  Arithmetic in fp32 (bf16 storage is widened
- * on load and rounded RNE on store).  Three kernel launches: the global-index
- * compaction, dQ/dQg (which leaves each row's log-sum-exp and D in the plan's
- * workspace), then dK/dV/dKg/dVg.  Errors as for lwattn_forward; too many
+ * on load and rounded RNE on store).  bf16: the global-index compaction
+ * (inside the dQ launch, by its first B workgroups, when that grid fits one
+ * round of workgroup slots), dQ (which leaves each row's log-sum-exp and D in
+ * the plan's workspace), the chunk sums of the global rows and keys and their
+ * merge (when max_global > 0; the merge inside the dK/dV launch when its last
+ * round has spare slots for it), dK/dV/dKg/dVg.  fp32: three launches, the
+ * compaction, dQ/dQg, then dK/dV/dKg/dVg.  Errors as for lwattn_forward; too many
  * global tokens is reported by lwattn_sync_status.  Shares the plan's
  * workspace with lwattn_forward: a forward and a backward of one plan must
  * not overlap (same stream, or ordered). */
@@ -304,8 +308,10 @@ lwattn_status lwattn_timing_read(lwattn_plan_t plan, float* ms, int32_t cap,
  * backward, up to `max_calls`): per kernel slot, the summed duration in
  * milliseconds over the recorded backwards.  Slots (*nkernels = 5): the
  * global-index compaction, dQ, the chunk sums of the global rows and keys, their
- * merge, dK/dV; a slot whose kernel a backward did not launch (fp32 storage
- * launches slots 0, 1 and 4 only) counts zero. */
+ * merge, dK/dV; a slot whose kernel a backward did not launch counts zero
+ * (fp32 launches slots 0, 1 and 4; bf16 skips slot 0 when the compaction runs
+ * inside dQ, slot 3 when the merge runs inside dK/dV, slots 2 and 3 without
+ * global tokens). */
 lwattn_status lwattn_timing_read_backward(lwattn_plan_t plan, float* ms, int32_t cap,
                                           int32_t* nkernels, int32_t* ncalls);
 lwattn_status lwattn_timing_disable(lwattn_plan_t plan);

@@ -47,7 +47,11 @@ struct BwParams {
                                 // kernels keep the log-sum-exp in log2 units
   float* gq;                    // [B,H,max_global,gsplit,68] per-chunk dQg sums, max, sum of exp
   float* gk;                    // [B,H,max_global,gsplit,128] per-chunk dK, dV sums of global keys
+  float* gml;                   // [B,H,max_global,gspad,2] per-chunk max and sum of exp of the global rows
   int gsplit, gchunk;           // position chunks of the global rows' / keys' sums, chunk length
+  int gspad;                    // gsplit rounded up to even (16-byte rows of gml)
+  int comp_fold;                // bf16: the dQ launch compacts the rows (its grid fits one round of slots)
+  int merge_fold;               // bf16: the dK/dV launch merges the chunk sums (in its last round's spare slots)
   int B, H, n, r, max_global, ntg, blocks_per_b;
   float scale;
 };
@@ -1089,7 +1093,17 @@ __device__ __forceinline__ bool merge_key_quadrants(f32x16 (&acc)[2], float& m, 
 // m the running maximum.  Also writes zero dQ rows for the block's non-local
 // rows, zero dQg rows for its non-global rows, and (log-sum-exp, D) of its
 // local rows.
-__device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint8_t* sm, TMeta (&tm)[3]) {
+// The row's global-index list comes from the compaction, which publishes the
+// epoch and the row's global count in one word.  With CF the
+// compaction runs in this launch (the first workgroups, cp): thread 0 polls
+// the word in the prologue (in the round trip of the first tiles) and, when
+// that came too early, again before the first global tile is issued; the
+// count reaches the other threads through LDS across the loop's barrier, and
+// the list is read with coherent loads after it.  Without it the compaction
+// was an earlier launch and the first poll sees the word.
+template <bool CF>
+__device__ void dq_local(const BwParams& p, const Params& cp, int b, int h, int rho, int blk, uint8_t* sm,
+                         TMeta (&tm)[3]) {
   // LDS: three slots of (K tile, V tile), then three Stage records; the
   // merge of the key quadrants reuses the slots once the tiles are done
   Stage* stg = reinterpret_cast<Stage*>(sm + 6 * TB);
@@ -1101,18 +1115,53 @@ __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint
   const int I0 = blk * T;
   const int64_t bh = (int64_t)b * p.H + h;
   const int64_t hoff = bh * n * 128;
-  int g = p.gcnt[b];
-  if (g > p.max_global) g = p.max_global;
   const int32_t* gidx = p.gidx + (int64_t)b * n;
   const int nwin = (T + 2 * r + T - 1) / T;
-  const int ntot = nwin + (g + T - 1) / T;
+  // the global count and with it the tile count, once the compaction is seen
+  __shared__ int s_g;
+  uint64_t seen = 0;
+  if (CF && t == 0) seen = coherent_load64(cp.ready_cnt + b);
+  int g = 0, ntot = nwin;
+  if constexpr (!CF) {
+    g = p.gcnt[b];
+    if (g > p.max_global) g = p.max_global;
+    ntot = nwin + (g + T - 1) / T;
+  }
+  // thread 0, ahead of a barrier: the row's count into s_g (-1: the wait gave
+  // up, bounded as in wait_ready, and the fault word is set)
+  auto resolve = [&]() {
+    if (t != 0) return;
+    int spins = 0;
+    while ((int32_t)(seen >> 32) != cp.epoch) {
+      if (++spins > cp.spin_limit) {
+        atomicOr(cp.fault, 1);
+        s_g = -1;
+        return;
+      }
+      __builtin_amdgcn_s_sleep(2);
+      seen = coherent_load64(cp.ready_cnt + b);
+    }
+    s_g = (int)(uint32_t)seen;
+  };
+  // every thread, behind that barrier
+  auto adopt = [&]() {
+    g = s_g;
+    if (g < 0) return false;
+    if (g > p.max_global) g = p.max_global;
+    ntot = nwin + (g + T - 1) / T;
+    return true;
+  };
   auto key_pos = [&](int kt, int R) {
     if (kt < nwin) {
       const int jp = I0 - r + T * kt + R;
       return jp >= 0 && jp < nr ? rho + jp * s : -1;
     }
     const int idx = T * (kt - nwin) + R;
-    return idx < g ? gidx[idx] : -1;
+    if (idx >= g) return -1;
+    if constexpr (CF)
+      return coherent_load(gidx + idx);
+    else
+      return gidx[idx];
   };
   const i32x4 dK = make_desc(p.K + hoff, n * 128);
   const i32x4 dV = make_desc(p.V + hoff, n * 128);
@@ -1156,6 +1205,13 @@ __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint
   // every load so far has landed, tile 0 too; from here on the only loads in
   // flight are the tiles' (and, at global tiles, the index reads)
   wait_all_loads();
+  // the count is needed before the first global tile is issued: at the
+  // iteration that issues tile nwin (kt = nwin - 2), or here when that is tile 1
+  if (CF && nwin < 2) {
+    resolve();
+    __syncthreads();
+    if (!adopt()) return;
+  }
   if (ntot > 1) prefetch(1, 1);
 
   const float c = p.scale * LOG2E;
@@ -1178,7 +1234,12 @@ __device__ void dq_local(const BwParams& p, int b, int h, int rho, int blk, uint
       // window tiles count local keys; the global tiles count global keys
       publish_bits(tm[cur], stage_kind(stg[cur], t) == (win ? 2 : 1));
     }
+    if (CF && kt + 2 == nwin) resolve();
     __syncthreads();
+    if (CF && kt + 2 == nwin && !adopt()) {
+      wait_vm<0>();   // no load into this workgroup's LDS outlives it
+      return;
+    }
     if (kt + 2 < ntot) prefetch(kt + 2, cur == 0 ? 2 : cur - 1);
     const uint8_t* tK = sm + cur * 2 * TB;
     // in the window, key 32 kq + k is within r of the row when key index
@@ -1284,6 +1345,7 @@ __device__ __forceinline__ bool sum_row_quadrants(f32x16 (&dk)[2], f32x16 (&dv)[
 // of (b, h), in one pass over the row tiles: the window's (with Q and the
 // local rows' statistics), then the global rows' (with Qg and theirs).  The
 // statistics must be in place.
+template <bool MF>
 __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uint8_t* sm, Meta (&mt)[2]) {
   float* xch = reinterpret_cast<float*>(sm + 4 * TB);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, kq = w & 1, rq = w >> 1;
@@ -1321,9 +1383,46 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
     const uint32_t buf = lds0 + (qt & 1) * 2 * TB;
     dma_tile(qt < nwin ? dQd : dQgd, buf, w, lane, p0, p1);
     dma_tile(dOd, buf + TB, w, lane, p0, p1);
-    if (t < T) fetch_meta(mr, lm, gm, st, pm, qt < nwin);
+    if (t < T) fetch_meta(mr, lm, gm, qt < nwin || !MF ? st : nullptr, pm, qt < nwin);
   };
   if (ntot > 0) prefetch(0);
+  // With MF the merge of the chunk sums runs beside this workgroup
+  // in the same launch, so the global rows' statistics are not in p.stats:
+  // (log-sum-exp, D) of global row `idx` of (b, h) is combined here from the
+  // chunks' (max, sum of exp) pairs (log2 units), 32 chunks a round trip
+  // (16-byte loads, all in flight together); D was stored beside the first
+  // chunk's dQg sum.  Those of the first two global tiles' rows are fetched
+  // in the round trip of the first window tile.
+  auto global_stat = [&](int idx) {
+    if (idx >= g) return make_float2(0.0f, 0.0f);
+    const int64_t row = bh * p.max_global + idx;
+    const float4* src = reinterpret_cast<const float4*>(p.gml + row * p.gspad * 2);
+    const float dd = p.gq[row * p.gsplit * 68 + 66];
+    float mm = -INFINITY, L = 0.0f;
+    for (int c0 = 0; 2 * c0 < p.gsplit; c0 += 16) {
+      float4 v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = 2 * (c0 + j) < p.gsplit ? src[c0 + j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      float e[32], f[32];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool a0 = 2 * (c0 + j) < p.gsplit, a1 = 2 * (c0 + j) + 1 < p.gsplit;
+        e[2 * j] = a0 ? v[j].x : -INFINITY;
+        f[2 * j] = a0 ? v[j].y : 0.0f;
+        e[2 * j + 1] = a1 ? v[j].z : -INFINITY;
+        f[2 * j + 1] = a1 ? v[j].w : 0.0f;
+      }
+      float gmx = mm;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) gmx = fmaxf(gmx, e[j]);
+      if (gmx == -INFINITY) continue;   // no real key in these chunks yet
+      L = mm == -INFINITY ? 0.0f : L * __builtin_amdgcn_exp2f(mm - gmx);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) L = fmaf(f[j], e[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(e[j] - gmx), L);
+      mm = gmx;
+    }
+    return make_float2(L > 0.0f ? mm + log2f(L) : INFINITY, dd);
+  };
 
   const int key = 32 * kq + qi;
   const int kps = J0 + key < nr ? rho + (J0 + key) * s : -1;
@@ -1331,6 +1430,9 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
   bf16x8 kf[4], vf[4];
   row_frags(kf, p.K + hoff, kps, h32);
   row_frags(vf, p.V + hoff, kps, h32);
+  const bool gfold = MF && t < T;
+  const float2 gst0 = gfold && ntot > nwin ? global_stat(t) : make_float2(0.0f, 0.0f);
+  const float2 gst1 = gfold && ntot > nwin + 1 ? global_stat(T + t) : make_float2(0.0f, 0.0f);
   f32x16 dk[2] = {}, dv[2] = {};
   const float c = p.scale * LOG2E;
   const bool all_win = __all(kkd == 2), all_real = __all(kkd != 0);
@@ -1356,9 +1458,12 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
       // window tiles count local rows; the global tiles count global rows
       const uint8_t kd = meta_kind(mr, win);
       const bool keep = kd == (win ? 2 : 1);
+      const float2 sv = win || !MF
+                            ? mr.st
+                            : (qt == nwin ? gst0 : qt == nwin + 1 ? gst1 : global_stat(T * (qt - nwin) + t));
       mt[cur].rkind[t] = kd;
-      mt[cur].lse[t] = keep ? mr.st.x : 0.0f;
-      mt[cur].dd[t] = keep ? mr.st.y : 0.0f;
+      mt[cur].lse[t] = keep ? sv.x : 0.0f;
+      mt[cur].dd[t] = keep ? sv.y : 0.0f;
       publish_bits(mt[cur], keep);
     }
     __syncthreads();
@@ -1464,7 +1569,11 @@ __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, ui
         for (int a = 0; a < 4; ++a)
           *reinterpret_cast<float4*>(dst + 32 * db + 8 * a + 4 * h32) =
               make_float4(acc[db][4 * a], acc[db][4 * a + 1], acc[db][4 * a + 2], acc[db][4 * a + 3]);
-      if (h32 == 0) *reinterpret_cast<float2*>(dst + 64) = make_float2(m, l);
+      if (h32 == 0) {
+        *reinterpret_cast<float4*>(dst + 64) = make_float4(m, l, dsum, 0.0f);
+        *reinterpret_cast<float2*>(p.gml + ((bh * p.max_global + T * gt + row) * p.gspad + sp) * 2) =
+            make_float2(m, l);
+      }
     }
   }
   // (2) wave w: global keys 32 (w & 1) + lane % 32 (lane = key), rows 32 (w >> 1) ..
@@ -1513,20 +1622,40 @@ __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, ui
 
 // Neighbouring blocks of a head share most of their window tiles: the
 // logical block order keeps them on one XCD, whose L2 then serves the overlap.
-__global__ __launch_bounds__(NTH) void dq_kernel(BwParams p) {
+// With CF, workgroups 0 .. B-1, first in dispatch order, compact
+// batch row blockIdx.x (cp: the forward's compaction and its publication)
+// before their own rows.
+template <bool CF>
+__global__ __launch_bounds__(NTH) void dq_kernel(BwParams p, Params cp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ TMeta mt[3];
+  if (CF && (int)blockIdx.x < p.B) {
+    compact_row(cp, blockIdx.x, sm);
+    __syncthreads();
+  }
   int b, h, rho, blk;
   decode_block(p, xcd_remap(blockIdx.x, gridDim.x), b, h, rho, blk);
-  dq_local(p, b, h, rho, blk, sm, mt);
+  dq_local<CF>(p, cp, b, h, rho, blk, sm, mt);
 }
 
+__device__ void global_merge(const BwParams& p, int64_t item, int lane);
+
+// With MF, the workgroups past the B * blocks_per_b key blocks (in the last
+// round's spare slots) merge the global rows' and keys' chunk sums
+// (global_merge, one item a wave): work of its own, which no key block waits
+// for (those combine the global rows' statistics themselves).
+template <bool MF>
 __global__ __launch_bounds__(NTH) void dkv_kernel(BwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ Meta mt[2];
+  const int nblk = p.B * p.blocks_per_b;
+  if (MF && (int)blockIdx.x >= nblk) {
+    global_merge(p, (int64_t)((int)blockIdx.x - nblk) * (NTH / 64) + (threadIdx.x >> 6), threadIdx.x & 63);
+    return;
+  }
   int b, h, rho, blk;
-  decode_block(p, xcd_remap(blockIdx.x, gridDim.x), b, h, rho, blk);
-  dkv_local(p, b, h, rho, blk, sm, mt);
+  decode_block(p, xcd_remap(blockIdx.x, nblk), b, h, rho, blk);
+  dkv_local<MF>(p, b, h, rho, blk, sm, mt);
 }
 
 __global__ __launch_bounds__(NTH) void global_chunk_kernel(BwParams p) {
@@ -1538,11 +1667,10 @@ __global__ __launch_bounds__(NTH) void global_chunk_kernel(BwParams p) {
 }
 
 // One wave per (b, h, global index): combines the chunk sums (offsets in log2
-// units) into dQg (and the row's log-sum-exp, log2 units, and D) and the
-// global key's dK, dV.  Lane = d.
-__global__ __launch_bounds__(NTH) void global_merge_kernel(BwParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * (NTH / 64) + (threadIdx.x >> 6);
+// units) into dQg and the global key's dK, dV, and (unless the merge runs
+// beside the dK/dV work, which combines them itself) the row's log-sum-exp
+// (log2 units) and D.  Lane = d.
+__device__ void global_merge(const BwParams& p, int64_t item, int lane) {
   if (item >= (int64_t)p.B * p.H * p.max_global) return;
   const int gi = (int)(item % p.max_global);
   const int64_t bh = item / p.max_global;
@@ -1574,14 +1702,20 @@ __global__ __launch_bounds__(NTH) void global_merge_kernel(BwParams p) {
     sv += k[sp * 128 + 64 + lane];
   }
   const int64_t ro = (bh * n + pos) * 128 + lane * 2;
-  const float dov = (float)*reinterpret_cast<const __bf16*>(p.dO + ro);
-  float dd = dov * (float)*reinterpret_cast<const __bf16*>(p.O + ro);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) dd += __shfl_xor(dd, o);
   *reinterpret_cast<__bf16*>(p.dQg + ro) = (__bf16)(L > 0.0f ? p.scale * a / L : 0.0f);
   *reinterpret_cast<__bf16*>(p.dK + ro) = (__bf16)(p.scale * sk);
   *reinterpret_cast<__bf16*>(p.dV + ro) = (__bf16)sv;
-  if (lane == 0) p.stats[bh * n + pos] = make_float2(L > 0.0f ? mm + log2f(L) : INFINITY, dd);
+  if (!p.merge_fold) {
+    const float dov = (float)*reinterpret_cast<const __bf16*>(p.dO + ro);
+    float dd = dov * (float)*reinterpret_cast<const __bf16*>(p.O + ro);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) dd += __shfl_xor(dd, o);
+    if (lane == 0) p.stats[bh * n + pos] = make_float2(L > 0.0f ? mm + log2f(L) : INFINITY, dd);
+  }
+}
+
+__global__ __launch_bounds__(NTH) void global_merge_kernel(BwParams p) {
+  global_merge(p, (int64_t)blockIdx.x * (NTH / 64) + (threadIdx.x >> 6), threadIdx.x & 63);
 }
 
 }  // namespace mk

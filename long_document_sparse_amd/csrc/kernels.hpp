@@ -128,6 +128,7 @@ struct Params {
   int32_t* tile_cnt;       // [B][H][nqt]: finished key slices of a query tile (0 between forwards)
   int32_t* ready;          // [B]: epoch of the last forward whose compaction of the row is done
   int32_t* fault;          // sticky: set when a workgroup gave up waiting for its row
+  uint64_t* ready_cnt;     // [B] or null: (epoch << 32) | global count, published beside ready
   int32_t epoch;           // this forward's number (> 0): what every workgroup waits for
   int32_t publish;         // what the compaction publishes (= epoch, except in a fault test)
   int32_t spin_limit;      // polls before a wait for a row gives up
@@ -215,6 +216,9 @@ struct SlotLay {
 // only after the epoch (or the slice counter) has been seen, behind a barrier,
 // so they observe what the release published.
 __device__ __forceinline__ int coherent_load(const int32_t* ptr) {
+  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t coherent_load64(const uint64_t* ptr) {
   return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float coherent_loadf(const float* ptr) {
@@ -615,7 +619,14 @@ __device__ void compact_row(const Params& p, int b, uint8_t* smem) {
   // this XCD's caches)
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (tid == 0) __hip_atomic_store(p.ready + b, p.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    __hip_atomic_store(p.ready + b, p.publish, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    // the epoch and the count in one word, for readers that want both from a
+    // single load (ordered after the release above)
+    if (p.ready_cnt)
+      __hip_atomic_store(p.ready_cnt + b, ((uint64_t)(uint32_t)p.publish << 32) | (uint32_t)carry,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Wait until batch row b is compacted for this forward.  The compaction

@@ -84,6 +84,7 @@ struct lwattn_plan_s {
   float* bpart_ml = nullptr;
   int32_t* bcnt = nullptr;
   int32_t* ready = nullptr;   // [B] epoch of the last compaction of each batch row
+  uint64_t* ready_cnt = nullptr;   // [B] (epoch << 32) | global count, written by the backward's compaction
   int32_t* fault = nullptr;   // sticky: a workgroup gave up waiting for its row
   int32_t epoch = 0;          // forwards launched (kept in 1 .. INT32_MAX - 1)
   bool inject_timeout = false; // fault test: the next forward's waits give up
@@ -92,11 +93,13 @@ struct lwattn_plan_s {
   // backward: 64-row blocks per head (all residue classes), per-row statistics
   int32_t* head_blk64 = nullptr;
   int blocks64_per_b = 0;
+  int ncu = 256;   // compute units of the plan's device
   float2* stats = nullptr;
   // bf16 backward: the global rows' and global keys' sums over position chunks
   int gsplit = 0, gchunk = 0;
   float* gq = nullptr;
   float* gk = nullptr;
+  float* gml = nullptr;
   // timing
   int timing_cap = 0;
   int timing_calls = 0;
@@ -122,6 +125,7 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->bpart_ml);
   (void)hipFree(p->bcnt);
   (void)hipFree(p->ready);
+  (void)hipFree(p->ready_cnt);
   (void)hipFree(p->fault);
   (void)hipFree(p->head_stride);
   (void)hipFree(p->head_blk);
@@ -129,6 +133,7 @@ static void free_plan(lwattn_plan_s* p) {
   (void)hipFree(p->stats);
   (void)hipFree(p->gq);
   (void)hipFree(p->gk);
+  (void)hipFree(p->gml);
   for (hipEvent_t e : p->events) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->bw_events) (void)hipEventDestroy(e);
   delete p;
@@ -520,6 +525,7 @@ static void forward_params(lwk::Params& prm, const lwattn_config& c, const FwdGe
                            const int32_t* stride, const int32_t* blk, const void* Q, const void* K, const void* V,
                            const void* Qg, const void* Kg, const void* Vg, const float* lmask, const float* gmask,
                            void* O, int32_t epoch) {
+  std::memset(&prm, 0, sizeof(prm));
   prm.Q = (const uint8_t*)Q;
   prm.K = (const uint8_t*)K;
   prm.V = (const uint8_t*)V;
@@ -714,6 +720,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, hip_device) == hipSuccess && v > 0)
       ncu = v;
   }
+  p->ncu = ncu;
   std::vector<int32_t> stride(H), blk(H + 1, 0), blk64(H + 1, 0);
   FwdGeom g;
   if (!forward_geometry(p->cfg, p->gap.data(), ncu, g, stride.data(), blk.data())) {
@@ -766,6 +773,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->bpart_ml, bpart_ml_floats(g) * 4);
   alloc((void**)&p->bcnt, std::max<size_t>(bcnt_words(g), 1) * 4);
   alloc((void**)&p->ready, (size_t)B * 4);
+  alloc((void**)&p->ready_cnt, (size_t)B * 8);
   alloc((void**)&p->fault, 4);
   alloc((void**)&p->head_stride, (size_t)H * 4);
   alloc((void**)&p->head_blk, (size_t)(H + 1) * 4);
@@ -787,6 +795,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
     const size_t rows = (size_t)B * H * cfg->max_global * p->gsplit;
     alloc((void**)&p->gq, rows * 68 * 4);
     alloc((void**)&p->gk, rows * 128 * 4);
+    alloc((void**)&p->gml, (size_t)B * H * cfg->max_global * ((p->gsplit + 1) / 2 * 2) * 2 * 4);
   }
   if (!ok) {
     free_plan(p);
@@ -799,6 +808,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
       (B > 0 && !hip_ok(hipMemset(p->gcnt, 0, (size_t)B * 4), "hipMemset")) ||
       !hip_ok(hipMemset(p->tile_cnt, 0, (size_t)B * H * (p->nqt > 0 ? p->nqt : 1) * 4), "hipMemset") ||
       (B > 0 && !hip_ok(hipMemset(p->ready, 0, (size_t)B * 4), "hipMemset")) ||
+      (B > 0 && !hip_ok(hipMemset(p->ready_cnt, 0, (size_t)B * 8), "hipMemset")) ||
       !hip_ok(hipMemset(p->fault, 0, 4), "hipMemset") ||
       !hip_ok(hipMemset(p->bcnt, 0, std::max<size_t>(bcnt_words(g), 1) * 4), "hipMemset") ||
       !hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize")) {
@@ -1039,7 +1049,8 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   if (!hip_ok(hipSetDevice(p->device), "hipSetDevice")) return LWATTN_E_DEVICE;
 
   // 1. the global-index compaction (published under a fresh epoch, so that the
-  //    next forward's waits still see a new number)
+  //    next forward's waits still see a new number): inside the dQ launch for
+  //    bf16, a launch of its own for fp32
   lwk::Params cp;
   std::memset(&cp, 0, sizeof(cp));
   cp.lmask = lmask;
@@ -1049,6 +1060,7 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   cp.gcnt = p->gcnt;
   cp.status = p->status;
   cp.ready = p->ready;
+  cp.ready_cnt = p->ready_cnt;
   cp.fault = p->fault;
   p->epoch = p->epoch >= INT32_MAX - 1 ? 1 : p->epoch + 1;
   cp.epoch = p->epoch;
@@ -1071,9 +1083,7 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
     launched |= (uint8_t)(1u << k);
     return p->bw_events[(size_t)p->bw_calls * 2 * kNumBwKernels + 2 * k + e];
   };
-  hipExtLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream,
-                        ev(0, 0), ev(0, 1), 0u, cp);
-  if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
+  cp.spin_limit = (1 << 18) + (int32_t)(c.n >> 2);   // as the forward's waits
 
   lwk::bw::BwParams bp;
   bp.Q = (const uint8_t*)Q;
@@ -1099,6 +1109,10 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   bp.stats = p->stats;
   bp.gq = p->gq;
   bp.gk = p->gk;
+  bp.gml = p->gml;
+  bp.gspad = (p->gsplit + 1) / 2 * 2;
+  bp.comp_fold = 0;
+  bp.merge_fold = 0;
   bp.gsplit = p->gsplit;
   bp.gchunk = p->gchunk;
   bp.B = c.B;
@@ -1113,8 +1127,9 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
   if (c.dtype == LWATTN_BF16) {
     // 2. dQ, dQg (zero) and the local rows' statistics; 3. the chunk sums of
-    // the global rows and keys; 4. their merge: dQg, the global rows'
-    // statistics, the global keys' dK, dV; 5. dK, dV (window), dKg, dVg
+    // the global rows and keys; 4. their merge: dQg, the global keys' dK, dV
+    // (and the global rows' statistics, unless it runs inside 5); 5. dK, dV
+    // (window), dKg, dVg
     namespace mk = lwk::bw::mk;
     const int64_t nblk = (int64_t)c.B * p->blocks64_per_b;
     const int64_t nchunk = (int64_t)c.B * c.H * bp.ntg * p->gsplit;
@@ -1122,21 +1137,45 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
     // tiles are read through 32-bit buffer offsets over a head's n rows
     if (nchunk > INT32_MAX || nmerge > INT32_MAX || (int64_t)c.n * 128 >= lwk::OOB_OFF)
       return LWATTN_E_UNSUPPORTED;
-    (void)hipFuncSetAttribute((const void*)mk::dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DQ_SMEM);
-    (void)hipFuncSetAttribute((const void*)mk::dkv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DKV_SMEM);
+    for (const void* f : {(const void*)mk::dq_kernel<true>, (const void*)mk::dq_kernel<false>})
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DQ_SMEM);
+    for (const void* f : {(const void*)mk::dkv_kernel<true>, (const void*)mk::dkv_kernel<false>})
+      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DKV_SMEM);
     (void)hipFuncSetAttribute((const void*)mk::global_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               mk::GS_SMEM);
-    hipExtLaunchKernelGGL(mk::dq_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DQ_SMEM, stream, ev(1, 0),
-                          ev(1, 1), 0u, bp);
-    if (nchunk > 0) {
+    // When the dQ grid fits one round of workgroup slots (three per compute
+    // unit), its first B workgroups compact the batch rows and the others
+    // wait for their row before their global tiles: no launch of its own.  On
+    // longer grids the first round would stall on that wait, so the
+    // compaction is a launch of its own there (measured, base: 101 -> 94 us
+    // with both folds; qa and long slower folded).
+    bp.comp_fold = nblk <= 3 * (int64_t)p->ncu && c.B <= nblk ? 1 : 0;
+    if (!bp.comp_fold)
+      hipExtLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream,
+                            ev(0, 0), ev(0, 1), 0u, cp);
+    hipExtLaunchKernelGGL(bp.comp_fold ? mk::dq_kernel<true> : mk::dq_kernel<false>, dim3((uint32_t)nblk),
+                          dim3(lwk::bw::NTH), mk::DQ_SMEM, stream, ev(1, 0), ev(1, 1), 0u, bp, cp);
+    if (nchunk > 0)
       hipExtLaunchKernelGGL(mk::global_chunk_kernel, dim3((uint32_t)nchunk), dim3(lwk::bw::NTH), mk::GS_SMEM,
                             stream, ev(2, 0), ev(2, 1), 0u, bp);
+    // The merge of the chunk sums runs in workgroups behind the key blocks of
+    // the dK/dV launch when the last round of that grid (two workgroups per
+    // compute unit) has the spare slots for them; otherwise (each merge
+    // workgroup would hold a key block's slot while it waits on memory) it is
+    // a launch of its own, which also leaves the global rows' statistics.
+    const int64_t dslots = 2 * (int64_t)p->ncu;
+    const int64_t mwg = nchunk > 0 ? nmerge : 0;
+    const int64_t spare = (nblk + dslots - 1) / dslots * dslots - nblk;
+    bp.merge_fold = mwg > 0 && mwg <= spare ? 1 : 0;
+    if (mwg > 0 && !bp.merge_fold)
       hipExtLaunchKernelGGL(mk::global_merge_kernel, dim3((uint32_t)nmerge), dim3(lwk::bw::NTH), 0, stream,
                             ev(3, 0), ev(3, 1), 0u, bp);
-    }
-    hipExtLaunchKernelGGL(mk::dkv_kernel, dim3((uint32_t)nblk), dim3(lwk::bw::NTH), mk::DKV_SMEM, stream,
-                          ev(4, 0), ev(4, 1), 0u, bp);
+    const int64_t ndkv = nblk + (bp.merge_fold ? mwg : 0);
+    hipExtLaunchKernelGGL(bp.merge_fold ? mk::dkv_kernel<true> : mk::dkv_kernel<false>, dim3((uint32_t)ndkv),
+                          dim3(lwk::bw::NTH), mk::DKV_SMEM, stream, ev(4, 0), ev(4, 1), 0u, bp);
   } else {
+    hipExtLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream,
+                          ev(0, 0), ev(0, 1), 0u, cp);
     // 2. dQ, dQg and the rows' statistics; 3. dK, dV, dKg, dVg
     (void)hipFuncSetAttribute((const void*)lwk::bw::dq_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DQ_SMEM);
     (void)hipFuncSetAttribute((const void*)lwk::bw::dkv_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::bw::DKV_SMEM);

@@ -117,9 +117,55 @@ def test_backward_kernel_timing(dtype):
     tot, calls = plan.timing_read_backward()
     plan.timing_disable()
     assert calls == 3
-    launched = (lw.BW_KERNELS if dtype == "bf16" else ("compact_kernel", "dq_kernel", "dkv_kernel"))
+    launched = (("dq_kernel", "global_chunk_kernel", "dkv_kernel") if dtype == "bf16"
+                else ("compact_kernel", "dq_kernel", "dkv_kernel"))
     for k in lw.BW_KERNELS:
         if k in launched:
             assert tot[k] > 0.0, (k, tot)
         else:
             assert tot[k] == 0.0, (k, tot)
+
+
+# Grids that take each mix of the backward's two folds on a 256-CU MI355X
+# (the compaction inside the dQ launch when its grid of 64-row blocks fits
+# three per compute unit; the merge of the chunk sums inside the dK/dV launch
+# when that grid's last round, two per compute unit, has room for it):
+# 13 x 64 = 832 blocks: compaction launched, merge folded (192 spare slots,
+# 65 merge workgroups); 8 x 64 = 512 blocks: compaction folded, merge
+# launched (no spare slot).  The kernel slots that recorded time say which.
+FOLD_CASES = [
+    # (B, H, n, window, n_global, compaction launched, merge launched)
+    (13, 1, 4096, 32, 20, True, False),
+    (8, 1, 4096, 32, 10, False, True),
+]
+
+
+@pytest.mark.parametrize("case", FOLD_CASES, ids=lambda c: f"B{c[0]}g{c[4]}")
+def test_backward_fold_modes(case):
+    B, H, n, window, ng, comp_launched, merge_launched = case
+    spec = workloads.custom(B, H, n, 64, window, "bf16", [0] * H, seed=33, n_global=ng,
+                            global_mode="random", pad_mode="per_batch", pad_hi=300)
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec, max_global=ng)
+    o = torch.empty_like(ts[0])
+    plan(*ts, lm, gm, out=o)
+    go = torch.from_numpy(_grad_out(x, 7)).to(ts[0].device).to(ts[0].dtype)
+    grads = tuple(torch.full_like(ts[0], float("nan")) for _ in range(6))
+    plan.timing_enable(2)
+    plan.backward(*ts, lm, gm, o, go, grads=grads)
+    tot, calls = plan.timing_read_backward()
+    plan.timing_disable()
+    assert plan.sync_status() == lw.OK
+    assert calls == 1
+    assert (tot["compact_kernel"] > 0.0) == comp_launched, tot
+    assert (tot["global_merge_kernel"] > 0.0) == merge_launched, tot
+    ins = [to_np64(t) for t in ts]
+    want = oracle.backward(*ins, x.lmask, x.gmask, to_np64(go), spec.window, spec.dilation, spec.scale)
+    for name, g, w in zip(NAMES, grads, want):
+        got = to_np64(g)
+        assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+        err = float(np.max(np.abs(got - w)))
+        ref = float(np.max(np.abs(w)))
+        say(f"fold modes {case}: {name}: max abs err {err:.3e}, max |g| {ref:.3e}")
+        assert err <= TOL["bf16"] * ref, name

@@ -317,11 +317,13 @@ lwattn_status lwattn_timing_read_backward(lwattn_plan_t plan, float* ms, int32_t
 lwattn_status lwattn_timing_disable(lwattn_plan_t plan);
 
 /* Testing aid for the failure path of the in-kernel wait (for test code only).
- * In the next forward of `plan`, the row compactions publish a number the
- * other workgroups do not wait for, and their waits give up after 64 polls:
- * every workgroup still exits normally, O is undefined, and
- * lwattn_sync_status reports LWATTN_E_DEVICE from then on (the plan is then
- * to be destroyed).  LWATTN_E_INVALID for a null plan. */
+ * In the next forward of `plan` (or bf16 backward, whichever comes first), the
+ * row compactions publish a number the other workgroups do not wait for, and
+ * their waits give up after 64 polls: every workgroup still exits normally,
+ * the outputs are undefined, and lwattn_sync_status reports LWATTN_E_DEVICE
+ * from then on (the plan is then to be destroyed).  A backward whose
+ * compaction is a launch of its own has no such wait and is unaffected.
+ * LWATTN_E_INVALID for a null plan. */
 lwattn_status lwattn_test_inject_wait_timeout(lwattn_plan_t plan);
 
 /* Allocation-free forward, for callers that cannot allocate device memory:

@@ -87,7 +87,7 @@ struct lwattn_plan_s {
   uint64_t* ready_cnt = nullptr;   // [B] (epoch << 32) | global count, written by the backward's compaction
   int32_t* fault = nullptr;   // sticky: a workgroup gave up waiting for its row
   int32_t epoch = 0;          // forwards launched (kept in 1 .. INT32_MAX - 1)
-  bool inject_timeout = false; // fault test: the next forward's waits give up
+  bool inject_timeout = false; // fault test: the next forward's (or bf16 backward's) waits give up
   int32_t* head_stride = nullptr;
   int32_t* head_blk = nullptr;
   // backward: 64-row blocks per head (all residue classes), per-row statistics
@@ -1084,6 +1084,13 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
     return p->bw_events[(size_t)p->bw_calls * 2 * kNumBwKernels + 2 * k + e];
   };
   cp.spin_limit = (1 << 18) + (int32_t)(c.n >> 2);   // as the forward's waits
+  if (p->inject_timeout && c.dtype == LWATTN_BF16) {
+    // fault test: the rows are published under another number and the dQ
+    // workgroups that wait for them (compaction inside dQ) give up at once
+    p->inject_timeout = false;
+    cp.publish = -1;
+    cp.spin_limit = 64;
+  }
 
   lwk::bw::BwParams bp;
   bp.Q = (const uint8_t*)Q;

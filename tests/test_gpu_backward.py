@@ -169,3 +169,39 @@ def test_backward_fold_modes(case):
         ref = float(np.max(np.abs(w)))
         say(f"fold modes {case}: {name}: max abs err {err:.3e}, max |g| {ref:.3e}")
         assert err <= TOL["bf16"] * ref, name
+
+
+def test_backward_folded_wait_timeout_is_reported_not_hung():
+    """The dQ launch's wait for the compaction inside it is bounded: under the
+    library's fault-test hook (rows published under a number nobody waits for,
+    a poll limit of 64) every workgroup still exits and the fault is reported,
+    stickily; the same inputs on a fresh plan give the oracle's gradients."""
+    spec = workloads.custom(2, 2, 333, 64, 40, "bf16", [0, 2], seed=21, n_global=5,
+                            global_mode="random", pad_mode="per_batch", pad_hi=80)
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    go = torch.from_numpy(_grad_out(x, 3)).to(ts[0].device).to(ts[0].dtype)
+    plan = make_plan(spec, max_global=5)
+    o = torch.empty_like(ts[0])
+    plan(*ts, lm, gm, out=o)
+    assert plan.sync_status() == lw.OK
+    grads = tuple(torch.empty_like(ts[0]) for _ in range(6))
+    lib = lw.load_library()
+    assert lib.lwattn_test_inject_wait_timeout(plan.handle) == lw.OK
+    plan.backward(*ts, lm, gm, o, go, grads=grads)
+    assert plan.sync_status() == lw.E_DEVICE
+    plan.close()
+    fresh = make_plan(spec, max_global=5)
+    o2 = torch.empty_like(ts[0])
+    fresh(*ts, lm, gm, out=o2)
+    grads = tuple(torch.full_like(ts[0], float("nan")) for _ in range(6))
+    fresh.backward(*ts, lm, gm, o2, go, grads=grads)
+    assert fresh.sync_status() == lw.OK
+    ins = [to_np64(t) for t in ts]
+    want = oracle.backward(*ins, x.lmask, x.gmask, to_np64(go), spec.window, spec.dilation, spec.scale)
+    for name, g, w in zip(NAMES, grads, want):
+        got = to_np64(g)
+        assert np.all(np.isfinite(got)), name
+        ref = float(np.max(np.abs(w)))
+        assert float(np.max(np.abs(got - w))) <= TOL["bf16"] * max(ref, 1e-30), name
+    fresh.close()

@@ -291,7 +291,7 @@ def run_causal_backward(args, spec, x, ts, lm, plan):
     from long_document_sparse_amd import flops as fl
     from long_document_sparse_amd import lwattn
     if spec.dtype != "bf16":
-        raise SystemExit("the causal variant runs on bf16 storage")
+        raise SystemExit("the causal variant's backward runs on bf16 storage")
     q, k, v = ts[0], ts[1], ts[2]
     g = torch.Generator().manual_seed(5)
     do = (torch.randn(q.shape, generator=g) / 8).to(q.device).to(torch.bfloat16)
@@ -357,8 +357,8 @@ def run_causal(args, spec, x, ts, lm, plan):
     import torch
     from long_document_sparse_amd import flops as fl
     from long_document_sparse_amd import lwattn
-    if spec.dtype != "bf16":
-        raise SystemExit("the causal variant runs on bf16 storage")
+    if spec.dtype not in ("bf16", "f16"):
+        raise SystemExit("the causal variant runs on 16-bit storage (bf16 or f16)")
     q, k, v = ts[0], ts[1], ts[2]
     o = torch.empty_like(q)
     plan.forward_causal(q, k, v, lm, out=o)
@@ -447,8 +447,8 @@ def run_blocksparse(args, spec, x, ts, lm, plan):
     import torch
     from long_document_sparse_amd import flops as fl
     from long_document_sparse_amd import lwattn, workloads
-    if spec.dtype != "bf16":
-        raise SystemExit("block-sparse attention runs on bf16 storage")
+    if spec.dtype not in ("bf16", "f16"):
+        raise SystemExit("block-sparse attention runs on 16-bit storage (bf16 or f16)")
     kw = workloads.BSPARSE_LAYOUT
     layout = workloads.blocksparse_layout(spec.H, spec.n, seed=spec.seed, **kw)
     rowptr, cols = workloads.layout_csr(layout)
@@ -736,8 +736,8 @@ def main():
         args.workload = {"causal": "charlm", "causal_backward": "charlm", "blocksparse": "bsparse", "layer": "ftlayer"}.get(args.which, "base")
     spec = workloads.named(args.workload)
     if args.dtype is not None:
-        if args.which not in ("forward", "layer"):
-            raise SystemExit("--dtype applies to the forward and layer passes")
+        if args.which not in ("forward", "layer", "causal", "blocksparse"):
+            raise SystemExit("--dtype applies to the forward, layer, causal and blocksparse passes")
         import dataclasses
         spec = dataclasses.replace(spec, dtype=args.dtype)
     x = workloads.generate(spec)

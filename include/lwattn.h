@@ -50,9 +50,10 @@ typedef struct lwattn_plan_s* lwattn_plan_t;
  * encoder guide, implementation scope: the float, half and bfloat16
  * instantiations).  Scores, softmax and the output accumulation are always
  * float32; with 16-bit storage the matrix cores take the probabilities rounded
- * to the storage type.  LWATTN_F16 (IEEE half) runs the forward
- * (lwattn_forward, lwattn_forward_noalloc) and the encoder layer; the backward,
- * causal and block-sparse calls return LWATTN_E_UNSUPPORTED for it. */
+ * to the storage type.  LWATTN_F16 (IEEE half) runs the forwards
+ * (lwattn_forward, lwattn_forward_noalloc, lwattn_forward_causal,
+ * lwattn_forward_blocksparse) and the encoder layer; the backwards return
+ * LWATTN_E_UNSUPPORTED for it. */
 typedef enum { LWATTN_F32 = 0, LWATTN_BF16 = 1, LWATTN_F16 = 2 } lwattn_dtype;
 
 typedef enum {
@@ -129,8 +130,9 @@ lwattn_status lwattn_forward(lwattn_plan_t plan,
  * softmax of scale <Q_i, K_j> over them, O_i = sum_j p_j V_j; a row with
  * lmask 0 gets O_i = 0.  The plan's max_global and any global mask play no
  * part.  Per-layer window sizes: one plan per window size.
- * Q, K, V, O: [B][H][n][64] bf16, 16-byte aligned, device memory; lmask float32
- * [B][n], 4-byte aligned.  Every element of O is written.  Enqueued on
+ * Q, K, V, O: [B][H][n][64] in the plan's 16-bit storage type (bf16 or fp16),
+ * 16-byte aligned, device memory; lmask float32 [B][n], 4-byte aligned.  Every
+ * element of O is written.  Enqueued on
  * `stream` (one kernel launch, no allocation, no host sync); it uses no plan
  * workspace, so it may overlap other calls of the same plan.
  * Errors: LWATTN_E_INVALID for a null plan or pointer or a misaligned one;
@@ -169,7 +171,8 @@ lwattn_status lwattn_backward_causal(lwattn_plan_t plan, const void* Q, const vo
  * listing (list a block once); a block index outside [0, nb) contributes no
  * key; a list longer than nb is cut to its first nb entries; offsets are
  * clamped into [0, nnz], so a malformed rowptr (negative, decreasing or past
- * nnz) never reads outside cols (its lists come out empty or cut).  Q, K, V, O: [B][H][n][64] bf16, 16-byte aligned;
+ * nnz) never reads outside cols (its lists come out empty or cut).  Q, K, V, O: [B][H][n][64] in the
+ * plan's 16-bit storage type (bf16 or fp16), 16-byte aligned;
  * lmask float32 [B][n].  Every element of O is written.  One kernel launch on
  * `stream`, no allocation, no host sync, no plan workspace.
  * Errors: LWATTN_E_INVALID for a null plan or pointer, a misaligned one or

@@ -919,6 +919,28 @@ __device__ __forceinline__ bf16x8 acc_frag(const f32x16& x, int c2) {
 
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// The same fragments for either 16-bit storage type S (bf16 or fp16): the
+// reads move raw 16-bit values, so a bf16-typed fragment is reinterpreted; the
+// accumulator's values are rounded to S.
+template <typename S>
+__device__ __forceinline__ svec<S, 8> as_frag(const bf16x8& f) {
+  return __builtin_bit_cast(svec<S, 8>, f);
+}
+template <typename S>
+__device__ __forceinline__ void row_frags_s(svec<S, 8> (&f)[4], const uint8_t* head, int pos, int h) {
+  bf16x8 r[4];
+  row_frags(r, head, pos, h);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) f[c] = as_frag<S>(r[c]);
+}
+template <typename S>
+__device__ __forceinline__ svec<S, 8> acc_frag_s(const f32x16& x, int c2) {
+  svec<S, 8> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (S)x[8 * c2 + j];
+  return f;
+}
+
 // Row pieces of a [.][64] gradient held as two d-block accumulators (element
 // (d, l % 32)) to global memory: lane writes d = 32 db + 8 a + 4 h .. +3.
 __device__ __forceinline__ void store_dT(uint8_t* rowptr, const f32x16 (&x)[2], float mul, int h) {
@@ -930,6 +952,20 @@ __device__ __forceinline__ void store_dT(uint8_t* rowptr, const f32x16 (&x)[2], 
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (__bf16)(x[db][4 * a + e] * mul);
       *reinterpret_cast<bf16x4*>(rowptr + (32 * db + 8 * a + 4 * h) * 2) = v;
+    }
+}
+
+// store_dT rounding to either 16-bit storage type S.
+template <typename S>
+__device__ __forceinline__ void store_dT_s(uint8_t* rowptr, const f32x16 (&x)[2], float mul, int h) {
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      svec<S, 4> v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (S)(x[db][4 * a + e] * mul);
+      *reinterpret_cast<svec<S, 4>*>(rowptr + (32 * db + 8 * a + 4 * h) * 2) = v;
     }
 }
 

@@ -1,4 +1,4 @@
-// Block-sparse attention over 64 x 64 blocks, bf16 storage, on the matrix
+// Block-sparse attention over 64 x 64 blocks, 16-bit storage (bf16 or fp16), on the matrix
 // cores.
 //
 // xFormers' attention-mask notes (gitcode xformers page): a per-head layout
@@ -38,6 +38,7 @@ struct BsParams {
 // dynamic LDS: three K, V tile pairs, three Stage records, then nb column indices
 constexpr int SMEM_BASE = 6 * TB + 3 * (int)sizeof(bw::mk::Stage);
 
+template <typename S>
 __device__ void bs_block(const BsParams& p, int b, int h, int qb, uint8_t* sm, TMeta (&tm)[3]) {
   bw::mk::Stage* stg = reinterpret_cast<bw::mk::Stage*>(sm + 6 * TB);
   int32_t* colsl = reinterpret_cast<int32_t*>(sm + SMEM_BASE);
@@ -58,8 +59,8 @@ __device__ void bs_block(const BsParams& p, int b, int h, int qb, uint8_t* sm, T
   const int row = 32 * rq + qi;
   const int rps = P0 + row < n ? P0 + row : -1;
   const bool rvalid = rps >= 0 && p.lmask[(int64_t)b * n + rps] != 0.0f;
-  bf16x8 qf[4];
-  row_frags(qf, p.Q + hoff, rps, h32);
+  svec<S, 8> qf[4];
+  row_frags_s<S>(qf, p.Q + hoff, rps, h32);
   wait_all_loads();   // the column list, the row's fragments
   __syncthreads();    // the column list is visible
 
@@ -114,21 +115,23 @@ __device__ void bs_block(const BsParams& p, int b, int h, int qb, uint8_t* sm, T
     if (p.causal) cm = kb < qb ? 0xFFFFFFFFu : (kb == qb ? bit_range_v(0, row - 32 * kq + 1) : 0u);
     const uint32_t M = rvalid ? vb & cm : 0u;
     const bool full = all_valid && vb == 0xFFFFFFFFu && (!p.causal || kb < qb);
-    cz::pv_tile(acc, m, l, tK, tK + TB, qf, M, full, c, kq, lane);
+    cz::pv_tile<S>(acc, m, l, tK, tK + TB, qf, M, full, c, kq, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && rps >= 0)
-    store_dT(p.O + hoff + (int64_t)rps * 128, acc, rvalid && l > 0.0f ? 1.0f / l : 0.0f, h32);
+    store_dT_s<S>(p.O + hoff + (int64_t)rps * 128, acc, rvalid && l > 0.0f ? 1.0f / l : 0.0f, h32);
 }
 
 // Neighbouring query blocks of a head list mostly the same key blocks: the
 // logical order keeps them on one XCD.
+// S: the 16-bit storage type (bf16 or fp16).
+template <typename S>
 __global__ __launch_bounds__(NTH) void blocksparse_kernel(BsParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ TMeta tm[3];
   const int lb = xcd_remap(blockIdx.x, gridDim.x);
   const int qb = lb % p.nb, bh = lb / p.nb;
-  bs_block(p, bh / p.H, bh % p.H, qb, sm, tm);
+  bs_block<S>(p, bh / p.H, bh % p.H, qb, sm, tm);
 }
 
 }  // namespace bsp

@@ -1,4 +1,5 @@
-// Causal variant of the window attention, bf16 storage, on the matrix cores.
+// Causal variant of the window attention, on the matrix cores: the forward for
+// 16-bit storage (bf16 or fp16), the backward for bf16.
 //
 // "LongFormer: The Long-Document Transformer" (reading notes), section
 // Implementation: an autoregressive language model uses the dilated sliding
@@ -40,13 +41,15 @@ struct CzParams {
 // One key tile of the running-softmax sum O^T += V^T P^T (lane = row, with the
 // row's Q fragments qf; keys 32 kq .. of the tile).  Bit k of M: key
 // 32 kq + k counts for the lane's row (ignored when `full`).
+// S: the 16-bit storage type (bf16 or fp16), the matrix cores' operand type.
+template <typename S>
 __device__ __forceinline__ void pv_tile(f32x16 (&acc)[2], float& m, float& l, const uint8_t* tK,
-                                        const uint8_t* tV, const bf16x8 (&qf)[4], uint32_t M, bool full,
+                                        const uint8_t* tV, const svec<S, 8> (&qf)[4], uint32_t M, bool full,
                                         float c, int kq, int lane) {
   const int h32 = lane >> 5, qi = lane & 31;
   f32x16 x = {};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) x = mfma_bf16(frag_row(tK, 32 * kq + qi, h32, k), qf[k], x);
+  for (int k = 0; k < 4; ++k) x = mfma16(as_frag<S>(frag_row(tK, 32 * kq + qi, h32, k)), qf[k], x);
   if (!full) mask_half(x, M, h32);
   float mr = x[0];
 #pragma unroll
@@ -70,9 +73,10 @@ __device__ __forceinline__ void pv_tile(f32x16 (&acc)[2], float& m, float& l, co
   }
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    const bf16x8 pb = acc_frag(x, c2);
+    const svec<S, 8> pb = acc_frag_s<S>(x, c2);
 #pragma unroll
-    for (int db = 0; db < 2; ++db) acc[db] = mfma_bf16(frag_tr(tV + 32 * kq * 128, c2, db, lane), pb, acc[db]);
+    for (int db = 0; db < 2; ++db)
+      acc[db] = mfma16(as_frag<S>(frag_tr(tV + 32 * kq * 128, c2, db, lane)), pb, acc[db]);
   }
 }
 
@@ -83,6 +87,7 @@ __device__ __forceinline__ bool interior(int kt, int r) { return kt >= 1 && T * 
 
 constexpr int SMEM = 6 * TB + 3 * (int)sizeof(bw::mk::Stage);   // three K, V tile pairs, three Stage records
 
+template <typename S>
 __device__ void causal_block(const CzParams& p, int b, int h, int rho, int blk, uint8_t* sm, TMeta (&tm)[3]) {
   bw::mk::Stage* stg = reinterpret_cast<bw::mk::Stage*>(sm + 6 * TB);
   float* xch = reinterpret_cast<float*>(sm);
@@ -122,8 +127,8 @@ __device__ void causal_block(const CzParams& p, int b, int h, int rho, int blk, 
   const int row = 32 * rq + qi;
   const int rps = I0 + row < nr ? rho + (I0 + row) * s : -1;
   const bool rvalid = rps >= 0 && p.lmask[(int64_t)b * n + rps] != 0.0f;
-  bf16x8 qf[4];
-  row_frags(qf, p.Q + hoff, rps, h32);
+  svec<S, 8> qf[4];
+  row_frags_s<S>(qf, p.Q + hoff, rps, h32);
   wait_all_loads();   // the row's fragments and tile 0
   if (nt > 1) prefetch(1, 1);
 
@@ -152,19 +157,20 @@ __device__ void causal_block(const CzParams& p, int b, int h, int rho, int blk, 
     const int a = row - T * kt - 32 * kq;
     const uint32_t M = rvalid ? kb & bit_range_v(a, a + r + 1) : 0u;
     const bool full = all_valid && kb == 0xFFFFFFFFu && interior(kt, r);
-    pv_tile(acc, m, l, tK, tK + TB, qf, M, full, c, kq, lane);
+    pv_tile<S>(acc, m, l, tK, tK + TB, qf, M, full, c, kq, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && rps >= 0)
-    store_dT(p.O + hoff + (int64_t)rps * 128, acc, rvalid && l > 0.0f ? 1.0f / l : 0.0f, h32);
+    store_dT_s<S>(p.O + hoff + (int64_t)rps * 128, acc, rvalid && l > 0.0f ? 1.0f / l : 0.0f, h32);
 }
 
+template <typename S>
 __global__ __launch_bounds__(NTH) void causal_kernel(CzParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ TMeta tm[3];
   int b, h, rho, blk;
   bw::decode_block(p, xcd_remap(blockIdx.x, gridDim.x), b, h, rho, blk);
-  causal_block(p, b, h, rho, blk, sm, tm);
+  causal_block<S>(p, b, h, rho, blk, sm, tm);
 }
 
 // ---------------------------------------------------------------------------

@@ -912,7 +912,7 @@ lwattn_status lwattn_forward_causal(lwattn_plan_t p, const void* Q, const void* 
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
-  if (c.dtype != LWATTN_BF16) return LWATTN_E_UNSUPPORTED;
+  if (c.dtype == LWATTN_F32) return LWATTN_E_UNSUPPORTED;
   // tiles are read through 32-bit buffer offsets over a head's n rows
   if ((int64_t)c.n * 128 >= lwk::OOB_OFF) return LWATTN_E_UNSUPPORTED;
   const void* ptrs[] = {Q, K, V, O};
@@ -936,9 +936,9 @@ lwattn_status lwattn_forward_causal(lwattn_plan_t p, const void* Q, const void* 
   cp.scale = c.scale;
   const int64_t grid = (int64_t)c.B * p->blocks64_per_b;
   if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
-  (void)hipFuncSetAttribute((const void*)lwk::cz::causal_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            lwk::cz::SMEM);
-  hipLaunchKernelGGL(lwk::cz::causal_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::SMEM, stream, cp);
+  const auto kern = c.dtype == LWATTN_F16 ? lwk::cz::causal_kernel<_Float16> : lwk::cz::causal_kernel<__bf16>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::cz::SMEM);
+  hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::SMEM, stream, cp);
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   return LWATTN_OK;
 }
@@ -996,7 +996,7 @@ lwattn_status lwattn_forward_blocksparse(lwattn_plan_t p, const void* Q, const v
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
-  if (c.dtype != LWATTN_BF16) return LWATTN_E_UNSUPPORTED;
+  if (c.dtype == LWATTN_F32) return LWATTN_E_UNSUPPORTED;
   // tiles are read through 32-bit buffer offsets over a head's n rows; the
   // column list of a query block lives in LDS
   const int64_t nb = ((int64_t)c.n + 63) / 64;
@@ -1026,9 +1026,10 @@ lwattn_status lwattn_forward_blocksparse(lwattn_plan_t p, const void* Q, const v
   const int64_t grid = (int64_t)c.B * c.H * nb;
   if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
   const uint32_t smem = (uint32_t)(lwk::bsp::SMEM_BASE + 4 * nb);
-  (void)hipFuncSetAttribute((const void*)lwk::bsp::blocksparse_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  hipLaunchKernelGGL(lwk::bsp::blocksparse_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), smem, stream, bp);
+  const auto kern =
+      c.dtype == LWATTN_F16 ? lwk::bsp::blocksparse_kernel<_Float16> : lwk::bsp::blocksparse_kernel<__bf16>;
+  (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(lwk::bw::NTH), smem, stream, bp);
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   return LWATTN_OK;
 }

@@ -202,7 +202,7 @@ class Plan:
 
     def forward_causal(self, q, k, v, lmask, out=None, stream=None):
         """Enqueue the causal variant (window taps at or before each row, no
-        global attention; bf16 plans); returns O (allocated if `out` is None)."""
+        global attention; bf16 or fp16 plans); returns O (allocated if `out` is None)."""
         import torch
         tdt = torch_dtype(self.dtype)
         for t, name in ((q, "q"), (k, "k"), (v, "v")):
@@ -248,7 +248,7 @@ class Plan:
         return dq, dk, dv
 
     def forward_blocksparse(self, q, k, v, lmask, rowptr, cols, causal=False, out=None, stream=None):
-        """Enqueue block-sparse attention over 64-blocks (bf16 plans): the
+        """Enqueue block-sparse attention over 64-blocks (bf16 or fp16 plans): the
         layout as CSR over (head, query block), int32 device tensors rowptr
         [H*nb + 1] and cols [nnz]; returns O (allocated if `out` is None)."""
         import torch

@@ -1,6 +1,7 @@
 """IEEE half (fp16) storage through the C ABI: the forward against the oracle,
-the allocation-free forward against the plan's, and the encoder layer against
-the oracle's layer.
+the allocation-free forward against the plan's, the causal and block-sparse
+forwards against the oracle's, and the encoder layer against the oracle's
+layer.
 
 Tolerance, from the arithmetic (as for bf16, with fp16's unit roundoff 2^-11
 in place of bf16's 2^-8): the oracle sees exactly the stored fp16 values; the
@@ -141,7 +142,7 @@ def test_f16_noalloc_matches_plan():
     assert torch.count_nonzero(status).item() == 0
 
 
-def test_f16_backward_causal_blocksparse_are_unsupported():
+def test_f16_backwards_are_unsupported():
     spec = workloads.custom(1, 2, 128, 64, 32, "f16", [0, 0], seed=36, n_global=1)
     x = workloads.generate(spec)
     ts, lm, gm = to_dev(x)
@@ -149,8 +150,9 @@ def test_f16_backward_causal_blocksparse_are_unsupported():
     o = plan(*ts, lm, gm)
     with pytest.raises(lw.LwattnError):
         plan.backward(*ts, lm, gm, o, o)
+    oc = plan.forward_causal(ts[0], ts[1], ts[2], lm)
     with pytest.raises(lw.LwattnError):
-        plan.forward_causal(ts[0], ts[1], ts[2], lm)
+        plan.backward_causal(ts[0], ts[1], ts[2], lm, oc, oc)
     plan.close()
 
 
@@ -190,3 +192,73 @@ def test_f16_layer_matches_oracle():
     assert np.all(np.isfinite(got))
     assert err.max() <= 5e-3
     layer.close()
+
+
+CAUSAL = [
+    # (B, H, n, window, dilation, pad_mode, pad_hi)
+    (2, 3, 333, 40, [0, 2, 5], "per_batch", 80),
+    (1, 2, 130, 400, [0, 0], "none", 0),          # window beyond the sequence
+    (2, 2, 257, 16, [1, 4], "scatter", 40),       # scattered pads
+    (1, 2, 1000, 300, [0, 1], "per_batch", 200),  # interior and edge tiles
+]
+
+
+@pytest.mark.parametrize("strong", [False, True], ids=["scaled", "strong"])
+@pytest.mark.parametrize("case", CAUSAL, ids=lambda c: f"B{c[0]}H{c[1]}n{c[2]}w{c[3]}{c[5]}")
+def test_f16_causal_matches_oracle(case, strong):
+    B, H, n, window, dil, pmode, phi = case
+    spec = workloads.custom(B, H, n, 64, window, "f16", dil, seed=31, n_global=0,
+                            pad_mode=pmode, pad_hi=phi, max_global=0)
+    say(f"f16 causal case {case} strong={strong}")
+    x = workloads.generate(spec, strong=strong)
+    q, k, v = (torch.from_numpy(a).to("cuda:0").to(torch.float16) for a in (x.Q, x.K, x.V))
+    lm = torch.from_numpy(x.lmask).to("cuda:0")
+    plan = make_plan(spec, max_global=0)
+    out = torch.full_like(q, float("nan"))
+    plan.forward_causal(q, k, v, lm, out=out)
+    torch.cuda.synchronize()
+    want = oracle.forward_causal(to_np64(q), to_np64(k), to_np64(v), x.lmask, window, dil, spec.scale)
+    got = to_np64(out)
+    assert np.all(np.isfinite(got))
+    rel = _rel_err(got, want)
+    say(f"f16 causal: rel err {rel:.3e}")
+    assert rel <= REL, rel
+    pad = x.lmask == 0
+    for b in range(B):
+        assert not np.any(got[b][:, pad[b]])
+
+
+BSPARSE = [
+    # (B, H, n, local, extra, causal, pad_mode, pad_hi)
+    (2, 3, 333, 2, 2, True, "per_batch", 80),
+    (1, 2, 257, 1, 3, False, "scatter", 40),
+    (2, 2, 1000, 4, 4, False, "per_batch", 200),
+]
+
+
+@pytest.mark.parametrize("strong", [False, True], ids=["scaled", "strong"])
+@pytest.mark.parametrize("case", BSPARSE, ids=lambda c: f"B{c[0]}H{c[1]}n{c[2]}l{c[3]}e{c[4]}{'c' if c[5] else ''}")
+def test_f16_blocksparse_matches_oracle(case, strong):
+    B, H, n, local, extra, causal, pmode, phi = case
+    spec = workloads.custom(B, H, n, 64, 0, "f16", [0] * H, seed=41, n_global=0,
+                            pad_mode=pmode, pad_hi=phi, max_global=0)
+    layout = workloads.blocksparse_layout(H, n, seed=9, local=local, extra=extra, causal=causal)
+    say(f"f16 block-sparse case {case} strong={strong}")
+    x = workloads.generate(spec, strong=strong)
+    q, k, v = (torch.from_numpy(a).to("cuda:0").to(torch.float16) for a in (x.Q, x.K, x.V))
+    lm = torch.from_numpy(x.lmask).to("cuda:0")
+    rowptr, cols = workloads.layout_csr(layout)
+    plan = make_plan(spec, max_global=0)
+    out = torch.full_like(q, float("nan"))
+    plan.forward_blocksparse(q, k, v, lm, torch.from_numpy(rowptr).to("cuda:0"),
+                             torch.from_numpy(cols).to("cuda:0"), causal=causal, out=out)
+    torch.cuda.synchronize()
+    want = oracle.forward_blocksparse(to_np64(q), to_np64(k), to_np64(v), x.lmask, layout, causal, spec.scale)
+    got = to_np64(out)
+    assert np.all(np.isfinite(got))
+    rel = _rel_err(got, want)
+    say(f"f16 block-sparse: rel err {rel:.3e}")
+    assert rel <= REL, rel
+    pad = x.lmask == 0
+    for b in range(B):
+        assert not np.any(got[b][:, pad[b]])

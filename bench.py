@@ -649,7 +649,7 @@ def run_backward(args, spec, x, ts, lm, gm, plan):
         raise SystemExit(f"backward failed: {lwattn.strerror(st)}")
     t_call = e0.elapsed_time(e1) * 1e-3 / args.steps        # s per backward, on the stream
     flop = fl.backward_flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
-    nbytes = fl.backward_bytes(x.lmask, x.gmask, spec.H, spec.d, 2 if spec.dtype == "bf16" else 4)
+    nbytes = fl.backward_bytes(x.lmask, x.gmask, spec.H, spec.d, 4 if spec.dtype == "f32" else 2)
     roofline = None
     if not args.no_timing:
         tot, calls = plan.timing_read_backward()
@@ -657,8 +657,8 @@ def run_backward(args, spec, x, ts, lm, gm, plan):
         kflop = fl.backward_kernel_flops(x.lmask, x.gmask, spec.window, spec.dilation, spec.d)
         per = {k: v / max(calls, 1) * 1e-3 for k, v in tot.items()}     # s per launch
         dom = max(per, key=per.get)
-        if spec.dtype == "bf16":
-            # the contractions run on bf16 matrix cores
+        if spec.dtype != "f32":
+            # the contractions run on the 16-bit matrix cores
             achieved = kflop[dom] / per[dom] / 1e12
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_MFMA,
                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_MFMA, 4), "traffic": None}
@@ -667,8 +667,8 @@ def run_backward(args, spec, x, ts, lm, gm, plan):
             achieved = flop / t_call / 1e12
             roofline = {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_FP32_VECTOR,
                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_VECTOR, 4), "traffic": None}
-        roofline.update({"kernel": dom if spec.dtype == "bf16" else "backward (all kernels)",
-                         "algorithmic_flop": kflop[dom] if spec.dtype == "bf16" else flop,
+        roofline.update({"kernel": dom if spec.dtype != "f32" else "backward (all kernels)",
+                         "algorithmic_flop": kflop[dom] if spec.dtype != "f32" else flop,
                          "kernel_us": {k: round(v * 1e6, 2) for k, v in per.items() if v > 0},
                          "timed_calls": calls, "source_sha256": source_hash()})
     tokens = spec.B * spec.n
@@ -736,8 +736,8 @@ def main():
         args.workload = {"causal": "charlm", "causal_backward": "charlm", "blocksparse": "bsparse", "layer": "ftlayer"}.get(args.which, "base")
     spec = workloads.named(args.workload)
     if args.dtype is not None:
-        if args.which not in ("forward", "layer", "causal", "blocksparse"):
-            raise SystemExit("--dtype applies to the forward, layer, causal and blocksparse passes")
+        if args.which not in ("forward", "layer", "causal", "blocksparse", "backward"):
+            raise SystemExit("--dtype applies to the forward, backward, layer, causal and blocksparse passes")
         import dataclasses
         spec = dataclasses.replace(spec, dtype=args.dtype)
     x = workloads.generate(spec)

@@ -52,8 +52,8 @@ typedef struct lwattn_plan_s* lwattn_plan_t;
  * float32; with 16-bit storage the matrix cores take the probabilities rounded
  * to the storage type.  LWATTN_F16 (IEEE half) runs the forwards
  * (lwattn_forward, lwattn_forward_noalloc, lwattn_forward_causal,
- * lwattn_forward_blocksparse) and the encoder layer; the backwards return
- * LWATTN_E_UNSUPPORTED for it. */
+ * lwattn_forward_blocksparse), lwattn_backward and the encoder layer;
+ * lwattn_backward_causal returns LWATTN_E_UNSUPPORTED for it. */
 typedef enum { LWATTN_F32 = 0, LWATTN_BF16 = 1, LWATTN_F16 = 2 } lwattn_dtype;
 
 typedef enum {
@@ -251,8 +251,9 @@ lwattn_status lwattn_layer_destroy(lwattn_layer_t layer);
  *   dQ, dK, dV, dQg, dKg, dVg : device [B,H,n,d], dtype; every element is
  *                         written (zero where no path reaches it).  They must
  *                         not overlap each other or any input.
- * All pointers 16-byte aligned.  Arithmetic in fp32 (bf16 storage is widened
- * on load and rounded RNE on store).  bf16: the global-index compaction
+ * All pointers 16-byte aligned.  Arithmetic in fp32 (16-bit storage is widened
+ * on load and rounded RNE on store).  16-bit storage (bf16 or fp16, on the
+ * matrix cores): the global-index compaction
  * (inside the dQ launch, by its first B workgroups, when that grid fits one
  * round of workgroup slots), dQ (which leaves each row's log-sum-exp and D in
  * the plan's workspace), the chunk sums of the global rows and keys and their
@@ -312,7 +313,7 @@ lwattn_status lwattn_timing_read(lwattn_plan_t plan, float* ms, int32_t cap,
  * milliseconds over the recorded backwards.  Slots (*nkernels = 5): the
  * global-index compaction, dQ, the chunk sums of the global rows and keys, their
  * merge, dK/dV; a slot whose kernel a backward did not launch counts zero
- * (fp32 launches slots 0, 1 and 4; bf16 skips slot 0 when the compaction runs
+ * (fp32 launches slots 0, 1 and 4; 16-bit storage skips slot 0 when the compaction runs
  * inside dQ, slot 3 when the merge runs inside dK/dV, slots 2 and 3 without
  * global tokens). */
 lwattn_status lwattn_timing_read_backward(lwattn_plan_t plan, float* ms, int32_t cap,
@@ -320,7 +321,7 @@ lwattn_status lwattn_timing_read_backward(lwattn_plan_t plan, float* ms, int32_t
 lwattn_status lwattn_timing_disable(lwattn_plan_t plan);
 
 /* Testing aid for the failure path of the in-kernel wait (for test code only).
- * In the next forward of `plan` (or bf16 backward, whichever comes first), the
+ * In the next forward of `plan` (or 16-bit backward, whichever comes first), the
  * row compactions publish a number the other workgroups do not wait for, and
  * their waits give up after 64 polls: every workgroup still exits normally,
  * the outputs are undefined, and lwattn_sync_status reports LWATTN_E_DEVICE

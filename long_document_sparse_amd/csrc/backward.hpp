@@ -969,6 +969,20 @@ __device__ __forceinline__ void store_dT_s(uint8_t* rowptr, const f32x16 (&x)[2]
     }
 }
 
+// <dO, O> of a row whose dO fragments are at hand (both half-lanes get it),
+// for either 16-bit storage type S.
+template <typename S>
+__device__ __forceinline__ float row_dot_s(const svec<S, 8> (&df)[4], const uint8_t* O, int pos, int h) {
+  svec<S, 8> of[4];
+  row_frags_s<S>(of, O, pos, h);
+  float a = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaf((float)df[c][e], (float)of[c][e], a);
+  return half_sum(a);
+}
+
 // <dO, O> of a row whose dO fragments are at hand (both half-lanes get it).
 __device__ __forceinline__ float row_dot(const bf16x8 (&df)[4], const uint8_t* O, int pos, int h) {
   bf16x8 of[4];
@@ -1041,15 +1055,16 @@ __device__ __forceinline__ bool interior_tile(int kt, int r) { return kt >= 1 &&
 // Exponents are in log2 units, c = scale log2(e); the running offset m (the
 // same in both halves of the row) moves only when a score passes it by more
 // than TAU, so the terms stay below 2^TAU; l is this lane's share of the sum.
+template <typename S>
 __device__ __forceinline__ void dq_tile(f32x16 (&acc)[2], float& m, float& l, const uint8_t* tK,
-                                        const uint8_t* tV, const bf16x8 (&qf)[4], const bf16x8 (&df)[4],
+                                        const uint8_t* tV, const svec<S, 8> (&qf)[4], const svec<S, 8> (&df)[4],
                                         float dsum, uint32_t M, bool full, float c, int kq, int lane) {
   const int h32 = lane >> 5, qi = lane & 31;
   f32x16 x = {}, e = {};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    x = mfma_bf16(frag_row(tK, 32 * kq + qi, h32, k), qf[k], x);
-    e = mfma_bf16(frag_row(tV, 32 * kq + qi, h32, k), df[k], e);
+    x = mfma16(as_frag<S>(frag_row(tK, 32 * kq + qi, h32, k)), qf[k], x);
+    e = mfma16(as_frag<S>(frag_row(tV, 32 * kq + qi, h32, k)), df[k], e);
   }
   if (!full) mask_half(x, M, h32);
   float mr = x[0];
@@ -1075,9 +1090,9 @@ __device__ __forceinline__ void dq_tile(f32x16 (&acc)[2], float& m, float& l, co
   }
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    const bf16x8 bs = acc_frag(x, c2);
+    const svec<S, 8> bs = acc_frag_s<S>(x, c2);
 #pragma unroll
-    for (int db = 0; db < 2; ++db) acc[db] = mfma_bf16(frag_tr(tK + 32 * kq * 128, c2, db, lane), bs, acc[db]);
+    for (int db = 0; db < 2; ++db) acc[db] = mfma16(as_frag<S>(frag_tr(tK + 32 * kq * 128, c2, db, lane)), bs, acc[db]);
   }
 }
 
@@ -1137,7 +1152,7 @@ __device__ __forceinline__ bool merge_key_quadrants(f32x16 (&acc)[2], float& m, 
 // count reaches the other threads through LDS across the loop's barrier, and
 // the list is read with coherent loads after it.  Without it the compaction
 // was an earlier launch and the first poll sees the word.
-template <bool CF>
+template <bool CF, typename S>
 __device__ void dq_local(const BwParams& p, const Params& cp, int b, int h, int rho, int blk, uint8_t* sm,
                          TMeta (&tm)[3]) {
   // LDS: three slots of (K tile, V tile), then three Stage records; the
@@ -1234,10 +1249,10 @@ __device__ void dq_local(const BwParams& p, const Params& cp, int b, int h, int 
   const int rps = I0 + row < nr ? rho + (I0 + row) * s : -1;
   const uint8_t rkd = kind_of(p, b, rps);
   const bool rlocal = rkd == 2;
-  bf16x8 qf[4], df[4];
-  row_frags(qf, p.Q + hoff, rps, h32);
-  row_frags(df, p.dO + hoff, rps, h32);
-  const float dsum = row_dot(df, p.O + hoff, rps, h32);
+  svec<S, 8> qf[4], df[4];
+  row_frags_s<S>(qf, p.Q + hoff, rps, h32);
+  row_frags_s<S>(df, p.dO + hoff, rps, h32);
+  const float dsum = row_dot_s<S>(df, p.O + hoff, rps, h32);
   // every load so far has landed, tile 0 too; from here on the only loads in
   // flight are the tiles' (and, at global tiles, the index reads)
   wait_all_loads();
@@ -1284,16 +1299,16 @@ __device__ void dq_local(const BwParams& p, const Params& cp, int b, int h, int 
     const int a = row - T * kt - 32 * kq;
     const uint32_t M = rlocal ? kb & (win ? bit_range_v(a, a + 2 * r + 1) : 0xFFFFFFFFu) : 0u;
     const bool full = all_local && kb == 0xFFFFFFFFu && (!win || interior_tile(kt, r));
-    dq_tile(acc, m, l, tK, tK + TB, qf, df, dsum, M, full, c, kq, lane);
+    dq_tile<S>(acc, m, l, tK, tK + TB, qf, df, dsum, M, full, c, kq, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && rps >= 0) {
     const float L = l, mm = m;
     const float mul = rlocal && L > 0.0f ? p.scale / L : 0.0f;
-    store_dT(p.dQ + hoff + (int64_t)rps * 128, acc, mul, h32);
+    store_dT_s<S>(p.dQ + hoff + (int64_t)rps * 128, acc, mul, h32);
     if (rkd != 1) {
       const f32x16 z[2] = {};
-      store_dT(p.dQg + hoff + (int64_t)rps * 128, z, 0.0f, h32);
+      store_dT_s<S>(p.dQg + hoff + (int64_t)rps * 128, z, 0.0f, h32);
     }
     if (rlocal && h32 == 0) p.stats[bh * n + rps] = make_float2(L > 0.0f ? mm + log2f(L) : INFINITY, dsum);
   }
@@ -1304,16 +1319,16 @@ __device__ void dq_local(const BwParams& p, const Params& cp, int b, int h, int 
 // order; P = exp2(c S - lse2(row)) (c = scale log2(e), lse2 the row's
 // log-sum-exp in log2 units, from mt.lse), dS = P (dP - D).  Bit k of M: row
 // 32 rq + k counts for the lane's key (ignored when `full`: every row counts).
-template <typename MT>
+template <typename S, typename MT>
 __device__ __forceinline__ void kv_tile(f32x16 (&dk)[2], f32x16 (&dv)[2], const uint8_t* tQ,
-                                        const uint8_t* tdO, const bf16x8 (&kf)[4], const bf16x8 (&vf)[4],
+                                        const uint8_t* tdO, const svec<S, 8> (&kf)[4], const svec<S, 8> (&vf)[4],
                                         const MT& mt, float c, int rq, int lane, uint32_t M, bool full) {
   const int h32 = lane >> 5, qi = lane & 31;
   f32x16 x = {}, e = {};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    x = mfma_bf16(frag_row(tQ, 32 * rq + qi, h32, k), kf[k], x);
-    e = mfma_bf16(frag_row(tdO, 32 * rq + qi, h32, k), vf[k], e);
+    x = mfma16(as_frag<S>(frag_row(tQ, 32 * rq + qi, h32, k)), kf[k], x);
+    e = mfma16(as_frag<S>(frag_row(tdO, 32 * rq + qi, h32, k)), vf[k], e);
   }
   if (!full) mask_half(x, M, h32);
   f32x16 pp;
@@ -1333,11 +1348,11 @@ __device__ __forceinline__ void kv_tile(f32x16 (&dk)[2], f32x16 (&dv)[2], const 
   }
 #pragma unroll
   for (int c2 = 0; c2 < 2; ++c2) {
-    const bf16x8 bs = acc_frag(x, c2), bp = acc_frag(pp, c2);
+    const svec<S, 8> bs = acc_frag_s<S>(x, c2), bp = acc_frag_s<S>(pp, c2);
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      dk[db] = mfma_bf16(frag_tr(tQ + 32 * rq * 128, c2, db, lane), bs, dk[db]);
-      dv[db] = mfma_bf16(frag_tr(tdO + 32 * rq * 128, c2, db, lane), bp, dv[db]);
+      dk[db] = mfma16(as_frag<S>(frag_tr(tQ + 32 * rq * 128, c2, db, lane)), bs, dk[db]);
+      dv[db] = mfma16(as_frag<S>(frag_tr(tdO + 32 * rq * 128, c2, db, lane)), bp, dv[db]);
     }
   }
 }
@@ -1381,7 +1396,7 @@ __device__ __forceinline__ bool sum_row_quadrants(f32x16 (&dk)[2], f32x16 (&dv)[
 // of (b, h), in one pass over the row tiles: the window's (with Q and the
 // local rows' statistics), then the global rows' (with Qg and theirs).  The
 // statistics must be in place.
-template <bool MF>
+template <bool MF, typename S>
 __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uint8_t* sm, Meta (&mt)[2]) {
   float* xch = reinterpret_cast<float*>(sm + 4 * TB);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, kq = w & 1, rq = w >> 1;
@@ -1463,9 +1478,9 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
   const int key = 32 * kq + qi;
   const int kps = J0 + key < nr ? rho + (J0 + key) * s : -1;
   const uint8_t kkd = kind_of(p, b, kps);
-  bf16x8 kf[4], vf[4];
-  row_frags(kf, p.K + hoff, kps, h32);
-  row_frags(vf, p.V + hoff, kps, h32);
+  svec<S, 8> kf[4], vf[4];
+  row_frags_s<S>(kf, p.K + hoff, kps, h32);
+  row_frags_s<S>(vf, p.V + hoff, kps, h32);
   const bool gfold = MF && t < T;
   const float2 gst0 = gfold && ntot > nwin ? global_stat(t) : make_float2(0.0f, 0.0f);
   const float2 gst1 = gfold && ntot > nwin + 1 ? global_stat(T + t) : make_float2(0.0f, 0.0f);
@@ -1475,16 +1490,16 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
   auto finish_window = [&]() {
     // global keys' dK, dV come from the chunk sums
     if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0 && kkd != 1) {
-      store_dT(p.dK + hoff + (int64_t)kps * 128, dk, p.scale, h32);
-      store_dT(p.dV + hoff + (int64_t)kps * 128, dv, 1.0f, h32);
+      store_dT_s<S>(p.dK + hoff + (int64_t)kps * 128, dk, p.scale, h32);
+      store_dT_s<S>(p.dV + hoff + (int64_t)kps * 128, dv, 1.0f, h32);
     }
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
       dk[db] = f32x16{};
       dv[db] = f32x16{};
     }
-    row_frags(kf, p.Kg + hoff, kps, h32);
-    row_frags(vf, p.Vg + hoff, kps, h32);
+    row_frags_s<S>(kf, p.Kg + hoff, kps, h32);
+    row_frags_s<S>(vf, p.Vg + hoff, kps, h32);
   };
   auto step = [&](int qt) {
     const int cur = qt & 1;
@@ -1511,15 +1526,15 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
     const int bk = 2 * r + key - T * qt - 32 * rq;
     const uint32_t M = win ? (kkd == 2 ? rb & bit_range_v(bk - 2 * r, bk + 1) : 0u) : (kkd != 0 ? rb : 0u);
     const bool full = rb == 0xFFFFFFFFu && (win ? all_win && interior_tile(qt, r) : all_real);
-    kv_tile(dk, dv, tQ, tQ + TB, kf, vf, mt[cur], c, rq, lane, M, full);
+    kv_tile<S>(dk, dv, tQ, tQ + TB, kf, vf, mt[cur], c, rq, lane, M, full);
   };
   // the window's row tiles; then the global rows' tiles (Kg, Vg fragments)
   for (int qt = 0; qt < nwin; ++qt) step(qt);
   finish_window();
   for (int qt = nwin; qt < ntot; ++qt) step(qt);
   if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0) {
-    store_dT(p.dKg + hoff + (int64_t)kps * 128, dk, p.scale, h32);
-    store_dT(p.dVg + hoff + (int64_t)kps * 128, dv, 1.0f, h32);
+    store_dT_s<S>(p.dKg + hoff + (int64_t)kps * 128, dk, p.scale, h32);
+    store_dT_s<S>(p.dVg + hoff + (int64_t)kps * 128, dv, 1.0f, h32);
   }
 }
 
@@ -1531,6 +1546,7 @@ __device__ void dkv_local(const BwParams& p, int b, int h, int rho, int blk, uin
 // chunk's tiles for each, the tiles double-buffered as in the dQ kernel.
 constexpr int GS_SMEM = 4 * TB + 2 * 64 * 64 * 4;
 
+template <typename S>
 __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, uint8_t* sm, Meta (&mt)[2]) {
   float* xch = reinterpret_cast<float*>(sm + 4 * TB);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -1574,10 +1590,10 @@ __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, ui
     const int rq = w & 1, kq = w >> 1;
     const int row = 32 * rq + qi;
     const int gps = T * gt + row < g ? gidx[row] : -1;
-    bf16x8 qf[4], df[4];
-    row_frags(qf, p.Qg + hoff, gps, h32);
-    row_frags(df, p.dO + hoff, gps, h32);
-    const float dsum = row_dot(df, p.O + hoff, gps, h32);
+    svec<S, 8> qf[4], df[4];
+    row_frags_s<S>(qf, p.Qg + hoff, gps, h32);
+    row_frags_s<S>(df, p.dO + hoff, gps, h32);
+    const float dsum = row_dot_s<S>(df, p.O + hoff, gps, h32);
     const float c = p.scale * LOG2E;
     const bool all_live = __all(gps >= 0);
     float m = -INFINITY, l = 0.0f;
@@ -1594,7 +1610,7 @@ __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, ui
       prefetch(st + 1);   // the first tile of part (2) follows the last of part (1)
       const uint8_t* tK = sm + cur * 2 * TB;
       const uint32_t kb = mt[cur].okm[kq];
-      dq_tile(acc, m, l, tK, tK + TB, qf, df, dsum, gps >= 0 ? kb : 0u, all_live && kb == 0xFFFFFFFFu, c, kq,
+      dq_tile<S>(acc, m, l, tK, tK + TB, qf, df, dsum, gps >= 0 ? kb : 0u, all_live && kb == 0xFFFFFFFFu, c, kq,
               lane);
     }
     if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && gps >= 0) {
@@ -1617,9 +1633,9 @@ __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, ui
     const int kq = w & 1, rq = w >> 1;
     const int key = 32 * kq + qi;
     const int kps = T * gt + key < g ? gidx[key] : -1;
-    bf16x8 kf[4], vf[4];
-    row_frags(kf, p.K + hoff, kps, h32);
-    row_frags(vf, p.V + hoff, kps, h32);
+    svec<S, 8> kf[4], vf[4];
+    row_frags_s<S>(kf, p.K + hoff, kps, h32);
+    row_frags_s<S>(vf, p.V + hoff, kps, h32);
     f32x16 dk[2] = {}, dv[2] = {};
     const float c = p.scale * LOG2E;
     const bool all_live = __all(kps >= 0);
@@ -1637,7 +1653,7 @@ __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, ui
       if (st + 1 < 2 * nt) prefetch(st + 1);
       const uint8_t* tQ = sm + cur * 2 * TB;
       const uint32_t rb = mt[cur].okm[rq];
-      kv_tile(dk, dv, tQ, tQ + TB, kf, vf, mt[cur], c, rq, lane, kps >= 0 ? rb : 0u,
+      kv_tile<S>(dk, dv, tQ, tQ + TB, kf, vf, mt[cur], c, rq, lane, kps >= 0 ? rb : 0u,
               all_live && rb == 0xFFFFFFFFu);
     }
     if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0) {
@@ -1661,7 +1677,7 @@ __device__ void global_chunk(const BwParams& p, int b, int h, int gt, int sp, ui
 // With CF, workgroups 0 .. B-1, first in dispatch order, compact
 // batch row blockIdx.x (cp: the forward's compaction and its publication)
 // before their own rows.
-template <bool CF>
+template <bool CF, typename S>
 __global__ __launch_bounds__(NTH) void dq_kernel(BwParams p, Params cp) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ TMeta mt[3];
@@ -1671,41 +1687,44 @@ __global__ __launch_bounds__(NTH) void dq_kernel(BwParams p, Params cp) {
   }
   int b, h, rho, blk;
   decode_block(p, xcd_remap(blockIdx.x, gridDim.x), b, h, rho, blk);
-  dq_local<CF>(p, cp, b, h, rho, blk, sm, mt);
+  dq_local<CF, S>(p, cp, b, h, rho, blk, sm, mt);
 }
 
+template <typename S>
 __device__ void global_merge(const BwParams& p, int64_t item, int lane);
 
 // With MF, the workgroups past the B * blocks_per_b key blocks (in the last
 // round's spare slots) merge the global rows' and keys' chunk sums
 // (global_merge, one item a wave): work of its own, which no key block waits
 // for (those combine the global rows' statistics themselves).
-template <bool MF>
+template <bool MF, typename S>
 __global__ __launch_bounds__(NTH) void dkv_kernel(BwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ Meta mt[2];
   const int nblk = p.B * p.blocks_per_b;
   if (MF && (int)blockIdx.x >= nblk) {
-    global_merge(p, (int64_t)((int)blockIdx.x - nblk) * (NTH / 64) + (threadIdx.x >> 6), threadIdx.x & 63);
+    global_merge<S>(p, (int64_t)((int)blockIdx.x - nblk) * (NTH / 64) + (threadIdx.x >> 6), threadIdx.x & 63);
     return;
   }
   int b, h, rho, blk;
   decode_block(p, xcd_remap(blockIdx.x, nblk), b, h, rho, blk);
-  dkv_local<MF>(p, b, h, rho, blk, sm, mt);
+  dkv_local<MF, S>(p, b, h, rho, blk, sm, mt);
 }
 
+template <typename S>
 __global__ __launch_bounds__(NTH) void global_chunk_kernel(BwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ Meta mt[2];
   const int sp = blockIdx.x % p.gsplit, rest = blockIdx.x / p.gsplit;
   const int gt = rest % p.ntg, bh = rest / p.ntg;
-  global_chunk(p, bh / p.H, bh % p.H, gt, sp, sm, mt);
+  global_chunk<S>(p, bh / p.H, bh % p.H, gt, sp, sm, mt);
 }
 
 // One wave per (b, h, global index): combines the chunk sums (offsets in log2
 // units) into dQg and the global key's dK, dV, and (unless the merge runs
 // beside the dK/dV work, which combines them itself) the row's log-sum-exp
 // (log2 units) and D.  Lane = d.
+template <typename S>
 __device__ void global_merge(const BwParams& p, int64_t item, int lane) {
   if (item >= (int64_t)p.B * p.H * p.max_global) return;
   const int gi = (int)(item % p.max_global);
@@ -1738,20 +1757,21 @@ __device__ void global_merge(const BwParams& p, int64_t item, int lane) {
     sv += k[sp * 128 + 64 + lane];
   }
   const int64_t ro = (bh * n + pos) * 128 + lane * 2;
-  *reinterpret_cast<__bf16*>(p.dQg + ro) = (__bf16)(L > 0.0f ? p.scale * a / L : 0.0f);
-  *reinterpret_cast<__bf16*>(p.dK + ro) = (__bf16)(p.scale * sk);
-  *reinterpret_cast<__bf16*>(p.dV + ro) = (__bf16)sv;
+  *reinterpret_cast<S*>(p.dQg + ro) = (S)(L > 0.0f ? p.scale * a / L : 0.0f);
+  *reinterpret_cast<S*>(p.dK + ro) = (S)(p.scale * sk);
+  *reinterpret_cast<S*>(p.dV + ro) = (S)sv;
   if (!p.merge_fold) {
-    const float dov = (float)*reinterpret_cast<const __bf16*>(p.dO + ro);
-    float dd = dov * (float)*reinterpret_cast<const __bf16*>(p.O + ro);
+    const float dov = (float)*reinterpret_cast<const S*>(p.dO + ro);
+    float dd = dov * (float)*reinterpret_cast<const S*>(p.O + ro);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) dd += __shfl_xor(dd, o);
     if (lane == 0) p.stats[bh * n + pos] = make_float2(L > 0.0f ? mm + log2f(L) : INFINITY, dd);
   }
 }
 
+template <typename S>
 __global__ __launch_bounds__(NTH) void global_merge_kernel(BwParams p) {
-  global_merge(p, (int64_t)blockIdx.x * (NTH / 64) + (threadIdx.x >> 6), threadIdx.x & 63);
+  global_merge<S>(p, (int64_t)blockIdx.x * (NTH / 64) + (threadIdx.x >> 6), threadIdx.x & 63);
 }
 
 }  // namespace mk

@@ -257,7 +257,7 @@ __device__ void causal_dq_block(const CzBwParams& p, int b, int h, int rho, int 
     const int a = row - T * kt - 32 * kq;
     const uint32_t M = rvalid ? kb & bit_range_v(a, a + r + 1) : 0u;
     const bool full = all_valid && kb == 0xFFFFFFFFu && interior(kt, r);
-    dq_tile(acc, m, l, tK, tK + TB, qf, df, dsum, M, full, c, kq, lane);
+    dq_tile<__bf16>(acc, m, l, tK, tK + TB, qf, df, dsum, M, full, c, kq, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && rps >= 0) {
@@ -342,7 +342,7 @@ __device__ void causal_dkv_block(const CzBwParams& p, int b, int h, int rho, int
     const int b0 = key - T * qt - 32 * rq;
     const uint32_t M = kvalid ? rb & bit_range_v(b0, b0 + r + 1) : 0u;
     const bool full = all_valid && rb == 0xFFFFFFFFu && interior(qt, r);
-    kv_tile(dk, dv, tQ, tQ + TB, kf, vf, tm[cur], c, rq, lane, M, full);
+    kv_tile<__bf16>(dk, dv, tQ, tQ + TB, kf, vf, tm[cur], c, rq, lane, M, full);
     cur = cur == 2 ? 0 : cur + 1;
   }
   if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0) {

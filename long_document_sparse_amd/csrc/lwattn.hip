@@ -87,7 +87,7 @@ struct lwattn_plan_s {
   uint64_t* ready_cnt = nullptr;   // [B] (epoch << 32) | global count, written by the backward's compaction
   int32_t* fault = nullptr;   // sticky: a workgroup gave up waiting for its row
   int32_t epoch = 0;          // forwards launched (kept in 1 .. INT32_MAX - 1)
-  bool inject_timeout = false; // fault test: the next forward's (or bf16 backward's) waits give up
+  bool inject_timeout = false; // fault test: the next forward's (or 16-bit backward's) waits give up
   int32_t* head_stride = nullptr;
   int32_t* head_blk = nullptr;
   // backward: 64-row blocks per head (all residue classes), per-row statistics
@@ -779,7 +779,7 @@ lwattn_status lwattn_plan(const lwattn_config* cfg, int hip_device, lwattn_plan_
   alloc((void**)&p->head_blk, (size_t)(H + 1) * 4);
   alloc((void**)&p->head_blk64, (size_t)(H + 1) * 4);
   alloc((void**)&p->stats, (size_t)B * H * n * sizeof(float2));
-  if (cfg->dtype == LWATTN_BF16 && cfg->max_global > 0 && n > 0 && B > 0 && H > 0) {
+  if (cfg->dtype != LWATTN_F32 && cfg->max_global > 0 && n > 0 && B > 0 && H > 0) {
     // the positions of a head are cut into chunks of whole 64-row tiles, as
     // many as bring the workgroups of the chunk sums (one per batch row, head,
     // 64 global rows and chunk) to about one round of slots, two per compute
@@ -1042,7 +1042,6 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
-  if (c.dtype == LWATTN_F16) return LWATTN_E_UNSUPPORTED;
   const void* ptrs[] = {Q, K, V, Qg, Kg, Vg, O, dO, dQ, dK, dV, dQg, dKg, dVg};
   for (const void* q : ptrs)
     if (!q || !aligned16(q)) return LWATTN_E_INVALID;
@@ -1085,7 +1084,7 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
     return p->bw_events[(size_t)p->bw_calls * 2 * kNumBwKernels + 2 * k + e];
   };
   cp.spin_limit = (1 << 18) + (int32_t)(c.n >> 2);   // as the forward's waits
-  if (p->inject_timeout && c.dtype == LWATTN_BF16) {
+  if (p->inject_timeout && c.dtype != LWATTN_F32) {
     // fault test: the rows are published under another number and the dQ
     // workgroups that wait for them (compaction inside dQ) give up at once
     p->inject_timeout = false;
@@ -1133,7 +1132,7 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
   bp.scale = c.scale;
   const int64_t grid = (int64_t)c.B * p->blocks64_per_b + (int64_t)c.B * c.H * bp.ntg;
   if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
-  if (c.dtype == LWATTN_BF16) {
+  if (c.dtype != LWATTN_F32) {
     // 2. dQ, dQg (zero) and the local rows' statistics; 3. the chunk sums of
     // the global rows and keys; 4. their merge: dQg, the global keys' dK, dV
     // (and the global rows' statistics, unless it runs inside 5); 5. dK, dV
@@ -1145,12 +1144,19 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
     // tiles are read through 32-bit buffer offsets over a head's n rows
     if (nchunk > INT32_MAX || nmerge > INT32_MAX || (int64_t)c.n * 128 >= lwk::OOB_OFF)
       return LWATTN_E_UNSUPPORTED;
-    for (const void* f : {(const void*)mk::dq_kernel<true>, (const void*)mk::dq_kernel<false>})
+    // the kernels of the plan's 16-bit storage type (bf16 or fp16)
+    const bool f16 = c.dtype == LWATTN_F16;
+    const auto dq_fold = f16 ? mk::dq_kernel<true, _Float16> : mk::dq_kernel<true, __bf16>;
+    const auto dq_plain = f16 ? mk::dq_kernel<false, _Float16> : mk::dq_kernel<false, __bf16>;
+    const auto dkv_fold = f16 ? mk::dkv_kernel<true, _Float16> : mk::dkv_kernel<true, __bf16>;
+    const auto dkv_plain = f16 ? mk::dkv_kernel<false, _Float16> : mk::dkv_kernel<false, __bf16>;
+    const auto chunk_k = f16 ? mk::global_chunk_kernel<_Float16> : mk::global_chunk_kernel<__bf16>;
+    const auto merge_k = f16 ? mk::global_merge_kernel<_Float16> : mk::global_merge_kernel<__bf16>;
+    for (const void* f : {(const void*)dq_fold, (const void*)dq_plain})
       (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DQ_SMEM);
-    for (const void* f : {(const void*)mk::dkv_kernel<true>, (const void*)mk::dkv_kernel<false>})
+    for (const void* f : {(const void*)dkv_fold, (const void*)dkv_plain})
       (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::DKV_SMEM);
-    (void)hipFuncSetAttribute((const void*)mk::global_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              mk::GS_SMEM);
+    (void)hipFuncSetAttribute((const void*)chunk_k, hipFuncAttributeMaxDynamicSharedMemorySize, mk::GS_SMEM);
     // When the dQ grid fits one round of workgroup slots (three per compute
     // unit), its first B workgroups compact the batch rows and the others
     // wait for their row before their global tiles: no launch of its own.  On
@@ -1161,10 +1167,10 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
     if (!bp.comp_fold)
       hipExtLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream,
                             ev(0, 0), ev(0, 1), 0u, cp);
-    hipExtLaunchKernelGGL(bp.comp_fold ? mk::dq_kernel<true> : mk::dq_kernel<false>, dim3((uint32_t)nblk),
+    hipExtLaunchKernelGGL(bp.comp_fold ? dq_fold : dq_plain, dim3((uint32_t)nblk),
                           dim3(lwk::bw::NTH), mk::DQ_SMEM, stream, ev(1, 0), ev(1, 1), 0u, bp, cp);
     if (nchunk > 0)
-      hipExtLaunchKernelGGL(mk::global_chunk_kernel, dim3((uint32_t)nchunk), dim3(lwk::bw::NTH), mk::GS_SMEM,
+      hipExtLaunchKernelGGL(chunk_k, dim3((uint32_t)nchunk), dim3(lwk::bw::NTH), mk::GS_SMEM,
                             stream, ev(2, 0), ev(2, 1), 0u, bp);
     // The merge of the chunk sums runs in workgroups behind the key blocks of
     // the dK/dV launch when the last round of that grid (two workgroups per
@@ -1176,10 +1182,10 @@ lwattn_status lwattn_backward(lwattn_plan_t p, const void* Q, const void* K, con
     const int64_t spare = (nblk + dslots - 1) / dslots * dslots - nblk;
     bp.merge_fold = mwg > 0 && mwg <= spare ? 1 : 0;
     if (mwg > 0 && !bp.merge_fold)
-      hipExtLaunchKernelGGL(mk::global_merge_kernel, dim3((uint32_t)nmerge), dim3(lwk::bw::NTH), 0, stream,
+      hipExtLaunchKernelGGL(merge_k, dim3((uint32_t)nmerge), dim3(lwk::bw::NTH), 0, stream,
                             ev(3, 0), ev(3, 1), 0u, bp);
     const int64_t ndkv = nblk + (bp.merge_fold ? mwg : 0);
-    hipExtLaunchKernelGGL(bp.merge_fold ? mk::dkv_kernel<true> : mk::dkv_kernel<false>, dim3((uint32_t)ndkv),
+    hipExtLaunchKernelGGL(bp.merge_fold ? dkv_fold : dkv_plain, dim3((uint32_t)ndkv),
                           dim3(lwk::bw::NTH), mk::DKV_SMEM, stream, ev(4, 0), ev(4, 1), 0u, bp);
   } else {
     hipExtLaunchKernelGGL(lwk::bw::compact_kernel, dim3(c.B), dim3(lwk::NT), (uint32_t)(lwk::NW * 4), stream,

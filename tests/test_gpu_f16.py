@@ -142,17 +142,62 @@ def test_f16_noalloc_matches_plan():
     assert torch.count_nonzero(status).item() == 0
 
 
-def test_f16_backwards_are_unsupported():
+def test_f16_causal_backward_is_unsupported():
     spec = workloads.custom(1, 2, 128, 64, 32, "f16", [0, 0], seed=36, n_global=1)
     x = workloads.generate(spec)
     ts, lm, gm = to_dev(x)
     plan = make_plan(spec)
-    o = plan(*ts, lm, gm)
-    with pytest.raises(lw.LwattnError):
-        plan.backward(*ts, lm, gm, o, o)
     oc = plan.forward_causal(ts[0], ts[1], ts[2], lm)
     with pytest.raises(lw.LwattnError):
         plan.backward_causal(ts[0], ts[1], ts[2], lm, oc, oc)
+    plan.close()
+
+
+# The backward in fp16 (the matrix-core kernels of bf16, with fp16 operands):
+# the bound of the bf16 backward (2e-2 of each tensor's largest entry, from
+# 2^-9 roundings of P, dS and the gradients) scaled to fp16's roundoff, 8
+# times smaller: 3e-3.  The last two grids take each mix of the launch folds
+# on a 256-CU device (compaction launched and merge folded; compaction folded
+# and merge launched), the first ones both folds.
+BWD = [
+    # (B, H, n, window, dilation, n_global, global_mode, pad_mode, pad_hi)
+    (2, 2, 333, 40, [0, 2], 5, "random", "per_batch", 80),
+    (1, 3, 300, 128, [0, 1, 3], 70, "random", "per_batch", 60),   # two global tiles
+    (1, 2, 257, 16, [1, 4], 0, "first", "scatter", 40),           # no globals
+    (13, 1, 4096, 32, [0], 20, "random", "per_batch", 300),
+    (8, 1, 4096, 32, [0], 10, "random", "per_batch", 300),
+]
+BWD_REL = 3e-3
+
+
+@pytest.mark.parametrize("case", BWD, ids=lambda c: f"B{c[0]}H{c[1]}n{c[2]}w{c[3]}g{c[5]}{c[7]}")
+def test_f16_backward_matches_oracle(case):
+    B, H, n, window, dil, ng, gmode, pmode, phi = case
+    spec = workloads.custom(B, H, n, 64, window, "f16", dil, seed=23, n_global=ng, global_mode=gmode,
+                            pad_mode=pmode, pad_hi=phi)
+    say(f"f16 backward case {case}")
+    x = workloads.generate(spec)
+    ts, lm, gm = to_dev(x)
+    plan = make_plan(spec, max_global=max(ng, 1))
+    o = torch.empty_like(ts[0])
+    plan(*ts, lm, gm, out=o)
+    go = torch.from_numpy(np.random.default_rng(3).standard_normal(x.tensors()[0].shape)).to(
+        ts[0].device).to(ts[0].dtype)
+    grads = tuple(torch.full_like(ts[0], float("nan")) for _ in range(6))
+    plan.backward(*ts, lm, gm, o, go, grads=grads)
+    assert plan.sync_status() == lw.OK
+    ins = [to_np64(t) for t in ts]
+    want = oracle.backward(*ins, x.lmask, x.gmask, to_np64(go), spec.window, spec.dilation, spec.scale)
+    for name, g, w in zip(("dQ", "dK", "dV", "dQg", "dKg", "dVg"), grads, want):
+        got = to_np64(g)
+        assert np.all(np.isfinite(got)), name
+        ref = float(np.max(np.abs(w)))
+        err = float(np.max(np.abs(got - w)))
+        say(f"f16 backward {name}: max abs err {err:.3e}, max |g| {ref:.3e}")
+        if ref == 0.0:
+            assert err == 0.0, name
+        else:
+            assert err <= BWD_REL * ref, name
     plan.close()
 
 

@@ -290,8 +290,8 @@ def run_causal_backward(args, spec, x, ts, lm, plan):
     import torch
     from long_document_sparse_amd import flops as fl
     from long_document_sparse_amd import lwattn
-    if spec.dtype != "bf16":
-        raise SystemExit("the causal variant's backward runs on bf16 storage")
+    if spec.dtype not in ("bf16", "f16"):
+        raise SystemExit("the causal variant's backward runs on 16-bit storage (bf16 or f16)")
     q, k, v = ts[0], ts[1], ts[2]
     g = torch.Generator().manual_seed(5)
     do = (torch.randn(q.shape, generator=g) / 8).to(q.device).to(torch.bfloat16)
@@ -736,8 +736,8 @@ def main():
         args.workload = {"causal": "charlm", "causal_backward": "charlm", "blocksparse": "bsparse", "layer": "ftlayer"}.get(args.which, "base")
     spec = workloads.named(args.workload)
     if args.dtype is not None:
-        if args.which not in ("forward", "layer", "causal", "blocksparse", "backward"):
-            raise SystemExit("--dtype applies to the forward, backward, layer, causal and blocksparse passes")
+        if args.which == "causal_backward" and args.dtype == "f32":
+            raise SystemExit("the causal variant runs on 16-bit storage (bf16 or f16)")
         import dataclasses
         spec = dataclasses.replace(spec, dtype=args.dtype)
     x = workloads.generate(spec)

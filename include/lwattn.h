@@ -52,8 +52,7 @@ typedef struct lwattn_plan_s* lwattn_plan_t;
  * float32; with 16-bit storage the matrix cores take the probabilities rounded
  * to the storage type.  LWATTN_F16 (IEEE half) runs the forwards
  * (lwattn_forward, lwattn_forward_noalloc, lwattn_forward_causal,
- * lwattn_forward_blocksparse), lwattn_backward and the encoder layer;
- * lwattn_backward_causal returns LWATTN_E_UNSUPPORTED for it. */
+ * lwattn_forward_blocksparse), the backwards and the encoder layer. */
 typedef enum { LWATTN_F32 = 0, LWATTN_BF16 = 1, LWATTN_F16 = 2 } lwattn_dtype;
 
 typedef enum {
@@ -146,8 +145,9 @@ lwattn_status lwattn_forward_causal(lwattn_plan_t plan, const void* Q, const voi
  * P_ij (dP_ij - D_i) with dP_ij = <dO_i, V_j> and D_i = <dO_i, O_i>;
  * dQ_i = scale sum_j dS_ij K_j, dK_j = scale sum_i dS_ij Q_i,
  * dV_j = sum_i P_ij dO_i).  O is the output of lwattn_forward_causal on the
- * same inputs.  Q, K, V, O, dO, dQ, dK, dV: [B][H][n][64] bf16, 16-byte
- * aligned, device memory; lmask float32 [B][n].  Every element of dQ, dK, dV
+ * same inputs.  Q, K, V, O, dO, dQ, dK, dV: [B][H][n][64] in the plan's 16-bit
+ * storage type (bf16 or fp16), 16-byte aligned, device memory; lmask float32
+ * [B][n].  Every element of dQ, dK, dV
  * is written (zero at rows and keys whose lmask is 0).  Enqueued on `stream`
  * (two kernel launches, no allocation, no host sync); it uses the plan's
  * per-row statistics buffer, so it must not overlap a backward of the same

@@ -1,5 +1,5 @@
-// Causal variant of the window attention, on the matrix cores: the forward for
-// 16-bit storage (bf16 or fp16), the backward for bf16.
+// Causal variant of the window attention, forward and backward, 16-bit
+// storage (bf16 or fp16), on the matrix cores.
 //
 // "LongFormer: The Long-Document Transformer" (reading notes), section
 // Implementation: an autoregressive language model uses the dilated sliding
@@ -192,6 +192,7 @@ struct CzBwParams {
 
 // dQ of the 64 rows I0 .. of residue class rho: key tiles I0 - r .. I0 + 63,
 // running softmax (the dQ kernel's tile step); stats of the valid rows.
+template <typename S>
 __device__ void causal_dq_block(const CzBwParams& p, int b, int h, int rho, int blk, uint8_t* sm,
                                 TMeta (&tm)[3]) {
   bw::mk::Stage* stg = reinterpret_cast<bw::mk::Stage*>(sm + 6 * TB);
@@ -229,10 +230,10 @@ __device__ void causal_dq_block(const CzBwParams& p, int b, int h, int rho, int 
   const int row = 32 * rq + qi;
   const int rps = I0 + row < nr ? rho + (I0 + row) * s : -1;
   const bool rvalid = rps >= 0 && p.lmask[(int64_t)b * n + rps] != 0.0f;
-  bf16x8 qf[4], df[4];
-  row_frags(qf, p.Q + hoff, rps, h32);
-  row_frags(df, p.dO + hoff, rps, h32);
-  const float dsum = row_dot(df, p.O + hoff, rps, h32);
+  svec<S, 8> qf[4], df[4];
+  row_frags_s<S>(qf, p.Q + hoff, rps, h32);
+  row_frags_s<S>(df, p.dO + hoff, rps, h32);
+  const float dsum = row_dot_s<S>(df, p.O + hoff, rps, h32);
   wait_all_loads();
   if (nt > 1) prefetch(1, 1);
   const float c = p.scale * LOG2E;
@@ -257,11 +258,11 @@ __device__ void causal_dq_block(const CzBwParams& p, int b, int h, int rho, int 
     const int a = row - T * kt - 32 * kq;
     const uint32_t M = rvalid ? kb & bit_range_v(a, a + r + 1) : 0u;
     const bool full = all_valid && kb == 0xFFFFFFFFu && interior(kt, r);
-    dq_tile<__bf16>(acc, m, l, tK, tK + TB, qf, df, dsum, M, full, c, kq, lane);
+    dq_tile<S>(acc, m, l, tK, tK + TB, qf, df, dsum, M, full, c, kq, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   if (merge_key_quadrants(acc, m, l, xch, rq, kq, lane) && rps >= 0) {
-    store_dT(p.dQ + hoff + (int64_t)rps * 128, acc, rvalid && l > 0.0f ? p.scale / l : 0.0f, h32);
+    store_dT_s<S>(p.dQ + hoff + (int64_t)rps * 128, acc, rvalid && l > 0.0f ? p.scale / l : 0.0f, h32);
     if (rvalid && h32 == 0) p.stats[bh * n + rps] = make_float2(l > 0.0f ? m + log2f(l) : INFINITY, dsum);
   }
 }
@@ -269,6 +270,7 @@ __device__ void causal_dq_block(const CzBwParams& p, int b, int h, int rho, int 
 // dK, dV of the 64 keys J0 .. of residue class rho: row tiles J0 .. J0 + 63 + r
 // (the rows at or after a key, within r), the dK/dV kernel's tile step with
 // the rows' statistics.
+template <typename S>
 __device__ void causal_dkv_block(const CzBwParams& p, int b, int h, int rho, int blk, uint8_t* sm,
                                  TMeta (&tm)[3]) {
   bw::mk::StageS* stg = reinterpret_cast<bw::mk::StageS*>(sm + 6 * TB);
@@ -309,9 +311,9 @@ __device__ void causal_dkv_block(const CzBwParams& p, int b, int h, int rho, int
   const int key = 32 * kq + qi;
   const int kps = J0 + key < nr ? rho + (J0 + key) * s : -1;
   const bool kvalid = kps >= 0 && p.lmask[(int64_t)b * n + kps] != 0.0f;
-  bf16x8 kf[4], vf[4];
-  row_frags(kf, p.K + hoff, kps, h32);
-  row_frags(vf, p.V + hoff, kps, h32);
+  svec<S, 8> kf[4], vf[4];
+  row_frags_s<S>(kf, p.K + hoff, kps, h32);
+  row_frags_s<S>(vf, p.V + hoff, kps, h32);
   wait_all_loads();
   if (nt > 1) prefetch(1, 1);
   const float c = p.scale * LOG2E;
@@ -342,32 +344,34 @@ __device__ void causal_dkv_block(const CzBwParams& p, int b, int h, int rho, int
     const int b0 = key - T * qt - 32 * rq;
     const uint32_t M = kvalid ? rb & bit_range_v(b0, b0 + r + 1) : 0u;
     const bool full = all_valid && rb == 0xFFFFFFFFu && interior(qt, r);
-    kv_tile<__bf16>(dk, dv, tQ, tQ + TB, kf, vf, tm[cur], c, rq, lane, M, full);
+    kv_tile<S>(dk, dv, tQ, tQ + TB, kf, vf, tm[cur], c, rq, lane, M, full);
     cur = cur == 2 ? 0 : cur + 1;
   }
   if (sum_row_quadrants(dk, dv, xch, rq, kq, lane) && kps >= 0) {
-    store_dT(p.dK + hoff + (int64_t)kps * 128, dk, kvalid ? p.scale : 0.0f, h32);
-    store_dT(p.dV + hoff + (int64_t)kps * 128, dv, kvalid ? 1.0f : 0.0f, h32);
+    store_dT_s<S>(p.dK + hoff + (int64_t)kps * 128, dk, kvalid ? p.scale : 0.0f, h32);
+    store_dT_s<S>(p.dV + hoff + (int64_t)kps * 128, dv, kvalid ? 1.0f : 0.0f, h32);
   }
 }
 
 constexpr int BW_DQ_SMEM = 6 * TB + 3 * (int)sizeof(bw::mk::Stage);
 constexpr int BW_DKV_SMEM = 6 * TB + 3 * (int)sizeof(bw::mk::StageS);
 
+template <typename S>
 __global__ __launch_bounds__(NTH) void causal_dq_kernel(CzBwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ TMeta tm[3];
   int b, h, rho, blk;
   bw::decode_block(p, xcd_remap(blockIdx.x, gridDim.x), b, h, rho, blk);
-  causal_dq_block(p, b, h, rho, blk, sm, tm);
+  causal_dq_block<S>(p, b, h, rho, blk, sm, tm);
 }
 
+template <typename S>
 __global__ __launch_bounds__(NTH) void causal_dkv_kernel(CzBwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t sm[];
   __shared__ TMeta tm[3];
   int b, h, rho, blk;
   bw::decode_block(p, xcd_remap(blockIdx.x, gridDim.x), b, h, rho, blk);
-  causal_dkv_block(p, b, h, rho, blk, sm, tm);
+  causal_dkv_block<S>(p, b, h, rho, blk, sm, tm);
 }
 
 }  // namespace cz

@@ -949,7 +949,7 @@ lwattn_status lwattn_backward_causal(lwattn_plan_t p, const void* Q, const void*
   if (!p) return LWATTN_E_INVALID;
   const lwattn_config& c = p->cfg;
   if ((int64_t)c.B * c.H * c.n == 0) return LWATTN_OK;   // empty problem
-  if (c.dtype != LWATTN_BF16) return LWATTN_E_UNSUPPORTED;
+  if (c.dtype == LWATTN_F32) return LWATTN_E_UNSUPPORTED;
   if ((int64_t)c.n * 128 >= lwk::OOB_OFF) return LWATTN_E_UNSUPPORTED;
   const void* ptrs[] = {Q, K, V, O, dO, dQ, dK, dV};
   for (const void* q : ptrs)
@@ -977,15 +977,14 @@ lwattn_status lwattn_backward_causal(lwattn_plan_t p, const void* Q, const void*
   bp.scale = c.scale;
   const int64_t grid = (int64_t)c.B * p->blocks64_per_b;
   if (grid > INT32_MAX) return LWATTN_E_UNSUPPORTED;
-  (void)hipFuncSetAttribute((const void*)lwk::cz::causal_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            lwk::cz::BW_DQ_SMEM);
-  (void)hipFuncSetAttribute((const void*)lwk::cz::causal_dkv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            lwk::cz::BW_DKV_SMEM);
+  const bool f16 = c.dtype == LWATTN_F16;
+  const auto dqk = f16 ? lwk::cz::causal_dq_kernel<_Float16> : lwk::cz::causal_dq_kernel<__bf16>;
+  const auto dkvk = f16 ? lwk::cz::causal_dkv_kernel<_Float16> : lwk::cz::causal_dkv_kernel<__bf16>;
+  (void)hipFuncSetAttribute((const void*)dqk, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::cz::BW_DQ_SMEM);
+  (void)hipFuncSetAttribute((const void*)dkvk, hipFuncAttributeMaxDynamicSharedMemorySize, lwk::cz::BW_DKV_SMEM);
   // dQ and the rows' statistics first; dK, dV read those statistics
-  hipLaunchKernelGGL(lwk::cz::causal_dq_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::BW_DQ_SMEM,
-                     stream, bp);
-  hipLaunchKernelGGL(lwk::cz::causal_dkv_kernel, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::BW_DKV_SMEM,
-                     stream, bp);
+  hipLaunchKernelGGL(dqk, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::BW_DQ_SMEM, stream, bp);
+  hipLaunchKernelGGL(dkvk, dim3((uint32_t)grid), dim3(lwk::bw::NTH), lwk::cz::BW_DKV_SMEM, stream, bp);
   if (!hip_ok(hipGetLastError(), "hipGetLastError")) return LWATTN_E_DEVICE;
   return LWATTN_OK;
 }

@@ -142,17 +142,6 @@ def test_f16_noalloc_matches_plan():
     assert torch.count_nonzero(status).item() == 0
 
 
-def test_f16_causal_backward_is_unsupported():
-    spec = workloads.custom(1, 2, 128, 64, 32, "f16", [0, 0], seed=36, n_global=1)
-    x = workloads.generate(spec)
-    ts, lm, gm = to_dev(x)
-    plan = make_plan(spec)
-    oc = plan.forward_causal(ts[0], ts[1], ts[2], lm)
-    with pytest.raises(lw.LwattnError):
-        plan.backward_causal(ts[0], ts[1], ts[2], lm, oc, oc)
-    plan.close()
-
-
 # The backward in fp16 (the matrix-core kernels of bf16, with fp16 operands):
 # the bound of the bf16 backward (2e-2 of each tensor's largest entry, from
 # 2^-9 roundings of P, dS and the gradients) scaled to fp16's roundoff, 8
@@ -307,3 +296,31 @@ def test_f16_blocksparse_matches_oracle(case, strong):
     pad = x.lmask == 0
     for b in range(B):
         assert not np.any(got[b][:, pad[b]])
+
+
+@pytest.mark.parametrize("case", CAUSAL[:3], ids=lambda c: f"B{c[0]}H{c[1]}n{c[2]}w{c[3]}{c[5]}")
+def test_f16_causal_backward_matches_oracle(case):
+    """The causal backward in fp16: the bound of the fp16 backward (3e-3 of
+    each tensor's largest entry)."""
+    B, H, n, window, dil, pmode, phi = case
+    spec = workloads.custom(B, H, n, 64, window, "f16", dil, seed=35, n_global=0,
+                            pad_mode=pmode, pad_hi=phi, max_global=0)
+    say(f"f16 causal backward case {case}")
+    x = workloads.generate(spec)
+    q, k, v = (torch.from_numpy(a).to("cuda:0").to(torch.float16) for a in (x.Q, x.K, x.V))
+    lm = torch.from_numpy(x.lmask).to("cuda:0")
+    plan = make_plan(spec, max_global=0)
+    o = plan.forward_causal(q, k, v, lm)
+    go = torch.from_numpy(np.random.default_rng(4).standard_normal(x.Q.shape)).to("cuda:0").to(torch.float16)
+    grads = plan.backward_causal(q, k, v, lm, o, go)
+    assert plan.sync_status() == lw.OK
+    want = oracle.backward_causal(to_np64(q), to_np64(k), to_np64(v), x.lmask, to_np64(go), window, dil,
+                                  spec.scale)
+    for name, g, w in zip(("dQ", "dK", "dV"), grads, want):
+        got = to_np64(g)
+        assert np.all(np.isfinite(got)), name
+        ref = float(np.max(np.abs(w)))
+        err = float(np.max(np.abs(got - w)))
+        say(f"f16 causal backward {name}: max abs err {err:.3e}, max |g| {ref:.3e}")
+        assert err <= (BWD_REL * ref if ref > 0 else 0.0), name
+    plan.close()
